@@ -1,0 +1,2 @@
+"""fp64 CPU oracle for the Gated DeltaNet recurrent forward (test infrastructure only)."""
+from .oracle import gdn_forward, build, max_threads  # noqa: F401

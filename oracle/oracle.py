@@ -1,0 +1,156 @@
+"""Python front end of the fp64 CPU oracle for the Gated DeltaNet recurrent forward.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The HIP library never calls it and the
+two share no code.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain fp64 loops, see its header for
+the recurrence and the layouts).  This module only builds that file with gcc if
+needed, converts inputs to the exact arrays the GPU receives (bf16 as raw bits,
+fp32 as is, fp32 initial state widened to fp64) and calls it through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "gdn_oracle.c")
+LIBRARY = os.path.join(_HERE, "libgdn_oracle.so")
+
+# Plain build: no fast-math, no FMA contraction, OpenMP over independent units.
+CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-std=c11"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(source: str = SOURCE, library: str = LIBRARY, extra_flags=()) -> str:
+    """Compile the oracle C source into a shared library (always rebuilds)."""
+    tmp = library + ".tmp%d" % os.getpid()
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-o", tmp, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, library)
+    return library
+
+
+def load(library: str = LIBRARY):
+    """Load (building on first use if absent) and type the oracle library."""
+    lib = ctypes.CDLL(library)
+    f = lib.gdn_oracle_forward
+    f.restype = ctypes.c_int
+    f.argtypes = [
+        ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32,
+    ]
+    lib.gdn_oracle_max_threads.restype = ctypes.c_int
+    lib.gdn_oracle_max_threads.argtypes = []
+    return lib
+
+
+def _get_lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+                build()
+            _lib = load(LIBRARY)
+        return _lib
+
+
+def _as_numpy(x):
+    """torch tensor or array -> (numpy array, io code). bf16 becomes uint16 bits."""
+    try:
+        import torch
+    except ImportError:  # pragma: no cover - torch is always present here
+        torch = None
+    if torch is not None and isinstance(x, torch.Tensor):
+        x = x.detach().cpu().contiguous()
+        if x.dtype == torch.bfloat16:
+            return x.view(torch.int16).numpy().view(np.uint16), 1
+        if x.dtype == torch.float32:
+            return x.numpy(), 0
+        if x.dtype == torch.float64:
+            return x.numpy(), 2
+        if x.dtype == torch.int32:
+            return x.numpy(), 3
+        raise TypeError("unsupported tensor dtype %s" % x.dtype)
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return x, 1
+    if x.dtype == np.float32:
+        return x, 0
+    if x.dtype == np.float64:
+        return x, 2
+    if x.dtype == np.int32:
+        return x, 3
+    raise TypeError("unsupported array dtype %s" % x.dtype)
+
+
+def gdn_forward(q, k, v, g, beta, cu_seqlens, h0=None, n_threads=None, library=None):
+    """Run the fp64 oracle.
+
+    q, k: [T, Hk, dk]; v: [T, Hv, dv] -- all fp32, or all bf16 (torch bf16 or raw
+    uint16 bits); g, beta: [T, Hv] fp32; cu_seqlens: [N+1] int32; h0: optional
+    [N, Hv, dv, dk] fp32 or fp64 (widened exactly).
+
+    Returns (out [T, Hv, dv] float64, hT [N, Hv, dv, dk] float64).
+    """
+    qn, qc = _as_numpy(q)
+    kn, kc = _as_numpy(k)
+    vn, vc = _as_numpy(v)
+    if not (qc == kc == vc and qc in (0, 1)):
+        raise TypeError("q, k, v must share one dtype: fp32 or bf16")
+    gn, gc = _as_numpy(g)
+    bn, bc = _as_numpy(beta)
+    if gc != 0 or bc != 0:
+        raise TypeError("g and beta must be fp32")
+    cu, cc = _as_numpy(cu_seqlens)
+    if cc != 3:
+        raise TypeError("cu_seqlens must be int32")
+    if qn.ndim != 3 or kn.shape != qn.shape or vn.ndim != 3:
+        raise ValueError("q, k must be [T, Hk, dk] and v [T, Hv, dv]")
+    T, hk, dk = qn.shape
+    hv, dv = vn.shape[1], vn.shape[2]
+    if vn.shape[0] != T or gn.shape != (T, hv) or bn.shape != (T, hv):
+        raise ValueError("inconsistent token / head shapes")
+    n = cu.shape[0] - 1
+    if n < 0 or (n > 0 and int(cu[-1]) != T):
+        raise ValueError("cu_seqlens[-1] must equal T")
+    h0n = None
+    if h0 is not None:
+        h0n, hc = _as_numpy(h0)
+        if hc not in (0, 2):
+            raise TypeError("h0 must be fp32 or fp64")
+        h0n = np.ascontiguousarray(h0n, dtype=np.float64)
+        if h0n.shape != (n, hv, dv, dk):
+            raise ValueError("h0 must be [N, Hv, dv, dk]")
+    out = np.zeros((T, hv, dv), dtype=np.float64)
+    hT = np.zeros((max(n, 0), hv, dv, dk), dtype=np.float64)
+    lib = load(library) if library is not None else _get_lib()
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+
+    def ptr(a):
+        return None if a is None or a.size == 0 else a.ctypes.data
+
+    rc = lib.gdn_oracle_forward(
+        n, ptr(cu), hk, hv, dk, dv, qc,
+        ptr(qn), ptr(kn), ptr(vn), ptr(gn), ptr(bn),
+        ptr(h0n), ptr(out), ptr(hT), int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (code %d)" % rc)
+    return out, hT
+
+
+def max_threads() -> int:
+    return int(_get_lib().gdn_oracle_max_threads())

@@ -1,0 +1,371 @@
+"""Pins for the fp64 oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` function takes a ``forward`` callable with the signature of
+``oracle.gdn_forward`` and raises AssertionError when the forward disagrees with
+
+  * brute-force products of the per-token transition matrices (a closed form of
+    the gated delta rule, evaluated with numpy matrix products);
+  * a finite-difference gradient of the delta-rule regression loss (the
+    Widrow-Hoff reading of the rule);
+  * hand-derived scalar values (tests/golden/scalar_delta_rule.json);
+  * invariants: identity when beta = g = 0, exact recall of a written value,
+    exact chunk-split carry, closed forms for beta = 0 and for a vanishing decay,
+    associative recall with orthonormal keys, linearity in (h0, v), and grouped
+    heads equal to duplicated key heads.
+
+The rule being pinned is the gated delta rule of Yang, Kautz and Hatamizadeh
+("Gated Delta Networks", ICLR 2025): S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T)
++ beta_t v_t k_t^T, o_t = S_t q_t, with S a dv x dk matrix, walked token by token
+per sequence as in the page "Defending Against the Training-Inference Numeric
+Mismatch in RL (Especially Linear Attention)", section 3.2.
+
+The tests run every pin on the real oracle (all must pass) and on deliberately
+broken copies of it (each copy must fail at least one pin).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+RTOL = 1e-11
+
+
+# ------------------------------------------------------------------ helpers
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def random_case(seed, lengths, hk, hv, dk, dv, with_h0=True, g_scale=1.0):
+    """fp32 inputs with the workload's distributions (numpy, for small pins)."""
+    r = _rng(seed)
+    T = int(sum(lengths))
+    q = _unit(r.standard_normal((T, hk, dk))).astype(np.float32)
+    k = _unit(r.standard_normal((T, hk, dk))).astype(np.float32)
+    v = r.standard_normal((T, hv, dv)).astype(np.float32)
+    g = (-np.log1p(np.exp(r.standard_normal((T, hv)))) * g_scale).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-r.standard_normal((T, hv))))).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    h0 = (0.5 * r.standard_normal((len(lengths), hv, dv, dk))).astype(np.float32) if with_h0 else None
+    return dict(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu, h0=h0)
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = max(np.linalg.norm(b), 1e-300)
+    return float(np.linalg.norm(a - b) / den)
+
+
+def _close(a, b, tol=RTOL, what=""):
+    e = _rel(a, b)
+    assert e <= tol, "%s: relative error %.3e > %.1e" % (what, e, tol)
+
+
+def bruteforce(case):
+    """Closed form via transition products.
+
+    With A_t = exp(g_t) (I - beta_t k_t k_t^T) (dk x dk) the rule reads
+    S_t = S_{t-1} A_t + beta_t v_t k_t^T, hence
+    S_t = S_0 A_1 ... A_t + sum_{s<=t} beta_s v_s k_s^T A_{s+1} ... A_t.
+    Every S_t is rebuilt from scratch from that sum (no recurrence is run).
+    """
+    q = case["q"].astype(np.float64)
+    k = case["k"].astype(np.float64)
+    v = case["v"].astype(np.float64)
+    g = case["g"].astype(np.float64)
+    beta = case["beta"].astype(np.float64)
+    cu = case["cu_seqlens"]
+    T, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    grp = hv // hk
+    N = len(cu) - 1
+    out = np.zeros((T, hv, dv))
+    hT = np.zeros((N, hv, dv, dk))
+    for n in range(N):
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        for h in range(hv):
+            kh = h // grp
+            S0 = np.zeros((dv, dk)) if case["h0"] is None else case["h0"][n, h].astype(np.float64)
+            A = [math.exp(g[t, h]) * (np.eye(dk) - beta[t, h] * np.outer(k[t, kh], k[t, kh]))
+                 for t in range(t0, t1)]
+            W = [beta[t, h] * np.outer(v[t, h], k[t, kh]) for t in range(t0, t1)]
+
+            def prod(a, b):
+                m = np.eye(dk)
+                for x in A[a:b]:
+                    m = m @ x
+                return m
+
+            St = S0
+            for t in range(t0, t1):
+                m = t - t0 + 1
+                St = S0 @ prod(0, m)
+                for s in range(m):
+                    St = St + W[s] @ prod(s + 1, m)
+                out[t, h] = St @ q[t, kh]
+            hT[n, h] = St
+    return out, hT
+
+
+# ---------------------------------------------------------------------- pins
+
+def pin_bruteforce_plain(forward):
+    """One sequence, no grouping, dk != dv (catches transposed state indexing)."""
+    c = random_case(11, [7], hk=1, hv=1, dk=5, dv=3)
+    out, hT = forward(**c)
+    bo, bh = bruteforce(c)
+    _close(out, bo, what="out vs transition products")
+    _close(hT, bh, what="hT vs transition products")
+
+
+def pin_bruteforce_grouped_varlen(forward):
+    """Grouped heads (2 value heads per key head), several sequences incl. an empty one."""
+    c = random_case(12, [3, 0, 6, 1], hk=2, hv=4, dk=4, dv=6)
+    out, hT = forward(**c)
+    bo, bh = bruteforce(c)
+    _close(out, bo, what="out vs transition products (grouped)")
+    _close(hT, bh, what="hT vs transition products (grouped)")
+    # the empty sequence hands its initial state through unchanged
+    assert np.array_equal(hT[1], c["h0"][1].astype(np.float64)), "empty sequence must return h0"
+
+
+def pin_bruteforce_no_h0(forward):
+    c = random_case(13, [5, 4], hk=1, hv=2, dk=3, dv=4, with_h0=False)
+    out, hT = forward(**c)
+    bo, bh = bruteforce(c)
+    _close(out, bo, what="out vs transition products (zero h0)")
+    _close(hT, bh, what="hT vs transition products (zero h0)")
+
+
+def _loss_grad_fd(S, kv, vv, eps=1e-3):
+    """Central finite-difference gradient of L(S) = 0.5 * ||S k - v||^2."""
+    G = np.zeros_like(S)
+    for j in range(S.shape[0]):
+        for i in range(S.shape[1]):
+            E = np.zeros_like(S)
+            E[j, i] = eps
+            lp = 0.5 * np.sum(((S + E) @ kv - vv) ** 2)
+            lm = 0.5 * np.sum(((S - E) @ kv - vv) ** 2)
+            G[j, i] = (lp - lm) / (2 * eps)
+    return G
+
+
+def pin_gradient_step(forward):
+    """One token: the new state is one gradient step of size beta on the regression
+    loss 0.5 ||S k - v||^2, taken at the decayed state exp(g) S_0 (the delta /
+    Widrow-Hoff rule with a decay applied first).  Gradient by finite differences."""
+    c = random_case(21, [1], hk=1, hv=1, dk=4, dv=3)
+    out, hT = forward(**c)
+    a = math.exp(float(c["g"][0, 0]))
+    b = float(c["beta"][0, 0])
+    S = a * c["h0"][0, 0].astype(np.float64)
+    kv = c["k"][0, 0].astype(np.float64)
+    vv = c["v"][0, 0].astype(np.float64)
+    expect = S - b * _loss_grad_fd(S, kv, vv)
+    _close(hT[0, 0], expect, tol=1e-9, what="gradient-step reading")
+    _close(out[0, 0], expect @ c["q"][0, 0].astype(np.float64), tol=1e-9, what="read-out of the new state")
+
+
+def pin_scalar_golden(forward):
+    """dk = dv = 1 hand-derived values (tests/golden/scalar_delta_rule.json)."""
+    with open(os.path.join(GOLDEN, "scalar_delta_rule.json")) as f:
+        fx = json.load(f)
+    for case in fx["cases"]:
+        T = len(case["v"])
+        c = dict(q=np.array(case["q"], np.float32).reshape(T, 1, 1),
+                 k=np.array(case["k"], np.float32).reshape(T, 1, 1),
+                 v=np.array(case["v"], np.float32).reshape(T, 1, 1),
+                 g=np.array(case["g"], np.float32).reshape(T, 1),
+                 beta=np.array(case["beta"], np.float32).reshape(T, 1),
+                 cu_seqlens=np.array([0, T], np.int32),
+                 h0=np.array(case["s0"], np.float32).reshape(1, 1, 1, 1))
+        out, hT = forward(**c)
+        np.testing.assert_allclose(out.reshape(-1), case["o"], rtol=case["rtol"], atol=0,
+                                   err_msg="scalar golden %s: outputs" % case["name"])
+        np.testing.assert_allclose(hT.reshape(-1), [case["s"][-1]], rtol=case["rtol"], atol=0,
+                                   err_msg="scalar golden %s: final state" % case["name"])
+
+
+def pin_identity_when_idle(forward):
+    """beta = 0 and g = 0: the state never changes (exactly) and o_t = h0 q_t."""
+    c = random_case(31, [6], hk=1, hv=2, dk=4, dv=5)
+    c["beta"][:] = 0.0
+    c["g"][:] = 0.0
+    out, hT = forward(**c)
+    assert np.array_equal(hT, c["h0"].astype(np.float64)), "state must be unchanged"
+    for t in range(6):
+        for h in range(2):
+            _close(out[t, h], c["h0"][0, h].astype(np.float64) @ c["q"][t, 0].astype(np.float64),
+                   what="idle read-out")
+
+
+def pin_exact_recall(forward):
+    """beta = 1 and a unit key: S_t k_t = v_t, since (I - k k^T) k = 0."""
+    c = random_case(32, [5], hk=1, hv=1, dk=6, dv=4)
+    k = _unit(_rng(33).standard_normal((5, 1, 6)))
+    c["k"] = k.astype(np.float32)
+    c["beta"][:] = 1.0
+    kk = c["k"].astype(np.float64)
+    for t in range(1, 6):
+        cc = dict(c)
+        cc["cu_seqlens"] = np.array([0, t], np.int32)
+        for key in ("q", "k", "v", "g", "beta"):
+            cc[key] = c[key][:t].copy()
+        _, hT = forward(**cc)
+        # the key is unit only up to fp32 rounding of its entries: renormalise
+        kt = kk[t - 1, 0]
+        nk = float(kt @ kt)
+        # S_t k = a S_{t-1}(k - k (k.k)) + v (k.k) -> v when k.k = 1; allow for the fp32 key norm
+        resid = hT[0, 0] @ kt - c["v"][t - 1, 0].astype(np.float64) * nk
+        assert np.linalg.norm(resid) <= 1e-6 * (1 + np.linalg.norm(c["v"][t - 1, 0])), \
+            "S_t k_t must equal v_t (residual %.3e)" % np.linalg.norm(resid)
+
+
+def pin_chunk_carry(forward):
+    """Splitting a sequence and carrying the fp64 state reproduces the full run exactly."""
+    c = random_case(41, [9], hk=1, hv=2, dk=4, dv=3)
+    out, hT = forward(**c)
+    cuts = [0, 4, 5, 9]
+    state = c["h0"].astype(np.float64)
+    outs = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        cc = dict(q=c["q"][a:b], k=c["k"][a:b], v=c["v"][a:b], g=c["g"][a:b], beta=c["beta"][a:b],
+                  cu_seqlens=np.array([0, b - a], np.int32), h0=state)
+        o, state = forward(**cc)
+        outs.append(o)
+    assert np.array_equal(np.concatenate(outs), out), "chunked outputs must be bit-identical"
+    assert np.array_equal(state, hT), "chunked final state must be bit-identical"
+
+
+def pin_no_write_closed_form(forward):
+    """beta = 0: o_t = exp(g_1 + ... + g_t) S_0 q_t (pure decay)."""
+    c = random_case(51, [6], hk=1, hv=2, dk=3, dv=4)
+    c["beta"][:] = 0.0
+    out, hT = forward(**c)
+    g = c["g"].astype(np.float64)
+    for h in range(2):
+        S0 = c["h0"][0, h].astype(np.float64)
+        for t in range(6):
+            _close(out[t, h], math.exp(g[:t + 1, h].sum()) * (S0 @ c["q"][t, 0].astype(np.float64)),
+                   what="pure decay read-out")
+        _close(hT[0, h], math.exp(g[:, h].sum()) * S0, what="pure decay state")
+
+
+def pin_full_forget(forward):
+    """exp(g) underflows to 0: S_t = beta_t v_t k_t^T and o_t = beta_t (k_t.q_t) v_t."""
+    c = random_case(52, [4], hk=1, hv=1, dk=5, dv=3)
+    c["g"][:] = -1.0e4
+    out, hT = forward(**c)
+    for t in range(4):
+        b = float(c["beta"][t, 0])
+        kv = c["k"][t, 0].astype(np.float64)
+        qv = c["q"][t, 0].astype(np.float64)
+        vv = c["v"][t, 0].astype(np.float64)
+        _close(out[t, 0], b * float(kv @ qv) * vv, what="full-forget read-out")
+    _close(hT[0, 0], float(c["beta"][3, 0]) * np.outer(c["v"][3, 0].astype(np.float64),
+                                                      c["k"][3, 0].astype(np.float64)),
+           what="full-forget state")
+
+
+def pin_associative_recall(forward):
+    """g = 0, beta = 1, orthonormal keys, zero start: every stored value is recalled."""
+    dk, dv, m = 6, 4, 5
+    r = _rng(61)
+    K, _ = np.linalg.qr(r.standard_normal((dk, dk)))
+    keys = K[:, :m].T  # m orthonormal rows
+    c = random_case(62, [m], hk=1, hv=1, dk=dk, dv=dv, with_h0=False)
+    c["k"] = keys.reshape(m, 1, dk).astype(np.float32)
+    c["g"][:] = 0.0
+    c["beta"][:] = 1.0
+    _, hT = forward(**c)
+    kk = c["k"].astype(np.float64)[:, 0]
+    # fp32 rounding of the keys breaks exact orthonormality slightly
+    for j in range(m):
+        _close(hT[0, 0] @ kk[j], c["v"][j, 0].astype(np.float64), tol=1e-6, what="recall of item %d" % j)
+
+
+def pin_linearity(forward):
+    """For fixed q, k, g, beta the map (h0, v) -> (out, hT) is linear."""
+    c1 = random_case(71, [5, 3], hk=1, hv=2, dk=3, dv=3)
+    c2 = random_case(72, [5, 3], hk=1, hv=2, dk=3, dv=3)
+    for key in ("q", "k", "g", "beta"):
+        c2[key] = c1[key]
+    a, b = 0.75, -1.25
+    mix = dict(c1)
+    mix["v"] = (a * c1["v"].astype(np.float64) + b * c2["v"].astype(np.float64))
+    mix["h0"] = (a * c1["h0"].astype(np.float64) + b * c2["h0"].astype(np.float64))
+    # feed the mixture in fp64 through the fp32 interface: keep it exactly representable
+    mix["v"] = mix["v"].astype(np.float32)
+    mix["h0"] = mix["h0"].astype(np.float32)
+    o1, s1 = forward(**c1)
+    o2, s2 = forward(**c2)
+    om, sm = forward(**mix)
+    # v/h0 mixtures rounded to fp32: compare against the same rounding applied on the right
+    _close(om, a * o1 + b * o2, tol=1e-6, what="linearity (out)")
+    _close(sm, a * s1 + b * s2, tol=1e-6, what="linearity (hT)")
+
+
+def pin_grouped_equals_duplicated(forward):
+    """Value head h reads key head h // (hv/hk): same bits as duplicating key heads."""
+    c = random_case(81, [4, 2], hk=2, hv=4, dk=3, dv=2)
+    out, hT = forward(**c)
+    d = dict(c)
+    d["q"] = np.repeat(c["q"], 2, axis=1)
+    d["k"] = np.repeat(c["k"], 2, axis=1)
+    out2, hT2 = forward(**d)
+    assert np.array_equal(out, out2) and np.array_equal(hT, hT2), "grouped heads must equal duplicated keys"
+
+
+def pin_gate_and_beta_per_value_head(forward):
+    """g and beta index the value head: value heads sharing a key head but with
+    different gates must evolve differently, each matching its own brute force."""
+    c = random_case(91, [5], hk=1, hv=2, dk=3, dv=3)
+    c["g"][:, 1] = c["g"][:, 0] * 3.0
+    c["beta"][:, 1] = 1.0 - c["beta"][:, 0]
+    out, hT = forward(**c)
+    bo, bh = bruteforce(c)
+    _close(out, bo, what="per-head gate/beta (out)")
+    _close(hT, bh, what="per-head gate/beta (hT)")
+
+
+def pin_bf16_inputs_widened_exactly(forward):
+    """bf16 inputs are read as their exact values (bits << 16)."""
+    import torch
+    c = random_case(95, [4], hk=1, hv=2, dk=4, dv=4)
+    cb = dict(c)
+    for key in ("q", "k", "v"):
+        cb[key] = torch.from_numpy(c[key]).to(torch.bfloat16)
+    out_b, hT_b = forward(**cb)
+    cf = dict(c)
+    for key in ("q", "k", "v"):
+        cf[key] = cb[key].to(torch.float32).numpy()
+    out_f, hT_f = forward(**cf)
+    assert np.array_equal(out_b, out_f) and np.array_equal(hT_b, hT_f), "bf16 must widen exactly"
+
+
+ALL_PINS = [
+    pin_bruteforce_plain,
+    pin_bruteforce_grouped_varlen,
+    pin_bruteforce_no_h0,
+    pin_gradient_step,
+    pin_scalar_golden,
+    pin_identity_when_idle,
+    pin_exact_recall,
+    pin_chunk_carry,
+    pin_no_write_closed_form,
+    pin_full_forget,
+    pin_associative_recall,
+    pin_linearity,
+    pin_grouped_equals_duplicated,
+    pin_gate_and_beta_per_value_head,
+    pin_bf16_inputs_widened_exactly,
+]

@@ -1,0 +1,78 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that the
+pins catch every one of them.  This is what makes the pins a real check: a pin
+set that a dropped term, a wrong sign, a wrong index or a swapped operand could
+slip past would not pin anything."""
+import functools
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+from oracle import oracle as oracle_mod
+
+# (name, text in gdn_oracle.c, replacement)
+MUTANTS = [
+    ("dropped_decay", "S[e] = a * S[e];", "S[e] = S[e];"),
+    ("gate_sign", "exp((double)g[t * hv + h])", "exp(-(double)g[t * hv + h])"),
+    ("gate_on_key_head", "exp((double)g[t * hv + h])", "exp((double)g[t * hv + kh])"),
+    ("dropped_beta", "const double u = b * (", "const double u = ("),
+    ("delta_sign", "(oracle_load(v, v_off + j, io_dtype) - p)", "(oracle_load(v, v_off + j, io_dtype) + p)"),
+    ("write_sign", "row[i] += u * oracle_load(k, qk_off + i, io_dtype);",
+     "row[i] -= u * oracle_load(k, qk_off + i, io_dtype);"),
+    ("write_with_query", "row[i] += u * oracle_load(k, qk_off + i, io_dtype);",
+     "row[i] += u * oracle_load(q, qk_off + i, io_dtype);"),
+    ("readout_with_key", "o += row[i] * oracle_load(q, qk_off + i, io_dtype);",
+     "o += row[i] * oracle_load(k, qk_off + i, io_dtype);"),
+    ("readout_before_write", "o += row[i] * oracle_load(q, qk_off + i, io_dtype);",
+     "o += (row[i] - u * oracle_load(k, qk_off + i, io_dtype)) * oracle_load(q, qk_off + i, io_dtype);"),
+    ("delta_on_undecayed_state", "p += row[i] * oracle_load(k, qk_off + i, io_dtype);",
+     "p += (row[i] / a) * oracle_load(k, qk_off + i, io_dtype);"),
+    ("group_map_modulo", "const int32_t kh = h / group;", "const int32_t kh = h % hk;"),
+    ("transposed_state", "double *row = S + (size_t)j * dk;", "double *row = S + (size_t)j;"),
+    ("value_index_key_heads", "const int64_t v_off = (t * hv + h) * (int64_t)dv;",
+     "const int64_t v_off = (t * hk + h) * (int64_t)dv;"),
+    ("dropped_h0", "S[e] = h0 ? h0[state_off + e] : 0.0;", "S[e] = 0.0;"),
+    ("query_scaled", "o += row[i] * oracle_load(q, qk_off + i, io_dtype);",
+     "o += row[i] * oracle_load(q, qk_off + i, io_dtype) / sqrt((double)dk);"),
+    ("bf16_low_half", "uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;",
+     "uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 15;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    with open(oracle_mod.SOURCE) as f:
+        src = f.read()
+    assert old in src, "mutation site for %s not found in the oracle source" % name
+    if name == "transposed_state":
+        # strided row: element (j, i) read from S[i * dv + j] instead of S[j * dk + i]
+        src = src.replace("double *row = S + (size_t)j * dk;", "double *row = S + (size_t)j;")
+        src = src.replace("row[i]", "row[(size_t)i * dv]")
+    else:
+        src = src.replace(old, new)
+    mpath = tmp_path / ("mutant_%s.c" % name)
+    mpath.write_text(src)
+    lib = str(tmp_path / ("libmutant_%s.so" % name))
+    oracle.build(str(mpath), lib)
+    fwd = functools.partial(oracle_mod.gdn_forward, library=lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(fwd)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, "mutant %s passed every pin" % name
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """Control: the same build path on an unmodified copy passes every pin."""
+    with open(oracle_mod.SOURCE) as f:
+        src = f.read()
+    mpath = tmp_path / "copy.c"
+    mpath.write_text(src)
+    lib = str(tmp_path / "libcopy.so")
+    oracle.build(str(mpath), lib)
+    fwd = functools.partial(oracle_mod.gdn_forward, library=lib)
+    for pin in oracle_pins.ALL_PINS:
+        pin(fwd)
