@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-invariant Gated DeltaNet recurrent forward on one MI355X.
+
+A step is one varlen prefill pass (gdn_fwd_varlen) over the 8-sequence batch with
+lengths drawn uniformly from [256, 4096] (16 query/key heads, 32 value heads,
+dk = dv = 128, bf16 q/k/v/out, fp32 gates and state, random initial states).
+``value`` is that pass's throughput in tokens/s with every input already in HBM.
+
+Also reported on the same line:
+  roofline      prefill kernel against the fp32 vector peak (7 dk dv flops per
+                token and value head: decay, key read-out, rank-1 write, query
+                read-out), from per-launch HIP events on the launch stream;
+  decode        one decode step at B = 64 and 256 against the HBM peak (state
+                read + written in place), rotating over state pools of >= 1 GiB
+                so the 256 MB Infinity Cache cannot hold them;
+  cpu_baseline  the fp64 oracle on the host cores, on a bounded sample;
+  parity        the timed outputs re-checked against the oracle (sampled heads).
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X: 256 CUs x 2.4 GHz x 256 flop/clk
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E
+METRIC = "GDN recurrent fwd tokens/s (prefill, decode) + % HBM/FP32-VALU roofline"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "invariant_linear_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kind, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was taken
+    on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "%s_traffic.json" % kind)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, stream):
+    """Per-launch durations (ms) from HIP events recorded on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
+
+
+def rel(x, r):
+    import numpy as np
+    x = np.asarray(x, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    return float(np.linalg.norm(x - r) / max(np.linalg.norm(r), 1e-300))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-key-heads", type=int, default=4, help="key heads in the CPU baseline sample")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the recurrent forward needs no collective and this "
+              "build measures a single MI355X (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from invariant_linear_attention_amd import gdn, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    gdn.load_library()
+
+    # ------------------------------------------------------------ prefill
+    w = synth.varlen_prefill(1001)
+    T = w.total_tokens
+    d = dict(q=w.q.to(dev), k=w.k.to(dev), v=w.v.to(dev), g=w.g.to(dev), beta=w.beta.to(dev),
+             h0=w.h0.to(dev), cu=w.cu_seqlens.to(dev))
+    out = torch.empty((T, 32, 128), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((w.n_seqs, 32, 128, 128), dtype=torch.float32, device=dev)
+
+    def prefill(_i):
+        gdn.gdn_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], out=out, hT=hT,
+                           stream=stream)
+
+    per, wall = time_launches(prefill, args.steps, args.warmup, stream)
+    ms = float(np.mean(per))
+    ms_med = float(np.median(per))
+    flops = 7.0 * 128 * 128 * 32 * T
+    tokens_per_s = T / (ms / 1e3)
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profile("prefill", src_hash)
+    roofline = {"bound": "alu", "achieved": flops / (ms / 1e3) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": flops / (ms / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                "traffic": traffic, "kernel": "gdn_prefill_kernel", "flops_per_launch": flops,
+                "launch_ms_mean": ms, "launch_ms_median": ms_med}
+
+    # parity of the timed outputs (sampled key heads; the oracle is test infrastructure)
+    from oracle import oracle
+    parity = {}
+    torch.cuda.synchronize()
+    for kh in (0, 15):
+        s = synth.head_slice(w, kh)
+        ro, rh = oracle.gdn_forward(s.q, s.k, s.v, s.g, s.beta, s.cu_seqlens, s.h0)
+        vs = slice(2 * kh, 2 * kh + 2)
+        parity["kh%d" % kh] = {"out": rel(out[:, vs].float().cpu().numpy(), ro),
+                               "state": rel(hT[:, vs].cpu().numpy(), rh)}
+    parity_ok = all(p["out"] <= 2e-3 and p["state"] <= 1e-4 for p in parity.values())
+
+    # ------------------------------------------------------------- decode
+    decode = None
+    if not args.no_decode:
+        decode = {}
+        for B in (64, 256):
+            bytes_state = B * 32 * 128 * 128 * 4
+            n_pools = max(4, int(np.ceil((1 << 30) / bytes_state)))
+            pools = [torch.randn((B, 32, 128, 128), device=dev) * 0.1 for _ in range(n_pools)]
+            dw = synth.make_workload(2000 + B, [1] * B)
+            dq, dk_, dv_, dg, db = (t.to(dev) for t in (dw.q, dw.k, dw.v, dw.g, dw.beta))
+            dout = torch.empty((B, 32, 128), dtype=torch.bfloat16, device=dev)
+
+            def dec(i, B=B):
+                gdn.gdn_decode_step(dq, dk_, dv_, dg, db, pools[i % n_pools], out=dout, stream=stream)
+
+            steps = max(args.steps, 2 * n_pools)
+            per_d, _ = time_launches(dec, steps, max(args.warmup, n_pools), stream)
+            ms_d = float(np.mean(per_d))
+            alg_bytes = B * (2 * 32 * 128 * 128 * 4 + 24832)
+            decode["B%d" % B] = {"tokens_per_s": B / (ms_d / 1e3), "launch_ms_mean": ms_d,
+                                 "launch_ms_median": float(np.median(per_d)),
+                                 "roofline": {"bound": "hbm", "achieved": alg_bytes / (ms_d / 1e3) / 1e9,
+                                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                              "frac": alg_bytes / (ms_d / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                              "traffic": traffic_from_profile("decode_B%d" % B, src_hash),
+                                              "bytes_per_launch": alg_bytes},
+                                 "state_pools": n_pools}
+            del pools
+
+    # ------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu:
+        kh_n = max(1, min(16, args.cpu_key_heads))
+        sample = synth.Workload(w.q[:, :kh_n].contiguous(), w.k[:, :kh_n].contiguous(),
+                                w.v[:, :2 * kh_n].contiguous(), w.g[:, :2 * kh_n].contiguous(),
+                                w.beta[:, :2 * kh_n].contiguous(), w.cu_seqlens, w.h0[:, :2 * kh_n].contiguous())
+        threads = os.cpu_count() or 1
+        t0 = time.perf_counter()
+        oracle.gdn_forward(sample.q, sample.k, sample.v, sample.g, sample.beta, sample.cu_seqlens, sample.h0,
+                           n_threads=threads)
+        dt = time.perf_counter() - t0
+        frac = (2 * kh_n) / 32.0
+        cpu = {"value": T * frac / dt, "unit": "tokens/s", "cores": min(threads, w.n_seqs * 2 * kh_n),
+               "kind": "oracle",
+               "sample": "fp64 oracle on %d of 32 value heads of the same 8-sequence batch (%d tokens), "
+                         "%.1f s, scaled to all heads" % (2 * kh_n, T, dt),
+               "seconds": dt}
+
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g=-softplus(N), beta=sigmoid(N))",
+        "config": {"workload": w.name, "lengths": w.lengths, "total_tokens": T, "hk": 16, "hv": 32, "dk": 128,
+                   "dv": 128, "io": "bf16", "state": "fp32", "seed": 1001},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode": decode,
+        "parity": {"ok": parity_ok, "max_rel_err": parity},
+        "kernel_source_hash": src_hash,
+        "wall_s_timed": wall,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+    if not parity_ok:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) batch-invariant Gated DeltaNet recurrent forward.
+ *
+ * The operation.  For every sequence n and every value head h (key head
+ * kh = h / (hv / hk)) the library walks the sequence's tokens in order against
+ * that sequence's own fp32 state S (a dv x dk matrix, element S[j][i]):
+ *
+ *     a_t = exp(g_t)
+ *     S_t = a_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t
+ *
+ * which is the gated delta rule (Yang, Kautz, Hatamizadeh, "Gated Delta
+ * Networks: Improving Mamba2 with Delta Rule", ICLR 2025).  Running this
+ * token-by-token recurrence for prefill, for decode and for a trainer's
+ * recompute alike, with one sequence's state touched by nothing but that
+ * sequence's tokens and no reduction across sequences, is what the page
+ * "Defending Against the Training-Inference Numeric Mismatch in RL (Especially
+ * Linear Attention)" (section 3.2, operator level) relies on to make the forward
+ * batch invariant.  No 1/sqrt(dk) scale is applied to q.
+ *
+ * Bitwise contract.  Every output element and every state element is produced
+ * by a fixed sequence of fp32 operations that depends only on that sequence's
+ * own inputs: never on the batch size, the position of the sequence in the
+ * batch, the other sequences, the launch shape, or whether a token arrives by
+ * gdn_fwd_varlen or by gdn_decode_step.  Splitting a sequence into several
+ * calls and passing hT of one call as h0 of the next gives the same bits as one
+ * call (the state is carried in fp32 without rounding).
+ *
+ * Layouts (all row-major, contiguous, token-major; T = total tokens):
+ *     q, k        [T][hk][dk]     io dtype
+ *     v, out      [T][hv][dv]     io dtype
+ *     g, beta     [T][hv]         fp32 (g is the log of the decay, beta the write strength)
+ *     h0, hT      [N][hv][dv][dk] fp32
+ *     state pool  [P][hv][dv][dk] fp32 (decode)
+ *     cu_seqlens  [N+1]           int32, device memory
+ *     state_idx   [B]             int32, device memory
+ * All array pointers are device pointers (hipMalloc'd or equivalent), aligned to
+ * 16 bytes.  The caller owns every buffer; the library allocates nothing, keeps
+ * no pointer after a call returns and has no global state, so it is reentrant.
+ * Work is enqueued on `stream` (a hipStream_t; NULL means the null stream) and
+ * the call returns without synchronising the host.
+ *
+ * Errors.  Argument problems that the host can see are reported before anything
+ * is enqueued; there is no fallback path and no partial mode.  Device-resident
+ * index arrays (cu_seqlens, state_idx) are not read by the host: the kernels
+ * clamp what they read so that a malformed array cannot make them access memory
+ * outside the buffers described by `gdn_dims`, but the results for such input
+ * are unspecified.
+ */
+#ifndef GDN_MI355X_H
+#define GDN_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,       /* negative or inconsistent sizes, hv % hk != 0, dv % 16 != 0 */
+    GDN_ERR_DTYPE = 3,       /* io_dtype is not GDN_F32 or GDN_BF16 */
+    GDN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    GDN_ERR_ALIAS = 5,       /* an output overlaps an input, or h0/hT partially overlap */
+    GDN_ERR_UNSUPPORTED = 6, /* dk not in {16, 32, 64, 128}, or a launch-plan request that does not fit */
+    GDN_ERR_HIP = 7          /* the HIP runtime refused the launch */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_F32 = 0,   /* q, k, v, out are fp32 */
+    GDN_BF16 = 1   /* q, k, v, out are bf16; out is rounded to nearest even */
+} gdn_dtype;
+
+typedef struct gdn_dims {
+    int32_t n_seqs;        /* N sequences (prefill) or B decode rows; 0 is a no-op */
+    int32_t hk;            /* query/key heads */
+    int32_t hv;            /* value heads, a multiple of hk */
+    int32_t dk;            /* key/query head dim: 16, 32, 64 or 128 */
+    int32_t dv;            /* value head dim: a positive multiple of 16 */
+    int32_t io_dtype;      /* gdn_dtype of q, k, v, out */
+    int64_t total_tokens;  /* T: rows of q/k/v/g/beta/out; decode requires T == n_seqs */
+    int32_t pool_size;     /* P: state pool entries (decode only; ignored by prefill) */
+    int32_t plan_rows;     /* launch shape: state rows per lane quad, 0 = automatic, else 1, 2 or 4 */
+    int32_t plan_waves;    /* launch shape: waves per workgroup, 0 = automatic, else 1, 2, 4 or 8 */
+    int32_t reserved;      /* must be 0 */
+} gdn_dims;
+/* plan_rows / plan_waves choose how state rows are spread over lanes and
+ * workgroups.  They never change a single bit of any result; they exist so that
+ * this can be tested and so that a caller can tune the launch. */
+
+/*
+ * Varlen prefill: run every sequence of a packed batch through the recurrence.
+ *
+ *   q, k, v, g, beta : inputs (layouts above); may be NULL only when T == 0
+ *   h0               : initial states [N][hv][dv][dk], or NULL for the zero state
+ *   cu_seqlens       : [N+1] device int32, cu[0] = 0, non-decreasing, cu[N] = T
+ *   out              : [T][hv][dv] outputs o_t (written for every token)
+ *   hT               : final states [N][hv][dv][dk], or NULL to skip writing them.
+ *                      hT == h0 (the same pointer) updates the states in place;
+ *                      any other overlap of the two is GDN_ERR_ALIAS.
+ * A sequence of length 0 writes no output and hands h0 (or zeros) to hT.
+ */
+gdn_status gdn_fwd_varlen(const gdn_dims *dims,
+                          const void *q, const void *k, const void *v,
+                          const float *g, const float *beta,
+                          const float *h0, const int32_t *cu_seqlens,
+                          void *out, float *hT, void *stream);
+
+/*
+ * Decode step: one token for each of B sequences, against states held in a pool
+ * and updated in place.
+ *
+ *   q, k, v, g, beta : this step's token of each sequence; q, k [B][hk][dk],
+ *                      v [B][hv][dv], g, beta [B][hv]   (dims->total_tokens == B)
+ *   state_pool       : [P][hv][dv][dk] fp32, read and written in place
+ *   state_idx        : [B] device int32: row b uses pool entry state_idx[b];
+ *                      NULL means entry b.  Entries must be distinct.  An entry
+ *                      outside [0, P) marks a padding row: its output is written
+ *                      as zeros and no state is read or written.
+ *   out              : [B][hv][dv] outputs
+ * The arithmetic is the one of gdn_fwd_varlen for a single token, bit for bit.
+ */
+gdn_status gdn_decode_step(const gdn_dims *dims,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           float *state_pool, const int32_t *state_idx,
+                           void *out, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *gdn_status_string(gdn_status status);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t gdn_abi_version(void);
+
+#define GDN_ABI_VERSION 100
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_MI355X_H */

@@ -1,0 +1,231 @@
+// gdn_api.hip -- the C ABI (include/gdn.h): argument checks, launch planning and
+// dispatch to the per-dk kernels.  Everything here runs on the host before any work
+// is enqueued; nothing here reads device memory, allocates or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+#include "gdn_internal.hpp"
+
+namespace gdn {
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void *p, uint64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, uintptr_t to) { return (reinterpret_cast<uintptr_t>(p) % to) == 0; }
+
+bool dk_supported(int dk) { return dk == 16 || dk == 32 || dk == 64 || dk == 128; }
+
+bool plan_available(int dk, int io, Plan plan) {
+    switch (dk) {
+        case 16: return plan_available_dk16(io, plan);
+        case 32: return plan_available_dk32(io, plan);
+        case 64: return plan_available_dk64(io, plan);
+        case 128: return plan_available_dk128(io, plan);
+        default: return false;
+    }
+}
+
+bool plan_fits(int dk, int dv, int io, Plan plan) {
+    return plan_available(dk, io, plan) && dv % (plan.waves * 16 * plan.rows) == 0;
+}
+
+// Rows per quad: the largest that still gives at least two waves per SIMD of the
+// chip (256 CUs x 4 SIMDs) when the problem is that large; the launch shape never
+// changes results, only how the rows are spread.
+Plan auto_plan(int dk, int dv, int io, int64_t units) {
+    const int64_t rows_total = units * dv;
+    const int cand_rows[3] = {4, 2, 1};
+    const int cand_waves[3] = {4, 2, 1};
+    int rows = 1;
+    for (int r : cand_rows) {
+        bool any = false;
+        for (int w : cand_waves) any = any || plan_fits(dk, dv, io, Plan{r, w});
+        if (any && rows_total / (16 * r) >= 2048) {
+            rows = r;
+            break;
+        }
+    }
+    for (int w : cand_waves)
+        if (plan_fits(dk, dv, io, Plan{rows, w})) return Plan{rows, w};
+    return Plan{1, 1};
+}
+
+gdn_status check_common(const gdn_dims *d) {
+    if (!d) return GDN_ERR_NULL;
+    if (d->reserved != 0) return GDN_ERR_SHAPE;
+    if (d->n_seqs < 0 || d->total_tokens < 0 || d->hk <= 0 || d->hv <= 0 || d->dk <= 0 || d->dv <= 0)
+        return GDN_ERR_SHAPE;
+    if (d->hv % d->hk != 0 || d->dv % 16 != 0) return GDN_ERR_SHAPE;
+    if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (!dk_supported(d->dk)) return GDN_ERR_UNSUPPORTED;
+    if (d->hv > 65535 || d->n_seqs > 65535) return GDN_ERR_SHAPE;  // grid y / z limits
+    return GDN_OK;
+}
+
+gdn_status resolve_plan(const gdn_dims *d, int64_t units, Plan *plan) {
+    if (d->plan_rows == 0 && d->plan_waves == 0) {
+        *plan = auto_plan(d->dk, d->dv, d->io_dtype, units);
+        return GDN_OK;
+    }
+    Plan p{d->plan_rows, d->plan_waves};
+    if (p.rows == 0 || p.waves == 0) {  // one of the two given: fill in the other
+        Plan a = auto_plan(d->dk, d->dv, d->io_dtype, units);
+        if (p.rows == 0) p.rows = a.rows;
+        if (p.waves == 0) {
+            p.waves = 0;
+            for (int w : {4, 2, 1})
+                if (plan_fits(d->dk, d->dv, d->io_dtype, Plan{p.rows, w})) {
+                    p.waves = w;
+                    break;
+                }
+            if (p.waves == 0) return GDN_ERR_UNSUPPORTED;
+        }
+    }
+    if (!plan_fits(d->dk, d->dv, d->io_dtype, p)) return GDN_ERR_UNSUPPORTED;
+    *plan = p;
+    return GDN_OK;
+}
+
+hipError_t dispatch_prefill(int dk, const PrefillParams &p, int io, Plan plan, hipStream_t s) {
+    switch (dk) {
+        case 16: return launch_prefill_dk16(p, io, plan, s);
+        case 32: return launch_prefill_dk32(p, io, plan, s);
+        case 64: return launch_prefill_dk64(p, io, plan, s);
+        default: return launch_prefill_dk128(p, io, plan, s);
+    }
+}
+
+hipError_t dispatch_decode(int dk, const DecodeParams &p, int io, Plan plan, hipStream_t s) {
+    switch (dk) {
+        case 16: return launch_decode_dk16(p, io, plan, s);
+        case 32: return launch_decode_dk32(p, io, plan, s);
+        case 64: return launch_decode_dk64(p, io, plan, s);
+        default: return launch_decode_dk128(p, io, plan, s);
+    }
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_fwd_varlen(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *h0, const int32_t *cu_seqlens, void *out, float *hT,
+                          void *stream) {
+    using namespace gdn;
+    gdn_status st = check_common(dims);
+    if (st != GDN_OK) return st;
+    const gdn_dims &d = *dims;
+    const int64_t T = d.total_tokens, N = d.n_seqs;
+    if (N == 0) return T == 0 ? GDN_OK : GDN_ERR_SHAPE;
+    if (!cu_seqlens) return GDN_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL;
+
+    const uint64_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
+    const uint64_t qk_bytes = (uint64_t)T * d.hk * d.dk * esz;
+    const uint64_t vo_bytes = (uint64_t)T * d.hv * d.dv * esz;
+    const uint64_t gb_bytes = (uint64_t)T * d.hv * 4;
+    const uint64_t s_bytes = (uint64_t)N * d.hv * d.dv * d.dk * 4;
+
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(h0, 16) ||
+        !aligned(hT, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(cu_seqlens, 4))
+        return GDN_ERR_ALIGN;
+
+    const Range rq = range_of(q, qk_bytes), rk = range_of(k, qk_bytes), rv = range_of(v, vo_bytes);
+    const Range rg = range_of(g, gb_bytes), rb = range_of(beta, gb_bytes);
+    const Range rh0 = range_of(h0, h0 ? s_bytes : 0), rhT = range_of(hT, hT ? s_bytes : 0);
+    const Range rcu = range_of(cu_seqlens, (uint64_t)(N + 1) * 4), ro = range_of(out, vo_bytes);
+    for (Range in : {rq, rk, rv, rg, rb, rh0, rcu, rhT})
+        if (overlap(ro, in)) return GDN_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, rg, rb, rcu})
+        if (overlap(rhT, in)) return GDN_ERR_ALIAS;
+    if (h0 && hT && h0 != hT && overlap(rh0, rhT)) return GDN_ERR_ALIAS;
+
+    Plan plan;
+    st = resolve_plan(dims, N * d.hv, &plan);
+    if (st != GDN_OK) return st;
+
+    PrefillParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0;
+    p.cu_seqlens = cu_seqlens; p.out = out; p.hT = hT;
+    p.total_tokens = T; p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dv = d.dv;
+    const hipError_t e = dispatch_prefill(d.dk, p, d.io_dtype, plan, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state_pool, const int32_t *state_idx, void *out,
+                           void *stream) {
+    using namespace gdn;
+    gdn_status st = check_common(dims);
+    if (st != GDN_OK) return st;
+    const gdn_dims &d = *dims;
+    const int64_t B = d.n_seqs;
+    if (d.total_tokens != B) return GDN_ERR_SHAPE;
+    if (d.pool_size < 0) return GDN_ERR_SHAPE;
+    if (B == 0) return GDN_OK;
+    if (!q || !k || !v || !g || !beta || !out || !state_pool) return GDN_ERR_NULL;
+    if (d.pool_size == 0 && !state_idx) return GDN_ERR_SHAPE;
+    if (!state_idx && d.pool_size < B) return GDN_ERR_SHAPE;  // identity map needs B entries
+
+    const uint64_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
+    const uint64_t qk_bytes = (uint64_t)B * d.hk * d.dk * esz;
+    const uint64_t vo_bytes = (uint64_t)B * d.hv * d.dv * esz;
+    const uint64_t gb_bytes = (uint64_t)B * d.hv * 4;
+    const uint64_t pool_bytes = (uint64_t)d.pool_size * d.hv * d.dv * d.dk * 4;
+
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(state_pool, 16) ||
+        !aligned(g, 4) || !aligned(beta, 4) || !aligned(state_idx, 4))
+        return GDN_ERR_ALIGN;
+
+    const Range rq = range_of(q, qk_bytes), rk = range_of(k, qk_bytes), rv = range_of(v, vo_bytes);
+    const Range rg = range_of(g, gb_bytes), rb = range_of(beta, gb_bytes);
+    const Range rp = range_of(state_pool, pool_bytes), ri = range_of(state_idx, state_idx ? (uint64_t)B * 4 : 0);
+    const Range ro = range_of(out, vo_bytes);
+    for (Range in : {rq, rk, rv, rg, rb, rp, ri})
+        if (overlap(ro, in)) return GDN_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, rg, rb, ri})
+        if (overlap(rp, in)) return GDN_ERR_ALIAS;
+
+    Plan plan;
+    st = resolve_plan(dims, B * d.hv, &plan);
+    if (st != GDN_OK) return st;
+
+    DecodeParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.pool = state_pool; p.state_idx = state_idx; p.out = out;
+    p.batch = (int32_t)B; p.hk = d.hk; p.hv = d.hv; p.dv = d.dv; p.pool_size = d.pool_size;
+    const hipError_t e = dispatch_decode(d.dk, p, d.io_dtype, plan, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+const char *gdn_status_string(gdn_status status) {
+    switch (status) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: sizes are negative or inconsistent";
+        case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: io_dtype must be GDN_F32 or GDN_BF16";
+        case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: a pointer is not aligned (16 bytes for arrays, 4 for g/beta/indices)";
+        case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output overlaps an input";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: dk or launch shape not supported";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime refused the launch";
+    }
+    return "unknown gdn_status";
+}
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,163 @@
+"""Thin Python binding of the C ABI in include/gdn.h.
+
+Argument marshalling only: every step of the recurrence runs in the HIP kernels of
+``libgdn.so``.  torch supplies device memory and the stream.  If the library has
+not been built, every call raises; there is no CPU or eager fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+STATUS = {
+    0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
+    5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_HIP",
+}
+EXPORTS = ("gdn_fwd_varlen", "gdn_decode_step", "gdn_status_string", "gdn_abi_version")
+
+
+class GdnDims(ctypes.Structure):
+    """Mirror of ``gdn_dims``."""
+    _fields_ = [
+        ("n_seqs", ctypes.c_int32), ("hk", ctypes.c_int32), ("hv", ctypes.c_int32),
+        ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int64), ("pool_size", ctypes.c_int32),
+        ("plan_rows", ctypes.c_int32), ("plan_waves", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__("%s (%d)" % (message, code))
+        self.code = code
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIBRARY):
+    """Load libgdn.so (once).  Raises if it is missing: build it first."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError("libgdn.so is not built (%s); run __graft_entry__.build() first" % path)
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        lib.gdn_fwd_varlen.restype = ctypes.c_int
+        lib.gdn_fwd_varlen.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdn_decode_step.restype = ctypes.c_int
+        lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdn_status_string.restype = ctypes.c_char_p
+        lib.gdn_status_string.argtypes = [ctypes.c_int]
+        lib.gdn_abi_version.restype = ctypes.c_int32
+        lib.gdn_abi_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().gdn_status_string(int(code)).decode()
+
+
+def _check(code: int):
+    if code != 0:
+        raise GdnError(code, status_string(code))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream or None
+    return int(stream.cuda_stream) or None
+
+
+def _io_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError("q/k/v/out must be bf16 or fp32, got %s" % t.dtype)
+
+
+def _need(t, name, dtype=None, cuda=True):
+    import torch
+    if t is None:
+        return
+    if cuda and not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def make_dims(q, v, n_seqs: int, total_tokens: int, pool_size: int = 0, plan: Tuple[int, int] = (0, 0)) -> GdnDims:
+    return GdnDims(n_seqs=int(n_seqs), hk=int(q.shape[1]), hv=int(v.shape[1]), dk=int(q.shape[2]),
+                   dv=int(v.shape[2]), io_dtype=_io_code(q), total_tokens=int(total_tokens),
+                   pool_size=int(pool_size), plan_rows=int(plan[0]), plan_waves=int(plan[1]), reserved=0)
+
+
+def gdn_fwd_varlen(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, stream=None, plan=(0, 0),
+                   want_state: bool = True):
+    """Varlen prefill (see include/gdn.h).  Tensors on the GPU, contiguous:
+    q, k [T, Hk, dk]; v [T, Hv, dv]; g, beta [T, Hv] fp32; h0 [N, Hv, dv, dk] fp32
+    or None; cu_seqlens [N+1] int32.  ``out`` / ``hT`` are allocated when None
+    (hT only if ``want_state``).  Returns (out, hT)."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    _need(h0, "h0", torch.float32)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    T = int(q.shape[0])
+    N = int(cu_seqlens.numel()) - 1
+    if out is None:
+        out = torch.empty((T, v.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+    if hT is None and want_state:
+        hT = torch.empty((N, v.shape[1], v.shape[2], q.shape[2]), dtype=torch.float32, device=q.device)
+    _need(out, "out", q.dtype)
+    _need(hT, "hT", torch.float32)
+    dims = make_dims(q, v, N, T, plan=plan)
+    _check(lib.gdn_fwd_varlen(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                              _ptr(cu_seqlens), _ptr(out), _ptr(hT), _stream_handle(stream)))
+    return out, hT
+
+
+def gdn_decode_step(q, k, v, g, beta, state_pool, state_idx=None, out=None, stream=None, plan=(0, 0)):
+    """One decode token per sequence (see include/gdn.h).  q, k [B, Hk, dk];
+    v [B, Hv, dv]; g, beta [B, Hv]; state_pool [P, Hv, dv, dk] fp32 updated in
+    place; state_idx [B] int32 or None (identity).  Returns out [B, Hv, dv]."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    _need(state_pool, "state_pool", torch.float32)
+    _need(state_idx, "state_idx", torch.int32)
+    B = int(q.shape[0])
+    if out is None:
+        out = torch.empty((B, v.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+    _need(out, "out", q.dtype)
+    dims = make_dims(q, v, B, B, pool_size=int(state_pool.shape[0]), plan=plan)
+    _check(lib.gdn_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(state_pool), _ptr(state_idx), _ptr(out), _stream_handle(stream)))
+    return out

@@ -1,0 +1,152 @@
+"""The C-ABI library on the host: it loads, exports what include/gdn.h declares,
+its struct layout matches, and every argument error is reported before any work
+is enqueued (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from invariant_linear_attention_amd import gdn
+    if not os.path.exists(gdn.LIBRARY):
+        pytest.fail("libgdn.so is not built; run __graft_entry__.build()")
+    return gdn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"gdn_fwd_varlen", "gdn_decode_step", "gdn_status_string", "gdn_abi_version"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version(lib):
+    text = open(HEADER).read()
+    want = int(re.search(r"#define GDN_ABI_VERSION (\d+)", text).group(1))
+    assert lib.gdn_abi_version() == want
+
+
+def test_status_strings(lib):
+    from invariant_linear_attention_amd import gdn
+    for code, name in gdn.STATUS.items():
+        assert gdn.status_string(code).startswith(name)
+
+
+def test_struct_layout_matches_c(tmp_path):
+    from invariant_linear_attention_amd.gdn import GdnDims
+    src = tmp_path / "layout.c"
+    fields = [f[0] for f in GdnDims._fields_]
+    body = "".join('printf("%s %%zu\\n", offsetof(gdn_dims, %s));' % (f, f) for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "gdn.h"\n'
+                   'int main(void){printf("size %%zu\\n", sizeof(gdn_dims));%s return 0;}\n' % body)
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.check_output([str(exe)]).decode().splitlines())
+    assert int(out["size"]) == ctypes.sizeof(GdnDims)
+    for f in fields:
+        assert int(out[f]) == getattr(GdnDims, f).offset, f
+
+
+# ------------------------------------------------------ argument errors (host)
+
+def _dims(**kw):
+    from invariant_linear_attention_amd.gdn import GdnDims
+    d = dict(n_seqs=2, hk=2, hv=4, dk=128, dv=128, io_dtype=1, total_tokens=10, pool_size=0,
+             plan_rows=0, plan_waves=0, reserved=0)
+    d.update(kw)
+    return GdnDims(**d)
+
+
+# Fake, well-separated, aligned addresses: the checks below fail before any launch.
+BASE = 0x7F0000000000
+MB = 1 << 24
+P = {name: BASE + i * MB for i, name in enumerate(["q", "k", "v", "g", "b", "h0", "cu", "out", "hT"])}
+
+
+def call_fwd(lib, dims, **over):
+    a = dict(P)
+    a.update(over)
+    return lib.gdn_fwd_varlen(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], a["v"], a["g"],
+                              a["b"], a["h0"], a["cu"], a["out"], a["hT"], None)
+
+
+def call_dec(lib, dims, **over):
+    a = dict(P)
+    a.update(over)
+    return lib.gdn_decode_step(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], a["v"], a["g"],
+                               a["b"], a.get("pool", a["h0"]), a.get("idx", a["cu"]), a["out"], None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(dims=None), 1),
+    (dict(reserved=1), 2),
+    (dict(n_seqs=-1), 2),
+    (dict(total_tokens=-5), 2),
+    (dict(hk=3), 2),
+    (dict(dv=24), 2),
+    (dict(io_dtype=7), 3),
+    (dict(dk=48), 6),
+    (dict(dk=256), 6),
+    (dict(plan_rows=3, plan_waves=1), 6),
+    (dict(plan_rows=2, plan_waves=8), 6),
+    (dict(plan_rows=4, plan_waves=4), 6),
+    (dict(n_seqs=0, total_tokens=3), 2),
+])
+def test_fwd_rejects_bad_dims(lib, case, code):
+    if case.get("dims", 0) is None:
+        assert call_fwd(lib, None) == code
+    else:
+        assert call_fwd(lib, _dims(**case)) == code
+
+
+def test_fwd_zero_sequences_is_a_noop(lib):
+    assert call_fwd(lib, _dims(n_seqs=0, total_tokens=0)) == 0
+
+
+@pytest.mark.parametrize("ptr", ["q", "k", "v", "g", "b", "cu", "out"])
+def test_fwd_rejects_null(lib, ptr):
+    assert call_fwd(lib, _dims(), **{ptr: None}) == 1
+
+
+@pytest.mark.parametrize("ptr,off", [("q", 8), ("v", 4), ("out", 2), ("h0", 8), ("hT", 12), ("g", 2), ("cu", 1)])
+def test_fwd_rejects_misaligned(lib, ptr, off):
+    assert call_fwd(lib, _dims(), **{ptr: P[ptr] + off}) == 4
+
+
+@pytest.mark.parametrize("over", [
+    dict(out=P["q"]), dict(out=P["v"] + 256), dict(out=P["hT"]), dict(out=P["h0"]),
+    dict(hT=P["k"]), dict(hT=P["h0"] + 4096),
+])
+def test_fwd_rejects_aliasing(lib, over):
+    assert call_fwd(lib, _dims(), **over) == 5
+
+
+@pytest.mark.parametrize("case,over,code", [
+    (dict(total_tokens=3), {}, 2),              # decode needs T == B
+    (dict(pool_size=-1, total_tokens=2), {}, 2),
+    (dict(total_tokens=2, pool_size=4), dict(pool=None), 1),
+    (dict(total_tokens=2, pool_size=4), dict(q=None), 1),
+    (dict(total_tokens=2, pool_size=1), dict(idx=None), 2),  # identity map needs B entries
+    (dict(total_tokens=2, pool_size=4), dict(out=P["q"]), 5),
+    (dict(total_tokens=2, pool_size=4), dict(pool=P["v"]), 5),
+    (dict(total_tokens=2, pool_size=4), dict(idx=P["cu"] + 2), 4),
+    (dict(total_tokens=2, pool_size=4, dk=40), {}, 6),
+])
+def test_decode_rejects(lib, case, over, code):
+    assert call_dec(lib, _dims(**case), **over) == code
+
+
+def test_decode_zero_batch_is_a_noop(lib):
+    assert call_dec(lib, _dims(n_seqs=0, total_tokens=0, pool_size=4)) == 0
