@@ -81,13 +81,18 @@ typedef struct gdn_dims {
     int32_t io_dtype;      /* gdn_dtype of q, k, v, out */
     int64_t total_tokens;  /* T: rows of q/k/v/g/beta/out; decode requires T == n_seqs */
     int32_t pool_size;     /* P: state pool entries (decode only; ignored by prefill) */
-    int32_t plan_rows;     /* launch shape: state rows per lane quad, 0 = automatic, else 1, 2 or 4 */
-    int32_t plan_waves;    /* launch shape: waves per workgroup, 0 = automatic, else 1, 2, 4 or 8 */
+    int32_t plan_lanes;    /* launch shape: lanes holding one state row, 0 = automatic, else 4, 8 or 16 */
+    int32_t plan_rows;     /* launch shape: state rows per lane, 0 = automatic, else 1, 2 or 4 */
+    int32_t plan_waves;    /* launch shape: waves per workgroup, 0 = automatic, else 1, 2 or 4 */
     int32_t reserved;      /* must be 0 */
 } gdn_dims;
-/* plan_rows / plan_waves choose how state rows are spread over lanes and
- * workgroups.  They never change a single bit of any result; they exist so that
- * this can be tested and so that a caller can tune the launch. */
+/* plan_lanes / plan_rows / plan_waves choose how state rows are spread over
+ * lanes, waves and workgroups.  They never change a single bit of any result
+ * (every row's arithmetic is fixed, see gdn_fwd_varlen); they exist so that this
+ * can be tested and so that a caller can tune the launch.  A field left at 0 is
+ * chosen by the library; a combination that is not compiled, or whose rows per
+ * workgroup (64 / lanes * rows * waves) do not divide dv, is GDN_ERR_UNSUPPORTED.
+ * gdn_decode_step uses plan_rows / plan_waves and always 4 lanes per row. */
 
 /*
  * Varlen prefill: run every sequence of a packed batch through the recurrence.
@@ -133,7 +138,7 @@ const char *gdn_status_string(gdn_status status);
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 100
+#define GDN_ABI_VERSION 101
 
 #ifdef __cplusplus
 }

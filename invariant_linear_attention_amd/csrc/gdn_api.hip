@@ -28,39 +28,51 @@ bool aligned(const void *p, uintptr_t to) { return (reinterpret_cast<uintptr_t>(
 
 bool dk_supported(int dk) { return dk == 16 || dk == 32 || dk == 64 || dk == 128; }
 
-bool plan_available(int dk, int io, Plan plan) {
+bool plan_available(int dk, bool decode, int io, Plan plan) {
     switch (dk) {
-        case 16: return plan_available_dk16(io, plan);
-        case 32: return plan_available_dk32(io, plan);
-        case 64: return plan_available_dk64(io, plan);
-        case 128: return plan_available_dk128(io, plan);
+        case 16: return plan_available_dk16(decode, io, plan);
+        case 32: return plan_available_dk32(decode, io, plan);
+        case 64: return plan_available_dk64(decode, io, plan);
+        case 128: return plan_available_dk128(decode, io, plan);
         default: return false;
     }
 }
 
-bool plan_fits(int dk, int dv, int io, Plan plan) {
-    return plan_available(dk, io, plan) && dv % (plan.waves * 16 * plan.rows) == 0;
+int rows_per_group(Plan plan) { return plan.waves * (64 / plan.lanes) * plan.rows; }
+
+bool plan_fits(int dk, int dv, bool decode, int io, Plan plan) {
+    return plan.lanes > 0 && plan.rows > 0 && plan.waves > 0 && plan_available(dk, decode, io, plan) &&
+           dv % rows_per_group(plan) == 0;
 }
 
-// Rows per quad: the largest that still gives at least two waves per SIMD of the
-// chip (256 CUs x 4 SIMDs) when the problem is that large; the launch shape never
-// changes results, only how the rows are spread.
-Plan auto_plan(int dk, int dv, int io, int64_t units) {
+// Automatic launch shape.  Rows are independent, so this only trades per-wave
+// efficiency against parallelism.  Measured on MI355X (dk = dv = 128, bf16): 16
+// lanes x 2 rows per lane is fastest when the batch has rows to spare, then 8
+// lanes x 1 row; when rows are scarce (one long sequence) 16 lanes x 1 row puts
+// the most waves on the chip.  Other head dims use 4 lanes per row.
+constexpr int64_t kWavesWanted = 4096;  // four per SIMD: lets longest-first ordering balance the tail
+
+Plan auto_plan(int dk, int dv, bool decode, int io, int64_t units) {
     const int64_t rows_total = units * dv;
-    const int cand_rows[3] = {4, 2, 1};
-    const int cand_waves[3] = {4, 2, 1};
-    int rows = 1;
-    for (int r : cand_rows) {
-        bool any = false;
-        for (int w : cand_waves) any = any || plan_fits(dk, dv, io, Plan{r, w});
-        if (any && rows_total / (16 * r) >= 2048) {
-            rows = r;
-            break;
+    if (decode) {
+        for (Plan pl : {Plan{4, 2, 4}, Plan{4, 2, 2}, Plan{4, 1, 4}, Plan{4, 1, 2}, Plan{4, 1, 1}})
+            if (plan_fits(dk, dv, true, io, pl)) return pl;
+        return Plan{4, 1, 1};
+    }
+    const Plan prefer[] = {Plan{16, 2, 4}, Plan{8, 1, 4}, Plan{16, 1, 4}, Plan{8, 1, 2}, Plan{4, 1, 4},
+                           Plan{4, 1, 2}, Plan{4, 1, 1}, Plan{16, 1, 2}, Plan{8, 1, 1}};
+    Plan best{0, 0, 0};
+    int64_t best_waves = -1;
+    for (Plan pl : prefer) {
+        if (!plan_fits(dk, dv, false, io, pl)) continue;
+        const int64_t waves = rows_total * pl.lanes / (64 * pl.rows);
+        if (waves >= kWavesWanted) return pl;
+        if (waves > best_waves) {  // otherwise keep the shape with the most waves
+            best = pl;
+            best_waves = waves;
         }
     }
-    for (int w : cand_waves)
-        if (plan_fits(dk, dv, io, Plan{rows, w})) return Plan{rows, w};
-    return Plan{1, 1};
+    return best_waves >= 0 ? best : Plan{4, 1, 1};
 }
 
 gdn_status check_common(const gdn_dims *d) {
@@ -75,26 +87,20 @@ gdn_status check_common(const gdn_dims *d) {
     return GDN_OK;
 }
 
-gdn_status resolve_plan(const gdn_dims *d, int64_t units, Plan *plan) {
-    if (d->plan_rows == 0 && d->plan_waves == 0) {
-        *plan = auto_plan(d->dk, d->dv, d->io_dtype, units);
-        return GDN_OK;
+gdn_status resolve_plan(const gdn_dims *d, bool decode, int64_t units, Plan *plan) {
+    const Plan a = auto_plan(d->dk, d->dv, decode, d->io_dtype, units);
+    Plan p{d->plan_lanes ? d->plan_lanes : (decode ? 4 : a.lanes), d->plan_rows ? d->plan_rows : a.rows,
+           d->plan_waves};
+    if (d->plan_rows == 0 && !plan_fits(d->dk, d->dv, decode, d->io_dtype, Plan{p.lanes, p.rows, 1})) p.rows = 1;
+    if (p.waves == 0) {
+        for (int w : {4, 2, 1})
+            if (plan_fits(d->dk, d->dv, decode, d->io_dtype, Plan{p.lanes, p.rows, w})) {
+                p.waves = w;
+                break;
+            }
+        if (p.waves == 0) return GDN_ERR_UNSUPPORTED;
     }
-    Plan p{d->plan_rows, d->plan_waves};
-    if (p.rows == 0 || p.waves == 0) {  // one of the two given: fill in the other
-        Plan a = auto_plan(d->dk, d->dv, d->io_dtype, units);
-        if (p.rows == 0) p.rows = a.rows;
-        if (p.waves == 0) {
-            p.waves = 0;
-            for (int w : {4, 2, 1})
-                if (plan_fits(d->dk, d->dv, d->io_dtype, Plan{p.rows, w})) {
-                    p.waves = w;
-                    break;
-                }
-            if (p.waves == 0) return GDN_ERR_UNSUPPORTED;
-        }
-    }
-    if (!plan_fits(d->dk, d->dv, d->io_dtype, p)) return GDN_ERR_UNSUPPORTED;
+    if (!plan_fits(d->dk, d->dv, decode, d->io_dtype, p)) return GDN_ERR_UNSUPPORTED;
     *plan = p;
     return GDN_OK;
 }
@@ -155,13 +161,15 @@ gdn_status gdn_fwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
     if (h0 && hT && h0 != hT && overlap(rh0, rhT)) return GDN_ERR_ALIAS;
 
     Plan plan;
-    st = resolve_plan(dims, N * d.hv, &plan);
+    st = resolve_plan(dims, false, N * d.hv, &plan);
     if (st != GDN_OK) return st;
 
     PrefillParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0;
     p.cu_seqlens = cu_seqlens; p.out = out; p.hT = hT;
     p.total_tokens = T; p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dv = d.dv;
+    // Longest-first ordering pays off when there are a few sequences of some length.
+    p.rank_by_length = (N > 1 && N <= kMaxRankedSeqs && T >= 32 * N) ? 1 : 0;
     const hipError_t e = dispatch_prefill(d.dk, p, d.io_dtype, plan, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -201,7 +209,7 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k, c
         if (overlap(rp, in)) return GDN_ERR_ALIAS;
 
     Plan plan;
-    st = resolve_plan(dims, B * d.hv, &plan);
+    st = resolve_plan(dims, true, B * d.hv, &plan);
     if (st != GDN_OK) return st;
 
     DecodeParams p{};

@@ -14,21 +14,39 @@
 namespace gdn {
 namespace {
 
-// Launch shapes compiled for this dk.  (rows per quad, waves per workgroup)
-constexpr bool shape_compiled(int rows, int waves) {
+// Prefill launch shapes compiled for this dk: (lanes, rows per lane, waves).
+// Lanes above 4 need whole leaves per lane: 8 lanes for dk >= 64, 16 for dk = 128.
+constexpr bool prefill_compiled(int lanes, int rows, int waves) {
     if (waves != 1 && waves != 2 && waves != 4) return false;
-    if (rows == 1 || rows == 2) return true;
-    return GDN_DK == 128 && rows == 4 && waves <= 2;
+    if (lanes == 4) return rows == 1 || rows == 2 || (GDN_DK == 128 && rows == 4 && waves <= 2);
+    if (lanes == 8) return GDN_DK >= 64 && (rows == 1 || rows == 2);
+    // (16, 1, 1) would own 4 rows per workgroup, less than one 16-byte bf16 vector.
+    if (lanes == 16) return GDN_DK == 128 && (rows == 2 || (rows == 1 && waves >= 2));
+    return false;
+}
+
+constexpr bool decode_compiled(int lanes, int rows, int waves) {
+    if (lanes != 4 || (waves != 1 && waves != 2 && waves != 4)) return false;
+    return rows == 1 || rows == 2 || (GDN_DK == 128 && rows == 4 && waves <= 2);
 }
 
 template <class IO>
 hipError_t prefill_io(const PrefillParams &p, Plan plan, hipStream_t s) {
-#define GDN_CASE(R_, NW_) \
-    if (plan.rows == R_ && plan.waves == NW_) return launch_prefill_t<GDN_DK, IO, R_, NW_>(p, s);
-    GDN_CASE(1, 1) GDN_CASE(1, 2) GDN_CASE(1, 4)
-    GDN_CASE(2, 1) GDN_CASE(2, 2) GDN_CASE(2, 4)
+#define GDN_CASE(L_, R_, NW_)                                                  \
+    if (plan.lanes == L_ && plan.rows == R_ && plan.waves == NW_)              \
+        return launch_prefill_t<GDN_DK, IO, L_, R_, NW_>(p, s);
+    GDN_CASE(4, 1, 1) GDN_CASE(4, 1, 2) GDN_CASE(4, 1, 4)
+    GDN_CASE(4, 2, 1) GDN_CASE(4, 2, 2) GDN_CASE(4, 2, 4)
 #if GDN_DK == 128
-    GDN_CASE(4, 1) GDN_CASE(4, 2)
+    GDN_CASE(4, 4, 1) GDN_CASE(4, 4, 2)
+#endif
+#if GDN_DK >= 64
+    GDN_CASE(8, 1, 1) GDN_CASE(8, 1, 2) GDN_CASE(8, 1, 4)
+    GDN_CASE(8, 2, 1) GDN_CASE(8, 2, 2) GDN_CASE(8, 2, 4)
+#endif
+#if GDN_DK == 128
+    GDN_CASE(16, 1, 2) GDN_CASE(16, 1, 4)
+    GDN_CASE(16, 2, 1) GDN_CASE(16, 2, 2) GDN_CASE(16, 2, 4)
 #endif
 #undef GDN_CASE
     return hipErrorInvalidValue;
@@ -37,7 +55,7 @@ hipError_t prefill_io(const PrefillParams &p, Plan plan, hipStream_t s) {
 template <class IO>
 hipError_t decode_io(const DecodeParams &p, Plan plan, hipStream_t s) {
 #define GDN_CASE(R_, NW_) \
-    if (plan.rows == R_ && plan.waves == NW_) return launch_decode_t<GDN_DK, IO, R_, NW_>(p, s);
+    if (plan.lanes == 4 && plan.rows == R_ && plan.waves == NW_) return launch_decode_t<GDN_DK, IO, R_, NW_>(p, s);
     GDN_CASE(1, 1) GDN_CASE(1, 2) GDN_CASE(1, 4)
     GDN_CASE(2, 1) GDN_CASE(2, 2) GDN_CASE(2, 4)
 #if GDN_DK == 128
@@ -49,8 +67,10 @@ hipError_t decode_io(const DecodeParams &p, Plan plan, hipStream_t s) {
 
 }  // namespace
 
-bool GDN_FN(plan_available)(int io_dtype, Plan plan) {
-    return (io_dtype == GDN_F32 || io_dtype == GDN_BF16) && shape_compiled(plan.rows, plan.waves);
+bool GDN_FN(plan_available)(bool decode, int io_dtype, Plan plan) {
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return false;
+    return decode ? decode_compiled(plan.lanes, plan.rows, plan.waves)
+                  : prefill_compiled(plan.lanes, plan.rows, plan.waves);
 }
 
 hipError_t GDN_FN(launch_prefill)(const PrefillParams &p, int io_dtype, Plan plan, hipStream_t s) {

@@ -9,6 +9,9 @@
 
 namespace gdn {
 
+// Largest batch whose sequences the prefill kernel orders longest first.
+constexpr int kMaxRankedSeqs = 128;
+
 // Kernel arguments of the varlen prefill (passed by value as the kernarg segment).
 struct PrefillParams {
     const void *q, *k, *v;
@@ -18,6 +21,7 @@ struct PrefillParams {
     float *hT;
     int64_t total_tokens;
     int32_t n_seqs, hk, hv, dv;
+    int32_t rank_by_length;  // workgroups take sequences longest first (n_seqs <= kMaxRankedSeqs)
 };
 
 // Kernel arguments of one decode step.
@@ -30,16 +34,18 @@ struct DecodeParams {
     int32_t batch, hk, hv, dv, pool_size;
 };
 
-// A launch shape: `rows` state rows per lane quad and `waves` waves per workgroup.
-// A workgroup owns waves * 16 * rows consecutive rows of one value head.
+// A launch shape: `lanes` lanes hold one state row, each lane holds `rows` rows,
+// and a workgroup has `waves` waves; it owns waves * (64 / lanes) * rows
+// consecutive rows of one value head.
 struct Plan {
+    int lanes;
     int rows;
     int waves;
 };
 
 // Per-head-dim entry points, defined in gdn_dk{16,32,64,128}.hip.
 #define GDN_DECLARE_DK(DK)                                                                     \
-    bool plan_available_dk##DK(int io_dtype, Plan plan);                                       \
+    bool plan_available_dk##DK(bool decode, int io_dtype, Plan plan);                                     \
     hipError_t launch_prefill_dk##DK(const PrefillParams &p, int io_dtype, Plan plan, hipStream_t s); \
     hipError_t launch_decode_dk##DK(const DecodeParams &p, int io_dtype, Plan plan, hipStream_t s);
 GDN_DECLARE_DK(16)

@@ -11,22 +11,28 @@
 // This fixes every bit of the result; nothing below depends on the batch, on where a
 // sequence sits in it, on the launch shape or on the kernel (prefill or decode):
 //
-//   * The row lives in the registers of one lane quad.  Lane l (0..3) holds the
-//     columns 16c + 4l + e for chunk c = 0 .. dk/16 - 1 and e = 0..3.
-//   * A dot product of the row with a dk-vector x is a fixed tree: each lane forms
-//     "leaf" sums over 8 columns (4 when dk = 16) -- two consecutive chunks, columns in
-//     (c, e) order, as one multiply followed by fused multiply-adds -- then adds its
-//     leaves pairwise ((L0+L1)+(L2+L3)), then the quad adds across lanes l^1 and
-//     then l^2 with DPP.  Every lane of the quad ends with the same bits.
+//   * Columns are grouped into "leaves" of 8 (4 when dk = 16).  With the column
+//     index written as 16c + 4l + e (l, e in 0..3, c in 0..dk/16-1), leaf (l, s)
+//     holds the columns with l fixed and c in {2s, 2s+1}, in (c, e) order (for
+//     dk = 16: c = 0 only).  A leaf sum is one multiply followed by fused
+//     multiply-adds in that order.
+//   * A dot product of the row with a dk-vector is a fixed binary tree over the
+//     leaves, in the leaf order m = l * (leaves per l) + s: pairs (2i, 2i+1) first,
+//     then pairs of pairs, and so on.
 //   * Per token, with ptil = S_{t-1} . k_t (that tree):
 //         a = 2^(g * log2 e) (hardware exp2),  p = a * ptil,  u = beta * (v_j - p)
 //         S[i] = fma(a, S[i], u * k_t[i])        for every column i
 //         o_j  = S_t . q_t                       (the same tree)
-//     and in prefill the next token's ptil = S_t . k_{t+1} is formed in the same sweep,
-//     with the same tree, which is the value a fresh sweep would give.
+//     and in prefill the next token's ptil = S_t . k_{t+1} is formed in the same
+//     pass, which is the value a separate pass would give.
 //
-// Rows never interact, so how rows are spread over quads, waves and workgroups is free
-// (a launch-shape choice); within a row the arithmetic above is fixed.
+// How a row is spread over lanes is a launch choice that cannot change those bits:
+// L lanes (4, 8 or 16, consecutive lanes of one DPP row) hold one row, each lane a
+// contiguous run of leaves; the lanes first add their own leaves pairwise, then the
+// remaining tree levels run across lanes with DPP (partners l^1 and l^2 inside a
+// quad, then half-row and row mirrors), so every level adds the same two partial
+// sums whichever lanes hold them.  Rows never interact, so the rows per lane, waves
+// per workgroup and workgroups per head are free as well.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -61,23 +67,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return x >> 16;
 }
 
-// Sum over the four lanes of a quad: partner l^1 (quad_perm 1,0,3,2), then l^2
-// (quad_perm 2,3,0,1).  Addition is commutative, so all four lanes get equal bits.
-__device__ __forceinline__ float quad_sum(float x) {
-    x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-    x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-    return x;
+// x + (x of the partner lane given by a DPP control)
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-template <int DK>
-struct Geo {
-    static_assert(DK == 16 || DK == 32 || DK == 64 || DK == 128, "unsupported dk");
-    static constexpr int C = DK / 4;             // columns per lane
-    static constexpr int NCH = C / 4;            // 4-column chunks per lane
-    static constexpr int LF = (C < 8) ? C : 8;   // leaf length (columns)
-    static constexpr int CPL = LF / 4;           // chunks per leaf
-    static constexpr int NLEAF = C / LF;         // leaves per lane
-};
+// Tree levels above the lane-local leaves, for a row held by L lanes:
+// quad_perm 1,0,3,2 (l^1), quad_perm 2,3,0,1 (l^2), row_half_mirror, row_mirror.
+// Addition is commutative, so both partners compute identical bits at every level.
+template <int L>
+__device__ __forceinline__ float lane_sum(float x) {
+    x = dpp_add<0xB1>(x);
+    x = dpp_add<0x4E>(x);
+    if constexpr (L >= 8) x = dpp_add<0x141>(x);
+    if constexpr (L >= 16) x = dpp_add<0x140>(x);
+    return x;
+}
 
 template <int N>
 __device__ __forceinline__ float leaf_tree(const float (&x)[N]) {
@@ -91,20 +97,48 @@ __device__ __forceinline__ float leaf_tree(const float (&x)[N]) {
     }
 }
 
-// res[r] = S[r] . x  for the R rows held by this lane (all quad lanes get the result).
-template <int DK, int R>
-__device__ __forceinline__ void row_dots(const float (&S)[R][DK / 4], const float (&x)[DK / 4], float (&res)[R]) {
-    using G = Geo<DK>;
+// Lane geometry for key dim DK with L lanes per row.
+template <int DK, int L>
+struct Geo {
+    static_assert(DK == 16 || DK == 32 || DK == 64 || DK == 128, "unsupported dk");
+    static_assert(L == 4 || L == 8 || L == 16, "lanes per row");
+    static constexpr int LF = (DK >= 32) ? 8 : 4;     // leaf length
+    static constexpr int CPL = LF / 4;                // 4-column chunks per leaf
+    static constexpr int NCH4 = DK / 16;              // chunks per l (the 4-lane view)
+    static constexpr int SUB = L / 4;                 // lanes sharing one l
+    static constexpr int NCH = NCH4 / SUB;            // chunks per lane
+    static constexpr int C = 4 * NCH;                 // columns per lane
+    static constexpr int NLEAF = NCH / CPL;           // leaves per lane
+    static constexpr int RG = 64 / L;                 // row groups per wave
+    static_assert(NCH >= CPL && NCH % CPL == 0, "a lane must hold whole leaves");
+    // First column of this lane's chunk j is col0 + 16 j.
+    __device__ static int col0(int lam) { return 16 * ((lam % SUB) * NCH) + 4 * (lam / SUB); }
+    // Where 16-column chunk c of a key/query row sits in LDS.  The chunks are
+    // permuted so that, at every step of a read, the L lanes of a row touch
+    // distinct LDS banks (lanes differing only in lam % SUB would otherwise read
+    // addresses 64*NCH bytes apart, which share banks).
+    __host__ __device__ static constexpr int lds_chunk(int c) { return c ^ ((c / NCH) & (SUB - 1)); }
+    // LDS float offset, inside one staged row, of this lane's chunk j.
+    __device__ static int lds_col(int lam, int j) {
+        return 16 * lds_chunk((lam % SUB) * NCH + j) + 4 * (lam / SUB);
+    }
+};
+
+// res[r] = S[r] . x  for the R rows held by this lane (every lane of the row gets it).
+template <int DK, int L, int R, int C>
+__device__ __forceinline__ void row_dots(const float (&S)[R][C], const float (&x)[C], float (&res)[R]) {
+    using G = Geo<DK, L>;
+    static_assert(C == G::C, "columns per lane");
     float acc[R][G::NLEAF];
 #pragma unroll
-    for (int c = 0; c < G::NCH; ++c) {
+    for (int j = 0; j < G::NCH; ++j) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int i = 4 * c + e;
-            const int lf = c / G::CPL;
+            const int i = 4 * j + e;
+            const int lf = j / G::CPL;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                if ((c % G::CPL) == 0 && e == 0)
+                if ((j % G::CPL) == 0 && e == 0)
                     acc[r][lf] = S[r][i] * x[i];
                 else
                     acc[r][lf] = __builtin_fmaf(S[r][i], x[i], acc[r][lf]);
@@ -112,62 +146,34 @@ __device__ __forceinline__ void row_dots(const float (&S)[R][DK / 4], const floa
         }
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) res[r] = quad_sum(leaf_tree<G::NLEAF>(acc[r]));
+    for (int r = 0; r < R; ++r) res[r] = lane_sum<L>(leaf_tree<G::NLEAF>(acc[r]));
 }
 
 // One token's state update and read-out for the R rows of this lane:
-//   S[r][i] = fma(a, S[r][i], u[r] * kc[i]);  o[r] = S[r] . q
-// and, when NEXT, ptil[r] = S[r] . kn with kn (the next token's key) copied into
-// registers on the way.  qchunk(c) / kchunk(c) return 4 columns of chunk c.
-template <int DK, int R, bool NEXT, class QF, class KF>
-__device__ __forceinline__ void update_sweep(float (&S)[R][DK / 4], const float (&kc)[DK / 4], float (&kn)[DK / 4],
-                                             QF qchunk, KF kchunk, float a, const float (&u)[R], float (&o)[R],
+//   S[r][i] = fma(a, S[r][i], u[r] * kc[i])  for all i, then o[r] = S[r] . qc,
+// then, when NEXT, ptil[r] = S[r] . kn (the next token's key).  Doing the whole
+// update before the read-outs gives the query and next-key loads time to land.
+template <int DK, int L, int R, bool NEXT, int C>
+__device__ __forceinline__ void update_sweep(float (&S)[R][C], const float (&kc)[C], const float (&qc)[C],
+                                             const float (&kn)[C], float a, const float (&u)[R], float (&o)[R],
                                              float (&ptil)[R]) {
-    using G = Geo<DK>;
-    float ao[R][G::NLEAF];
-    float ap[R][G::NLEAF];
 #pragma unroll
-    for (int c = 0; c < G::NCH; ++c) {
-        const float4 q4 = qchunk(c);
-        const float qe[4] = {q4.x, q4.y, q4.z, q4.w};
-        float ke[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (NEXT) {
-            const float4 k4 = kchunk(c);
-            ke[0] = k4.x; ke[1] = k4.y; ke[2] = k4.z; ke[3] = k4.w;
-            kn[4 * c + 0] = k4.x; kn[4 * c + 1] = k4.y; kn[4 * c + 2] = k4.z; kn[4 * c + 3] = k4.w;
-        }
+    for (int i = 0; i < C; ++i) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 4 * c + e;
-            const int lf = c / G::CPL;
-            const bool first = (c % G::CPL) == 0 && e == 0;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float w = u[r] * kc[i];
-                const float s = __builtin_fmaf(a, S[r][i], w);
-                S[r][i] = s;
-                if (first) {
-                    ao[r][lf] = s * qe[e];
-                    if constexpr (NEXT) ap[r][lf] = s * ke[e];
-                } else {
-                    ao[r][lf] = __builtin_fmaf(s, qe[e], ao[r][lf]);
-                    if constexpr (NEXT) ap[r][lf] = __builtin_fmaf(s, ke[e], ap[r][lf]);
-                }
-            }
+        for (int r = 0; r < R; ++r) {
+            const float w = u[r] * kc[i];
+            S[r][i] = __builtin_fmaf(a, S[r][i], w);
         }
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        o[r] = quad_sum(leaf_tree<G::NLEAF>(ao[r]));
-        if constexpr (NEXT) ptil[r] = quad_sum(leaf_tree<G::NLEAF>(ap[r]));
-    }
+    row_dots<DK, L, R>(S, qc, o);
+    if constexpr (NEXT) row_dots<DK, L, R>(S, kn, ptil);
 }
 
 // ------------------------------------------------------------------ io types
 
 struct IoBf16 {
     static constexpr int VEC = 8;  // elements per 16-byte vector
-    static constexpr int ID = GDN_BF16;
+    static constexpr int ESZ = 2;
     __device__ static void unpack(const uint4 &raw, float *f) {
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -192,7 +198,7 @@ struct IoBf16 {
 
 struct IoF32 {
     static constexpr int VEC = 4;
-    static constexpr int ID = GDN_F32;
+    static constexpr int ESZ = 4;
     __device__ static void unpack(const uint4 &raw, float *f) {
         f[0] = __uint_as_float(raw.x);
         f[1] = __uint_as_float(raw.y);
@@ -208,69 +214,62 @@ struct IoF32 {
 
 // ------------------------------------------------------------- prefill kernel
 
-// Tokens staged per block through LDS (double-buffered).
-constexpr int kTokenBlock = 16;
-
-template <int DK, class IO, int R, int NW>
+template <int DK, class IO, int L, int R, int NW>
 struct PrefillShape {
-    static constexpr int TB = kTokenBlock;
-    static constexpr int RW = NW * 16 * R;          // rows per workgroup
-    static constexpr int NT = NW * 64;              // threads per workgroup
-    static constexpr int KVEC = DK / IO::VEC;       // 16-byte vectors per key/query row
-    static constexpr int VVEC = RW / IO::VEC;       // 16-byte vectors per value row slice
-    static constexpr int KITEMS = (TB + 1) * KVEC;  // keys: TB tokens + the next block's first
-    static constexpr int QITEMS = TB * KVEC;
-    static constexpr int VITEMS = TB * VVEC;
+    static constexpr int TB = (NW >= 2) ? 16 : 8;    // tokens per staged block
+    static constexpr int TS = TB + 1;                // staged tokens: the block and the next block's first
+    static constexpr int RW = NW * (64 / L) * R;     // rows per workgroup
+    static constexpr int NT = NW * 64;               // threads per workgroup
+    static constexpr int KVEC = DK / IO::VEC;        // 16-byte vectors per key/query row
+    static constexpr int VVEC = RW / IO::VEC;        // 16-byte vectors per value row slice
+    static constexpr int KITEMS = TS * KVEC;
+    static constexpr int VITEMS = TS * VVEC;
     static constexpr int KSLOTS = (KITEMS + NT - 1) / NT;
-    static constexpr int QSLOTS = (QITEMS + NT - 1) / NT;
     static constexpr int VSLOTS = (VITEMS + NT - 1) / NT;
-    static_assert(2 * TB <= NT, "gate/beta staging needs 2*TB threads");
+    static constexpr int TT = L / R;                 // tokens buffered per output store
+    static_assert(2 * TS <= NT, "gate/beta staging needs 2*(TB+1) threads");
     static_assert(RW % IO::VEC == 0, "row slice must be whole vectors");
+    static_assert(TB % TT == 0, "output flushes must align with token blocks");
 };
 
-template <int DK, class IO, int R, int NW>
-struct PrefillLds {
-    using Sh = PrefillShape<DK, IO, R, NW>;
-    float k[2][Sh::TB + 1][DK];
-    float q[2][Sh::TB][DK];
-    float v[2][Sh::TB][Sh::RW];
-    float a[2][Sh::TB];
-    float b[2][Sh::TB];
+template <int DK, class IO, int L, int R, int NW>
+struct alignas(16) PrefillLds {
+    using Sh = PrefillShape<DK, IO, L, R, NW>;
+    float k[2][Sh::TS][DK];   // key rows, fp32, chunks permuted by Geo::lds_chunk
+    float q[2][Sh::TS][DK];   // query rows, same layout
+    float v[2][Sh::TS][Sh::RW];
+    float a[2][Sh::TS];       // decay factors exp(g)
+    float b[2][Sh::TS];       // beta
 };
 
 // Global -> register stage of one token block (issued early), then register -> LDS.
-template <int DK, class IO, int R, int NW>
+template <int DK, class IO, int L, int R, int NW>
 struct Stager {
-    using Sh = PrefillShape<DK, IO, R, NW>;
+    using Sh = PrefillShape<DK, IO, L, R, NW>;
+    using G = Geo<DK, L>;
     uint4 kr[Sh::KSLOTS];
-    uint4 qr[Sh::QSLOTS];
+    uint4 qr[Sh::KSLOTS];
     uint4 vr[Sh::VSLOTS];
     float gb;
 
     __device__ __forceinline__ void load(const PrefillParams &p, int64_t t0, int64_t te, int kh, int h, int row0,
                                          int tid) {
         const uint4 zero = make_uint4(0, 0, 0, 0);
+        const char *kb = static_cast<const char *>(p.k);
+        const char *qb = static_cast<const char *>(p.q);
+        const char *vb = static_cast<const char *>(p.v);
 #pragma unroll
         for (int s = 0; s < Sh::KSLOTS; ++s) {
             const int it = tid + s * Sh::NT;
             const int ti = it / Sh::KVEC, vec = it % Sh::KVEC;
             const int64_t t = t0 + ti;
             kr[s] = zero;
-            if (it < Sh::KITEMS && t < te)
-                kr[s] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(p.k) +
-                                                         ((size_t)(t * p.hk + kh) * DK + (size_t)vec * IO::VEC) *
-                                                             (IO::VEC == 8 ? 2 : 4));
-        }
-#pragma unroll
-        for (int s = 0; s < Sh::QSLOTS; ++s) {
-            const int it = tid + s * Sh::NT;
-            const int ti = it / Sh::KVEC, vec = it % Sh::KVEC;
-            const int64_t t = t0 + ti;
             qr[s] = zero;
-            if (it < Sh::QITEMS && t < te)
-                qr[s] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(p.q) +
-                                                         ((size_t)(t * p.hk + kh) * DK + (size_t)vec * IO::VEC) *
-                                                             (IO::VEC == 8 ? 2 : 4));
+            if (it < Sh::KITEMS && t < te) {
+                const size_t off = ((size_t)(t * p.hk + kh) * DK + (size_t)vec * IO::VEC) * IO::ESZ;
+                kr[s] = *reinterpret_cast<const uint4 *>(kb + off);
+                qr[s] = *reinterpret_cast<const uint4 *>(qb + off);
+            }
         }
 #pragma unroll
         for (int s = 0; s < Sh::VSLOTS; ++s) {
@@ -280,18 +279,20 @@ struct Stager {
             vr[s] = zero;
             if (it < Sh::VITEMS && t < te)
                 vr[s] = *reinterpret_cast<const uint4 *>(
-                    static_cast<const char *>(p.v) +
-                    ((size_t)(t * p.hv + h) * p.dv + row0 + (size_t)vec * IO::VEC) * (IO::VEC == 8 ? 2 : 4));
+                    vb + ((size_t)(t * p.hv + h) * p.dv + row0 + (size_t)vec * IO::VEC) * IO::ESZ);
         }
         gb = 0.f;
-        if (tid < 2 * Sh::TB) {
-            const int ti = tid % Sh::TB;
+        if (tid < 2 * Sh::TS) {
+            const int ti = tid % Sh::TS;
             const int64_t t = t0 + ti;
-            if (t < te) gb = (tid < Sh::TB) ? p.g[t * p.hv + h] : p.beta[t * p.hv + h];
+            if (t < te) gb = (tid < Sh::TS) ? p.g[t * p.hv + h] : p.beta[t * p.hv + h];
         }
     }
 
-    __device__ __forceinline__ void store(PrefillLds<DK, IO, R, NW> &L, int buf, int tid) const {
+    // Columns [col, col + 4) of a key/query row go to their permuted LDS chunk.
+    __device__ static float *row_slot(float *row, int col) { return row + 16 * G::lds_chunk(col / 16) + col % 16; }
+
+    __device__ __forceinline__ void store(PrefillLds<DK, IO, L, R, NW> &Ld, int buf, int tid) const {
 #pragma unroll
         for (int s = 0; s < Sh::KSLOTS; ++s) {
             const int it = tid + s * Sh::NT;
@@ -301,20 +302,12 @@ struct Stager {
                 IO::unpack(kr[s], f);
 #pragma unroll
                 for (int x = 0; x < IO::VEC; x += 4)
-                    *reinterpret_cast<float4 *>(&L.k[buf][ti][vec * IO::VEC + x]) =
+                    *reinterpret_cast<float4 *>(row_slot(Ld.k[buf][ti], vec * IO::VEC + x)) =
                         make_float4(f[x], f[x + 1], f[x + 2], f[x + 3]);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < Sh::QSLOTS; ++s) {
-            const int it = tid + s * Sh::NT;
-            if (it < Sh::QITEMS) {
-                const int ti = it / Sh::KVEC, vec = it % Sh::KVEC;
-                float f[IO::VEC];
                 IO::unpack(qr[s], f);
 #pragma unroll
                 for (int x = 0; x < IO::VEC; x += 4)
-                    *reinterpret_cast<float4 *>(&L.q[buf][ti][vec * IO::VEC + x]) =
+                    *reinterpret_cast<float4 *>(row_slot(Ld.q[buf][ti], vec * IO::VEC + x)) =
                         make_float4(f[x], f[x + 1], f[x + 2], f[x + 3]);
             }
         }
@@ -327,30 +320,74 @@ struct Stager {
                 IO::unpack(vr[s], f);
 #pragma unroll
                 for (int x = 0; x < IO::VEC; x += 4)
-                    *reinterpret_cast<float4 *>(&L.v[buf][ti][vec * IO::VEC + x]) =
+                    *reinterpret_cast<float4 *>(&Ld.v[buf][ti][vec * IO::VEC + x]) =
                         make_float4(f[x], f[x + 1], f[x + 2], f[x + 3]);
             }
         }
-        if (tid < Sh::TB)
-            L.a[buf][tid] = decay_factor(gb);
-        else if (tid < 2 * Sh::TB)
-            L.b[buf][tid - Sh::TB] = gb;
+        if (tid < Sh::TS)
+            Ld.a[buf][tid] = decay_factor(gb);
+        else if (tid < 2 * Sh::TS)
+            Ld.b[buf][tid - Sh::TS] = gb;
     }
 };
 
+// The per-token inputs one lane carries from one token to the next: the key (the
+// next token's key is read during the current token's pass) and the scalars.
+template <int C, int R>
+struct TokRegs {
+    float k[C];
+    float v[R];
+    float a, beta;
+};
+
+// Work order.  Workgroups start in blockIdx order and the sequence walk is serial,
+// so the longest sequences should start first (longest-processing-time-first list
+// scheduling); otherwise a long sequence that starts late sets the kernel's end.
+// When asked (rank_by_length, at most kMaxRankedSeqs sequences) each workgroup
+// ranks the lengths itself (descending, ties by index) and takes the sequence of
+// rank blockIdx.z; otherwise it takes sequence blockIdx.z.  Which sequence a
+// workgroup serves never changes any result.
+__device__ __forceinline__ int seq_by_length_rank(const int32_t *cu, int n_seqs, int rank, int tid, int nthreads) {
+    __shared__ int32_t s_len[kMaxRankedSeqs];
+    __shared__ int s_pick;
+    for (int m = tid; m < n_seqs; m += nthreads) s_len[m] = cu[m + 1] - cu[m];
+    __syncthreads();
+    for (int m = tid; m < n_seqs; m += nthreads) {
+        const int lm = s_len[m];
+        int r = 0;
+        for (int i = 0; i < n_seqs; ++i) {
+            const int li = s_len[i];
+            r += (li > lm) || (li == lm && i < m);
+        }
+        if (r == rank) s_pick = m;
+    }
+    __syncthreads();
+    return s_pick;
+}
+
+#ifndef GDN_PREFILL_WAVES_PER_EU
+#define GDN_PREFILL_WAVES_PER_EU 1
+#endif
+
 // One workgroup = (sequence n = blockIdx.z, value head h = blockIdx.y, row tile blockIdx.x).
-template <int DK, class IO, int R, int NW>
-__global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(PrefillParams p) {
-    using Sh = PrefillShape<DK, IO, R, NW>;
-    constexpr int C = DK / 4, NCH = C / 4, TB = Sh::TB;
-    __shared__ PrefillLds<DK, IO, R, NW> L;
+template <int DK, class IO, int L, int R, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GDN_PREFILL_WAVES_PER_EU)))
+void gdn_prefill_kernel(PrefillParams p) {
+    using Sh = PrefillShape<DK, IO, L, R, NW>;
+    using G = Geo<DK, L>;
+    constexpr int C = G::C, NCH = G::NCH, TB = Sh::TB, RG = G::RG, TT = Sh::TT;
+    __shared__ PrefillLds<DK, IO, L, R, NW> Ld;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int l = lane & 3, qd = lane >> 2;
-    const int n = blockIdx.z, h = blockIdx.y;
+    const int lam = lane % L, grp = lane / L;
+    const int col0 = G::col0(lam);
+    const int h = blockIdx.y;
     const int row0 = blockIdx.x * Sh::RW;
     const int kh = h / (p.hv / p.hk);
+    // (ties break by index, so the ranks are a permutation and exactly one thread picks)
+    const int n = p.rank_by_length ? seq_by_length_rank(p.cu_seqlens, p.n_seqs, blockIdx.z, tid, NW * 64)
+                                   : (int)blockIdx.z;
 
     // Sequence bounds, clamped into [0, T] so that a malformed cu_seqlens cannot
     // send the kernel outside the buffers.
@@ -359,34 +396,57 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(PrefillParams p) {
     te = te < tb ? tb : (te > p.total_tokens ? p.total_tokens : te);
     const int64_t len = te - tb;
 
-    const int wrow = wave * 16 * R + qd;  // this lane's first row inside the tile (rows wrow + 16 r)
+    // This lane's rows inside the tile: wrow + RG * r.
+    const int wrow = wave * RG * R + grp;
     const size_t state_row0 = ((size_t)n * p.hv + h) * p.dv + row0 + wrow;
 
     float S[R][C];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
+        for (int j = 0; j < NCH; ++j) {
             float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (p.h0) x = *reinterpret_cast<const float4 *>(p.h0 + (state_row0 + 16 * r) * DK + 16 * c + 4 * l);
-            S[r][4 * c + 0] = x.x; S[r][4 * c + 1] = x.y; S[r][4 * c + 2] = x.z; S[r][4 * c + 3] = x.w;
+            if (p.h0) x = *reinterpret_cast<const float4 *>(p.h0 + (state_row0 + RG * r) * DK + col0 + 16 * j);
+            S[r][4 * j + 0] = x.x; S[r][4 * j + 1] = x.y; S[r][4 * j + 2] = x.z; S[r][4 * j + 3] = x.w;
         }
     }
 
     if (len > 0) {
         const int nblk = (int)((len + TB - 1) / TB);
-        Stager<DK, IO, R, NW> st;
+        Stager<DK, IO, L, R, NW> st;
         st.load(p, tb, te, kh, h, row0, tid);
-        st.store(L, 0, tid);
+        st.store(Ld, 0, tid);
         __syncthreads();
 
-        float kA[C], kB[C], ptil[R];
+        // LDS float offsets of this lane's chunks within a staged row.
+        int lcol[NCH];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const float4 x = *reinterpret_cast<const float4 *>(&L.k[0][0][16 * c + 4 * l]);
-            kA[4 * c + 0] = x.x; kA[4 * c + 1] = x.y; kA[4 * c + 2] = x.z; kA[4 * c + 3] = x.w;
-        }
-        row_dots<DK, R>(S, kA, ptil);
+        for (int j = 0; j < NCH; ++j) lcol[j] = G::lds_col(lam, j);
+        auto read_cols = [&](float (&dst)[C], const float *row) {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const float4 x = *reinterpret_cast<const float4 *>(row + lcol[j]);
+                dst[4 * j + 0] = x.x; dst[4 * j + 1] = x.y; dst[4 * j + 2] = x.z; dst[4 * j + 3] = x.w;
+            }
+        };
+        auto fetch = [&](TokRegs<C, R> &X, int buf, int ti) {
+            read_cols(X.k, Ld.k[buf][ti]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) X.v[r] = Ld.v[buf][ti][wrow + RG * r];
+            X.a = Ld.a[buf][ti];
+            X.beta = Ld.b[buf][ti];
+        };
+
+        // Outputs are kept in registers and stored TT tokens at a time: lane lam
+        // keeps token (lam % TT) of its row lam / TT.
+        const int my_slot = lam % TT, my_r = lam / TT;
+        const size_t out_row = (size_t)h * p.dv + row0 + wrow + RG * my_r;
+        float obuf = 0.f;
+
+        TokRegs<C, R> A, B;
+        float ptil[R];
+        fetch(A, 0, 0);
+        row_dots<DK, L, R>(S, A.k, ptil);
 
         for (int blk = 0; blk < nblk; ++blk) {
             const int buf = blk & 1;
@@ -394,32 +454,43 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(PrefillParams p) {
             if (blk + 1 < nblk) st.load(p, t0 + TB, te, kh, h, row0, tid);
             const int nt = (int)((te - t0) < TB ? (te - t0) : TB);
 
-            auto step = [&](float (&kc)[C], float (&kn)[C], int ti) {
-                const float a = L.a[buf][ti];
-                const float beta = L.b[buf][ti];
+            // cur holds token ti; nxt receives token ti + 1 (staged row ti + 1 <= TB).
+            auto step = [&](TokRegs<C, R> &cur, TokRegs<C, R> &nxt, int ti) {
                 float u[R], o[R];
 #pragma unroll
-                for (int r = 0; r < R; ++r) u[r] = delta_coeff(a, ptil[r], L.v[buf][ti][wrow + 16 * r], beta);
-                update_sweep<DK, R, true>(
-                    S, kc, kn,
-                    [&](int c) { return *reinterpret_cast<const float4 *>(&L.q[buf][ti][16 * c + 4 * l]); },
-                    [&](int c) { return *reinterpret_cast<const float4 *>(&L.k[buf][ti + 1][16 * c + 4 * l]); }, a,
-                    u, o, ptil);
+                for (int r = 0; r < R; ++r) u[r] = delta_coeff(cur.a, ptil[r], cur.v[r], cur.beta);
+                float qc[C];
+                read_cols(qc, Ld.q[buf][ti]);
+                fetch(nxt, buf, ti + 1);
+                update_sweep<DK, L, R, true>(S, cur.k, qc, nxt.k, cur.a, u, o, ptil);
                 float ov = o[0];
 #pragma unroll
                 for (int r = 1; r < R; ++r)
-                    if (l == r) ov = o[r];
-                if (l < R) IO::store1(p.out, (size_t)((t0 + ti) * p.hv + h) * p.dv + row0 + wrow + 16 * l, ov);
+                    if (my_r == r) ov = o[r];
+                if (my_slot == ti % TT) obuf = ov;
+                if (ti % TT == TT - 1)
+                    IO::store1(p.out, (size_t)(t0 + ti - (TT - 1) + my_slot) * p.hv * p.dv + out_row, obuf);
             };
 
-            int ti = 0;
-            for (; ti + 1 < nt; ti += 2) {
-                step(kA, kB, ti);
-                step(kB, kA, ti + 1);
+            if (nt == TB) {
+#pragma unroll
+                for (int ti = 0; ti < TB; ti += 2) {
+                    step(A, B, ti);
+                    step(B, A, ti + 1);
+                }
+            } else {
+                int ti = 0;
+                for (; ti + 1 < nt; ti += 2) {
+                    step(A, B, ti);
+                    step(B, A, ti + 1);
+                }
+                if (ti < nt) step(A, B, ti);
+                const int rem = nt % TT;  // tokens kept but not yet stored
+                if (rem != 0 && my_slot < rem)
+                    IO::store1(p.out, (size_t)(t0 + nt - rem + my_slot) * p.hv * p.dv + out_row, obuf);
             }
-            if (ti < nt) step(kA, kB, ti);
 
-            if (blk + 1 < nblk) st.store(L, buf ^ 1, tid);
+            if (blk + 1 < nblk) st.store(Ld, buf ^ 1, tid);
             __syncthreads();
         }
     }
@@ -428,9 +499,9 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
 #pragma unroll
-            for (int c = 0; c < NCH; ++c)
-                *reinterpret_cast<float4 *>(p.hT + (state_row0 + 16 * r) * DK + 16 * c + 4 * l) =
-                    make_float4(S[r][4 * c + 0], S[r][4 * c + 1], S[r][4 * c + 2], S[r][4 * c + 3]);
+            for (int j = 0; j < NCH; ++j)
+                *reinterpret_cast<float4 *>(p.hT + (state_row0 + RG * r) * DK + col0 + 16 * j) =
+                    make_float4(S[r][4 * j + 0], S[r][4 * j + 1], S[r][4 * j + 2], S[r][4 * j + 3]);
         }
     }
 }
@@ -438,22 +509,26 @@ __global__ __launch_bounds__(NW * 64) void gdn_prefill_kernel(PrefillParams p) {
 // -------------------------------------------------------------- decode kernel
 
 // One workgroup = (batch row b = blockIdx.z, value head h = blockIdx.y, row tile blockIdx.x).
+// Four lanes per row: the state streams once through registers.
 template <int DK, class IO, int R, int NW>
 __global__ __launch_bounds__(NW * 64) void gdn_decode_kernel(DecodeParams p) {
-    constexpr int C = DK / 4, NCH = C / 4;
-    constexpr int RW = NW * 16 * R;
+    constexpr int L = 4;
+    using G = Geo<DK, L>;
+    constexpr int C = G::C, RG = G::RG;
+    constexpr int RW = NW * RG * R;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int l = lane & 3, qd = lane >> 2;
+    const int lam = lane % L, grp = lane / L;
+    const int col0 = G::col0(lam);
     const int b = blockIdx.z, h = blockIdx.y;
     const int row0 = blockIdx.x * RW;
     const int kh = h / (p.hv / p.hk);
-    const int wrow = wave * 16 * R + qd;
+    const int wrow = wave * RG * R + grp;
     const size_t orow = ((size_t)b * p.hv + h) * p.dv + row0 + wrow;
 
     const int slot = p.state_idx ? p.state_idx[b] : b;
     if (slot < 0 || slot >= p.pool_size) {  // padding row: zero output, no state access
-        if (l < R) IO::store1(p.out, orow + 16 * l, 0.f);
+        if (lam < R) IO::store1(p.out, orow + RG * lam, 0.f);
         return;
     }
     float *st = p.pool + (((size_t)slot * p.hv + h) * p.dv + row0 + wrow) * DK;
@@ -462,56 +537,52 @@ __global__ __launch_bounds__(NW * 64) void gdn_decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const float4 x = *reinterpret_cast<const float4 *>(st + (size_t)16 * r * DK + 16 * c + 4 * l);
-            S[r][4 * c + 0] = x.x; S[r][4 * c + 1] = x.y; S[r][4 * c + 2] = x.z; S[r][4 * c + 3] = x.w;
+        for (int j = 0; j < G::NCH; ++j) {
+            const float4 x = *reinterpret_cast<const float4 *>(st + (size_t)RG * r * DK + col0 + 16 * j);
+            S[r][4 * j + 0] = x.x; S[r][4 * j + 1] = x.y; S[r][4 * j + 2] = x.z; S[r][4 * j + 3] = x.w;
         }
     }
     float kx[C], qx[C];
-    const size_t qk0 = ((size_t)b * p.hk + kh) * DK;
+    const size_t qk0 = ((size_t)b * p.hk + kh) * DK + col0;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const float4 k4 = IO::load4(p.k, qk0 + 16 * c + 4 * l);
-        const float4 q4 = IO::load4(p.q, qk0 + 16 * c + 4 * l);
-        kx[4 * c + 0] = k4.x; kx[4 * c + 1] = k4.y; kx[4 * c + 2] = k4.z; kx[4 * c + 3] = k4.w;
-        qx[4 * c + 0] = q4.x; qx[4 * c + 1] = q4.y; qx[4 * c + 2] = q4.z; qx[4 * c + 3] = q4.w;
+    for (int j = 0; j < G::NCH; ++j) {
+        const float4 k4 = IO::load4(p.k, qk0 + 16 * j);
+        const float4 q4 = IO::load4(p.q, qk0 + 16 * j);
+        kx[4 * j + 0] = k4.x; kx[4 * j + 1] = k4.y; kx[4 * j + 2] = k4.z; kx[4 * j + 3] = k4.w;
+        qx[4 * j + 0] = q4.x; qx[4 * j + 1] = q4.y; qx[4 * j + 2] = q4.z; qx[4 * j + 3] = q4.w;
     }
     const float a = decay_factor(p.g[(size_t)b * p.hv + h]);
     const float beta = p.beta[(size_t)b * p.hv + h];
 
     float ptil[R], u[R], o[R];
-    row_dots<DK, R>(S, kx, ptil);
+    row_dots<DK, L, R>(S, kx, ptil);
 #pragma unroll
-    for (int r = 0; r < R; ++r) u[r] = delta_coeff(a, ptil[r], IO::load1(p.v, orow + 16 * r), beta);
-    float unused[C];
-    update_sweep<DK, R, false>(
-        S, kx, unused,
-        [&](int c) { return make_float4(qx[4 * c + 0], qx[4 * c + 1], qx[4 * c + 2], qx[4 * c + 3]); },
-        [&](int c) { return make_float4(0.f, 0.f, 0.f, 0.f); }, a, u, o, ptil);
+    for (int r = 0; r < R; ++r) u[r] = delta_coeff(a, ptil[r], IO::load1(p.v, orow + RG * r), beta);
+    update_sweep<DK, L, R, false>(S, kx, qx, kx, a, u, o, ptil);
 
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c)
-            *reinterpret_cast<float4 *>(st + (size_t)16 * r * DK + 16 * c + 4 * l) =
-                make_float4(S[r][4 * c + 0], S[r][4 * c + 1], S[r][4 * c + 2], S[r][4 * c + 3]);
+        for (int j = 0; j < G::NCH; ++j)
+            *reinterpret_cast<float4 *>(st + (size_t)RG * r * DK + col0 + 16 * j) =
+                make_float4(S[r][4 * j + 0], S[r][4 * j + 1], S[r][4 * j + 2], S[r][4 * j + 3]);
     }
     float ov = o[0];
 #pragma unroll
     for (int r = 1; r < R; ++r)
-        if (l == r) ov = o[r];
-    if (l < R) IO::store1(p.out, orow + 16 * l, ov);
+        if (lam == r) ov = o[r];
+    if (lam < R) IO::store1(p.out, orow + RG * lam, ov);
 }
 
 // ------------------------------------------------------------ launch helpers
 
-template <int DK, class IO, int R, int NW>
+template <int DK, class IO, int L, int R, int NW>
 hipError_t launch_prefill_t(const PrefillParams &p, hipStream_t s) {
-    constexpr int RW = NW * 16 * R;
+    constexpr int RW = NW * (64 / L) * R;
     dim3 grid(p.dv / RW, p.hv, p.n_seqs), block(NW * 64);
     void *args[] = {const_cast<PrefillParams *>(&p)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, R, NW>), grid, block, args, 0,
-                           s);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, L, R, NW>), grid, block,
+                           args, 0, s);
 }
 
 template <int DK, class IO, int R, int NW>

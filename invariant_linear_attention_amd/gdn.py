@@ -28,7 +28,8 @@ class GdnDims(ctypes.Structure):
         ("n_seqs", ctypes.c_int32), ("hk", ctypes.c_int32), ("hv", ctypes.c_int32),
         ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
         ("total_tokens", ctypes.c_int64), ("pool_size", ctypes.c_int32),
-        ("plan_rows", ctypes.c_int32), ("plan_waves", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("plan_lanes", ctypes.c_int32), ("plan_rows", ctypes.c_int32), ("plan_waves", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -107,13 +108,19 @@ def _need(t, name, dtype=None, cuda=True):
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
 
 
-def make_dims(q, v, n_seqs: int, total_tokens: int, pool_size: int = 0, plan: Tuple[int, int] = (0, 0)) -> GdnDims:
+def make_dims(q, v, n_seqs: int, total_tokens: int, pool_size: int = 0, plan=(0, 0, 0)) -> GdnDims:
+    """``plan`` = (lanes per row, rows per lane, waves per workgroup); 0 = automatic.
+    A 2-tuple means (rows, waves) with automatic lanes."""
+    plan = tuple(int(x) for x in plan)
+    if len(plan) == 2:
+        plan = (0,) + plan
     return GdnDims(n_seqs=int(n_seqs), hk=int(q.shape[1]), hv=int(v.shape[1]), dk=int(q.shape[2]),
                    dv=int(v.shape[2]), io_dtype=_io_code(q), total_tokens=int(total_tokens),
-                   pool_size=int(pool_size), plan_rows=int(plan[0]), plan_waves=int(plan[1]), reserved=0)
+                   pool_size=int(pool_size), plan_lanes=plan[0], plan_rows=plan[1], plan_waves=plan[2],
+                   reserved=0)
 
 
-def gdn_fwd_varlen(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, stream=None, plan=(0, 0),
+def gdn_fwd_varlen(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, stream=None, plan=(0, 0, 0),
                    want_state: bool = True):
     """Varlen prefill (see include/gdn.h).  Tensors on the GPU, contiguous:
     q, k [T, Hk, dk]; v [T, Hv, dv]; g, beta [T, Hv] fp32; h0 [N, Hv, dv, dk] fp32
@@ -141,7 +148,7 @@ def gdn_fwd_varlen(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, stream=N
     return out, hT
 
 
-def gdn_decode_step(q, k, v, g, beta, state_pool, state_idx=None, out=None, stream=None, plan=(0, 0)):
+def gdn_decode_step(q, k, v, g, beta, state_pool, state_idx=None, out=None, stream=None, plan=(0, 0, 0)):
     """One decode token per sequence (see include/gdn.h).  q, k [B, Hk, dk];
     v [B, Hv, dv]; g, beta [B, Hv]; state_pool [P, Hv, dv, dk] fp32 updated in
     place; state_idx [B] int32 or None (identity).  Returns out [B, Hv, dv]."""

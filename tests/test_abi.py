@@ -64,7 +64,7 @@ def test_struct_layout_matches_c(tmp_path):
 def _dims(**kw):
     from invariant_linear_attention_amd.gdn import GdnDims
     d = dict(n_seqs=2, hk=2, hv=4, dk=128, dv=128, io_dtype=1, total_tokens=10, pool_size=0,
-             plan_rows=0, plan_waves=0, reserved=0)
+             plan_lanes=0, plan_rows=0, plan_waves=0, reserved=0)
     d.update(kw)
     return GdnDims(**d)
 
@@ -102,6 +102,10 @@ def call_dec(lib, dims, **over):
     (dict(plan_rows=3, plan_waves=1), 6),
     (dict(plan_rows=2, plan_waves=8), 6),
     (dict(plan_rows=4, plan_waves=4), 6),
+    (dict(plan_lanes=2), 6),
+    (dict(plan_lanes=16, plan_rows=4), 6),
+    (dict(plan_lanes=16, plan_rows=1, plan_waves=1), 6),
+    (dict(dk=32, plan_lanes=8), 6),
     (dict(n_seqs=0, total_tokens=3), 2),
 ])
 def test_fwd_rejects_bad_dims(lib, case, code):

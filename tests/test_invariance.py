@@ -47,10 +47,25 @@ def test_alone_vs_in_batch(gpu):
         assert bit_equal(sa[0], sb[n]), "sequence %d state changed in the batch" % n
 
 
+PLANS = [(4, 1, 1), (4, 1, 2), (4, 1, 4), (4, 2, 1), (4, 2, 2), (4, 2, 4), (4, 4, 1), (4, 4, 2),
+         (8, 1, 1), (8, 1, 2), (8, 1, 4), (8, 2, 1), (8, 2, 2), (8, 2, 4),
+         (16, 1, 2), (16, 1, 4), (16, 2, 1), (16, 2, 2), (16, 2, 4), (0, 0, 0)]
+
+
 def test_every_launch_shape_gives_the_same_bits(gpu):
+    """Lanes per row, rows per lane and waves per workgroup move rows around the
+    chip; none of them may change a bit."""
     w = small_batch()
-    ref_o, ref_s = run_prefill(gpu, w, plan=(1, 1))
-    for plan in [(1, 2), (1, 4), (2, 1), (2, 2), (2, 4), (4, 1), (4, 2), (0, 0)]:
+    ref_o, ref_s = run_prefill(gpu, w, plan=(4, 1, 1))
+    for plan in PLANS:
+        o, s = run_prefill(gpu, w, plan=plan)
+        assert bit_equal(o, ref_o) and bit_equal(s, ref_s), "plan %s changed the bits" % (plan,)
+
+
+def test_launch_shapes_dk64(gpu):
+    w = synth.make_workload(6, [33, 0, 70], hk=2, hv=4, dk=64, dv=64, h0_std=0.1)
+    ref_o, ref_s = run_prefill(gpu, w, plan=(4, 1, 1))
+    for plan in [(4, 2, 2), (8, 1, 1), (8, 2, 4), (0, 0, 0)]:
         o, s = run_prefill(gpu, w, plan=plan)
         assert bit_equal(o, ref_o) and bit_equal(s, ref_s), "plan %s changed the bits" % (plan,)
 
