@@ -80,6 +80,32 @@ def rel(x, r):
     return float(np.linalg.norm(x - r) / max(np.linalg.norm(r), 1e-300))
 
 
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
+
+
+def pmc_pass(dev, stream):
+    """One launch of each kernel, preceded by a plain device copy of COPY_BYTES whose
+    FETCH_SIZE / WRITE_SIZE readings calibrate the counters' units."""
+    import torch
+
+    from invariant_linear_attention_amd import gdn, synth
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    w = synth.varlen_prefill(1001)
+    d = [t.to(dev) for t in (w.q, w.k, w.v, w.g, w.beta, w.h0, w.cu_seqlens)]
+    gdn.gdn_fwd_varlen(*d, stream=stream)
+    torch.cuda.synchronize()
+    B = 256
+    dw = synth.make_workload(2000 + B, [1] * B)
+    pool = torch.randn((B, 32, 128, 128), device=dev) * 0.1
+    gdn.gdn_decode_step(*(t.to(dev) for t in (dw.q, dw.k, dw.v, dw.g, dw.beta)), pool, stream=stream)
+    torch.cuda.synchronize()
+    print("pmc pass: copy %d bytes, prefill %d tokens, decode B=%d" % (COPY_BYTES, w.total_tokens, B), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,7 +113,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-key-heads", type=int, default=4, help="key heads in the CPU baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="host time spent on the CPU oracle baseline")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="no timing: one copy of a known size (counter calibration), then one launch each of the "
+                         "prefill (the benchmark batch) and of decode at B=256, for rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the recurrent forward needs no collective and this "
@@ -103,6 +132,9 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     gdn.load_library()
+    if args.pmc_pass:
+        pmc_pass(dev, stream)
+        return
 
     # ------------------------------------------------------------ prefill
     w = synth.varlen_prefill(1001)
@@ -172,20 +204,20 @@ def main():
     # ------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu:
-        kh_n = max(1, min(16, args.cpu_key_heads))
-        sample = synth.Workload(w.q[:, :kh_n].contiguous(), w.k[:, :kh_n].contiguous(),
-                                w.v[:, :2 * kh_n].contiguous(), w.g[:, :2 * kh_n].contiguous(),
-                                w.beta[:, :2 * kh_n].contiguous(), w.cu_seqlens, w.h0[:, :2 * kh_n].contiguous())
+        # The fp64 oracle on every head of the same batch, repeated until about
+        # --cpu-seconds of host time have passed (at least one full pass).
         threads = os.cpu_count() or 1
-        t0 = time.perf_counter()
-        oracle.gdn_forward(sample.q, sample.k, sample.v, sample.g, sample.beta, sample.cu_seqlens, sample.h0,
-                           n_threads=threads)
-        dt = time.perf_counter() - t0
-        frac = (2 * kh_n) / 32.0
-        cpu = {"value": T * frac / dt, "unit": "tokens/s", "cores": min(threads, w.n_seqs * 2 * kh_n),
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            oracle.gdn_forward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, w.h0, n_threads=threads)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= args.cpu_seconds:
+                break
+        cpu = {"value": passes * T / dt, "unit": "tokens/s", "cores": min(threads, w.n_seqs * 32),
                "kind": "oracle",
-               "sample": "fp64 oracle on %d of 32 value heads of the same 8-sequence batch (%d tokens), "
-                         "%.1f s, scaled to all heads" % (2 * kh_n, T, dt),
+               "sample": "fp64 oracle, all 32 value heads of the same 8-sequence batch (%d tokens), %d pass(es) "
+                         "in %.1f s" % (T, passes, dt),
                "seconds": dt}
 
     line = {

@@ -83,7 +83,7 @@ typedef struct gdn_dims {
     int32_t pool_size;     /* P: state pool entries (decode only; ignored by prefill) */
     int32_t plan_lanes;    /* launch shape: lanes holding one state row, 0 = automatic, else 4, 8 or 16 */
     int32_t plan_rows;     /* launch shape: state rows per lane, 0 = automatic, else 1, 2 or 4 */
-    int32_t plan_waves;    /* launch shape: waves per workgroup, 0 = automatic, else 1, 2 or 4 */
+    int32_t plan_waves;    /* launch shape: waves per workgroup, 0 = automatic, else 1, 2, 4 or 8 */
     int32_t reserved;      /* must be 0 */
 } gdn_dims;
 /* plan_lanes / plan_rows / plan_waves choose how state rows are spread over

@@ -83,7 +83,7 @@ gdn_status check_common(const gdn_dims *d) {
     if (d->hv % d->hk != 0 || d->dv % 16 != 0) return GDN_ERR_SHAPE;
     if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_ERR_DTYPE;
     if (!dk_supported(d->dk)) return GDN_ERR_UNSUPPORTED;
-    if (d->hv > 65535 || d->n_seqs > 65535) return GDN_ERR_SHAPE;  // grid y / z limits
+    if (d->hv > 65535 || d->n_seqs > 65535) return GDN_ERR_SHAPE;  // decode grid y / z limits
     return GDN_OK;
 }
 
@@ -93,7 +93,7 @@ gdn_status resolve_plan(const gdn_dims *d, bool decode, int64_t units, Plan *pla
            d->plan_waves};
     if (d->plan_rows == 0 && !plan_fits(d->dk, d->dv, decode, d->io_dtype, Plan{p.lanes, p.rows, 1})) p.rows = 1;
     if (p.waves == 0) {
-        for (int w : {4, 2, 1})
+        for (int w : {4, 2, 1, 8})
             if (plan_fits(d->dk, d->dv, decode, d->io_dtype, Plan{p.lanes, p.rows, w})) {
                 p.waves = w;
                 break;

@@ -17,11 +17,12 @@ namespace {
 // Prefill launch shapes compiled for this dk: (lanes, rows per lane, waves).
 // Lanes above 4 need whole leaves per lane: 8 lanes for dk >= 64, 16 for dk = 128.
 constexpr bool prefill_compiled(int lanes, int rows, int waves) {
+    if (waves == 8) return GDN_DK == 128 && ((lanes == 8 && rows == 1) || (lanes == 16 && rows == 2));
     if (waves != 1 && waves != 2 && waves != 4) return false;
     if (lanes == 4) return rows == 1 || rows == 2 || (GDN_DK == 128 && rows == 4 && waves <= 2);
     if (lanes == 8) return GDN_DK >= 64 && (rows == 1 || rows == 2);
     // (16, 1, 1) would own 4 rows per workgroup, less than one 16-byte bf16 vector.
-    if (lanes == 16) return GDN_DK == 128 && (rows == 2 || (rows == 1 && waves >= 2));
+    if (lanes == 16) return GDN_DK == 128 && (rows == 2 || rows == 4 || (rows == 1 && waves >= 2));
     return false;
 }
 
@@ -46,7 +47,9 @@ hipError_t prefill_io(const PrefillParams &p, Plan plan, hipStream_t s) {
 #endif
 #if GDN_DK == 128
     GDN_CASE(16, 1, 2) GDN_CASE(16, 1, 4)
-    GDN_CASE(16, 2, 1) GDN_CASE(16, 2, 2) GDN_CASE(16, 2, 4)
+    GDN_CASE(16, 2, 1) GDN_CASE(16, 2, 2) GDN_CASE(16, 2, 4) GDN_CASE(16, 2, 8)
+    GDN_CASE(16, 4, 1) GDN_CASE(16, 4, 2) GDN_CASE(16, 4, 4)
+    GDN_CASE(8, 1, 8)
 #endif
 #undef GDN_CASE
     return hipErrorInvalidValue;

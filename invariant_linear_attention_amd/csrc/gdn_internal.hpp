@@ -22,6 +22,7 @@ struct PrefillParams {
     int64_t total_tokens;
     int32_t n_seqs, hk, hv, dv;
     int32_t rank_by_length;  // workgroups take sequences longest first (n_seqs <= kMaxRankedSeqs)
+    int32_t tiles;           // row tiles per value head (set by the launcher)
 };
 
 // Kernel arguments of one decode step.

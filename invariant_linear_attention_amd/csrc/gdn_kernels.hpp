@@ -59,18 +59,10 @@ __device__ __forceinline__ float delta_coeff(float a, float ptil, float v, float
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t x = __float_as_uint(f);
-    if ((x & 0x7fffffffu) > 0x7f800000u) return (x >> 16) | 0x0040u;
-    x += 0x7fffu + ((x >> 16) & 1u);
-    return x >> 16;
-}
-
 // x + (x of the partner lane given by a DPP control)
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float x) {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Tree levels above the lane-local leaves, for a row held by L lanes:
@@ -191,8 +183,9 @@ struct IoBf16 {
     __device__ static float load1(const void *base, size_t idx) {
         return bf16_to_f32(static_cast<const uint16_t *>(base)[idx]);
     }
+    // Round to nearest even (v_cvt_pk_bf16_f32), the same conversion in every kernel.
     __device__ static void store1(void *base, size_t idx, float f) {
-        static_cast<uint16_t *>(base)[idx] = static_cast<uint16_t>(f32_to_bf16_rne(f));
+        static_cast<uint16_t *>(base)[idx] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
     }
 };
 
@@ -365,6 +358,42 @@ __device__ __forceinline__ int seq_by_length_rank(const int32_t *cu, int n_seqs,
     return s_pick;
 }
 
+// Which (sequence rank, value head, row tile) a prefill workgroup serves.
+//
+// Workgroups are handed to the eight XCDs round robin by id, and each XCD has its
+// own L2.  All workgroups that read the same key/query rows (the `group` of one
+// sequence and one key head: hv/hk value heads x tiles) are given ids that are
+// equal modulo 8, so they run on one XCD and read q/k from HBM once, not once per
+// XCD.  Groups are numbered rank-major, so lower ids still go to longer sequences.
+// A trailing partial round of groups (fewer than 8 left) is mapped in order.
+struct WorkItem {
+    int rank, kh, h, tile;
+};
+
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ WorkItem work_item(const PrefillParams &p, int id) {
+    const int gv = p.hv / p.hk;                 // value heads per key head
+    const int gsize = gv * p.tiles;             // workgroups per group
+    const int ngroups = p.n_seqs * p.hk;
+    const int full = (ngroups / kXcds) * kXcds * gsize;  // workgroups in whole rounds of 8 groups
+    int g, member;
+    if (id < full) {
+        const int xcd = id % kXcds, slot = id / kXcds;
+        g = (slot / gsize) * kXcds + xcd;
+        member = slot % gsize;
+    } else {
+        g = full / gsize + (id - full) / gsize;
+        member = (id - full) % gsize;
+    }
+    WorkItem w;
+    w.rank = g / p.hk;
+    w.kh = g % p.hk;
+    w.h = w.kh * gv + member / p.tiles;
+    w.tile = member % p.tiles;
+    return w;
+}
+
 #ifndef GDN_PREFILL_WAVES_PER_EU
 #define GDN_PREFILL_WAVES_PER_EU 1
 #endif
@@ -382,12 +411,11 @@ void gdn_prefill_kernel(PrefillParams p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int lam = lane % L, grp = lane / L;
     const int col0 = G::col0(lam);
-    const int h = blockIdx.y;
-    const int row0 = blockIdx.x * Sh::RW;
-    const int kh = h / (p.hv / p.hk);
+    const WorkItem wi = work_item(p, blockIdx.x);
+    const int h = wi.h, kh = wi.kh;
+    const int row0 = wi.tile * Sh::RW;
     // (ties break by index, so the ranks are a permutation and exactly one thread picks)
-    const int n = p.rank_by_length ? seq_by_length_rank(p.cu_seqlens, p.n_seqs, blockIdx.z, tid, NW * 64)
-                                   : (int)blockIdx.z;
+    const int n = p.rank_by_length ? seq_by_length_rank(p.cu_seqlens, p.n_seqs, wi.rank, tid, NW * 64) : wi.rank;
 
     // Sequence bounds, clamped into [0, T] so that a malformed cu_seqlens cannot
     // send the kernel outside the buffers.
@@ -579,8 +607,10 @@ __global__ __launch_bounds__(NW * 64) void gdn_decode_kernel(DecodeParams p) {
 template <int DK, class IO, int L, int R, int NW>
 hipError_t launch_prefill_t(const PrefillParams &p, hipStream_t s) {
     constexpr int RW = NW * (64 / L) * R;
-    dim3 grid(p.dv / RW, p.hv, p.n_seqs), block(NW * 64);
-    void *args[] = {const_cast<PrefillParams *>(&p)};
+    PrefillParams q = p;
+    q.tiles = p.dv / RW;
+    dim3 grid((unsigned)q.tiles * p.hv * p.n_seqs), block(NW * 64);
+    void *args[] = {&q};
     return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, L, R, NW>), grid, block,
                            args, 0, s);
 }

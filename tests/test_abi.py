@@ -100,10 +100,10 @@ def call_dec(lib, dims, **over):
     (dict(dk=48), 6),
     (dict(dk=256), 6),
     (dict(plan_rows=3, plan_waves=1), 6),
-    (dict(plan_rows=2, plan_waves=8), 6),
-    (dict(plan_rows=4, plan_waves=4), 6),
+    (dict(plan_lanes=4, plan_rows=2, plan_waves=8), 6),
+    (dict(plan_lanes=4, plan_rows=4, plan_waves=4), 6),
     (dict(plan_lanes=2), 6),
-    (dict(plan_lanes=16, plan_rows=4), 6),
+    (dict(plan_lanes=16, plan_rows=3), 6),
     (dict(plan_lanes=16, plan_rows=1, plan_waves=1), 6),
     (dict(dk=32, plan_lanes=8), 6),
     (dict(n_seqs=0, total_tokens=3), 2),

@@ -48,8 +48,9 @@ def test_alone_vs_in_batch(gpu):
 
 
 PLANS = [(4, 1, 1), (4, 1, 2), (4, 1, 4), (4, 2, 1), (4, 2, 2), (4, 2, 4), (4, 4, 1), (4, 4, 2),
-         (8, 1, 1), (8, 1, 2), (8, 1, 4), (8, 2, 1), (8, 2, 2), (8, 2, 4),
-         (16, 1, 2), (16, 1, 4), (16, 2, 1), (16, 2, 2), (16, 2, 4), (0, 0, 0)]
+         (8, 1, 1), (8, 1, 2), (8, 1, 4), (8, 1, 8), (8, 2, 1), (8, 2, 2), (8, 2, 4),
+         (16, 1, 2), (16, 1, 4), (16, 2, 1), (16, 2, 2), (16, 2, 4), (16, 2, 8),
+         (16, 4, 1), (16, 4, 2), (16, 4, 4), (0, 0, 0)]
 
 
 def test_every_launch_shape_gives_the_same_bits(gpu):
