@@ -16,7 +16,8 @@ Also reported on the same line:
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample;
   parity        the timed outputs re-checked against the oracle (sampled heads).
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 50] [--no-cpu]
+(the warm-up also lets the GPU clock settle: the first ~20 launches run up to 25% slower)
 """
 import argparse
 import hashlib
@@ -110,7 +111,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="host time spent on the CPU oracle baseline")

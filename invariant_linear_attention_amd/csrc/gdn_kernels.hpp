@@ -20,7 +20,8 @@
 //     leaves, in the leaf order m = l * (leaves per l) + s: pairs (2i, 2i+1) first,
 //     then pairs of pairs, and so on.
 //   * Per token, with ptil = S_{t-1} . k_t (that tree):
-//         a = 2^(g * log2 e) (hardware exp2),  p = a * ptil,  u = beta * (v_j - p)
+//         a = 2^(g * log2 e) (hardware exp2),  ab = a * beta,  bv = beta * v_j
+//         u = fma(-ab, ptil, bv)                 (= beta (v_j - a ptil))
 //         S[i] = fma(a, S[i], u * k_t[i])        for every column i
 //         o_j  = S_t . q_t                       (the same tree)
 //     and in prefill the next token's ptil = S_t . k_{t+1} is formed in the same
@@ -51,11 +52,12 @@ __device__ __forceinline__ float decay_factor(float g) {
     return __builtin_amdgcn_exp2f(g * 1.44269504088896340736f);
 }
 
-// u_j = beta * (v_j - a * ptil_j): the delta-rule write coefficient.
-__device__ __forceinline__ float delta_coeff(float a, float ptil, float v, float beta) {
-    const float p = a * ptil;
-    return beta * (v - p);
-}
+// The delta-rule write coefficient u_j = beta (v_j - a ptil_j), evaluated as
+// fma(-ab, ptil_j, bv_j) with ab = a * beta (once per token and head) and
+// bv_j = beta * v_j (once per token and row, when v is staged).
+__device__ __forceinline__ float scaled_decay(float a, float beta) { return a * beta; }
+__device__ __forceinline__ float scaled_value(float beta, float v) { return beta * v; }
+__device__ __forceinline__ float delta_coeff(float ab, float ptil, float bv) { return __builtin_fmaf(-ab, ptil, bv); }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -220,7 +222,7 @@ struct PrefillShape {
     static constexpr int KSLOTS = (KITEMS + NT - 1) / NT;
     static constexpr int VSLOTS = (VITEMS + NT - 1) / NT;
     static constexpr int TT = L / R;                 // tokens buffered per output store
-    static_assert(2 * TS <= NT, "gate/beta staging needs 2*(TB+1) threads");
+    static_assert(TS <= NT, "gate/beta staging needs TB+1 threads");
     static_assert(RW % IO::VEC == 0, "row slice must be whole vectors");
     static_assert(TB % TT == 0, "output flushes must align with token blocks");
 };
@@ -230,9 +232,9 @@ struct alignas(16) PrefillLds {
     using Sh = PrefillShape<DK, IO, L, R, NW>;
     float k[2][Sh::TS][DK];   // key rows, fp32, chunks permuted by Geo::lds_chunk
     float q[2][Sh::TS][DK];   // query rows, same layout
-    float v[2][Sh::TS][Sh::RW];
-    float a[2][Sh::TS];       // decay factors exp(g)
-    float b[2][Sh::TS];       // beta
+    float v[2][Sh::TS][Sh::RW];  // beta * v
+    float a[2][Sh::TS];          // decay factors exp(g)
+    float ab[2][Sh::TS];         // a * beta
 };
 
 // Global -> register stage of one token block (issued early), then register -> LDS.
@@ -243,7 +245,8 @@ struct Stager {
     uint4 kr[Sh::KSLOTS];
     uint4 qr[Sh::KSLOTS];
     uint4 vr[Sh::VSLOTS];
-    float gb;
+    float vbeta[Sh::VSLOTS];  // beta of each staged value vector's token
+    float gt, bt;             // g and beta of token tid (tid < TS)
 
     __device__ __forceinline__ void load(const PrefillParams &p, int64_t t0, int64_t te, int kh, int h, int row0,
                                          int tid) {
@@ -270,15 +273,18 @@ struct Stager {
             const int ti = it / Sh::VVEC, vec = it % Sh::VVEC;
             const int64_t t = t0 + ti;
             vr[s] = zero;
-            if (it < Sh::VITEMS && t < te)
+            vbeta[s] = 0.f;
+            if (it < Sh::VITEMS && t < te) {
                 vr[s] = *reinterpret_cast<const uint4 *>(
                     vb + ((size_t)(t * p.hv + h) * p.dv + row0 + (size_t)vec * IO::VEC) * IO::ESZ);
+                vbeta[s] = p.beta[t * p.hv + h];
+            }
         }
-        gb = 0.f;
-        if (tid < 2 * Sh::TS) {
-            const int ti = tid % Sh::TS;
-            const int64_t t = t0 + ti;
-            if (t < te) gb = (tid < Sh::TS) ? p.g[t * p.hv + h] : p.beta[t * p.hv + h];
+        gt = 0.f;
+        bt = 0.f;
+        if (tid < Sh::TS && t0 + tid < te) {
+            gt = p.g[(t0 + tid) * p.hv + h];
+            bt = p.beta[(t0 + tid) * p.hv + h];
         }
     }
 
@@ -312,15 +318,18 @@ struct Stager {
                 float f[IO::VEC];
                 IO::unpack(vr[s], f);
 #pragma unroll
+                for (int x = 0; x < IO::VEC; ++x) f[x] = scaled_value(vbeta[s], f[x]);
+#pragma unroll
                 for (int x = 0; x < IO::VEC; x += 4)
                     *reinterpret_cast<float4 *>(&Ld.v[buf][ti][vec * IO::VEC + x]) =
                         make_float4(f[x], f[x + 1], f[x + 2], f[x + 3]);
             }
         }
-        if (tid < Sh::TS)
-            Ld.a[buf][tid] = decay_factor(gb);
-        else if (tid < 2 * Sh::TS)
-            Ld.b[buf][tid - Sh::TS] = gb;
+        if (tid < Sh::TS) {
+            const float a = decay_factor(gt);
+            Ld.a[buf][tid] = a;
+            Ld.ab[buf][tid] = scaled_decay(a, bt);
+        }
     }
 };
 
@@ -329,8 +338,8 @@ struct Stager {
 template <int C, int R>
 struct TokRegs {
     float k[C];
-    float v[R];
-    float a, beta;
+    float bv[R];  // beta * v of this lane's rows
+    float a, ab;  // exp(g), exp(g) * beta
 };
 
 // Work order.  Workgroups start in blockIdx order and the sequence walk is serial,
@@ -460,9 +469,9 @@ void gdn_prefill_kernel(PrefillParams p) {
         auto fetch = [&](TokRegs<C, R> &X, int buf, int ti) {
             read_cols(X.k, Ld.k[buf][ti]);
 #pragma unroll
-            for (int r = 0; r < R; ++r) X.v[r] = Ld.v[buf][ti][wrow + RG * r];
+            for (int r = 0; r < R; ++r) X.bv[r] = Ld.v[buf][ti][wrow + RG * r];
             X.a = Ld.a[buf][ti];
-            X.beta = Ld.b[buf][ti];
+            X.ab = Ld.ab[buf][ti];
         };
 
         // Outputs are kept in registers and stored TT tokens at a time: lane lam
@@ -484,9 +493,12 @@ void gdn_prefill_kernel(PrefillParams p) {
 
             // cur holds token ti; nxt receives token ti + 1 (staged row ti + 1 <= TB).
             auto step = [&](TokRegs<C, R> &cur, TokRegs<C, R> &nxt, int ti) {
+#ifdef GDN_TOKEN_SCHED_FENCE
+                __builtin_amdgcn_sched_barrier(0);
+#endif
                 float u[R], o[R];
 #pragma unroll
-                for (int r = 0; r < R; ++r) u[r] = delta_coeff(cur.a, ptil[r], cur.v[r], cur.beta);
+                for (int r = 0; r < R; ++r) u[r] = delta_coeff(cur.ab, ptil[r], cur.bv[r]);
                 float qc[C];
                 read_cols(qc, Ld.q[buf][ti]);
                 fetch(nxt, buf, ti + 1);
@@ -581,11 +593,12 @@ __global__ __launch_bounds__(NW * 64) void gdn_decode_kernel(DecodeParams p) {
     }
     const float a = decay_factor(p.g[(size_t)b * p.hv + h]);
     const float beta = p.beta[(size_t)b * p.hv + h];
+    const float ab = scaled_decay(a, beta);
 
     float ptil[R], u[R], o[R];
     row_dots<DK, L, R>(S, kx, ptil);
 #pragma unroll
-    for (int r = 0; r < R; ++r) u[r] = delta_coeff(a, ptil[r], IO::load1(p.v, orow + RG * r), beta);
+    for (int r = 0; r < R; ++r) u[r] = delta_coeff(ab, ptil[r], scaled_value(beta, IO::load1(p.v, orow + RG * r)));
     update_sweep<DK, L, R, false>(S, kx, qx, kx, a, u, o, ptil);
 
 #pragma unroll
