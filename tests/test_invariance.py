@@ -228,3 +228,40 @@ def test_long_context_chunked_8x8192(gpu):
     oc, sc = _chunked(gpu, w, list(range(0, 65536 + 1, 8192)), d=d)
     say("long context: chunked equal = %s" % (bit_equal(o, oc) and bit_equal(s, sc)))
     assert bit_equal(o, oc) and bit_equal(s, sc)
+
+
+@pytest.mark.parametrize("dk,dv,io", [(16, 16, torch.float32), (16, 48, torch.bfloat16), (32, 32, torch.bfloat16),
+                                      (64, 64, torch.float32), (64, 128, torch.bfloat16), (128, 128, torch.float32)])
+def test_decode_equals_prefill_every_head_dim(gpu, dk, dv, io):
+    """For every supported key dim and io dtype: prefill 20 tokens, then decode 3
+    steps; each step's output and the final state equal a 23-token prefill."""
+    w = synth.make_workload(21, [23, 23], hk=2, hv=4, dk=dk, dv=dv, io_dtype=io, h0_std=0.1)
+    o_full, s_full = run_prefill(gpu, w)
+    d = to_dev(w)
+    idx_pre = torch.cat([torch.arange(23 * n, 23 * n + 20) for n in range(2)]).to(DEV)
+    cu_pre = torch.tensor([0, 20, 40], dtype=torch.int32, device=DEV)
+    _, pool = gpu.gdn_fwd_varlen(d["q"][idx_pre].contiguous(), d["k"][idx_pre].contiguous(),
+                                 d["v"][idx_pre].contiguous(), d["g"][idx_pre].contiguous(),
+                                 d["beta"][idx_pre].contiguous(), d["h0"], cu_pre)
+    for t in range(20, 23):
+        rows = torch.tensor([t, 23 + t], device=DEV)
+        o = gpu.gdn_decode_step(d["q"][rows].contiguous(), d["k"][rows].contiguous(), d["v"][rows].contiguous(),
+                                d["g"][rows].contiguous(), d["beta"][rows].contiguous(), pool)
+        torch.cuda.synchronize()
+        assert bit_equal(o, o_full[rows]), "dk=%d step %d output" % (dk, t)
+    assert bit_equal(pool, s_full), "dk=%d final state" % dk
+
+
+def test_all_empty_batch_with_null_inputs(gpu):
+    """T = 0 with sequences present: q/k/v/g/beta/out may be NULL; hT = h0."""
+    h0 = torch.randn((3, 4, 128, 128), device=DEV)
+    hT = torch.empty_like(h0)
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    dims = gpu.GdnDims(n_seqs=3, hk=2, hv=4, dk=128, dv=128, io_dtype=gpu.GDN_BF16, total_tokens=0,
+                       pool_size=0, plan_lanes=0, plan_rows=0, plan_waves=0, reserved=0)
+    import ctypes
+    lib = gpu.load_library()
+    rc = lib.gdn_fwd_varlen(ctypes.byref(dims), None, None, None, None, None, h0.data_ptr(), cu.data_ptr(),
+                            None, hT.data_ptr(), None)
+    torch.cuda.synchronize()
+    assert rc == 0 and bit_equal(hT, h0)
