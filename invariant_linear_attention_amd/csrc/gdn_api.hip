@@ -46,9 +46,9 @@ bool plan_fits(int dk, int dv, bool decode, int io, Plan plan) {
 }
 
 // Automatic launch shape.  Rows are independent, so this only trades per-wave
-// efficiency against parallelism.  Measured on MI355X (dk = dv = 128, bf16): 16
-// lanes x 2 rows per lane is fastest when the batch has rows to spare, then 8
-// lanes x 1 row; when rows are scarce (one long sequence) 16 lanes x 1 row puts
+// efficiency against parallelism.  Measured on MI355X (dk = dv = 128, bf16): 8
+// lanes x 1 row per lane is fastest when the batch has rows to spare, then 16
+// lanes x 2 rows; when rows are scarce (one long sequence) 16 lanes x 1 row puts
 // the most waves on the chip.  Other head dims use 4 lanes per row.
 constexpr int64_t kWavesWanted = 4096;  // four per SIMD: lets longest-first ordering balance the tail
 
@@ -59,7 +59,7 @@ Plan auto_plan(int dk, int dv, bool decode, int io, int64_t units) {
             if (plan_fits(dk, dv, true, io, pl)) return pl;
         return Plan{4, 1, 1};
     }
-    const Plan prefer[] = {Plan{16, 2, 4}, Plan{8, 1, 4}, Plan{16, 1, 4}, Plan{8, 1, 2}, Plan{4, 1, 4},
+    const Plan prefer[] = {Plan{8, 1, 4}, Plan{16, 2, 4}, Plan{16, 1, 4}, Plan{8, 1, 2}, Plan{4, 1, 4},
                            Plan{4, 1, 2}, Plan{4, 1, 1}, Plan{16, 1, 2}, Plan{8, 1, 1}};
     Plan best{0, 0, 0};
     int64_t best_waves = -1;

@@ -222,6 +222,9 @@ struct PrefillShape {
     static constexpr int KSLOTS = (KITEMS + NT - 1) / NT;
     static constexpr int VSLOTS = (VITEMS + NT - 1) / NT;
     static constexpr int TT = L / R;                 // tokens buffered per output store
+    // Guards between token steps of full blocks: 1 = every token, 2 = every pair,
+    // 0 = none.  Chosen per shape from measurements on MI355X.
+    static constexpr int GUARD = (L == 16) ? (R == 1 ? 2 : 0) : 1;
     static_assert(TS <= NT, "gate/beta staging needs TB+1 threads");
     static_assert(RW % IO::VEC == 0, "row slice must be whole vectors");
     static_assert(TB % TT == 0, "output flushes must align with token blocks");
@@ -512,23 +515,46 @@ void gdn_prefill_kernel(PrefillParams p) {
                     IO::store1(p.out, (size_t)(t0 + ti - (TT - 1) + my_slot) * p.hv * p.dv + out_row, obuf);
             };
 
-            if (nt == TB) {
+            // Full token blocks are fully unrolled.  The last block of a sequence
+            // may be partial; uniform guards skip its missing tokens.  Where guards
+            // also sit between steps of full blocks they bound how far the compiler
+            // hoists work across tokens, which trades some in-wave overlap for fewer
+            // registers (more waves per SIMD); the best trade depends on the shape
+            // (measured on MI355X), see Sh::GUARD.
+            if constexpr (Sh::GUARD == 0) {
+                if (nt == TB) {
+#pragma unroll
+                    for (int ti = 0; ti < TB; ti += 2) {
+                        step(A, B, ti);
+                        step(B, A, ti + 1);
+                    }
+                } else {
+#pragma unroll
+                    for (int ti = 0; ti < TB; ti += 2) {
+                        if (ti < nt) step(A, B, ti);
+                        if (ti + 1 < nt) step(B, A, ti + 1);
+                    }
+                }
+            } else if constexpr (Sh::GUARD == 2) {
 #pragma unroll
                 for (int ti = 0; ti < TB; ti += 2) {
-                    step(A, B, ti);
-                    step(B, A, ti + 1);
+                    if (ti + 1 < nt) {
+                        step(A, B, ti);
+                        step(B, A, ti + 1);
+                    } else if (ti < nt) {
+                        step(A, B, ti);
+                    }
                 }
             } else {
-                int ti = 0;
-                for (; ti + 1 < nt; ti += 2) {
-                    step(A, B, ti);
-                    step(B, A, ti + 1);
+#pragma unroll
+                for (int ti = 0; ti < TB; ti += 2) {
+                    if (ti < nt) step(A, B, ti);
+                    if (ti + 1 < nt) step(B, A, ti + 1);
                 }
-                if (ti < nt) step(A, B, ti);
-                const int rem = nt % TT;  // tokens kept but not yet stored
-                if (rem != 0 && my_slot < rem)
-                    IO::store1(p.out, (size_t)(t0 + nt - rem + my_slot) * p.hv * p.dv + out_row, obuf);
             }
+            const int rem = nt % TT;  // tokens kept but not yet stored (partial block only)
+            if (rem != 0 && my_slot < rem)
+                IO::store1(p.out, (size_t)(t0 + nt - rem + my_slot) * p.hv * p.dv + out_row, obuf);
 
             if (blk + 1 < nblk) st.store(Ld, buf ^ 1, tid);
             __syncthreads();
