@@ -132,13 +132,22 @@ gdn_status gdn_decode_step(const gdn_dims *dims,
                            float *state_pool, const int32_t *state_idx,
                            void *out, void *stream);
 
+/*
+ * Launch shape query (host only: no device memory is read and nothing is enqueued).
+ * Runs the same dimension checks and launch planning as gdn_fwd_varlen (decode = 0)
+ * or gdn_decode_step (decode != 0) for *dims, and on GDN_OK writes the shape that
+ * call would use to shape[0..2] = {lanes per state row, rows per lane, waves per
+ * workgroup}.  Pointer checks are not part of it.  shape may not be NULL.
+ */
+gdn_status gdn_query_plan(const gdn_dims *dims, int32_t decode, int32_t *shape);
+
 /* Human-readable name of a status code (static storage). */
 const char *gdn_status_string(gdn_status status);
 
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 101
+#define GDN_ABI_VERSION 102
 
 #ifdef __cplusplus
 }

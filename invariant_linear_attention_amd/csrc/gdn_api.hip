@@ -49,13 +49,17 @@ bool plan_fits(int dk, int dv, bool decode, int io, Plan plan) {
 // efficiency against parallelism.  Measured on MI355X (dk = dv = 128, bf16): 8
 // lanes x 1 row per lane is fastest when the batch has rows to spare, then 16
 // lanes x 2 rows; when rows are scarce (one long sequence) 16 lanes x 1 row puts
-// the most waves on the chip.  Other head dims use 4 lanes per row.
+// the most waves on the chip.  Smaller heads take the same order over the shapes
+// compiled for them (dk = 64: 8 or 4 lanes per row; dk = 16, 32: 4).
 constexpr int64_t kWavesWanted = 4096;  // four per SIMD: lets longest-first ordering balance the tail
 
 Plan auto_plan(int dk, int dv, bool decode, int io, int64_t units) {
     const int64_t rows_total = units * dv;
     if (decode) {
-        for (Plan pl : {Plan{4, 2, 4}, Plan{4, 2, 2}, Plan{4, 1, 4}, Plan{4, 1, 2}, Plan{4, 1, 1}})
+        // One row per lane and one wave per workgroup: the state stream is the whole
+        // cost, and this shape measured fastest at B = 64 and 256 and gives small
+        // batches the most workgroups.
+        for (Plan pl : {Plan{4, 1, 1}, Plan{4, 1, 2}, Plan{4, 2, 1}})
             if (plan_fits(dk, dv, true, io, pl)) return pl;
         return Plan{4, 1, 1};
     }
@@ -89,11 +93,17 @@ gdn_status check_common(const gdn_dims *d) {
 
 gdn_status resolve_plan(const gdn_dims *d, bool decode, int64_t units, Plan *plan) {
     const Plan a = auto_plan(d->dk, d->dv, decode, d->io_dtype, units);
+    if (d->plan_lanes == 0 && d->plan_rows == 0 && d->plan_waves == 0) {
+        if (!plan_fits(d->dk, d->dv, decode, d->io_dtype, a)) return GDN_ERR_UNSUPPORTED;
+        *plan = a;
+        return GDN_OK;
+    }
+    // Partly pinned: fill the free fields from the automatic shape where it fits.
     Plan p{d->plan_lanes ? d->plan_lanes : (decode ? 4 : a.lanes), d->plan_rows ? d->plan_rows : a.rows,
            d->plan_waves};
     if (d->plan_rows == 0 && !plan_fits(d->dk, d->dv, decode, d->io_dtype, Plan{p.lanes, p.rows, 1})) p.rows = 1;
     if (p.waves == 0) {
-        for (int w : {4, 2, 1, 8})
+        for (int w : {a.waves, 4, 2, 1, 8})
             if (plan_fits(d->dk, d->dv, decode, d->io_dtype, Plan{p.lanes, p.rows, w})) {
                 p.waves = w;
                 break;
@@ -218,6 +228,20 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k, c
     p.batch = (int32_t)B; p.hk = d.hk; p.hv = d.hv; p.dv = d.dv; p.pool_size = d.pool_size;
     const hipError_t e = dispatch_decode(d.dk, p, d.io_dtype, plan, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_query_plan(const gdn_dims *dims, int32_t decode, int32_t *shape) {
+    using namespace gdn;
+    if (!shape) return GDN_ERR_NULL;
+    const gdn_status st = check_common(dims);
+    if (st != GDN_OK) return st;
+    Plan plan;
+    const gdn_status sp = resolve_plan(dims, decode != 0, (int64_t)dims->n_seqs * dims->hv, &plan);
+    if (sp != GDN_OK) return sp;
+    shape[0] = plan.lanes;
+    shape[1] = plan.rows;
+    shape[2] = plan.waves;
+    return GDN_OK;
 }
 
 const char *gdn_status_string(gdn_status status) {

@@ -19,7 +19,7 @@ STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
     5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_HIP",
 }
-EXPORTS = ("gdn_fwd_varlen", "gdn_decode_step", "gdn_status_string", "gdn_abi_version")
+EXPORTS = ("gdn_fwd_varlen", "gdn_decode_step", "gdn_query_plan", "gdn_status_string", "gdn_abi_version")
 
 
 class GdnDims(ctypes.Structure):
@@ -57,6 +57,8 @@ def load_library(path: str = LIBRARY):
         lib.gdn_fwd_varlen.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdn_query_plan.restype = ctypes.c_int
+        lib.gdn_query_plan.argtypes = [ctypes.POINTER(GdnDims), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_abi_version.restype = ctypes.c_int32
@@ -118,6 +120,14 @@ def make_dims(q, v, n_seqs: int, total_tokens: int, pool_size: int = 0, plan=(0,
                    dv=int(v.shape[2]), io_dtype=_io_code(q), total_tokens=int(total_tokens),
                    pool_size=int(pool_size), plan_lanes=plan[0], plan_rows=plan[1], plan_waves=plan[2],
                    reserved=0)
+
+
+def gdn_query_plan(dims: GdnDims, decode: bool = False) -> Tuple[int, int, int]:
+    """(lanes per row, rows per lane, waves per workgroup) that gdn_fwd_varlen
+    (or gdn_decode_step when ``decode``) would launch for ``dims``.  Host only."""
+    shape = (ctypes.c_int32 * 3)()
+    _check(load_library().gdn_query_plan(ctypes.byref(dims), int(bool(decode)), shape))
+    return tuple(int(x) for x in shape)
 
 
 def gdn_fwd_varlen(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, stream=None, plan=(0, 0, 0),

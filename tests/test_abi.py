@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"gdn_fwd_varlen", "gdn_decode_step", "gdn_status_string", "gdn_abi_version"}
+    assert set(names) == {"gdn_fwd_varlen", "gdn_decode_step", "gdn_query_plan", "gdn_status_string",
+                          "gdn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -154,3 +155,57 @@ def test_decode_rejects(lib, case, over, code):
 
 def test_decode_zero_batch_is_a_noop(lib):
     assert call_dec(lib, _dims(n_seqs=0, total_tokens=0, pool_size=4)) == 0
+
+
+# ------------------------------------------------------------- launch planning
+
+def _plan(decode=False, **kw):
+    from invariant_linear_attention_amd import gdn
+    return gdn.gdn_query_plan(_dims(**kw), decode)
+
+
+def test_plan_benchmark_batch():
+    # 8 sequences x 32 value heads x 128 rows: enough rows for 8 lanes x 1 row, 4 waves
+    assert _plan(n_seqs=8, hk=16, hv=32, total_tokens=17459) == (8, 1, 4)
+
+
+def test_plan_single_long_sequence():
+    # one sequence, 32 heads: rows are scarce, 16 lanes per row spread them widest
+    assert _plan(n_seqs=1, hk=16, hv=32, total_tokens=65536) == (16, 1, 4)
+
+
+@pytest.mark.parametrize("B", [1, 8, 64, 256])
+def test_plan_decode(B):
+    assert _plan(decode=True, n_seqs=B, hk=16, hv=32, total_tokens=B, pool_size=B) == (4, 1, 1)
+
+
+@pytest.mark.parametrize("dk,lanes", [(16, 4), (32, 4), (64, 8)])
+def test_plan_smaller_heads(dk, lanes):
+    # a lane holds at least 4 columns (dk = 16, 32: 4 lanes per row; dk = 64: 8)
+    got = _plan(n_seqs=8, dk=dk, dv=64, total_tokens=100)
+    assert got[0] == lanes and (64 // got[0]) * got[1] * got[2] <= 64
+
+
+def test_plan_pinned_fields_are_kept():
+    assert _plan(plan_lanes=16, plan_rows=2, plan_waves=8) == (16, 2, 8)
+    assert _plan(plan_lanes=4)[0] == 4
+    lanes, rows, waves = _plan(plan_waves=2)
+    assert waves == 2
+    assert _plan(decode=True, plan_rows=2, total_tokens=2, pool_size=2)[:2] == (4, 2)
+
+
+def test_plan_rejects_like_the_entry_points():
+    from invariant_linear_attention_amd import gdn
+    with pytest.raises(gdn.GdnError) as e:
+        _plan(plan_lanes=16, plan_rows=3)
+    assert e.value.code == 6
+    with pytest.raises(gdn.GdnError) as e:
+        _plan(dk=48)
+    assert e.value.code == 6
+    with pytest.raises(gdn.GdnError) as e:
+        _plan(reserved=1)
+    assert e.value.code == 2
+
+
+def test_plan_null_shape(lib):
+    assert lib.gdn_query_plan(ctypes.byref(_dims()), 0, None) == 1
