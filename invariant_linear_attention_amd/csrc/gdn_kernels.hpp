@@ -147,7 +147,14 @@ __device__ __forceinline__ void row_dots(const float (&S)[R][C], const float (&x
 //   S[r][i] = fma(a, S[r][i], u[r] * kc[i])  for all i, then o[r] = S[r] . qc,
 // then, when NEXT, ptil[r] = S[r] . kn (the next token's key).  Doing the whole
 // update before the read-outs gives the query and next-key loads time to land.
-template <int DK, int L, int R, bool NEXT, int C>
+//
+// TIED writes each new state element into the register of the old one (a
+// three-address v_fma_f32 with its result tied to S).  Left to itself the compiler
+// uses the two-address v_fmac_f32, whose result lands in the product's register;
+// where a uniform branch follows every token, the state must then be copied back
+// at each join, 16 moves per token for 16 columns per lane.  Same instruction,
+// same rounding, same bits: only the register assignment differs.
+template <int DK, int L, int R, bool NEXT, bool TIED = false, int C>
 __device__ __forceinline__ void update_sweep(float (&S)[R][C], const float (&kc)[C], const float (&qc)[C],
                                              const float (&kn)[C], float a, const float (&u)[R], float (&o)[R],
                                              float (&ptil)[R]) {
@@ -156,7 +163,10 @@ __device__ __forceinline__ void update_sweep(float (&S)[R][C], const float (&kc)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const float w = u[r] * kc[i];
-            S[r][i] = __builtin_fmaf(a, S[r][i], w);
+            if constexpr (TIED)
+                asm("v_fma_f32 %0, %1, %0, %2" : "+v"(S[r][i]) : "v"(a), "v"(w));
+            else
+                S[r][i] = __builtin_fmaf(a, S[r][i], w);
         }
     }
     row_dots<DK, L, R>(S, qc, o);
@@ -224,7 +234,11 @@ struct PrefillShape {
     static constexpr int TT = L / R;                 // tokens buffered per output store
     // Guards between token steps of full blocks: 1 = every token, 2 = every pair,
     // 0 = none.  Chosen per shape from measurements on MI355X.
+#ifdef GDN_PREFILL_GUARD
+    static constexpr int GUARD = GDN_PREFILL_GUARD;
+#else
     static constexpr int GUARD = (L == 16) ? (R == 1 ? 2 : 0) : 1;
+#endif
     static_assert(TS <= NT, "gate/beta staging needs TB+1 threads");
     static_assert(RW % IO::VEC == 0, "row slice must be whole vectors");
     static_assert(TB % TT == 0, "output flushes must align with token blocks");
@@ -505,7 +519,7 @@ void gdn_prefill_kernel(PrefillParams p) {
                 float qc[C];
                 read_cols(qc, Ld.q[buf][ti]);
                 fetch(nxt, buf, ti + 1);
-                update_sweep<DK, L, R, true>(S, cur.k, qc, nxt.k, cur.a, u, o, ptil);
+                update_sweep<DK, L, R, true, Sh::GUARD == 1>(S, cur.k, qc, nxt.k, cur.a, u, o, ptil);
                 float ov = o[0];
 #pragma unroll
                 for (int r = 1; r < R; ++r)
