@@ -11,12 +11,16 @@ Also reported on the same line:
                 token and value head: decay, key read-out, rank-1 write, query
                 read-out), from per-launch HIP events on the launch stream;
   decode        one decode step at B = 64 and 256 against the HBM peak (state
-                read + written in place), rotating over state pools of >= 1 GiB
-                so the 256 MB Infinity Cache cannot hold them;
+                read + written in place), and its latency at B = 1 and 8, rotating
+                over state pools of >= 1 GiB so the 256 MB Infinity Cache cannot
+                hold them;
+  workloads     the same prefill kernel on the 65,536-token sequence (whole, and
+                as 8 chunks of 8,192 carried in place through the state) and on
+                the 64-sequence mixed batch, against the same fp32 roofline;
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample;
   parity        the timed outputs re-checked against the oracle (sampled heads).
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 50] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 50] [--no-cpu] [--no-decode] [--no-workloads]
 (the warm-up also lets the GPU clock settle: the first ~20 launches run up to 25% slower)
 """
 import argparse
@@ -74,6 +78,17 @@ def time_launches(fn, steps, warmup, stream):
     return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def rel(x, r):
     import numpy as np
     x = np.asarray(x, dtype=np.float64)
@@ -114,6 +129,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the long-context and mixed-batch lines")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="host time spent on the CPU oracle baseline")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="no timing: one copy of a known size (counter calibration), then one launch each of the "
@@ -177,7 +193,7 @@ def main():
     decode = None
     if not args.no_decode:
         decode = {}
-        for B in (64, 256):
+        for B in (1, 8, 64, 256):
             bytes_state = B * 32 * 128 * 128 * 4
             n_pools = max(4, int(np.ceil((1 << 30) / bytes_state)))
             pools = [torch.randn((B, 32, 128, 128), device=dev) * 0.1 for _ in range(n_pools)]
@@ -193,6 +209,7 @@ def main():
             ms_d = float(np.mean(per_d))
             alg_bytes = B * (2 * 32 * 128 * 128 * 4 + 24832)
             decode["B%d" % B] = {"tokens_per_s": B / (ms_d / 1e3), "launch_ms_mean": ms_d,
+                                 "latency_us_median": float(np.median(per_d)) * 1e3,
                                  "launch_ms_median": float(np.median(per_d)),
                                  "roofline": {"bound": "hbm", "achieved": alg_bytes / (ms_d / 1e3) / 1e9,
                                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -201,6 +218,49 @@ def main():
                                               "bytes_per_launch": alg_bytes},
                                  "state_pools": n_pools}
             del pools
+
+    # ------------------------------------------------ other prefill workloads
+    workloads = None
+    if not args.no_workloads:
+        workloads = {}
+
+        def prefill_line(name, wl, chunks=1):
+            Tw = wl.total_tokens
+            dd = [t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta)]
+            cu = wl.cu_seqlens.to(dev)
+            outw = torch.empty((Tw, 32, 128), dtype=torch.bfloat16, device=dev)
+            state = (wl.h0.to(dev) if wl.h0 is not None
+                     else torch.zeros((wl.n_seqs, 32, 128, 128), dtype=torch.float32, device=dev))
+            if chunks == 1:
+                def run(_i):
+                    gdn.gdn_fwd_varlen(*dd, state, cu, out=outw, hT=state, stream=stream)
+            else:
+                # one sequence cut into equal chunks; each launch resumes in place
+                assert wl.n_seqs == 1 and Tw % chunks == 0
+                step_len = Tw // chunks
+                cu_c = torch.tensor([0, step_len], dtype=torch.int32, device=dev)
+                views = [[t[c * step_len:(c + 1) * step_len] for t in dd] for c in range(chunks)]
+                outs = [outw[c * step_len:(c + 1) * step_len] for c in range(chunks)]
+
+                def run(_i):
+                    for c in range(chunks):
+                        gdn.gdn_fwd_varlen(*views[c], state, cu_c, out=outs[c], hT=state, stream=stream)
+            reps = max(3, min(args.steps, int(200.0 / max(Tw / 2000.0, 1.0))))
+            per_w, _ = time_launches(run, reps, 3, stream)
+            msw = float(np.median(per_w))
+            fl = 7.0 * 128 * 128 * 32 * Tw
+            workloads[name] = {"tokens": Tw, "n_seqs": wl.n_seqs, "chunks": chunks, "ms_median": msw,
+                               "tokens_per_s": Tw / (msw / 1e3),
+                               "roofline_frac": fl / (msw / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                               "plan": list(gdn.gdn_query_plan(gdn.make_dims(dd[0], dd[2], wl.n_seqs if chunks == 1 else 1,
+                                                                             Tw // chunks)))}
+            del dd, outw, state
+
+        lc = synth.long_context(1003)
+        prefill_line("long_context_65536", lc)
+        prefill_line("long_context_65536_as_8x8192", lc, chunks=8)
+        del lc
+        prefill_line("mixed_batch_64", synth.mixed_batch(1004))
 
     # ------------------------------------------------------- CPU baseline
     cpu = None
@@ -216,7 +276,7 @@ def main():
             if dt >= args.cpu_seconds:
                 break
         cpu = {"value": passes * T / dt, "unit": "tokens/s", "cores": min(threads, w.n_seqs * 32),
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(),
                "sample": "fp64 oracle, all 32 value heads of the same 8-sequence batch (%d tokens), %d pass(es) "
                          "in %.1f s" % (T, passes, dt),
                "seconds": dt}
@@ -239,6 +299,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "decode": decode,
+        "workloads": workloads,
         "parity": {"ok": parity_ok, "max_rel_err": parity},
         "kernel_source_hash": src_hash,
         "wall_s_timed": wall,

@@ -37,6 +37,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <cstddef>
 #include <stdint.h>
 
 #include "gdn_internal.hpp"
@@ -251,7 +252,7 @@ struct alignas(16) PrefillLds {
     float q[2][Sh::TS][DK];   // query rows, same layout
     float v[2][Sh::TS][Sh::RW];  // beta * v
     float a[2][Sh::TS];          // decay factors exp(g)
-    float ab[2][Sh::TS];         // a * beta
+    float ab[2][Sh::TS];         // a * beta (must follow a: read as a[buf] + 2 * TS)
 };
 
 // Global -> register stage of one token block (issued early), then register -> LDS.
@@ -483,12 +484,20 @@ void gdn_prefill_kernel(PrefillParams p) {
                 dst[4 * j + 0] = x.x; dst[4 * j + 1] = x.y; dst[4 * j + 2] = x.z; dst[4 * j + 3] = x.w;
             }
         };
+        // The decay scalars of the current buffer are read through a VGPR pointer set
+        // once per block; left alone the compiler rebuilds this uniform address (an
+        // SGPR move and an add) at every token.  ab[buf] lies 2 * TS floats past a[buf].
+        typedef __attribute__((address_space(3))) const float lds_f32;
+        using LdsT = PrefillLds<DK, IO, L, R, NW>;
+        static_assert(offsetof(LdsT, ab) == offsetof(LdsT, a) + sizeof(float) * 2 * Sh::TS, "ab follows a");
+        lds_f32 *arow = (lds_f32 *)&Ld.a[0][0];
+        asm volatile("" : "+v"(arow));
         auto fetch = [&](TokRegs<C, R> &X, int buf, int ti) {
             read_cols(X.k, Ld.k[buf][ti]);
 #pragma unroll
             for (int r = 0; r < R; ++r) X.bv[r] = Ld.v[buf][ti][wrow + RG * r];
-            X.a = Ld.a[buf][ti];
-            X.ab = Ld.ab[buf][ti];
+            X.a = arow[ti];
+            X.ab = arow[ti + 2 * Sh::TS];
         };
 
         // Outputs are kept in registers and stored TT tokens at a time: lane lam
@@ -507,6 +516,8 @@ void gdn_prefill_kernel(PrefillParams p) {
             const int64_t t0 = tb + (int64_t)blk * TB;
             if (blk + 1 < nblk) st.load(p, t0 + TB, te, kh, h, row0, tid);
             const int nt = (int)((te - t0) < TB ? (te - t0) : TB);
+            arow = (lds_f32 *)&Ld.a[buf][0];
+            asm volatile("" : "+v"(arow));
 
             // cur holds token ti; nxt receives token ti + 1 (staged row ti + 1 <= TB).
             auto step = [&](TokRegs<C, R> &cur, TokRegs<C, R> &nxt, int ti) {
