@@ -256,6 +256,30 @@ def main():
                                                                              Tw // chunks)))}
             del dd, outw, state
 
+        # The benchmark batch through the state pool with a snapshot every 256 tokens
+        # (prefix caching): 8 source slots, 8 destination slots, one slot per snapshot.
+        N, blk = w.n_seqs, 256
+        n_snap = max(w.lengths) // blk
+        pool = torch.zeros((2 * N + N * n_snap, 32, 128, 128), dtype=torch.float32, device=dev)
+        pool[:N] = d["h0"]
+        src = torch.arange(N, dtype=torch.int32, device=dev)
+        dst = torch.arange(N, 2 * N, dtype=torch.int32, device=dev)
+        snap = torch.arange(2 * N, 2 * N + N * n_snap, dtype=torch.int32, device=dev).view(N, n_snap)
+        outp = torch.empty_like(out)
+
+        def pooled(_i):
+            gdn.gdn_fwd_varlen_pool(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], pool, src_idx=src,
+                                    dst_idx=dst, snap_idx=snap, snap_block=blk, out=outp, stream=stream)
+
+        per_p, _ = time_launches(pooled, args.steps, 5, stream)
+        msp = float(np.median(per_p))
+        torch.cuda.synchronize()
+        workloads["varlen_prefill_pool_snapshots_256"] = {
+            "tokens": T, "n_seqs": N, "snapshots": int(sum(L // blk for L in w.lengths)), "ms_median": msp,
+            "tokens_per_s": T / (msp / 1e3), "roofline_frac": flops / (msp / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+            "same_bits_as_plain": bool(torch.equal(outp.view(torch.int16), out.view(torch.int16)))}
+        del pool, outp
+
         lc = synth.long_context(1003)
         prefill_line("long_context_65536", lc)
         prefill_line("long_context_65536_as_8x8192", lc, chunks=8)

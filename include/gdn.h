@@ -31,7 +31,7 @@
  *     v, out      [T][hv][dv]     io dtype
  *     g, beta     [T][hv]         fp32 (g is the log of the decay, beta the write strength)
  *     h0, hT      [N][hv][dv][dk] fp32
- *     state pool  [P][hv][dv][dk] fp32 (decode)
+ *     state pool  [P][hv][dv][dk] fp32 (decode, pooled prefill)
  *     cu_seqlens  [N+1]           int32, device memory
  *     state_idx   [B]             int32, device memory
  * All array pointers are device pointers (hipMalloc'd or equivalent), aligned to
@@ -42,7 +42,7 @@
  *
  * Errors.  Argument problems that the host can see are reported before anything
  * is enqueued; there is no fallback path and no partial mode.  Device-resident
- * index arrays (cu_seqlens, state_idx) are not read by the host: the kernels
+ * index arrays (cu_seqlens, state_idx, the pool slot arrays) are not read by the host: the kernels
  * clamp what they read so that a malformed array cannot make them access memory
  * outside the buffers described by `gdn_dims`, but the results for such input
  * are unspecified.
@@ -113,6 +113,54 @@ gdn_status gdn_fwd_varlen(const gdn_dims *dims,
                           void *out, float *hT, void *stream);
 
 /*
+ * Varlen prefill against a state pool, for prefix caching.  The state handling
+ * follows what the page "Defending Against the Training-Inference Numeric
+ * Mismatch in RL (Especially Linear Attention)" (section 3.2, "Solution") keeps
+ * from its serving stack: the recurrent state lives in a cache of slots, and in
+ * that stack's "align" cache mode the state is also saved at block-aligned
+ * token positions so that a later request sharing the prefix can resume from it.
+ *
+ * Same operation, inputs, outputs and bitwise contract as gdn_fwd_varlen; only
+ * where states come from and go to differs.  P = dims->pool_size (> 0).
+ *
+ *   state_pool   : [P][hv][dv][dk] fp32, read and written in place
+ *   src_idx      : [N] device int32, or NULL.  Sequence n starts from slot
+ *                  src_idx[n]; an entry outside [0, P) means the zero state.
+ *                  NULL means slot n (then P >= N is required).
+ *   dst_idx      : [N] device int32, or NULL.  The final state of sequence n goes
+ *                  to slot dst_idx[n]; an entry outside [0, P) means it is not
+ *                  written.  NULL means slot n (then P >= N is required).
+ *   pos0         : [N] device int32, or NULL (all 0): tokens of sequence n that
+ *                  earlier calls already processed.  Used only to place snapshots.
+ *   snap_block   : 0 (no snapshots), or a positive multiple of 16.
+ *   snap_idx     : [N][snap_per_seq] device int32 (required when snap_block > 0).
+ *                  Sequence n's snapshot j is the state after the token that brings
+ *                  its absolute position (pos0[n] + tokens done in this call) to the
+ *                  j-th multiple of snap_block above pos0[n]; it is stored to slot
+ *                  snap_idx[n * snap_per_seq + j], or skipped when that entry is
+ *                  outside [0, P) or j >= snap_per_seq.  A snapshot holds exactly
+ *                  the bits that hT would hold for a call ending at that token.
+ *   out          : [T][hv][dv] outputs, as in gdn_fwd_varlen.
+ *
+ * Slots written by a call (dst and snapshot entries) must differ from each other
+ * and from the slots other sequences of the same call read; a sequence may write
+ * the slot it reads from (in place).  These device-side conditions are not
+ * checked; breaking them gives unspecified results but no access outside the pool.
+ * Errors: as gdn_fwd_varlen, plus GDN_ERR_SHAPE for P <= 0, a bad snap_block or
+ * snap_per_seq, or NULL src_idx / dst_idx with P < N; GDN_ERR_NULL for a NULL
+ * pool, or NULL snap_idx with snap_block > 0; GDN_ERR_ALIAS when out or the pool
+ * overlaps another argument.
+ */
+gdn_status gdn_fwd_varlen_pool(const gdn_dims *dims,
+                               const void *q, const void *k, const void *v,
+                               const float *g, const float *beta,
+                               const int32_t *cu_seqlens, float *state_pool,
+                               const int32_t *src_idx, const int32_t *dst_idx,
+                               const int32_t *pos0, const int32_t *snap_idx,
+                               int32_t snap_block, int32_t snap_per_seq,
+                               void *out, void *stream);
+
+/*
  * Decode step: one token for each of B sequences, against states held in a pool
  * and updated in place.
  *
@@ -147,7 +195,7 @@ const char *gdn_status_string(gdn_status status);
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 102
+#define GDN_ABI_VERSION 103
 
 #ifdef __cplusplus
 }

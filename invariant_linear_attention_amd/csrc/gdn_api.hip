@@ -134,6 +134,23 @@ hipError_t dispatch_decode(int dk, const DecodeParams &p, int io, Plan plan, hip
 }
 
 }  // namespace
+namespace {
+
+// Planning and launch shared by both varlen entry points (arguments already checked).
+gdn_status launch_varlen(const gdn_dims *dims, PrefillParams &p, void *stream) {
+    const gdn_dims &d = *dims;
+    const int64_t T = d.total_tokens, N = d.n_seqs;
+    Plan plan;
+    const gdn_status st = resolve_plan(dims, false, N * d.hv, &plan);
+    if (st != GDN_OK) return st;
+    p.total_tokens = T; p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dv = d.dv;
+    // Longest-first ordering pays off when there are a few sequences of some length.
+    p.rank_by_length = (N > 1 && N <= kMaxRankedSeqs && T >= 32 * N) ? 1 : 0;
+    const hipError_t e = dispatch_prefill(d.dk, p, d.io_dtype, plan, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // namespace
 }  // namespace gdn
 
 extern "C" {
@@ -170,18 +187,66 @@ gdn_status gdn_fwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
         if (overlap(rhT, in)) return GDN_ERR_ALIAS;
     if (h0 && hT && h0 != hT && overlap(rh0, rhT)) return GDN_ERR_ALIAS;
 
-    Plan plan;
-    st = resolve_plan(dims, false, N * d.hv, &plan);
-    if (st != GDN_OK) return st;
-
     PrefillParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0;
     p.cu_seqlens = cu_seqlens; p.out = out; p.hT = hT;
-    p.total_tokens = T; p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dv = d.dv;
-    // Longest-first ordering pays off when there are a few sequences of some length.
-    p.rank_by_length = (N > 1 && N <= kMaxRankedSeqs && T >= 32 * N) ? 1 : 0;
-    const hipError_t e = dispatch_prefill(d.dk, p, d.io_dtype, plan, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    p.pool_size = (int32_t)N;
+    return launch_varlen(dims, p, stream);
+}
+
+gdn_status gdn_fwd_varlen_pool(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const int32_t *cu_seqlens, float *state_pool,
+                               const int32_t *src_idx, const int32_t *dst_idx, const int32_t *pos0,
+                               const int32_t *snap_idx, int32_t snap_block, int32_t snap_per_seq, void *out,
+                               void *stream) {
+    using namespace gdn;
+    gdn_status st = check_common(dims);
+    if (st != GDN_OK) return st;
+    const gdn_dims &d = *dims;
+    const int64_t T = d.total_tokens, N = d.n_seqs;
+    if (d.pool_size <= 0 || snap_block < 0 || snap_per_seq < 0) return GDN_ERR_SHAPE;
+    if (snap_block > 0 && (snap_block % kSnapshotGranule != 0 || snap_per_seq == 0)) return GDN_ERR_SHAPE;
+    if (N == 0) return T == 0 ? GDN_OK : GDN_ERR_SHAPE;
+    if (!cu_seqlens || !state_pool) return GDN_ERR_NULL;
+    if (snap_block > 0 && !snap_idx) return GDN_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL;
+
+    const uint64_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
+    const uint64_t qk_bytes = (uint64_t)T * d.hk * d.dk * esz;
+    const uint64_t vo_bytes = (uint64_t)T * d.hv * d.dv * esz;
+    const uint64_t gb_bytes = (uint64_t)T * d.hv * 4;
+    const uint64_t pool_bytes = (uint64_t)d.pool_size * d.hv * d.dv * d.dk * 4;
+    const uint64_t idx_bytes = (uint64_t)N * 4;
+
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(state_pool, 16) ||
+        !aligned(g, 4) || !aligned(beta, 4) || !aligned(cu_seqlens, 4) || !aligned(src_idx, 4) ||
+        !aligned(dst_idx, 4) || !aligned(pos0, 4) || !aligned(snap_idx, 4))
+        return GDN_ERR_ALIGN;
+
+    const Range rq = range_of(q, qk_bytes), rk = range_of(k, qk_bytes), rv = range_of(v, vo_bytes);
+    const Range rg = range_of(g, gb_bytes), rb = range_of(beta, gb_bytes);
+    const Range rp = range_of(state_pool, pool_bytes), rcu = range_of(cu_seqlens, (uint64_t)(N + 1) * 4);
+    const Range rs = range_of(src_idx, src_idx ? idx_bytes : 0), rd = range_of(dst_idx, dst_idx ? idx_bytes : 0);
+    const Range r0 = range_of(pos0, pos0 ? idx_bytes : 0);
+    const Range rn = range_of(snap_idx, snap_block > 0 ? idx_bytes * (uint64_t)snap_per_seq : 0);
+    const Range ro = range_of(out, vo_bytes);
+    for (Range in : {rq, rk, rv, rg, rb, rp, rcu, rs, rd, r0, rn})
+        if (overlap(ro, in)) return GDN_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, rg, rb, rcu, rs, rd, r0, rn})
+        if (overlap(rp, in)) return GDN_ERR_ALIAS;
+
+    PrefillParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.h0 = state_pool; p.hT = state_pool; p.snap = state_pool;
+    p.cu_seqlens = cu_seqlens; p.out = out;
+    p.src_idx = src_idx; p.dst_idx = dst_idx; p.pos0 = pos0;
+    // Without an index array the slot is the sequence index: the pool must hold them.
+    if ((!src_idx || !dst_idx) && d.pool_size < N) return GDN_ERR_SHAPE;
+    p.pool_size = d.pool_size;
+    if (snap_block > 0) {
+        p.snap_idx = snap_idx; p.snap_block = snap_block; p.snap_per_seq = snap_per_seq;
+    }
+    return launch_varlen(dims, p, stream);
 }
 
 gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,

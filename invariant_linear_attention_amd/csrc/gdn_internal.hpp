@@ -12,15 +12,31 @@ namespace gdn {
 // Largest batch whose sequences the prefill kernel orders longest first.
 constexpr int kMaxRankedSeqs = 128;
 
+// Snapshot spacing must be a multiple of this (and so of every token block, which
+// bounds snapshots to one per block).
+constexpr int kSnapshotGranule = 16;
+
 // Kernel arguments of the varlen prefill (passed by value as the kernarg segment).
+// Initial and final states are addressed by slot: slot n of h0 / hT for sequence n,
+// or, when src_idx / dst_idx are given, slot src_idx[n] / dst_idx[n] of a pool of
+// pool_size entries (a slot outside [0, pool_size) means none: zero state, or no
+// write).  Snapshots (snap_block > 0) store the state reached at every absolute
+// position that is a multiple of snap_block, counting pos0[n] tokens already
+// behind sequence n, into pool slots snap_idx[n * snap_per_seq + j].
 struct PrefillParams {
     const void *q, *k, *v;
     const float *g, *beta, *h0;
     const int32_t *cu_seqlens;
     void *out;
     float *hT;
+    const int32_t *src_idx, *dst_idx;  // null: slot = sequence index
+    const int32_t *pos0;               // null: no tokens behind any sequence
+    const int32_t *snap_idx;           // [n_seqs][snap_per_seq]
+    float *snap;                       // snapshot pool
     int64_t total_tokens;
     int32_t n_seqs, hk, hv, dv;
+    int32_t pool_size;                 // slots of h0 / hT / snap when indexed
+    int32_t snap_block, snap_per_seq;  // 0: no snapshots
     int32_t rank_by_length;  // workgroups take sequences longest first (n_seqs <= kMaxRankedSeqs)
     int32_t tiles;           // row tiles per value head (set by the launcher)
 };

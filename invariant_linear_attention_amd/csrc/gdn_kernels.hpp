@@ -266,8 +266,9 @@ struct Stager {
     float vbeta[Sh::VSLOTS];  // beta of each staged value vector's token
     float gt, bt;             // g and beta of token tid (tid < TS)
 
-    __device__ __forceinline__ void load(const PrefillParams &p, int64_t t0, int64_t te, int kh, int h, int row0,
-                                         int tid) {
+    // Rows ti = 0 .. TS-1 hold token t0 + ti; tokens outside [ts, te) are zero.
+    __device__ __forceinline__ void load(const PrefillParams &p, int64_t t0, int64_t ts, int64_t te, int kh, int h,
+                                         int row0, int tid) {
         const uint4 zero = make_uint4(0, 0, 0, 0);
         const char *kb = static_cast<const char *>(p.k);
         const char *qb = static_cast<const char *>(p.q);
@@ -279,7 +280,7 @@ struct Stager {
             const int64_t t = t0 + ti;
             kr[s] = zero;
             qr[s] = zero;
-            if (it < Sh::KITEMS && t < te) {
+            if (it < Sh::KITEMS && t >= ts && t < te) {
                 const size_t off = ((size_t)(t * p.hk + kh) * DK + (size_t)vec * IO::VEC) * IO::ESZ;
                 kr[s] = *reinterpret_cast<const uint4 *>(kb + off);
                 qr[s] = *reinterpret_cast<const uint4 *>(qb + off);
@@ -292,7 +293,7 @@ struct Stager {
             const int64_t t = t0 + ti;
             vr[s] = zero;
             vbeta[s] = 0.f;
-            if (it < Sh::VITEMS && t < te) {
+            if (it < Sh::VITEMS && t >= ts && t < te) {
                 vr[s] = *reinterpret_cast<const uint4 *>(
                     vb + ((size_t)(t * p.hv + h) * p.dv + row0 + (size_t)vec * IO::VEC) * IO::ESZ);
                 vbeta[s] = p.beta[t * p.hv + h];
@@ -300,7 +301,7 @@ struct Stager {
         }
         gt = 0.f;
         bt = 0.f;
-        if (tid < Sh::TS && t0 + tid < te) {
+        if (tid < Sh::TS && t0 + tid >= ts && t0 + tid < te) {
             gt = p.g[(t0 + tid) * p.hv + h];
             bt = p.beta[(t0 + tid) * p.hv + h];
         }
@@ -425,8 +426,10 @@ __device__ __forceinline__ WorkItem work_item(const PrefillParams &p, int id) {
 #define GDN_PREFILL_WAVES_PER_EU 1
 #endif
 
-// One workgroup = (sequence n = blockIdx.z, value head h = blockIdx.y, row tile blockIdx.x).
-template <int DK, class IO, int L, int R, int NW>
+// One workgroup = (sequence, value head, row tile), from blockIdx.x (see work_item).
+// SNAP compiles the snapshot support (block grid aligned to absolute positions);
+// without it the token loop carries none of that logic.
+template <int DK, class IO, int L, int R, int NW, bool SNAP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GDN_PREFILL_WAVES_PER_EU)))
 void gdn_prefill_kernel(PrefillParams p) {
     using Sh = PrefillShape<DK, IO, L, R, NW>;
@@ -453,23 +456,65 @@ void gdn_prefill_kernel(PrefillParams p) {
 
     // This lane's rows inside the tile: wrow + RG * r.
     const int wrow = wave * RG * R + grp;
-    const size_t state_row0 = ((size_t)n * p.hv + h) * p.dv + row0 + wrow;
+    // Element offset of this lane's first state row within state slot `slot`.
+    auto state_at = [&](int64_t slot) -> size_t {
+        return (((size_t)slot * p.hv + h) * p.dv + row0 + wrow) * DK + col0;
+    };
+    auto slot_of = [&](const int32_t *idx) -> int64_t {  // -1: none
+        if (!idx) return n;
+        const int64_t s = idx[n];
+        return (s >= 0 && s < p.pool_size) ? s : -1;
+    };
+    auto store_state = [&](float *base, int64_t slot, const float (&St)[R][C]) {
+        float *dst = base + state_at(slot);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+                *reinterpret_cast<float4 *>(dst + (size_t)RG * r * DK + 16 * j) =
+                    make_float4(St[r][4 * j + 0], St[r][4 * j + 1], St[r][4 * j + 2], St[r][4 * j + 3]);
+        }
+    };
 
     float S[R][C];
+    {
+        const int64_t src = p.h0 ? slot_of(p.src_idx) : -1;
+        const float *h0row = src >= 0 ? p.h0 + state_at(src) : nullptr;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+        for (int r = 0; r < R; ++r) {
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (p.h0) x = *reinterpret_cast<const float4 *>(p.h0 + (state_row0 + RG * r) * DK + col0 + 16 * j);
-            S[r][4 * j + 0] = x.x; S[r][4 * j + 1] = x.y; S[r][4 * j + 2] = x.z; S[r][4 * j + 3] = x.w;
+            for (int j = 0; j < NCH; ++j) {
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (h0row) x = *reinterpret_cast<const float4 *>(h0row + (size_t)RG * r * DK + 16 * j);
+                S[r][4 * j + 0] = x.x; S[r][4 * j + 1] = x.y; S[r][4 * j + 2] = x.z; S[r][4 * j + 3] = x.w;
+            }
         }
     }
 
+    // Snapshots.  base = tokens already behind this sequence.  The token blocks are
+    // laid on the grid of absolute positions: the first block starts at slot
+    // lo0 = base % TB, so every block ends on a multiple of TB and each multiple of
+    // snap_block (itself a multiple of TB) is the end of some block.  Without
+    // snapshots lo0 = 0 and block b simply covers tokens [tb + b TB, tb + (b+1) TB).
+    int64_t base = 0;
+    if (SNAP && p.pos0) {
+        base = p.pos0[n];
+        base = base < 0 ? 0 : base;
+    }
+    const int lo0 = SNAP ? (int)(base % TB) : 0;
+    auto snapshot_after = [&](int64_t done) {  // done: tokens of this call behind the state
+        const int64_t pos = base + done;
+        if (!SNAP || p.snap_block <= 0 || done <= 0 || pos % p.snap_block != 0) return;
+        const int64_t j = pos / p.snap_block - base / p.snap_block - 1;
+        if (j < 0 || j >= p.snap_per_seq) return;
+        const int64_t slot = p.snap_idx[(int64_t)n * p.snap_per_seq + j];
+        if (slot >= 0 && slot < p.pool_size) store_state(p.snap, slot, S);
+    };
+
     if (len > 0) {
-        const int nblk = (int)((len + TB - 1) / TB);
+        const int nblk = (int)((len + lo0 + TB - 1) / TB);
         Stager<DK, IO, L, R, NW> st;
-        st.load(p, tb, te, kh, h, row0, tid);
+        st.load(p, tb - lo0, tb, te, kh, h, row0, tid);
         st.store(Ld, 0, tid);
         __syncthreads();
 
@@ -506,15 +551,21 @@ void gdn_prefill_kernel(PrefillParams p) {
         const size_t out_row = (size_t)h * p.dv + row0 + wrow + RG * my_r;
         float obuf = 0.f;
 
+        // Slot ti is processed with cur = A when ti is even and cur = B when odd, so
+        // the first token (slot lo0) starts in both.
         TokRegs<C, R> A, B;
         float ptil[R];
-        fetch(A, 0, 0);
+        fetch(A, 0, lo0);
+        if constexpr (SNAP) B = A;
         row_dots<DK, L, R>(S, A.k, ptil);
 
         for (int blk = 0; blk < nblk; ++blk) {
             const int buf = blk & 1;
-            const int64_t t0 = tb + (int64_t)blk * TB;
-            if (blk + 1 < nblk) st.load(p, t0 + TB, te, kh, h, row0, tid);
+            // Slot ti of this block is token t0 + ti; slots [lo, nt) are tokens of the
+            // sequence (lo > 0 only in a first block that starts mid-grid).
+            const int lo = (SNAP && blk == 0) ? lo0 : 0;
+            const int64_t t0 = tb - lo0 + (int64_t)blk * TB;
+            if (blk + 1 < nblk) st.load(p, t0 + TB, tb, te, kh, h, row0, tid);
             const int nt = (int)((te - t0) < TB ? (te - t0) : TB);
             arow = (lds_f32 *)&Ld.a[buf][0];
             asm volatile("" : "+v"(arow));
@@ -536,18 +587,18 @@ void gdn_prefill_kernel(PrefillParams p) {
                 for (int r = 1; r < R; ++r)
                     if (my_r == r) ov = o[r];
                 if (my_slot == ti % TT) obuf = ov;
-                if (ti % TT == TT - 1)
+                if (ti % TT == TT - 1 && (!SNAP || ti - (TT - 1) + my_slot >= lo))
                     IO::store1(p.out, (size_t)(t0 + ti - (TT - 1) + my_slot) * p.hv * p.dv + out_row, obuf);
             };
 
             // Full token blocks are fully unrolled.  The last block of a sequence
-            // may be partial; uniform guards skip its missing tokens.  Where guards
-            // also sit between steps of full blocks they bound how far the compiler
-            // hoists work across tokens, which trades some in-wave overlap for fewer
-            // registers (more waves per SIMD); the best trade depends on the shape
-            // (measured on MI355X), see Sh::GUARD.
+            // may be partial (and a first block may start mid-grid); uniform guards
+            // skip the missing slots.  Where guards also sit between steps of full
+            // blocks they bound how far the compiler hoists work across tokens, which
+            // trades some in-wave overlap for fewer registers (more waves per SIMD);
+            // the best trade depends on the shape (measured on MI355X), see Sh::GUARD.
             if constexpr (Sh::GUARD == 0) {
-                if (nt == TB) {
+                if (lo == 0 && nt == TB) {
 #pragma unroll
                     for (int ti = 0; ti < TB; ti += 2) {
                         step(A, B, ti);
@@ -556,30 +607,32 @@ void gdn_prefill_kernel(PrefillParams p) {
                 } else {
 #pragma unroll
                     for (int ti = 0; ti < TB; ti += 2) {
-                        if (ti < nt) step(A, B, ti);
-                        if (ti + 1 < nt) step(B, A, ti + 1);
+                        if (ti >= lo && ti < nt) step(A, B, ti);
+                        if (ti + 1 >= lo && ti + 1 < nt) step(B, A, ti + 1);
                     }
                 }
             } else if constexpr (Sh::GUARD == 2) {
 #pragma unroll
                 for (int ti = 0; ti < TB; ti += 2) {
-                    if (ti + 1 < nt) {
+                    if (ti >= lo && ti + 1 < nt) {
                         step(A, B, ti);
                         step(B, A, ti + 1);
-                    } else if (ti < nt) {
-                        step(A, B, ti);
+                    } else {
+                        if (ti >= lo && ti < nt) step(A, B, ti);
+                        if (ti + 1 >= lo && ti + 1 < nt) step(B, A, ti + 1);
                     }
                 }
             } else {
 #pragma unroll
                 for (int ti = 0; ti < TB; ti += 2) {
-                    if (ti < nt) step(A, B, ti);
-                    if (ti + 1 < nt) step(B, A, ti + 1);
+                    if (ti >= lo && ti < nt) step(A, B, ti);
+                    if (ti + 1 >= lo && ti + 1 < nt) step(B, A, ti + 1);
                 }
             }
             const int rem = nt % TT;  // tokens kept but not yet stored (partial block only)
-            if (rem != 0 && my_slot < rem)
+            if (rem != 0 && my_slot < rem && (!SNAP || nt - rem + my_slot >= lo))
                 IO::store1(p.out, (size_t)(t0 + nt - rem + my_slot) * p.hv * p.dv + out_row, obuf);
+            if constexpr (SNAP) snapshot_after(t0 + nt - tb);
 
             if (blk + 1 < nblk) st.store(Ld, buf ^ 1, tid);
             __syncthreads();
@@ -587,13 +640,8 @@ void gdn_prefill_kernel(PrefillParams p) {
     }
 
     if (p.hT) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-#pragma unroll
-            for (int j = 0; j < NCH; ++j)
-                *reinterpret_cast<float4 *>(p.hT + (state_row0 + RG * r) * DK + col0 + 16 * j) =
-                    make_float4(S[r][4 * j + 0], S[r][4 * j + 1], S[r][4 * j + 2], S[r][4 * j + 3]);
-        }
+        const int64_t dst = slot_of(p.dst_idx);
+        if (dst >= 0) store_state(p.hT, dst, S);
     }
 }
 
@@ -675,8 +723,9 @@ hipError_t launch_prefill_t(const PrefillParams &p, hipStream_t s) {
     q.tiles = p.dv / RW;
     dim3 grid((unsigned)q.tiles * p.hv * p.n_seqs), block(NW * 64);
     void *args[] = {&q};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, L, R, NW>), grid, block,
-                           args, 0, s);
+    const void *fn = p.snap_block > 0 ? reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, L, R, NW, true>)
+                                      : reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, L, R, NW, false>);
+    return hipLaunchKernel(fn, grid, block, args, 0, s);
 }
 
 template <int DK, class IO, int R, int NW>

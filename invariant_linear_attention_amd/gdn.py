@@ -19,7 +19,8 @@ STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
     5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_HIP",
 }
-EXPORTS = ("gdn_fwd_varlen", "gdn_decode_step", "gdn_query_plan", "gdn_status_string", "gdn_abi_version")
+EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_query_plan", "gdn_status_string",
+           "gdn_abi_version")
 
 
 class GdnDims(ctypes.Structure):
@@ -55,6 +56,9 @@ def load_library(path: str = LIBRARY):
         vp = ctypes.c_void_p
         lib.gdn_fwd_varlen.restype = ctypes.c_int
         lib.gdn_fwd_varlen.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdn_fwd_varlen_pool.restype = ctypes.c_int
+        lib.gdn_fwd_varlen_pool.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            ctypes.c_int32, ctypes.c_int32, vp, vp]
         lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdn_query_plan.restype = ctypes.c_int
@@ -156,6 +160,40 @@ def gdn_fwd_varlen(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, stream=N
     _check(lib.gdn_fwd_varlen(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
                               _ptr(cu_seqlens), _ptr(out), _ptr(hT), _stream_handle(stream)))
     return out, hT
+
+
+def gdn_fwd_varlen_pool(q, k, v, g, beta, cu_seqlens, state_pool, src_idx=None, dst_idx=None, pos0=None,
+                        snap_idx=None, snap_block: int = 0, out=None, stream=None, plan=(0, 0, 0)):
+    """Varlen prefill against a state pool (see include/gdn.h).  state_pool
+    [P, Hv, dv, dk] fp32 is read and written in place; src_idx / dst_idx / pos0
+    [N] int32 or None; snap_idx [N, S] int32 (required when snap_block > 0).
+    Returns out [T, Hv, dv]."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    _need(state_pool, "state_pool", torch.float32)
+    for name, t in (("src_idx", src_idx), ("dst_idx", dst_idx), ("pos0", pos0), ("snap_idx", snap_idx)):
+        _need(t, name, torch.int32)
+    T = int(q.shape[0])
+    N = int(cu_seqlens.numel()) - 1
+    snap_per_seq = 0
+    if snap_idx is not None:
+        if snap_idx.dim() != 2 or int(snap_idx.shape[0]) != N:
+            raise ValueError("snap_idx must be [N, snapshots per sequence]")
+        snap_per_seq = int(snap_idx.shape[1])
+    if out is None:
+        out = torch.empty((T, v.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+    _need(out, "out", q.dtype)
+    dims = make_dims(q, v, N, T, pool_size=int(state_pool.shape[0]), plan=plan)
+    _check(lib.gdn_fwd_varlen_pool(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(cu_seqlens), _ptr(state_pool), _ptr(src_idx), _ptr(dst_idx), _ptr(pos0),
+                                   _ptr(snap_idx), int(snap_block), snap_per_seq, _ptr(out),
+                                   _stream_handle(stream)))
+    return out
 
 
 def gdn_decode_step(q, k, v, g, beta, state_pool, state_idx=None, out=None, stream=None, plan=(0, 0, 0)):

@@ -27,8 +27,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"gdn_fwd_varlen", "gdn_decode_step", "gdn_query_plan", "gdn_status_string",
-                          "gdn_abi_version"}
+    assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_query_plan",
+                          "gdn_status_string", "gdn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -73,7 +73,8 @@ def _dims(**kw):
 # Fake, well-separated, aligned addresses: the checks below fail before any launch.
 BASE = 0x7F0000000000
 MB = 1 << 24
-P = {name: BASE + i * MB for i, name in enumerate(["q", "k", "v", "g", "b", "h0", "cu", "out", "hT"])}
+P = {name: BASE + i * MB for i, name in enumerate(["q", "k", "v", "g", "b", "h0", "cu", "out", "hT",
+                                                   "src", "dst", "pos0", "snap"])}
 
 
 def call_fwd(lib, dims, **over):
@@ -151,6 +152,50 @@ def test_fwd_rejects_aliasing(lib, over):
 ])
 def test_decode_rejects(lib, case, over, code):
     assert call_dec(lib, _dims(**case), **over) == code
+
+
+def call_pool(lib, dims, snap_block=0, snap_per_seq=0, **over):
+    a = dict(P)
+    a.update(over)
+    return lib.gdn_fwd_varlen_pool(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], a["v"],
+                                   a["g"], a["b"], a["cu"], a.get("pool", a["h0"]), a["src"], a["dst"], a["pos0"],
+                                   a["snap"], snap_block, snap_per_seq, a["out"], None)
+
+
+@pytest.mark.parametrize("case,kw,code", [
+    (dict(pool_size=0), {}, 2),                                       # a pool has slots
+    (dict(pool_size=4), dict(snap_block=-16, snap_per_seq=1), 2),
+    (dict(pool_size=4), dict(snap_block=24, snap_per_seq=1), 2),      # not a multiple of 16
+    (dict(pool_size=4), dict(snap_block=32, snap_per_seq=0), 2),      # snapshots need slots
+    (dict(pool_size=4), dict(snap_per_seq=-1), 2),
+    (dict(pool_size=4), dict(snap_block=32, snap_per_seq=2, snap=None), 1),
+    (dict(pool_size=4), dict(pool=None), 1),
+    (dict(pool_size=4), dict(cu=None), 1),
+    (dict(pool_size=4), dict(q=None), 1),
+    (dict(pool_size=1), dict(src=None), 2),                          # identity slots need P >= N
+    (dict(pool_size=1), dict(dst=None), 2),
+    (dict(pool_size=4), dict(pool=P["h0"] + 8), 4),
+    (dict(pool_size=4), dict(src=P["src"] + 2), 4),
+    (dict(pool_size=4), dict(snap=P["snap"] + 1, snap_block=16, snap_per_seq=1), 4),
+    (dict(pool_size=4), dict(out=P["h0"]), 5),                       # out overlaps the pool
+    (dict(pool_size=4), dict(pool=P["v"]), 5),                       # pool overlaps an input
+    (dict(pool_size=4), dict(out=P["pos0"]), 5),
+    (dict(pool_size=4, dk=40), {}, 6),
+    (dict(pool_size=4, plan_lanes=16, plan_rows=3), {}, 6),
+    (dict(pool_size=4, n_seqs=0, total_tokens=3), {}, 2),
+])
+def test_pool_rejects(lib, case, kw, code):
+    kw = dict(kw)
+    sb, sp = kw.pop("snap_block", 0), kw.pop("snap_per_seq", 0)
+    assert call_pool(lib, _dims(**case), snap_block=sb, snap_per_seq=sp, **kw) == code
+
+
+def test_pool_null_dims(lib):
+    assert call_pool(lib, None) == 1
+
+
+def test_pool_zero_sequences_is_a_noop(lib):
+    assert call_pool(lib, _dims(n_seqs=0, total_tokens=0, pool_size=4)) == 0
 
 
 def test_decode_zero_batch_is_a_noop(lib):
