@@ -233,13 +233,12 @@ struct PrefillShape {
     static constexpr int KSLOTS = (KITEMS + NT - 1) / NT;
     static constexpr int VSLOTS = (VITEMS + NT - 1) / NT;
     static constexpr int TT = L / R;                 // tokens buffered per output store
-    // Guards between token steps of full blocks: 1 = every token, 2 = every pair,
-    // 0 = none.  Chosen per shape from measurements on MI355X.
-#ifdef GDN_PREFILL_GUARD
-    static constexpr int GUARD = GDN_PREFILL_GUARD;
-#else
-    static constexpr int GUARD = (L == 16) ? (R == 1 ? 2 : 0) : 1;
-#endif
+    // Guards between token steps of full blocks: 1 = every token, 0 = none.  Chosen
+    // per shape from measurements on MI355X: a guard after every token keeps
+    // registers (and waves per SIMD) for the 4- and 8-lane shapes; 16 lanes per row
+    // is the shape for scarce rows (about one wave per SIMD), where the compiler's
+    // freedom to schedule across tokens matters more than registers.
+    static constexpr int GUARD = (L == 16) ? 0 : 1;
     static_assert(TS <= NT, "gate/beta staging needs TB+1 threads");
     static_assert(RW % IO::VEC == 0, "row slice must be whole vectors");
     static_assert(TB % TT == 0, "output flushes must align with token blocks");
@@ -607,17 +606,6 @@ void gdn_prefill_kernel(PrefillParams p) {
                 } else {
 #pragma unroll
                     for (int ti = 0; ti < TB; ti += 2) {
-                        if (ti >= lo && ti < nt) step(A, B, ti);
-                        if (ti + 1 >= lo && ti + 1 < nt) step(B, A, ti + 1);
-                    }
-                }
-            } else if constexpr (Sh::GUARD == 2) {
-#pragma unroll
-                for (int ti = 0; ti < TB; ti += 2) {
-                    if (ti >= lo && ti + 1 < nt) {
-                        step(A, B, ti);
-                        step(B, A, ti + 1);
-                    } else {
                         if (ti >= lo && ti < nt) step(A, B, ti);
                         if (ti + 1 >= lo && ti + 1 < nt) step(B, A, ti + 1);
                     }
