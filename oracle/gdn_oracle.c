@@ -32,15 +32,18 @@
  * value heads share one key head).  No 1/sqrt(dk) scale is applied to q.
  *
  * Layouts (all contiguous, token-major):
- *   q, k   : [T][hk][dk]   fp32 (io_dtype 0) or bf16 bits (io_dtype 1)
- *   v      : [T][hv][dv]   same dtype as q
- *   g, beta: [T][hv]       fp32
+ *   q, k   : [T][hk][dk]   qk_dtype: fp32 (0), bf16 bits (1) or fp64 (2)
+ *   v      : [T][hv][dv]   v_dtype, same codes
+ *   g, beta: [T][hv]       gate_dtype: fp32 (0) or fp64 (2)
  *   h0, hT : [N][hv][dv][dk] fp64 (h0 may be NULL = zero state, hT may be NULL)
  *   out    : [T][hv][dv]   fp64
  *   cu_seqlens: [N+1] int32, cu[0] = 0, non-decreasing, cu[N] = T.
  *
  * Parallelism: OpenMP over independent (sequence, value head) units only; the
  * arithmetic inside a unit is the sequential loop above.
+ *
+ * gdn_oracle_preprocess (below) forms q, k, g and beta from the raw inputs of the
+ * fused path in fp64; its results feed gdn_oracle_forward with dtype code 2.
  */
 #include <math.h>
 #include <stdint.h>
@@ -55,6 +58,8 @@ static double oracle_load(const void *base, int64_t idx, int io_dtype)
 {
     if (io_dtype == 0)
         return (double)((const float *)base)[idx];
+    if (io_dtype == 2)
+        return ((const double *)base)[idx];
     /* bf16 is the top half of an IEEE binary32; the widening is exact. */
     uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
     float f;
@@ -65,9 +70,9 @@ static double oracle_load(const void *base, int64_t idx, int io_dtype)
 /* Returns 0 on success, a negative value on a bad argument. */
 int gdn_oracle_forward(int32_t n_seqs, const int32_t *cu_seqlens,
                        int32_t hk, int32_t hv, int32_t dk, int32_t dv,
-                       int32_t io_dtype,
+                       int32_t qk_dtype, int32_t v_dtype, int32_t gate_dtype,
                        const void *q, const void *k, const void *v,
-                       const float *g, const float *beta,
+                       const void *g, const void *beta,
                        const double *h0, double *out, double *hT,
                        int32_t n_threads)
 {
@@ -75,7 +80,7 @@ int gdn_oracle_forward(int32_t n_seqs, const int32_t *cu_seqlens,
         return -1;
     if (hv % hk != 0)
         return -2;
-    if (io_dtype != 0 && io_dtype != 1)
+    if (qk_dtype < 0 || qk_dtype > 2 || v_dtype < 0 || v_dtype > 2 || (gate_dtype != 0 && gate_dtype != 2))
         return -3;
     if (n_seqs == 0)
         return 0;
@@ -112,8 +117,8 @@ int gdn_oracle_forward(int32_t n_seqs, const int32_t *cu_seqlens,
             S[e] = h0 ? h0[state_off + e] : 0.0;
 
         for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
-            const double a = exp((double)g[t * hv + h]);
-            const double b = (double)beta[t * hv + h];
+            const double a = exp(oracle_load(g, t * hv + h, gate_dtype));
+            const double b = oracle_load(beta, t * hv + h, gate_dtype);
             const int64_t qk_off = (t * hk + kh) * (int64_t)dk;
             const int64_t v_off = (t * hv + h) * (int64_t)dv;
 
@@ -124,13 +129,13 @@ int gdn_oracle_forward(int32_t n_seqs, const int32_t *cu_seqlens,
                 double *row = S + (size_t)j * dk;
                 double p = 0.0;
                 for (int32_t i = 0; i < dk; ++i)
-                    p += row[i] * oracle_load(k, qk_off + i, io_dtype);
-                const double u = b * (oracle_load(v, v_off + j, io_dtype) - p);
+                    p += row[i] * oracle_load(k, qk_off + i, qk_dtype);
+                const double u = b * (oracle_load(v, v_off + j, v_dtype) - p);
                 for (int32_t i = 0; i < dk; ++i)
-                    row[i] += u * oracle_load(k, qk_off + i, io_dtype);
+                    row[i] += u * oracle_load(k, qk_off + i, qk_dtype);
                 double o = 0.0;
                 for (int32_t i = 0; i < dk; ++i)
-                    o += row[i] * oracle_load(q, qk_off + i, io_dtype);
+                    o += row[i] * oracle_load(q, qk_off + i, qk_dtype);
                 out[v_off + j] = o;
             }
         }
@@ -139,6 +144,66 @@ int gdn_oracle_forward(int32_t n_seqs, const int32_t *cu_seqlens,
         free(S);
     }
     return status;
+}
+
+/*
+ * Preprocessing of the fused path, in fp64, from the raw per-token inputs:
+ *
+ *   q'[t][kh][:] = q[t][kh][:] / sqrt(sum_i q[t][kh][i]^2 + eps)     (same for k)
+ *   g[t][h]      = -exp(A_log[h]) * softplus(a[t][h] + dt_bias[h]),
+ *                  softplus(x) = log(1 + exp(x)), evaluated as log1p(exp(x))
+ *   beta[t][h]   = 1 / (1 + exp(-b[t][h]))
+ *
+ * This is the gate and key/query handling of the gated delta rule layer (Yang,
+ * Kautz, Hatamizadeh, ICLR 2025: L2-normalised keys and queries; a Mamba2-style
+ * decay exp(-exp(A_log) softplus(.)) and a sigmoid write strength).  The page
+ * "Defending Against the Training-Inference Numeric Mismatch in RL (Especially
+ * Linear Attention)" (section 3.1) keeps A_log in fp32, as here.
+ *
+ * q, k: [T][hk][dk] in io_dtype (0 fp32, 1 bf16); a, b: [T][hv] fp32;
+ * A_log: [hv] fp32; dt_bias: [hv] fp32 or NULL (zero).  Outputs in fp64:
+ * qn, kn: [T][hk][dk]; g, beta: [T][hv].  With norm_qk == 0, qn and kn are the
+ * inputs widened; with A_log == NULL, g and beta are a and b widened.
+ */
+int gdn_oracle_preprocess(int64_t T, int32_t hk, int32_t hv, int32_t dk, int32_t io_dtype,
+                          const void *q, const void *k, const float *a, const float *b,
+                          const float *A_log, const float *dt_bias, int32_t norm_qk, double eps,
+                          double *qn, double *kn, double *g, double *beta)
+{
+    if (T < 0 || hk <= 0 || hv <= 0 || dk <= 0 || (io_dtype != 0 && io_dtype != 1))
+        return -1;
+    if (T > 0 && (!q || !k || !a || !b || !qn || !kn || !g || !beta))
+        return -4;
+    for (int64_t r = 0; r < T * hk; ++r) {
+        const int64_t off = r * dk;
+        double sq = 0.0, sk = 0.0;
+        for (int32_t i = 0; i < dk; ++i) {
+            const double x = oracle_load(q, off + i, io_dtype);
+            const double y = oracle_load(k, off + i, io_dtype);
+            sq += x * x;
+            sk += y * y;
+        }
+        const double dq = norm_qk ? sqrt(sq + eps) : 1.0;
+        const double dkn = norm_qk ? sqrt(sk + eps) : 1.0;
+        for (int32_t i = 0; i < dk; ++i) {
+            qn[off + i] = oracle_load(q, off + i, io_dtype) / dq;
+            kn[off + i] = oracle_load(k, off + i, io_dtype) / dkn;
+        }
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < hv; ++h) {
+            const int64_t i = t * hv + h;
+            if (A_log) {
+                const double x = (double)a[i] + (dt_bias ? (double)dt_bias[h] : 0.0);
+                g[i] = -exp((double)A_log[h]) * log1p(exp(x));
+                beta[i] = 1.0 / (1.0 + exp(-(double)b[i]));
+            } else {
+                g[i] = (double)a[i];
+                beta[i] = (double)b[i];
+            }
+        }
+    }
+    return 0;
 }
 
 int gdn_oracle_max_threads(void)

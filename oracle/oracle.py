@@ -46,11 +46,19 @@ def load(library: str = LIBRARY):
     f.argtypes = [
         ctypes.c_int32, ctypes.c_void_p,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-        ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int32,
+    ]
+    p = lib.gdn_oracle_preprocess
+    p.restype = ctypes.c_int
+    p.argtypes = [
+        ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_double,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
     ]
     lib.gdn_oracle_max_threads.restype = ctypes.c_int
     lib.gdn_oracle_max_threads.argtypes = []
@@ -99,21 +107,22 @@ def _as_numpy(x):
 def gdn_forward(q, k, v, g, beta, cu_seqlens, h0=None, n_threads=None, library=None):
     """Run the fp64 oracle.
 
-    q, k: [T, Hk, dk]; v: [T, Hv, dv] -- all fp32, or all bf16 (torch bf16 or raw
-    uint16 bits); g, beta: [T, Hv] fp32; cu_seqlens: [N+1] int32; h0: optional
-    [N, Hv, dv, dk] fp32 or fp64 (widened exactly).
+    q, k: [T, Hk, dk] and v: [T, Hv, dv], each fp32, bf16 (torch bf16 or raw
+    uint16 bits) or fp64 (q and k share one dtype); g, beta: [T, Hv] fp32 or fp64
+    (one dtype); cu_seqlens: [N+1] int32; h0: optional [N, Hv, dv, dk] fp32 or
+    fp64.  Every input is widened exactly.
 
     Returns (out [T, Hv, dv] float64, hT [N, Hv, dv, dk] float64).
     """
     qn, qc = _as_numpy(q)
     kn, kc = _as_numpy(k)
     vn, vc = _as_numpy(v)
-    if not (qc == kc == vc and qc in (0, 1)):
-        raise TypeError("q, k, v must share one dtype: fp32 or bf16")
+    if not (qc == kc and qc in (0, 1, 2) and vc in (0, 1, 2)):
+        raise TypeError("q and k must share one dtype; q, k, v must be fp32, bf16 or fp64")
     gn, gc = _as_numpy(g)
     bn, bc = _as_numpy(beta)
-    if gc != 0 or bc != 0:
-        raise TypeError("g and beta must be fp32")
+    if gc != bc or gc not in (0, 2):
+        raise TypeError("g and beta must both be fp32 or both fp64")
     cu, cc = _as_numpy(cu_seqlens)
     if cc != 3:
         raise TypeError("cu_seqlens must be int32")
@@ -144,12 +153,62 @@ def gdn_forward(q, k, v, g, beta, cu_seqlens, h0=None, n_threads=None, library=N
         return None if a is None or a.size == 0 else a.ctypes.data
 
     rc = lib.gdn_oracle_forward(
-        n, ptr(cu), hk, hv, dk, dv, qc,
+        n, ptr(cu), hk, hv, dk, dv, qc, vc, gc,
         ptr(qn), ptr(kn), ptr(vn), ptr(gn), ptr(bn),
         ptr(h0n), ptr(out), ptr(hT), int(n_threads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
     return out, hT
+
+
+def preprocess(q, k, a, b, A_log=None, dt_bias=None, norm_qk=True, eps=1e-6, library=None):
+    """fp64 preprocessing of the fused path (see gdn_oracle_preprocess).
+
+    q, k: [T, Hk, dk] fp32 or bf16 (one dtype); a, b: [T, Hv] fp32; A_log, dt_bias:
+    [Hv] fp32 or None.  Returns (q', k', g, beta), all float64.
+    """
+    qn, qc = _as_numpy(q)
+    kn, kc = _as_numpy(k)
+    if not (qc == kc and qc in (0, 1)):
+        raise TypeError("q and k must share one dtype: fp32 or bf16")
+    an, ac = _as_numpy(a)
+    bn, bc = _as_numpy(b)
+    if ac != 0 or bc != 0:
+        raise TypeError("a and b must be fp32")
+    T, hk, dk = qn.shape
+    hv = an.shape[1]
+    if kn.shape != qn.shape or an.shape != (T, hv) or bn.shape != (T, hv):
+        raise ValueError("inconsistent shapes")
+    Ln = Dn = None
+    if A_log is not None:
+        Ln, lc = _as_numpy(A_log)
+        if lc != 0 or Ln.shape != (hv,):
+            raise ValueError("A_log must be fp32 [Hv]")
+    if dt_bias is not None:
+        Dn, dc = _as_numpy(dt_bias)
+        if dc != 0 or Dn.shape != (hv,):
+            raise ValueError("dt_bias must be fp32 [Hv]")
+    q2 = np.zeros((T, hk, dk), dtype=np.float64)
+    k2 = np.zeros((T, hk, dk), dtype=np.float64)
+    g2 = np.zeros((T, hv), dtype=np.float64)
+    b2 = np.zeros((T, hv), dtype=np.float64)
+    lib = load(library) if library is not None else _get_lib()
+
+    def ptr(x):
+        return None if x is None or x.size == 0 else x.ctypes.data
+
+    rc = lib.gdn_oracle_preprocess(T, hk, hv, dk, qc, ptr(qn), ptr(kn), ptr(an), ptr(bn), ptr(Ln), ptr(Dn),
+                                   1 if norm_qk else 0, float(eps), ptr(q2), ptr(k2), ptr(g2), ptr(b2))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (code %d)" % rc)
+    return q2, k2, g2, b2
+
+
+def gdn_forward_fused(q, k, v, a, b, cu_seqlens, h0=None, A_log=None, dt_bias=None, norm_qk=True, eps=1e-6,
+                      n_threads=None, library=None):
+    """preprocess() followed by gdn_forward() on its fp64 results."""
+    q2, k2, g2, b2 = preprocess(q, k, a, b, A_log, dt_bias, norm_qk, eps, library=library)
+    return gdn_forward(q2, k2, v, g2, b2, cu_seqlens, h0, n_threads=n_threads, library=library)
 
 
 def max_threads() -> int:

@@ -369,3 +369,120 @@ ALL_PINS = [
     pin_gate_and_beta_per_value_head,
     pin_bf16_inputs_widened_exactly,
 ]
+
+
+# ------------------------------------------------- fused-path preprocessing
+#
+# Pins for oracle.preprocess (q/k L2 normalisation and the gate / write strength
+# from raw logits).  Each takes (preprocess, forward) callables with the
+# signatures of oracle.preprocess and oracle.gdn_forward and checks values that
+# mathematics fixes: norms, the constants softplus(0) = ln 2 and sigmoid(ln 3) =
+# 3/4, the asymptotes of softplus, and the full-forget closed form of the rule.
+
+def _raw_case(seed, T, hk, hv, dk, scale=3.0):
+    r = _rng(seed)
+    q = (scale * r.standard_normal((T, hk, dk))).astype(np.float32)
+    k = (scale * r.standard_normal((T, hk, dk))).astype(np.float32)
+    a = r.standard_normal((T, hv)).astype(np.float32)
+    b = r.standard_normal((T, hv)).astype(np.float32)
+    return q, k, a, b
+
+
+def pin_pre_norm_closed_form(preprocess, forward):
+    """|q'|^2 = |q|^2 / (|q|^2 + eps), q' parallel to q (eps large enough to see)."""
+    q, k, a, b = _raw_case(101, 5, 2, 2, 8, scale=0.05)
+    eps = 1e-2
+    q2, k2, _, _ = preprocess(q, k, a, b, norm_qk=True, eps=eps)
+    for x, x2 in ((q, q2), (k, k2)):
+        x = x.astype(np.float64)
+        ss = np.sum(x * x, axis=-1)
+        _close(np.sum(x2 * x2, axis=-1), ss / (ss + eps), 1e-13, "normalised length")
+        cos = np.sum(x * x2, axis=-1) / (np.sqrt(ss) * np.linalg.norm(x2, axis=-1))
+        _close(cos, np.ones_like(cos), 1e-14, "direction")
+
+
+def pin_pre_unit_rows(preprocess, forward):
+    """With the default tiny eps, rows of moderate size come out of unit length."""
+    q, k, a, b = _raw_case(102, 4, 3, 3, 16)
+    q2, k2, _, _ = preprocess(q, k, a, b)
+    for x2 in (q2, k2):
+        _close(np.linalg.norm(x2, axis=-1), np.ones(x2.shape[:2]), 1e-7, "unit rows")
+
+
+def pin_pre_norm_off_is_widening(preprocess, forward):
+    q, k, a, b = _raw_case(103, 3, 1, 2, 4)
+    q2, k2, g2, b2 = preprocess(q, k, a, b, norm_qk=False)
+    assert np.array_equal(q2, q.astype(np.float64)) and np.array_equal(k2, k.astype(np.float64))
+    assert np.array_equal(g2, a.astype(np.float64)) and np.array_equal(b2, b.astype(np.float64))
+
+
+def pin_pre_gate_constants(preprocess, forward):
+    """softplus(0) = ln 2; softplus(x) -> x (x large), -> exp(x) (x very negative);
+    sigmoid(0) = 1/2, sigmoid(+-ln 3) = 3/4, 1/4; A_log and dt_bias per value head."""
+    hv = 4
+    A_log = np.array([0.0, math.log(2.0), -1.0, 0.5], dtype=np.float32)
+    dt_bias = np.array([0.0, 1.0, -2.0, 0.25], dtype=np.float32)
+    x = np.array([0.0, 40.0, -40.0], dtype=np.float64)
+    a = (x[:, None] - dt_bias[None, :].astype(np.float64)).astype(np.float32)   # a + dt_bias = x (exactly here)
+    b = np.array([[0.0, math.log(3.0), -math.log(3.0), 0.0]] * 3, dtype=np.float32)
+    q = np.ones((3, 1, 2), dtype=np.float32)
+    _, _, g2, b2 = preprocess(q, q, a, b, A_log=A_log, dt_bias=dt_bias, norm_qk=False)
+    amp = np.exp(A_log.astype(np.float64))
+    xs = a.astype(np.float64) + dt_bias.astype(np.float64)[None, :]
+    _close(g2[0], -amp * math.log(2.0) * np.ones(hv), 1e-15, "softplus(0) = ln 2")
+    _close(g2[1], -amp * xs[1], 1e-15, "softplus(x) ~ x")
+    _close(g2[2], -amp * np.exp(xs[2]), 1e-12, "softplus(x) ~ exp(x)")
+    want_b = 1.0 / (1.0 + np.exp(-b.astype(np.float64)))
+    _close(b2[:, 0], 0.5 * np.ones(3), 1e-16, "sigmoid(0)")
+    _close(b2[:, 1], want_b[:, 1], 1e-15, "sigmoid(ln 3)")
+    assert abs(b2[0, 1] - 0.75) < 1e-7 and abs(b2[0, 2] - 0.25) < 1e-7
+
+
+def pin_pre_gate_without_A_log_passes_through(preprocess, forward):
+    q, k, a, b = _raw_case(104, 3, 1, 3, 4)
+    _, _, g2, b2 = preprocess(q, k, a, b, A_log=None, norm_qk=True)
+    assert np.array_equal(g2, a.astype(np.float64)) and np.array_equal(b2, b.astype(np.float64))
+
+
+def pin_pre_full_forget_through_the_rule(preprocess, forward):
+    """A huge a + dt_bias makes exp(g) vanish: the state after a token is
+    beta v k'^T and o = beta (k'.q') v, with beta = sigmoid(b) and q', k' unit."""
+    T, hk, hv, dk, dv = 2, 1, 2, 4, 3
+    q, k, _, b = _raw_case(105, T, hk, hv, dk)
+    a = np.full((T, hv), 800.0, dtype=np.float32)
+    A_log = np.zeros(hv, dtype=np.float32)
+    v = _rng(106).standard_normal((T, hv, dv)).astype(np.float32)
+    q2, k2, g2, b2 = preprocess(q, k, a, b, A_log=A_log, eps=0.0)   # exact unit rows
+    cu = np.array([0, T], dtype=np.int32)
+    h0 = _rng(107).standard_normal((1, hv, dv, dk)).astype(np.float32)
+    out, hT = forward(q2, k2, v, g2, b2, cu, h0)
+    t = T - 1
+    for h in range(hv):
+        bt = 1.0 / (1.0 + math.exp(-float(b[t, h])))
+        kk = k[t, 0].astype(np.float64) / np.linalg.norm(k[t, 0].astype(np.float64))
+        qq = q[t, 0].astype(np.float64) / np.linalg.norm(q[t, 0].astype(np.float64))
+        vv = v[t, h].astype(np.float64)
+        _close(hT[0, h], bt * np.outer(vv, kk), 1e-12, "state after a full forget")
+        _close(out[t, h], bt * float(kk @ qq) * vv, 1e-12, "output after a full forget")
+
+
+def pin_pre_bf16_rows(preprocess, forward):
+    """bf16 raw q/k are widened exactly before normalising."""
+    import torch
+    q, k, a, b = _raw_case(108, 3, 2, 2, 8)
+    qb = torch.from_numpy(q).to(torch.bfloat16)
+    kb = torch.from_numpy(k).to(torch.bfloat16)
+    q2b, k2b, _, _ = preprocess(qb, kb, a, b)
+    q2f, k2f, _, _ = preprocess(qb.float().numpy(), kb.float().numpy(), a, b)
+    assert np.array_equal(q2b, q2f) and np.array_equal(k2b, k2f)
+
+
+PRE_PINS = [
+    pin_pre_norm_closed_form,
+    pin_pre_unit_rows,
+    pin_pre_norm_off_is_widening,
+    pin_pre_gate_constants,
+    pin_pre_gate_without_A_log_passes_through,
+    pin_pre_full_forget_through_the_rule,
+    pin_pre_bf16_rows,
+]

@@ -11,6 +11,11 @@ def test_oracle_pin(pin):
     pin(oracle.gdn_forward)
 
 
+@pytest.mark.parametrize("pin", oracle_pins.PRE_PINS, ids=lambda p: p.__name__)
+def test_oracle_preprocessing_pin(pin):
+    pin(oracle.preprocess, oracle.gdn_forward)
+
+
 def test_bruteforce_is_not_the_recurrence():
     """The brute force must itself respect the transition-product algebra: with
     one token and S0 = 0 it reduces to beta v k^T, whatever the gate."""

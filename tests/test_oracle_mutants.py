@@ -14,30 +14,70 @@ from oracle import oracle as oracle_mod
 # (name, text in gdn_oracle.c, replacement)
 MUTANTS = [
     ("dropped_decay", "S[e] = a * S[e];", "S[e] = S[e];"),
-    ("gate_sign", "exp((double)g[t * hv + h])", "exp(-(double)g[t * hv + h])"),
-    ("gate_on_key_head", "exp((double)g[t * hv + h])", "exp((double)g[t * hv + kh])"),
+    ("gate_sign", "exp(oracle_load(g, t * hv + h, gate_dtype))", "exp(-oracle_load(g, t * hv + h, gate_dtype))"),
+    ("gate_on_key_head", "exp(oracle_load(g, t * hv + h, gate_dtype))", "exp(oracle_load(g, t * hv + kh, gate_dtype))"),
     ("dropped_beta", "const double u = b * (", "const double u = ("),
-    ("delta_sign", "(oracle_load(v, v_off + j, io_dtype) - p)", "(oracle_load(v, v_off + j, io_dtype) + p)"),
-    ("write_sign", "row[i] += u * oracle_load(k, qk_off + i, io_dtype);",
-     "row[i] -= u * oracle_load(k, qk_off + i, io_dtype);"),
-    ("write_with_query", "row[i] += u * oracle_load(k, qk_off + i, io_dtype);",
-     "row[i] += u * oracle_load(q, qk_off + i, io_dtype);"),
-    ("readout_with_key", "o += row[i] * oracle_load(q, qk_off + i, io_dtype);",
-     "o += row[i] * oracle_load(k, qk_off + i, io_dtype);"),
-    ("readout_before_write", "o += row[i] * oracle_load(q, qk_off + i, io_dtype);",
-     "o += (row[i] - u * oracle_load(k, qk_off + i, io_dtype)) * oracle_load(q, qk_off + i, io_dtype);"),
-    ("delta_on_undecayed_state", "p += row[i] * oracle_load(k, qk_off + i, io_dtype);",
-     "p += (row[i] / a) * oracle_load(k, qk_off + i, io_dtype);"),
+    ("delta_sign", "(oracle_load(v, v_off + j, v_dtype) - p)", "(oracle_load(v, v_off + j, v_dtype) + p)"),
+    ("write_sign", "row[i] += u * oracle_load(k, qk_off + i, qk_dtype);",
+     "row[i] -= u * oracle_load(k, qk_off + i, qk_dtype);"),
+    ("write_with_query", "row[i] += u * oracle_load(k, qk_off + i, qk_dtype);",
+     "row[i] += u * oracle_load(q, qk_off + i, qk_dtype);"),
+    ("readout_with_key", "o += row[i] * oracle_load(q, qk_off + i, qk_dtype);",
+     "o += row[i] * oracle_load(k, qk_off + i, qk_dtype);"),
+    ("readout_before_write", "o += row[i] * oracle_load(q, qk_off + i, qk_dtype);",
+     "o += (row[i] - u * oracle_load(k, qk_off + i, qk_dtype)) * oracle_load(q, qk_off + i, qk_dtype);"),
+    ("delta_on_undecayed_state", "p += row[i] * oracle_load(k, qk_off + i, qk_dtype);",
+     "p += (row[i] / a) * oracle_load(k, qk_off + i, qk_dtype);"),
     ("group_map_modulo", "const int32_t kh = h / group;", "const int32_t kh = h % hk;"),
     ("transposed_state", "double *row = S + (size_t)j * dk;", "double *row = S + (size_t)j;"),
     ("value_index_key_heads", "const int64_t v_off = (t * hv + h) * (int64_t)dv;",
      "const int64_t v_off = (t * hk + h) * (int64_t)dv;"),
     ("dropped_h0", "S[e] = h0 ? h0[state_off + e] : 0.0;", "S[e] = 0.0;"),
-    ("query_scaled", "o += row[i] * oracle_load(q, qk_off + i, io_dtype);",
-     "o += row[i] * oracle_load(q, qk_off + i, io_dtype) / sqrt((double)dk);"),
+    ("query_scaled", "o += row[i] * oracle_load(q, qk_off + i, qk_dtype);",
+     "o += row[i] * oracle_load(q, qk_off + i, qk_dtype) / sqrt((double)dk);"),
     ("bf16_low_half", "uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;",
      "uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 15;"),
 ]
+
+
+# Mistakes in the fused-path preprocessing, caught by the preprocessing pins.
+PRE_MUTANTS = [
+    ("norm_without_eps", "const double dq = norm_qk ? sqrt(sq + eps) : 1.0;",
+     "const double dq = norm_qk ? sqrt(sq) : 1.0;"),
+    ("norm_q_by_k", "const double dq = norm_qk ? sqrt(sq + eps) : 1.0;",
+     "const double dq = norm_qk ? sqrt(sk + eps) : 1.0;"),
+    ("norm_squared", "qn[off + i] = oracle_load(q, off + i, io_dtype) / dq;",
+     "qn[off + i] = oracle_load(q, off + i, io_dtype) / (dq * dq);"),
+    ("softplus_as_exp", "log1p(exp(x))", "exp(x)"),
+    ("softplus_as_identity", "log1p(exp(x))", "x"),
+    ("A_log_not_exponentiated", "g[i] = -exp((double)A_log[h]) * ", "g[i] = -(double)A_log[h] * "),
+    ("gate_sign_pre", "g[i] = -exp((double)A_log[h]) * ", "g[i] = exp((double)A_log[h]) * "),
+    ("dt_bias_dropped", "(dt_bias ? (double)dt_bias[h] : 0.0)", "0.0"),
+    ("A_log_first_head", "exp((double)A_log[h])", "exp((double)A_log[0])"),
+    ("sigmoid_sign", "beta[i] = 1.0 / (1.0 + exp(-(double)b[i]));", "beta[i] = 1.0 / (1.0 + exp((double)b[i]));"),
+    ("bf16_low_half_pre", "uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;",
+     "uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 15;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PRE_MUTANTS, ids=[m[0] for m in PRE_MUTANTS])
+def test_preprocessing_pins_catch_mutant(tmp_path, name, old, new):
+    with open(oracle_mod.SOURCE) as f:
+        src = f.read()
+    assert old in src, "mutation site for %s not found in the oracle source" % name
+    mpath = tmp_path / ("pre_mutant_%s.c" % name)
+    mpath.write_text(src.replace(old, new))
+    lib = str(tmp_path / ("libpre_mutant_%s.so" % name))
+    oracle.build(str(mpath), lib)
+    pre = functools.partial(oracle_mod.preprocess, library=lib)
+    fwd = functools.partial(oracle_mod.gdn_forward, library=lib)
+    caught = []
+    for pin in oracle_pins.PRE_PINS:
+        try:
+            pin(pre, fwd)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, "preprocessing mutant %s passed every pin" % name
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -76,3 +116,6 @@ def test_unmutated_copy_passes(tmp_path):
     fwd = functools.partial(oracle_mod.gdn_forward, library=lib)
     for pin in oracle_pins.ALL_PINS:
         pin(fwd)
+    pre = functools.partial(oracle_mod.preprocess, library=lib)
+    for pin in oracle_pins.PRE_PINS:
+        pin(pre, fwd)
