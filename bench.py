@@ -15,8 +15,10 @@ Also reported on the same line:
                 over state pools of >= 1 GiB so the 256 MB Infinity Cache cannot
                 hold them;
   workloads     the same prefill kernel on the 65,536-token sequence (whole, and
-                as 8 chunks of 8,192 carried in place through the state) and on
-                the 64-sequence mixed batch, against the same fp32 roofline;
+                as 8 chunks of 8,192 carried in place through the state), on
+                the 64-sequence mixed batch, through the state pool with
+                snapshots, and with fused preprocessing, against the same fp32
+                roofline;
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample;
   parity        the timed outputs re-checked against the oracle (sampled heads).
 
@@ -279,6 +281,25 @@ def main():
             "tokens_per_s": T / (msp / 1e3), "roofline_frac": flops / (msp / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
             "same_bits_as_plain": bool(torch.equal(outp.view(torch.int16), out.view(torch.int16)))}
         del pool, outp
+
+        # The benchmark batch's shape on raw inputs with both fused preprocessing steps
+        # (in-kernel q/k L2 norm; gate and beta from logits).
+        rw = synth.make_raw_workload(1001, w.lengths, h0_std=0.1)
+        rd = [t.to(dev) for t in (rw.q, rw.k, rw.v, rw.g, rw.beta, rw.h0, rw.cu_seqlens)]
+        A_log, dt_bias = rw.meta["A_log"].to(dev), rw.meta["dt_bias"].to(dev)
+        pre = gdn.make_preproc(norm_qk=True, eps=1e-6, A_log=A_log, dt_bias=dt_bias)
+        outr = torch.empty_like(out)
+        hTr = torch.empty_like(hT)
+
+        def fused(_i):
+            gdn.gdn_fwd_varlen(*rd, out=outr, hT=hTr, stream=stream, pre=pre)
+
+        per_f, _ = time_launches(fused, args.steps, 5, stream)
+        msf = float(np.median(per_f))
+        workloads["varlen_prefill_fused_preprocessing"] = {
+            "tokens": T, "n_seqs": w.n_seqs, "ms_median": msf, "tokens_per_s": T / (msf / 1e3),
+            "roofline_frac": flops / (msf / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+        del rd, outr, hTr
 
         lc = synth.long_context(1003)
         prefill_line("long_context_65536", lc)

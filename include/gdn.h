@@ -72,6 +72,34 @@ typedef enum gdn_dtype {
     GDN_BF16 = 1   /* q, k, v, out are bf16; out is rounded to nearest even */
 } gdn_dtype;
 
+/*
+ * Fused preprocessing (optional, through gdn_dims.pre; NULL means none).  These
+ * are the steps the gated delta rule layer runs right before the recurrence
+ * (Yang, Kautz, Hatamizadeh, ICLR 2025): L2-normalised queries and keys, a decay
+ * exp(g) with g = -exp(A_log) softplus(a + dt_bias) and a write strength
+ * beta = sigmoid(b).  The page "Defending Against the Training-Inference Numeric
+ * Mismatch in RL (Especially Linear Attention)" (section 3.1) keeps A_log in fp32,
+ * as here.  Done inside the kernels they cost no extra pass over HBM, and they
+ * are evaluated by one fixed sequence of fp32 operations in every kernel, so the
+ * bitwise contract covers them too.
+ *
+ *   GDN_PRE_QK_L2NORM   every query and key row x (dk values) is replaced by
+ *                       x * rsqrt(sum_i x_i^2 + eps) before use, in fp32
+ *                       (sum over leaves of 4 consecutive columns, pairwise).
+ *   GDN_PRE_GATE_LOGITS the `g` argument holds logits a and the `beta` argument
+ *                       logits b (fp32, [T][hv]); the kernels form
+ *                       g = -exp(A_log[h]) * softplus(a + dt_bias[h]) (softplus(x)
+ *                       = x for x > 20) and beta = sigmoid(b).
+ */
+enum { GDN_PRE_QK_L2NORM = 1, GDN_PRE_GATE_LOGITS = 2 };
+
+typedef struct gdn_preproc {
+    int32_t flags;          /* GDN_PRE_* bits */
+    float eps;              /* added to the sum of squares (finite, >= 0; 1e-6 is usual) */
+    const float *A_log;     /* [hv] fp32 device; required with GDN_PRE_GATE_LOGITS */
+    const float *dt_bias;   /* [hv] fp32 device, or NULL for zero */
+} gdn_preproc;
+
 typedef struct gdn_dims {
     int32_t n_seqs;        /* N sequences (prefill) or B decode rows; 0 is a no-op */
     int32_t hk;            /* query/key heads */
@@ -85,6 +113,7 @@ typedef struct gdn_dims {
     int32_t plan_rows;     /* launch shape: state rows per lane, 0 = automatic, else 1, 2 or 4 */
     int32_t plan_waves;    /* launch shape: waves per workgroup, 0 = automatic, else 1, 2, 4 or 8 */
     int32_t reserved;      /* must be 0 */
+    const gdn_preproc *pre; /* fused preprocessing, or NULL (host memory, read during the call) */
 } gdn_dims;
 /* plan_lanes / plan_rows / plan_waves choose how state rows are spread over
  * lanes, waves and workgroups.  They never change a single bit of any result
@@ -195,7 +224,7 @@ const char *gdn_status_string(gdn_status status);
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 103
+#define GDN_ABI_VERSION 200
 
 #ifdef __cplusplus
 }

@@ -2,6 +2,7 @@
 // dispatch to the per-dk kernels.  Everything here runs on the host before any work
 // is enqueued; nothing here reads device memory, allocates or synchronises.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "gdn.h"
@@ -88,7 +89,32 @@ gdn_status check_common(const gdn_dims *d) {
     if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_ERR_DTYPE;
     if (!dk_supported(d->dk)) return GDN_ERR_UNSUPPORTED;
     if (d->hv > 65535 || d->n_seqs > 65535) return GDN_ERR_SHAPE;  // decode grid y / z limits
+    if (const gdn_preproc *pre = d->pre) {
+        if (pre->flags & ~(GDN_PRE_QK_L2NORM | GDN_PRE_GATE_LOGITS)) return GDN_ERR_UNSUPPORTED;
+        if (!isfinite(pre->eps) || pre->eps < 0.f) return GDN_ERR_SHAPE;
+        if ((pre->flags & GDN_PRE_GATE_LOGITS) && !pre->A_log) return GDN_ERR_NULL;
+        if (!aligned(pre->A_log, 4) || !aligned(pre->dt_bias, 4)) return GDN_ERR_ALIGN;
+    }
     return GDN_OK;
+}
+
+// Device arrays the preprocessing reads (A_log, dt_bias), for the alias checks.
+Range pre_range(const gdn_dims *d, int which) {
+    const gdn_preproc *pre = d->pre;
+    if (!pre || !(pre->flags & GDN_PRE_GATE_LOGITS)) return Range{0, 0};
+    return range_of(which == 0 ? pre->A_log : pre->dt_bias, (uint64_t)d->hv * 4);
+}
+
+template <class Params>
+void apply_pre(const gdn_dims *d, Params &p) {
+    if (const gdn_preproc *pre = d->pre) {
+        p.pre_flags = pre->flags;
+        p.pre_eps = pre->eps;
+        if (pre->flags & GDN_PRE_GATE_LOGITS) {
+            p.A_log = pre->A_log;
+            p.dt_bias = pre->dt_bias;
+        }
+    }
 }
 
 gdn_status resolve_plan(const gdn_dims *d, bool decode, int64_t units, Plan *plan) {
@@ -181,9 +207,10 @@ gdn_status gdn_fwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
     const Range rg = range_of(g, gb_bytes), rb = range_of(beta, gb_bytes);
     const Range rh0 = range_of(h0, h0 ? s_bytes : 0), rhT = range_of(hT, hT ? s_bytes : 0);
     const Range rcu = range_of(cu_seqlens, (uint64_t)(N + 1) * 4), ro = range_of(out, vo_bytes);
-    for (Range in : {rq, rk, rv, rg, rb, rh0, rcu, rhT})
+    const Range ra = pre_range(dims, 0), rdb = pre_range(dims, 1);
+    for (Range in : {rq, rk, rv, rg, rb, rh0, rcu, rhT, ra, rdb})
         if (overlap(ro, in)) return GDN_ERR_ALIAS;
-    for (Range in : {rq, rk, rv, rg, rb, rcu})
+    for (Range in : {rq, rk, rv, rg, rb, rcu, ra, rdb})
         if (overlap(rhT, in)) return GDN_ERR_ALIAS;
     if (h0 && hT && h0 != hT && overlap(rh0, rhT)) return GDN_ERR_ALIAS;
 
@@ -191,6 +218,7 @@ gdn_status gdn_fwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0;
     p.cu_seqlens = cu_seqlens; p.out = out; p.hT = hT;
     p.pool_size = (int32_t)N;
+    apply_pre(dims, p);
     return launch_varlen(dims, p, stream);
 }
 
@@ -230,9 +258,10 @@ gdn_status gdn_fwd_varlen_pool(const gdn_dims *dims, const void *q, const void *
     const Range r0 = range_of(pos0, pos0 ? idx_bytes : 0);
     const Range rn = range_of(snap_idx, snap_block > 0 ? idx_bytes * (uint64_t)snap_per_seq : 0);
     const Range ro = range_of(out, vo_bytes);
-    for (Range in : {rq, rk, rv, rg, rb, rp, rcu, rs, rd, r0, rn})
+    const Range ra = pre_range(dims, 0), rdb = pre_range(dims, 1);
+    for (Range in : {rq, rk, rv, rg, rb, rp, rcu, rs, rd, r0, rn, ra, rdb})
         if (overlap(ro, in)) return GDN_ERR_ALIAS;
-    for (Range in : {rq, rk, rv, rg, rb, rcu, rs, rd, r0, rn})
+    for (Range in : {rq, rk, rv, rg, rb, rcu, rs, rd, r0, rn, ra, rdb})
         if (overlap(rp, in)) return GDN_ERR_ALIAS;
 
     PrefillParams p{};
@@ -246,6 +275,7 @@ gdn_status gdn_fwd_varlen_pool(const gdn_dims *dims, const void *q, const void *
     if (snap_block > 0) {
         p.snap_idx = snap_idx; p.snap_block = snap_block; p.snap_per_seq = snap_per_seq;
     }
+    apply_pre(dims, p);
     return launch_varlen(dims, p, stream);
 }
 
@@ -278,9 +308,10 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k, c
     const Range rg = range_of(g, gb_bytes), rb = range_of(beta, gb_bytes);
     const Range rp = range_of(state_pool, pool_bytes), ri = range_of(state_idx, state_idx ? (uint64_t)B * 4 : 0);
     const Range ro = range_of(out, vo_bytes);
-    for (Range in : {rq, rk, rv, rg, rb, rp, ri})
+    const Range ra = pre_range(dims, 0), rdb = pre_range(dims, 1);
+    for (Range in : {rq, rk, rv, rg, rb, rp, ri, ra, rdb})
         if (overlap(ro, in)) return GDN_ERR_ALIAS;
-    for (Range in : {rq, rk, rv, rg, rb, ri})
+    for (Range in : {rq, rk, rv, rg, rb, ri, ra, rdb})
         if (overlap(rp, in)) return GDN_ERR_ALIAS;
 
     Plan plan;
@@ -291,6 +322,7 @@ gdn_status gdn_decode_step(const gdn_dims *dims, const void *q, const void *k, c
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.pool = state_pool; p.state_idx = state_idx; p.out = out;
     p.batch = (int32_t)B; p.hk = d.hk; p.hv = d.hv; p.dv = d.dv; p.pool_size = d.pool_size;
+    apply_pre(dims, p);
     const hipError_t e = dispatch_decode(d.dk, p, d.io_dtype, plan, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

@@ -39,6 +39,10 @@ struct PrefillParams {
     int32_t snap_block, snap_per_seq;  // 0: no snapshots
     int32_t rank_by_length;  // workgroups take sequences longest first (n_seqs <= kMaxRankedSeqs)
     int32_t tiles;           // row tiles per value head (set by the launcher)
+    // fused preprocessing (gdn_preproc): GDN_PRE_* flags; g / beta hold logits when gated
+    const float *A_log, *dt_bias;
+    float pre_eps;
+    int32_t pre_flags;
 };
 
 // Kernel arguments of one decode step.
@@ -49,6 +53,9 @@ struct DecodeParams {
     const int32_t *state_idx;
     void *out;
     int32_t batch, hk, hv, dv, pool_size;
+    const float *A_log, *dt_bias;  // fused preprocessing, as in PrefillParams
+    float pre_eps;
+    int32_t pre_flags;
 };
 
 // A launch shape: `lanes` lanes hold one state row, each lane holds `rows` rows,

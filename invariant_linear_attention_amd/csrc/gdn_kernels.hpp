@@ -62,6 +62,35 @@ __device__ __forceinline__ float delta_coeff(float ab, float ptil, float bv) { r
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// ------------------------------------------------- fused preprocessing numerics
+//
+// One fixed sequence of fp32 operations per quantity, used by every kernel:
+//   softplus(x) = x for x > 20, else log2(1 + 2^(x log2 e)) ln 2   (hardware exp2/log2)
+//   g           = -exp(A_log) * softplus(a + dt_bias),  exp(A_log) = 2^(A_log log2 e)
+//   beta        = rcp(1 + 2^(-b log2 e))                            (hardware rcp)
+//   L2 norm     : x * rsq(sumsq + eps), sumsq over leaves of 4 consecutive columns
+//                 (x0*x0, then fma with x1, x2, x3), added pairwise in column order.
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.693147180559945309417f;
+
+__device__ __forceinline__ float softplus_f32(float x) {
+    return x > 20.f ? x : __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(x * kLog2e)) * kLn2;
+}
+__device__ __forceinline__ float gate_amplitude(float A_log) { return __builtin_amdgcn_exp2f(A_log * kLog2e); }
+__device__ __forceinline__ float gate_from_logit(float amp, float dt_bias, float a) {
+    return -amp * softplus_f32(a + dt_bias);
+}
+__device__ __forceinline__ float sigmoid_f32(float b) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-b * kLog2e));
+}
+__device__ __forceinline__ float sumsq4(float x0, float x1, float x2, float x3) {
+    float s = x0 * x0;
+    s = __builtin_fmaf(x1, x1, s);
+    s = __builtin_fmaf(x2, x2, s);
+    return __builtin_fmaf(x3, x3, s);
+}
+__device__ __forceinline__ float norm_scale(float sumsq, float eps) { return __builtin_amdgcn_rsqf(sumsq + eps); }
+
 // x + (x of the partner lane given by a DPP control)
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float x) {
@@ -80,19 +109,35 @@ __device__ __forceinline__ float lane_sum(float x) {
     return x;
 }
 
+// Pairwise tree over N partial sums held by one lane, in index order.
 template <int N>
 __device__ __forceinline__ float leaf_tree(const float (&x)[N]) {
     if constexpr (N == 1) {
         return x[0];
     } else if constexpr (N == 2) {
         return x[0] + x[1];
-    } else {
-        static_assert(N == 4, "leaf count");
+    } else if constexpr (N == 4) {
         return (x[0] + x[1]) + (x[2] + x[3]);
+    } else {
+        static_assert(N == 8, "leaf count");
+        return ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
     }
 }
 
 // Lane geometry for key dim DK with L lanes per row.
+// Sum over N consecutive lanes (N a power of two up to 32, groups aligned to N),
+// as a pairwise tree over lane index: every lane of the group gets the sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (N >= 2) x = dpp_add<0xB1>(x);
+    if constexpr (N >= 4) x = dpp_add<0x4E>(x);
+    if constexpr (N >= 8) x = dpp_add<0x141>(x);
+    if constexpr (N >= 16) x = dpp_add<0x140>(x);
+    if constexpr (N >= 32) x = x + __shfl_xor(x, 16);
+    static_assert(N >= 1 && N <= 32 && (N & (N - 1)) == 0, "group size");
+    return x;
+}
+
 template <int DK, int L>
 struct Geo {
     static_assert(DK == 16 || DK == 32 || DK == 64 || DK == 128, "unsupported dk");
@@ -309,23 +354,47 @@ struct Stager {
     // Columns [col, col + 4) of a key/query row go to their permuted LDS chunk.
     __device__ static float *row_slot(float *row, int col) { return row + 16 * G::lds_chunk(col / 16) + col % 16; }
 
-    __device__ __forceinline__ void store(PrefillLds<DK, IO, L, R, NW> &Ld, int buf, int tid) const {
+    // Row sum of squares of a key/query row: this thread's leaves of 4 columns
+    // (pairwise), then the KVEC threads of the row (a pairwise tree over thread
+    // index); every thread of the row gets it.  Threads past the staged items hold
+    // zeros and still take part, so whole lane groups run the cross-lane levels.
+    __device__ static float row_sumsq(const float (&f)[IO::VEC]) {
+        float leaves[IO::VEC / 4];
+#pragma unroll
+        for (int x = 0; x < IO::VEC / 4; ++x) leaves[x] = sumsq4(f[4 * x], f[4 * x + 1], f[4 * x + 2], f[4 * x + 3]);
+        return group_sum<Sh::KVEC>(leaf_tree<IO::VEC / 4>(leaves));
+    }
+
+    // pre: GDN_PRE_* flags; amp = exp(A_log[h]), dtb = dt_bias[h] (gated inputs only).
+    __device__ __forceinline__ void store(PrefillLds<DK, IO, L, R, NW> &Ld, int buf, int tid, int pre, float eps,
+                                          float amp, float dtb) const {
 #pragma unroll
         for (int s = 0; s < Sh::KSLOTS; ++s) {
             const int it = tid + s * Sh::NT;
+            const int ti = it / Sh::KVEC, vec = it % Sh::KVEC;
+            // Without the norm, slots past the staged items (whole waves, often) skip
+            // the unpacking; with it every lane of a row group must take part.
+            if (!(pre & GDN_PRE_QK_L2NORM) && it >= Sh::KITEMS) continue;
+            float fk[IO::VEC], fq[IO::VEC];
+            IO::unpack(kr[s], fk);
+            IO::unpack(qr[s], fq);
+            if (pre & GDN_PRE_QK_L2NORM) {
+                const float ik = norm_scale(row_sumsq(fk), eps), iq = norm_scale(row_sumsq(fq), eps);
+#pragma unroll
+                for (int x = 0; x < IO::VEC; ++x) {
+                    fk[x] = fk[x] * ik;
+                    fq[x] = fq[x] * iq;
+                }
+            }
             if (it < Sh::KITEMS) {
-                const int ti = it / Sh::KVEC, vec = it % Sh::KVEC;
-                float f[IO::VEC];
-                IO::unpack(kr[s], f);
 #pragma unroll
                 for (int x = 0; x < IO::VEC; x += 4)
                     *reinterpret_cast<float4 *>(row_slot(Ld.k[buf][ti], vec * IO::VEC + x)) =
-                        make_float4(f[x], f[x + 1], f[x + 2], f[x + 3]);
-                IO::unpack(qr[s], f);
+                        make_float4(fk[x], fk[x + 1], fk[x + 2], fk[x + 3]);
 #pragma unroll
                 for (int x = 0; x < IO::VEC; x += 4)
                     *reinterpret_cast<float4 *>(row_slot(Ld.q[buf][ti], vec * IO::VEC + x)) =
-                        make_float4(f[x], f[x + 1], f[x + 2], f[x + 3]);
+                        make_float4(fq[x], fq[x + 1], fq[x + 2], fq[x + 3]);
             }
         }
 #pragma unroll
@@ -335,8 +404,9 @@ struct Stager {
                 const int ti = it / Sh::VVEC, vec = it % Sh::VVEC;
                 float f[IO::VEC];
                 IO::unpack(vr[s], f);
+                const float bvs = (pre & GDN_PRE_GATE_LOGITS) ? sigmoid_f32(vbeta[s]) : vbeta[s];
 #pragma unroll
-                for (int x = 0; x < IO::VEC; ++x) f[x] = scaled_value(vbeta[s], f[x]);
+                for (int x = 0; x < IO::VEC; ++x) f[x] = scaled_value(bvs, f[x]);
 #pragma unroll
                 for (int x = 0; x < IO::VEC; x += 4)
                     *reinterpret_cast<float4 *>(&Ld.v[buf][ti][vec * IO::VEC + x]) =
@@ -344,9 +414,10 @@ struct Stager {
             }
         }
         if (tid < Sh::TS) {
-            const float a = decay_factor(gt);
+            const bool gated = pre & GDN_PRE_GATE_LOGITS;
+            const float a = decay_factor(gated ? gate_from_logit(amp, dtb, gt) : gt);
             Ld.a[buf][tid] = a;
-            Ld.ab[buf][tid] = scaled_decay(a, bt);
+            Ld.ab[buf][tid] = scaled_decay(a, gated ? sigmoid_f32(bt) : bt);
         }
     }
 };
@@ -426,9 +497,10 @@ __device__ __forceinline__ WorkItem work_item(const PrefillParams &p, int id) {
 #endif
 
 // One workgroup = (sequence, value head, row tile), from blockIdx.x (see work_item).
-// SNAP compiles the snapshot support (block grid aligned to absolute positions);
-// without it the token loop carries none of that logic.
-template <int DK, class IO, int L, int R, int NW, bool SNAP>
+// EXT compiles the extended features, state snapshots (block grid aligned to
+// absolute positions) and fused preprocessing; without it the kernel carries
+// none of that logic.
+template <int DK, class IO, int L, int R, int NW, bool EXT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GDN_PREFILL_WAVES_PER_EU)))
 void gdn_prefill_kernel(PrefillParams p) {
     using Sh = PrefillShape<DK, IO, L, R, NW>;
@@ -496,14 +568,14 @@ void gdn_prefill_kernel(PrefillParams p) {
     // snap_block (itself a multiple of TB) is the end of some block.  Without
     // snapshots lo0 = 0 and block b simply covers tokens [tb + b TB, tb + (b+1) TB).
     int64_t base = 0;
-    if (SNAP && p.pos0) {
+    if (EXT && p.snap_block > 0 && p.pos0) {
         base = p.pos0[n];
         base = base < 0 ? 0 : base;
     }
-    const int lo0 = SNAP ? (int)(base % TB) : 0;
+    const int lo0 = EXT ? (int)(base % TB) : 0;
     auto snapshot_after = [&](int64_t done) {  // done: tokens of this call behind the state
         const int64_t pos = base + done;
-        if (!SNAP || p.snap_block <= 0 || done <= 0 || pos % p.snap_block != 0) return;
+        if (!EXT || p.snap_block <= 0 || done <= 0 || pos % p.snap_block != 0) return;
         const int64_t j = pos / p.snap_block - base / p.snap_block - 1;
         if (j < 0 || j >= p.snap_per_seq) return;
         const int64_t slot = p.snap_idx[(int64_t)n * p.snap_per_seq + j];
@@ -512,9 +584,12 @@ void gdn_prefill_kernel(PrefillParams p) {
 
     if (len > 0) {
         const int nblk = (int)((len + lo0 + TB - 1) / TB);
+        const int pre = EXT ? p.pre_flags : 0;
+        const float amp = (pre & GDN_PRE_GATE_LOGITS) ? gate_amplitude(p.A_log[h]) : 0.f;
+        const float dtb = ((pre & GDN_PRE_GATE_LOGITS) && p.dt_bias) ? p.dt_bias[h] : 0.f;
         Stager<DK, IO, L, R, NW> st;
         st.load(p, tb - lo0, tb, te, kh, h, row0, tid);
-        st.store(Ld, 0, tid);
+        st.store(Ld, 0, tid, pre, p.pre_eps, amp, dtb);
         __syncthreads();
 
         // LDS float offsets of this lane's chunks within a staged row.
@@ -555,14 +630,14 @@ void gdn_prefill_kernel(PrefillParams p) {
         TokRegs<C, R> A, B;
         float ptil[R];
         fetch(A, 0, lo0);
-        if constexpr (SNAP) B = A;
+        if constexpr (EXT) B = A;
         row_dots<DK, L, R>(S, A.k, ptil);
 
         for (int blk = 0; blk < nblk; ++blk) {
             const int buf = blk & 1;
             // Slot ti of this block is token t0 + ti; slots [lo, nt) are tokens of the
             // sequence (lo > 0 only in a first block that starts mid-grid).
-            const int lo = (SNAP && blk == 0) ? lo0 : 0;
+            const int lo = (EXT && blk == 0) ? lo0 : 0;
             const int64_t t0 = tb - lo0 + (int64_t)blk * TB;
             if (blk + 1 < nblk) st.load(p, t0 + TB, tb, te, kh, h, row0, tid);
             const int nt = (int)((te - t0) < TB ? (te - t0) : TB);
@@ -586,7 +661,7 @@ void gdn_prefill_kernel(PrefillParams p) {
                 for (int r = 1; r < R; ++r)
                     if (my_r == r) ov = o[r];
                 if (my_slot == ti % TT) obuf = ov;
-                if (ti % TT == TT - 1 && (!SNAP || ti - (TT - 1) + my_slot >= lo))
+                if (ti % TT == TT - 1 && (!EXT || ti - (TT - 1) + my_slot >= lo))
                     IO::store1(p.out, (size_t)(t0 + ti - (TT - 1) + my_slot) * p.hv * p.dv + out_row, obuf);
             };
 
@@ -618,11 +693,11 @@ void gdn_prefill_kernel(PrefillParams p) {
                 }
             }
             const int rem = nt % TT;  // tokens kept but not yet stored (partial block only)
-            if (rem != 0 && my_slot < rem && (!SNAP || nt - rem + my_slot >= lo))
+            if (rem != 0 && my_slot < rem && (!EXT || nt - rem + my_slot >= lo))
                 IO::store1(p.out, (size_t)(t0 + nt - rem + my_slot) * p.hv * p.dv + out_row, obuf);
-            if constexpr (SNAP) snapshot_after(t0 + nt - tb);
+            if constexpr (EXT) snapshot_after(t0 + nt - tb);
 
-            if (blk + 1 < nblk) st.store(Ld, buf ^ 1, tid);
+            if (blk + 1 < nblk) st.store(Ld, buf ^ 1, tid, pre, p.pre_eps, amp, dtb);
             __syncthreads();
         }
     }
@@ -637,7 +712,7 @@ void gdn_prefill_kernel(PrefillParams p) {
 
 // One workgroup = (batch row b = blockIdx.z, value head h = blockIdx.y, row tile blockIdx.x).
 // Four lanes per row: the state streams once through registers.
-template <int DK, class IO, int R, int NW>
+template <int DK, class IO, int R, int NW, bool EXT>
 __global__ __launch_bounds__(NW * 64) void gdn_decode_kernel(DecodeParams p) {
     constexpr int L = 4;
     using G = Geo<DK, L>;
@@ -678,8 +753,34 @@ __global__ __launch_bounds__(NW * 64) void gdn_decode_kernel(DecodeParams p) {
         kx[4 * j + 0] = k4.x; kx[4 * j + 1] = k4.y; kx[4 * j + 2] = k4.z; kx[4 * j + 3] = k4.w;
         qx[4 * j + 0] = q4.x; qx[4 * j + 1] = q4.y; qx[4 * j + 2] = q4.z; qx[4 * j + 3] = q4.w;
     }
-    const float a = decay_factor(p.g[(size_t)b * p.hv + h]);
-    const float beta = p.beta[(size_t)b * p.hv + h];
+    const int pre = EXT ? p.pre_flags : 0;
+    if (pre & GDN_PRE_QK_L2NORM) {
+        // The staging order of the prefill kernel: leaves of 4 columns (this lane
+        // holds leaf 4j + lam of chunk j), pairs across lam, then chunks pairwise.
+        float ck[G::NCH], cq[G::NCH];
+#pragma unroll
+        for (int j = 0; j < G::NCH; ++j) {
+            ck[j] = group_sum<4>(sumsq4(kx[4 * j], kx[4 * j + 1], kx[4 * j + 2], kx[4 * j + 3]));
+            cq[j] = group_sum<4>(sumsq4(qx[4 * j], qx[4 * j + 1], qx[4 * j + 2], qx[4 * j + 3]));
+        }
+        const float ik = norm_scale(leaf_tree<G::NCH>(ck), p.pre_eps);
+        const float iq = norm_scale(leaf_tree<G::NCH>(cq), p.pre_eps);
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            kx[i] = kx[i] * ik;
+            qx[i] = qx[i] * iq;
+        }
+    }
+    float a, beta;
+    if (pre & GDN_PRE_GATE_LOGITS) {
+        const float amp = gate_amplitude(p.A_log[h]);
+        const float dtb = p.dt_bias ? p.dt_bias[h] : 0.f;
+        a = decay_factor(gate_from_logit(amp, dtb, p.g[(size_t)b * p.hv + h]));
+        beta = sigmoid_f32(p.beta[(size_t)b * p.hv + h]);
+    } else {
+        a = decay_factor(p.g[(size_t)b * p.hv + h]);
+        beta = p.beta[(size_t)b * p.hv + h];
+    }
     const float ab = scaled_decay(a, beta);
 
     float ptil[R], u[R], o[R];
@@ -711,8 +812,9 @@ hipError_t launch_prefill_t(const PrefillParams &p, hipStream_t s) {
     q.tiles = p.dv / RW;
     dim3 grid((unsigned)q.tiles * p.hv * p.n_seqs), block(NW * 64);
     void *args[] = {&q};
-    const void *fn = p.snap_block > 0 ? reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, L, R, NW, true>)
-                                      : reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, L, R, NW, false>);
+    const bool ext = p.snap_block > 0 || p.pre_flags != 0;
+    const void *fn = ext ? reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, L, R, NW, true>)
+                         : reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, L, R, NW, false>);
     return hipLaunchKernel(fn, grid, block, args, 0, s);
 }
 
@@ -721,8 +823,9 @@ hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s) {
     constexpr int RW = NW * 16 * R;
     dim3 grid(p.dv / RW, p.hv, p.batch), block(NW * 64);
     void *args[] = {const_cast<DecodeParams *>(&p)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gdn_decode_kernel<DK, IO, R, NW>), grid, block, args, 0,
-                           s);
+    const void *fn = p.pre_flags != 0 ? reinterpret_cast<const void *>(&gdn_decode_kernel<DK, IO, R, NW, true>)
+                                      : reinterpret_cast<const void *>(&gdn_decode_kernel<DK, IO, R, NW, false>);
+    return hipLaunchKernel(fn, grid, block, args, 0, s);
 }
 
 }  // namespace gdn

@@ -23,6 +23,15 @@ EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_quer
            "gdn_abi_version")
 
 
+GDN_PRE_QK_L2NORM, GDN_PRE_GATE_LOGITS = 1, 2
+
+
+class GdnPreproc(ctypes.Structure):
+    """Mirror of ``gdn_preproc``."""
+    _fields_ = [("flags", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
+
+
 class GdnDims(ctypes.Structure):
     """Mirror of ``gdn_dims``."""
     _fields_ = [
@@ -30,7 +39,7 @@ class GdnDims(ctypes.Structure):
         ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
         ("total_tokens", ctypes.c_int64), ("pool_size", ctypes.c_int32),
         ("plan_lanes", ctypes.c_int32), ("plan_rows", ctypes.c_int32), ("plan_waves", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("pre", ctypes.POINTER(GdnPreproc)),
     ]
 
 
@@ -114,16 +123,32 @@ def _need(t, name, dtype=None, cuda=True):
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
 
 
-def make_dims(q, v, n_seqs: int, total_tokens: int, pool_size: int = 0, plan=(0, 0, 0)) -> GdnDims:
+def make_preproc(norm_qk: bool = False, eps: float = 1e-6, A_log=None, dt_bias=None) -> GdnPreproc:
+    """Fused preprocessing (see gdn_preproc in include/gdn.h): ``norm_qk`` L2-normalises
+    q and k rows in the kernel; with ``A_log`` (fp32 [Hv] on the GPU) the ``g`` and
+    ``beta`` arguments of the call are the logits a and b, and the kernel forms
+    g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b)."""
+    import torch
+    _need(A_log, "A_log", torch.float32)
+    _need(dt_bias, "dt_bias", torch.float32)
+    flags = (GDN_PRE_QK_L2NORM if norm_qk else 0) | (GDN_PRE_GATE_LOGITS if A_log is not None else 0)
+    pre = GdnPreproc(flags=flags, eps=float(eps), A_log=_ptr(A_log), dt_bias=_ptr(dt_bias))
+    pre._keep = (A_log, dt_bias)
+    return pre
+
+
+def make_dims(q, v, n_seqs: int, total_tokens: int, pool_size: int = 0, plan=(0, 0, 0), pre=None) -> GdnDims:
     """``plan`` = (lanes per row, rows per lane, waves per workgroup); 0 = automatic.
-    A 2-tuple means (rows, waves) with automatic lanes."""
+    A 2-tuple means (rows, waves) with automatic lanes.  ``pre``: a GdnPreproc or None."""
     plan = tuple(int(x) for x in plan)
     if len(plan) == 2:
         plan = (0,) + plan
-    return GdnDims(n_seqs=int(n_seqs), hk=int(q.shape[1]), hv=int(v.shape[1]), dk=int(q.shape[2]),
+    dims = GdnDims(n_seqs=int(n_seqs), hk=int(q.shape[1]), hv=int(v.shape[1]), dk=int(q.shape[2]),
                    dv=int(v.shape[2]), io_dtype=_io_code(q), total_tokens=int(total_tokens),
                    pool_size=int(pool_size), plan_lanes=plan[0], plan_rows=plan[1], plan_waves=plan[2],
-                   reserved=0)
+                   reserved=0, pre=ctypes.pointer(pre) if pre is not None else None)
+    dims._keep = pre
+    return dims
 
 
 def gdn_query_plan(dims: GdnDims, decode: bool = False) -> Tuple[int, int, int]:
@@ -135,7 +160,7 @@ def gdn_query_plan(dims: GdnDims, decode: bool = False) -> Tuple[int, int, int]:
 
 
 def gdn_fwd_varlen(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, stream=None, plan=(0, 0, 0),
-                   want_state: bool = True):
+                   want_state: bool = True, pre=None):
     """Varlen prefill (see include/gdn.h).  Tensors on the GPU, contiguous:
     q, k [T, Hk, dk]; v [T, Hv, dv]; g, beta [T, Hv] fp32; h0 [N, Hv, dv, dk] fp32
     or None; cu_seqlens [N+1] int32.  ``out`` / ``hT`` are allocated when None
@@ -156,14 +181,14 @@ def gdn_fwd_varlen(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, stream=N
         hT = torch.empty((N, v.shape[1], v.shape[2], q.shape[2]), dtype=torch.float32, device=q.device)
     _need(out, "out", q.dtype)
     _need(hT, "hT", torch.float32)
-    dims = make_dims(q, v, N, T, plan=plan)
+    dims = make_dims(q, v, N, T, plan=plan, pre=pre)
     _check(lib.gdn_fwd_varlen(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
                               _ptr(cu_seqlens), _ptr(out), _ptr(hT), _stream_handle(stream)))
     return out, hT
 
 
 def gdn_fwd_varlen_pool(q, k, v, g, beta, cu_seqlens, state_pool, src_idx=None, dst_idx=None, pos0=None,
-                        snap_idx=None, snap_block: int = 0, out=None, stream=None, plan=(0, 0, 0)):
+                        snap_idx=None, snap_block: int = 0, out=None, stream=None, plan=(0, 0, 0), pre=None):
     """Varlen prefill against a state pool (see include/gdn.h).  state_pool
     [P, Hv, dv, dk] fp32 is read and written in place; src_idx / dst_idx / pos0
     [N] int32 or None; snap_idx [N, S] int32 (required when snap_block > 0).
@@ -188,7 +213,7 @@ def gdn_fwd_varlen_pool(q, k, v, g, beta, cu_seqlens, state_pool, src_idx=None, 
     if out is None:
         out = torch.empty((T, v.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
     _need(out, "out", q.dtype)
-    dims = make_dims(q, v, N, T, pool_size=int(state_pool.shape[0]), plan=plan)
+    dims = make_dims(q, v, N, T, pool_size=int(state_pool.shape[0]), plan=plan, pre=pre)
     _check(lib.gdn_fwd_varlen_pool(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                    _ptr(cu_seqlens), _ptr(state_pool), _ptr(src_idx), _ptr(dst_idx), _ptr(pos0),
                                    _ptr(snap_idx), int(snap_block), snap_per_seq, _ptr(out),
@@ -196,7 +221,7 @@ def gdn_fwd_varlen_pool(q, k, v, g, beta, cu_seqlens, state_pool, src_idx=None, 
     return out
 
 
-def gdn_decode_step(q, k, v, g, beta, state_pool, state_idx=None, out=None, stream=None, plan=(0, 0, 0)):
+def gdn_decode_step(q, k, v, g, beta, state_pool, state_idx=None, out=None, stream=None, plan=(0, 0, 0), pre=None):
     """One decode token per sequence (see include/gdn.h).  q, k [B, Hk, dk];
     v [B, Hv, dv]; g, beta [B, Hv]; state_pool [P, Hv, dv, dk] fp32 updated in
     place; state_idx [B] int32 or None (identity).  Returns out [B, Hv, dv]."""
@@ -212,7 +237,7 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, state_idx=None, out=None, stre
     if out is None:
         out = torch.empty((B, v.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
     _need(out, "out", q.dtype)
-    dims = make_dims(q, v, B, B, pool_size=int(state_pool.shape[0]), plan=plan)
+    dims = make_dims(q, v, B, B, pool_size=int(state_pool.shape[0]), plan=plan, pre=pre)
     _check(lib.gdn_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(state_pool), _ptr(state_idx), _ptr(out), _stream_handle(stream)))
     return out

@@ -101,6 +101,38 @@ def make_workload(seed: int, lengths, hk=HK, hv=HV, dk=DK, dv=DV, io_dtype=torch
                     meta=dict(seed=int(seed)))
 
 
+def make_raw_workload(seed: int, lengths, hk=HK, hv=HV, dk=DK, dv=DV, io_dtype=torch.bfloat16,
+                      h0_std: float = 0.0, name: str = "") -> Workload:
+    """Raw inputs for the fused-preprocessing path.
+
+    q, k: N(0, 1) rows scaled by a per-(token, head) factor in [0.25, 4], not
+    normalised; v: N(0, 1); the ``g`` and ``beta`` fields hold the logits a, b
+    ~ N(0, 1); meta["A_log"] = log U(1, 16) and meta["dt_bias"] ~ U(ln 1e-3, ln 0.1)
+    per value head (fp32), the usual initial ranges of a decay amplitude and of
+    its time-step bias.
+    """
+    gen = torch.Generator().manual_seed(int(seed) + 104729)
+    lengths = [int(n) for n in lengths]
+    T = sum(lengths)
+
+    def rows(shape):
+        x = _normal(gen, shape)
+        scale = torch.exp2(torch.rand(shape[:-1] + (1,), generator=gen) * 4.0 - 2.0)
+        return (x * scale).to(io_dtype)
+
+    q = rows((T, hk, dk))
+    k = rows((T, hk, dk))
+    v = _normal(gen, (T, hv, dv)).to(io_dtype)
+    a = _normal(gen, (T, hv))
+    b = _normal(gen, (T, hv))
+    A_log = torch.log(1.0 + 15.0 * torch.rand((hv,), generator=gen))
+    dt_bias = math.log(1e-3) + (math.log(0.1) - math.log(1e-3)) * torch.rand((hv,), generator=gen)
+    h0 = _normal(gen, (len(lengths), hv, dv, dk)) * float(h0_std) if h0_std > 0 else None
+    return Workload(q.contiguous(), k.contiguous(), v.contiguous(), a.contiguous(), b.contiguous(),
+                    cu_from_lengths(lengths), h0, name=name or "raw",
+                    meta=dict(seed=int(seed), A_log=A_log.float(), dt_bias=dt_bias.float(), raw=True))
+
+
 # ---------------------------------------------------------------- the workloads
 
 def tiny(seed: int = 1000) -> Workload:

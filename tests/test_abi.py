@@ -254,3 +254,69 @@ def test_plan_rejects_like_the_entry_points():
 
 def test_plan_null_shape(lib):
     assert lib.gdn_query_plan(ctypes.byref(_dims()), 0, None) == 1
+
+
+# ------------------------------------------------------ fused preprocessing
+
+def test_preproc_layout_matches_c(tmp_path):
+    from invariant_linear_attention_amd.gdn import GdnPreproc
+    src = tmp_path / "pre.c"
+    fields = [f[0] for f in GdnPreproc._fields_]
+    body = "".join('printf("%s %%zu\\n", offsetof(gdn_preproc, %s));' % (f, f) for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "gdn.h"\n'
+                   'int main(void){printf("size %%zu\\n", sizeof(gdn_preproc));%s return 0;}\n' % body)
+    exe = tmp_path / "pre"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.check_output([str(exe)]).decode().splitlines())
+    assert int(out["size"]) == ctypes.sizeof(GdnPreproc)
+    for f in fields:
+        assert int(out[f]) == getattr(GdnPreproc, f).offset, f
+
+
+def _pre_dims(flags=3, eps=1e-6, A_log=BASE + 40 * MB, dt_bias=BASE + 41 * MB, **kw):
+    from invariant_linear_attention_amd.gdn import GdnPreproc
+    pre = GdnPreproc(flags=flags, eps=eps, A_log=A_log, dt_bias=dt_bias)
+    d = _dims(**kw)
+    d.pre = ctypes.pointer(pre)
+    d._keep = pre
+    return d
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=4), 6),                        # unknown flag
+    (dict(flags=-1), 6),
+    (dict(eps=-1.0), 2),
+    (dict(eps=float("nan")), 2),
+    (dict(eps=float("inf")), 2),
+    (dict(A_log=None), 1),                     # the gate needs A_log
+    (dict(A_log=BASE + 40 * MB + 2), 4),
+    (dict(dt_bias=BASE + 41 * MB + 1), 4),
+])
+def test_preproc_rejected_everywhere(lib, kw, code):
+    assert call_fwd(lib, _pre_dims(**kw)) == code
+    assert call_dec(lib, _pre_dims(total_tokens=2, pool_size=4, **kw)) == code
+    assert call_pool(lib, _pre_dims(pool_size=4, **kw)) == code
+    from invariant_linear_attention_amd import gdn
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.gdn_query_plan(_pre_dims(**kw))
+    assert e.value.code == code
+
+
+def test_preproc_norm_only_needs_no_gate_arrays(lib):
+    # flags = norm only: A_log NULL is fine; nothing launches because hk = 3 is bad
+    assert call_fwd(lib, _pre_dims(flags=1, A_log=None, dt_bias=None, hk=3)) == 2
+    from invariant_linear_attention_amd import gdn
+    lanes, rows, waves = gdn.gdn_query_plan(_pre_dims(flags=1, A_log=None, dt_bias=None))
+    assert lanes in (4, 8, 16) and rows in (1, 2, 4) and waves in (1, 2, 4, 8)
+
+
+@pytest.mark.parametrize("over", [dict(out=BASE + 40 * MB), dict(hT=BASE + 41 * MB)])
+def test_preproc_outputs_may_not_overlap_gate_arrays(lib, over):
+    assert call_fwd(lib, _pre_dims(), **over) == 5
+
+
+def test_preproc_pool_and_decode_alias(lib):
+    assert call_pool(lib, _pre_dims(pool_size=4), out=BASE + 40 * MB) == 5
+    assert call_pool(lib, _pre_dims(pool_size=4), pool=BASE + 41 * MB) == 5
+    assert call_dec(lib, _pre_dims(total_tokens=2, pool_size=4), out=BASE + 41 * MB) == 5
+    assert call_dec(lib, _pre_dims(total_tokens=2, pool_size=4), pool=BASE + 40 * MB) == 5
