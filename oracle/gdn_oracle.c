@@ -206,6 +206,67 @@ int gdn_oracle_preprocess(int64_t T, int32_t hk, int32_t hv, int32_t dk, int32_t
     return 0;
 }
 
+/*
+ * Short causal convolution of the gated delta rule layer, in fp64: for every
+ * sequence n, channel c and token t of the sequence, with K taps,
+ *
+ *   z[t][c] = bias[c] + sum_{j=0}^{K-1} w[c][j] * x(t - (K-1) + j, c)
+ *   y[t][c] = z / (1 + exp(-z))        (SiLU; with silu == 0, y = z)
+ *
+ * where x(s, c) for s before the sequence's first token is taken from the
+ * sequence's convolution state: state[n][c][m] holds the input m - (K-1) tokens
+ * before the first token (m = 0 .. K-2, oldest first), or 0 when state is NULL.
+ * After the sequence, state_out[n][c][m] = x(last - (K-2) + m, c), i.e. the last
+ * K-1 inputs, again oldest first (reaching back into the old state when the
+ * sequence is shorter than K-1).  This is the depthwise causal convolution with
+ * a carried state that the layer runs on its q, k and v projections (Yang, Kautz,
+ * Hatamizadeh, ICLR 2025); the page "Defending Against the Training-Inference
+ * Numeric Mismatch in RL (Especially Linear Attention)" (section 3.2, "Solution")
+ * keeps that conv state in the serving stack's cache.
+ *
+ * x: [T][C] in io_dtype (0 fp32, 1 bf16); w: [C][K] fp32; bias: [C] fp32 or NULL;
+ * state, state_out: [N][C][K-1] fp64 (either may be NULL); y: [T][C] fp64.
+ */
+int gdn_oracle_short_conv(int32_t n_seqs, const int32_t *cu_seqlens, int32_t C, int32_t K, int32_t io_dtype,
+                          const void *x, const float *w, const float *bias, const double *state,
+                          int32_t silu, double *y, double *state_out)
+{
+    if (n_seqs < 0 || C <= 0 || K < 1 || (io_dtype != 0 && io_dtype != 1))
+        return -1;
+    if (n_seqs == 0)
+        return 0;
+    if (!cu_seqlens || !w || (cu_seqlens[n_seqs] > 0 && (!x || !y)))
+        return -4;
+    const int32_t M = K - 1;
+    for (int32_t n = 0; n < n_seqs; ++n) {
+        const int64_t tb = cu_seqlens[n], te = cu_seqlens[n + 1];
+        if (te < tb)
+            return -5;
+        for (int32_t c = 0; c < C; ++c) {
+            /* x(s, c) for s = tb - M .. te - 1, as a plain array: the old state first */
+            const int64_t len = te - tb;
+            double *win = (double *)malloc(sizeof(double) * (size_t)(M + len + 1));
+            if (!win)
+                return -6;
+            for (int32_t m = 0; m < M; ++m)
+                win[m] = state ? state[((int64_t)n * C + c) * M + m] : 0.0;
+            for (int64_t t = 0; t < len; ++t)
+                win[M + t] = oracle_load(x, (tb + t) * C + c, io_dtype);
+            for (int64_t t = 0; t < len; ++t) {
+                double z = bias ? (double)bias[c] : 0.0;
+                for (int32_t j = 0; j < K; ++j)
+                    z += (double)w[(int64_t)c * K + j] * win[t + j];
+                y[(tb + t) * C + c] = silu ? z / (1.0 + exp(-z)) : z;
+            }
+            if (state_out)
+                for (int32_t m = 0; m < M; ++m)
+                    state_out[((int64_t)n * C + c) * M + m] = win[len + m];
+            free(win);
+        }
+    }
+    return 0;
+}
+
 int gdn_oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -60,6 +60,11 @@ def load(library: str = LIBRARY):
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_double,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
     ]
+    c = lib.gdn_oracle_short_conv
+    c.restype = ctypes.c_int
+    c.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p]
     lib.gdn_oracle_max_threads.restype = ctypes.c_int
     lib.gdn_oracle_max_threads.argtypes = []
     return lib
@@ -213,3 +218,52 @@ def gdn_forward_fused(q, k, v, a, b, cu_seqlens, h0=None, A_log=None, dt_bias=No
 
 def max_threads() -> int:
     return int(_get_lib().gdn_oracle_max_threads())
+
+
+def short_conv(x, w, cu_seqlens, bias=None, state=None, silu=True, library=None):
+    """fp64 short causal convolution with a carried state (see gdn_oracle_short_conv).
+
+    x: [T, C] fp32 or bf16; w: [C, K] fp32; bias: [C] fp32 or None; state:
+    [N, C, K-1] (fp32, bf16 or fp64; widened exactly) or None.
+    Returns (y [T, C] float64, state_out [N, C, K-1] float64).
+    """
+    xn, xc = _as_numpy(x)
+    if xc not in (0, 1):
+        raise TypeError("x must be fp32 or bf16")
+    wn, wc = _as_numpy(w)
+    if wc != 0 or wn.ndim != 2:
+        raise TypeError("w must be fp32 [C, K]")
+    cu, cc = _as_numpy(cu_seqlens)
+    if cc != 3:
+        raise TypeError("cu_seqlens must be int32")
+    T, C = xn.shape
+    K = wn.shape[1]
+    if wn.shape[0] != C:
+        raise ValueError("w must be [C, K]")
+    n = cu.shape[0] - 1
+    bn = None
+    if bias is not None:
+        bn, bc = _as_numpy(bias)
+        if bc != 0 or bn.shape != (C,):
+            raise ValueError("bias must be fp32 [C]")
+    sn = None
+    if state is not None:
+        sn, sc = _as_numpy(state)
+        if sc == 1:
+            import torch
+            sn = torch.from_numpy(sn.view(np.int16)).view(torch.bfloat16).float().numpy()
+        sn = np.ascontiguousarray(sn, dtype=np.float64)
+        if sn.shape != (n, C, K - 1):
+            raise ValueError("state must be [N, C, K-1]")
+    y = np.zeros((T, C), dtype=np.float64)
+    so = np.zeros((max(n, 0), C, K - 1), dtype=np.float64)
+    lib = load(library) if library is not None else _get_lib()
+
+    def ptr(a):
+        return None if a is None or a.size == 0 else a.ctypes.data
+
+    rc = lib.gdn_oracle_short_conv(n, ptr(cu), C, K, xc, ptr(xn), ptr(wn), ptr(bn), ptr(sn), 1 if silu else 0,
+                                   ptr(y), ptr(so))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (code %d)" % rc)
+    return y, so

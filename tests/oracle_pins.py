@@ -486,3 +486,101 @@ PRE_PINS = [
     pin_pre_full_forget_through_the_rule,
     pin_pre_bf16_rows,
 ]
+
+
+# ------------------------------------------------------------ short conv
+#
+# Pins for oracle.short_conv (causal depthwise convolution with a carried state,
+# then SiLU).  Each takes a ``conv`` callable with its signature.
+
+def _conv_case(seed, lengths, C, K, with_state=True):
+    r = _rng(seed)
+    T = int(sum(lengths))
+    x = r.standard_normal((T, C)).astype(np.float32)
+    w = r.standard_normal((C, K)).astype(np.float32)
+    bias = r.standard_normal(C).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    state = r.standard_normal((len(lengths), C, K - 1)) if with_state else None
+    return x, w, bias, cu, state
+
+
+def pin_conv_impulse_response(conv):
+    """A unit impulse at token t0 (zero state) comes out as the taps, newest tap first."""
+    C, K, T, t0 = 3, 4, 12, 5
+    x = np.zeros((T, C), dtype=np.float32)
+    x[t0] = 1.0
+    w = _rng(201).standard_normal((C, K)).astype(np.float32)
+    y, _ = conv(x, w, np.array([0, T], dtype=np.int32), silu=False)
+    for d in range(K):
+        _close(y[t0 + d], w[:, K - 1 - d].astype(np.float64), 1e-15, "impulse tap %d" % d)
+    assert not y[:t0].any() and not y[t0 + K:].any(), "response outside the taps"
+
+
+def pin_conv_matches_numpy_convolve(conv):
+    """Per channel, y is numpy's full convolution of [old state, x] with the taps."""
+    x, w, bias, cu, state = _conv_case(202, [9, 1, 5], C=4, K=4)
+    y, so = conv(x, w, cu, bias=bias, state=state, silu=False)
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        for c in range(x.shape[1]):
+            sig = np.concatenate([state[n, c], x[a:b, c].astype(np.float64)])
+            full = np.convolve(sig, w[c, ::-1].astype(np.float64))
+            want = full[w.shape[1] - 1:w.shape[1] - 1 + (b - a)] + float(bias[c])
+            _close(y[a:b, c], want, 1e-13, "channel %d of sequence %d" % (c, n))
+            _close(so[n, c], sig[len(sig) - (w.shape[1] - 1):], 0.0 + 1e-300, "state out")
+
+
+def pin_conv_state_carry(conv):
+    """Cutting a sequence and carrying the fp64 state reproduces it exactly."""
+    x, w, bias, cu, state = _conv_case(203, [17], C=5, K=4)
+    y, so = conv(x, w, cu, bias=bias, state=state)
+    st = state
+    parts = []
+    for a, b in ((0, 2), (2, 3), (3, 11), (11, 17)):
+        yp, st = conv(x[a:b], w, np.array([0, b - a], dtype=np.int32), bias=bias, state=st)
+        parts.append(yp)
+    assert np.array_equal(np.concatenate(parts), y) and np.array_equal(st, so)
+
+
+def pin_conv_causal(conv):
+    x, w, bias, cu, state = _conv_case(204, [10], C=2, K=4)
+    y, _ = conv(x, w, cu, bias=bias, state=state)
+    x2 = x.copy()
+    x2[6:] = 7.0
+    y2, _ = conv(x2, w, cu, bias=bias, state=state)
+    assert np.array_equal(y[:6], y2[:6]) and not np.array_equal(y[6:], y2[6:])
+
+
+def pin_conv_constant_and_silu(conv):
+    """Constant input a, zero state, no bias: a * sum(w) once the window is full;
+    SiLU values silu(0) = 0 and silu(ln 3) = (3/4) ln 3 from bias alone."""
+    C, K, T = 2, 4, 8
+    w = _rng(205).standard_normal((C, K)).astype(np.float32)
+    x = np.full((T, C), 1.5, dtype=np.float32)
+    y, _ = conv(x, w, np.array([0, T], dtype=np.int32), silu=False)
+    _close(y[K - 1:], np.tile(1.5 * w.astype(np.float64).sum(axis=1), (T - K + 1, 1)), 1e-15, "constant input")
+    bias = np.array([0.0, math.log(3.0)], dtype=np.float32)
+    y0, _ = conv(np.zeros((3, C), dtype=np.float32), w, np.array([0, 3], dtype=np.int32), bias=bias)
+    assert np.all(y0[:, 0] == 0.0)
+    # bias[1] is ln 3 rounded to fp32, which moves silu by ~5e-9 relative
+    _close(y0[:, 1], np.full(3, 0.75 * math.log(3.0)), 1e-7, "silu(ln 3)")
+
+
+def pin_conv_short_sequence_state(conv):
+    """A sequence shorter than K-1 keeps the newest part of the old state."""
+    C, K = 1, 4
+    w = np.ones((C, K), dtype=np.float32)
+    state = np.array([[[10.0, 20.0, 30.0]]])
+    x = np.array([[1.0]], dtype=np.float32)
+    y, so = conv(x, w, np.array([0, 1], dtype=np.int32), state=state, silu=False)
+    assert y[0, 0] == 61.0 and np.array_equal(so[0, 0], [20.0, 30.0, 1.0])
+
+
+CONV_PINS = [
+    pin_conv_impulse_response,
+    pin_conv_matches_numpy_convolve,
+    pin_conv_state_carry,
+    pin_conv_causal,
+    pin_conv_constant_and_silu,
+    pin_conv_short_sequence_state,
+]

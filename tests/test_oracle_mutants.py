@@ -60,6 +60,44 @@ PRE_MUTANTS = [
 ]
 
 
+# Mistakes in the short convolution, caught by the convolution pins.
+CONV_MUTANTS = [
+    ("taps_reversed", "z += (double)w[(int64_t)c * K + j] * win[t + j];",
+     "z += (double)w[(int64_t)c * K + (K - 1 - j)] * win[t + j];"),
+    ("window_off_by_one", "z += (double)w[(int64_t)c * K + j] * win[t + j];",
+     "z += (double)w[(int64_t)c * K + j] * win[t + j + 1];"),
+    ("bias_dropped", "double z = bias ? (double)bias[c] : 0.0;", "double z = 0.0;"),
+    ("silu_as_sigmoid", "y[(tb + t) * C + c] = silu ? z / (1.0 + exp(-z)) : z;",
+     "y[(tb + t) * C + c] = silu ? 1.0 / (1.0 + exp(-z)) : z;"),
+    ("state_newest_first", "win[m] = state ? state[((int64_t)n * C + c) * M + m] : 0.0;",
+     "win[m] = state ? state[((int64_t)n * C + c) * M + (M - 1 - m)] : 0.0;"),
+    ("state_ignored", "win[m] = state ? state[((int64_t)n * C + c) * M + m] : 0.0;", "win[m] = 0.0;"),
+    ("state_out_first_inputs", "state_out[((int64_t)n * C + c) * M + m] = win[len + m];",
+     "state_out[((int64_t)n * C + c) * M + m] = win[m];"),
+    ("channel_stride", "win[M + t] = oracle_load(x, (tb + t) * C + c, io_dtype);",
+     "win[M + t] = oracle_load(x, (tb + t) * C + (c + 1) % C, io_dtype);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", CONV_MUTANTS, ids=[m[0] for m in CONV_MUTANTS])
+def test_conv_pins_catch_mutant(tmp_path, name, old, new):
+    with open(oracle_mod.SOURCE) as f:
+        src = f.read()
+    assert old in src, "mutation site for %s not found in the oracle source" % name
+    mpath = tmp_path / ("conv_mutant_%s.c" % name)
+    mpath.write_text(src.replace(old, new))
+    lib = str(tmp_path / ("libconv_mutant_%s.so" % name))
+    oracle.build(str(mpath), lib)
+    conv = functools.partial(oracle_mod.short_conv, library=lib)
+    caught = []
+    for pin in oracle_pins.CONV_PINS:
+        try:
+            pin(conv)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, "convolution mutant %s passed every pin" % name
+
+
 @pytest.mark.parametrize("name,old,new", PRE_MUTANTS, ids=[m[0] for m in PRE_MUTANTS])
 def test_preprocessing_pins_catch_mutant(tmp_path, name, old, new):
     with open(oracle_mod.SOURCE) as f:
@@ -119,3 +157,6 @@ def test_unmutated_copy_passes(tmp_path):
     pre = functools.partial(oracle_mod.preprocess, library=lib)
     for pin in oracle_pins.PRE_PINS:
         pin(pre, fwd)
+    conv = functools.partial(oracle_mod.short_conv, library=lib)
+    for pin in oracle_pins.CONV_PINS:
+        pin(conv)
