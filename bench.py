@@ -18,7 +18,8 @@ Also reported on the same line:
                 as 8 chunks of 8,192 carried in place through the state), on
                 the 64-sequence mixed batch, through the state pool with
                 snapshots, and with fused preprocessing, against the same fp32
-                roofline;
+                roofline; the short convolution on the batch's q|k|v channels
+                against the HBM roofline;
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample;
   parity        the timed outputs re-checked against the oracle (sampled heads).
 
@@ -300,6 +301,39 @@ def main():
             "tokens": T, "n_seqs": w.n_seqs, "ms_median": msf, "tokens_per_s": T / (msf / 1e3),
             "roofline_frac": flops / (msf / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
         del rd, outr, hTr
+
+        # The short convolution on the q|k|v channels of the benchmark batch (HBM-bound:
+        # x read once, y written once) and as one decode step at B = 256.
+        C, K = 2 * 16 * 128 + 32 * 128, 4
+        gen = torch.Generator().manual_seed(1005)
+        xc = torch.randn((T, C), generator=gen).to(torch.bfloat16).to(dev)
+        wc = (0.5 * torch.randn((C, K), generator=gen)).to(dev)
+        bc = (0.1 * torch.randn((C,), generator=gen)).to(dev)
+        pool_c = torch.zeros((w.n_seqs, C, K - 1), dtype=torch.bfloat16, device=dev)
+        yc = torch.empty_like(xc)
+
+        def conv(_i):
+            gdn.gdn_short_conv(xc, wc, d["cu"], pool_c, bias=bc, y=yc, stream=stream)
+
+        per_c, _ = time_launches(conv, args.steps, 5, stream)
+        msc = float(np.median(per_c))
+        cbytes = 2.0 * T * C * 2 + 2.0 * w.n_seqs * C * (K - 1) * 2
+        Bd = 256
+        xd = xc[:Bd].contiguous()
+        cud = torch.arange(Bd + 1, dtype=torch.int32, device=dev)
+        pool_d = torch.zeros((Bd, C, K - 1), dtype=torch.bfloat16, device=dev)
+        yd = torch.empty_like(xd)
+
+        def conv_dec(_i):
+            gdn.gdn_short_conv(xd, wc, cud, pool_d, bias=bc, y=yd, stream=stream)
+
+        per_cd, _ = time_launches(conv_dec, args.steps, 5, stream)
+        workloads["short_conv_varlen"] = {
+            "tokens": T, "channels": C, "taps": K, "ms_median": msc, "tokens_per_s": T / (msc / 1e3),
+            "roofline": {"bound": "hbm", "achieved": cbytes / (msc / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": cbytes / (msc / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": cbytes}}
+        workloads["short_conv_decode_B256"] = {"latency_us_median": float(np.median(per_cd)) * 1e3}
+        del xc, yc, pool_c, xd, yd, pool_d
 
         lc = synth.long_context(1003)
         prefill_line("long_context_65536", lc)

@@ -218,13 +218,62 @@ gdn_status gdn_decode_step(const gdn_dims *dims,
  */
 gdn_status gdn_query_plan(const gdn_dims *dims, int32_t decode, int32_t *shape);
 
+/*
+ * Short causal convolution with a carried state (the step that feeds the
+ * recurrence its q, k and v).  For every sequence n, channel c and token t of the
+ * sequence, with K taps:
+ *
+ *     z = bias[c] + sum_{j=0}^{K-1} w[c][j] * x(t - (K-1) + j, c)      (fp32, j ascending, fma)
+ *     y[t][c] = z * sigmoid(z)   (GDN_CONV_SILU; else y = z), rounded to the io dtype
+ *
+ * where x(s, c) for s before the sequence's first token is read from the
+ * sequence's state: state[slot][c][m] is the input m - (K-1) tokens before the
+ * first token (oldest first).  Afterwards the state slot holds the sequence's
+ * last K-1 inputs (reaching back into the old state for sequences shorter than
+ * K-1).  Every output depends only on its own sequence's inputs, so the bitwise
+ * contract holds: a decode step is a call whose sequences have one token each,
+ * and cutting a sequence into calls that carry the state gives the same bits.
+ * The page "Defending Against the Training-Inference Numeric Mismatch in RL
+ * (Especially Linear Attention)" (section 3.2, "Solution") keeps this conv state
+ * in the serving stack's cache beside the recurrent state.
+ *
+ *   x, y        : [T][C] io dtype (y is written for every token)
+ *   w           : [C][K] fp32;  bias: [C] fp32 or NULL
+ *   cu_seqlens  : [N+1] device int32, as for gdn_fwd_varlen
+ *   state_pool  : [P][C][K-1] io dtype, read and written in place
+ *   src_idx / dst_idx : [N] device int32 or NULL (slot n, then P >= N).  An entry
+ *                 outside [0, P) means the zero state / no write.  The same slot
+ *                 may be read and written by one sequence (in place); a slot
+ *                 written for one sequence must not be read or written for
+ *                 another in the same call.
+ * Errors: NULL, SHAPE (K outside 2..8, C <= 0 or not a multiple of 16 bytes of
+ * elements (8 bf16, 4 fp32), P <= 0, P < N without index arrays, T inconsistent),
+ * DTYPE, ALIGN (x, y, state 16 bytes; w, bias, indices 4 bytes),
+ * ALIAS (y or the pool overlapping another argument).
+ */
+enum { GDN_CONV_SILU = 1 };
+
+typedef struct gdn_conv_dims {
+    int32_t n_seqs;        /* N; 0 is a no-op */
+    int32_t channels;      /* C */
+    int32_t taps;          /* K, 2 .. 8 */
+    int32_t io_dtype;      /* gdn_dtype of x, y and the state pool */
+    int64_t total_tokens;  /* T */
+    int32_t pool_size;     /* P */
+    int32_t flags;         /* GDN_CONV_* bits */
+} gdn_conv_dims;
+
+gdn_status gdn_short_conv(const gdn_conv_dims *dims, const void *x, const float *w, const float *bias,
+                          const int32_t *cu_seqlens, void *state_pool, const int32_t *src_idx,
+                          const int32_t *dst_idx, void *y, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *gdn_status_string(gdn_status status);
 
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 200
+#define GDN_ABI_VERSION 201
 
 #ifdef __cplusplus
 }

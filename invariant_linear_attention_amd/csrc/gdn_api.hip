@@ -341,6 +341,45 @@ gdn_status gdn_query_plan(const gdn_dims *dims, int32_t decode, int32_t *shape) 
     return GDN_OK;
 }
 
+gdn_status gdn_short_conv(const gdn_conv_dims *dims, const void *x, const float *w, const float *bias,
+                          const int32_t *cu_seqlens, void *state_pool, const int32_t *src_idx,
+                          const int32_t *dst_idx, void *y, void *stream) {
+    using namespace gdn;
+    if (!dims) return GDN_ERR_NULL;
+    const gdn_conv_dims &d = *dims;
+    const int64_t T = d.total_tokens, N = d.n_seqs, C = d.channels, K = d.taps;
+    if (N < 0 || T < 0 || C <= 0 || K < 2 || K > 8 || d.pool_size <= 0 || N > 65535) return GDN_ERR_SHAPE;
+    if (d.flags & ~GDN_CONV_SILU) return GDN_ERR_UNSUPPORTED;
+    if (d.io_dtype != GDN_F32 && d.io_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (N == 0) return T == 0 ? GDN_OK : GDN_ERR_SHAPE;
+    if (!cu_seqlens || !w || !state_pool) return GDN_ERR_NULL;
+    if (T > 0 && (!x || !y)) return GDN_ERR_NULL;
+    if ((!src_idx || !dst_idx) && d.pool_size < N) return GDN_ERR_SHAPE;
+    if ((T + 15) / 16 * ((C + 255) / 256) > 0xFFFFFFFFll) return GDN_ERR_SHAPE;  // 1-D grid
+
+    const uintptr_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
+    if (C % (16 / esz) != 0) return GDN_ERR_SHAPE;  // whole 16-byte channel vectors
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(state_pool, 16) || !aligned(w, 4) || !aligned(bias, 4) ||
+        !aligned(cu_seqlens, 4) || !aligned(src_idx, 4) || !aligned(dst_idx, 4))
+        return GDN_ERR_ALIGN;
+    const Range rx = range_of(x, (uint64_t)T * C * esz), ry = range_of(y, (uint64_t)T * C * esz);
+    const Range rw = range_of(w, (uint64_t)C * K * 4), rb = range_of(bias, bias ? (uint64_t)C * 4 : 0);
+    const Range rp = range_of(state_pool, (uint64_t)d.pool_size * C * (K - 1) * esz);
+    const Range rc = range_of(cu_seqlens, (uint64_t)(N + 1) * 4);
+    const Range rs = range_of(src_idx, src_idx ? (uint64_t)N * 4 : 0), rd = range_of(dst_idx, dst_idx ? (uint64_t)N * 4 : 0);
+    for (Range in : {rx, rw, rb, rp, rc, rs, rd})
+        if (overlap(ry, in)) return GDN_ERR_ALIAS;
+    for (Range in : {rx, rw, rb, rc, rs, rd})
+        if (overlap(rp, in)) return GDN_ERR_ALIAS;
+
+    ConvParams p{};
+    p.x = x; p.w = w; p.bias = bias; p.cu_seqlens = cu_seqlens; p.src_idx = src_idx; p.dst_idx = dst_idx;
+    p.state = state_pool; p.y = y; p.total_tokens = T; p.n_seqs = (int32_t)N; p.channels = (int32_t)C;
+    p.taps = (int32_t)K; p.pool_size = d.pool_size; p.silu = (d.flags & GDN_CONV_SILU) ? 1 : 0;
+    const hipError_t e = launch_short_conv(p, d.io_dtype, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 const char *gdn_status_string(gdn_status status) {
     switch (status) {
         case GDN_OK: return "GDN_OK";

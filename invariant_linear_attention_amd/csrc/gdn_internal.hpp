@@ -58,6 +58,18 @@ struct DecodeParams {
     int32_t pre_flags;
 };
 
+// Kernel arguments of the short convolution (gdn_short_conv).
+struct ConvParams {
+    const void *x;
+    const float *w, *bias;
+    const int32_t *cu_seqlens, *src_idx, *dst_idx;
+    void *state;
+    void *y;
+    int64_t total_tokens;
+    int32_t n_seqs, channels, taps, pool_size, silu;
+};
+hipError_t launch_short_conv(const ConvParams &p, int io_dtype, hipStream_t s);
+
 // A launch shape: `lanes` lanes hold one state row, each lane holds `rows` rows,
 // and a workgroup has `waves` waves; it owns waves * (64 / lanes) * rows
 // consecutive rows of one value head.

@@ -245,6 +245,15 @@ struct IoBf16 {
     __device__ static void store1(void *base, size_t idx, float f) {
         static_cast<uint16_t *>(base)[idx] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
     }
+    // VEC consecutive elements from idx (16-byte aligned), rounded as store1 does.
+    __device__ static void store_vec(void *base, size_t idx, const float (&f)[VEC]) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(f[2 * i])) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(f[2 * i + 1])) << 16);
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + idx) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
 };
 
 struct IoF32 {
@@ -261,6 +270,9 @@ struct IoF32 {
     }
     __device__ static float load1(const void *base, size_t idx) { return static_cast<const float *>(base)[idx]; }
     __device__ static void store1(void *base, size_t idx, float f) { static_cast<float *>(base)[idx] = f; }
+    __device__ static void store_vec(void *base, size_t idx, const float (&f)[VEC]) {
+        *reinterpret_cast<float4 *>(static_cast<float *>(base) + idx) = make_float4(f[0], f[1], f[2], f[3]);
+    }
 };
 
 // ------------------------------------------------------------- prefill kernel

@@ -19,8 +19,8 @@ STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
     5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_HIP",
 }
-EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_query_plan", "gdn_status_string",
-           "gdn_abi_version")
+EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv", "gdn_query_plan",
+           "gdn_status_string", "gdn_abi_version")
 
 
 GDN_PRE_QK_L2NORM, GDN_PRE_GATE_LOGITS = 1, 2
@@ -40,6 +40,18 @@ class GdnDims(ctypes.Structure):
         ("total_tokens", ctypes.c_int64), ("pool_size", ctypes.c_int32),
         ("plan_lanes", ctypes.c_int32), ("plan_rows", ctypes.c_int32), ("plan_waves", ctypes.c_int32),
         ("reserved", ctypes.c_int32), ("pre", ctypes.POINTER(GdnPreproc)),
+    ]
+
+
+GDN_CONV_SILU = 1
+
+
+class GdnConvDims(ctypes.Structure):
+    """Mirror of ``gdn_conv_dims``."""
+    _fields_ = [
+        ("n_seqs", ctypes.c_int32), ("channels", ctypes.c_int32), ("taps", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32), ("total_tokens", ctypes.c_int64), ("pool_size", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -70,6 +82,8 @@ def load_library(path: str = LIBRARY):
                                             ctypes.c_int32, ctypes.c_int32, vp, vp]
         lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdn_short_conv.restype = ctypes.c_int
+        lib.gdn_short_conv.argtypes = [ctypes.POINTER(GdnConvDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdn_query_plan.restype = ctypes.c_int
         lib.gdn_query_plan.argtypes = [ctypes.POINTER(GdnDims), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
         lib.gdn_status_string.restype = ctypes.c_char_p
@@ -241,3 +255,28 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, state_idx=None, out=None, stre
     _check(lib.gdn_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(state_pool), _ptr(state_idx), _ptr(out), _stream_handle(stream)))
     return out
+
+
+def gdn_short_conv(x, w, cu_seqlens, state_pool, bias=None, src_idx=None, dst_idx=None, silu: bool = True,
+                   y=None, stream=None):
+    """Short causal convolution with a carried state (see include/gdn.h).  x [T, C]
+    (bf16 or fp32, on the GPU); w [C, K] fp32; state_pool [P, C, K-1] in x's dtype,
+    updated in place; src_idx / dst_idx [N] int32 or None.  Returns y [T, C]."""
+    import torch
+    lib = load_library()
+    _need(x, "x")
+    _need(w, "w", torch.float32)
+    _need(bias, "bias", torch.float32)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    _need(state_pool, "state_pool", x.dtype)
+    _need(src_idx, "src_idx", torch.int32)
+    _need(dst_idx, "dst_idx", torch.int32)
+    T, C = int(x.shape[0]), int(x.shape[1])
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype)
+    dims = GdnConvDims(n_seqs=int(cu_seqlens.numel()) - 1, channels=C, taps=int(w.shape[1]), io_dtype=_io_code(x),
+                       total_tokens=T, pool_size=int(state_pool.shape[0]), flags=GDN_CONV_SILU if silu else 0)
+    _check(lib.gdn_short_conv(ctypes.byref(dims), _ptr(x), _ptr(w), _ptr(bias), _ptr(cu_seqlens), _ptr(state_pool),
+                              _ptr(src_idx), _ptr(dst_idx), _ptr(y), _stream_handle(stream)))
+    return y

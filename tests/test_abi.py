@@ -27,8 +27,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_query_plan",
-                          "gdn_status_string", "gdn_abi_version"}
+    assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
+                          "gdn_query_plan", "gdn_status_string", "gdn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -320,3 +320,59 @@ def test_preproc_pool_and_decode_alias(lib):
     assert call_pool(lib, _pre_dims(pool_size=4), pool=BASE + 41 * MB) == 5
     assert call_dec(lib, _pre_dims(total_tokens=2, pool_size=4), out=BASE + 41 * MB) == 5
     assert call_dec(lib, _pre_dims(total_tokens=2, pool_size=4), pool=BASE + 40 * MB) == 5
+
+
+
+# ------------------------------------------------------------- short conv
+
+def test_conv_dims_layout_matches_c(tmp_path):
+    from invariant_linear_attention_amd.gdn import GdnConvDims
+    src = tmp_path / "conv.c"
+    fields = [f[0] for f in GdnConvDims._fields_]
+    body = "".join('printf("%s %%zu\\n", offsetof(gdn_conv_dims, %s));' % (f, f) for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "gdn.h"\n'
+                   'int main(void){printf("size %%zu\\n", sizeof(gdn_conv_dims));%s return 0;}\n' % body)
+    exe = tmp_path / "conv"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.check_output([str(exe)]).decode().splitlines())
+    assert int(out["size"]) == ctypes.sizeof(GdnConvDims)
+    for f in fields:
+        assert int(out[f]) == getattr(GdnConvDims, f).offset, f
+
+
+def _cdims(**kw):
+    from invariant_linear_attention_amd.gdn import GdnConvDims
+    d = dict(n_seqs=2, channels=64, taps=4, io_dtype=1, total_tokens=10, pool_size=4, flags=1)
+    d.update(kw)
+    return GdnConvDims(**d)
+
+
+CP = {name: BASE + (20 + i) * MB for i, name in enumerate(["x", "w", "b", "cu", "pool", "src", "dst", "y"])}
+
+
+def call_conv(lib, dims, **over):
+    a = dict(CP)
+    a.update(over)
+    return lib.gdn_short_conv(ctypes.byref(dims) if dims is not None else None, a["x"], a["w"], a["b"], a["cu"],
+                              a["pool"], a["src"], a["dst"], a["y"], None)
+
+
+@pytest.mark.parametrize("case,over,code", [
+    (dict(taps=1), {}, 2), (dict(taps=9), {}, 2), (dict(channels=0), {}, 2), (dict(pool_size=0), {}, 2),
+    (dict(n_seqs=-1), {}, 2), (dict(total_tokens=-1), {}, 2), (dict(flags=2), {}, 6), (dict(io_dtype=5), {}, 3),
+    (dict(n_seqs=0, total_tokens=4), {}, 2),
+    ({}, dict(cu=None), 1), ({}, dict(w=None), 1), ({}, dict(pool=None), 1), ({}, dict(x=None), 1),
+    ({}, dict(y=None), 1),
+    (dict(pool_size=1), dict(src=None), 2),
+    ({}, dict(x=CP["x"] + 2), 4), ({}, dict(w=CP["w"] + 2), 4), ({}, dict(pool=CP["pool"] + 8), 4),
+    (dict(io_dtype=0), dict(y=CP["y"] + 8), 4), (dict(channels=60), {}, 2), (dict(io_dtype=0, channels=62), {}, 2),
+    ({}, dict(y=CP["x"]), 5), ({}, dict(y=CP["pool"]), 5), ({}, dict(pool=CP["w"]), 5),
+    ({}, dict(pool=CP["x"] + 16), 5),
+])
+def test_conv_rejects(lib, case, over, code):
+    assert call_conv(lib, _cdims(**case), **over) == code
+
+
+def test_conv_null_dims_and_noop(lib):
+    assert call_conv(lib, None) == 1
+    assert call_conv(lib, _cdims(n_seqs=0, total_tokens=0)) == 0
