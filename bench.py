@@ -99,6 +99,19 @@ def rel(x, r):
     return float(np.linalg.norm(x - r) / max(np.linalg.norm(r), 1e-300))
 
 
+def head_parity(synth, oracle, wl, out, hT, kh, fused=None):
+    """Normwise errors of key head kh's value heads against the fp64 oracle."""
+    s = synth.head_slice(wl, kh)
+    G = out.shape[1] // wl.q.shape[1]
+    vs = slice(G * kh, G * kh + G)
+    if fused is None:
+        ro, rh = oracle.gdn_forward(s.q, s.k, s.v, s.g, s.beta, s.cu_seqlens, s.h0)
+    else:
+        ro, rh = oracle.gdn_forward_fused(s.q, s.k, s.v, s.g, s.beta, s.cu_seqlens, s.h0,
+                                          A_log=fused[0][vs], dt_bias=fused[1][vs])
+    return {"out": rel(out[:, vs].float().cpu().numpy(), ro), "state": rel(hT[:, vs].cpu().numpy(), rh)}
+
+
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 
@@ -147,6 +160,7 @@ def main():
     import torch
 
     from invariant_linear_attention_amd import gdn, synth
+    from oracle import oracle
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -181,7 +195,6 @@ def main():
                 "launch_ms_mean": ms, "launch_ms_median": ms_med}
 
     # parity of the timed outputs (sampled key heads; the oracle is test infrastructure)
-    from oracle import oracle
     parity = {}
     torch.cuda.synchronize()
     for kh in (0, 15):
@@ -211,7 +224,16 @@ def main():
             per_d, _ = time_launches(dec, steps, max(args.warmup, n_pools), stream)
             ms_d = float(np.mean(per_d))
             alg_bytes = B * (2 * 32 * 128 * 128 * 4 + 24832)
-            decode["B%d" % B] = {"tokens_per_s": B / (ms_d / 1e3), "launch_ms_mean": ms_d,
+            # one checked step: rows 0..3 against the oracle from the same states
+            nb = min(4, B)
+            pchk = pools[0].clone()
+            h0c = pchk[:nb].cpu()
+            ochk = gdn.gdn_decode_step(dq, dk_, dv_, dg, db, pchk, stream=stream)
+            torch.cuda.synchronize()
+            ro_d, rh_d = oracle.gdn_forward(dw.q[:nb], dw.k[:nb], dw.v[:nb], dw.g[:nb], dw.beta[:nb],
+                                            synth.cu_from_lengths([1] * nb), h0c)
+            dpar = {"out": rel(ochk[:nb].float().cpu().numpy(), ro_d), "state": rel(pchk[:nb].cpu().numpy(), rh_d)}
+            decode["B%d" % B] = {"tokens_per_s": B / (ms_d / 1e3), "launch_ms_mean": ms_d, "parity": dpar,
                                  "latency_us_median": float(np.median(per_d)) * 1e3,
                                  "launch_ms_median": float(np.median(per_d)),
                                  "roofline": {"bound": "hbm", "achieved": alg_bytes / (ms_d / 1e3) / 1e9,
@@ -227,7 +249,7 @@ def main():
     if not args.no_workloads:
         workloads = {}
 
-        def prefill_line(name, wl, chunks=1):
+        def prefill_line(name, wl, chunks=1, parity_heads=(0,)):
             Tw = wl.total_tokens
             dd = [t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta)]
             cu = wl.cu_seqlens.to(dev)
@@ -251,12 +273,18 @@ def main():
             reps = max(3, min(args.steps, int(200.0 / max(Tw / 2000.0, 1.0))))
             per_w, _ = time_launches(run, reps, 3, stream)
             msw = float(np.median(per_w))
+            # one checked run from the original initial states (the timed runs carried them on)
+            state.copy_(wl.h0.to(dev) if wl.h0 is not None else torch.zeros_like(state))
+            run(0)
+            torch.cuda.synchronize()
+            par = {"kh%d" % kh: head_parity(synth, oracle, wl, outw, state, kh) for kh in parity_heads}
             fl = 7.0 * 128 * 128 * 32 * Tw
             workloads[name] = {"tokens": Tw, "n_seqs": wl.n_seqs, "chunks": chunks, "ms_median": msw,
                                "tokens_per_s": Tw / (msw / 1e3),
                                "roofline_frac": fl / (msw / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
                                "plan": list(gdn.gdn_query_plan(gdn.make_dims(dd[0], dd[2], wl.n_seqs if chunks == 1 else 1,
-                                                                             Tw // chunks)))}
+                                                                             Tw // chunks))),
+                               "parity": par}
             del dd, outw, state
 
         # The benchmark batch through the state pool with a snapshot every 256 tokens
@@ -299,7 +327,9 @@ def main():
         msf = float(np.median(per_f))
         workloads["varlen_prefill_fused_preprocessing"] = {
             "tokens": T, "n_seqs": w.n_seqs, "ms_median": msf, "tokens_per_s": T / (msf / 1e3),
-            "roofline_frac": flops / (msf / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+            "roofline_frac": flops / (msf / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+            "parity": {"kh0": head_parity(synth, oracle, rw, outr, hTr, 0,
+                                          fused=(rw.meta["A_log"], rw.meta["dt_bias"]))}}
         del rd, outr, hTr
 
         # The short convolution on the q|k|v channels of the benchmark batch (HBM-bound:
@@ -332,6 +362,13 @@ def main():
             "tokens": T, "channels": C, "taps": K, "ms_median": msc, "tokens_per_s": T / (msc / 1e3),
             "roofline": {"bound": "hbm", "achieved": cbytes / (msc / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": cbytes / (msc / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": cbytes}}
+        # one checked run from the zero state, on the first 256 channels
+        pool_c.zero_()
+        conv(0)
+        torch.cuda.synchronize()
+        ry, _ = oracle.short_conv(xc[:, :256].cpu(), wc[:256].cpu(), w.cu_seqlens, bias=bc[:256].cpu(),
+                                  state=torch.zeros((w.n_seqs, 256, K - 1)))
+        workloads["short_conv_varlen"]["parity"] = {"y_first256": rel(yc[:, :256].float().cpu().numpy(), ry)}
         workloads["short_conv_decode_B256"] = {"latency_us_median": float(np.median(per_cd)) * 1e3}
         del xc, yc, pool_c, xd, yd, pool_d
 
@@ -339,7 +376,7 @@ def main():
         prefill_line("long_context_65536", lc)
         prefill_line("long_context_65536_as_8x8192", lc, chunks=8)
         del lc
-        prefill_line("mixed_batch_64", synth.mixed_batch(1004))
+        prefill_line("mixed_batch_64", synth.mixed_batch(1004), parity_heads=(0, 15))
 
     # ------------------------------------------------------- CPU baseline
     cpu = None
@@ -359,6 +396,16 @@ def main():
                "sample": "fp64 oracle, all 32 value heads of the same 8-sequence batch (%d tokens), %d pass(es) "
                          "in %.1f s" % (T, passes, dt),
                "seconds": dt}
+
+    # every line's parity re-check must pass as well
+    def line_ok(par):
+        return all((v.get("out", 0.0) <= 2e-3 and v.get("state", 0.0) <= 1e-4 and v.get("y_first256", 0.0) <= 2e-3)
+                   if isinstance(v, dict) else True for v in par.values())
+    for rec in list((decode or {}).values()) + list((workloads or {}).values()):
+        if "parity" in rec:
+            par = rec["parity"]
+            ok = line_ok(par) if any(isinstance(v, dict) for v in par.values()) else line_ok({"x": par})
+            parity_ok = parity_ok and ok
 
     line = {
         "metric": METRIC,
