@@ -116,7 +116,8 @@ COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 
 def pmc_pass(dev, stream):
-    """One launch of each kernel, preceded by a plain device copy of COPY_BYTES whose
+    """One launch of each kernel (prefill, decode at B = 256, the short convolution
+    and its state update), preceded by a plain device copy of COPY_BYTES whose
     FETCH_SIZE / WRITE_SIZE readings calibrate the counters' units."""
     import torch
 
@@ -135,7 +136,16 @@ def pmc_pass(dev, stream):
     pool = torch.randn((B, 32, 128, 128), device=dev) * 0.1
     gdn.gdn_decode_step(*(t.to(dev) for t in (dw.q, dw.k, dw.v, dw.g, dw.beta)), pool, stream=stream)
     torch.cuda.synchronize()
-    print("pmc pass: copy %d bytes, prefill %d tokens, decode B=%d" % (COPY_BYTES, w.total_tokens, B), flush=True)
+    del pool
+    C, K = 2 * 16 * 128 + 32 * 128, 4   # the short convolution on the batch's q|k|v channels
+    gen = torch.Generator().manual_seed(1005)
+    xc = torch.randn((w.total_tokens, C), generator=gen).to(torch.bfloat16).to(dev)
+    wc = (0.5 * torch.randn((C, K), generator=gen)).to(dev)
+    pool_c = torch.zeros((w.n_seqs, C, K - 1), dtype=torch.bfloat16, device=dev)
+    gdn.gdn_short_conv(xc, wc, d[6], pool_c, stream=stream)
+    torch.cuda.synchronize()
+    print("pmc pass: copy %d bytes, prefill %d tokens, decode B=%d, conv %d channels" % (
+        COPY_BYTES, w.total_tokens, B, C), flush=True)
 
 
 def main():
@@ -361,7 +371,8 @@ def main():
         workloads["short_conv_varlen"] = {
             "tokens": T, "channels": C, "taps": K, "ms_median": msc, "tokens_per_s": T / (msc / 1e3),
             "roofline": {"bound": "hbm", "achieved": cbytes / (msc / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": cbytes / (msc / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": cbytes}}
+                         "frac": cbytes / (msc / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": cbytes,
+                         "traffic": traffic_from_profile("short_conv", src_hash)}}
         # one checked run from the zero state, on the first 256 channels
         pool_c.zero_()
         conv(0)
