@@ -267,6 +267,218 @@ int gdn_oracle_short_conv(int32_t n_seqs, const int32_t *cu_seqlens, int32_t C, 
     return 0;
 }
 
+/*
+ * Gradients of the recurrent forward (reverse-mode differentiation of the loop of
+ * gdn_oracle_forward), in fp64.
+ *
+ * The page "Defending Against the Training-Inference Numeric Mismatch in RL
+ * (Especially Linear Attention)" (section 3.2) keeps the training backward on the
+ * chunked kernel while every forward runs the recurrence; forward parity says
+ * nothing about gradients, so this function gives them from the definition.
+ * Token t's forward step, exactly as gdn_oracle_forward takes it, is
+ *
+ *   Sd  = a S_{t-1}             (a = exp(g_t), b = beta_t)
+ *   p   = Sd k                  (a dv-vector)
+ *   u   = b (v - p)
+ *   S_t = Sd + u k^T
+ *   o   = S_t q
+ *
+ * and its adjoint, walked from the last token of a sequence to the first with
+ * D = dL/dS_t (D = dhT, or 0, before the last token), is, line by line:
+ *
+ *   D  += dO q^T                 dq += S_t^T dO
+ *   du  = D k                    dk += D^T u
+ *   dv  = b du                   dbeta = du . (v - p)
+ *   dp  = -b du
+ *   Dd  = D + dp k^T             dk += Sd^T dp
+ *   dg  = a <Dd, S_{t-1}>        (dL/da = <Dd, S_{t-1}>, da/dg = a)
+ *   D   = a Dd                   (= dL/dS_{t-1})
+ *
+ * and dh0 = D after the first token.  dq and dk of key head kh add up over the
+ * value heads that read it, in head order.
+ *
+ * The states S_{t-1} are not stored for the whole sequence: the forward pass keeps
+ * one every ORACLE_CKPT tokens and the states of a stretch are recomputed from its
+ * checkpoint by the same step, which gives the same values as keeping them all.
+ *
+ * Inputs as gdn_oracle_forward (dtype codes 0 fp32, 1 bf16 bits, 2 fp64), plus
+ * dout [T][hv][dv] in dout_dtype and dhT [N][hv][dv][dk] fp64 or NULL (= 0).
+ * Outputs, fp64: dq, dk [T][hk][dk]; dv [T][hv][dv]; dg, dbeta [T][hv];
+ * dh0 [N][hv][dv][dk].
+ */
+#define ORACLE_CKPT 32
+
+/* One forward step on S (dv x dk, in place); p_out (dv) receives p = Sd k. */
+static void oracle_step(double *S, int32_t dv, int32_t dk, double a, double b,
+                        const double *kv, const double *vv, double *p_out)
+{
+    for (int64_t e = 0; e < (int64_t)dv * dk; ++e)
+        S[e] = a * S[e];
+    for (int32_t j = 0; j < dv; ++j) {
+        double *row = S + (size_t)j * dk;
+        double p = 0.0;
+        for (int32_t i = 0; i < dk; ++i)
+            p += row[i] * kv[i];
+        const double u = b * (vv[j] - p);
+        for (int32_t i = 0; i < dk; ++i)
+            row[i] += u * kv[i];
+        if (p_out)
+            p_out[j] = p;
+    }
+}
+
+int gdn_oracle_backward(int32_t n_seqs, const int32_t *cu_seqlens,
+                        int32_t hk, int32_t hv, int32_t dk, int32_t dv,
+                        int32_t qk_dtype, int32_t v_dtype, int32_t gate_dtype, int32_t dout_dtype,
+                        const void *q, const void *k, const void *v,
+                        const void *g, const void *beta, const double *h0,
+                        const void *dout, const double *dhT,
+                        double *dq, double *dk_out, double *dv_out, double *dg, double *dbeta, double *dh0,
+                        int32_t n_threads)
+{
+    if (n_seqs < 0 || hk <= 0 || hv <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    if (hv % hk != 0)
+        return -2;
+    if (qk_dtype < 0 || qk_dtype > 2 || v_dtype < 0 || v_dtype > 2 || dout_dtype < 0 || dout_dtype > 2 ||
+        (gate_dtype != 0 && gate_dtype != 2))
+        return -3;
+    if (n_seqs == 0)
+        return 0;
+    if (!cu_seqlens || !dh0)
+        return -4;
+    if (cu_seqlens[0] != 0)
+        return -5;
+    for (int32_t n = 0; n < n_seqs; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n])
+            return -5;
+    const int64_t total = cu_seqlens[n_seqs];
+    if (total > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk_out || !dv_out || !dg || !dbeta))
+        return -4;
+
+    const int32_t group = hv / hk;
+    const int64_t SZ = (int64_t)dv * dk;
+    int status = 0;
+    if (n_threads <= 0)
+        n_threads = 1;
+    if (total > 0) {
+        memset(dq, 0, sizeof(double) * (size_t)total * hk * dk);
+        memset(dk_out, 0, sizeof(double) * (size_t)total * hk * dk);
+    }
+
+    /* One unit = (sequence, key head): its value heads run in order, so the sums
+       into dq and dk of that key head have a fixed order. */
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
+    for (int64_t unit = 0; unit < (int64_t)n_seqs * hk; ++unit) {
+        const int32_t n = (int32_t)(unit / hk);
+        const int32_t kh = (int32_t)(unit % hk);
+        const int64_t tb = cu_seqlens[n], len = cu_seqlens[n + 1] - tb;
+        const int64_t n_ck = len / ORACLE_CKPT + 1;
+        double *ck = (double *)malloc(sizeof(double) * (size_t)(n_ck * SZ));
+        double *st = (double *)malloc(sizeof(double) * (size_t)((ORACLE_CKPT + 1) * SZ));
+        double *pv = (double *)malloc(sizeof(double) * (size_t)(ORACLE_CKPT * dv));
+        double *D = (double *)malloc(sizeof(double) * (size_t)SZ);
+        double *kv = (double *)malloc(sizeof(double) * (size_t)dk);
+        double *qv = (double *)malloc(sizeof(double) * (size_t)dk);
+        double *vv = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *dO = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *du = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!ck || !st || !pv || !D || !kv || !qv || !vv || !dO || !du || !dp) {
+#pragma omp atomic write
+            status = -6;
+        } else {
+            for (int32_t h = kh * group; h < (kh + 1) * group; ++h) {
+                const size_t state_off = ((size_t)n * hv + h) * (size_t)SZ;
+                /* forward pass, keeping the state before every ORACLE_CKPT-th token */
+                double *S = st;
+                for (int64_t e = 0; e < SZ; ++e)
+                    S[e] = h0 ? h0[state_off + e] : 0.0;
+                for (int64_t t = 0; t < len; ++t) {
+                    if (t % ORACLE_CKPT == 0)
+                        memcpy(ck + (t / ORACLE_CKPT) * SZ, S, sizeof(double) * (size_t)SZ);
+                    const int64_t tt = tb + t;
+                    for (int32_t i = 0; i < dk; ++i)
+                        kv[i] = oracle_load(k, (tt * hk + kh) * (int64_t)dk + i, qk_dtype);
+                    for (int32_t j = 0; j < dv; ++j)
+                        vv[j] = oracle_load(v, (tt * hv + h) * (int64_t)dv + j, v_dtype);
+                    oracle_step(S, dv, dk, exp(oracle_load(g, tt * hv + h, gate_dtype)),
+                                oracle_load(beta, tt * hv + h, gate_dtype), kv, vv, NULL);
+                }
+                /* backward pass */
+                for (int64_t e = 0; e < SZ; ++e)
+                    D[e] = dhT ? dhT[state_off + e] : 0.0;
+                for (int64_t c = (len - 1) / ORACLE_CKPT; len > 0 && c >= 0; --c) {
+                    const int64_t c0 = c * ORACLE_CKPT;
+                    const int64_t c1 = (c0 + ORACLE_CKPT < len) ? c0 + ORACLE_CKPT : len;
+                    /* st[m] = state before token c0 + m, for m = 0 .. c1 - c0 */
+                    memcpy(st, ck + c * SZ, sizeof(double) * (size_t)SZ);
+                    for (int64_t t = c0; t < c1; ++t) {
+                        const int64_t tt = tb + t, m = t - c0;
+                        memcpy(st + (m + 1) * SZ, st + m * SZ, sizeof(double) * (size_t)SZ);
+                        for (int32_t i = 0; i < dk; ++i)
+                            kv[i] = oracle_load(k, (tt * hk + kh) * (int64_t)dk + i, qk_dtype);
+                        for (int32_t j = 0; j < dv; ++j)
+                            vv[j] = oracle_load(v, (tt * hv + h) * (int64_t)dv + j, v_dtype);
+                        oracle_step(st + (m + 1) * SZ, dv, dk, exp(oracle_load(g, tt * hv + h, gate_dtype)),
+                                    oracle_load(beta, tt * hv + h, gate_dtype), kv, vv, pv + m * dv);
+                    }
+                    for (int64_t t = c1 - 1; t >= c0; --t) {
+                        const int64_t tt = tb + t, m = t - c0;
+                        const double *Sprev = st + m * SZ, *Snew = st + (m + 1) * SZ, *p = pv + m * dv;
+                        const double a = exp(oracle_load(g, tt * hv + h, gate_dtype));
+                        const double b = oracle_load(beta, tt * hv + h, gate_dtype);
+                        const int64_t qk_off = (tt * hk + kh) * (int64_t)dk, v_off = (tt * hv + h) * (int64_t)dv;
+                        for (int32_t i = 0; i < dk; ++i) {
+                            kv[i] = oracle_load(k, qk_off + i, qk_dtype);
+                            qv[i] = oracle_load(q, qk_off + i, qk_dtype);
+                        }
+                        for (int32_t j = 0; j < dv; ++j) {
+                            vv[j] = oracle_load(v, v_off + j, v_dtype);
+                            dO[j] = oracle_load(dout, v_off + j, dout_dtype);
+                        }
+                        /* o = S_t q */
+                        for (int32_t j = 0; j < dv; ++j)
+                            for (int32_t i = 0; i < dk; ++i) {
+                                D[(size_t)j * dk + i] += dO[j] * qv[i];
+                                dq[qk_off + i] += Snew[(size_t)j * dk + i] * dO[j];
+                            }
+                        /* S_t = Sd + u k^T, u = b (v - p) */
+                        double db = 0.0;
+                        for (int32_t j = 0; j < dv; ++j) {
+                            double s = 0.0;
+                            for (int32_t i = 0; i < dk; ++i)
+                                s += D[(size_t)j * dk + i] * kv[i];
+                            du[j] = s;
+                            const double u = b * (vv[j] - p[j]);
+                            for (int32_t i = 0; i < dk; ++i)
+                                dk_out[qk_off + i] += D[(size_t)j * dk + i] * u;
+                            dv_out[v_off + j] = b * du[j];
+                            db += du[j] * (vv[j] - p[j]);
+                            dp[j] = -b * du[j];
+                        }
+                        dbeta[tt * hv + h] = db;
+                        /* p = Sd k, Sd = a S_{t-1} */
+                        double da = 0.0;
+                        for (int32_t j = 0; j < dv; ++j)
+                            for (int32_t i = 0; i < dk; ++i) {
+                                const size_t e = (size_t)j * dk + i;
+                                D[e] += dp[j] * kv[i];
+                                dk_out[qk_off + i] += a * Sprev[e] * dp[j];
+                                da += D[e] * Sprev[e];
+                                D[e] = a * D[e];
+                            }
+                        dg[tt * hv + h] = a * da;
+                    }
+                }
+                memcpy(dh0 + state_off, D, sizeof(double) * (size_t)SZ);
+            }
+        }
+        free(ck); free(st); free(pv); free(D); free(kv); free(qv); free(vv); free(dO); free(du); free(dp);
+    }
+    return status;
+}
+
 int gdn_oracle_max_threads(void)
 {
 #ifdef _OPENMP

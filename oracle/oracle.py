@@ -65,6 +65,18 @@ def load(library: str = LIBRARY):
     c.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                   ctypes.c_void_p, ctypes.c_void_p]
+    b = lib.gdn_oracle_backward
+    b.restype = ctypes.c_int
+    b.argtypes = [
+        ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32,
+    ]
     lib.gdn_oracle_max_threads.restype = ctypes.c_int
     lib.gdn_oracle_max_threads.argtypes = []
     return lib
@@ -267,3 +279,66 @@ def short_conv(x, w, cu_seqlens, bias=None, state=None, silu=True, library=None)
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
     return y, so
+
+
+def gdn_backward(q, k, v, g, beta, cu_seqlens, dout, h0=None, dhT=None, n_threads=None, library=None):
+    """fp64 gradients of gdn_forward (see gdn_oracle_backward).
+
+    Inputs as gdn_forward, plus dout [T, Hv, dv] (fp32, bf16 or fp64) and dhT
+    (optional [N, Hv, dv, dk], fp32 or fp64): the gradient of the loss with respect
+    to the outputs and to the final state.  Returns a dict of float64 arrays:
+    dq, dk [T, Hk, dk]; dv [T, Hv, dv]; dg, dbeta [T, Hv]; dh0 [N, Hv, dv, dk].
+    """
+    qn, qc = _as_numpy(q)
+    kn, kc = _as_numpy(k)
+    vn, vc = _as_numpy(v)
+    if not (qc == kc and qc in (0, 1, 2) and vc in (0, 1, 2)):
+        raise TypeError("q and k must share one dtype; q, k, v must be fp32, bf16 or fp64")
+    gn, gc = _as_numpy(g)
+    bn, bc = _as_numpy(beta)
+    if gc != bc or gc not in (0, 2):
+        raise TypeError("g and beta must both be fp32 or both fp64")
+    dn, dc = _as_numpy(dout)
+    if dc not in (0, 1, 2):
+        raise TypeError("dout must be fp32, bf16 or fp64")
+    cu, cc = _as_numpy(cu_seqlens)
+    if cc != 3:
+        raise TypeError("cu_seqlens must be int32")
+    T, hk, dk = qn.shape
+    hv, dv = vn.shape[1], vn.shape[2]
+    if kn.shape != qn.shape or vn.shape[0] != T or gn.shape != (T, hv) or bn.shape != (T, hv) or \
+            dn.shape != (T, hv, dv):
+        raise ValueError("inconsistent shapes")
+    n = cu.shape[0] - 1
+    if n < 0 or (n > 0 and int(cu[-1]) != T):
+        raise ValueError("cu_seqlens[-1] must equal T")
+
+    def state(x, name):
+        if x is None:
+            return None
+        xn, xc = _as_numpy(x)
+        if xc not in (0, 2):
+            raise TypeError("%s must be fp32 or fp64" % name)
+        xn = np.ascontiguousarray(xn, dtype=np.float64)
+        if xn.shape != (n, hv, dv, dk):
+            raise ValueError("%s must be [N, Hv, dv, dk]" % name)
+        return xn
+
+    h0n, dhn = state(h0, "h0"), state(dhT, "dhT")
+    res = {"dq": np.zeros((T, hk, dk)), "dk": np.zeros((T, hk, dk)), "dv": np.zeros((T, hv, dv)),
+           "dg": np.zeros((T, hv)), "dbeta": np.zeros((T, hv)), "dh0": np.zeros((max(n, 0), hv, dv, dk))}
+    lib = load(library) if library is not None else _get_lib()
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+
+    def ptr(a):
+        return None if a is None or a.size == 0 else a.ctypes.data
+
+    rc = lib.gdn_oracle_backward(
+        n, ptr(cu), hk, hv, dk, dv, qc, vc, gc, dc,
+        ptr(qn), ptr(kn), ptr(vn), ptr(gn), ptr(bn), ptr(h0n), ptr(dn), ptr(dhn),
+        ptr(res["dq"]), ptr(res["dk"]), ptr(res["dv"]), ptr(res["dg"]), ptr(res["dbeta"]), ptr(res["dh0"]),
+        int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (code %d)" % rc)
+    return res

@@ -584,3 +584,155 @@ CONV_PINS = [
     pin_conv_constant_and_silu,
     pin_conv_short_sequence_state,
 ]
+
+
+# ----------------------------------------------------- gradient (backward) pins
+#
+# Each takes ``backward`` (signature of oracle.gdn_backward) and ``forward``
+# (oracle.gdn_forward, itself pinned above).  The loss is
+# L = sum(dout * out) + sum(dhT * hT), so backward(...) must return dL/d(input).
+
+def _grad_case(seed, lengths, hk, hv, dk, dv, with_h0=True, with_dhT=True):
+    c = random_case(seed, lengths, hk, hv, dk, dv, with_h0=with_h0)
+    c = {k: (v.astype(np.float64) if isinstance(v, np.ndarray) and v.dtype == np.float32 else v)
+         for k, v in c.items()}
+    r = _rng(seed + 1)
+    T, N = int(sum(lengths)), len(lengths)
+    c_d = dict(dout=r.standard_normal((T, hv, dv)),
+               dhT=r.standard_normal((N, hv, dv, dk)) if with_dhT else None)
+    return c, c_d
+
+
+def _loss(forward, c, d):
+    out, hT = forward(**c)
+    L = float((out * d["dout"]).sum())
+    if d["dhT"] is not None:
+        L += float((hT * d["dhT"]).sum())
+    return L
+
+
+GRAD_NAMES = {"q": "dq", "k": "dk", "v": "dv", "g": "dg", "beta": "dbeta", "h0": "dh0"}
+
+
+def pin_grad_finite_differences(backward, forward):
+    """Every gradient against central differences of the (pinned) forward, on a
+    grouped varlen case with an empty sequence, h0 and dhT, all in fp64."""
+    c, d = _grad_case(61, [4, 0, 6], hk=1, hv=2, dk=3, dv=2)
+    r = backward(**c, **d)
+    eps = 1e-6
+    for name, gname in GRAD_NAMES.items():
+        x = c[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = _loss(forward, c, d)
+            x[idx] = keep - eps
+            lm = _loss(forward, c, d)
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        _close(r[gname], fd, tol=1e-7, what="d%s vs finite differences" % name)
+
+
+def pin_grad_one_token_closed_form(backward, forward):
+    """One token from a zero state: out = b (k.q) v and hT = b v k^T, so
+    L = b (k.q)(v.dO) + b v^T dhT k and each gradient is a short formula."""
+    c, d = _grad_case(62, [1], hk=1, hv=1, dk=4, dv=3, with_h0=False)
+    r = backward(**c, **d)
+    q, k, v = c["q"][0, 0], c["k"][0, 0], c["v"][0, 0]
+    a, b = math.exp(c["g"][0, 0]), c["beta"][0, 0]
+    dO, W = d["dout"][0, 0], d["dhT"][0, 0]
+    # L = b (k.q)(v.dO) + b v^T W k
+    _close(r["dq"][0, 0], b * (v @ dO) * k, what="one-token dq")
+    _close(r["dk"][0, 0], b * (v @ dO) * q + b * (W.T @ v), what="one-token dk")
+    _close(r["dv"][0, 0], b * (k @ q) * dO + b * (W @ k), what="one-token dv")
+    _close(r["dbeta"][0, 0], (k @ q) * (v @ dO) + v @ W @ k, what="one-token dbeta")
+    assert r["dg"][0, 0] == 0.0, "the gate cannot act on a zero state"
+    # dL/dS0 = a (I - b k k^T)^T-side: D = dO q^T + W, du = D k, dh0 = a (D - b du k^T)
+    D = np.outer(dO, q) + W
+    _close(r["dh0"][0, 0], a * (D - b * np.outer(D @ k, k)), what="one-token dh0")
+
+
+def pin_grad_no_write_closed_form(backward, forward):
+    """beta = 0 (pure decay, o_t = A_t S0 q_t with A_t = exp(g_1 + ... + g_t)):
+    dq_t = A_t S0^T dO_t, dk = dv = 0, dg_t = sum_{s>=t} A_s dO_s.S0 q_s + A_T <dhT, S0>,
+    dh0 = sum_s A_s dO_s q_s^T + A_T dhT, dbeta_t = (D_t k_t).(v_t - A_t S0 k_t)
+    with D_t = sum_{s>=t} (A_s / A_t) dO_s q_s^T + (A_T / A_t) dhT."""
+    c, d = _grad_case(63, [5], hk=1, hv=1, dk=3, dv=4)
+    c["beta"][:] = 0.0
+    r = backward(**c, **d)
+    g = c["g"][:, 0]
+    A = np.exp(np.cumsum(g))
+    S0 = c["h0"][0, 0]
+    q, k, v, dO, W = c["q"][:, 0], c["k"][:, 0], c["v"][:, 0], d["dout"][:, 0], d["dhT"][0, 0]
+    T = 5
+    for t in range(T):
+        _close(r["dq"][t, 0], A[t] * (S0.T @ dO[t]), what="pure decay dq")
+        dg = sum(A[s] * dO[s] @ S0 @ q[s] for s in range(t, T)) + A[-1] * float((W * S0).sum())
+        _close(r["dg"][t, 0], dg, what="pure decay dg")
+        D = sum((A[s] / A[t]) * np.outer(dO[s], q[s]) for s in range(t, T)) + (A[-1] / A[t]) * W
+        _close(r["dbeta"][t, 0], (D @ k[t]) @ (v[t] - A[t] * (S0 @ k[t])), what="pure decay dbeta")
+    assert not r["dk"].any() and not r["dv"].any()
+    _close(r["dh0"][0, 0], sum(A[s] * np.outer(dO[s], q[s]) for s in range(T)) + A[-1] * W, what="pure decay dh0")
+
+
+def pin_grad_gate_identity(backward, forward):
+    """dg_t = <dhT, hT> + sum_{s >= t} (dO_s . o_s - dv_s . v_s) within a sequence:
+    scaling S_{t-1} by a_t telescopes through <dL/dS, S> (derivation: with
+    Phi_t = <D_t, S_t>, Phi_{t-1} = dO_{t-1}.o_{t-1} + dg_t and Phi_t = dg_t + beta_t du_t.v_t)."""
+    c, d = _grad_case(64, [7, 3], hk=1, hv=2, dk=3, dv=3)
+    r = backward(**c, **d)
+    out, hT = forward(**c)
+    cu = c["cu_seqlens"]
+    for n in range(2):
+        for h in range(2):
+            tb, te = int(cu[n]), int(cu[n + 1])
+            acc = float((d["dhT"][n, h] * hT[n, h]).sum())
+            for t in range(te - 1, tb - 1, -1):
+                acc += float(d["dout"][t, h] @ out[t, h] - r["dv"][t, h] @ c["v"][t, h])
+                _close(r["dg"][t, h], acc, tol=1e-10, what="gate identity")
+
+
+def pin_grad_split_sequence(backward, forward):
+    """Cutting a sequence in two and chaining the halves through (hT -> h0,
+    dh0 of the second -> dhT of the first) reproduces the whole backward."""
+    c, d = _grad_case(65, [9], hk=1, hv=2, dk=2, dv=3)
+    whole = backward(**c, **d)
+    cut = 4
+    first = {k: (v[:cut] if k in ("q", "k", "v", "g", "beta") else v) for k, v in c.items()}
+    first["cu_seqlens"] = np.array([0, cut], dtype=np.int32)
+    _, hmid = forward(**first)
+    second = {k: (v[cut:] if k in ("q", "k", "v", "g", "beta") else v) for k, v in c.items()}
+    second["cu_seqlens"] = np.array([0, 9 - cut], dtype=np.int32)
+    second["h0"] = hmid
+    r2 = backward(**second, dout=d["dout"][cut:], dhT=d["dhT"])
+    r1 = backward(**first, dout=d["dout"][:cut], dhT=r2["dh0"])
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        _close(np.concatenate([r1[key], r2[key]]), whole[key], tol=1e-10, what="split %s" % key)
+    _close(r1["dh0"], whole["dh0"], tol=1e-10, what="split dh0")
+
+
+def pin_grad_grouped_heads(backward, forward):
+    """Two key heads, each read by two value heads: dq and dk of a key head are
+    the sums of what its value heads give with every key head duplicated."""
+    c, d = _grad_case(66, [5, 2], hk=2, hv=4, dk=3, dv=2)
+    r = backward(**c, **d)
+    dup = dict(c)
+    dup["q"] = np.repeat(c["q"], 2, axis=1)
+    dup["k"] = np.repeat(c["k"], 2, axis=1)
+    rd = backward(**dup, **d)
+    for kh in range(2):
+        _close(r["dq"][:, kh], rd["dq"][:, 2 * kh:2 * kh + 2].sum(axis=1), tol=1e-12, what="grouped dq")
+        _close(r["dk"][:, kh], rd["dk"][:, 2 * kh:2 * kh + 2].sum(axis=1), tol=1e-12, what="grouped dk")
+    for key in ("dv", "dg", "dbeta", "dh0"):
+        _close(r[key], rd[key], tol=1e-12, what="grouped %s" % key)
+
+
+GRAD_PINS = [
+    pin_grad_finite_differences,
+    pin_grad_one_token_closed_form,
+    pin_grad_no_write_closed_form,
+    pin_grad_gate_identity,
+    pin_grad_split_sequence,
+    pin_grad_grouped_heads,
+]

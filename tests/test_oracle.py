@@ -16,6 +16,11 @@ def test_oracle_short_conv_pin(pin):
     pin(oracle.short_conv)
 
 
+@pytest.mark.parametrize("pin", oracle_pins.GRAD_PINS, ids=lambda p: p.__name__)
+def test_oracle_gradient_pin(pin):
+    pin(oracle.gdn_backward, oracle.gdn_forward)
+
+
 @pytest.mark.parametrize("pin", oracle_pins.PRE_PINS, ids=lambda p: p.__name__)
 def test_oracle_preprocessing_pin(pin):
     pin(oracle.preprocess, oracle.gdn_forward)

@@ -79,6 +79,48 @@ CONV_MUTANTS = [
 ]
 
 
+# Mistakes in the gradients, caught by the gradient pins.
+GRAD_MUTANTS = [
+    ("dq_from_previous_state", "dq[qk_off + i] += Snew[(size_t)j * dk + i] * dO[j];",
+     "dq[qk_off + i] += Sprev[(size_t)j * dk + i] * dO[j];"),
+    ("dk_without_readout_term", "dk_out[qk_off + i] += a * Sprev[e] * dp[j];", "(void)0;"),
+    ("dk_readout_undecayed", "dk_out[qk_off + i] += a * Sprev[e] * dp[j];",
+     "dk_out[qk_off + i] += Sprev[e] * dp[j];"),
+    ("dk_without_write_term", "dk_out[qk_off + i] += D[(size_t)j * dk + i] * u;", "(void)u;"),
+    ("dp_sign", "dp[j] = -b * du[j];", "dp[j] = b * du[j];"),
+    ("dbeta_without_readout", "db += du[j] * (vv[j] - p[j]);", "db += du[j] * vv[j];"),
+    ("dv_without_beta", "dv_out[v_off + j] = b * du[j];", "dv_out[v_off + j] = du[j];"),
+    ("dg_not_chained", "dg[tt * hv + h] = a * da;", "dg[tt * hv + h] = da;"),
+    ("adjoint_not_decayed", "D[e] = a * D[e];", "D[e] = D[e];"),
+    ("adjoint_misses_output", "D[(size_t)j * dk + i] += dO[j] * qv[i];", "(void)0;"),
+    ("adjoint_misses_readout", "D[e] += dp[j] * kv[i];", "(void)0;"),
+    ("recompute_off_by_one", "*Snew = st + (m + 1) * SZ", "*Snew = st + m * SZ"),
+    ("dhT_ignored", "D[e] = dhT ? dhT[state_off + e] : 0.0;", "D[e] = 0.0;"),
+    ("value_heads_of_next_group", "for (int32_t h = kh * group; h < (kh + 1) * group; ++h) {",
+     "for (int32_t h = kh; h < kh + group; ++h) {"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", GRAD_MUTANTS, ids=[m[0] for m in GRAD_MUTANTS])
+def test_gradient_pins_catch_mutant(tmp_path, name, old, new):
+    with open(oracle_mod.SOURCE) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation site for %s not found once in the oracle source" % name
+    mpath = tmp_path / ("grad_mutant_%s.c" % name)
+    mpath.write_text(src.replace(old, new))
+    lib = str(tmp_path / ("libgrad_mutant_%s.so" % name))
+    oracle.build(str(mpath), lib)
+    bwd = functools.partial(oracle_mod.gdn_backward, library=lib)
+    fwd = functools.partial(oracle_mod.gdn_forward, library=lib)
+    caught = []
+    for pin in oracle_pins.GRAD_PINS:
+        try:
+            pin(bwd, fwd)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, "gradient mutant %s passed every pin" % name
+
+
 @pytest.mark.parametrize("name,old,new", CONV_MUTANTS, ids=[m[0] for m in CONV_MUTANTS])
 def test_conv_pins_catch_mutant(tmp_path, name, old, new):
     with open(oracle_mod.SOURCE) as f:
