@@ -267,13 +267,56 @@ gdn_status gdn_short_conv(const gdn_conv_dims *dims, const void *x, const float 
                           const int32_t *cu_seqlens, void *state_pool, const int32_t *src_idx,
                           const int32_t *dst_idx, void *y, void *stream);
 
+/*
+ * Backward of gdn_fwd_varlen: gradients of a loss L with respect to every input,
+ * given dL/dout and (optionally) dL/dhT.  The page "Defending Against the
+ * Training-Inference Numeric Mismatch in RL (Especially Linear Attention)"
+ * (section 3.2) runs the recurrence in every forward and leaves the trainer's
+ * backward to a separate kernel; this is that backward for the same recurrence.
+ * With p_t = S_{t-1} k_t and u_t = beta_t (v_t - a_t p_t) (so S_t = a_t S_{t-1} +
+ * u_t k_t^T), and D_t = dL/dS_t walked from the last token back
+ * (D <- D + dO_t q_t^T, du_t = D k_t, D <- a_t (D - beta_t du_t k_t^T)):
+ *
+ *     dq_t = S_t^T dO_t                 dk_t = D_t^T u_t - a_t beta_t S_{t-1}^T du_t
+ *     dv_t = beta_t du_t                dbeta_t = du_t . (v_t - a_t p_t)
+ *     dg_t = <dhT, hT> + sum_{s >= t in the sequence} (dO_s . o_s - dv_s . v_s)
+ *     dh0  = D_0
+ *
+ * dq and dk of a key head add up the value heads that read it.  All sums have a
+ * fixed order and nothing crosses sequences, so the gradients are deterministic
+ * and do not depend on the batch; they are fp32 computations, not bitwise equal
+ * to any other path.
+ *
+ *   q, k, v, g, beta, h0, cu_seqlens : the forward's inputs (dims->pre must be NULL)
+ *   dout        : [T][hv][dv] io dtype, dL/dout
+ *   dhT         : [N][hv][dv][dk] fp32, dL/dhT, or NULL for zero
+ *   dq, dk      : [T][hk][dk] fp32 outputs
+ *   dv          : [T][hv][dv] fp32 output
+ *   dg, dbeta   : [T][hv] fp32 outputs
+ *   dh0         : [N][hv][dv][dk] fp32 output, or NULL to skip it
+ *   workspace   : device scratch of at least gdn_bwd_workspace_size bytes, 16-byte
+ *                 aligned, owned by the caller; its contents on entry do not matter
+ * dk and dv must each be 32, 64 or 128 (else GDN_ERR_UNSUPPORTED, as are a set
+ * dims->pre and plan fields).  Outputs and workspace must not overlap each other
+ * or an input (GDN_ERR_ALIAS); a workspace smaller than needed is GDN_ERR_SHAPE.
+ */
+gdn_status gdn_bwd_workspace_size(const gdn_dims *dims, uint64_t *bytes);
+
+gdn_status gdn_bwd_varlen(const gdn_dims *dims,
+                          const void *q, const void *k, const void *v,
+                          const float *g, const float *beta,
+                          const float *h0, const int32_t *cu_seqlens,
+                          const void *dout, const float *dhT,
+                          float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dh0,
+                          void *workspace, uint64_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *gdn_status_string(gdn_status status);
 
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 201
+#define GDN_ABI_VERSION 202
 
 #ifdef __cplusplus
 }

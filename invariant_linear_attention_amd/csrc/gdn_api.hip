@@ -380,6 +380,77 @@ gdn_status gdn_short_conv(const gdn_conv_dims *dims, const void *x, const float 
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_bwd_workspace_size(const gdn_dims *dims, uint64_t *bytes) {
+    using namespace gdn;
+    if (!bytes) return GDN_ERR_NULL;
+    const gdn_status st = check_common(dims);
+    if (st != GDN_OK) return st;
+    *bytes = backward_workspace(dims->total_tokens, dims->n_seqs, dims->hv, dims->dk, dims->dv).total;
+    return GDN_OK;
+}
+
+gdn_status gdn_bwd_varlen(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *h0, const int32_t *cu_seqlens, const void *dout,
+                          const float *dhT, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dh0,
+                          void *workspace, uint64_t workspace_bytes, void *stream) {
+    using namespace gdn;
+    gdn_status st = check_common(dims);
+    if (st != GDN_OK) return st;
+    const gdn_dims &d = *dims;
+    if (d.pre || d.plan_lanes || d.plan_rows || d.plan_waves) return GDN_ERR_UNSUPPORTED;
+    auto bwd_dim = [](int x) { return x == 32 || x == 64 || x == 128; };
+    if (!bwd_dim(d.dk) || !bwd_dim(d.dv)) return GDN_ERR_UNSUPPORTED;
+    const int64_t T = d.total_tokens, N = d.n_seqs;
+    if (N == 0) return T == 0 ? GDN_OK : GDN_ERR_SHAPE;
+    if (!cu_seqlens || !workspace) return GDN_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
+        return GDN_ERR_NULL;
+    const BwdWorkspace ws = backward_workspace(T, N, d.hv, d.dk, d.dv);
+    if (workspace_bytes < ws.total) return GDN_ERR_SHAPE;
+    if (N * d.hv * (int64_t)(d.dv / 32 > d.dk / 32 ? d.dv / 32 : d.dk / 32) > 0x7FFFFFFFll ||
+        (T * d.hk + 3) / 4 > 0x7FFFFFFFll)
+        return GDN_ERR_SHAPE;  // 1-D grids
+
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(h0, 16) ||
+        !aligned(dhT, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dh0, 16) ||
+        !aligned(workspace, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(dg, 4) || !aligned(dbeta, 4) ||
+        !aligned(cu_seqlens, 4))
+        return GDN_ERR_ALIGN;
+
+    const uint64_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
+    const uint64_t qk_n = (uint64_t)T * d.hk * d.dk, vo_n = (uint64_t)T * d.hv * d.dv;
+    const uint64_t gb_bytes = (uint64_t)T * d.hv * 4, s_bytes = (uint64_t)N * d.hv * d.dv * d.dk * 4;
+    const Range inputs[] = {range_of(q, qk_n * esz), range_of(k, qk_n * esz), range_of(v, vo_n * esz),
+                            range_of(g, gb_bytes), range_of(beta, gb_bytes), range_of(h0, h0 ? s_bytes : 0),
+                            range_of(cu_seqlens, (uint64_t)(N + 1) * 4), range_of(dout, vo_n * esz),
+                            range_of(dhT, dhT ? s_bytes : 0)};
+    const Range outputs[] = {range_of(dq, qk_n * 4), range_of(dk, qk_n * 4), range_of(dv, vo_n * 4),
+                             range_of(dg, gb_bytes), range_of(dbeta, gb_bytes), range_of(dh0, dh0 ? s_bytes : 0),
+                             range_of(workspace, ws.total)};
+    for (size_t i = 0; i < sizeof(outputs) / sizeof(outputs[0]); ++i) {
+        for (const Range &in : inputs)
+            if (overlap(outputs[i], in)) return GDN_ERR_ALIAS;
+        for (size_t j = i + 1; j < sizeof(outputs) / sizeof(outputs[0]); ++j)
+            if (overlap(outputs[i], outputs[j])) return GDN_ERR_ALIAS;
+    }
+
+    char *w = static_cast<char *>(workspace);
+    BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.dout = dout; p.g = g; p.beta = beta; p.h0 = h0; p.dhT = dhT;
+    p.cu_seqlens = cu_seqlens;
+    p.grad_q = dq; p.grad_k = dk; p.grad_v = dv; p.grad_g = dg; p.grad_beta = dbeta; p.grad_h0 = dh0;
+    p.pbuf = reinterpret_cast<float *>(w + ws.p);
+    p.dubuf = reinterpret_cast<float *>(w + ws.du);
+    p.dkbuf = reinterpret_cast<float *>(w + ws.dk);
+    p.dqbuf = reinterpret_cast<float *>(w + ws.dq);
+    p.cbuf = reinterpret_cast<float *>(w + ws.c);
+    p.hT = reinterpret_cast<float *>(w + ws.hT);
+    p.total_tokens = T; p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dk = d.dk; p.dv = d.dv;
+    p.rank_by_length = (N > 1 && N <= kMaxRankedSeqs && T >= 32 * N) ? 1 : 0;
+    const hipError_t e = launch_backward(p, d.io_dtype, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 const char *gdn_status_string(gdn_status status) {
     switch (status) {
         case GDN_OK: return "GDN_OK";

@@ -1,0 +1,415 @@
+// gdn_bwd.hip -- gradients of the recurrent forward (gdn_bwd_varlen).
+//
+// Forward step of token t (per sequence and value head; S is dv x dk, row j):
+//     p_t = S_{t-1} k_t,   u_t = beta_t (v_t - a_t p_t),   S_t = a_t S_{t-1} + u_t k_t^T,
+//     o_t = S_t q_t,       a_t = exp(g_t)
+// (the gated delta rule of Yang, Kautz and Hatamizadeh, ICLR 2025; the page "Defending
+// Against the Training-Inference Numeric Mismatch in RL (Especially Linear
+// Attention)", section 3.2, runs it token by token in every forward and keeps the
+// training backward as a separate kernel).
+//
+// With D_t = dL/dS_t, the adjoint walked from the last token back is
+//     D  <- D + dO_t q_t^T;   du_t = D k_t;   D <- a_t (D - beta_t du_t k_t^T)
+// and the gradients are
+//     dv_t = beta_t du_t,  dbeta_t = du_t . (v_t - a_t p_t),
+//     dq_t = S_t^T dO_t,   dk_t = D_t^T u_t + S_{t-1}^T (-a_t beta_t du_t),
+//     dg_t = <dhT, hT> + sum_{s >= t} (dO_s . o_s - dv_s . v_s),   dh0 = D_0.
+// The gate gradient needs no state inner product: with Phi_t = <D_t, S_t>,
+// Phi_{t-1} = dO_{t-1} . o_{t-1} + dg_t and Phi_t = dg_t + beta_t du_t . v_t, so dg is a
+// reverse running sum within the sequence; dO_s . o_s = q_s . dq_s.
+//
+// Every gradient is then a row-wise quantity of some state, which keeps the
+// forward's layout (L lanes hold one state row, row dots finished by DPP, no
+// reduction across rows) in each of four passes over the tokens:
+//
+//   F0 forward  over S   (rows j, columns i): p_t, and hT
+//   R1 reverse  over D   (rows j, columns i): du_t, and dh0 = D_0
+//   R2 reverse  over D^T (rows i, columns j): (D_t^T u_t)_i             -> dk
+//   F3 forward  over S^T (rows i, columns j): (S_{t-1}^T w_t)_i, w_t = -a_t beta_t du_t,
+//                                            and (S_t^T dO_t)_i          -> dk, dq
+//
+// then one kernel per (token, key head) sums the value heads of a key head, forms
+// dv, dbeta and the gate term, and one per (sequence, value head) runs the reverse
+// sum for dg.  Every sum has a fixed order and nothing crosses sequences, so the
+// gradients are deterministic and do not depend on the batch.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_internal.hpp"
+#include "gdn_kernels.hpp"
+
+#pragma clang fp contract(off)
+
+namespace gdn {
+namespace {
+
+enum BwdPass { kF0 = 0, kR1 = 1, kR2 = 2, kF3 = 3 };
+
+constexpr int kBwdLanes = 8;   // lanes per state row
+constexpr int kBwdWaves = 4;   // waves per workgroup
+constexpr int kBwdRows = kBwdWaves * (64 / kBwdLanes);  // rows per workgroup (32)
+constexpr int kBwdThreads = kBwdWaves * 64;
+constexpr int kBwdTB = 16;     // tokens per staged block
+
+// Number of column vectors and row scalars each pass stages per token.
+constexpr int cols_of(int pass) { return pass == kF0 ? 1 : (pass == kR1 ? 2 : 3); }
+constexpr int rows_of(int pass) { return pass == kR2 ? 2 : 1; }
+
+template <int C>
+__device__ __forceinline__ float lane_dot(const float (&x)[C], const float (&y)[C]) {
+    constexpr int K = C >= 16 ? 4 : (C >= 8 ? 2 : 1);  // independent chains
+    float acc[K];
+#pragma unroll
+    for (int c = 0; c < K; ++c) acc[c] = x[c] * y[c];
+#pragma unroll
+    for (int c = K; c < C; ++c) acc[c % K] = __builtin_fmaf(x[c], y[c], acc[c % K]);
+    if constexpr (K == 1) return acc[0];
+    else if constexpr (K == 2) return acc[0] + acc[1];
+    else return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+template <int NC>
+struct alignas(16) BwdLds {
+    float cv[3][kBwdTB][NC];     // column vectors of each staged token
+    float rs[2][kBwdTB][kBwdRows];  // row scalars of this tile
+    float a[kBwdTB], b[kBwdTB];  // exp(g), beta
+};
+
+// One workgroup = (sequence, value head, tile of 32 state rows) for pass PASS.
+// NC: length of a state row (dk for F0 / R1, dv for R2 / F3).
+template <int PASS, int NC, class IO>
+__global__ __launch_bounds__(kBwdThreads) void gdn_bwd_pass_kernel(BwdParams p) {
+    constexpr int C = NC / kBwdLanes;
+    constexpr bool REV = (PASS == kR1 || PASS == kR2);
+    constexpr int NCV = cols_of(PASS), NRS = rows_of(PASS);
+    __shared__ BwdLds<NC> Ld;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lam = lane % kBwdLanes, grp = lane / kBwdLanes;
+    const int rows = (PASS == kF0 || PASS == kR1) ? p.dv : p.dk;  // state rows of this pass
+    const int tiles = rows / kBwdRows;
+    const int tile = blockIdx.x % tiles;
+    const int h = (blockIdx.x / tiles) % p.hv;
+    const int rank = blockIdx.x / (tiles * p.hv);
+    const int n = p.rank_by_length ? seq_by_length_rank(p.cu_seqlens, p.n_seqs, rank, tid, kBwdThreads) : rank;
+    const int kh = h / (p.hv / p.hk);
+    const int lrow = wave * (64 / kBwdLanes) + grp;  // row within the tile
+    const int row = tile * kBwdRows + lrow;
+    const int col0 = lam * C;
+
+    int64_t tb = p.cu_seqlens[n], te = p.cu_seqlens[n + 1];
+    tb = tb < 0 ? 0 : (tb > p.total_tokens ? p.total_tokens : tb);
+    te = te < tb ? tb : (te > p.total_tokens ? p.total_tokens : te);
+
+    // state slice: row `row`, columns col0 .. col0 + C - 1
+    const size_t sbase = ((size_t)n * p.hv + h) * (size_t)p.dv * p.dk;
+    float X[C];
+    {
+        const float *init = (PASS == kF0 || PASS == kF3) ? p.h0 : p.dhT;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            float x = 0.f;
+            if (init) {
+                // F0 / R1 hold rows j (dv) of a dv x dk matrix; R2 / F3 hold its transpose
+                x = (PASS == kF0 || PASS == kR1) ? init[sbase + (size_t)row * p.dk + col0 + c]
+                                                 : init[sbase + (size_t)(col0 + c) * p.dk + row];
+            }
+            X[c] = x;
+        }
+    }
+
+    const int64_t len = te - tb;
+    const int nblk = (int)((len + kBwdTB - 1) / kBwdTB);
+    for (int blk = 0; blk < nblk; ++blk) {
+        // Forward passes take block blk from the start, reverse passes from the end.
+        const int64_t t0 = REV ? (te - (int64_t)(blk + 1) * kBwdTB) : (tb + (int64_t)blk * kBwdTB);
+        const int64_t s0 = t0 < tb ? tb : t0;                     // first token of the block
+        const int64_t s1 = (t0 + kBwdTB > te) ? te : t0 + kBwdTB;  // one past the last
+        const int nt = (int)(s1 - s0);
+
+        // ---- stage the block's tokens (slot ti = token s0 + ti)
+        for (int idx = tid; idx < nt * NC; idx += kBwdThreads) {
+            const int ti = idx / NC, c = idx % NC;
+            const int64_t t = s0 + ti;
+            const size_t qk = ((size_t)t * p.hk + kh) * p.dk + c;  // F0 / R1 columns (dk)
+            const size_t vv = ((size_t)t * p.hv + h) * p.dv + c;   // R2 / F3 columns (dv)
+            if constexpr (PASS == kF0) {
+                Ld.cv[0][ti][c] = IO::load1(p.k, qk);
+            } else if constexpr (PASS == kR1) {
+                Ld.cv[0][ti][c] = IO::load1(p.q, qk);
+                Ld.cv[1][ti][c] = IO::load1(p.k, qk);
+            } else {
+                const float a = decay_factor(p.g[(size_t)t * p.hv + h]);
+                const float b = p.beta[(size_t)t * p.hv + h];
+                const float u = b * (IO::load1(p.v, vv) - a * p.pbuf[vv]);
+                const float dvv = b * p.dubuf[vv];
+                const float dO = IO::load1(p.dout, vv);
+                if constexpr (PASS == kR2) {
+                    Ld.cv[0][ti][c] = dO;
+                    Ld.cv[1][ti][c] = u;
+                    Ld.cv[2][ti][c] = dvv;
+                } else {
+                    Ld.cv[0][ti][c] = -a * dvv;  // w_t = -a_t beta_t du_t
+                    Ld.cv[1][ti][c] = u;
+                    Ld.cv[2][ti][c] = dO;
+                }
+            }
+        }
+        for (int idx = tid; idx < nt * kBwdRows; idx += kBwdThreads) {
+            const int ti = idx / kBwdRows, r = idx % kBwdRows;
+            const int64_t t = s0 + ti;
+            const int rr = tile * kBwdRows + r;
+            if constexpr (PASS == kF0) {
+                Ld.rs[0][ti][r] = IO::load1(p.v, ((size_t)t * p.hv + h) * p.dv + rr);
+            } else if constexpr (PASS == kR1) {
+                Ld.rs[0][ti][r] = IO::load1(p.dout, ((size_t)t * p.hv + h) * p.dv + rr);
+            } else {
+                const size_t qk = ((size_t)t * p.hk + kh) * p.dk + rr;
+                Ld.rs[0][ti][r] = (PASS == kR2) ? IO::load1(p.q, qk) : IO::load1(p.k, qk);
+                if constexpr (PASS == kR2) Ld.rs[1][ti][r] = IO::load1(p.k, qk);
+            }
+        }
+        if (tid < nt) {
+            const int64_t t = s0 + tid;
+            Ld.a[tid] = decay_factor(p.g[(size_t)t * p.hv + h]);
+            Ld.b[tid] = p.beta[(size_t)t * p.hv + h];
+        }
+        __syncthreads();
+
+        // ---- walk the block's tokens in this pass's direction
+        for (int step = 0; step < nt; ++step) {
+            const int ti = REV ? nt - 1 - step : step;
+            const int64_t t = s0 + ti;
+            const float a = Ld.a[ti], b = Ld.b[ti];
+            float v0[C], v1[C];
+#pragma unroll
+            for (int j = 0; j < C / 4; ++j) {
+                const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[0][ti][col0 + 4 * j]);
+                v0[4 * j] = x.x; v0[4 * j + 1] = x.y; v0[4 * j + 2] = x.z; v0[4 * j + 3] = x.w;
+            }
+            if constexpr (NCV >= 2) {
+#pragma unroll
+                for (int j = 0; j < C / 4; ++j) {
+                    const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[1][ti][col0 + 4 * j]);
+                    v1[4 * j] = x.x; v1[4 * j + 1] = x.y; v1[4 * j + 2] = x.z; v1[4 * j + 3] = x.w;
+                }
+            }
+            const float r0 = Ld.rs[0][ti][lrow];
+            if constexpr (PASS == kF0) {
+                // p = S_{t-1} k;  u = beta (v - a p);  S = a S + u k^T
+                const float pt = lane_sum<kBwdLanes>(lane_dot<C>(X, v0));
+                if (lam == 0) p.pbuf[((size_t)t * p.hv + h) * p.dv + row] = pt;
+                const float u = b * (r0 - a * pt);
+#pragma unroll
+                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(a, X[c], u * v0[c]);
+            } else if constexpr (PASS == kR1) {
+                // D += dO q^T;  du = D k;  D = a (D - beta du k^T)
+#pragma unroll
+                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(r0, v0[c], X[c]);
+                const float du = lane_sum<kBwdLanes>(lane_dot<C>(X, v1));
+                if (lam == 0) p.dubuf[((size_t)t * p.hv + h) * p.dv + row] = du;
+                const float bdu = b * du;
+#pragma unroll
+                for (int c = 0; c < C; ++c) X[c] = a * __builtin_fmaf(-bdu, v1[c], X[c]);
+            } else if constexpr (PASS == kR2) {
+                // E = D^T:  E += q dO^T;  y = E u;  E = a (E - k dv^T)
+                float v2[C];
+#pragma unroll
+                for (int j = 0; j < C / 4; ++j) {
+                    const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[2][ti][col0 + 4 * j]);
+                    v2[4 * j] = x.x; v2[4 * j + 1] = x.y; v2[4 * j + 2] = x.z; v2[4 * j + 3] = x.w;
+                }
+                const float r1 = Ld.rs[1][ti][lrow];
+#pragma unroll
+                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(r0, v0[c], X[c]);
+                const float y = lane_sum<kBwdLanes>(lane_dot<C>(X, v1));
+                if (lam == 0) p.dkbuf[((size_t)t * p.hv + h) * p.dk + row] = y;
+#pragma unroll
+                for (int c = 0; c < C; ++c) X[c] = a * __builtin_fmaf(-r1, v2[c], X[c]);
+            } else {
+                // P = S^T:  y1 = P w (old state);  P = a P + k u^T;  y2 = P dO (new state)
+                float v2[C];
+#pragma unroll
+                for (int j = 0; j < C / 4; ++j) {
+                    const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[2][ti][col0 + 4 * j]);
+                    v2[4 * j] = x.x; v2[4 * j + 1] = x.y; v2[4 * j + 2] = x.z; v2[4 * j + 3] = x.w;
+                }
+                const float y1 = lane_sum<kBwdLanes>(lane_dot<C>(X, v0));
+#pragma unroll
+                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(a, X[c], r0 * v1[c]);
+                const float y2 = lane_sum<kBwdLanes>(lane_dot<C>(X, v2));
+                if (lam == 0) {
+                    const size_t o = ((size_t)t * p.hv + h) * p.dk + row;
+                    p.dkbuf[o] = p.dkbuf[o] + y1;  // R2 wrote the other term
+                    p.dqbuf[o] = y2;
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // final states: hT after F0 (only needed for <dhT, hT>), dh0 = D_0 after R1
+    float *dst = (PASS == kF0) ? (p.dhT ? p.hT : nullptr) : (PASS == kR1 ? p.grad_h0 : nullptr);
+    if (dst) {
+#pragma unroll
+        for (int c = 0; c < C; c += 4)
+            *reinterpret_cast<float4 *>(dst + sbase + (size_t)row * p.dk + col0 + c) =
+                make_float4(X[c], X[c + 1], X[c + 2], X[c + 3]);
+    }
+}
+
+// Sum over the 64 lanes of a wave (pairwise over lane index; every lane gets it).
+__device__ __forceinline__ float wave_sum(float x) {
+    x = group_sum<32>(x);
+    return x + __shfl_xor(x, 32);
+}
+
+// One wave per (token, key head): dq and dk of the key head (its value heads in
+// order), and per value head dv = beta du, dbeta = du . (v - a p) and the gate term
+// c = q . dq_h - dv . v.
+template <class IO>
+__global__ __launch_bounds__(256) void gdn_bwd_finish_kernel(BwdParams p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= p.total_tokens * p.hk) return;
+    const int64_t t = item / p.hk;
+    const int kh = (int)(item % p.hk);
+    const int G = p.hv / p.hk;
+    for (int i = lane; i < p.dk; i += 64) {
+        float sq = 0.f, sk = 0.f;
+        for (int m = 0; m < G; ++m) {
+            const size_t o = ((size_t)t * p.hv + kh * G + m) * p.dk + i;
+            sq += p.dqbuf[o];
+            sk += p.dkbuf[o];
+        }
+        const size_t oq = ((size_t)t * p.hk + kh) * p.dk + i;
+        p.grad_q[oq] = sq;
+        p.grad_k[oq] = sk;
+    }
+    for (int m = 0; m < G; ++m) {
+        const int h = kh * G + m;
+        const float a = decay_factor(p.g[(size_t)t * p.hv + h]);
+        const float b = p.beta[(size_t)t * p.hv + h];
+        float db = 0.f, dvv = 0.f, qdq = 0.f;
+        for (int j = lane; j < p.dv; j += 64) {
+            const size_t o = ((size_t)t * p.hv + h) * p.dv + j;
+            const float du = p.dubuf[o], v = IO::load1(p.v, o);
+            const float dv = b * du;
+            p.grad_v[o] = dv;
+            db = __builtin_fmaf(du, v - a * p.pbuf[o], db);
+            dvv = __builtin_fmaf(dv, v, dvv);
+        }
+        for (int i = lane; i < p.dk; i += 64)
+            qdq = __builtin_fmaf(IO::load1(p.q, ((size_t)t * p.hk + kh) * p.dk + i),
+                                 p.dqbuf[((size_t)t * p.hv + h) * p.dk + i], qdq);
+        db = wave_sum(db);
+        dvv = wave_sum(dvv);
+        qdq = wave_sum(qdq);
+        if (lane == 0) {
+            p.grad_beta[(size_t)t * p.hv + h] = db;
+            p.cbuf[(size_t)t * p.hv + h] = qdq - dvv;
+        }
+    }
+}
+
+// One workgroup per (sequence, value head): dg_t = <dhT, hT> + sum_{s >= t} c_s,
+// accumulated in fp64.  Thread k owns a contiguous stretch of the sequence; the
+// stretch sums are combined in a fixed order.
+__global__ __launch_bounds__(256) void gdn_bwd_gate_kernel(BwdParams p) {
+    __shared__ double red[256];
+    const int tid = threadIdx.x;
+    const int n = blockIdx.x / p.hv, h = blockIdx.x % p.hv;
+    int64_t tb = p.cu_seqlens[n], te = p.cu_seqlens[n + 1];
+    tb = tb < 0 ? 0 : (tb > p.total_tokens ? p.total_tokens : tb);
+    te = te < tb ? tb : (te > p.total_tokens ? p.total_tokens : te);
+
+    double base = 0.0;
+    if (p.dhT) {  // <dhT, hT>
+        const size_t s = ((size_t)n * p.hv + h) * (size_t)p.dv * p.dk;
+        double acc = 0.0;
+        for (int64_t e = tid; e < (int64_t)p.dv * p.dk; e += 256)
+            acc += (double)p.dhT[s + e] * (double)p.hT[s + e];
+        red[tid] = acc;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if (tid < w) red[tid] += red[tid + w];
+            __syncthreads();
+        }
+        base = red[0];
+        __syncthreads();
+    }
+    const int64_t len = te - tb;
+    const int64_t per = (len + 255) / 256;
+    const int64_t c0 = tb + tid * per, c1 = (c0 + per < te) ? c0 + per : te;
+    double mine = 0.0;
+    for (int64_t t = c0; t < c1; ++t) mine += (double)p.cbuf[(size_t)t * p.hv + h];
+    red[tid] = mine;
+    __syncthreads();
+    // suffix over the stretches after this one, added in stretch order
+    double after = base;
+    for (int k = 255; k > tid; --k) after += red[k];
+    double run = after;
+    for (int64_t t = c1 - 1; t >= c0; --t) {
+        run += (double)p.cbuf[(size_t)t * p.hv + h];
+        p.grad_g[(size_t)t * p.hv + h] = (float)run;
+    }
+}
+
+template <int PASS, int NC, class IO>
+hipError_t launch_pass(const BwdParams &p, hipStream_t s) {
+    const int rows = (PASS == kF0 || PASS == kR1) ? p.dv : p.dk;
+    const dim3 grid((unsigned)((int64_t)p.n_seqs * p.hv * (rows / kBwdRows)));
+    hipLaunchKernelGGL((gdn_bwd_pass_kernel<PASS, NC, IO>), grid, dim3(kBwdThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int PASS, class IO>
+hipError_t pass_for_dims(const BwdParams &p, hipStream_t s) {
+    const int nc = (PASS == kF0 || PASS == kR1) ? p.dk : p.dv;
+    switch (nc) {
+        case 32: return launch_pass<PASS, 32, IO>(p, s);
+        case 64: return launch_pass<PASS, 64, IO>(p, s);
+        case 128: return launch_pass<PASS, 128, IO>(p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <class IO>
+hipError_t backward_io(const BwdParams &p, hipStream_t s) {
+    hipError_t e;
+    if ((e = pass_for_dims<kF0, IO>(p, s)) != hipSuccess) return e;
+    if ((e = pass_for_dims<kR1, IO>(p, s)) != hipSuccess) return e;
+    if ((e = pass_for_dims<kR2, IO>(p, s)) != hipSuccess) return e;
+    if ((e = pass_for_dims<kF3, IO>(p, s)) != hipSuccess) return e;
+    if (p.total_tokens > 0) {
+        const int64_t items = p.total_tokens * p.hk;
+        hipLaunchKernelGGL((gdn_bwd_finish_kernel<IO>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(gdn_bwd_gate_kernel, dim3((unsigned)((int64_t)p.n_seqs * p.hv)), dim3(256), 0, s, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+uint64_t round_up(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+}  // namespace
+
+BwdWorkspace backward_workspace(int64_t T, int64_t N, int hv, int dk, int dv) {
+    BwdWorkspace w{};
+    uint64_t off = 0;
+    w.p = off;  off += round_up((uint64_t)T * hv * dv * 4);
+    w.du = off; off += round_up((uint64_t)T * hv * dv * 4);
+    w.dk = off; off += round_up((uint64_t)T * hv * dk * 4);
+    w.dq = off; off += round_up((uint64_t)T * hv * dk * 4);
+    w.c = off;  off += round_up((uint64_t)T * hv * 4);
+    w.hT = off; off += round_up((uint64_t)N * hv * dv * dk * 4);
+    w.total = off;
+    return w;
+}
+
+hipError_t launch_backward(const BwdParams &p, int io_dtype, hipStream_t s) {
+    return io_dtype == GDN_BF16 ? backward_io<IoBf16>(p, s) : backward_io<IoF32>(p, s);
+}
+
+}  // namespace gdn

@@ -70,6 +70,32 @@ struct ConvParams {
 };
 hipError_t launch_short_conv(const ConvParams &p, int io_dtype, hipStream_t s);
 
+// Kernel arguments of the backward (gdn_bwd_varlen).  The four row passes and the
+// two finishing kernels share them; each reads and writes the parts it needs.
+struct BwdParams {
+    const void *q, *k, *v, *dout;    // io dtype
+    const float *g, *beta, *h0, *dhT;
+    const int32_t *cu_seqlens;
+    float *grad_q, *grad_k, *grad_v, *grad_g, *grad_beta, *grad_h0;  // outputs (grad_h0 may be null)
+    // workspace
+    float *pbuf;   // [T][hv][dv]   p_t = S_{t-1} k_t
+    float *dubuf;  // [T][hv][dv]   du_t = dL/du_t
+    float *dkbuf;  // [T][hv][dk]   dk of each value head
+    float *dqbuf;  // [T][hv][dk]   dq of each value head
+    float *cbuf;   // [T][hv]       q_t . dq_t - dv_t . v_t (the gate term)
+    float *hT;     // [N][hv][dv][dk] final state (when dhT is given)
+    int64_t total_tokens;
+    int32_t n_seqs, hk, hv, dk, dv;
+    int32_t rank_by_length;
+};
+hipError_t launch_backward(const BwdParams &p, int io_dtype, hipStream_t s);
+// Workspace layout of the backward: byte offsets of pbuf, dubuf, dkbuf, dqbuf,
+// cbuf and hT, and the total.
+struct BwdWorkspace {
+    uint64_t p, du, dk, dq, c, hT, total;
+};
+BwdWorkspace backward_workspace(int64_t T, int64_t N, int hv, int dk, int dv);
+
 // A launch shape: `lanes` lanes hold one state row, each lane holds `rows` rows,
 // and a workgroup has `waves` waves; it owns waves * (64 / lanes) * rows
 // consecutive rows of one value head.

@@ -20,7 +20,7 @@ STATUS = {
     5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_HIP",
 }
 EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv", "gdn_query_plan",
-           "gdn_status_string", "gdn_abi_version")
+           "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_status_string", "gdn_abi_version")
 
 
 GDN_PRE_QK_L2NORM, GDN_PRE_GATE_LOGITS = 1, 2
@@ -84,6 +84,10 @@ def load_library(path: str = LIBRARY):
         lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdn_short_conv.restype = ctypes.c_int
         lib.gdn_short_conv.argtypes = [ctypes.POINTER(GdnConvDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdn_bwd_workspace_size.restype = ctypes.c_int
+        lib.gdn_bwd_workspace_size.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(ctypes.c_uint64)]
+        lib.gdn_bwd_varlen.restype = ctypes.c_int
+        lib.gdn_bwd_varlen.argtypes = [ctypes.POINTER(GdnDims)] + [vp] * 16 + [ctypes.c_uint64, vp]
         lib.gdn_query_plan.restype = ctypes.c_int
         lib.gdn_query_plan.argtypes = [ctypes.POINTER(GdnDims), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
         lib.gdn_status_string.restype = ctypes.c_char_p
@@ -199,6 +203,49 @@ def gdn_fwd_varlen(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, stream=N
     _check(lib.gdn_fwd_varlen(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
                               _ptr(cu_seqlens), _ptr(out), _ptr(hT), _stream_handle(stream)))
     return out, hT
+
+
+def gdn_bwd_workspace_size(dims: GdnDims) -> int:
+    """Workspace bytes gdn_bwd_varlen needs for ``dims`` (host only)."""
+    n = ctypes.c_uint64(0)
+    _check(load_library().gdn_bwd_workspace_size(ctypes.byref(dims), ctypes.byref(n)))
+    return int(n.value)
+
+
+def gdn_bwd_varlen(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=None, grads=None, stream=None,
+                   want_dh0: bool = True):
+    """Backward of gdn_fwd_varlen (see include/gdn.h).  Inputs as gdn_fwd_varlen plus
+    dout [T, Hv, dv] (dtype of q) and dhT [N, Hv, dv, dk] fp32 or None.  ``workspace``
+    (a uint8 device tensor of at least gdn_bwd_workspace_size bytes) and ``grads``
+    (a dict of output tensors) are allocated when None.  Returns a dict of fp32
+    tensors: dq, dk [T, Hk, dk]; dv [T, Hv, dv]; dg, dbeta [T, Hv]; dh0."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _need(t, name, q.dtype)
+    for name, t in (("g", g), ("beta", beta), ("h0", h0), ("dhT", dhT)):
+        _need(t, name, torch.float32)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    T, hk, dk = (int(x) for x in q.shape)
+    hv, dv = int(v.shape[1]), int(v.shape[2])
+    N = int(cu_seqlens.numel()) - 1
+    dims = make_dims(q, v, N, T)
+    if workspace is None:
+        workspace = torch.empty(gdn_bwd_workspace_size(dims), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    if grads is None:
+        f32 = dict(dtype=torch.float32, device=q.device)
+        grads = {"dq": torch.empty((T, hk, dk), **f32), "dk": torch.empty((T, hk, dk), **f32),
+                 "dv": torch.empty((T, hv, dv), **f32), "dg": torch.empty((T, hv), **f32),
+                 "dbeta": torch.empty((T, hv), **f32),
+                 "dh0": torch.empty((N, hv, dv, dk), **f32) if want_dh0 else None}
+    for name, t in grads.items():
+        _need(t, name, torch.float32)
+    _check(lib.gdn_bwd_varlen(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                              _ptr(cu_seqlens), _ptr(dout), _ptr(dhT), _ptr(grads["dq"]), _ptr(grads["dk"]),
+                              _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["dbeta"]), _ptr(grads.get("dh0")),
+                              _ptr(workspace), int(workspace.numel()), _stream_handle(stream)))
+    return grads
 
 
 def gdn_fwd_varlen_pool(q, k, v, g, beta, cu_seqlens, state_pool, src_idx=None, dst_idx=None, pos0=None,

@@ -28,7 +28,8 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
-                          "gdn_query_plan", "gdn_status_string", "gdn_abi_version"}
+                          "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_status_string",
+                          "gdn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -376,3 +377,67 @@ def test_conv_rejects(lib, case, over, code):
 def test_conv_null_dims_and_noop(lib):
     assert call_conv(lib, None) == 1
     assert call_conv(lib, _cdims(n_seqs=0, total_tokens=0)) == 0
+
+
+# ------------------------------------------------------------------ backward
+
+BP = {name: BASE + (40 + i) * MB for i, name in enumerate(
+    ["q", "k", "v", "g", "b", "h0", "cu", "dout", "dhT", "dq", "dk", "dv", "dg", "db", "dh0", "ws"])}
+
+
+def ws_size(lib, dims):
+    n = ctypes.c_uint64(0)
+    assert lib.gdn_bwd_workspace_size(ctypes.byref(dims), ctypes.byref(n)) == 0
+    return int(n.value)
+
+
+def call_bwd(lib, dims, ws_bytes=None, **over):
+    a = dict(BP)
+    a.update(over)
+    if ws_bytes is None:
+        ws_bytes = ws_size(lib, dims) if dims is not None else 0
+    return lib.gdn_bwd_varlen(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], a["v"], a["g"],
+                              a["b"], a["h0"], a["cu"], a["dout"], a["dhT"], a["dq"], a["dk"], a["dv"], a["dg"],
+                              a["db"], a["dh0"], a["ws"], ctypes.c_uint64(ws_bytes), None)
+
+
+def test_bwd_workspace_size(lib):
+    """p, du (T hv dv), dk, dq (T hv dk), the gate term (T hv) and a final state
+    per (sequence, head), each rounded up to 256 bytes."""
+    up = lambda x: (x + 255) // 256 * 256
+    T, N, hv, dk, dv = 10, 2, 4, 128, 64
+    want = 2 * up(T * hv * dv * 4) + 2 * up(T * hv * dk * 4) + up(T * hv * 4) + up(N * hv * dv * dk * 4)
+    assert ws_size(lib, _dims(dv=dv)) == want
+    n = ctypes.c_uint64(0)
+    assert lib.gdn_bwd_workspace_size(None, ctypes.byref(n)) == 1
+    assert lib.gdn_bwd_workspace_size(ctypes.byref(_dims()), None) == 1
+    assert lib.gdn_bwd_workspace_size(ctypes.byref(_dims(hv=3)), ctypes.byref(n)) == 2
+
+
+@pytest.mark.parametrize("case,over,code", [
+    (dict(dk=16), {}, 6), (dict(dv=16), {}, 6), (dict(dv=96), {}, 6), (dict(plan_lanes=8), {}, 6),
+    (dict(hv=3), {}, 2), (dict(io_dtype=7), {}, 3), (dict(n_seqs=0, total_tokens=3), {}, 2),
+    ({}, dict(cu=None), 1), ({}, dict(ws=None), 1), ({}, dict(q=None), 1), ({}, dict(dout=None), 1),
+    ({}, dict(dq=None), 1), ({}, dict(dg=None), 1), ({}, dict(db=None), 1), ({}, dict(dv=None), 1),
+    ({}, dict(q=BP["q"] + 8), 4), ({}, dict(dout=BP["dout"] + 8), 4), ({}, dict(ws=BP["ws"] + 4), 4),
+    ({}, dict(dq=BP["dq"] + 4), 4), ({}, dict(g=BP["g"] + 2), 4),
+    ({}, dict(dq=BP["q"]), 5), ({}, dict(dk=BP["dq"]), 5), ({}, dict(ws=BP["dout"]), 5),
+    ({}, dict(dh0=BP["h0"]), 5), ({}, dict(dv=BP["ws"] + 256), 5), ({}, dict(dg=BP["db"]), 5),
+])
+def test_bwd_rejects(lib, case, over, code):
+    assert call_bwd(lib, _dims(**case), ws_bytes=(1 << 30), **over) == code
+
+
+def test_bwd_small_workspace_and_noop(lib):
+    d = _dims()
+    assert call_bwd(lib, d, ws_bytes=ws_size(lib, d) - 1) == 2
+    assert call_bwd(lib, None) == 1
+    assert call_bwd(lib, _dims(n_seqs=0, total_tokens=0), ws_bytes=0) == 0
+
+
+def test_bwd_rejects_preprocessing(lib):
+    from invariant_linear_attention_amd import gdn
+    pre = gdn.make_preproc(norm_qk=True)
+    d = _dims()
+    d.pre = ctypes.pointer(pre)
+    assert call_bwd(lib, d, ws_bytes=1 << 30) == 6
