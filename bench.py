@@ -19,7 +19,9 @@ Also reported on the same line:
                 the 64-sequence mixed batch, through the state pool with
                 snapshots, and with fused preprocessing, against the same fp32
                 roofline; the short convolution on the batch's q|k|v channels
-                against the HBM roofline;
+                against the HBM roofline; the backward (gdn_bwd_varlen) on the
+                benchmark batch against the fp32 roofline on its 18 flops per
+                state element and token;
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample;
   parity        the timed outputs re-checked against the oracle (sampled heads).
 
@@ -389,6 +391,41 @@ def main():
         del lc
         prefill_line("mixed_batch_64", synth.mixed_batch(1004), parity_heads=(0, 15))
 
+        # The backward (gdn_bwd_varlen) on the benchmark batch, dL/dout ~ N(0, 1) in
+        # bf16 and dL/dhT ~ N(0, 1), against the FP32-VALU roofline on its algorithmic
+        # work: 18 flops per state element and token (recompute p and the write: 5;
+        # the adjoint D += dO q^T, du = D k, D -= beta du k^T, D *= a: 7; dq = S^T dO,
+        # dk = D^T u + S^T w: 6).
+        gen = torch.Generator().manual_seed(1006)
+        dout_c = torch.randn(tuple(w.v.shape), generator=gen).to(torch.bfloat16)
+        dhT_c = torch.randn((w.n_seqs, 32, 128, 128), generator=gen)
+        dout_d, dhT_d = dout_c.to(dev), dhT_c.to(dev)
+        bdims = gdn.make_dims(d["q"], d["v"], w.n_seqs, T)
+        ws = torch.empty(gdn.gdn_bwd_workspace_size(bdims), dtype=torch.uint8, device=dev)
+        grads = gdn.gdn_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                                   workspace=ws, stream=stream)
+
+        def bwd(_i):
+            gdn.gdn_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                               workspace=ws, grads=grads, stream=stream)
+
+        per_b, _ = time_launches(bwd, args.steps, 3, stream)
+        msb = float(np.median(per_b))
+        bflops = 18.0 * 128 * 128 * 32 * T
+        s0 = synth.head_slice(w, 0)
+        rb = oracle.gdn_backward(s0.q, s0.k, s0.v, s0.g, s0.beta, s0.cu_seqlens, dout_c[:, 0:2].contiguous(),
+                                 h0=s0.h0, dhT=dhT_c[:, 0:2].contiguous())
+        got = {"dq": grads["dq"][:, 0:1], "dk": grads["dk"][:, 0:1], "dv": grads["dv"][:, 0:2],
+               "dbeta": grads["dbeta"][:, 0:2], "dg": grads["dg"][:, 0:2], "dh0": grads["dh0"][:, 0:2]}
+        workloads["backward_varlen_prefill"] = {
+            "tokens": T, "n_seqs": w.n_seqs, "ms_median": msb, "tokens_per_s": T / (msb / 1e3),
+            "launches": 6, "workspace_bytes": int(ws.numel()),
+            "roofline": {"bound": "alu", "achieved": bflops / (msb / 1e3) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": bflops / (msb / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                         "flops_per_launch": bflops},
+            "parity": {"kh0_grads": {k: rel(v.cpu().numpy(), rb[k]) for k, v in got.items()}}}
+        del dout_d, dhT_d, ws, grads
+
     # ------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu:
@@ -409,9 +446,13 @@ def main():
                "seconds": dt}
 
     # every line's parity re-check must pass as well
+    def grads_ok(gr):  # the backward's gates: 1e-4 normwise, dg 1e-3
+        return all(e <= (1e-3 if k == "dg" else 1e-4) for k, e in gr.items())
+
     def line_ok(par):
         return all((v.get("out", 0.0) <= 2e-3 and v.get("state", 0.0) <= 1e-4 and v.get("y_first256", 0.0) <= 2e-3)
-                   if isinstance(v, dict) else True for v in par.values())
+                   if isinstance(v, dict) and "dq" not in v else (grads_ok(v) if isinstance(v, dict) else True)
+                   for v in par.values())
     for rec in list((decode or {}).values()) + list((workloads or {}).values()):
         if "parity" in rec:
             par = rec["parity"]

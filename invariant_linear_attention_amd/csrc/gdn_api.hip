@@ -439,7 +439,7 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
     p.q = q; p.k = k; p.v = v; p.dout = dout; p.g = g; p.beta = beta; p.h0 = h0; p.dhT = dhT;
     p.cu_seqlens = cu_seqlens;
     p.grad_q = dq; p.grad_k = dk; p.grad_v = dv; p.grad_g = dg; p.grad_beta = dbeta; p.grad_h0 = dh0;
-    p.pbuf = reinterpret_cast<float *>(w + ws.p);
+    p.rbuf = reinterpret_cast<float *>(w + ws.p);
     p.dubuf = reinterpret_cast<float *>(w + ws.du);
     p.dkbuf = reinterpret_cast<float *>(w + ws.dk);
     p.dqbuf = reinterpret_cast<float *>(w + ws.dq);

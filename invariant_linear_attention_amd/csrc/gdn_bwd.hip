@@ -22,7 +22,7 @@
 // forward's layout (L lanes hold one state row, row dots finished by DPP, no
 // reduction across rows) in each of four passes over the tokens:
 //
-//   F0 forward  over S   (rows j, columns i): p_t, and hT
+//   F0 forward  over S   (rows j, columns i): r_t = v_t - a_t p_t, and hT
 //   R1 reverse  over D   (rows j, columns i): du_t, and dh0 = D_0
 //   R2 reverse  over D^T (rows i, columns j): (D_t^T u_t)_i             -> dk
 //   F3 forward  over S^T (rows i, columns j): (S_{t-1}^T w_t)_i, w_t = -a_t beta_t du_t,
@@ -51,10 +51,6 @@ constexpr int kBwdRows = kBwdWaves * (64 / kBwdLanes);  // rows per workgroup (3
 constexpr int kBwdThreads = kBwdWaves * 64;
 constexpr int kBwdTB = 16;     // tokens per staged block
 
-// Number of column vectors and row scalars each pass stages per token.
-constexpr int cols_of(int pass) { return pass == kF0 ? 1 : (pass == kR1 ? 2 : 3); }
-constexpr int rows_of(int pass) { return pass == kR2 ? 2 : 1; }
-
 template <int C>
 __device__ __forceinline__ float lane_dot(const float (&x)[C], const float (&y)[C]) {
     constexpr int K = C >= 16 ? 4 : (C >= 8 ? 2 : 1);  // independent chains
@@ -70,8 +66,8 @@ __device__ __forceinline__ float lane_dot(const float (&x)[C], const float (&y)[
 
 template <int NC>
 struct alignas(16) BwdLds {
-    float cv[3][kBwdTB][NC];     // column vectors of each staged token
-    float rs[2][kBwdTB][kBwdRows];  // row scalars of this tile
+    float cv[3][kBwdTB][NC];        // column vectors of each staged token (up to three)
+    float rs[2][kBwdTB][kBwdRows];  // row scalars of this tile (up to two)
     float a[kBwdTB], b[kBwdTB];  // exp(g), beta
 };
 
@@ -81,7 +77,6 @@ template <int PASS, int NC, class IO>
 __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_pass_kernel(BwdParams p) {
     constexpr int C = NC / kBwdLanes;
     constexpr bool REV = (PASS == kR1 || PASS == kR2);
-    constexpr int NCV = cols_of(PASS), NRS = rows_of(PASS);
     __shared__ BwdLds<NC> Ld;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -120,90 +115,150 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_pass_kernel(BwdParams p) 
 
     const int64_t len = te - tb;
     const int nblk = (int)((len + kBwdTB - 1) / kBwdTB);
-    for (int blk = 0; blk < nblk; ++blk) {
-        // Forward passes take block blk from the start, reverse passes from the end.
+    // Forward passes take block blk from the start, reverse passes from the end;
+    // slot ti of a block is token s0 + ti.
+    auto block_first = [&](int blk) -> int64_t {
         const int64_t t0 = REV ? (te - (int64_t)(blk + 1) * kBwdTB) : (tb + (int64_t)blk * kBwdTB);
-        const int64_t s0 = t0 < tb ? tb : t0;                     // first token of the block
-        const int64_t s1 = (t0 + kBwdTB > te) ? te : t0 + kBwdTB;  // one past the last
-        const int nt = (int)(s1 - s0);
+        return t0 < tb ? tb : t0;
+    };
+    auto block_len = [&](int blk) -> int {
+        const int64_t t0 = REV ? (te - (int64_t)(blk + 1) * kBwdTB) : (tb + (int64_t)blk * kBwdTB);
+        const int64_t s1 = (t0 + kBwdTB > te) ? te : t0 + kBwdTB;
+        return (int)(s1 - (t0 < tb ? tb : t0));
+    };
 
-        // ---- stage the block's tokens (slot ti = token s0 + ti)
-        for (int idx = tid; idx < nt * NC; idx += kBwdThreads) {
-            const int ti = idx / NC, c = idx % NC;
+    // Staging: a block's global reads go to registers, then to LDS.  (Issuing them
+    // one block ahead measured no faster: the other waves on the SIMD already
+    // cover their latency, and the registers held across a block cost occupancy.)
+    // Column items are four columns of one token; row items one row of one token.
+    constexpr int NC4 = NC / 4;
+    constexpr int CITEMS = (kBwdTB * NC4 + kBwdThreads - 1) / kBwdThreads;
+    constexpr int RITEMS = (kBwdTB * kBwdRows + kBwdThreads - 1) / kBwdThreads;
+    float4 cr[CITEMS][3];
+    float rr[RITEMS][2];
+    float sa = 0.f, sb = 0.f;
+    auto fetch = [&](int blk) {
+        const int64_t s0 = block_first(blk);
+        const int nt = block_len(blk);
+#pragma unroll
+        for (int it = 0; it < CITEMS; ++it) {
+            const int idx = tid + it * kBwdThreads;
+            if (idx >= nt * NC4) continue;
+            const int ti = idx / NC4, c = 4 * (idx % NC4);
             const int64_t t = s0 + ti;
-            const size_t qk = ((size_t)t * p.hk + kh) * p.dk + c;  // F0 / R1 columns (dk)
-            const size_t vv = ((size_t)t * p.hv + h) * p.dv + c;   // R2 / F3 columns (dv)
-            if constexpr (PASS == kF0) {
-                Ld.cv[0][ti][c] = IO::load1(p.k, qk);
-            } else if constexpr (PASS == kR1) {
-                Ld.cv[0][ti][c] = IO::load1(p.q, qk);
-                Ld.cv[1][ti][c] = IO::load1(p.k, qk);
-            } else {
-                const float a = decay_factor(p.g[(size_t)t * p.hv + h]);
-                const float b = p.beta[(size_t)t * p.hv + h];
-                const float u = b * (IO::load1(p.v, vv) - a * p.pbuf[vv]);
-                const float dvv = b * p.dubuf[vv];
-                const float dO = IO::load1(p.dout, vv);
-                if constexpr (PASS == kR2) {
-                    Ld.cv[0][ti][c] = dO;
-                    Ld.cv[1][ti][c] = u;
-                    Ld.cv[2][ti][c] = dvv;
+            if constexpr (PASS == kF0 || PASS == kR1) {
+                const size_t qk = ((size_t)t * p.hk + kh) * p.dk + c;
+                if constexpr (PASS == kF0) {
+                    cr[it][0] = IO::load4(p.k, qk);
                 } else {
-                    Ld.cv[0][ti][c] = -a * dvv;  // w_t = -a_t beta_t du_t
-                    Ld.cv[1][ti][c] = u;
-                    Ld.cv[2][ti][c] = dO;
+                    cr[it][0] = IO::load4(p.q, qk);
+                    cr[it][1] = IO::load4(p.k, qk);
+                }
+            } else {
+                const size_t vv = ((size_t)t * p.hv + h) * p.dv + c;
+                const float b = p.beta[(size_t)t * p.hv + h];
+                const float4 r = *reinterpret_cast<const float4 *>(p.rbuf + vv);
+                const float4 du = *reinterpret_cast<const float4 *>(p.dubuf + vv);
+                const float4 u = make_float4(b * r.x, b * r.y, b * r.z, b * r.w);
+                const float4 dvv = make_float4(b * du.x, b * du.y, b * du.z, b * du.w);
+                const float4 dO = IO::load4(p.dout, vv);
+                if constexpr (PASS == kR2) {
+                    cr[it][0] = dO;
+                    cr[it][1] = u;
+                    cr[it][2] = dvv;
+                } else {
+                    const float na = -decay_factor(p.g[(size_t)t * p.hv + h]);  // w_t = -a_t beta_t du_t
+                    cr[it][0] = make_float4(na * dvv.x, na * dvv.y, na * dvv.z, na * dvv.w);
+                    cr[it][1] = u;
+                    cr[it][2] = dO;
                 }
             }
         }
-        for (int idx = tid; idx < nt * kBwdRows; idx += kBwdThreads) {
+#pragma unroll
+        for (int it = 0; it < RITEMS; ++it) {
+            const int idx = tid + it * kBwdThreads;
+            if (idx >= nt * kBwdRows) continue;
             const int ti = idx / kBwdRows, r = idx % kBwdRows;
             const int64_t t = s0 + ti;
-            const int rr = tile * kBwdRows + r;
+            const int rw = tile * kBwdRows + r;
             if constexpr (PASS == kF0) {
-                Ld.rs[0][ti][r] = IO::load1(p.v, ((size_t)t * p.hv + h) * p.dv + rr);
+                rr[it][0] = IO::load1(p.v, ((size_t)t * p.hv + h) * p.dv + rw);
             } else if constexpr (PASS == kR1) {
-                Ld.rs[0][ti][r] = IO::load1(p.dout, ((size_t)t * p.hv + h) * p.dv + rr);
+                rr[it][0] = IO::load1(p.dout, ((size_t)t * p.hv + h) * p.dv + rw);
+            } else if constexpr (PASS == kR2) {
+                const size_t qk = ((size_t)t * p.hk + kh) * p.dk + rw;
+                rr[it][0] = IO::load1(p.q, qk);
+                rr[it][1] = IO::load1(p.k, qk);
             } else {
-                const size_t qk = ((size_t)t * p.hk + kh) * p.dk + rr;
-                Ld.rs[0][ti][r] = (PASS == kR2) ? IO::load1(p.q, qk) : IO::load1(p.k, qk);
-                if constexpr (PASS == kR2) Ld.rs[1][ti][r] = IO::load1(p.k, qk);
+                rr[it][0] = IO::load1(p.k, ((size_t)t * p.hk + kh) * p.dk + rw);
+                rr[it][1] = p.dkbuf[((size_t)t * p.hv + h) * p.dk + rw];  // R2's term of dk
             }
         }
         if (tid < nt) {
             const int64_t t = s0 + tid;
-            Ld.a[tid] = decay_factor(p.g[(size_t)t * p.hv + h]);
-            Ld.b[tid] = p.beta[(size_t)t * p.hv + h];
+            sa = decay_factor(p.g[(size_t)t * p.hv + h]);
+            sb = p.beta[(size_t)t * p.hv + h];
         }
+    };
+    auto commit = [&](int blk) {
+        const int nt = block_len(blk);
+        constexpr int NV = (PASS == kF0) ? 1 : (PASS == kR1 ? 2 : 3);
+        constexpr int NR = (PASS == kR2 || PASS == kF3) ? 2 : 1;
+#pragma unroll
+        for (int it = 0; it < CITEMS; ++it) {
+            const int idx = tid + it * kBwdThreads;
+            if (idx >= nt * NC4) continue;
+            const int ti = idx / NC4, c = 4 * (idx % NC4);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) *reinterpret_cast<float4 *>(&Ld.cv[v][ti][c]) = cr[it][v];
+        }
+#pragma unroll
+        for (int it = 0; it < RITEMS; ++it) {
+            const int idx = tid + it * kBwdThreads;
+            if (idx >= nt * kBwdRows) continue;
+            const int ti = idx / kBwdRows, r = idx % kBwdRows;
+#pragma unroll
+            for (int v = 0; v < NR; ++v) Ld.rs[v][ti][r] = rr[it][v];
+        }
+        if (tid < nt) {
+            Ld.a[tid] = sa;
+            Ld.b[tid] = sb;
+        }
+    };
+
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int64_t s0 = block_first(blk);
+        const int nt = block_len(blk);
+        fetch(blk);
+        commit(blk);
         __syncthreads();
 
         // ---- walk the block's tokens in this pass's direction
-        for (int step = 0; step < nt; ++step) {
-            const int ti = REV ? nt - 1 - step : step;
-            const int64_t t = s0 + ti;
-            const float a = Ld.a[ti], b = Ld.b[ti];
-            float v0[C], v1[C];
+        auto load_cols = [&](float (&dst)[C], int which, int ti) {
 #pragma unroll
             for (int j = 0; j < C / 4; ++j) {
-                const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[0][ti][col0 + 4 * j]);
-                v0[4 * j] = x.x; v0[4 * j + 1] = x.y; v0[4 * j + 2] = x.z; v0[4 * j + 3] = x.w;
+                const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[which][ti][col0 + 4 * j]);
+                dst[4 * j] = x.x; dst[4 * j + 1] = x.y; dst[4 * j + 2] = x.z; dst[4 * j + 3] = x.w;
             }
-            if constexpr (NCV >= 2) {
-#pragma unroll
-                for (int j = 0; j < C / 4; ++j) {
-                    const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[1][ti][col0 + 4 * j]);
-                    v1[4 * j] = x.x; v1[4 * j + 1] = x.y; v1[4 * j + 2] = x.z; v1[4 * j + 3] = x.w;
-                }
-            }
+        };
+        auto step = [&](int stp) {
+            const int ti = REV ? nt - 1 - stp : stp;
+            const int64_t t = s0 + ti;
+            const float a = Ld.a[ti], b = Ld.b[ti];
             const float r0 = Ld.rs[0][ti][lrow];
+            float v0[C], v1[C];
+            load_cols(v0, 0, ti);
             if constexpr (PASS == kF0) {
-                // p = S_{t-1} k;  u = beta (v - a p);  S = a S + u k^T
+                // p = S_{t-1} k;  r = v - a p;  S = a S + (beta r) k^T
                 const float pt = lane_sum<kBwdLanes>(lane_dot<C>(X, v0));
-                if (lam == 0) p.pbuf[((size_t)t * p.hv + h) * p.dv + row] = pt;
-                const float u = b * (r0 - a * pt);
+                const float rt = r0 - a * pt;
+                if (lam == 0) p.rbuf[((size_t)t * p.hv + h) * p.dv + row] = rt;
+                const float u = b * rt;
 #pragma unroll
                 for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(a, X[c], u * v0[c]);
             } else if constexpr (PASS == kR1) {
                 // D += dO q^T;  du = D k;  D = a (D - beta du k^T)
+                load_cols(v1, 1, ti);
 #pragma unroll
                 for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(r0, v0[c], X[c]);
                 const float du = lane_sum<kBwdLanes>(lane_dot<C>(X, v1));
@@ -214,11 +269,8 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_pass_kernel(BwdParams p) 
             } else if constexpr (PASS == kR2) {
                 // E = D^T:  E += q dO^T;  y = E u;  E = a (E - k dv^T)
                 float v2[C];
-#pragma unroll
-                for (int j = 0; j < C / 4; ++j) {
-                    const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[2][ti][col0 + 4 * j]);
-                    v2[4 * j] = x.x; v2[4 * j + 1] = x.y; v2[4 * j + 2] = x.z; v2[4 * j + 3] = x.w;
-                }
+                load_cols(v1, 1, ti);
+                load_cols(v2, 2, ti);
                 const float r1 = Ld.rs[1][ti][lrow];
 #pragma unroll
                 for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(r0, v0[c], X[c]);
@@ -229,21 +281,24 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_pass_kernel(BwdParams p) 
             } else {
                 // P = S^T:  y1 = P w (old state);  P = a P + k u^T;  y2 = P dO (new state)
                 float v2[C];
-#pragma unroll
-                for (int j = 0; j < C / 4; ++j) {
-                    const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[2][ti][col0 + 4 * j]);
-                    v2[4 * j] = x.x; v2[4 * j + 1] = x.y; v2[4 * j + 2] = x.z; v2[4 * j + 3] = x.w;
-                }
+                load_cols(v1, 1, ti);
+                load_cols(v2, 2, ti);
                 const float y1 = lane_sum<kBwdLanes>(lane_dot<C>(X, v0));
 #pragma unroll
                 for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(a, X[c], r0 * v1[c]);
                 const float y2 = lane_sum<kBwdLanes>(lane_dot<C>(X, v2));
                 if (lam == 0) {
                     const size_t o = ((size_t)t * p.hv + h) * p.dk + row;
-                    p.dkbuf[o] = p.dkbuf[o] + y1;  // R2 wrote the other term
+                    p.dkbuf[o] = Ld.rs[1][ti][lrow] + y1;
                     p.dqbuf[o] = y2;
                 }
             }
+        };
+        if (nt == kBwdTB) {
+#pragma unroll
+            for (int stp = 0; stp < kBwdTB; ++stp) step(stp);
+        } else {
+            for (int stp = 0; stp < nt; ++stp) step(stp);
         }
         __syncthreads();
     }
@@ -288,7 +343,6 @@ __global__ __launch_bounds__(256) void gdn_bwd_finish_kernel(BwdParams p) {
     }
     for (int m = 0; m < G; ++m) {
         const int h = kh * G + m;
-        const float a = decay_factor(p.g[(size_t)t * p.hv + h]);
         const float b = p.beta[(size_t)t * p.hv + h];
         float db = 0.f, dvv = 0.f, qdq = 0.f;
         for (int j = lane; j < p.dv; j += 64) {
@@ -296,7 +350,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_finish_kernel(BwdParams p) {
             const float du = p.dubuf[o], v = IO::load1(p.v, o);
             const float dv = b * du;
             p.grad_v[o] = dv;
-            db = __builtin_fmaf(du, v - a * p.pbuf[o], db);
+            db = __builtin_fmaf(du, p.rbuf[o], db);
             dvv = __builtin_fmaf(dv, v, dvv);
         }
         for (int i = lane; i < p.dk; i += 64)

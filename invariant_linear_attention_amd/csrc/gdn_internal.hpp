@@ -78,7 +78,7 @@ struct BwdParams {
     const int32_t *cu_seqlens;
     float *grad_q, *grad_k, *grad_v, *grad_g, *grad_beta, *grad_h0;  // outputs (grad_h0 may be null)
     // workspace
-    float *pbuf;   // [T][hv][dv]   p_t = S_{t-1} k_t
+    float *rbuf;   // [T][hv][dv]   r_t = v_t - a_t S_{t-1} k_t  (u_t = beta_t r_t)
     float *dubuf;  // [T][hv][dv]   du_t = dL/du_t
     float *dkbuf;  // [T][hv][dk]   dk of each value head
     float *dqbuf;  // [T][hv][dk]   dq of each value head
@@ -89,7 +89,7 @@ struct BwdParams {
     int32_t rank_by_length;
 };
 hipError_t launch_backward(const BwdParams &p, int io_dtype, hipStream_t s);
-// Workspace layout of the backward: byte offsets of pbuf, dubuf, dkbuf, dqbuf,
+// Workspace layout of the backward: byte offsets of rbuf, dubuf, dkbuf, dqbuf,
 // cbuf and hT, and the total.
 struct BwdWorkspace {
     uint64_t p, du, dk, dq, c, hT, total;
