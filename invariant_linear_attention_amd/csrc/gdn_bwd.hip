@@ -64,6 +64,17 @@ __device__ __forceinline__ float lane_dot(const float (&x)[C], const float (&y)[
     else return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
+// LDS position (in 4-float chunks) of lane lam's j-th chunk of a staged column vector.
+// The 8 lanes of a row read their j-th chunks together; with 16 columns per lane
+// (NC = 128) chunk j of lanes lam and lam + 4 would fall on the same banks, so those
+// lanes take their chunks in a rotated order.  Narrower rows do not conflict.
+template <int NC>
+__device__ __forceinline__ int bwd_chunk_slot(int lam, int j) {
+    constexpr int CH = NC / kBwdLanes / 4;  // chunks per lane
+    if constexpr (CH == 4) return lam * CH + ((j + (lam >> 2)) & 3);
+    else return lam * CH + j;
+}
+
 template <int NC>
 struct alignas(16) BwdLds {
     float cv[3][kBwdTB][NC];        // column vectors of each staged token (up to three)
@@ -91,6 +102,9 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_pass_kernel(BwdParams p) 
     const int lrow = wave * (64 / kBwdLanes) + grp;  // row within the tile
     const int row = tile * kBwdRows + lrow;
     const int col0 = lam * C;
+    int lchunk[C / 4];  // LDS float offsets of this lane's column chunks
+#pragma unroll
+    for (int j = 0; j < C / 4; ++j) lchunk[j] = 4 * bwd_chunk_slot<NC>(lam, j);
 
     int64_t tb = p.cu_seqlens[n], te = p.cu_seqlens[n + 1];
     tb = tb < 0 ? 0 : (tb > p.total_tokens ? p.total_tokens : tb);
@@ -208,9 +222,10 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_pass_kernel(BwdParams p) 
         for (int it = 0; it < CITEMS; ++it) {
             const int idx = tid + it * kBwdThreads;
             if (idx >= nt * NC4) continue;
-            const int ti = idx / NC4, c = 4 * (idx % NC4);
+            const int ch = idx % NC4, ti = idx / NC4;
+            const int slot = bwd_chunk_slot<NC>(ch / (C / 4), ch % (C / 4));
 #pragma unroll
-            for (int v = 0; v < NV; ++v) *reinterpret_cast<float4 *>(&Ld.cv[v][ti][c]) = cr[it][v];
+            for (int v = 0; v < NV; ++v) *reinterpret_cast<float4 *>(&Ld.cv[v][ti][4 * slot]) = cr[it][v];
         }
 #pragma unroll
         for (int it = 0; it < RITEMS; ++it) {
@@ -237,7 +252,7 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_pass_kernel(BwdParams p) 
         auto load_cols = [&](float (&dst)[C], int which, int ti) {
 #pragma unroll
             for (int j = 0; j < C / 4; ++j) {
-                const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[which][ti][col0 + 4 * j]);
+                const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[which][ti][lchunk[j]]);
                 dst[4 * j] = x.x; dst[4 * j + 1] = x.y; dst[4 * j + 2] = x.z; dst[4 * j + 3] = x.w;
             }
         };
