@@ -249,71 +249,114 @@ __global__ __launch_bounds__(kBwdThreads) void gdn_bwd_pass_kernel(BwdParams p) 
         __syncthreads();
 
         // ---- walk the block's tokens in this pass's direction
-        auto load_cols = [&](float (&dst)[C], int which, int ti) {
+        // A token's LDS values go to one of two register sets, so the next token's
+        // reads can be issued while this one computes.  Each row's results are kept
+        // for 8 tokens (lane lam holds the token of step 8m + lam) and stored together.
+        constexpr int NV = (PASS == kF0) ? 1 : (PASS == kR1 ? 2 : 3);
+        constexpr int NR = (PASS == kR2 || PASS == kF3) ? 2 : 1;
+        struct Tok {
+            float v[NV][C];
+            float r[NR];
+            float a, b;
+        };
+        auto slot_of = [&](int stp) { return REV ? nt - 1 - stp : stp; };
+        auto load_tok = [&](Tok &X_, int stp) {
+            const int ti = slot_of(stp);
 #pragma unroll
-            for (int j = 0; j < C / 4; ++j) {
-                const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[which][ti][lchunk[j]]);
-                dst[4 * j] = x.x; dst[4 * j + 1] = x.y; dst[4 * j + 2] = x.z; dst[4 * j + 3] = x.w;
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int j = 0; j < C / 4; ++j) {
+                    const float4 x = *reinterpret_cast<const float4 *>(&Ld.cv[v][ti][lchunk[j]]);
+                    X_.v[v][4 * j] = x.x; X_.v[v][4 * j + 1] = x.y; X_.v[v][4 * j + 2] = x.z; X_.v[v][4 * j + 3] = x.w;
+                }
+#pragma unroll
+            for (int v = 0; v < NR; ++v) X_.r[v] = Ld.rs[v][ti][lrow];
+            X_.a = Ld.a[ti];
+            X_.b = Ld.b[ti];
+        };
+        float ob0 = 0.f, ob1 = 0.f;  // kept results (F3 keeps two)
+        // row output of token slot ti: rbuf / dubuf (rows dv) or dkbuf / dqbuf (rows dk)
+        auto out_index = [&](int ti) -> size_t {
+            return ((size_t)(s0 + ti) * p.hv + h) * (size_t)((PASS == kF0 || PASS == kR1) ? p.dv : p.dk) + row;
+        };
+        auto flush = [&](int stp) {  // after step stp: store the kept results of steps (stp & ~7) .. stp
+            const int sl = (stp & ~7) + lam;
+            if (sl > stp) return;
+            const size_t o = out_index(slot_of(sl));
+            if constexpr (PASS == kF0) p.rbuf[o] = ob0;
+            else if constexpr (PASS == kR1) p.dubuf[o] = ob0;
+            else if constexpr (PASS == kR2) p.dkbuf[o] = ob0;
+            else {
+                p.dkbuf[o] = ob0;
+                p.dqbuf[o] = ob1;
             }
         };
-        auto step = [&](int stp) {
-            const int ti = REV ? nt - 1 - stp : stp;
-            const int64_t t = s0 + ti;
-            const float a = Ld.a[ti], b = Ld.b[ti];
-            const float r0 = Ld.rs[0][ti][lrow];
-            float v0[C], v1[C];
-            load_cols(v0, 0, ti);
+        auto compute = [&](const Tok &T_, int stp) {
+            const float a = T_.a, b = T_.b;
+            float y0 = 0.f, y1 = 0.f;
             if constexpr (PASS == kF0) {
                 // p = S_{t-1} k;  r = v - a p;  S = a S + (beta r) k^T
-                const float pt = lane_sum<kBwdLanes>(lane_dot<C>(X, v0));
-                const float rt = r0 - a * pt;
-                if (lam == 0) p.rbuf[((size_t)t * p.hv + h) * p.dv + row] = rt;
-                const float u = b * rt;
+                const float pt = lane_sum<kBwdLanes>(lane_dot<C>(X, T_.v[0]));
+                y0 = T_.r[0] - a * pt;
+                const float u = b * y0;
 #pragma unroll
-                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(a, X[c], u * v0[c]);
+                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(a, X[c], u * T_.v[0][c]);
             } else if constexpr (PASS == kR1) {
                 // D += dO q^T;  du = D k;  D = a (D - beta du k^T)
-                load_cols(v1, 1, ti);
 #pragma unroll
-                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(r0, v0[c], X[c]);
-                const float du = lane_sum<kBwdLanes>(lane_dot<C>(X, v1));
-                if (lam == 0) p.dubuf[((size_t)t * p.hv + h) * p.dv + row] = du;
-                const float bdu = b * du;
+                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(T_.r[0], T_.v[0][c], X[c]);
+                y0 = lane_sum<kBwdLanes>(lane_dot<C>(X, T_.v[1]));
+                const float bdu = b * y0;
 #pragma unroll
-                for (int c = 0; c < C; ++c) X[c] = a * __builtin_fmaf(-bdu, v1[c], X[c]);
+                for (int c = 0; c < C; ++c) X[c] = a * __builtin_fmaf(-bdu, T_.v[1][c], X[c]);
             } else if constexpr (PASS == kR2) {
                 // E = D^T:  E += q dO^T;  y = E u;  E = a (E - k dv^T)
-                float v2[C];
-                load_cols(v1, 1, ti);
-                load_cols(v2, 2, ti);
-                const float r1 = Ld.rs[1][ti][lrow];
 #pragma unroll
-                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(r0, v0[c], X[c]);
-                const float y = lane_sum<kBwdLanes>(lane_dot<C>(X, v1));
-                if (lam == 0) p.dkbuf[((size_t)t * p.hv + h) * p.dk + row] = y;
+                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(T_.r[0], T_.v[0][c], X[c]);
+                y0 = lane_sum<kBwdLanes>(lane_dot<C>(X, T_.v[1]));
 #pragma unroll
-                for (int c = 0; c < C; ++c) X[c] = a * __builtin_fmaf(-r1, v2[c], X[c]);
+                for (int c = 0; c < C; ++c) X[c] = a * __builtin_fmaf(-T_.r[1], T_.v[2][c], X[c]);
             } else {
                 // P = S^T:  y1 = P w (old state);  P = a P + k u^T;  y2 = P dO (new state)
-                float v2[C];
-                load_cols(v1, 1, ti);
-                load_cols(v2, 2, ti);
-                const float y1 = lane_sum<kBwdLanes>(lane_dot<C>(X, v0));
+                y0 = T_.r[1] + lane_sum<kBwdLanes>(lane_dot<C>(X, T_.v[0]));  // plus R2's term of dk
 #pragma unroll
-                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(a, X[c], r0 * v1[c]);
-                const float y2 = lane_sum<kBwdLanes>(lane_dot<C>(X, v2));
-                if (lam == 0) {
-                    const size_t o = ((size_t)t * p.hv + h) * p.dk + row;
-                    p.dkbuf[o] = Ld.rs[1][ti][lrow] + y1;
-                    p.dqbuf[o] = y2;
-                }
+                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(a, X[c], T_.r[0] * T_.v[1][c]);
+                y1 = lane_sum<kBwdLanes>(lane_dot<C>(X, T_.v[2]));
+            }
+            if (lam == (stp & 7)) {
+                ob0 = y0;
+                ob1 = y1;
             }
         };
-        if (nt == kBwdTB) {
+        if (nt == kBwdTB && (PASS == kF0 || PASS == kR1)) {
+            // F0 and R1 carry their dot on the recurrence's critical path, so the next
+            // token's reads go ahead of it.  (R2 and F3 would need more than 168
+            // registers for a second set and lose a wave per SIMD: measured slower.)
+            Tok A, B;
+            load_tok(A, 0);
 #pragma unroll
-            for (int stp = 0; stp < kBwdTB; ++stp) step(stp);
+            for (int stp = 0; stp < kBwdTB; stp += 2) {
+                load_tok(B, stp + 1);
+                compute(A, stp);
+                if (stp + 2 < kBwdTB) load_tok(A, stp + 2);
+                compute(B, stp + 1);
+                if ((stp + 1) % 8 == 7) flush(stp + 1);
+            }
+        } else if (nt == kBwdTB) {
+#pragma unroll
+            for (int stp = 0; stp < kBwdTB; ++stp) {
+                Tok A;
+                load_tok(A, stp);
+                compute(A, stp);
+                if ((stp & 7) == 7) flush(stp);
+            }
         } else {
-            for (int stp = 0; stp < nt; ++stp) step(stp);
+            for (int stp = 0; stp < nt; ++stp) {
+                Tok A;
+                load_tok(A, stp);
+                compute(A, stp);
+                if ((stp & 7) == 7 || stp == nt - 1) flush(stp);
+            }
         }
         __syncthreads();
     }
