@@ -119,7 +119,7 @@ COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 def pmc_pass(dev, stream):
     """One launch of each kernel (prefill, decode at B = 256, the short convolution
-    and its state update), preceded by a plain device copy of COPY_BYTES whose
+    and its state update, the backward's six), preceded by a plain device copy of COPY_BYTES whose
     FETCH_SIZE / WRITE_SIZE readings calibrate the counters' units."""
     import torch
 
@@ -146,7 +146,13 @@ def pmc_pass(dev, stream):
     pool_c = torch.zeros((w.n_seqs, C, K - 1), dtype=torch.bfloat16, device=dev)
     gdn.gdn_short_conv(xc, wc, d[6], pool_c, stream=stream)
     torch.cuda.synchronize()
-    print("pmc pass: copy %d bytes, prefill %d tokens, decode B=%d, conv %d channels" % (
+    del xc, pool_c
+    gen = torch.Generator().manual_seed(1006)  # the backward, as in its benchmark line
+    dout = torch.randn(tuple(w.v.shape), generator=gen).to(torch.bfloat16).to(dev)
+    dhT = torch.randn((w.n_seqs, 32, 128, 128), generator=gen).to(dev)
+    gdn.gdn_bwd_varlen(*d, dout, dhT, stream=stream)
+    torch.cuda.synchronize()
+    print("pmc pass: copy %d bytes, prefill %d tokens, decode B=%d, conv %d channels, backward" % (
         COPY_BYTES, w.total_tokens, B, C), flush=True)
 
 
