@@ -310,13 +310,59 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims,
                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dh0,
                           void *workspace, uint64_t workspace_bytes, void *stream);
 
+/*
+ * Chunked form with a replaying decode.  gdn_fwd_varlen and gdn_decode_step make
+ * decode match prefill by running token by token everywhere, as the page
+ * "Defending Against the Training-Inference Numeric Mismatch in RL (Especially
+ * Linear Attention)" (section 3.2) does; the other way is to keep a chunked
+ * prefill and have decode reproduce the chunk's arithmetic, which needs fixed
+ * chunk boundaries.
+ * Here chunks are the 16-token stretches at positions 16c .. 16c+15 of a
+ * sequence.  Within a chunk, with S0 its starting state, G_m = g_0 + .. + g_m,
+ * Gam_m = exp(G_m) and Gam_{m,r} = exp(G_m - G_r):
+ *
+ *   u_m = beta_m (v_m - Gam_m S0 k_m) - sum_{r<m} beta_m Gam_{m,r} (k_m . k_r) u_r
+ *   o_m = Gam_m S0 q_m + sum_{s<=m} Gam_{m,s} (q_m . k_s) u_s
+ *   chunk end:  S = Gam_15 S0 + sum_s Gam_{15,s} u_s k_s^T
+ *
+ * (the same rule as gdn_fwd_varlen, written from the chunk's start; results
+ * agree with it to rounding, not bitwise).  Each token's arithmetic depends only
+ * on S0 and its chunk's earlier tokens, so the state between calls is a
+ * gdn_chunk_state, and every split of a sequence into calls -- a decode step of one
+ * token included -- gives the same bits, as do batch-mates and batch order.
+ *
+ *   in   : the sequences' chunked states, or NULL for empty ones (zero state, no
+ *          open chunk).  A state with S = h0 and count = 0 starts from h0.
+ *   out  : where the new chunked states go (all five arrays).  in and out must not
+ *          overlap (call with two buffers and swap).
+ *   o    : [T][hv][dv] outputs, io dtype.
+ * dk must be 64 or 128 and dv a multiple of 32 (else GDN_ERR_UNSUPPORTED, as are
+ * dims->pre and plan fields).  Errors as gdn_fwd_varlen; a count outside 0..15 is
+ * clamped on the device.
+ */
+enum { GDN_CHUNK = 16 };
+
+typedef struct gdn_chunk_state {
+    float *S;        /* [N][hv][dv][dk] fp32: state at the start of the open chunk */
+    float *k;        /* [N][16][hk][dk] fp32: keys of the open chunk's tokens */
+    float *u;        /* [N][16][hv][dv] fp32: their write vectors u */
+    float *G;        /* [N][16][hv]     fp32: cumulative log decay within the chunk */
+    int32_t *count;  /* [N]             tokens in the open chunk, 0 .. 15 */
+} gdn_chunk_state;
+
+gdn_status gdn_fwd_chunked(const gdn_dims *dims,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const int32_t *cu_seqlens,
+                           const gdn_chunk_state *in, const gdn_chunk_state *out,
+                           void *o, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *gdn_status_string(gdn_status status);
 
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 202
+#define GDN_ABI_VERSION 203
 
 #ifdef __cplusplus
 }

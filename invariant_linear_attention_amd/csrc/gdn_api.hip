@@ -451,6 +451,60 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_fwd_chunked(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const int32_t *cu_seqlens, const gdn_chunk_state *in,
+                           const gdn_chunk_state *out, void *o, void *stream) {
+    using namespace gdn;
+    gdn_status st = check_common(dims);
+    if (st != GDN_OK) return st;
+    const gdn_dims &d = *dims;
+    if (d.pre || d.plan_lanes || d.plan_rows || d.plan_waves) return GDN_ERR_UNSUPPORTED;
+    if ((d.dk != 64 && d.dk != 128) || d.dv % 32 != 0) return GDN_ERR_UNSUPPORTED;
+    const int64_t T = d.total_tokens, N = d.n_seqs;
+    if (N == 0) return T == 0 ? GDN_OK : GDN_ERR_SHAPE;
+    if (!cu_seqlens || !out || !out->S || !out->k || !out->u || !out->G || !out->count) return GDN_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
+    // an incoming state with an open chunk needs its k, u and G
+    if (in && in->count && (!in->k || !in->u || !in->G)) return GDN_ERR_NULL;
+    if (N * d.hv * (int64_t)(d.dv / 32) > 0x7FFFFFFFll) return GDN_ERR_SHAPE;
+
+    const uint64_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
+    const uint64_t s_bytes = (uint64_t)N * d.hv * d.dv * d.dk * 4;
+    const uint64_t k_bytes = (uint64_t)N * GDN_CHUNK * d.hk * d.dk * 4;
+    const uint64_t u_bytes = (uint64_t)N * GDN_CHUNK * d.hv * d.dv * 4;
+    const uint64_t G_bytes = (uint64_t)N * GDN_CHUNK * d.hv * 4, c_bytes = (uint64_t)N * 4;
+    const gdn_chunk_state none{};
+    const gdn_chunk_state &i = in ? *in : none;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(g, 4) ||
+        !aligned(beta, 4) || !aligned(cu_seqlens, 4) || !aligned(out->S, 16) || !aligned(out->k, 16) ||
+        !aligned(out->u, 4) || !aligned(out->G, 4) || !aligned(out->count, 4) || !aligned(i.S, 16) ||
+        !aligned(i.k, 4) || !aligned(i.u, 4) || !aligned(i.G, 4) || !aligned(i.count, 4))
+        return GDN_ERR_ALIGN;
+    const uint64_t qk_n = (uint64_t)T * d.hk * d.dk, vo_n = (uint64_t)T * d.hv * d.dv;
+    const Range inputs[] = {range_of(q, qk_n * esz), range_of(k, qk_n * esz), range_of(v, vo_n * esz),
+                            range_of(g, (uint64_t)T * d.hv * 4), range_of(beta, (uint64_t)T * d.hv * 4),
+                            range_of(cu_seqlens, (uint64_t)(N + 1) * 4), range_of(i.S, i.S ? s_bytes : 0),
+                            range_of(i.k, i.k ? k_bytes : 0), range_of(i.u, i.u ? u_bytes : 0),
+                            range_of(i.G, i.G ? G_bytes : 0), range_of(i.count, i.count ? c_bytes : 0)};
+    const Range outputs[] = {range_of(o, vo_n * esz), range_of(out->S, s_bytes), range_of(out->k, k_bytes),
+                             range_of(out->u, u_bytes), range_of(out->G, G_bytes), range_of(out->count, c_bytes)};
+    for (size_t a = 0; a < sizeof(outputs) / sizeof(outputs[0]); ++a) {
+        for (const Range &r : inputs)
+            if (overlap(outputs[a], r)) return GDN_ERR_ALIAS;
+        for (size_t b = a + 1; b < sizeof(outputs) / sizeof(outputs[0]); ++b)
+            if (overlap(outputs[a], outputs[b])) return GDN_ERR_ALIAS;
+    }
+
+    ChunkedParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu_seqlens = cu_seqlens;
+    p.in_S = i.S; p.in_k = i.k; p.in_u = i.u; p.in_G = i.G; p.in_count = i.count;
+    p.out_S = out->S; p.out_k = out->k; p.out_u = out->u; p.out_G = out->G; p.out_count = out->count;
+    p.out = o;
+    p.total_tokens = T; p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dk = d.dk; p.dv = d.dv;
+    const hipError_t e = launch_chunked(p, d.io_dtype, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 const char *gdn_status_string(gdn_status status) {
     switch (status) {
         case GDN_OK: return "GDN_OK";

@@ -96,6 +96,24 @@ struct BwdWorkspace {
 };
 BwdWorkspace backward_workspace(int64_t T, int64_t N, int hv, int dk, int dv);
 
+// Kernel arguments of the chunked form with its replaying decode (gdn_fwd_chunked).
+// A chunked state is the state at the start of the open chunk plus that chunk's
+// keys, write vectors u and cumulative log decays, and its token count.
+constexpr int kChunkLen = 16;
+struct ChunkedParams {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const int32_t *cu_seqlens;
+    const float *in_S, *in_k, *in_u, *in_G;  // null in_S: zero state; null in_count: empty chunk
+    const int32_t *in_count;
+    float *out_S, *out_k, *out_u, *out_G;
+    int32_t *out_count;
+    void *out;
+    int64_t total_tokens;
+    int32_t n_seqs, hk, hv, dk, dv;
+};
+hipError_t launch_chunked(const ChunkedParams &p, int io_dtype, hipStream_t s);
+
 // A launch shape: `lanes` lanes hold one state row, each lane holds `rows` rows,
 // and a workgroup has `waves` waves; it owns waves * (64 / lanes) * rows
 // consecutive rows of one value head.

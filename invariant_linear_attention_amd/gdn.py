@@ -20,7 +20,9 @@ STATUS = {
     5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_HIP",
 }
 EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv", "gdn_query_plan",
-           "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_status_string", "gdn_abi_version")
+           "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_fwd_chunked", "gdn_status_string", "gdn_abi_version")
+
+GDN_CHUNK = 16
 
 
 GDN_PRE_QK_L2NORM, GDN_PRE_GATE_LOGITS = 1, 2
@@ -65,6 +67,12 @@ _lock = threading.Lock()
 _lib = None
 
 
+class GdnChunkState(ctypes.Structure):
+    """Mirror of ``gdn_chunk_state``."""
+    _fields_ = [("S", ctypes.c_void_p), ("k", ctypes.c_void_p), ("u", ctypes.c_void_p), ("G", ctypes.c_void_p),
+                ("count", ctypes.c_void_p)]
+
+
 def load_library(path: str = LIBRARY):
     """Load libgdn.so (once).  Raises if it is missing: build it first."""
     global _lib
@@ -88,6 +96,9 @@ def load_library(path: str = LIBRARY):
         lib.gdn_bwd_workspace_size.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(ctypes.c_uint64)]
         lib.gdn_bwd_varlen.restype = ctypes.c_int
         lib.gdn_bwd_varlen.argtypes = [ctypes.POINTER(GdnDims)] + [vp] * 16 + [ctypes.c_uint64, vp]
+        lib.gdn_fwd_chunked.restype = ctypes.c_int
+        lib.gdn_fwd_chunked.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp,
+                                        ctypes.POINTER(GdnChunkState), ctypes.POINTER(GdnChunkState), vp, vp]
         lib.gdn_query_plan.restype = ctypes.c_int
         lib.gdn_query_plan.argtypes = [ctypes.POINTER(GdnDims), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
         lib.gdn_status_string.restype = ctypes.c_char_p
@@ -246,6 +257,57 @@ def gdn_bwd_varlen(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=N
                               _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["dbeta"]), _ptr(grads.get("dh0")),
                               _ptr(workspace), int(workspace.numel()), _stream_handle(stream)))
     return grads
+
+
+def make_chunk_state(n_seqs: int, hk: int, hv: int, dk: int, dv: int, device, h0=None):
+    """A chunked state (see gdn_fwd_chunked): dict of S [N, hv, dv, dk], k [N, 16, hk, dk],
+    u [N, 16, hv, dv], G [N, 16, hv] (fp32) and count [N] (int32), with an empty open
+    chunk and S = h0 (or zeros)."""
+    import torch
+    f32 = dict(dtype=torch.float32, device=device)
+    S = torch.zeros((n_seqs, hv, dv, dk), **f32) if h0 is None else h0.to(device=device, dtype=torch.float32).clone()
+    return {"S": S.contiguous(), "k": torch.zeros((n_seqs, GDN_CHUNK, hk, dk), **f32),
+            "u": torch.zeros((n_seqs, GDN_CHUNK, hv, dv), **f32), "G": torch.zeros((n_seqs, GDN_CHUNK, hv), **f32),
+            "count": torch.zeros((n_seqs,), dtype=torch.int32, device=device)}
+
+
+def _chunk_struct(st):
+    if st is None:
+        return None
+    return GdnChunkState(_ptr(st["S"]), _ptr(st["k"]), _ptr(st["u"]), _ptr(st["G"]), _ptr(st["count"]))
+
+
+def gdn_fwd_chunked(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=None, stream=None):
+    """Chunked form with a replaying decode (see include/gdn.h).  ``state_in`` is a
+    chunked state dict (make_chunk_state) or None for empty states; ``state_out``
+    (allocated when None) receives the new states and must not overlap ``state_in``.
+    Returns (out [T, Hv, dv], state_out)."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    T, hk, dk = (int(x) for x in q.shape)
+    hv, dv = int(v.shape[1]), int(v.shape[2])
+    N = int(cu_seqlens.numel()) - 1
+    for st in (state_in, state_out):
+        if st is not None:
+            for name in ("S", "k", "u", "G"):
+                _need(st[name], "state." + name, torch.float32)
+            _need(st["count"], "state.count", torch.int32)
+    if state_out is None:
+        state_out = make_chunk_state(N, hk, hv, dk, dv, q.device)
+    if out is None:
+        out = torch.empty((T, hv, dv), dtype=q.dtype, device=q.device)
+    _need(out, "out", q.dtype)
+    dims = make_dims(q, v, N, T)
+    sin, sout = _chunk_struct(state_in), _chunk_struct(state_out)
+    _check(lib.gdn_fwd_chunked(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                               ctypes.byref(sin) if sin is not None else None, ctypes.byref(sout), _ptr(out),
+                               _stream_handle(stream)))
+    return out, state_out
 
 
 def gdn_fwd_varlen_pool(q, k, v, g, beta, cu_seqlens, state_pool, src_idx=None, dst_idx=None, pos0=None,

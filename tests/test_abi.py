@@ -28,8 +28,8 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
-                          "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_status_string",
-                          "gdn_abi_version"}
+                          "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_fwd_chunked",
+                          "gdn_status_string", "gdn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -441,3 +441,40 @@ def test_bwd_rejects_preprocessing(lib):
     d = _dims()
     d.pre = ctypes.pointer(pre)
     assert call_bwd(lib, d, ws_bytes=1 << 30) == 6
+
+
+# ------------------------------------------------------------------ chunked form
+
+CH = {name: BASE + (80 + i) * MB for i, name in enumerate(
+    ["q", "k", "v", "g", "b", "cu", "o", "iS", "ik", "iu", "iG", "ic", "oS", "ok", "ou", "oG", "oc"])}
+
+
+def call_chunked(lib, dims, with_in=True, **over):
+    from invariant_linear_attention_amd.gdn import GdnChunkState
+    a = dict(CH)
+    a.update(over)
+    sin = GdnChunkState(a["iS"], a["ik"], a["iu"], a["iG"], a["ic"])
+    sout = GdnChunkState(a["oS"], a["ok"], a["ou"], a["oG"], a["oc"])
+    return lib.gdn_fwd_chunked(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], a["v"], a["g"],
+                               a["b"], a["cu"], ctypes.byref(sin) if with_in else None, ctypes.byref(sout), a["o"],
+                               None)
+
+
+@pytest.mark.parametrize("case,over,code", [
+    (dict(dk=32), {}, 6), (dict(dk=16), {}, 6), (dict(dv=48), {}, 6), (dict(plan_rows=1), {}, 6),
+    (dict(hv=3), {}, 2), (dict(io_dtype=4), {}, 3), (dict(n_seqs=0, total_tokens=2), {}, 2),
+    ({}, dict(cu=None), 1), ({}, dict(oS=None), 1), ({}, dict(oc=None), 1), ({}, dict(q=None), 1),
+    ({}, dict(o=None), 1), ({}, dict(ik=None), 1),
+    ({}, dict(q=CH["q"] + 8), 4), ({}, dict(oS=CH["oS"] + 4), 4), ({}, dict(oc=CH["oc"] + 2), 4),
+    ({}, dict(oS=CH["iS"]), 5), ({}, dict(ou=CH["iu"] + 64), 5), ({}, dict(o=CH["v"]), 5),
+    ({}, dict(oG=CH["ou"]), 5), ({}, dict(oc=CH["q"]), 5),
+])
+def test_chunked_rejects(lib, case, over, code):
+    assert call_chunked(lib, _dims(**case), **over) == code
+
+
+def test_chunked_null_in_and_noop(lib):
+    assert call_chunked(lib, None) == 1
+    assert call_chunked(lib, _dims(n_seqs=0, total_tokens=0)) == 0
+    # no incoming state is allowed (empty states); a missing out array is not
+    assert call_chunked(lib, _dims(n_seqs=0, total_tokens=0), with_in=False) == 0

@@ -1,0 +1,149 @@
+"""The chunked form with a replaying decode (gdn_fwd_chunked).
+
+Parity: outputs against the fp64 recurrence oracle (the chunked form is the same
+rule written from each chunk's start), and the final state, rebuilt on the host in
+fp64 from the chunked state (S at the open chunk's start plus its u, k and G),
+against the oracle's hT, under the same gates as the recurrent path.
+Bitwise: any split of a sequence into calls, one-token decode steps included,
+and any batch give the same outputs and chunked states.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import OUT_TOL, STATE_TOL, bit_equal, say, seq_errors, state_errors, to_dev
+from invariant_linear_attention_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+CK = 16
+
+
+def final_state(st):
+    """fp64 state after the open chunk's tokens: Gam_{c-1} S0 + sum_s Gam_{c-1,s} u_s k_s^T."""
+    S0 = st["S"].double().cpu().numpy()
+    K = st["k"].double().cpu().numpy()
+    U = st["u"].double().cpu().numpy()
+    G = st["G"].double().cpu().numpy()
+    cnt = st["count"].cpu().numpy()
+    N, hv = S0.shape[0], S0.shape[1]
+    hk = K.shape[2]
+    out = S0.copy()
+    for n in range(N):
+        c = int(cnt[n])
+        if c == 0:
+            continue
+        for h in range(hv):
+            kh = h // (hv // hk)
+            Gl = G[n, c - 1, h]
+            acc = np.exp(Gl) * S0[n, h]
+            for s in range(c):
+                acc += np.exp(Gl - G[n, s, h]) * np.outer(U[n, s, h], K[n, s, kh])
+            out[n, h] = acc
+    return out
+
+
+def run(gdn, w, st_in=None, d=None):
+    d = d if d is not None else to_dev(w)
+    out, st = gdn.gdn_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], st_in)
+    torch.cuda.synchronize()
+    return out, st
+
+
+def start_state(gdn, w):
+    return gdn.make_chunk_state(w.n_seqs, w.q.shape[1], w.v.shape[1], w.q.shape[2], w.v.shape[2], DEV,
+                                h0=w.h0)
+
+
+def states_equal(a, b):
+    """Same count and S, and the same k, u and G in the open chunk's slots."""
+    if not torch.equal(a["count"], b["count"]) or not bit_equal(a["S"], b["S"]):
+        return False
+    for n, c in enumerate(a["count"].cpu().tolist()):
+        for key in ("k", "u", "G"):
+            if not bit_equal(a[key][n, :c], b[key][n, :c]):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("dk,dv,io", [(128, 128, torch.bfloat16), (64, 64, torch.float32), (128, 32, torch.bfloat16)])
+@pytest.mark.parametrize("h0", [0.0, 0.1])
+def test_parity(gpu, dk, dv, io, h0):
+    from oracle import oracle
+    lengths = [37, 0, 1, 16, 15, 17, 100, 33]
+    w = synth.make_workload(500 + dk + dv, lengths, hk=2, hv=4, dk=dk, dv=dv, io_dtype=io, h0_std=h0)
+    out, st = run(gpu, w, start_state(gpu, w) if h0 > 0 else None)
+    ro, rh = oracle.gdn_forward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, w.h0)
+    errs = seq_errors(out.float().cpu().numpy(), ro, w.cu_seqlens.tolist())
+    serr = state_errors(final_state(st), rh)
+    say("chunked dk=%d dv=%d %s h0=%.1f: out %.2e state %.2e" % (dk, dv, io, h0, max(errs), max(serr)))
+    assert max(errs) <= OUT_TOL[io] and max(serr) <= STATE_TOL
+    assert st["count"].cpu().tolist() == [n % CK for n in lengths]
+
+
+def test_parity_benchmark_batch(gpu):
+    """The benchmark batch, oracle on two key heads."""
+    from oracle import oracle
+    w = synth.varlen_prefill(1001)
+    out, st = run(gpu, w, start_state(gpu, w))
+    fs = final_state(st)
+    for kh in (0, 9):
+        s = synth.head_slice(w, kh)
+        ro, rh = oracle.gdn_forward(s.q, s.k, s.v, s.g, s.beta, s.cu_seqlens, s.h0)
+        vs = slice(2 * kh, 2 * kh + 2)
+        e = max(seq_errors(out[:, vs].float().cpu().numpy(), ro, w.cu_seqlens.tolist()))
+        es = max(state_errors(fs[:, vs], rh))
+        say("chunked benchmark batch kh%d: out %.2e state %.2e" % (kh, e, es))
+        assert e <= OUT_TOL[torch.bfloat16] and es <= STATE_TOL
+
+
+def test_split_calls_and_decode_replay(gpu):
+    """One call over the whole sequences == the same tokens in several calls
+    (cuts inside and at chunk boundaries, one-token decode steps), bit for bit."""
+    lengths = [70, 23, 48]
+    w = synth.make_workload(601, lengths, hk=2, hv=4, dk=128, dv=64, h0_std=0.1)
+    st0 = start_state(gpu, w)
+    ref_out, ref_st = run(gpu, w, st0)
+    cuts = [0, 1, 2, 5, 16, 17, 31, 32, 33, 40, 47, 48, 61, 70]
+    cu = w.cu_seqlens.tolist()
+    st = st0
+    outs = {n: [] for n in range(len(lengths))}
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        # every sequence advances by its share of [a, b) (clipped to its length)
+        segs = [(min(a, L), min(b, L)) for L in lengths]
+        q, k, v, g, beta, cs = [], [], [], [], [], [0]
+        for n, (x, y) in enumerate(segs):
+            sl = slice(cu[n] + x, cu[n] + y)
+            q.append(w.q[sl]); k.append(w.k[sl]); v.append(w.v[sl]); g.append(w.g[sl]); beta.append(w.beta[sl])
+            cs.append(cs[-1] + (y - x))
+        part = synth.Workload(torch.cat(q), torch.cat(k), torch.cat(v), torch.cat(g), torch.cat(beta),
+                              torch.tensor(cs, dtype=torch.int32), None)
+        o, st = run(gpu, part, st)
+        for n in range(len(lengths)):
+            outs[n].append(o[cs[n]:cs[n + 1]])
+    for n in range(len(lengths)):
+        assert bit_equal(torch.cat(outs[n]), ref_out[cu[n]:cu[n + 1]]), n
+    assert states_equal(st, ref_st)
+    say("chunked: %d calls (decode steps included) == one call, bitwise" % (len(cuts) - 1))
+
+
+def test_alone_vs_in_batch(gpu):
+    w = synth.make_workload(611, [50, 3, 130, 0, 17], hk=2, hv=4, dk=128, dv=128, h0_std=0.1)
+    ref_out, ref_st = run(gpu, w, start_state(gpu, w))
+    cu = w.cu_seqlens.tolist()
+    for n in range(w.n_seqs):
+        s = synth.select(w, [n])
+        o, st = run(gpu, s, start_state(gpu, s))
+        assert bit_equal(o, ref_out[cu[n]:cu[n + 1]]), n
+        assert bit_equal(st["S"][0], ref_st["S"][n]) and int(st["count"][0]) == int(ref_st["count"][n])
+        c = int(st["count"][0])
+        for key in ("k", "u", "G"):
+            assert bit_equal(st[key][0, :c], ref_st[key][n, :c]), (n, key)
+
+
+def test_empty_call_keeps_state(gpu):
+    w = synth.make_workload(621, [20, 5], hk=1, hv=2, dk=64, dv=64, h0_std=0.1)
+    _, st = run(gpu, w, start_state(gpu, w))
+    e = synth.Workload(w.q[:0], w.k[:0], w.v[:0], w.g[:0], w.beta[:0], torch.tensor([0, 0, 0], dtype=torch.int32), None)
+    _, st2 = run(gpu, e, st)
+    assert states_equal(st, st2)
