@@ -65,15 +65,6 @@ __device__ __forceinline__ float chunk_lane_dot(const float (&x)[C], const float
     else return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-// dot of two LDS rows of length DK, one thread, ascending index
-template <int DK>
-__device__ __forceinline__ float serial_dot(const float *a, const float *b) {
-    float s = a[0] * b[0];
-#pragma unroll 8
-    for (int i = 1; i < DK; ++i) s = __builtin_fmaf(a[i], b[i], s);
-    return s;
-}
-
 // One workgroup = (sequence n, value head h, tile of 32 state rows).
 template <int DK, class IO>
 __global__ __launch_bounds__(kChThreads) void gdn_chunked_kernel(ChunkedParams p) {
@@ -142,21 +133,34 @@ __global__ __launch_bounds__(kChThreads) void gdn_chunked_kernel(ChunkedParams p
             const int m = ms + idx / kChRows, r = idx % kChRows;
             Ld.v[m][r] = IO::load1(p.v, ((size_t)(t_of_slot0 + m) * p.hv + h) * p.dv + tile * kChRows + r);
         }
-        if (tid == 0) {  // cumulative log decay, slot order
+        if (wave == 0) {  // cumulative log decay, added in slot order (lane j holds g of slot ms + j)
+            const float gj = lane < take ? p.g[(size_t)(t_of_slot0 + ms + lane) * p.hv + h] : 0.f;
             float acc = ms > 0 ? Ld.G[ms - 1] : 0.f;
-            for (int m = ms; m < me; ++m) {
-                acc = acc + p.g[(size_t)(t_of_slot0 + m) * p.hv + h];
-                Ld.G[m] = acc;
+            for (int j = 0; j < take; ++j) {
+                acc = acc + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gj), j));
+                if (lane == j) Ld.G[ms + j] = acc;
             }
         }
         if (tid < take) Ld.beta[ms + tid] = p.beta[(size_t)(t_of_slot0 + ms + tid) * p.hv + h];
         __syncthreads();
 
-        // ---- coefficient tables of the new slots (one thread per entry)
-        for (int e = tid; e < take * kCk; e += kChThreads) {
+        // ---- coefficient tables of the new slots: each entry's dot is spread over the
+        // 8 lanes of a group (C columns each, then the lane tree), 32 groups per
+        // workgroup; entry e = (m, r) of the (take x 16) table.
+        for (int e0 = 0; e0 < take * kCk; e0 += kChThreads / kChLanes) {
+            const int e = e0 + tid / kChLanes;
             const int m = ms + e / kCk, r = e % kCk;
-            if (r < m) Ld.ckk[m][r] = Ld.beta[m] * decay_factor(Ld.G[m] - Ld.G[r]) * serial_dot<DK>(Ld.k[m], Ld.k[r]);
-            if (r <= m) Ld.cqk[m][r] = decay_factor(Ld.G[m] - Ld.G[r]) * serial_dot<DK>(Ld.q[m], Ld.k[r]);
+            const bool live = e < take * kCk && r <= m;
+            float kv[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) kv[c] = Ld.k[live ? r : 0][col0 + c];
+            const float dkk = lane_sum<kChLanes>(chunk_lane_dot<C>(kv, &Ld.k[live ? m : 0][col0]));
+            const float dqk = lane_sum<kChLanes>(chunk_lane_dot<C>(kv, &Ld.q[live ? m : 0][col0]));
+            if (live && lam == 0) {
+                const float gm = decay_factor(Ld.G[m] - Ld.G[r]);
+                if (r < m) Ld.ckk[m][r] = Ld.beta[m] * gm * dkk;
+                Ld.cqk[m][r] = gm * dqk;
+            }
         }
         if (tid < take) Ld.gam[ms + tid] = decay_factor(Ld.G[ms + tid]);
         if (me == kCk && tid < kCk) Ld.cst[tid] = decay_factor(Ld.G[kCk - 1] - Ld.G[tid]);
