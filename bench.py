@@ -21,7 +21,8 @@ Also reported on the same line:
                 roofline; the short convolution on the batch's q|k|v channels
                 against the HBM roofline; the backward (gdn_bwd_varlen) on the
                 benchmark batch against the fp32 roofline on its 18 flops per
-                state element and token;
+                state element and token; the chunked form with its replaying
+                decode (gdn_fwd_chunked) on the same batch and at B = 256;
   cpu_baseline  the fp64 oracle on the host cores, on a bounded sample;
   parity        the timed outputs re-checked against the oracle (sampled heads).
 
@@ -431,6 +432,43 @@ def main():
                          "flops_per_launch": bflops},
             "parity": {"kh0_grads": {k: rel(v.cpu().numpy(), rb[k]) for k, v in got.items()}}}
         del dout_d, dhT_d, ws, grads
+
+        # The chunked form with a replaying decode (gdn_fwd_chunked): the benchmark
+        # batch as one prefill from h0, and one decode step at B = 256 through the
+        # chunked state; the same 7 dk dv flops per token as the recurrent lines.
+        st_in = gdn.make_chunk_state(w.n_seqs, 16, 32, 128, 128, dev, h0=d["h0"])
+        st_out = gdn.make_chunk_state(w.n_seqs, 16, 32, 128, 128, dev)
+        och = torch.empty((T, 32, 128), dtype=torch.bfloat16, device=dev)
+
+        def chunked(_i):
+            gdn.gdn_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], st_in, st_out, out=och,
+                                stream=stream)
+
+        per_ch, _ = time_launches(chunked, args.steps, 3, stream)
+        msch = float(np.median(per_ch))
+        Bc = 256
+        dwc = synth.make_workload(2000 + Bc, [1] * Bc)
+        dcd = [t.to(dev) for t in (dwc.q, dwc.k, dwc.v, dwc.g, dwc.beta, dwc.cu_seqlens)]
+        sts = [gdn.make_chunk_state(Bc, 16, 32, 128, 128, dev) for _ in range(2)]
+        for s_ in sts:
+            s_["S"].normal_(0.0, 0.1)
+            s_["count"].fill_(7)
+        ocd = torch.empty((Bc, 32, 128), dtype=torch.bfloat16, device=dev)
+
+        def chunked_dec(_i):
+            gdn.gdn_fwd_chunked(*dcd, sts[0], sts[1], out=ocd, stream=stream)
+
+        per_cd2, _ = time_launches(chunked_dec, args.steps, 3, stream)
+        chunked(0)
+        torch.cuda.synchronize()
+        s0 = synth.head_slice(w, 0)
+        ro, _ = oracle.gdn_forward(s0.q, s0.k, s0.v, s0.g, s0.beta, s0.cu_seqlens, s0.h0)
+        workloads["chunked_prefill_replay"] = {
+            "tokens": T, "n_seqs": w.n_seqs, "chunk": 16, "ms_median": msch, "tokens_per_s": T / (msch / 1e3),
+            "roofline_frac": flops / (msch / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+            "decode_B256_latency_us_median": float(np.median(per_cd2)) * 1e3,
+            "parity": {"kh0": {"out": rel(och[:, 0:2].float().cpu().numpy(), ro)}}}
+        del st_in, st_out, och, sts, ocd
 
     # ------------------------------------------------------- CPU baseline
     cpu = None
