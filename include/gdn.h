@@ -314,9 +314,12 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims,
  * Chunked form with a replaying decode.  gdn_fwd_varlen and gdn_decode_step make
  * decode match prefill by running token by token everywhere, as the page
  * "Defending Against the Training-Inference Numeric Mismatch in RL (Especially
- * Linear Attention)" (section 3.2) does; the other way is to keep a chunked
- * prefill and have decode reproduce the chunk's arithmetic, which needs fixed
- * chunk boundaries.
+ * Linear Attention)" (section 3.2) does.  The other way, in the summary of
+ * "Finish RL Training Faster: Bitwise-Consistent, High-Performance, Agent-Driven"
+ * (section "Consistency has several layers"), keeps a chunked prefill and has
+ * decode replay its computation order; that needs chunk boundaries that do not
+ * move, since a recurrent state carries where it was cut (the bitwise-parity
+ * post on linear attention, "Why linear attention is the next wall").
  * Here chunks are the 16-token stretches at positions 16c .. 16c+15 of a
  * sequence.  Within a chunk, with S0 its starting state, G_m = g_0 + .. + g_m,
  * Gam_m = exp(G_m) and Gam_{m,r} = exp(G_m - G_r):

@@ -3,9 +3,12 @@
 //
 // The page "Defending Against the Training-Inference Numeric Mismatch in RL
 // (Especially Linear Attention)" (section 3.2) makes prefill and decode agree by
-// running the recurrence token by token everywhere.  The other way it discusses is
-// to keep a chunked prefill and have decode reproduce the chunk's arithmetic, which
-// needs fixed chunk boundaries.  This file is that design.
+// running the recurrence token by token everywhere.  The summary of "Finish RL
+// Training Faster: Bitwise-Consistent, High-Performance, Agent-Driven" (section
+// "Consistency has several layers") describes the other way: a chunked prefill
+// whose decode replays its computation order.  That needs chunk boundaries that do
+// not move with the serving split (the bitwise-parity post on linear attention,
+// "Why linear attention is the next wall").  This file is that design.
 //
 // Chunks are the 16-token stretches of a sequence at positions 16c .. 16c + 15.
 // Within a chunk, with S0 the state at its start, G_m = g_0 + ... + g_m (cumulative
