@@ -340,8 +340,9 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims,
  *          overlap (call with two buffers and swap).
  *   o    : [T][hv][dv] outputs, io dtype.
  * dk must be 64 or 128 and dv a multiple of 32 (else GDN_ERR_UNSUPPORTED, as are
- * dims->pre and plan fields).  Errors as gdn_fwd_varlen; a count outside 0..15 is
- * clamped on the device.
+ * dims->pre and plan fields).  Errors as gdn_fwd_varlen (S and k of both states
+ * 16-byte aligned; u, G, count 4-byte); a count outside 0..15 is clamped on the
+ * device.
  */
 enum { GDN_CHUNK = 16 };
 

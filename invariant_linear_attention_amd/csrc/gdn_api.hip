@@ -478,7 +478,7 @@ gdn_status gdn_fwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(g, 4) ||
         !aligned(beta, 4) || !aligned(cu_seqlens, 4) || !aligned(out->S, 16) || !aligned(out->k, 16) ||
         !aligned(out->u, 4) || !aligned(out->G, 4) || !aligned(out->count, 4) || !aligned(i.S, 16) ||
-        !aligned(i.k, 4) || !aligned(i.u, 4) || !aligned(i.G, 4) || !aligned(i.count, 4))
+        !aligned(i.k, 16) || !aligned(i.u, 4) || !aligned(i.G, 4) || !aligned(i.count, 4))
         return GDN_ERR_ALIGN;
     const uint64_t qk_n = (uint64_t)T * d.hk * d.dk, vo_n = (uint64_t)T * d.hv * d.dv;
     const Range inputs[] = {range_of(q, qk_n * esz), range_of(k, qk_n * esz), range_of(v, vo_n * esz),

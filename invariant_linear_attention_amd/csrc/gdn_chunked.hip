@@ -55,8 +55,28 @@ struct alignas(16) ChunkLds {
     float beta[kCk];
 };
 
+// LDS position (in 4-float chunks) of lane lam's j-th 4-column chunk of a key or
+// query row.  With 16 columns per lane (dk = 128) the j-th chunks of lanes lam and
+// lam + 4 would share banks, so those lanes keep their chunks in a rotated order.
+template <int DK>
+__device__ __forceinline__ int ch_slot(int lam, int j) {
+    constexpr int CH = DK / kChLanes / 4;
+    if constexpr (CH == 4) return lam * CH + ((j + (lam >> 2)) & 3);
+    else return lam * CH + j;
+}
+
+// This lane's C columns of an LDS key/query row (chunk offsets lch).
 template <int C>
-__device__ __forceinline__ float chunk_lane_dot(const float (&x)[C], const float *y) {
+__device__ __forceinline__ void load_cols(float (&dst)[C], const float *row, const int (&lch)[C / 4]) {
+#pragma unroll
+    for (int j = 0; j < C / 4; ++j) {
+        const float4 x = *reinterpret_cast<const float4 *>(row + lch[j]);
+        dst[4 * j] = x.x; dst[4 * j + 1] = x.y; dst[4 * j + 2] = x.z; dst[4 * j + 3] = x.w;
+    }
+}
+
+template <int C>
+__device__ __forceinline__ float chunk_lane_dot(const float (&x)[C], const float (&y)[C]) {
     constexpr int K = C >= 16 ? 4 : (C >= 8 ? 2 : 1);
     float acc[K];
 #pragma unroll
@@ -85,6 +105,11 @@ __global__ __launch_bounds__(kChThreads) void gdn_chunked_kernel(ChunkedParams p
     const int lrow = wave * (64 / kChLanes) + grp;
     const int row = tile * kChRows + lrow;
     const int col0 = lam * C;
+    int lch[C / 4];  // LDS float offsets of this lane's column chunks in a key/query row
+#pragma unroll
+    for (int j = 0; j < C / 4; ++j) lch[j] = 4 * ch_slot<DK>(lam, j);
+    // where 4-column chunk c4 of a row is kept (the inverse view of lch, for staging)
+    auto stage_off = [](int c4) { return 4 * ch_slot<DK>((4 * c4) / C, ((4 * c4) % C) / 4); };
 
     int64_t tb = p.cu_seqlens[n], te = p.cu_seqlens[n + 1];
     tb = tb < 0 ? 0 : (tb > p.total_tokens ? p.total_tokens : tb);
@@ -111,9 +136,10 @@ __global__ __launch_bounds__(kChThreads) void gdn_chunked_kernel(ChunkedParams p
         ureg[m] = 0.f;
         if (m < m0) ureg[m] = p.in_u[(((size_t)n * kCk + m) * p.hv + h) * p.dv + row];
     }
-    for (int idx = tid; idx < m0 * DK; idx += kChThreads) {
-        const int m = idx / DK, i = idx % DK;
-        Ld.k[m][i] = p.in_k[(((size_t)n * kCk + m) * p.hk + kh) * DK + i];
+    for (int idx = tid; idx < m0 * (DK / 4); idx += kChThreads) {
+        const int m = idx / (DK / 4), c4 = idx % (DK / 4);
+        *reinterpret_cast<float4 *>(&Ld.k[m][stage_off(c4)]) =
+            *reinterpret_cast<const float4 *>(p.in_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + 4 * c4);
     }
     if (tid < m0) Ld.G[tid] = p.in_G[((size_t)n * kCk + tid) * p.hv + h];
     __syncthreads();
@@ -126,11 +152,11 @@ __global__ __launch_bounds__(kChThreads) void gdn_chunked_kernel(ChunkedParams p
         const int64_t t_of_slot0 = tb + done - ms;  // token index of slot 0
 
         // ---- stage the new slots
-        for (int idx = tid; idx < take * DK; idx += kChThreads) {
-            const int m = ms + idx / DK, i = idx % DK;
-            const size_t qk = ((size_t)(t_of_slot0 + m) * p.hk + kh) * DK + i;
-            Ld.k[m][i] = IO::load1(p.k, qk);
-            Ld.q[m][i] = IO::load1(p.q, qk);
+        for (int idx = tid; idx < take * (DK / 4); idx += kChThreads) {
+            const int m = ms + idx / (DK / 4), c4 = idx % (DK / 4);
+            const size_t qk = ((size_t)(t_of_slot0 + m) * p.hk + kh) * DK + 4 * c4;
+            *reinterpret_cast<float4 *>(&Ld.k[m][stage_off(c4)]) = IO::load4(p.k, qk);
+            *reinterpret_cast<float4 *>(&Ld.q[m][stage_off(c4)]) = IO::load4(p.q, qk);
         }
         for (int idx = tid; idx < take * kChRows; idx += kChThreads) {
             const int m = ms + idx / kChRows, r = idx % kChRows;
@@ -154,11 +180,12 @@ __global__ __launch_bounds__(kChThreads) void gdn_chunked_kernel(ChunkedParams p
             const int e = e0 + tid / kChLanes;
             const int m = ms + e / kCk, r = e % kCk;
             const bool live = e < take * kCk && r <= m;
-            float kv[C];
-#pragma unroll
-            for (int c = 0; c < C; ++c) kv[c] = Ld.k[live ? r : 0][col0 + c];
-            const float dkk = lane_sum<kChLanes>(chunk_lane_dot<C>(kv, &Ld.k[live ? m : 0][col0]));
-            const float dqk = lane_sum<kChLanes>(chunk_lane_dot<C>(kv, &Ld.q[live ? m : 0][col0]));
+            float kv[C], km[C], qm[C];
+            load_cols<C>(kv, Ld.k[live ? r : 0], lch);
+            load_cols<C>(km, Ld.k[live ? m : 0], lch);
+            load_cols<C>(qm, Ld.q[live ? m : 0], lch);
+            const float dkk = lane_sum<kChLanes>(chunk_lane_dot<C>(kv, km));
+            const float dqk = lane_sum<kChLanes>(chunk_lane_dot<C>(kv, qm));
             if (live && lam == 0) {
                 const float gm = decay_factor(Ld.G[m] - Ld.G[r]);
                 if (r < m) Ld.ckk[m][r] = Ld.beta[m] * gm * dkk;
@@ -173,8 +200,11 @@ __global__ __launch_bounds__(kChThreads) void gdn_chunked_kernel(ChunkedParams p
 #pragma unroll
         for (int m = 0; m < kCk; ++m) {
             if (m < ms || m >= me) continue;
-            const float w = lane_sum<kChLanes>(chunk_lane_dot<C>(X, &Ld.k[m][col0]));
-            const float z = lane_sum<kChLanes>(chunk_lane_dot<C>(X, &Ld.q[m][col0]));
+            float km[C], qm[C];
+            load_cols<C>(km, Ld.k[m], lch);
+            load_cols<C>(qm, Ld.q[m], lch);
+            const float w = lane_sum<kChLanes>(chunk_lane_dot<C>(X, km));
+            const float z = lane_sum<kChLanes>(chunk_lane_dot<C>(X, qm));
             float u = Ld.beta[m] * (Ld.v[m][lrow] - Ld.gam[m] * w);
 #pragma unroll
             for (int r = 0; r < m; ++r) u = __builtin_fmaf(-Ld.ckk[m][r], ureg[r], u);
@@ -193,8 +223,10 @@ __global__ __launch_bounds__(kChThreads) void gdn_chunked_kernel(ChunkedParams p
 #pragma unroll
             for (int s = 0; s < kCk; ++s) {
                 const float cs = Ld.cst[s] * ureg[s];
+                float ks[C];
+                load_cols<C>(ks, Ld.k[s], lch);
 #pragma unroll
-                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(cs, Ld.k[s][col0 + c], X[c]);
+                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(cs, ks[c], X[c]);
             }
         }
         done += take;
@@ -211,9 +243,10 @@ __global__ __launch_bounds__(kChThreads) void gdn_chunked_kernel(ChunkedParams p
     for (int m = 0; m < kCk; ++m)
         if (m < mo && lam == 0) p.out_u[(((size_t)n * kCk + m) * p.hv + h) * p.dv + row] = ureg[m];
     if (tile == 0 && h % G_ == 0)
-        for (int idx = tid; idx < mo * DK; idx += kChThreads) {
-            const int m = idx / DK, i = idx % DK;
-            p.out_k[(((size_t)n * kCk + m) * p.hk + kh) * DK + i] = Ld.k[m][i];
+        for (int idx = tid; idx < mo * (DK / 4); idx += kChThreads) {
+            const int m = idx / (DK / 4), c4 = idx % (DK / 4);
+            *reinterpret_cast<float4 *>(p.out_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + 4 * c4) =
+                *reinterpret_cast<const float4 *>(&Ld.k[m][stage_off(c4)]);
         }
     if (tile == 0 && tid < mo) p.out_G[((size_t)n * kCk + tid) * p.hv + h] = Ld.G[tid];
     if (tile == 0 && h == 0 && tid == 0) p.out_count[n] = mo;

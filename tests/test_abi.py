@@ -466,6 +466,7 @@ def call_chunked(lib, dims, with_in=True, **over):
     ({}, dict(cu=None), 1), ({}, dict(oS=None), 1), ({}, dict(oc=None), 1), ({}, dict(q=None), 1),
     ({}, dict(o=None), 1), ({}, dict(ik=None), 1),
     ({}, dict(q=CH["q"] + 8), 4), ({}, dict(oS=CH["oS"] + 4), 4), ({}, dict(oc=CH["oc"] + 2), 4),
+    ({}, dict(ik=CH["ik"] + 4), 4), ({}, dict(ok=CH["ok"] + 8), 4),
     ({}, dict(oS=CH["iS"]), 5), ({}, dict(ou=CH["iu"] + 64), 5), ({}, dict(o=CH["v"]), 5),
     ({}, dict(oG=CH["ou"]), 5), ({}, dict(oc=CH["q"]), 5),
 ])
