@@ -147,3 +147,28 @@ def test_empty_call_keeps_state(gpu):
     e = synth.Workload(w.q[:0], w.k[:0], w.v[:0], w.g[:0], w.beta[:0], torch.tensor([0, 0, 0], dtype=torch.int32), None)
     _, st2 = run(gpu, e, st)
     assert states_equal(st, st2)
+
+
+def test_decode_replay_benchmark_heads(gpu):
+    """16/32 heads, dk = dv = 128: a 512-token prefill then 9 one-token decode steps
+    (crossing a chunk end) equal a 521-token prefill, outputs and state bit for bit,
+    for a batch of 3 sequences."""
+    L0, steps = 512, 9
+    w = synth.make_workload(631, [L0 + steps] * 3, h0_std=0.1)
+    ref_out, ref_st = run(gpu, w, start_state(gpu, w))
+    cu = w.cu_seqlens.tolist()
+
+    def part(a, b):
+        idx = torch.cat([torch.arange(cu[n] + a, cu[n] + b) for n in range(3)])
+        return synth.Workload(w.q[idx], w.k[idx], w.v[idx], w.g[idx], w.beta[idx],
+                              synth.cu_from_lengths([b - a] * 3), None)
+
+    out0, st = run(gpu, part(0, L0), start_state(gpu, w))
+    for n in range(3):
+        assert bit_equal(out0[n * L0:(n + 1) * L0], ref_out[cu[n]:cu[n] + L0]), n
+    for j in range(steps):
+        o, st = run(gpu, part(L0 + j, L0 + j + 1), st)
+        for n in range(3):
+            assert bit_equal(o[n:n + 1], ref_out[cu[n] + L0 + j:cu[n] + L0 + j + 1]), (n, j)
+    assert states_equal(st, ref_st)
+    say("chunked: 512-token prefill + 9 decode steps == 521-token prefill, 32 heads, bitwise")
