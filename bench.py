@@ -418,6 +418,22 @@ def main():
 
         per_b, _ = time_launches(bwd, args.steps, 3, stream)
         msb = float(np.median(per_b))
+        # the training forward (also saves p_t) and the backward fed its p_t
+        out_t = torch.empty((T, 32, 128), dtype=torch.bfloat16, device=dev)
+        hT_t = torch.empty((w.n_seqs, 32, 128, 128), dtype=torch.float32, device=dev)
+        sp_t = torch.empty((T, 32, 128), dtype=torch.float32, device=dev)
+
+        def fwd_train(_i):
+            gdn.gdn_fwd_varlen_train(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], out=out_t, hT=hT_t,
+                                     saved_p=sp_t, stream=stream)
+
+        per_ft, _ = time_launches(fwd_train, args.steps, 3, stream)
+
+        def bwd_saved(_i):
+            gdn.gdn_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                               workspace=ws, grads=grads, stream=stream, saved_p=sp_t, hT=hT_t)
+
+        per_bs, _ = time_launches(bwd_saved, args.steps, 3, stream)
         bflops = 18.0 * 128 * 128 * 32 * T
         s0 = synth.head_slice(w, 0)
         rb = oracle.gdn_backward(s0.q, s0.k, s0.v, s0.g, s0.beta, s0.cu_seqlens, dout_c[:, 0:2].contiguous(),
@@ -427,11 +443,13 @@ def main():
         workloads["backward_varlen_prefill"] = {
             "tokens": T, "n_seqs": w.n_seqs, "ms_median": msb, "tokens_per_s": T / (msb / 1e3),
             "launches": 6, "workspace_bytes": int(ws.numel()),
+            "train_forward_ms_median": float(np.median(per_ft)),
+            "ms_median_with_saved_p": float(np.median(per_bs)),
             "roofline": {"bound": "alu", "achieved": bflops / (msb / 1e3) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": bflops / (msb / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
                          "flops_per_launch": bflops},
             "parity": {"kh0_grads": {k: rel(v.cpu().numpy(), rb[k]) for k, v in got.items()}}}
-        del dout_d, dhT_d, ws, grads
+        del dout_d, dhT_d, ws, grads, out_t, hT_t, sp_t
 
         # The chunked form with a replaying decode (gdn_fwd_chunked): the benchmark
         # batch as one prefill from h0, and one decode step at B = 256 through the

@@ -142,6 +142,19 @@ gdn_status gdn_fwd_varlen(const gdn_dims *dims,
                           void *out, float *hT, void *stream);
 
 /*
+ * Training forward: gdn_fwd_varlen that also writes saved_p [T][hv][dv] fp32, the
+ * key read-out p_t = S_{t-1} k_t of every token and row (the value the recurrence
+ * forms for u_t), for gdn_bwd_varlen.  out and hT are bit-identical to
+ * gdn_fwd_varlen's.  dims->pre must be NULL (GDN_ERR_UNSUPPORTED); saved_p may be
+ * NULL only when T == 0 and must not overlap any other argument.
+ */
+gdn_status gdn_fwd_varlen_train(const gdn_dims *dims,
+                                const void *q, const void *k, const void *v,
+                                const float *g, const float *beta,
+                                const float *h0, const int32_t *cu_seqlens,
+                                void *out, float *hT, float *saved_p, void *stream);
+
+/*
  * Varlen prefill against a state pool, for prefix caching.  The state handling
  * follows what the page "Defending Against the Training-Inference Numeric
  * Mismatch in RL (Especially Linear Attention)" (section 3.2, "Solution") keeps
@@ -290,6 +303,10 @@ gdn_status gdn_short_conv(const gdn_conv_dims *dims, const void *x, const float 
  *   q, k, v, g, beta, h0, cu_seqlens : the forward's inputs (dims->pre must be NULL)
  *   dout        : [T][hv][dv] io dtype, dL/dout
  *   dhT         : [N][hv][dv][dk] fp32, dL/dhT, or NULL for zero
+ *   saved_p     : p_t from gdn_fwd_varlen_train on the same inputs, or NULL.  Given, the
+ *                 backward skips its own forward recompute (one of its four passes).
+ *   hT          : the forward's final states; required when saved_p and dhT are both
+ *                 given (for <dhT, hT>), otherwise ignored and may be NULL
  *   dq, dk      : [T][hk][dk] fp32 outputs
  *   dv          : [T][hv][dv] fp32 output
  *   dg, dbeta   : [T][hv] fp32 outputs
@@ -307,6 +324,7 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims,
                           const float *g, const float *beta,
                           const float *h0, const int32_t *cu_seqlens,
                           const void *dout, const float *dhT,
+                          const float *saved_p, const float *hT,
                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dh0,
                           void *workspace, uint64_t workspace_bytes, void *stream);
 
@@ -366,7 +384,7 @@ const char *gdn_status_string(gdn_status status);
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 203
+#define GDN_ABI_VERSION 204
 
 #ifdef __cplusplus
 }

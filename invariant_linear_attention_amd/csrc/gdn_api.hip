@@ -179,12 +179,11 @@ gdn_status launch_varlen(const gdn_dims *dims, PrefillParams &p, void *stream) {
 }  // namespace
 }  // namespace gdn
 
-extern "C" {
-
-gdn_status gdn_fwd_varlen(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
-                          const float *beta, const float *h0, const int32_t *cu_seqlens, void *out, float *hT,
-                          void *stream) {
-    using namespace gdn;
+namespace gdn {
+namespace {
+gdn_status fwd_varlen(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const float *h0, const int32_t *cu_seqlens, void *out, float *hT,
+                      float *save_p, void *stream) {
     gdn_status st = check_common(dims);
     if (st != GDN_OK) return st;
     const gdn_dims &d = *dims;
@@ -200,26 +199,48 @@ gdn_status gdn_fwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
     const uint64_t s_bytes = (uint64_t)N * d.hv * d.dv * d.dk * 4;
 
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(h0, 16) ||
-        !aligned(hT, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(cu_seqlens, 4))
+        !aligned(hT, 16) || !aligned(save_p, 4) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(cu_seqlens, 4))
         return GDN_ERR_ALIGN;
 
     const Range rq = range_of(q, qk_bytes), rk = range_of(k, qk_bytes), rv = range_of(v, vo_bytes);
     const Range rg = range_of(g, gb_bytes), rb = range_of(beta, gb_bytes);
     const Range rh0 = range_of(h0, h0 ? s_bytes : 0), rhT = range_of(hT, hT ? s_bytes : 0);
     const Range rcu = range_of(cu_seqlens, (uint64_t)(N + 1) * 4), ro = range_of(out, vo_bytes);
+    const Range rp = range_of(save_p, save_p ? (uint64_t)T * d.hv * d.dv * 4 : 0);
     const Range ra = pre_range(dims, 0), rdb = pre_range(dims, 1);
-    for (Range in : {rq, rk, rv, rg, rb, rh0, rcu, rhT, ra, rdb})
+    for (Range in : {rq, rk, rv, rg, rb, rh0, rcu, rhT, ra, rdb, rp})
         if (overlap(ro, in)) return GDN_ERR_ALIAS;
-    for (Range in : {rq, rk, rv, rg, rb, rcu, ra, rdb})
+    for (Range in : {rq, rk, rv, rg, rb, rcu, ra, rdb, rp})
         if (overlap(rhT, in)) return GDN_ERR_ALIAS;
+    for (Range in : {rq, rk, rv, rg, rb, rh0, rcu, ra, rdb})
+        if (overlap(rp, in)) return GDN_ERR_ALIAS;
     if (h0 && hT && h0 != hT && overlap(rh0, rhT)) return GDN_ERR_ALIAS;
 
     PrefillParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0;
     p.cu_seqlens = cu_seqlens; p.out = out; p.hT = hT;
     p.pool_size = (int32_t)N;
+    p.save_p = save_p;
     apply_pre(dims, p);
     return launch_varlen(dims, p, stream);
+}
+}  // namespace
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_fwd_varlen(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *h0, const int32_t *cu_seqlens, void *out, float *hT,
+                          void *stream) {
+    return gdn::fwd_varlen(dims, q, k, v, g, beta, h0, cu_seqlens, out, hT, nullptr, stream);
+}
+
+gdn_status gdn_fwd_varlen_train(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                                const float *beta, const float *h0, const int32_t *cu_seqlens, void *out, float *hT,
+                                float *saved_p, void *stream) {
+    if (dims && dims->pre) return GDN_ERR_UNSUPPORTED;
+    if (dims && dims->total_tokens > 0 && !saved_p) return GDN_ERR_NULL;
+    return gdn::fwd_varlen(dims, q, k, v, g, beta, h0, cu_seqlens, out, hT, saved_p, stream);
 }
 
 gdn_status gdn_fwd_varlen_pool(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
@@ -391,8 +412,9 @@ gdn_status gdn_bwd_workspace_size(const gdn_dims *dims, uint64_t *bytes) {
 
 gdn_status gdn_bwd_varlen(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
                           const float *beta, const float *h0, const int32_t *cu_seqlens, const void *dout,
-                          const float *dhT, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dh0,
-                          void *workspace, uint64_t workspace_bytes, void *stream) {
+                          const float *dhT, const float *saved_p, const float *hT, float *dq, float *dk, float *dv,
+                          float *dg, float *dbeta, float *dh0, void *workspace, uint64_t workspace_bytes,
+                          void *stream) {
     using namespace gdn;
     gdn_status st = check_common(dims);
     if (st != GDN_OK) return st;
@@ -405,6 +427,7 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
     if (!cu_seqlens || !workspace) return GDN_ERR_NULL;
     if (T > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
         return GDN_ERR_NULL;
+    if (saved_p && dhT && !hT) return GDN_ERR_NULL;  // <dhT, hT> needs the forward's hT
     const BwdWorkspace ws = backward_workspace(T, N, d.hv, d.dk, d.dv);
     if (workspace_bytes < ws.total) return GDN_ERR_SHAPE;
     if (N * d.hv * (int64_t)(d.dv / 32 > d.dk / 32 ? d.dv / 32 : d.dk / 32) > 0x7FFFFFFFll ||
@@ -413,8 +436,8 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
 
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(h0, 16) ||
         !aligned(dhT, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dh0, 16) ||
-        !aligned(workspace, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(dg, 4) || !aligned(dbeta, 4) ||
-        !aligned(cu_seqlens, 4))
+        !aligned(workspace, 16) || !aligned(saved_p, 16) || !aligned(hT, 16) || !aligned(g, 4) ||
+        !aligned(beta, 4) || !aligned(dg, 4) || !aligned(dbeta, 4) || !aligned(cu_seqlens, 4))
         return GDN_ERR_ALIGN;
 
     const uint64_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
@@ -423,7 +446,8 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
     const Range inputs[] = {range_of(q, qk_n * esz), range_of(k, qk_n * esz), range_of(v, vo_n * esz),
                             range_of(g, gb_bytes), range_of(beta, gb_bytes), range_of(h0, h0 ? s_bytes : 0),
                             range_of(cu_seqlens, (uint64_t)(N + 1) * 4), range_of(dout, vo_n * esz),
-                            range_of(dhT, dhT ? s_bytes : 0)};
+                            range_of(dhT, dhT ? s_bytes : 0), range_of(saved_p, saved_p ? vo_n * 4 : 0),
+                            range_of(hT, hT ? s_bytes : 0)};
     const Range outputs[] = {range_of(dq, qk_n * 4), range_of(dk, qk_n * 4), range_of(dv, vo_n * 4),
                              range_of(dg, gb_bytes), range_of(dbeta, gb_bytes), range_of(dh0, dh0 ? s_bytes : 0),
                              range_of(workspace, ws.total)};
@@ -445,6 +469,8 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
     p.dqbuf = reinterpret_cast<float *>(w + ws.dq);
     p.cbuf = reinterpret_cast<float *>(w + ws.c);
     p.hT = reinterpret_cast<float *>(w + ws.hT);
+    p.saved_p = saved_p;
+    if (saved_p) p.hT = const_cast<float *>(hT);  // F0 is skipped: <dhT, hT> reads the caller's hT
     p.total_tokens = T; p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dk = d.dk; p.dv = d.dv;
     p.rank_by_length = (N > 1 && N <= kMaxRankedSeqs && T >= 32 * N) ? 1 : 0;
     const hipError_t e = launch_backward(p, d.io_dtype, static_cast<hipStream_t>(stream));

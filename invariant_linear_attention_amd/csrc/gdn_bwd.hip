@@ -486,10 +486,34 @@ hipError_t pass_for_dims(const BwdParams &p, hipStream_t s) {
     }
 }
 
+// With p_t saved by the training forward, r = v - a p is formed elementwise in place
+// of the F0 pass (same formula as F0's, on the forward's p).
+template <class IO>
+__global__ __launch_bounds__(256) void gdn_bwd_r_from_p_kernel(BwdParams p) {
+    const int64_t n4 = p.total_tokens * p.hv * (p.dv / 4);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        const int64_t e = 4 * i;
+        const int64_t th = e / p.dv;  // token * hv + head
+        const float a = decay_factor(p.g[th]);
+        const float4 v = IO::load4(p.v, (size_t)e);
+        const float4 pv = *reinterpret_cast<const float4 *>(p.saved_p + e);
+        *reinterpret_cast<float4 *>(p.rbuf + e) = make_float4(v.x - a * pv.x, v.y - a * pv.y, v.z - a * pv.z, v.w - a * pv.w);
+    }
+}
+
 template <class IO>
 hipError_t backward_io(const BwdParams &p, hipStream_t s) {
     hipError_t e;
-    if ((e = pass_for_dims<kF0, IO>(p, s)) != hipSuccess) return e;
+    if (p.saved_p) {
+        const int64_t n4 = p.total_tokens * p.hv * (p.dv / 4);
+        if (n4 > 0) {
+            const int64_t blocks = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;
+            hipLaunchKernelGGL((gdn_bwd_r_from_p_kernel<IO>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    } else if ((e = pass_for_dims<kF0, IO>(p, s)) != hipSuccess) {
+        return e;
+    }
     if ((e = pass_for_dims<kR1, IO>(p, s)) != hipSuccess) return e;
     if ((e = pass_for_dims<kR2, IO>(p, s)) != hipSuccess) return e;
     if ((e = pass_for_dims<kF3, IO>(p, s)) != hipSuccess) return e;

@@ -43,6 +43,7 @@ struct PrefillParams {
     const float *A_log, *dt_bias;
     float pre_eps;
     int32_t pre_flags;
+    float *save_p;  // [T][hv][dv] p_t = S_{t-1} k_t for the backward, or null (extended instance only)
 };
 
 // Kernel arguments of one decode step.
@@ -84,6 +85,7 @@ struct BwdParams {
     float *dqbuf;  // [T][hv][dk]   dq of each value head
     float *cbuf;   // [T][hv]       q_t . dq_t - dv_t . v_t (the gate term)
     float *hT;     // [N][hv][dv][dk] final state (when dhT is given)
+    const float *saved_p;  // [T][hv][dv] p_t saved by the training forward: F0 is skipped
     int64_t total_tokens;
     int32_t n_seqs, hk, hv, dk, dv;
     int32_t rank_by_length;

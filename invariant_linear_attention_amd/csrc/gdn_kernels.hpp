@@ -636,6 +636,10 @@ void gdn_prefill_kernel(PrefillParams p) {
         const int my_slot = lam % TT, my_r = lam / TT;
         const size_t out_row = (size_t)h * p.dv + row0 + wrow + RG * my_r;
         float obuf = 0.f;
+        // The training forward also keeps p_t = S_{t-1} k_t (ptil before the step) for
+        // the backward, buffered and stored like the outputs.
+        const bool save = EXT && p.save_p != nullptr;
+        float pbuf = 0.f;
 
         // Slot ti is processed with cur = A when ti is even and cur = B when odd, so
         // the first token (slot lo0) starts in both.
@@ -664,6 +668,15 @@ void gdn_prefill_kernel(PrefillParams p) {
                 float u[R], o[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) u[r] = delta_coeff(cur.ab, ptil[r], cur.bv[r]);
+                if constexpr (EXT) {
+                    if (save) {
+                        float pv = ptil[0];
+#pragma unroll
+                        for (int r = 1; r < R; ++r)
+                            if (my_r == r) pv = ptil[r];
+                        if (my_slot == ti % TT) pbuf = pv;
+                    }
+                }
                 float qc[C];
                 read_cols(qc, Ld.q[buf][ti]);
                 fetch(nxt, buf, ti + 1);
@@ -673,8 +686,12 @@ void gdn_prefill_kernel(PrefillParams p) {
                 for (int r = 1; r < R; ++r)
                     if (my_r == r) ov = o[r];
                 if (my_slot == ti % TT) obuf = ov;
-                if (ti % TT == TT - 1 && (!EXT || ti - (TT - 1) + my_slot >= lo))
-                    IO::store1(p.out, (size_t)(t0 + ti - (TT - 1) + my_slot) * p.hv * p.dv + out_row, obuf);
+                if (ti % TT == TT - 1 && (!EXT || ti - (TT - 1) + my_slot >= lo)) {
+                    const size_t oi = (size_t)(t0 + ti - (TT - 1) + my_slot) * p.hv * p.dv + out_row;
+                    IO::store1(p.out, oi, obuf);
+                    if constexpr (EXT)
+                        if (save) p.save_p[oi] = pbuf;
+                }
             };
 
             // Full token blocks are fully unrolled.  The last block of a sequence
@@ -705,8 +722,12 @@ void gdn_prefill_kernel(PrefillParams p) {
                 }
             }
             const int rem = nt % TT;  // tokens kept but not yet stored (partial block only)
-            if (rem != 0 && my_slot < rem && (!EXT || nt - rem + my_slot >= lo))
-                IO::store1(p.out, (size_t)(t0 + nt - rem + my_slot) * p.hv * p.dv + out_row, obuf);
+            if (rem != 0 && my_slot < rem && (!EXT || nt - rem + my_slot >= lo)) {
+                const size_t oi = (size_t)(t0 + nt - rem + my_slot) * p.hv * p.dv + out_row;
+                IO::store1(p.out, oi, obuf);
+                if constexpr (EXT)
+                    if (save) p.save_p[oi] = pbuf;
+            }
             if constexpr (EXT) snapshot_after(t0 + nt - tb);
 
             if (blk + 1 < nblk) st.store(Ld, buf ^ 1, tid, pre, p.pre_eps, amp, dtb);
@@ -824,7 +845,7 @@ hipError_t launch_prefill_t(const PrefillParams &p, hipStream_t s) {
     q.tiles = p.dv / RW;
     dim3 grid((unsigned)q.tiles * p.hv * p.n_seqs), block(NW * 64);
     void *args[] = {&q};
-    const bool ext = p.snap_block > 0 || p.pre_flags != 0;
+    const bool ext = p.snap_block > 0 || p.pre_flags != 0 || p.save_p != nullptr;
     const void *fn = ext ? reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, L, R, NW, true>)
                          : reinterpret_cast<const void *>(&gdn_prefill_kernel<DK, IO, L, R, NW, false>);
     return hipLaunchKernel(fn, grid, block, args, 0, s);

@@ -19,7 +19,7 @@ STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
     5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_HIP",
 }
-EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv", "gdn_query_plan",
+EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv", "gdn_query_plan",
            "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_fwd_chunked", "gdn_status_string", "gdn_abi_version")
 
 GDN_CHUNK = 16
@@ -95,7 +95,9 @@ def load_library(path: str = LIBRARY):
         lib.gdn_bwd_workspace_size.restype = ctypes.c_int
         lib.gdn_bwd_workspace_size.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(ctypes.c_uint64)]
         lib.gdn_bwd_varlen.restype = ctypes.c_int
-        lib.gdn_bwd_varlen.argtypes = [ctypes.POINTER(GdnDims)] + [vp] * 16 + [ctypes.c_uint64, vp]
+        lib.gdn_bwd_varlen.argtypes = [ctypes.POINTER(GdnDims)] + [vp] * 18 + [ctypes.c_uint64, vp]
+        lib.gdn_fwd_varlen_train.restype = ctypes.c_int
+        lib.gdn_fwd_varlen_train.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdn_fwd_chunked.restype = ctypes.c_int
         lib.gdn_fwd_chunked.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp,
                                         ctypes.POINTER(GdnChunkState), ctypes.POINTER(GdnChunkState), vp, vp]
@@ -223,18 +225,47 @@ def gdn_bwd_workspace_size(dims: GdnDims) -> int:
     return int(n.value)
 
 
+def gdn_fwd_varlen_train(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, saved_p=None, stream=None):
+    """gdn_fwd_varlen that also returns p_t = S_{t-1} k_t [T, Hv, dv] fp32 for the
+    backward.  Returns (out, hT, saved_p)."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    _need(g, "g", torch.float32)
+    _need(beta, "beta", torch.float32)
+    _need(h0, "h0", torch.float32)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    T = int(q.shape[0])
+    N = int(cu_seqlens.numel()) - 1
+    if out is None:
+        out = torch.empty((T, v.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+    if hT is None:
+        hT = torch.empty((N, v.shape[1], v.shape[2], q.shape[2]), dtype=torch.float32, device=q.device)
+    if saved_p is None:
+        saved_p = torch.empty((T, v.shape[1], v.shape[2]), dtype=torch.float32, device=q.device)
+    for name, t, dt in (("out", out, q.dtype), ("hT", hT, torch.float32), ("saved_p", saved_p, torch.float32)):
+        _need(t, name, dt)
+    dims = make_dims(q, v, N, T)
+    _check(lib.gdn_fwd_varlen_train(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                                    _ptr(cu_seqlens), _ptr(out), _ptr(hT), _ptr(saved_p), _stream_handle(stream)))
+    return out, hT, saved_p
+
+
 def gdn_bwd_varlen(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=None, grads=None, stream=None,
-                   want_dh0: bool = True):
+                   want_dh0: bool = True, saved_p=None, hT=None):
     """Backward of gdn_fwd_varlen (see include/gdn.h).  Inputs as gdn_fwd_varlen plus
     dout [T, Hv, dv] (dtype of q) and dhT [N, Hv, dv, dk] fp32 or None.  ``workspace``
     (a uint8 device tensor of at least gdn_bwd_workspace_size bytes) and ``grads``
     (a dict of output tensors) are allocated when None.  Returns a dict of fp32
-    tensors: dq, dk [T, Hk, dk]; dv [T, Hv, dv]; dg, dbeta [T, Hv]; dh0."""
+    tensors: dq, dk [T, Hk, dk]; dv [T, Hv, dv]; dg, dbeta [T, Hv]; dh0.  ``saved_p`` (and
+    ``hT`` when dhT is given) from gdn_fwd_varlen_train skip the backward's own
+    forward recompute."""
     import torch
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need(t, name, q.dtype)
-    for name, t in (("g", g), ("beta", beta), ("h0", h0), ("dhT", dhT)):
+    for name, t in (("g", g), ("beta", beta), ("h0", h0), ("dhT", dhT), ("saved_p", saved_p), ("hT", hT)):
         _need(t, name, torch.float32)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
     T, hk, dk = (int(x) for x in q.shape)
@@ -253,7 +284,8 @@ def gdn_bwd_varlen(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=N
     for name, t in grads.items():
         _need(t, name, torch.float32)
     _check(lib.gdn_bwd_varlen(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
-                              _ptr(cu_seqlens), _ptr(dout), _ptr(dhT), _ptr(grads["dq"]), _ptr(grads["dk"]),
+                              _ptr(cu_seqlens), _ptr(dout), _ptr(dhT), _ptr(saved_p), _ptr(hT),
+                              _ptr(grads["dq"]), _ptr(grads["dk"]),
                               _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["dbeta"]), _ptr(grads.get("dh0")),
                               _ptr(workspace), int(workspace.numel()), _stream_handle(stream)))
     return grads

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
+    assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
                           "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_fwd_chunked",
                           "gdn_status_string", "gdn_abi_version"}
     for name in names:
@@ -382,7 +382,7 @@ def test_conv_null_dims_and_noop(lib):
 # ------------------------------------------------------------------ backward
 
 BP = {name: BASE + (40 + i) * MB for i, name in enumerate(
-    ["q", "k", "v", "g", "b", "h0", "cu", "dout", "dhT", "dq", "dk", "dv", "dg", "db", "dh0", "ws"])}
+    ["q", "k", "v", "g", "b", "h0", "cu", "dout", "dhT", "dq", "dk", "dv", "dg", "db", "dh0", "ws", "sp", "hT"])}
 
 
 def ws_size(lib, dims):
@@ -397,8 +397,8 @@ def call_bwd(lib, dims, ws_bytes=None, **over):
     if ws_bytes is None:
         ws_bytes = ws_size(lib, dims) if dims is not None else 0
     return lib.gdn_bwd_varlen(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], a["v"], a["g"],
-                              a["b"], a["h0"], a["cu"], a["dout"], a["dhT"], a["dq"], a["dk"], a["dv"], a["dg"],
-                              a["db"], a["dh0"], a["ws"], ctypes.c_uint64(ws_bytes), None)
+                              a["b"], a["h0"], a["cu"], a["dout"], a["dhT"], a.get("sp"), a.get("hT"), a["dq"],
+                              a["dk"], a["dv"], a["dg"], a["db"], a["dh0"], a["ws"], ctypes.c_uint64(ws_bytes), None)
 
 
 def test_bwd_workspace_size(lib):
@@ -423,6 +423,7 @@ def test_bwd_workspace_size(lib):
     ({}, dict(dq=BP["dq"] + 4), 4), ({}, dict(g=BP["g"] + 2), 4),
     ({}, dict(dq=BP["q"]), 5), ({}, dict(dk=BP["dq"]), 5), ({}, dict(ws=BP["dout"]), 5),
     ({}, dict(dh0=BP["h0"]), 5), ({}, dict(dv=BP["ws"] + 256), 5), ({}, dict(dg=BP["db"]), 5),
+    ({}, dict(hT=None), 1), ({}, dict(sp=BP["sp"] + 4), 4), ({}, dict(dq=BP["sp"]), 5), ({}, dict(ws=BP["hT"]), 5),
 ])
 def test_bwd_rejects(lib, case, over, code):
     assert call_bwd(lib, _dims(**case), ws_bytes=(1 << 30), **over) == code
@@ -479,3 +480,20 @@ def test_chunked_null_in_and_noop(lib):
     assert call_chunked(lib, _dims(n_seqs=0, total_tokens=0)) == 0
     # no incoming state is allowed (empty states); a missing out array is not
     assert call_chunked(lib, _dims(n_seqs=0, total_tokens=0), with_in=False) == 0
+
+
+def test_fwd_train_rejects(lib):
+    def call(dims, **over):
+        a = dict(P)
+        a["sp"] = BASE + 70 * MB
+        a.update(over)
+        return lib.gdn_fwd_varlen_train(ctypes.byref(dims), a["q"], a["k"], a["v"], a["g"], a["b"], a["h0"], a["cu"],
+                                        a["out"], a["hT"], a["sp"], None)
+    from invariant_linear_attention_amd import gdn
+    assert call(_dims(), sp=None) == 1
+    assert call(_dims(), sp=P["q"]) == 5
+    assert call(_dims(), sp=P["out"] + 64) == 5
+    assert call(_dims(), sp=BASE + 70 * MB + 2) == 4
+    d = _dims()
+    d.pre = ctypes.pointer(gdn.make_preproc(norm_qk=True))
+    assert call(d) == 6

@@ -157,3 +157,41 @@ def test_workspace_contents_do_not_matter(gpu):
     for key in ("dq", "dk", "dv", "dg", "dbeta"):
         assert torch.equal(r0[key], r1[key]), key
     assert all(bool(torch.isfinite(r0[key]).all()) for key in r0)
+
+
+def test_training_forward_and_saved_p(gpu):
+    """gdn_fwd_varlen_train: out and hT bit-identical to gdn_fwd_varlen; saved_p
+    equals p_t = S_{t-1} k_t from the oracle (its state after the first t-1 tokens,
+    times k_t); the backward fed saved_p (and hT) meets the same gates."""
+    from invariant_linear_attention_amd import gdn
+    from oracle import oracle
+    w = synth.make_workload(361, [23, 0, 9], hk=2, hv=4, dk=64, dv=64, io_dtype=torch.float32, h0_std=0.1)
+    d = to_dev(w)
+    out0, hT0 = gdn.gdn_fwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"])
+    out1, hT1, sp = gdn.gdn_fwd_varlen_train(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(hT0, hT1)
+    cu = w.cu_seqlens.tolist()
+    sp_c = sp.cpu().double().numpy()
+    kk = w.k.double().numpy()
+    worst = 0.0
+    for n in (0, 2):
+        for t in range(cu[n + 1] - cu[n]):
+            pre = synth.token_slice(synth.select(w, [n]), 0, t, h0=w.h0[n:n + 1])
+            if t == 0:
+                S = w.h0[n].double().numpy()
+            else:
+                _, S = oracle.gdn_forward(pre.q, pre.k, pre.v, pre.g, pre.beta, pre.cu_seqlens, pre.h0)
+                S = S[0]
+            for h in range(4):
+                ref = S[h] @ kk[cu[n] + t, h // 2]
+                got = sp_c[cu[n] + t, h]
+                worst = max(worst, float(np.linalg.norm(got - ref) / np.linalg.norm(ref)))
+    say("saved p_t vs oracle: max rel err %.2e" % worst)
+    assert worst <= 1e-4
+    dout, dhT = grad_inputs(w, 17)
+    ref = oracle.gdn_backward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, dout, h0=w.h0, dhT=dhT)
+    r = gdn.gdn_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu_seqlens"], dout.to(DEV),
+                           dhT.to(DEV), saved_p=sp, hT=hT1)
+    torch.cuda.synchronize()
+    check_grads(w, r, ref, "bwd with saved p", dout)
