@@ -97,11 +97,13 @@ def test_parity_benchmark_batch(gpu):
         assert e <= OUT_TOL[torch.bfloat16] and es <= STATE_TOL
 
 
-def test_split_calls_and_decode_replay(gpu):
+@pytest.mark.parametrize("hk,hv", [(2, 4), (1, 8)])
+def test_split_calls_and_decode_replay(gpu, hk, hv):
     """One call over the whole sequences == the same tokens in several calls
-    (cuts inside and at chunk boundaries, one-token decode steps), bit for bit."""
+    (cuts inside and at chunk boundaries, one-token decode steps), bit for bit;
+    with 8 value heads on one key head the key cache has one writer for eight readers."""
     lengths = [70, 23, 48]
-    w = synth.make_workload(601, lengths, hk=2, hv=4, dk=128, dv=64, h0_std=0.1)
+    w = synth.make_workload(601, lengths, hk=hk, hv=hv, dk=128, dv=64, h0_std=0.1)
     st0 = start_state(gpu, w)
     ref_out, ref_st = run(gpu, w, st0)
     cuts = [0, 1, 2, 5, 16, 17, 31, 32, 33, 40, 47, 48, 61, 70]
