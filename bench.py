@@ -66,6 +66,11 @@ def traffic_from_profile(kind, src_hash):
     return rec.get("bytes_per_launch")
 
 
+def progress(msg):
+    """One line per finished section on stderr (the JSON line stays alone on stdout)."""
+    print("bench: %s" % msg, file=sys.stderr, flush=True)
+
+
 def time_launches(fn, steps, warmup, stream):
     """Per-launch durations (ms) from HIP events recorded on the launch stream."""
     import torch
@@ -223,6 +228,7 @@ def main():
         parity["kh%d" % kh] = {"out": rel(out[:, vs].float().cpu().numpy(), ro),
                                "state": rel(hT[:, vs].cpu().numpy(), rh)}
     parity_ok = all(p["out"] <= 2e-3 and p["state"] <= 1e-4 for p in parity.values())
+    progress("prefill %.3f ms (mean of %d launches), parity %s" % (ms, args.steps, parity_ok))
 
     # ------------------------------------------------------------- decode
     decode = None
@@ -262,6 +268,7 @@ def main():
                                               "bytes_per_launch": alg_bytes},
                                  "state_pools": n_pools}
             del pools
+            progress("decode B=%d %.1f us" % (B, ms_d * 1e3))
 
     # ------------------------------------------------ other prefill workloads
     workloads = None
@@ -305,6 +312,7 @@ def main():
                                                                              Tw // chunks))),
                                "parity": par}
             del dd, outw, state
+            progress("%s %.3f ms" % (name, msw))
 
         # The benchmark batch through the state pool with a snapshot every 256 tokens
         # (prefix caching): 8 source slots, 8 destination slots, one slot per snapshot.
@@ -329,6 +337,7 @@ def main():
             "tokens_per_s": T / (msp / 1e3), "roofline_frac": flops / (msp / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
             "same_bits_as_plain": bool(torch.equal(outp.view(torch.int16), out.view(torch.int16)))}
         del pool, outp
+        progress("pool with snapshots %.3f ms" % msp)
 
         # The benchmark batch's shape on raw inputs with both fused preprocessing steps
         # (in-kernel q/k L2 norm; gate and beta from logits).
@@ -350,6 +359,7 @@ def main():
             "parity": {"kh0": head_parity(synth, oracle, rw, outr, hTr, 0,
                                           fused=(rw.meta["A_log"], rw.meta["dt_bias"]))}}
         del rd, outr, hTr
+        progress("fused preprocessing %.3f ms" % msf)
 
         # The short convolution on the q|k|v channels of the benchmark batch (HBM-bound:
         # x read once, y written once) and as one decode step at B = 256.
@@ -391,6 +401,7 @@ def main():
         workloads["short_conv_varlen"]["parity"] = {"y_first256": rel(yc[:, :256].float().cpu().numpy(), ry)}
         workloads["short_conv_decode_B256"] = {"latency_us_median": float(np.median(per_cd)) * 1e3}
         del xc, yc, pool_c, xd, yd, pool_d
+        progress("short convolution %.3f ms" % msc)
 
         lc = synth.long_context(1003)
         prefill_line("long_context_65536", lc)
@@ -450,6 +461,7 @@ def main():
                          "flops_per_launch": bflops},
             "parity": {"kh0_grads": {k: rel(v.cpu().numpy(), rb[k]) for k, v in got.items()}}}
         del dout_d, dhT_d, ws, grads, out_t, hT_t, sp_t
+        progress("backward %.3f ms" % msb)
 
         # The chunked form with a replaying decode (gdn_fwd_chunked): the benchmark
         # batch as one prefill from h0, and one decode step at B = 256 through the
@@ -487,6 +499,7 @@ def main():
             "decode_B256_latency_us_median": float(np.median(per_cd2)) * 1e3,
             "parity": {"kh0": {"out": rel(och[:, 0:2].float().cpu().numpy(), ro)}}}
         del st_in, st_out, och, sts, ocd
+        progress("chunked form %.3f ms" % msch)
 
     # ------------------------------------------------------- CPU baseline
     cpu = None
