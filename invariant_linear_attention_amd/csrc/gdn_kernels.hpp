@@ -288,6 +288,12 @@ struct PrefillShape {
     static constexpr int KITEMS = TS * KVEC;
     static constexpr int VITEMS = TS * VVEC;
     static constexpr int KSLOTS = (KITEMS + NT - 1) / NT;
+    // Query rows: only the block's own TB tokens are read (the extra staged row
+    // exists for the next token's key read-out), so one slot fewer where TB rows
+    // fit the workgroup's threads (4 VGPRs: 8 lanes x 2 rows then fits three waves
+    // per SIMD).
+    static constexpr int QITEMS = TB * KVEC;
+    static constexpr int QSLOTS = (QITEMS + NT - 1) / NT;
     static constexpr int VSLOTS = (VITEMS + NT - 1) / NT;
     static constexpr int TT = L / R;                 // tokens buffered per output store
     // Guards between token steps of full blocks: 1 = every token, 0 = none.  Chosen
@@ -325,7 +331,7 @@ struct Stager {
     using Sh = PrefillShape<DK, IO, L, R, NW>;
     using G = Geo<DK, L>;
     uint4 kr[Sh::KSLOTS];
-    uint4 qr[Sh::KSLOTS];
+    uint4 qr[Sh::QSLOTS];
     uint4 vr[Sh::VSLOTS];
     float vbeta[Sh::VSLOTS];  // beta of each staged value vector's token
     float gt, bt;             // g and beta of token tid (tid < TS)
@@ -342,12 +348,13 @@ struct Stager {
             const int it = tid + s * Sh::NT;
             const int ti = it / Sh::KVEC, vec = it % Sh::KVEC;
             const int64_t t = t0 + ti;
+            const bool in = t >= ts && t < te;
+            const size_t off = ((size_t)(t * p.hk + kh) * DK + (size_t)vec * IO::VEC) * IO::ESZ;
             kr[s] = zero;
-            qr[s] = zero;
-            if (it < Sh::KITEMS && t >= ts && t < te) {
-                const size_t off = ((size_t)(t * p.hk + kh) * DK + (size_t)vec * IO::VEC) * IO::ESZ;
-                kr[s] = *reinterpret_cast<const uint4 *>(kb + off);
-                qr[s] = *reinterpret_cast<const uint4 *>(qb + off);
+            if (it < Sh::KITEMS && in) kr[s] = *reinterpret_cast<const uint4 *>(kb + off);
+            if (s < Sh::QSLOTS) {
+                qr[s] = zero;
+                if (it < Sh::QITEMS && in) qr[s] = *reinterpret_cast<const uint4 *>(qb + off);
             }
         }
 #pragma unroll
@@ -395,26 +402,33 @@ struct Stager {
             // Without the norm, slots past the staged items (whole waves, often) skip
             // the unpacking; with it every lane of a row group must take part.
             if (!(pre & GDN_PRE_QK_L2NORM) && it >= Sh::KITEMS) continue;
-            float fk[IO::VEC], fq[IO::VEC];
+            float fk[IO::VEC];
             IO::unpack(kr[s], fk);
-            IO::unpack(qr[s], fq);
             if (pre & GDN_PRE_QK_L2NORM) {
-                const float ik = norm_scale(row_sumsq(fk), eps), iq = norm_scale(row_sumsq(fq), eps);
+                const float ik = norm_scale(row_sumsq(fk), eps);
 #pragma unroll
-                for (int x = 0; x < IO::VEC; ++x) {
-                    fk[x] = fk[x] * ik;
-                    fq[x] = fq[x] * iq;
-                }
+                for (int x = 0; x < IO::VEC; ++x) fk[x] = fk[x] * ik;
             }
             if (it < Sh::KITEMS) {
 #pragma unroll
                 for (int x = 0; x < IO::VEC; x += 4)
                     *reinterpret_cast<float4 *>(row_slot(Ld.k[buf][ti], vec * IO::VEC + x)) =
                         make_float4(fk[x], fk[x + 1], fk[x + 2], fk[x + 3]);
+            }
+            if (s < Sh::QSLOTS) {  // (a constant: every lane of a row group takes part)
+                float fq[IO::VEC];
+                IO::unpack(qr[s < Sh::QSLOTS ? s : 0], fq);
+                if (pre & GDN_PRE_QK_L2NORM) {
+                    const float iq = norm_scale(row_sumsq(fq), eps);
 #pragma unroll
-                for (int x = 0; x < IO::VEC; x += 4)
-                    *reinterpret_cast<float4 *>(row_slot(Ld.q[buf][ti], vec * IO::VEC + x)) =
-                        make_float4(fq[x], fq[x + 1], fq[x + 2], fq[x + 3]);
+                    for (int x = 0; x < IO::VEC; ++x) fq[x] = fq[x] * iq;
+                }
+                if (it < Sh::QITEMS) {
+#pragma unroll
+                    for (int x = 0; x < IO::VEC; x += 4)
+                        *reinterpret_cast<float4 *>(row_slot(Ld.q[buf][ti], vec * IO::VEC + x)) =
+                            make_float4(fq[x], fq[x + 1], fq[x + 2], fq[x + 3]);
+                }
             }
         }
 #pragma unroll
