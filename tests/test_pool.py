@@ -159,7 +159,8 @@ def test_snapshots_against_oracle(gpu):
             assert e <= STATE_TOL
 
 
-PLANS = [(8, 1, 4), (8, 1, 1), (16, 1, 4), (16, 2, 4), (16, 1, 2), (4, 1, 4), (4, 2, 1), (4, 1, 1)]
+PLANS = [(8, 1, 4), (8, 1, 1), (16, 1, 4), (16, 2, 4), (16, 1, 2), (4, 1, 4), (4, 2, 1), (4, 1, 1), (8, 1, 8),
+         (8, 2, 4), (16, 2, 8)]
 
 
 def test_snapshots_across_launch_shapes(gpu):

@@ -97,7 +97,8 @@ def test_alone_vs_in_batch_and_shapes(gpu):
     for n in range(w.n_seqs):
         o, h = run(gpu, synth.select(w, [n]), pre)
         assert bit_equal(o, ref_out[cu[n]:cu[n + 1]]) and bit_equal(h[0], ref_hT[n]), n
-    for plan in [(8, 1, 1), (16, 1, 4), (16, 2, 4), (4, 1, 4), (4, 2, 1), (8, 2, 2), (16, 4, 1)]:
+    for plan in [(8, 1, 1), (16, 1, 4), (16, 2, 4), (4, 1, 4), (4, 2, 1), (8, 2, 2), (16, 4, 1), (8, 1, 8), (8, 2, 4),
+                 (16, 2, 8)]:
         o, h = run(gpu, w, pre, plan=plan)
         assert bit_equal(o, ref_out) and bit_equal(h, ref_hT), plan
 
