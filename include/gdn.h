@@ -88,8 +88,10 @@ typedef enum gdn_dtype {
  *                       (sum over leaves of 4 consecutive columns, pairwise).
  *   GDN_PRE_GATE_LOGITS the `g` argument holds logits a and the `beta` argument
  *                       logits b (fp32, [T][hv]); the kernels form
- *                       g = -exp(A_log[h]) * softplus(a + dt_bias[h]) (softplus(x)
- *                       = x for x > 20) and beta = sigmoid(b).
+ *                       g = -exp(A_log[h]) * softplus(a + dt_bias[h]) and
+ *                       beta = sigmoid(b), with softplus(x) = max(x, 0) +
+ *                       log1p(exp(-|x|)) evaluated to a few fp32 ulps over the
+ *                       whole range (no cut-off for large or very negative x).
  */
 enum { GDN_PRE_QK_L2NORM = 1, GDN_PRE_GATE_LOGITS = 2 };
 
@@ -204,7 +206,11 @@ gdn_status gdn_fwd_varlen_pool(const gdn_dims *dims,
 
 /*
  * Decode step: one token for each of B sequences, against states held in a pool
- * and updated in place.
+ * and updated in place.  The page "Defending Against the Training-Inference
+ * Numeric Mismatch in RL (Especially Linear Attention)" (section 3.2, "Solution")
+ * runs decode on the same recurrent kernel as prefill and the trainer's
+ * recompute, over the recurrent state its serving stack keeps per request; this
+ * is that step, with the pool standing for that state cache.
  *
  *   q, k, v, g, beta : this step's token of each sequence; q, k [B][hk][dk],
  *                      v [B][hv][dv], g, beta [B][hv]   (dims->total_tokens == B)
@@ -378,7 +384,12 @@ gdn_status gdn_fwd_chunked(const gdn_dims *dims,
                            const gdn_chunk_state *in, const gdn_chunk_state *out,
                            void *o, void *stream);
 
-/* Human-readable name of a status code (static storage). */
+/* Human-readable description of a status code (static storage; an unknown code
+ * gives "unknown gdn_status").  Every refusal is reported as one of these codes rather than
+ * served by another, non-invariant path: the bitwise-parity post on linear
+ * attention ("Why linear attention is the next wall") describes a serving stack
+ * that refuses batch-invariant mode outright, with no fallback and no partial
+ * mode, when a kernel cannot honour it, and this library keeps that convention. */
 const char *gdn_status_string(gdn_status status);
 
 /* ABI version of this header (major * 100 + minor). */

@@ -65,7 +65,11 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 // ------------------------------------------------- fused preprocessing numerics
 //
 // One fixed sequence of fp32 operations per quantity, used by every kernel:
-//   softplus(x) = x for x > 20, else log2(1 + 2^(x log2 e)) ln 2   (hardware exp2/log2)
+//   softplus(x) = max(x, 0) + log1p(y),  y = 2^(-|x| log2 e)  (hardware exp2)
+//                 log1p(y) = y when 1 + y rounds to 1, else log2(w) ln 2 * (y / (w - 1))
+//                 with w = 1 + y rounded (the correction of the rounding of 1 + y
+//                 keeps the relative error a few ulps for small y, where log2(w) alone
+//                 loses up to 2^-24 / y; w - 1 is exact)
 //   g           = -exp(A_log) * softplus(a + dt_bias),  exp(A_log) = 2^(A_log log2 e)
 //   beta        = rcp(1 + 2^(-b log2 e))                            (hardware rcp)
 //   L2 norm     : x * rsq(sumsq + eps), sumsq over leaves of 4 consecutive columns
@@ -74,7 +78,10 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.693147180559945309417f;
 
 __device__ __forceinline__ float softplus_f32(float x) {
-    return x > 20.f ? x : __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(x * kLog2e)) * kLn2;
+    const float y = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
+    const float w = 1.f + y;
+    const float l = (w == 1.f) ? y : (__builtin_amdgcn_logf(w) * kLn2) * (y / (w - 1.f));
+    return __builtin_fmaxf(x, 0.f) + l;
 }
 __device__ __forceinline__ float gate_amplitude(float A_log) { return __builtin_amdgcn_exp2f(A_log * kLog2e); }
 __device__ __forceinline__ float gate_from_logit(float amp, float dt_bias, float a) {

@@ -19,8 +19,9 @@ STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
     5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_HIP",
 }
-EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv", "gdn_query_plan",
-           "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_fwd_chunked", "gdn_status_string", "gdn_abi_version")
+EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
+           "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_fwd_chunked",
+           "gdn_status_string", "gdn_abi_version")
 
 GDN_CHUNK = 16
 
@@ -154,6 +155,59 @@ def _need(t, name, dtype=None, cuda=True):
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
 
 
+def _shape(t, name, shape):
+    """Raise ValueError unless ``t`` (when given) has exactly ``shape``."""
+    if t is None:
+        return
+    if tuple(int(x) for x in t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _dims_of(q, k, v, g, beta, cu_seqlens=None, require_cu=False):
+    """Check the shapes of one packed batch against each other; returns
+    (T, hk, dk, hv, dv, N).  The C ABI sizes every buffer from these numbers, so a
+    tensor of another shape would be read or written past its end: every such
+    mismatch is refused here, before anything is launched."""
+    if q is None or v is None:
+        raise ValueError("q and v are required")
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [T, Hk, dk] and v [T, Hv, dv], got %s and %s" % (tuple(q.shape), tuple(v.shape)))
+    T, hk, dk = (int(x) for x in q.shape)
+    hv, dv = int(v.shape[1]), int(v.shape[2])
+    _shape(k, "k", (T, hk, dk))
+    _shape(v, "v", (T, hv, dv))
+    _shape(g, "g", (T, hv))
+    _shape(beta, "beta", (T, hv))
+    N = None
+    if cu_seqlens is None and require_cu:
+        raise ValueError("cu_seqlens is required")
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-D [N+1] tensor, got %s" % (tuple(cu_seqlens.shape),))
+        N = int(cu_seqlens.numel()) - 1
+    return T, hk, dk, hv, dv, N
+
+
+def _check_pre(pre, hv):
+    """The preprocessing arrays A_log / dt_bias must hold one value per value head."""
+    if pre is None:
+        return
+    for name, t in zip(("A_log", "dt_bias"), getattr(pre, "_keep", (None, None))):
+        if t is not None and (t.dim() != 1 or int(t.numel()) != hv):
+            raise ValueError("%s must be [Hv] = [%d], got %s" % (name, hv, tuple(t.shape)))
+
+
+def _check_pool(state_pool, hv, dv, dk):
+    if state_pool is None or state_pool.dim() != 4 or tuple(int(x) for x in state_pool.shape[1:]) != (hv, dv, dk):
+        raise ValueError("state_pool must be [P, Hv, dv, dk] = [P, %d, %d, %d], got %s"
+                         % (hv, dv, dk, None if state_pool is None else tuple(state_pool.shape)))
+
+
+def _check_index(t, name, n):
+    if t is not None and (t.dim() != 1 or int(t.numel()) != n):
+        raise ValueError("%s must be a 1-D tensor of %d entries, got %s" % (name, n, tuple(t.shape)))
+
+
 def make_preproc(norm_qk: bool = False, eps: float = 1e-6, A_log=None, dt_bias=None) -> GdnPreproc:
     """Fused preprocessing (see gdn_preproc in include/gdn.h): ``norm_qk`` L2-normalises
     q and k rows in the kernel; with ``A_log`` (fp32 [Hv] on the GPU) the ``g`` and
@@ -197,6 +251,11 @@ def gdn_fwd_varlen(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, stream=N
     or None; cu_seqlens [N+1] int32.  ``out`` / ``hT`` are allocated when None
     (hT only if ``want_state``).  Returns (out, hT)."""
     import torch
+    T, hk, dk, hv, dv, N = _dims_of(q, k, v, g, beta, cu_seqlens, require_cu=True)
+    _shape(h0, "h0", (N, hv, dv, dk))
+    _shape(out, "out", (T, hv, dv))
+    _shape(hT, "hT", (N, hv, dv, dk))
+    _check_pre(pre, hv)
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
@@ -204,12 +263,10 @@ def gdn_fwd_varlen(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, stream=N
     _need(beta, "beta", torch.float32)
     _need(h0, "h0", torch.float32)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
-    T = int(q.shape[0])
-    N = int(cu_seqlens.numel()) - 1
     if out is None:
-        out = torch.empty((T, v.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+        out = torch.empty((T, hv, dv), dtype=q.dtype, device=q.device)
     if hT is None and want_state:
-        hT = torch.empty((N, v.shape[1], v.shape[2], q.shape[2]), dtype=torch.float32, device=q.device)
+        hT = torch.empty((N, hv, dv, dk), dtype=torch.float32, device=q.device)
     _need(out, "out", q.dtype)
     _need(hT, "hT", torch.float32)
     dims = make_dims(q, v, N, T, plan=plan, pre=pre)
@@ -229,6 +286,11 @@ def gdn_fwd_varlen_train(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, sa
     """gdn_fwd_varlen that also returns p_t = S_{t-1} k_t [T, Hv, dv] fp32 for the
     backward.  Returns (out, hT, saved_p)."""
     import torch
+    T, hk, dk, hv, dv, N = _dims_of(q, k, v, g, beta, cu_seqlens, require_cu=True)
+    _shape(h0, "h0", (N, hv, dv, dk))
+    _shape(out, "out", (T, hv, dv))
+    _shape(hT, "hT", (N, hv, dv, dk))
+    _shape(saved_p, "saved_p", (T, hv, dv))
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
@@ -236,14 +298,12 @@ def gdn_fwd_varlen_train(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, sa
     _need(beta, "beta", torch.float32)
     _need(h0, "h0", torch.float32)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
-    T = int(q.shape[0])
-    N = int(cu_seqlens.numel()) - 1
     if out is None:
-        out = torch.empty((T, v.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+        out = torch.empty((T, hv, dv), dtype=q.dtype, device=q.device)
     if hT is None:
-        hT = torch.empty((N, v.shape[1], v.shape[2], q.shape[2]), dtype=torch.float32, device=q.device)
+        hT = torch.empty((N, hv, dv, dk), dtype=torch.float32, device=q.device)
     if saved_p is None:
-        saved_p = torch.empty((T, v.shape[1], v.shape[2]), dtype=torch.float32, device=q.device)
+        saved_p = torch.empty((T, hv, dv), dtype=torch.float32, device=q.device)
     for name, t, dt in (("out", out, q.dtype), ("hT", hT, torch.float32), ("saved_p", saved_p, torch.float32)):
         _need(t, name, dt)
     dims = make_dims(q, v, N, T)
@@ -262,15 +322,27 @@ def gdn_bwd_varlen(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=N
     ``hT`` when dhT is given) from gdn_fwd_varlen_train skip the backward's own
     forward recompute."""
     import torch
+    T, hk, dk, hv, dv, N = _dims_of(q, k, v, g, beta, cu_seqlens, require_cu=True)
+    _shape(h0, "h0", (N, hv, dv, dk))
+    _shape(dout, "dout", (T, hv, dv))
+    _shape(dhT, "dhT", (N, hv, dv, dk))
+    _shape(saved_p, "saved_p", (T, hv, dv))
+    _shape(hT, "hT", (N, hv, dv, dk))
+    if grads is not None:
+        want = {"dq": (T, hk, dk), "dk": (T, hk, dk), "dv": (T, hv, dv), "dg": (T, hv), "dbeta": (T, hv),
+                "dh0": (N, hv, dv, dk)}
+        for name, shp in want.items():
+            if name != "dh0" and grads.get(name) is None:
+                raise ValueError("grads[%r] is required" % name)
+            _shape(grads.get(name), name, shp)
+    if workspace is not None and workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need(t, name, q.dtype)
     for name, t in (("g", g), ("beta", beta), ("h0", h0), ("dhT", dhT), ("saved_p", saved_p), ("hT", hT)):
         _need(t, name, torch.float32)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
-    T, hk, dk = (int(x) for x in q.shape)
-    hv, dv = int(v.shape[1]), int(v.shape[2])
-    N = int(cu_seqlens.numel()) - 1
     dims = make_dims(q, v, N, T)
     if workspace is None:
         workspace = torch.empty(gdn_bwd_workspace_size(dims), dtype=torch.uint8, device=q.device)
@@ -315,15 +387,22 @@ def gdn_fwd_chunked(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=
     (allocated when None) receives the new states and must not overlap ``state_in``.
     Returns (out [T, Hv, dv], state_out)."""
     import torch
+    T, hk, dk, hv, dv, N = _dims_of(q, k, v, g, beta, cu_seqlens, require_cu=True)
+    want = {"S": (N, hv, dv, dk), "k": (N, GDN_CHUNK, hk, dk), "u": (N, GDN_CHUNK, hv, dv), "G": (N, GDN_CHUNK, hv),
+            "count": (N,)}
+    for which, st in (("state_in", state_in), ("state_out", state_out)):
+        if st is not None:
+            for name, shp in want.items():
+                if st.get(name) is None:
+                    raise ValueError("%s[%r] is required" % (which, name))
+                _shape(st[name], "%s.%s" % (which, name), shp)
+    _shape(out, "out", (T, hv, dv))
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
     _need(g, "g", torch.float32)
     _need(beta, "beta", torch.float32)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
-    T, hk, dk = (int(x) for x in q.shape)
-    hv, dv = int(v.shape[1]), int(v.shape[2])
-    N = int(cu_seqlens.numel()) - 1
     for st in (state_in, state_out):
         if st is not None:
             for name in ("S", "k", "u", "G"):
@@ -349,6 +428,12 @@ def gdn_fwd_varlen_pool(q, k, v, g, beta, cu_seqlens, state_pool, src_idx=None, 
     [N] int32 or None; snap_idx [N, S] int32 (required when snap_block > 0).
     Returns out [T, Hv, dv]."""
     import torch
+    T, hk, dk, hv, dv, N = _dims_of(q, k, v, g, beta, cu_seqlens, require_cu=True)
+    _check_pool(state_pool, hv, dv, dk)
+    for name, t in (("src_idx", src_idx), ("dst_idx", dst_idx), ("pos0", pos0)):
+        _check_index(t, name, N)
+    _shape(out, "out", (T, hv, dv))
+    _check_pre(pre, hv)
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
@@ -358,8 +443,6 @@ def gdn_fwd_varlen_pool(q, k, v, g, beta, cu_seqlens, state_pool, src_idx=None, 
     _need(state_pool, "state_pool", torch.float32)
     for name, t in (("src_idx", src_idx), ("dst_idx", dst_idx), ("pos0", pos0), ("snap_idx", snap_idx)):
         _need(t, name, torch.int32)
-    T = int(q.shape[0])
-    N = int(cu_seqlens.numel()) - 1
     snap_per_seq = 0
     if snap_idx is not None:
         if snap_idx.dim() != 2 or int(snap_idx.shape[0]) != N:
@@ -381,6 +464,11 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, state_idx=None, out=None, stre
     v [B, Hv, dv]; g, beta [B, Hv]; state_pool [P, Hv, dv, dk] fp32 updated in
     place; state_idx [B] int32 or None (identity).  Returns out [B, Hv, dv]."""
     import torch
+    B, hk, dk, hv, dv, _ = _dims_of(q, k, v, g, beta)
+    _check_pool(state_pool, hv, dv, dk)
+    _check_index(state_idx, "state_idx", B)
+    _shape(out, "out", (B, hv, dv))
+    _check_pre(pre, hv)
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
@@ -388,9 +476,8 @@ def gdn_decode_step(q, k, v, g, beta, state_pool, state_idx=None, out=None, stre
     _need(beta, "beta", torch.float32)
     _need(state_pool, "state_pool", torch.float32)
     _need(state_idx, "state_idx", torch.int32)
-    B = int(q.shape[0])
     if out is None:
-        out = torch.empty((B, v.shape[1], v.shape[2]), dtype=q.dtype, device=q.device)
+        out = torch.empty((B, hv, dv), dtype=q.dtype, device=q.device)
     _need(out, "out", q.dtype)
     dims = make_dims(q, v, B, B, pool_size=int(state_pool.shape[0]), plan=plan, pre=pre)
     _check(lib.gdn_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
@@ -404,6 +491,21 @@ def gdn_short_conv(x, w, cu_seqlens, state_pool, bias=None, src_idx=None, dst_id
     (bf16 or fp32, on the GPU); w [C, K] fp32; state_pool [P, C, K-1] in x's dtype,
     updated in place; src_idx / dst_idx [N] int32 or None.  Returns y [T, C]."""
     import torch
+    if x is None or x.dim() != 2 or w is None or w.dim() != 2:
+        raise ValueError("x must be [T, C] and w [C, K]")
+    T, C = int(x.shape[0]), int(x.shape[1])
+    K = int(w.shape[1])
+    _shape(w, "w", (C, K))
+    _shape(bias, "bias", (C,))
+    if cu_seqlens is None or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D [N+1] tensor")
+    N = int(cu_seqlens.numel()) - 1
+    if state_pool is None or state_pool.dim() != 3 or tuple(int(s) for s in state_pool.shape[1:]) != (C, K - 1):
+        raise ValueError("state_pool must be [P, C, K-1] = [P, %d, %d], got %s"
+                         % (C, K - 1, None if state_pool is None else tuple(state_pool.shape)))
+    _check_index(src_idx, "src_idx", N)
+    _check_index(dst_idx, "dst_idx", N)
+    _shape(y, "y", (T, C))
     lib = load_library()
     _need(x, "x")
     _need(w, "w", torch.float32)
@@ -412,7 +514,6 @@ def gdn_short_conv(x, w, cu_seqlens, state_pool, bias=None, src_idx=None, dst_id
     _need(state_pool, "state_pool", x.dtype)
     _need(src_idx, "src_idx", torch.int32)
     _need(dst_idx, "dst_idx", torch.int32)
-    T, C = int(x.shape[0]), int(x.shape[1])
     if y is None:
         y = torch.empty_like(x)
     _need(y, "y", x.dtype)

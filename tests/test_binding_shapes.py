@@ -1,0 +1,167 @@
+"""The Python binding refuses tensors whose shapes do not match each other, before
+anything reaches the C ABI.
+
+The ABI sizes every buffer from the dimensions it is given (T and N from q and
+cu_seqlens, heads and head dims from q and v), so a k, g, beta, h0, hT, out,
+pool or index array of another shape would be read or written past its end.
+These checks run on host tensors: the shape checks come before the device and
+dtype checks and before the library is touched, so nothing here needs a GPU.
+"""
+import pytest
+import torch
+
+from invariant_linear_attention_amd import gdn
+
+T, N, HK, HV, DK, DV = 10, 2, 2, 4, 16, 32
+
+
+def batch():
+    bf = dict(dtype=torch.bfloat16)
+    return dict(q=torch.zeros((T, HK, DK), **bf), k=torch.zeros((T, HK, DK), **bf), v=torch.zeros((T, HV, DV), **bf),
+                g=torch.zeros((T, HV)), beta=torch.zeros((T, HV)), h0=torch.zeros((N, HV, DV, DK)),
+                cu_seqlens=torch.tensor([0, 4, T], dtype=torch.int32))
+
+
+WRONG = {
+    "k": torch.zeros((T, HK + 1, DK), dtype=torch.bfloat16),
+    "v": torch.zeros((T - 1, HV, DV), dtype=torch.bfloat16),
+    "g": torch.zeros((T, HK)),
+    "beta": torch.zeros((T + 1, HV)),
+    "h0": torch.zeros((N, HV, DV, DK + 1)),
+    "cu_seqlens": torch.zeros((1, N + 1), dtype=torch.int32),
+}
+
+
+def expect_shape_error(fn, *a, **kw):
+    with pytest.raises(ValueError) as e:
+        fn(*a, **kw)
+    assert "must" in str(e.value) or "required" in str(e.value)
+
+
+@pytest.mark.parametrize("name", sorted(WRONG))
+def test_fwd_varlen_refuses(name):
+    b = batch()
+    b[name] = WRONG[name]
+    expect_shape_error(gdn.gdn_fwd_varlen, b["q"], b["k"], b["v"], b["g"], b["beta"], b["h0"], b["cu_seqlens"])
+
+
+@pytest.mark.parametrize("which,shape", [("out", (T, HV, DV + 16)), ("hT", (N + 1, HV, DV, DK))])
+def test_fwd_varlen_refuses_outputs(which, shape):
+    b = batch()
+    kw = {which: torch.zeros(shape, dtype=torch.bfloat16 if which == "out" else torch.float32)}
+    expect_shape_error(gdn.gdn_fwd_varlen, b["q"], b["k"], b["v"], b["g"], b["beta"], b["h0"], b["cu_seqlens"], **kw)
+
+
+def test_fwd_varlen_train_refuses_saved_p():
+    b = batch()
+    expect_shape_error(gdn.gdn_fwd_varlen_train, b["q"], b["k"], b["v"], b["g"], b["beta"], b["h0"], b["cu_seqlens"],
+                       saved_p=torch.zeros((T, HV, DK + 1)))
+
+
+@pytest.mark.parametrize("name", sorted(WRONG))
+def test_pool_refuses(name):
+    b = batch()
+    b[name] = WRONG[name]
+    pool = torch.zeros((3, HV, DV, DK))
+    expect_shape_error(gdn.gdn_fwd_varlen_pool, b["q"], b["k"], b["v"], b["g"], b["beta"], b["cu_seqlens"], pool)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(state_pool=torch.zeros((3, HV, DK, DV + 16))),
+    dict(src_idx=torch.zeros((N + 1,), dtype=torch.int32)),
+    dict(dst_idx=torch.zeros((N, 1), dtype=torch.int32)),
+    dict(pos0=torch.zeros((1,), dtype=torch.int32)),
+])
+def test_pool_refuses_pool_and_indices(kw):
+    b = batch()
+    pool = kw.pop("state_pool", torch.zeros((3, HV, DV, DK)))
+    expect_shape_error(gdn.gdn_fwd_varlen_pool, b["q"], b["k"], b["v"], b["g"], b["beta"], b["cu_seqlens"], pool, **kw)
+
+
+def decode_args(B=3):
+    bf = dict(dtype=torch.bfloat16)
+    return [torch.zeros((B, HK, DK), **bf), torch.zeros((B, HK, DK), **bf), torch.zeros((B, HV, DV), **bf),
+            torch.zeros((B, HV)), torch.zeros((B, HV)), torch.zeros((5, HV, DV, DK))]
+
+
+@pytest.mark.parametrize("pos,bad", [
+    (1, torch.zeros((3, HK, DK + 16), dtype=torch.bfloat16)),
+    (2, torch.zeros((2, HV, DV), dtype=torch.bfloat16)),
+    (3, torch.zeros((3, HK))),
+    (4, torch.zeros((3, HV, 1))),
+    (5, torch.zeros((5, HV, DV, DK + 4))),
+])
+def test_decode_refuses(pos, bad):
+    a = decode_args()
+    a[pos] = bad
+    expect_shape_error(gdn.gdn_decode_step, *a)
+
+
+@pytest.mark.parametrize("kw", [dict(state_idx=torch.zeros((2,), dtype=torch.int32)),
+                                dict(out=torch.zeros((3, HV, DK + 16), dtype=torch.bfloat16))])
+def test_decode_refuses_index_and_out(kw):
+    expect_shape_error(gdn.gdn_decode_step, *decode_args(), **kw)
+
+
+def test_preproc_arrays_must_cover_every_value_head():
+    b = batch()
+    pre = gdn.GdnPreproc(flags=gdn.GDN_PRE_GATE_LOGITS, eps=1e-6, A_log=None, dt_bias=None)
+    pre._keep = (torch.zeros((HV - 1,)), None)
+    expect_shape_error(gdn.gdn_fwd_varlen, b["q"], b["k"], b["v"], b["g"], b["beta"], b["h0"], b["cu_seqlens"], pre=pre)
+
+
+@pytest.mark.parametrize("name,shape", [("dout", (T, HV, DV + 1)), ("dhT", (N, HV, DV, 1)), ("saved_p", (1, HV, DV)),
+                                        ("hT", (N, HV + 1, DV, DK))])
+def test_backward_refuses(name, shape):
+    b = batch()
+    kw = dict(dout=torch.zeros((T, HV, DV), dtype=torch.bfloat16))
+    kw[name] = torch.zeros(shape, dtype=torch.bfloat16 if name == "dout" else torch.float32)
+    dout = kw.pop("dout")
+    expect_shape_error(gdn.gdn_bwd_varlen, b["q"], b["k"], b["v"], b["g"], b["beta"], b["h0"], b["cu_seqlens"], dout,
+                       **kw)
+
+
+def test_backward_refuses_gradient_buffers():
+    b = batch()
+    f = torch.zeros
+    grads = {"dq": f((T, HK, DK)), "dk": f((T, HK, DK)), "dv": f((T, HV, DV)), "dg": f((T, HV)),
+             "dbeta": f((T, HV, 1)), "dh0": None}
+    expect_shape_error(gdn.gdn_bwd_varlen, b["q"], b["k"], b["v"], b["g"], b["beta"], b["h0"], b["cu_seqlens"],
+                       torch.zeros((T, HV, DV), dtype=torch.bfloat16), grads=grads)
+
+
+def test_chunked_refuses_state_shapes():
+    b = batch()
+    st = {"S": torch.zeros((N, HV, DV, DK)), "k": torch.zeros((N, 16, HK, DK)), "u": torch.zeros((N, 16, HV, DV)),
+          "G": torch.zeros((N, 16, HV)), "count": torch.zeros((N,), dtype=torch.int32)}
+    for name, shape in (("S", (N, HV, DV, DK * 2)), ("k", (N, 8, HK, DK)), ("u", (N, 16, HK, DV)),
+                        ("G", (N, 16)), ("count", (N + 1,))):
+        bad = dict(st)
+        bad[name] = torch.zeros(shape, dtype=st[name].dtype)
+        expect_shape_error(gdn.gdn_fwd_chunked, b["q"], b["k"], b["v"], b["g"], b["beta"], b["cu_seqlens"], bad)
+
+
+@pytest.mark.parametrize("kw", [dict(bias=torch.zeros((7,))), dict(src_idx=torch.zeros((3,), dtype=torch.int32)),
+                                dict(y=torch.zeros((T, 16), dtype=torch.bfloat16))])
+def test_short_conv_refuses(kw):
+    C, K = 32, 4
+    x = torch.zeros((T, C), dtype=torch.bfloat16)
+    w = torch.zeros((C, K))
+    pool = torch.zeros((N, C, K - 1), dtype=torch.bfloat16)
+    expect_shape_error(gdn.gdn_short_conv, x, w, torch.tensor([0, 4, T], dtype=torch.int32), pool, **kw)
+
+
+def test_short_conv_refuses_state_pool():
+    C, K = 32, 4
+    expect_shape_error(gdn.gdn_short_conv, torch.zeros((T, C), dtype=torch.bfloat16), torch.zeros((C, K)),
+                       torch.tensor([0, 4, T], dtype=torch.int32), torch.zeros((N, C, K), dtype=torch.bfloat16))
+
+
+def test_matching_shapes_pass_the_shape_checks():
+    """With every shape right, the call gets past the shape checks and stops at the
+    first device check (host tensors), so the checks above are what refused."""
+    b = batch()
+    with pytest.raises(ValueError, match="device tensor"):
+        gdn.gdn_fwd_varlen(b["q"], b["k"], b["v"], b["g"], b["beta"], b["h0"], b["cu_seqlens"])
+    with pytest.raises(ValueError, match="device tensor"):
+        gdn.gdn_decode_step(*decode_args())

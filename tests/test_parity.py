@@ -2,8 +2,9 @@
 
 Small cases are checked in full (several row tiles, ragged sequence tails, empty
 sequences, every head dim and io dtype).  The full-size workloads run on the GPU
-at full size in the launch shape the benchmark uses, and the oracle recomputes a
-sample of them (whole key heads, whole sequences) one by one.
+at full size in the launch shape the benchmark uses, and the oracle recomputes
+all of them: every sequence, head and token, and every sequence of the B = 256
+decode step against its 513-token oracle run.
 """
 import numpy as np
 import pytest
@@ -48,59 +49,57 @@ def test_small_shapes(gpu, name, lengths, hk, hv, dk, dv, io, h0):
     check_parity(w, out, hT, ro, rh, name)
 
 
-def _sampled(gpu, w, key_heads, label):
-    """Full-size GPU run; oracle on the listed key heads (and their value heads)."""
+def _full(gpu, w, label):
+    """Full-size GPU run in the benchmark's launch shape; the oracle recomputes
+    every sequence, key head and token (one call, so its threads spread over all
+    (sequence, value head) units), and the gates apply to every element."""
     out, hT = run_prefill(gpu, w)
-    grp = w.dims["hv"] // w.dims["hk"]
-    for kh in key_heads:
-        s = synth.head_slice(w, kh)
-        ro, rh = oracle_of(s)
-        vs = slice(kh * grp, (kh + 1) * grp)
-        check_parity(s, out[:, vs].contiguous(), hT[:, vs].contiguous(), ro, rh, "%s kh=%d" % (label, kh))
+    say("%s: GPU done (%d tokens, %d sequences); oracle on every head" % (label, w.total_tokens, w.n_seqs))
+    ro, rh = oracle_of(w)
+    check_parity(w, out, hT, ro, rh, label)
     return out, hT
 
 
-def test_varlen_prefill_full_size_sampled(gpu):
-    """8 sequences of 256..4096 tokens, 16/32 heads, dk=dv=128, bf16 io, random h0."""
+def test_varlen_prefill_full_size(gpu):
+    """8 sequences of 256..4096 tokens, 16/32 heads, dk=dv=128, bf16 io, random h0:
+    all 32 value heads against the oracle."""
     w = synth.varlen_prefill(1001)
     say("lengths %s" % w.lengths)
-    _sampled(gpu, w, [0, 7, 15], "varlen_prefill")
+    _full(gpu, w, "varlen_prefill")
 
 
-def test_mixed_batch_full_size_sampled(gpu):
-    """64 sequences: 32 prefill chunks (16..8192 tokens) and 32 single-token decodes."""
+def test_mixed_batch_full_size(gpu):
+    """64 sequences: 32 prefill chunks (16..8192 tokens) and 32 single-token
+    decodes, a quarter resuming from cached states: every head against the oracle."""
     w = synth.mixed_batch(1004)
-    _sampled(gpu, w, [3], "mixed_batch")
+    _full(gpu, w, "mixed_batch")
 
 
-def test_long_context_full_size_sampled(gpu):
-    """One sequence of 65,536 tokens from the zero state; oracle on one key head."""
+def test_long_context_full_size(gpu):
+    """One sequence of 65,536 tokens from the zero state: every head against the oracle."""
     w = synth.long_context(1003)
-    _sampled(gpu, w, [9], "long_context")
+    _full(gpu, w, "long_context")
 
 
 def test_decode_after_prefill_vs_oracle(gpu):
-    """512-token prefill, then one decode step per sequence, against the oracle's
-    513-token run (sampled sequences of a 64-sequence batch)."""
-    w = synth.decode_history(1002, batch=64, prefix=512, steps=1)
-    pre = synth.permute(w, range(64))
-    # split each sequence into its 512-token prefix and its last token
+    """512-token prefill of 256 sequences, then one decode step at B = 256, against
+    the oracle's 513-token run of every sequence (outputs and final states)."""
+    B = 256
+    w = synth.decode_history(1002, batch=B, prefix=512, steps=1)
     cu = w.cu_seqlens.tolist()
-    first = torch.cat([torch.arange(cu[i], cu[i] + 512) for i in range(64)])
-    last = torch.tensor([cu[i] + 512 for i in range(64)])
+    first = torch.cat([torch.arange(cu[i], cu[i] + 512) for i in range(B)])
+    last = torch.tensor([cu[i] + 512 for i in range(B)])
     dev = "cuda"
     d = to_dev(w, dev)
-    cu_pre = torch.arange(0, 64 * 512 + 1, 512, dtype=torch.int32, device=dev)
-    _, pool = gpu.gdn_fwd_varlen(d["q"][first.to(dev)].contiguous(), d["k"][first.to(dev)].contiguous(),
-                                 d["v"][first.to(dev)].contiguous(), d["g"][first.to(dev)].contiguous(),
-                                 d["beta"][first.to(dev)].contiguous(), None, cu_pre)
-    li = last.to(dev)
+    fi, li = first.to(dev), last.to(dev)
+    cu_pre = torch.arange(0, B * 512 + 1, 512, dtype=torch.int32, device=dev)
+    _, pool = gpu.gdn_fwd_varlen(d["q"][fi].contiguous(), d["k"][fi].contiguous(), d["v"][fi].contiguous(),
+                                 d["g"][fi].contiguous(), d["beta"][fi].contiguous(), None, cu_pre)
     o = gpu.gdn_decode_step(d["q"][li].contiguous(), d["k"][li].contiguous(), d["v"][li].contiguous(),
                             d["g"][li].contiguous(), d["beta"][li].contiguous(), pool)
     torch.cuda.synchronize()
-    for s in (0, 37, 63):
-        sw = synth.select(pre, [s])
-        ro, rh = oracle_of(sw)
-        # the decode output is the sequence's last token; the pool holds its final state
-        one = synth.token_slice(sw, 0, 1)  # shape carrier for the metric (one token)
-        check_parity(one, o[s:s + 1], pool[s:s + 1], ro[-1:], rh, "decode seq %d" % s)
+    say("decode B=%d: GPU done; oracle on %d x 513 tokens" % (B, B))
+    ro, rh = oracle_of(w)
+    # the decode outputs are each sequence's last token; the pool holds its final state
+    one = synth.make_workload(0, [1] * B, hk=1, hv=1, dk=16, dv=16)  # carrier of cu_seqlens = 0..B
+    check_parity(one, o, pool, ro[last.numpy()], rh, "decode B=%d after 512-token prefill" % B)

@@ -144,3 +144,54 @@ def test_decode_batch_sizes(gpu):
         torch.cuda.synchronize()
         assert bit_equal(o, o_all[:Bs]) and bit_equal(p2, pool[:Bs]), Bs
     say("decode with preprocessing: batch sizes 1/8/64 agree bitwise")
+
+
+def _very_negative_logits(seed, lengths, hv=8, io=torch.bfloat16):
+    """Raw inputs whose gate argument a + dt_bias lies in [-30, -5] (softplus far
+    below 1, where log(1 + e^x) must not be formed from a rounded 1 + e^x), with a
+    large decay amplitude exp(A_log) in [1e3, 1e4] so that g = -exp(A_log)
+    softplus(a + dt_bias) spans (-67, 0) and the decay's accuracy reaches the state."""
+    w = raw(seed, lengths, hv=hv, io=io)
+    gen = torch.Generator().manual_seed(seed + 1)
+    A_log = torch.log(1e3 + 9e3 * torch.rand((hv,), generator=gen))
+    x = -30.0 + 25.0 * torch.rand(tuple(w.g.shape), generator=gen)
+    a = (x - w.meta["dt_bias"][None, :]).contiguous()
+    meta = dict(w.meta, A_log=A_log.float())
+    return synth.Workload(w.q, w.k, w.v, a, w.beta, w.cu_seqlens, w.h0, meta=meta)
+
+
+def test_gate_from_very_negative_logits(gpu):
+    """a + dt_bias in [-30, -5]: the fused gate against the fp64 oracle, which
+    evaluates log1p(exp(x)) there."""
+    w = _very_negative_logits(101, [37, 200, 1, 64])
+    pre, keep = pre_for(gpu, w)
+    out, hT = run(gpu, w, pre)
+    ro, rh = oracle_ref(w)
+    check_parity(w, out, hT, ro, rh, label="gate logits in [-30, -5]")
+
+
+def test_decay_from_very_negative_logits_one_token(gpu):
+    """With beta = sigmoid(-200) = 0 a decode step only decays: S_1 = a S_0, so a
+    state of ones returns the kernel's decay a = exp(g) itself.  Its error against
+    exp(-exp(A_log) log1p(exp(x))) in fp64 stays at the rounding of g (about
+    2e-6 relative from the arguments of the two exponentials, scaled by |g|), for
+    x down to -30; forming log(1 + e^x) from a rounded 1 + e^x misses it by up to
+    6e-4 at x = -12."""
+    import numpy as np
+    hv, B = 8, 256
+    w = _very_negative_logits(111, [1] * B, hv=hv)
+    b = torch.full((B, hv), -200.0)
+    pre, keep = pre_for(gpu, w, norm=False)
+    d = to_dev(w)
+    pool = torch.ones((B, hv, 128, 128), device=DEV)
+    gpu.gdn_decode_step(d["q"], d["k"], d["v"], d["g"], b.to(DEV), pool, pre=pre)
+    torch.cuda.synchronize()
+    got = pool[:, :, 0, 0].double().cpu().numpy()
+    assert bool((pool == pool[:, :, :1, :1]).all()), "a decay-only step must scale every element alike"
+    x = (w.g + w.meta["dt_bias"][None, :]).double().numpy()
+    g = -np.exp(w.meta["A_log"].double().numpy())[None, :] * np.log1p(np.exp(x))
+    ref = np.exp(g)
+    err = np.abs(got - ref) / ref
+    bound = 2e-6 + 4e-6 * np.abs(g)
+    say("decay from logits in [-30, -5]: max rel err %.3e (|g| up to %.1f)" % (err.max(), np.abs(g).max()))
+    assert (err <= bound).all(), "decay error %.3e at g=%.3e" % (err.max(), g.flat[int(np.argmax(err / bound))])
