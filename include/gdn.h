@@ -37,6 +37,8 @@
  * All array pointers are device pointers (hipMalloc'd or equivalent), aligned to
  * 16 bytes.  The caller owns every buffer; the library allocates nothing, keeps
  * no pointer after a call returns and has no global state, so it is reentrant.
+ * (The one exception is gdn_bwd_varlen_noalloc, which uses a fixed scratch array
+ * that each device holds for the life of the process; see there.)
  * Work is enqueued on `stream` (a hipStream_t; NULL means the null stream) and
  * the call returns without synchronising the host.
  *
@@ -64,7 +66,8 @@ typedef enum gdn_status {
     GDN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     GDN_ERR_ALIAS = 5,       /* an output overlaps an input, or h0/hT partially overlap */
     GDN_ERR_UNSUPPORTED = 6, /* dk not in {16, 32, 64, 128}, or a launch-plan request that does not fit */
-    GDN_ERR_HIP = 7          /* the HIP runtime refused the launch */
+    GDN_ERR_HIP = 7,         /* the HIP runtime refused the launch */
+    GDN_ERR_CAPACITY = 8     /* gdn_bwd_varlen_noalloc: the call needs more than its fixed scratch */
 } gdn_status;
 
 typedef enum gdn_dtype {
@@ -335,6 +338,38 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims,
                           void *workspace, uint64_t workspace_bytes, void *stream);
 
 /*
+ * Allocation-free backward, for callers that cannot allocate or pass device
+ * memory during the call: code under HIP graph capture, tight serving or training
+ * loops, and harnesses that forbid allocation.  Same operation, arguments (minus
+ * the workspace), checks and bits as gdn_bwd_varlen; the workspace is instead a
+ * fixed array of GDN_NOALLOC_SCRATCH_BYTES (64 MiB) in device memory, one per
+ * device, which that device holds until the process ends.  The call allocates
+ * nothing and calls no allocating routine; its first call on a device looks up
+ * the array's address (hipGetSymbolAddress) and keeps it.
+ *
+ * Capacity: the call needs gdn_bwd_workspace_size(dims) bytes of it, about
+ * 8 hv (dk + dv) bytes per token plus 4 hv dv dk bytes per sequence (64 KiB per
+ * token and 2 MiB per sequence at hv = 32, dk = dv = 128: about 990 tokens for one
+ * sequence); a call that needs more returns GDN_ERR_CAPACITY before anything
+ * touches the device.
+ *
+ * Every call on one device shares that device's array: calls on one device that
+ * may overlap in time (different streams, or host threads without ordering) race
+ * on it and give unspecified gradients; calls ordered on one stream are safe.  The
+ * array's contents on entry do not matter (the backward overwrites what it reads).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+gdn_status gdn_bwd_varlen_noalloc(const gdn_dims *dims,
+                                  const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta,
+                                  const float *h0, const int32_t *cu_seqlens,
+                                  const void *dout, const float *dhT,
+                                  const float *saved_p, const float *hT,
+                                  float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dh0,
+                                  void *stream);
+
+/*
  * Chunked form with a replaying decode.  gdn_fwd_varlen and gdn_decode_step make
  * decode match prefill by running token by token everywhere, as the page
  * "Defending Against the Training-Inference Numeric Mismatch in RL (Especially
@@ -395,7 +430,7 @@ const char *gdn_status_string(gdn_status status);
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 204
+#define GDN_ABI_VERSION 205
 
 #ifdef __cplusplus
 }

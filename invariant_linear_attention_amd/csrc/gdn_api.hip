@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gdn.h"
 #include "gdn_internal.hpp"
 
@@ -410,20 +412,33 @@ gdn_status gdn_bwd_workspace_size(const gdn_dims *dims, uint64_t *bytes) {
     return GDN_OK;
 }
 
-gdn_status gdn_bwd_varlen(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
-                          const float *beta, const float *h0, const int32_t *cu_seqlens, const void *dout,
-                          const float *dhT, const float *saved_p, const float *hT, float *dq, float *dk, float *dv,
-                          float *dg, float *dbeta, float *dh0, void *workspace, uint64_t workspace_bytes,
-                          void *stream) {
-    using namespace gdn;
+}  // extern "C"
+
+namespace gdn {
+namespace {
+
+// Dimension checks of the backward that need no pointer (shared by both entry points).
+gdn_status bwd_check_dims(const gdn_dims *dims) {
     gdn_status st = check_common(dims);
     if (st != GDN_OK) return st;
     const gdn_dims &d = *dims;
     if (d.pre || d.plan_lanes || d.plan_rows || d.plan_waves) return GDN_ERR_UNSUPPORTED;
     auto bwd_dim = [](int x) { return x == 32 || x == 64 || x == 128; };
     if (!bwd_dim(d.dk) || !bwd_dim(d.dv)) return GDN_ERR_UNSUPPORTED;
+    if (d.n_seqs == 0 && d.total_tokens != 0) return GDN_ERR_SHAPE;
+    return GDN_OK;
+}
+
+gdn_status bwd_varlen_impl(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *h0, const int32_t *cu_seqlens, const void *dout,
+                           const float *dhT, const float *saved_p, const float *hT, float *dq, float *dk, float *dv,
+                           float *dg, float *dbeta, float *dh0, void *workspace, uint64_t workspace_bytes,
+                           void *stream) {
+    gdn_status st = bwd_check_dims(dims);
+    if (st != GDN_OK) return st;
+    const gdn_dims &d = *dims;
     const int64_t T = d.total_tokens, N = d.n_seqs;
-    if (N == 0) return T == 0 ? GDN_OK : GDN_ERR_SHAPE;
+    if (N == 0) return GDN_OK;
     if (!cu_seqlens || !workspace) return GDN_ERR_NULL;
     if (T > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
         return GDN_ERR_NULL;
@@ -475,6 +490,58 @@ gdn_status gdn_bwd_varlen(const gdn_dims *dims, const void *q, const void *k, co
     p.rank_by_length = (N > 1 && N <= kMaxRankedSeqs && T >= 32 * N) ? 1 : 0;
     const hipError_t e = launch_backward(p, d.io_dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// The allocation-free backward's workspace: one fixed array per device, resident
+// for the life of the process.  Host code never passes `scratch` itself to a
+// kernel (on the host that name is only a stand-in); it takes the array's device
+// address from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+
+// Device address of the current device's scratch array, or null on a HIP error.
+void *scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_addr[dev].store(ptr, std::memory_order_release);  // every thread finds the same address
+    return ptr;
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_bwd_varlen(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *h0, const int32_t *cu_seqlens, const void *dout,
+                          const float *dhT, const float *saved_p, const float *hT, float *dq, float *dk, float *dv,
+                          float *dg, float *dbeta, float *dh0, void *workspace, uint64_t workspace_bytes,
+                          void *stream) {
+    return gdn::bwd_varlen_impl(dims, q, k, v, g, beta, h0, cu_seqlens, dout, dhT, saved_p, hT, dq, dk, dv, dg, dbeta,
+                                dh0, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_bwd_varlen_noalloc(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, const float *h0, const int32_t *cu_seqlens, const void *dout,
+                                  const float *dhT, const float *saved_p, const float *hT, float *dq, float *dk,
+                                  float *dv, float *dg, float *dbeta, float *dh0, void *stream) {
+    using namespace gdn;
+    // Sizes first, on the host only: a call that would not fit is refused before
+    // any HIP call.
+    gdn_status st = bwd_check_dims(dims);
+    if (st != GDN_OK) return st;
+    if (dims->n_seqs == 0) return GDN_OK;
+    const BwdWorkspace ws = backward_workspace(dims->total_tokens, dims->n_seqs, dims->hv, dims->dk, dims->dv);
+    if (ws.total > (uint64_t)GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_CAPACITY;
+    void *ptr = scratch_address();
+    if (!ptr) return GDN_ERR_HIP;
+    return bwd_varlen_impl(dims, q, k, v, g, beta, h0, cu_seqlens, dout, dhT, saved_p, hT, dq, dk, dv, dg, dbeta,
+                           dh0, ptr, (uint64_t)GDN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 gdn_status gdn_fwd_chunked(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
@@ -541,6 +608,8 @@ const char *gdn_status_string(gdn_status status) {
         case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output overlaps an input";
         case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: dk or launch shape not supported";
         case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime refused the launch";
+        case GDN_ERR_CAPACITY:
+            return "GDN_ERR_CAPACITY: the call needs more than the allocation-free entry point's fixed scratch";
     }
     return "unknown gdn_status";
 }

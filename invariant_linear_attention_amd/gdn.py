@@ -17,10 +17,11 @@ LIBRARY = os.path.join(PKG, "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 STATUS = {
     0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
-    5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_HIP",
+    5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_HIP", 8: "GDN_ERR_CAPACITY",
 }
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
-           "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_fwd_chunked",
+           "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_bwd_varlen_noalloc", "gdn_fwd_chunked",
            "gdn_status_string", "gdn_abi_version")
 
 GDN_CHUNK = 16
@@ -97,6 +98,8 @@ def load_library(path: str = LIBRARY):
         lib.gdn_bwd_workspace_size.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(ctypes.c_uint64)]
         lib.gdn_bwd_varlen.restype = ctypes.c_int
         lib.gdn_bwd_varlen.argtypes = [ctypes.POINTER(GdnDims)] + [vp] * 18 + [ctypes.c_uint64, vp]
+        lib.gdn_bwd_varlen_noalloc.restype = ctypes.c_int
+        lib.gdn_bwd_varlen_noalloc.argtypes = [ctypes.POINTER(GdnDims)] + [vp] * 18
         lib.gdn_fwd_varlen_train.restype = ctypes.c_int
         lib.gdn_fwd_varlen_train.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdn_fwd_chunked.restype = ctypes.c_int
@@ -313,16 +316,20 @@ def gdn_fwd_varlen_train(q, k, v, g, beta, h0, cu_seqlens, out=None, hT=None, sa
 
 
 def gdn_bwd_varlen(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=None, grads=None, stream=None,
-                   want_dh0: bool = True, saved_p=None, hT=None):
+                   want_dh0: bool = True, saved_p=None, hT=None, noalloc: bool = False):
     """Backward of gdn_fwd_varlen (see include/gdn.h).  Inputs as gdn_fwd_varlen plus
     dout [T, Hv, dv] (dtype of q) and dhT [N, Hv, dv, dk] fp32 or None.  ``workspace``
     (a uint8 device tensor of at least gdn_bwd_workspace_size bytes) and ``grads``
     (a dict of output tensors) are allocated when None.  Returns a dict of fp32
     tensors: dq, dk [T, Hk, dk]; dv [T, Hv, dv]; dg, dbeta [T, Hv]; dh0.  ``saved_p`` (and
     ``hT`` when dhT is given) from gdn_fwd_varlen_train skip the backward's own
-    forward recompute."""
+    forward recompute.  ``noalloc`` calls gdn_bwd_varlen_noalloc instead: no workspace
+    (the library's fixed per-device scratch serves), for calls that fit it; then
+    ``grads`` must be given, so that nothing at all is allocated."""
     import torch
     T, hk, dk, hv, dv, N = _dims_of(q, k, v, g, beta, cu_seqlens, require_cu=True)
+    if noalloc and (workspace is not None or grads is None):
+        raise ValueError("noalloc takes no workspace and needs preallocated grads")
     _shape(h0, "h0", (N, hv, dv, dk))
     _shape(dout, "dout", (T, hv, dv))
     _shape(dhT, "dhT", (N, hv, dv, dk))
@@ -344,6 +351,14 @@ def gdn_bwd_varlen(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=N
         _need(t, name, torch.float32)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
     dims = make_dims(q, v, N, T)
+    if noalloc:
+        for name, t in grads.items():
+            _need(t, name, torch.float32)
+        _check(lib.gdn_bwd_varlen_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                          _ptr(h0), _ptr(cu_seqlens), _ptr(dout), _ptr(dhT), _ptr(saved_p), _ptr(hT),
+                                          _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dg"]),
+                                          _ptr(grads["dbeta"]), _ptr(grads.get("dh0")), _stream_handle(stream)))
+        return grads
     if workspace is None:
         workspace = torch.empty(gdn_bwd_workspace_size(dims), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8)

@@ -28,7 +28,8 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
-                          "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_fwd_chunked",
+                          "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_bwd_varlen_noalloc",
+                          "gdn_fwd_chunked",
                           "gdn_status_string", "gdn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -497,3 +498,41 @@ def test_fwd_train_rejects(lib):
     d = _dims()
     d.pre = ctypes.pointer(gdn.make_preproc(norm_qk=True))
     assert call(d) == 6
+
+
+# ------------------------------------------------- allocation-free backward
+
+def call_bwd_noalloc(lib, dims, **over):
+    a = dict(BP)
+    a.update(over)
+    return lib.gdn_bwd_varlen_noalloc(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], a["v"],
+                                      a["g"], a["b"], a["h0"], a["cu"], a["dout"], a["dhT"], a.get("sp"), a.get("hT"),
+                                      a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dh0"], None)
+
+
+def test_noalloc_scratch_constant_matches_header(lib):
+    from invariant_linear_attention_amd import gdn
+    text = open(HEADER).read()
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", text)
+    assert int(m.group(1)) << int(m.group(2)) == gdn.GDN_NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(hv=3), 2), (dict(dk=16), 6), (dict(io_dtype=7), 3), (dict(n_seqs=0, total_tokens=3), 2),
+    (dict(n_seqs=0, total_tokens=0), 0),
+    # 1100 tokens at hv = 32, dk = dv = 128 need about 72 MB: more than the 64 MiB scratch
+    (dict(n_seqs=1, total_tokens=1100, hk=16, hv=32), 8),
+    (dict(n_seqs=40, total_tokens=40, hk=16, hv=32), 8),   # 40 final states of 2 MiB each
+])
+def test_noalloc_refuses_on_the_host(lib, case, code):
+    """Sizes are checked before any HIP call: these return without a GPU."""
+    assert call_bwd_noalloc(lib, _dims(**case)) == code
+    assert call_bwd_noalloc(lib, None) == 1
+
+
+def test_noalloc_capacity_is_the_workspace_size(lib):
+    from invariant_linear_attention_amd import gdn
+    fits = _dims(n_seqs=1, total_tokens=990, hk=16, hv=32)
+    over = _dims(n_seqs=1, total_tokens=993, hk=16, hv=32)
+    assert ws_size(lib, fits) <= gdn.GDN_NOALLOC_SCRATCH_BYTES < ws_size(lib, over)
+    assert call_bwd_noalloc(lib, over) == 8
