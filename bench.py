@@ -573,42 +573,75 @@ def main():
         checks.append((rec_b, "parity", bwd_check))
         progress("backward %.3f ms" % msb)
 
-        # The chunked form with a replaying decode (gdn_fwd_chunked): the benchmark
-        # batch as one prefill from h0, and one decode step at B = 256 through the
-        # chunked state; the same 7 dk dv flops per token as the recurrent lines.
+        # The chunked form with a replaying decode (gdn_fwd_chunked, matrix cores for the
+        # products with the state): the benchmark batch as one prefill from h0, and one
+        # in-place decode step at B = 256 from states a chunked prefill left at every
+        # position of an open chunk (512 + n % 16 tokens for sequence n); the same
+        # 7 dk dv flops per token as the recurrent lines.
         st_in = gdn.make_chunk_state(w.n_seqs, 16, 32, 128, 128, dev, h0=d["h0"])
         st_out = gdn.make_chunk_state(w.n_seqs, 16, 32, 128, 128, dev)
         och = torch.empty((T, 32, 128), dtype=torch.bfloat16, device=dev)
+        ws_c = torch.empty(gdn.gdn_chunked_workspace_size(gdn.make_dims(d["q"], d["v"], w.n_seqs, T)),
+                           dtype=torch.uint8, device=dev)
 
         def chunked(_i):
             gdn.gdn_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], st_in, st_out, out=och,
-                                stream=stream)
+                                stream=stream, workspace=ws_c)
 
         per_ch, _, _ = time_launches(chunked, args.steps, 3, stream)
         msch = float(np.median(per_ch))
-        Bc = 256
-        dwc = synth.make_workload(2000 + Bc, [1] * Bc)
-        dcd = [t.to(dev) for t in (dwc.q, dwc.k, dwc.v, dwc.g, dwc.beta, dwc.cu_seqlens)]
-        sts = [gdn.make_chunk_state(Bc, 16, 32, 128, 128, dev) for _ in range(2)]
-        for s_ in sts:
-            s_["S"].normal_(0.0, 0.1)
-            s_["count"].fill_(7)
-        ocd = torch.empty((Bc, 32, 128), dtype=torch.bfloat16, device=dev)
-
-        def chunked_dec(_i):
-            gdn.gdn_fwd_chunked(*dcd, sts[0], sts[1], out=ocd, stream=stream)
-
-        per_cd2, _, _ = time_launches(chunked_dec, args.steps, 3, stream, hold=hold, hold_ms=20.0)
         chunked(0)
         torch.cuda.synchronize()
         got_ch = och.cpu()
+        Bc = 256
+        hl = synth.make_workload(1012, [512 + n % 16 + 1 for n in range(Bc)])
+        cuh = hl.cu_seqlens.tolist()
+        pre_i = torch.cat([torch.arange(cuh[n], cuh[n + 1] - 1) for n in range(Bc)])
+        last_i = torch.tensor([cuh[n + 1] - 1 for n in range(Bc)])
+        hp = [getattr(hl, nm)[pre_i].contiguous().to(dev) for nm in ("q", "k", "v", "g", "beta")]
+        cu_p = synth.cu_from_lengths([512 + n % 16 for n in range(Bc)]).to(dev)
+        _, st_d = gdn.gdn_fwd_chunked(*hp, cu_p, None, stream=stream)
+        del hp
+        dcd = [getattr(hl, nm)[last_i].contiguous().to(dev) for nm in ("q", "k", "v", "g", "beta")]
+        cu_d = torch.arange(Bc + 1, dtype=torch.int32, device=dev)
+        ws_d = torch.empty(gdn.gdn_chunked_workspace_size(gdn.make_dims(dcd[0], dcd[2], Bc, Bc)),
+                           dtype=torch.uint8, device=dev)
+        ocd = torch.empty((Bc, 32, 128), dtype=torch.bfloat16, device=dev)
+        cnt_out = torch.empty((Bc,), dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        # the checked step first (the timed ones then repeat it in place on the same states)
+        work = {k_: v_.clone() for k_, v_ in st_d.items()}
+        gdn.gdn_fwd_chunked(*dcd, cu_d, work, out=ocd, stream=stream, workspace=ws_d, inplace=True,
+                            count_out=cnt_out)
+        torch.cuda.synchronize()
+        got_cd = ocd[:4].cpu()
+        del work
+
+        def chunked_dec(_i):
+            gdn.gdn_fwd_chunked(*dcd, cu_d, st_d, out=ocd, stream=stream, workspace=ws_d, inplace=True,
+                                count_out=cnt_out)
+
+        per_cd2, _, _ = time_launches(chunked_dec, max(args.steps, 50), 10, stream, hold=hold, hold_ms=40.0)
         rec_ch = {"tokens": T, "n_seqs": w.n_seqs, "chunk": 16, "ms_median": msch, "tokens_per_s": T / (msch / 1e3),
                   "launch_ms_percentiles": percentiles(per_ch),
                   "roofline_frac": FLOPS_PER_TOKEN * T / (msch / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
-                  "decode_B256_latency_us_mean": float(np.mean(per_cd2)) * 1e3}
+                  "decode_B256_inplace_us_mean": float(np.mean(per_cd2)) * 1e3,
+                  "decode_B256_launch_ms_percentiles": percentiles(per_cd2),
+                  "decode_states": "chunked prefill of 512 + n % 16 tokens (every open-chunk position)"}
         workloads["chunked_prefill_replay"] = rec_ch
-        del st_in, st_out, och, sts, ocd
-        progress("chunked form %.3f ms" % msch)
+        del st_in, st_out, och, st_d, ocd, ws_c, ws_d
+
+        def chunked_check():
+            ro, rh = oracle.gdn_forward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, w.h0)
+            res = {"all_heads": {"out": seq_rel_max(got_ch.float().numpy(), ro, w.cu_seqlens.tolist())}}
+            four = synth.select(hl, [0, 1, 2, 3])
+            ro4, _ = oracle.gdn_forward(four.q, four.k, four.v, four.g, four.beta, four.cu_seqlens, None)
+            c4 = four.cu_seqlens.tolist()
+            ro_last = ro4[[c4[i + 1] - 1 for i in range(4)]]
+            res["decode_B256_first4"] = {"out": seq_rel_max(got_cd.float().numpy(), ro_last, list(range(5)))}
+            return res
+        checks.append((rec_ch, "parity", chunked_check))
+        progress("chunked form %.3f ms, decode B=256 %.1f us" % (msch, float(np.mean(per_cd2)) * 1e3))
 
     # ------------------------------------------------ the benchmark step
     # W warm-up launches queued right before the K timed ones; then the timed

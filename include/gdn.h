@@ -377,47 +377,65 @@ gdn_status gdn_bwd_varlen_noalloc(const gdn_dims *dims,
  * "Finish RL Training Faster: Bitwise-Consistent, High-Performance, Agent-Driven"
  * (section "Consistency has several layers"), keeps a chunked prefill and has
  * decode replay its computation order; that needs chunk boundaries that do not
- * move, since a recurrent state carries where it was cut (the bitwise-parity
- * post on linear attention, "Why linear attention is the next wall").
+ * move, since a recurrent state carries where it was cut (the bitwise-parity post
+ * on linear attention, "Why linear attention is the next wall").
  * Here chunks are the 16-token stretches at positions 16c .. 16c+15 of a
- * sequence.  Within a chunk, with S0 its starting state, G_m = g_0 + .. + g_m,
- * Gam_m = exp(G_m) and Gam_{m,r} = exp(G_m - G_r):
+ * sequence.  Within a chunk, with S0 its starting state, a_m = exp(g_m),
+ * Gam_{m,r} = a_m a_{m-1} .. a_{r+1} (1 for r = m), Gam_m = Gam_{m,0} a_0,
+ * A[m][r] = beta_m Gam_{m,r} (k_m . k_r) (r < m) and T = (I + A)^-1:
  *
- *   u_m = beta_m (v_m - Gam_m S0 k_m) - sum_{r<m} beta_m Gam_{m,r} (k_m . k_r) u_r
+ *   R_m = beta_m (v_m - Gam_m S0 k_m),   U = T R   (u_m = R_m - sum_{r<m} A[m][r] u_r)
  *   o_m = Gam_m S0 q_m + sum_{s<=m} Gam_{m,s} (q_m . k_s) u_s
  *   chunk end:  S = Gam_15 S0 + sum_s Gam_{15,s} u_s k_s^T
  *
  * (the same rule as gdn_fwd_varlen, written from the chunk's start; results
- * agree with it to rounding, not bitwise).  Each token's arithmetic depends only
- * on S0 and its chunk's earlier tokens, so the state between calls is a
- * gdn_chunk_state, and every split of a sequence into calls -- a decode step of one
- * token included -- gives the same bits, as do batch-mates and batch order.
+ * agree with it to rounding, not bitwise).  Every product runs on the matrix cores
+ * (fp32 MFMA, fp32 accumulation).  Each token's results depend only on S0 and its
+ * chunk's tokens up to it (later tokens enter only as exact zero products, and +0
+ * is added so a zero result has one sign), so the state between calls is a
+ * gdn_chunk_state, and every split of a sequence into calls -- a decode step of
+ * one token included -- gives the same bits, as do batch-mates and batch order.
+ * Non-finite inputs are the exception: since 0 x NaN is NaN, a NaN or infinity in
+ * a token reaches the outputs of its whole 16-token chunk (never an earlier chunk
+ * or another sequence), and a decode step, which has not seen the later tokens,
+ * then differs from a prefill of the chunk.
  *
  *   in   : the sequences' chunked states, or NULL for empty ones (zero state, no
  *          open chunk).  A state with S = h0 and count = 0 starts from h0.
- *   out  : where the new chunked states go (all five arrays).  in and out must not
- *          overlap (call with two buffers and swap).
+ *   out  : where the new chunked states go (all six arrays).  out may share S, k,
+ *          r, a and b with in (the same five pointers: an in-place update, which
+ *          then writes S only when a chunk closes) when every sequence of the call
+ *          has exactly one token (total_tokens == n_seqs, a decode step); the count
+ *          arrays must always differ.  Any other overlap is GDN_ERR_ALIAS.
  *   o    : [T][hv][dv] outputs, io dtype.
- * dk must be 64 or 128 and dv a multiple of 32 (else GDN_ERR_UNSUPPORTED, as are
- * dims->pre and plan fields).  Errors as gdn_fwd_varlen (S and k of both states
- * 16-byte aligned; u, G, count 4-byte); a count outside 0..15 is clamped on the
- * device.
+ *   workspace : device scratch of at least gdn_chunked_workspace_size bytes,
+ *          16-byte aligned, owned by the caller; its contents on entry do not
+ *          matter.  About 2.3 KB per (chunk touched, value head).
+ * dk must be 64 or 128, dv a multiple of 16 and hv / hk at most 16 (else
+ * GDN_ERR_UNSUPPORTED, as are dims->pre, plan_lanes and plan_rows).  plan_waves (0 = automatic, else 1, 2 or
+ * 4) is how many waves share one 16-row state tile, each holding a part of its
+ * dk columns; it never changes a bit.  Errors as gdn_fwd_varlen (S and k of both
+ * states 16-byte aligned; r, a, b, count 4-byte); a count outside 0..15 is clamped
+ * on the device.
  */
 enum { GDN_CHUNK = 16 };
 
 typedef struct gdn_chunk_state {
     float *S;        /* [N][hv][dv][dk] fp32: state at the start of the open chunk */
     float *k;        /* [N][16][hk][dk] fp32: keys of the open chunk's tokens */
-    float *u;        /* [N][16][hv][dv] fp32: their write vectors u */
-    float *G;        /* [N][16][hv]     fp32: cumulative log decay within the chunk */
+    float *r;        /* [N][16][hv][dv] fp32: their R rows beta (v - Gam S0 k) */
+    float *a;        /* [N][16][hv]     fp32: their decay factors exp(g) */
+    float *b;        /* [N][16][hv]     fp32: their betas */
     int32_t *count;  /* [N]             tokens in the open chunk, 0 .. 15 */
 } gdn_chunk_state;
+
+gdn_status gdn_chunked_workspace_size(const gdn_dims *dims, uint64_t *bytes);
 
 gdn_status gdn_fwd_chunked(const gdn_dims *dims,
                            const void *q, const void *k, const void *v,
                            const float *g, const float *beta, const int32_t *cu_seqlens,
                            const gdn_chunk_state *in, const gdn_chunk_state *out,
-                           void *o, void *stream);
+                           void *o, void *workspace, uint64_t workspace_bytes, void *stream);
 
 /* Human-readable description of a status code (static storage; an unknown code
  * gives "unknown gdn_status").  Every refusal is reported as one of these codes rather than
@@ -430,7 +448,7 @@ const char *gdn_status_string(gdn_status status);
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 205
+#define GDN_ABI_VERSION 207
 
 #ifdef __cplusplus
 }

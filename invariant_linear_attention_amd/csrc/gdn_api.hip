@@ -544,56 +544,89 @@ gdn_status gdn_bwd_varlen_noalloc(const gdn_dims *dims, const void *q, const voi
                            dh0, ptr, (uint64_t)GDN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+gdn_status gdn_chunked_workspace_size(const gdn_dims *dims, uint64_t *bytes) {
+    using namespace gdn;
+    if (!bytes) return GDN_ERR_NULL;
+    const gdn_status st = check_common(dims);
+    if (st != GDN_OK) return st;
+    *bytes = (uint64_t)chunk_ws_slots(dims->total_tokens, dims->n_seqs) * dims->hv * kChunkRec * 4;
+    return GDN_OK;
+}
+
 gdn_status gdn_fwd_chunked(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
                            const float *beta, const int32_t *cu_seqlens, const gdn_chunk_state *in,
-                           const gdn_chunk_state *out, void *o, void *stream) {
+                           const gdn_chunk_state *out, void *o, void *workspace, uint64_t workspace_bytes,
+                           void *stream) {
     using namespace gdn;
     gdn_status st = check_common(dims);
     if (st != GDN_OK) return st;
     const gdn_dims &d = *dims;
-    if (d.pre || d.plan_lanes || d.plan_rows || d.plan_waves) return GDN_ERR_UNSUPPORTED;
-    if ((d.dk != 64 && d.dk != 128) || d.dv % 32 != 0) return GDN_ERR_UNSUPPORTED;
+    if (d.pre || d.plan_lanes || d.plan_rows) return GDN_ERR_UNSUPPORTED;
+    if (d.plan_waves != 0 && d.plan_waves != 1 && d.plan_waves != 2 && d.plan_waves != 4) return GDN_ERR_UNSUPPORTED;
+    if ((d.dk != 64 && d.dk != 128) || d.dv % 16 != 0 || d.hv / d.hk > 16) return GDN_ERR_UNSUPPORTED;
     const int64_t T = d.total_tokens, N = d.n_seqs;
     if (N == 0) return T == 0 ? GDN_OK : GDN_ERR_SHAPE;
-    if (!cu_seqlens || !out || !out->S || !out->k || !out->u || !out->G || !out->count) return GDN_ERR_NULL;
+    if (!cu_seqlens || !out || !out->S || !out->k || !out->r || !out->a || !out->b || !out->count || !workspace)
+        return GDN_ERR_NULL;
     if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
-    // an incoming state with an open chunk needs its k, u and G
-    if (in && in->count && (!in->k || !in->u || !in->G)) return GDN_ERR_NULL;
-    if (N * d.hv * (int64_t)(d.dv / 32) > 0x7FFFFFFFll) return GDN_ERR_SHAPE;
+    // an incoming state with an open chunk needs its k, r, a and b
+    if (in && in->count && (!in->k || !in->r || !in->a || !in->b)) return GDN_ERR_NULL;
+    const int64_t slots = chunk_ws_slots(T, N);
+    if (workspace_bytes < (uint64_t)slots * d.hv * kChunkRec * 4) return GDN_ERR_SHAPE;
+    if (slots > 0x7FFFFFFFll || N * d.hv * (int64_t)(d.dv / 16) > 0x7FFFFFFFll) return GDN_ERR_SHAPE;
 
     const uint64_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
     const uint64_t s_bytes = (uint64_t)N * d.hv * d.dv * d.dk * 4;
     const uint64_t k_bytes = (uint64_t)N * GDN_CHUNK * d.hk * d.dk * 4;
-    const uint64_t u_bytes = (uint64_t)N * GDN_CHUNK * d.hv * d.dv * 4;
-    const uint64_t G_bytes = (uint64_t)N * GDN_CHUNK * d.hv * 4, c_bytes = (uint64_t)N * 4;
+    const uint64_t r_bytes = (uint64_t)N * GDN_CHUNK * d.hv * d.dv * 4;
+    const uint64_t a_bytes = (uint64_t)N * GDN_CHUNK * d.hv * 4, c_bytes = (uint64_t)N * 4;
     const gdn_chunk_state none{};
     const gdn_chunk_state &i = in ? *in : none;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(g, 4) ||
         !aligned(beta, 4) || !aligned(cu_seqlens, 4) || !aligned(out->S, 16) || !aligned(out->k, 16) ||
-        !aligned(out->u, 4) || !aligned(out->G, 4) || !aligned(out->count, 4) || !aligned(i.S, 16) ||
-        !aligned(i.k, 16) || !aligned(i.u, 4) || !aligned(i.G, 4) || !aligned(i.count, 4))
+        !aligned(out->r, 4) || !aligned(out->a, 4) || !aligned(out->b, 4) || !aligned(out->count, 4) ||
+        !aligned(i.S, 16) || !aligned(i.k, 16) || !aligned(i.r, 4) || !aligned(i.a, 4) || !aligned(i.b, 4) ||
+        !aligned(i.count, 4) || !aligned(workspace, 16))
         return GDN_ERR_ALIGN;
+    // in place: the same S, k, r, a and b arrays, one token per sequence, distinct counts
+    const bool inplace = in && i.S == out->S && i.k == out->k && i.r == out->r && i.a == out->a && i.b == out->b;
+    if (inplace && (T != N || i.count == out->count)) return GDN_ERR_ALIAS;
     const uint64_t qk_n = (uint64_t)T * d.hk * d.dk, vo_n = (uint64_t)T * d.hv * d.dv;
+    const Range ws = range_of(workspace, (uint64_t)slots * d.hv * kChunkRec * 4);
     const Range inputs[] = {range_of(q, qk_n * esz), range_of(k, qk_n * esz), range_of(v, vo_n * esz),
                             range_of(g, (uint64_t)T * d.hv * 4), range_of(beta, (uint64_t)T * d.hv * 4),
-                            range_of(cu_seqlens, (uint64_t)(N + 1) * 4), range_of(i.S, i.S ? s_bytes : 0),
-                            range_of(i.k, i.k ? k_bytes : 0), range_of(i.u, i.u ? u_bytes : 0),
-                            range_of(i.G, i.G ? G_bytes : 0), range_of(i.count, i.count ? c_bytes : 0)};
+                            range_of(cu_seqlens, (uint64_t)(N + 1) * 4),
+                            range_of(inplace ? nullptr : i.S, i.S ? s_bytes : 0),
+                            range_of(inplace ? nullptr : i.k, i.k ? k_bytes : 0),
+                            range_of(inplace ? nullptr : i.r, i.r ? r_bytes : 0),
+                            range_of(inplace ? nullptr : i.a, i.a ? a_bytes : 0),
+                            range_of(inplace ? nullptr : i.b, i.b ? a_bytes : 0),
+                            range_of(i.count, i.count ? c_bytes : 0)};
     const Range outputs[] = {range_of(o, vo_n * esz), range_of(out->S, s_bytes), range_of(out->k, k_bytes),
-                             range_of(out->u, u_bytes), range_of(out->G, G_bytes), range_of(out->count, c_bytes)};
-    for (size_t a = 0; a < sizeof(outputs) / sizeof(outputs[0]); ++a) {
+                             range_of(out->r, r_bytes), range_of(out->a, a_bytes), range_of(out->b, a_bytes),
+                             range_of(out->count, c_bytes), ws};
+    for (size_t x = 0; x < sizeof(outputs) / sizeof(outputs[0]); ++x) {
         for (const Range &r : inputs)
-            if (overlap(outputs[a], r)) return GDN_ERR_ALIAS;
-        for (size_t b = a + 1; b < sizeof(outputs) / sizeof(outputs[0]); ++b)
-            if (overlap(outputs[a], outputs[b])) return GDN_ERR_ALIAS;
+            if (overlap(outputs[x], r)) return GDN_ERR_ALIAS;
+        for (size_t y = x + 1; y < sizeof(outputs) / sizeof(outputs[0]); ++y)
+            if (overlap(outputs[x], outputs[y])) return GDN_ERR_ALIAS;
     }
 
     ChunkedParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.cu_seqlens = cu_seqlens;
-    p.in_S = i.S; p.in_k = i.k; p.in_u = i.u; p.in_G = i.G; p.in_count = i.count;
-    p.out_S = out->S; p.out_k = out->k; p.out_u = out->u; p.out_G = out->G; p.out_count = out->count;
+    p.in_S = i.S; p.in_k = i.k; p.in_r = i.r; p.in_a = i.a; p.in_b = i.b; p.in_count = i.count;
+    p.out_S = out->S; p.out_k = out->k; p.out_r = out->r; p.out_a = out->a; p.out_b = out->b;
+    p.out_count = out->count;
     p.out = o;
+    p.ws = static_cast<float *>(workspace);
+    p.ws_slots = slots;
     p.total_tokens = T; p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dk = d.dk; p.dv = d.dv;
+    p.rank_by_length = (N > 1 && N <= kMaxRankedSeqs && T >= 32 * N) ? 1 : 0;
+    p.inplace = inplace ? 1 : 0;
+    // Waves per 16-row tile: split the dk quarters over more waves when the call
+    // has few tiles to spread over the chip's 1024 SIMDs (never changes a bit).
+    const int64_t units = N * d.hv * (int64_t)(d.dv / 16);
+    p.waves = d.plan_waves ? d.plan_waves : (units < 1024 ? 4 : (units <= 4096 ? 2 : 1));
     const hipError_t e = launch_chunked(p, d.io_dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

@@ -1,5 +1,5 @@
-// gdn_chunked.hip -- the chunked form of the gated delta rule with a decode that
-// replays it (gdn_fwd_chunked).
+// gdn_chunked.hip -- the chunked form of the gated delta rule on the matrix cores,
+// with a decode that replays it (gdn_fwd_chunked).
 //
 // The page "Defending Against the Training-Inference Numeric Mismatch in RL
 // (Especially Linear Attention)" (section 3.2) makes prefill and decode agree by
@@ -11,22 +11,42 @@
 // "Why linear attention is the next wall").  This file is that design.
 //
 // Chunks are the 16-token stretches of a sequence at positions 16c .. 16c + 15.
-// Within a chunk, with S0 the state at its start, G_m = g_0 + ... + g_m (cumulative
-// log decay, slot order), Gam_m = exp(G_m) and Gam_{m,r} = exp(G_m - G_r):
+// Within a chunk, with S0 the state at its start and a_m = exp(g_m):
 //
-//     w_m = S0 k_m,   z_m = S0 q_m                                  (row dots)
-//     u_m = beta_m (v_m - Gam_m w_m) - sum_{r<m} beta_m Gam_{m,r} (k_m . k_r) u_r
-//     o_m = Gam_m z_m + sum_{s<=m} Gam_{m,s} (q_m . k_s) u_s
-//     at the chunk's end:  S = Gam_15 S0 + sum_{s} Gam_{15,s} u_s k_s^T
+//     Gam_{m,r} = a_m a_{m-1} ... a_{r+1}   (r < m; 1 for r = m),   Gam_m = Gam_{m,0} a_0
+//     P_m = S0 k_m,   Z_m = S0 q_m,   R_m = beta_m (v_m - Gam_m P_m)
+//     A[m][r] = beta_m Gam_{m,r} (k_m . k_r)  (r < m),   T = (I + A)^-1   (unit lower triangular)
+//     U = T R            (so u_m = R_m - sum_{r<m} A[m][r] u_r)
+//     O = Gam Z + B U,   B[m][s] = Gam_{m,s} (q_m . k_s)  (s <= m)
+//     at the chunk's end:  S = Gam_15 S0 + sum_s Gam_{15,s} u_s k_s^T
 //
 // which is the recurrence S_m = a_m S_{m-1} + u_m k_m^T, o_m = S_m q_m written from
-// the chunk's start (S_m = Gam_m S0 + sum_{s<=m} Gam_{m,s} u_s k_s^T).  Every
-// quantity of token m depends only on S0 and the chunk's tokens up to m, each with
-// one fixed sequence of fp32 operations.  The state between calls is therefore S0
-// plus the open chunk's k, u and G (and its token count), and any split of a
-// sequence into calls, a decode step of one token included, gives the same bits.
+// the chunk's start (the WY form of the delta rule's products).  Every product with
+// the state, U, O, the chunk-end update and the key/query Gram tiles run as fp32 MFMA
+// (v_mfma_f32_16x16x4f32, fp32 accumulation); T comes from a per-column forward
+// substitution in a separate, fully parallel kernel, so a chunk's walk has no serial
+// vector chain.
+//
+// Fixed arithmetic.  Every quantity is one fixed sequence of operations whatever the
+// batch, the launch or the split of a sequence into calls:
+//   * an MFMA dot over dk is the chain of instructions t = 0 .. dk/16-1, i = 0 .. 3,
+//     instruction (t, i) adding the products of columns 16t + 4g + i, g = 0..3; an
+//     output element depends only on its own row and column of the operands, so a
+//     decode step that holds one token in its tile forms that token's bits;
+//   * a product over the chunk's tokens (U, O, the chunk-end update) is the chain of
+//     instructions r = 0..3, instruction r adding the tokens 4g + r, g = 0..3.  T and
+//     B are zero above the diagonal, so a later token enters an earlier token's
+//     result only as exact zero products; a decode step holds zeros for the tokens it
+//     has not seen, the sums agree, and +0 is added to U and O so that an exactly
+//     zero result has one sign.  (A NaN or infinity in a token therefore reaches the
+//     earlier tokens of its chunk, 0 x NaN being NaN; finite inputs replay exactly.)
+//   * Gam products, the coefficient tables and T are fixed-order fp32 chains.
+// The state between calls is S0 plus the open chunk's keys, R rows, decay factors
+// and betas (and its token count); a decode step runs the same two kernels.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "gdn_internal.hpp"
 #include "gdn_kernels.hpp"
@@ -36,231 +56,595 @@
 namespace gdn {
 namespace {
 
-constexpr int kCk = kChunkLen;       // tokens per chunk (16)
-constexpr int kChLanes = 8;          // lanes per state row
-constexpr int kChWaves = 4;
-constexpr int kChRows = kChWaves * (64 / kChLanes);  // rows per workgroup (32)
-constexpr int kChThreads = kChWaves * 64;
+constexpr int kCk = kChunkLen;   // tokens per chunk (16)
 
-template <int DK>
-struct alignas(16) ChunkLds {
-    float k[kCk][DK];       // keys of the chunk's slots (cached or new)
-    float q[kCk][DK];       // queries of the new slots
-    float v[kCk][kChRows];  // values of this tile's rows
-    float ckk[kCk][kCk];    // beta_m Gam_{m,r} (k_m . k_r), r < m
-    float cqk[kCk][kCk];    // Gam_{m,s} (q_m . k_s), s <= m
-    float cst[kCk];         // Gam_{15,s}: weights of the chunk-end state update
-    float G[kCk];           // cumulative log decay of each slot
-    float gam[kCk];         // Gam_m
-    float beta[kCk];
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// D = C + A B on a 16 x 16 x 4 fp32 tile.  Lane l = x + 16 g supplies A[x][g] and
+// B[g][x]; it receives D[4 g + r][x] in component r.
+__device__ __forceinline__ f4 mfma_16x16x4(float a, float b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f4 f4_zero() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not
+// for its global loads (__syncthreads also fences global memory, which would make
+// every chunk wait for the reads it has just sent out for the next one).  The
+// memory clobber keeps the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Clamped sequence bounds and chunk bookkeeping shared by both kernels.
+struct SeqChunks {
+    int64_t tb, len;  // first token of the sequence in this call, tokens in this call
+    int c0;           // tokens already in the open chunk (from the incoming state)
+    int nch;          // chunks this call touches
+    int64_t base;     // first workspace slot of the sequence
 };
 
-// LDS position (in 4-float chunks) of lane lam's j-th 4-column chunk of a key or
-// query row.  With 16 columns per lane (dk = 128) the j-th chunks of lanes lam and
-// lam + 4 would share banks, so those lanes keep their chunks in a rotated order.
-template <int DK>
-__device__ __forceinline__ int ch_slot(int lam, int j) {
-    constexpr int CH = DK / kChLanes / 4;
-    if constexpr (CH == 4) return lam * CH + ((j + (lam >> 2)) & 3);
-    else return lam * CH + j;
+__device__ __forceinline__ int64_t clamp_tok(int64_t x, int64_t T) { return x < 0 ? 0 : (x > T ? T : x); }
+
+__device__ __forceinline__ SeqChunks seq_chunks(const ChunkedParams &p, int n) {
+    SeqChunks s;
+    s.tb = clamp_tok(p.cu_seqlens[n], p.total_tokens);
+    int64_t te = clamp_tok(p.cu_seqlens[n + 1], p.total_tokens);
+    te = te < s.tb ? s.tb : te;
+    s.len = te - s.tb;
+    int c0 = p.in_count ? p.in_count[n] : 0;
+    s.c0 = c0 < 0 ? 0 : (c0 > kCk - 1 ? kCk - 1 : c0);
+    s.nch = s.len > 0 ? (int)((s.c0 + s.len + kCk - 1) / kCk) : 0;
+    s.base = chunk_slot_base(s.tb, n);
+    return s;
 }
 
-// This lane's C columns of an LDS key/query row (chunk offsets lch).
-template <int C>
-__device__ __forceinline__ void load_cols(float (&dst)[C], const float *row, const int (&lch)[C / 4]) {
-#pragma unroll
-    for (int j = 0; j < C / 4; ++j) {
-        const float4 x = *reinterpret_cast<const float4 *>(row + lch[j]);
-        dst[4 * j] = x.x; dst[4 * j + 1] = x.y; dst[4 * j + 2] = x.z; dst[4 * j + 3] = x.w;
-    }
-}
-
-template <int C>
-__device__ __forceinline__ float chunk_lane_dot(const float (&x)[C], const float (&y)[C]) {
-    constexpr int K = C >= 16 ? 4 : (C >= 8 ? 2 : 1);
-    float acc[K];
-#pragma unroll
-    for (int c = 0; c < K; ++c) acc[c] = x[c] * y[c];
-#pragma unroll
-    for (int c = K; c < C; ++c) acc[c % K] = __builtin_fmaf(x[c], y[c], acc[c % K]);
-    if constexpr (K == 1) return acc[0];
-    else if constexpr (K == 2) return acc[0] + acc[1];
-    else return (acc[0] + acc[1]) + (acc[2] + acc[3]);
-}
-
-// One workgroup = (sequence n, value head h, tile of 32 state rows).
+// ------------------------------------------------------------------- prep kernel
+//
+// One workgroup (256 threads) per (workspace slot, key head).  It stages the chunk's
+// keys (cached and new) and new queries, forms the Gram tiles K K^T and Q K^T with
+// MFMA (waves 0 and 1), then for each value head of the key head writes the record
+// the main kernel reads: A[m][r] = (beta_m Gam_{m,r}) (k_m . k_r) for r < m,
+// B[m][s] = Gam_{m,s} (q_m . k_s) for s <= m (rows of the chunk's new tokens only),
+// Gam_m, the chunk-end weights Gam_{15,s} and the decay factors a_m.
 template <int DK, class IO>
-__global__ __launch_bounds__(kChThreads) void gdn_chunked_kernel(ChunkedParams p) {
-    constexpr int C = DK / kChLanes;
-    __shared__ ChunkLds<DK> Ld;
+__global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(ChunkedParams p) {
+    constexpr int NT = DK / 16;
+    constexpr int KP = DK + 4;  // padded LDS row
+    __shared__ float Ks[kCk][KP];
+    __shared__ float Qs[kCk][KP];
+    __shared__ float kap[kCk][kCk + 1];
+    __shared__ float xi[kCk][kCk + 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lam = lane % kChLanes, grp = lane / kChLanes;
-    const int tiles = p.dv / kChRows;
-    const int tile = blockIdx.x % tiles;
-    const int h = (blockIdx.x / tiles) % p.hv;
-    const int n = blockIdx.x / (tiles * p.hv);
-    const int G_ = p.hv / p.hk;
-    const int kh = h / G_;
-    const int lrow = wave * (64 / kChLanes) + grp;
-    const int row = tile * kChRows + lrow;
-    const int col0 = lam * C;
-    int lch[C / 4];  // LDS float offsets of this lane's column chunks in a key/query row
-#pragma unroll
-    for (int j = 0; j < C / 4; ++j) lch[j] = 4 * ch_slot<DK>(lam, j);
-    // where 4-column chunk c4 of a row is kept (the inverse view of lch, for staging)
-    auto stage_off = [](int c4) { return 4 * ch_slot<DK>((4 * c4) / C, ((4 * c4) % C) / 4); };
+    const int64_t slot = blockIdx.x;
+    const int kh = blockIdx.y;
+    const int tid = threadIdx.x;
+    // The sequence owning this slot: the last n with base(n) <= slot.
+    int lo = 0, hi = p.n_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (chunk_slot_base(clamp_tok(p.cu_seqlens[mid], p.total_tokens), mid) <= slot)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int n = lo;
+    const SeqChunks sc = seq_chunks(p, n);
+    const int64_t j = slot - sc.base;
+    if (j < 0 || j >= sc.nch || slot >= p.ws_slots) return;  // uniform over the workgroup
+    const int m0 = j == 0 ? sc.c0 : 0;
+    const int64_t left = sc.c0 + sc.len - kCk * j;
+    const int m1 = left < kCk ? (int)left : kCk;
+    const int64_t t0 = sc.tb + kCk * j - sc.c0;  // token index of chunk position 0
 
-    int64_t tb = p.cu_seqlens[n], te = p.cu_seqlens[n + 1];
-    tb = tb < 0 ? 0 : (tb > p.total_tokens ? p.total_tokens : tb);
-    te = te < tb ? tb : (te > p.total_tokens ? p.total_tokens : te);
-    const int64_t len = te - tb;
-
-    // incoming state: S0 rows, the open chunk's count, u (this row), k and G
-    int m0 = 0;
-    if (p.in_count) {
-        m0 = p.in_count[n];
-        m0 = m0 < 0 ? 0 : (m0 >= kCk ? kCk - 1 : m0);
+    // One round of reads: the chunk's key rows (cached and new) and new query rows,
+    // and the decay factors and betas of every value head of this key head.
+    constexpr int kMaxG = 16;  // value heads per key head handled per workgroup (host-checked)
+    __shared__ float decs[kMaxG][kCk], bets[kMaxG][kCk];
+    const int G = p.hv / p.hk;
+    for (int it = tid; it < kCk * (DK / 4); it += 256) {
+        const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+        if (m < m1) {
+            if (m < m0) {  // cached key of the open chunk (fp32)
+                kv = *reinterpret_cast<const float4 *>(p.in_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + c);
+            } else {
+                const size_t e = ((size_t)(t0 + m) * p.hk + kh) * DK + c;
+                kv = IO::load4(p.k, e);
+                qv = IO::load4(p.q, e);
+            }
+        }
+        *reinterpret_cast<float4 *>(&Ks[m][c]) = kv;
+        *reinterpret_cast<float4 *>(&Qs[m][c]) = qv;
     }
-    const size_t sbase = (((size_t)n * p.hv + h) * p.dv + row) * DK + col0;
-    float X[C];
-#pragma unroll
-    for (int c = 0; c < C; c += 4) {
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (p.in_S) x = *reinterpret_cast<const float4 *>(p.in_S + sbase + c);
-        X[c] = x.x; X[c + 1] = x.y; X[c + 2] = x.z; X[c + 3] = x.w;
+    for (int it = tid; it < G * kCk; it += 256) {
+        const int gi = it / kCk, m = it % kCk, h = kh * G + gi;
+        float a = 0.f, b = 0.f;
+        if (m < m1) {
+            if (m < m0) {
+                a = p.in_a[((size_t)n * kCk + m) * p.hv + h];
+                b = p.in_b[((size_t)n * kCk + m) * p.hv + h];
+            } else {
+                a = decay_factor(p.g[(size_t)(t0 + m) * p.hv + h]);
+                b = p.beta[(size_t)(t0 + m) * p.hv + h];
+            }
+        }
+        decs[gi][m] = a;
+        bets[gi][m] = b;
     }
-    float ureg[kCk];
-#pragma unroll
-    for (int m = 0; m < kCk; ++m) {
-        ureg[m] = 0.f;
-        if (m < m0) ureg[m] = p.in_u[(((size_t)n * kCk + m) * p.hv + h) * p.dv + row];
-    }
-    for (int idx = tid; idx < m0 * (DK / 4); idx += kChThreads) {
-        const int m = idx / (DK / 4), c4 = idx % (DK / 4);
-        *reinterpret_cast<float4 *>(&Ld.k[m][stage_off(c4)]) =
-            *reinterpret_cast<const float4 *>(p.in_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + 4 * c4);
-    }
-    if (tid < m0) Ld.G[tid] = p.in_G[((size_t)n * kCk + tid) * p.hv + h];
     __syncthreads();
 
-    int ms = m0;            // first open slot of the current chunk
-    int64_t done = 0;       // tokens of this call processed
-    while (done < len) {
-        const int take = (int)((len - done) < (int64_t)(kCk - ms) ? (len - done) : (kCk - ms));
-        const int me = ms + take;                // slots [ms, me) are new tokens
-        const int64_t t_of_slot0 = tb + done - ms;  // token index of slot 0
-
-        // ---- stage the new slots
-        for (int idx = tid; idx < take * (DK / 4); idx += kChThreads) {
-            const int m = ms + idx / (DK / 4), c4 = idx % (DK / 4);
-            const size_t qk = ((size_t)(t_of_slot0 + m) * p.hk + kh) * DK + 4 * c4;
-            *reinterpret_cast<float4 *>(&Ld.k[m][stage_off(c4)]) = IO::load4(p.k, qk);
-            *reinterpret_cast<float4 *>(&Ld.q[m][stage_off(c4)]) = IO::load4(p.q, qk);
-        }
-        for (int idx = tid; idx < take * kChRows; idx += kChThreads) {
-            const int m = ms + idx / kChRows, r = idx % kChRows;
-            Ld.v[m][r] = IO::load1(p.v, ((size_t)(t_of_slot0 + m) * p.hv + h) * p.dv + tile * kChRows + r);
-        }
-        if (wave == 0) {  // cumulative log decay, added in slot order (lane j holds g of slot ms + j)
-            const float gj = lane < take ? p.g[(size_t)(t_of_slot0 + ms + lane) * p.hv + h] : 0.f;
-            float acc = ms > 0 ? Ld.G[ms - 1] : 0.f;
-            for (int j = 0; j < take; ++j) {
-                acc = acc + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gj), j));
-                if (lane == j) Ld.G[ms + j] = acc;
-            }
-        }
-        if (tid < take) Ld.beta[ms + tid] = p.beta[(size_t)(t_of_slot0 + ms + tid) * p.hv + h];
-        __syncthreads();
-
-        // ---- coefficient tables of the new slots: each entry's dot is spread over the
-        // 8 lanes of a group (C columns each, then the lane tree), 32 groups per
-        // workgroup; entry e = (m, r) of the (take x 16) table.
-        for (int e0 = 0; e0 < take * kCk; e0 += kChThreads / kChLanes) {
-            const int e = e0 + tid / kChLanes;
-            const int m = ms + e / kCk, r = e % kCk;
-            const bool live = e < take * kCk && r <= m;
-            float kv[C], km[C], qm[C];
-            load_cols<C>(kv, Ld.k[live ? r : 0], lch);
-            load_cols<C>(km, Ld.k[live ? m : 0], lch);
-            load_cols<C>(qm, Ld.q[live ? m : 0], lch);
-            const float dkk = lane_sum<kChLanes>(chunk_lane_dot<C>(kv, km));
-            const float dqk = lane_sum<kChLanes>(chunk_lane_dot<C>(kv, qm));
-            if (live && lam == 0) {
-                const float gm = decay_factor(Ld.G[m] - Ld.G[r]);
-                if (r < m) Ld.ckk[m][r] = Ld.beta[m] * gm * dkk;
-                Ld.cqk[m][r] = gm * dqk;
-            }
-        }
-        if (tid < take) Ld.gam[ms + tid] = decay_factor(Ld.G[ms + tid]);
-        if (me == kCk && tid < kCk) Ld.cst[tid] = decay_factor(Ld.G[kCk - 1] - Ld.G[tid]);
-        __syncthreads();
-
-        // ---- the new slots, in order (unrolled over the 16 slots, guarded)
+    const int wave = tid >> 6, lane = tid & 63, x = lane & 15, g = lane >> 4;
+    if (wave < 2) {
+        // wave 0: kap = K K^T, wave 1: xi = Q K^T  (A rows from K or Q, B rows from K)
+        const float(*Arows)[KP] = wave == 0 ? Ks : Qs;
+        f4 acc = f4_zero();
 #pragma unroll
-        for (int m = 0; m < kCk; ++m) {
-            if (m < ms || m >= me) continue;
-            float km[C], qm[C];
-            load_cols<C>(km, Ld.k[m], lch);
-            load_cols<C>(qm, Ld.q[m], lch);
-            const float w = lane_sum<kChLanes>(chunk_lane_dot<C>(X, km));
-            const float z = lane_sum<kChLanes>(chunk_lane_dot<C>(X, qm));
-            float u = Ld.beta[m] * (Ld.v[m][lrow] - Ld.gam[m] * w);
-#pragma unroll
-            for (int r = 0; r < m; ++r) u = __builtin_fmaf(-Ld.ckk[m][r], ureg[r], u);
-            ureg[m] = u;
-            float o = Ld.gam[m] * z;
-#pragma unroll
-            for (int s = 0; s <= m; ++s) o = __builtin_fmaf(Ld.cqk[m][s], ureg[s], o);
-            if (lam == 0) IO::store1(p.out, ((size_t)(t_of_slot0 + m) * p.hv + h) * p.dv + row, o);
+        for (int t = 0; t < NT; ++t) {
+            const float4 a4 = *reinterpret_cast<const float4 *>(&Arows[x][16 * t + 4 * g]);
+            const float4 b4 = *reinterpret_cast<const float4 *>(&Ks[x][16 * t + 4 * g]);
+            acc = mfma_16x16x4(a4.x, b4.x, acc);
+            acc = mfma_16x16x4(a4.y, b4.y, acc);
+            acc = mfma_16x16x4(a4.z, b4.z, acc);
+            acc = mfma_16x16x4(a4.w, b4.w, acc);
         }
-
-        // ---- chunk complete: fold it into the state
-        if (me == kCk) {
-            const float g15 = Ld.gam[kCk - 1];
+        float(*dst)[kCk + 1] = wave == 0 ? kap : xi;
 #pragma unroll
-            for (int c = 0; c < C; ++c) X[c] = g15 * X[c];
-#pragma unroll
-            for (int s = 0; s < kCk; ++s) {
-                const float cs = Ld.cst[s] * ureg[s];
-                float ks[C];
-                load_cols<C>(ks, Ld.k[s], lch);
-#pragma unroll
-                for (int c = 0; c < C; ++c) X[c] = __builtin_fmaf(cs, ks[c], X[c]);
-            }
-        }
-        done += take;
-        ms = me == kCk ? 0 : me;
-        __syncthreads();
+        for (int r = 0; r < 4; ++r) dst[4 * g + r][x] = acc[r];
     }
 
-    // ---- outgoing state: S0 of the open chunk, its count, k, u and G
+    __shared__ float Am[kCk][kCk + 1];
+    const int m = tid / kCk, r = tid % kCk;
+    for (int gi = 0; gi < G; ++gi) {
+        const int h = kh * G + gi;
+        __syncthreads();  // Gram tiles written; Am free again
+        const float *dec = decs[gi], *bet = bets[gi];
+        // Gam_{m,r} = a_m a_{m-1} ... a_{r+1}, left to right (1 for r >= m); the
+        // factors come from registers, s descending, each taken when r < s <= m
+        float dreg[kCk];
 #pragma unroll
-    for (int c = 0; c < C; c += 4)
-        *reinterpret_cast<float4 *>(p.out_S + sbase + c) = make_float4(X[c], X[c + 1], X[c + 2], X[c + 3]);
-    const int mo = ms;  // tokens in the open chunk after this call
+        for (int s = 0; s < kCk; ++s) dreg[s] = dec[s];
+        float gmr = 1.f;
 #pragma unroll
-    for (int m = 0; m < kCk; ++m)
-        if (m < mo && lam == 0) p.out_u[(((size_t)n * kCk + m) * p.hv + h) * p.dv + row] = ureg[m];
-    if (tile == 0 && h % G_ == 0)
-        for (int idx = tid; idx < mo * (DK / 4); idx += kChThreads) {
-            const int m = idx / (DK / 4), c4 = idx % (DK / 4);
-            *reinterpret_cast<float4 *>(p.out_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + 4 * c4) =
-                *reinterpret_cast<const float4 *>(&Ld.k[m][stage_off(c4)]);
+        for (int s = kCk - 1; s >= 0; --s) gmr = (s <= m && s > r) ? gmr * dreg[s] : gmr;
+        const bool row = m < m1;
+        Am[m][r] = (row && r < m) ? (bet[m] * gmr) * kap[m][r] : 0.f;
+        const bool newrow = m >= m0 && m < m1;
+        float *rec = p.ws + ((size_t)slot * p.hv + h) * kChunkRec;
+        rec[kRecB + m * kCk + r] = (newrow && r <= m) ? gmr * xi[m][r] : 0.f;
+        if (r == 0) rec[kRecGam + m] = row ? gmr * dreg[0] : 0.f;
+        if (m == kCk - 1) rec[kRecD + r] = gmr;
+        if (r == 0) {
+            rec[kRecDecay + m] = dec[m];
+            rec[kRecBeta + m] = bet[m];
         }
-    if (tile == 0 && tid < mo) p.out_G[((size_t)n * kCk + tid) * p.hv + h] = Ld.G[tid];
-    if (tile == 0 && h == 0 && tid == 0) p.out_count[n] = mo;
+        __syncthreads();
+        // T = (I + A)^-1 by columns: lane k of wave 0 walks column k,
+        // T[m][k] = -(sum_{r=k}^{m-1} A[m][r] T[r][k]) (r ascending), T[k][k] = 1.
+        if (tid < kCk) {
+            const int k = tid;
+            float col[kCk];
+#pragma unroll
+            for (int mm = 0; mm < kCk; ++mm) {
+                float acc = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < mm; ++rr)
+                    if (rr >= k) acc = __builtin_fmaf(Am[mm][rr], col[rr], acc);
+                col[mm] = mm < k ? 0.f : (mm == k ? 1.f : -acc);
+                if (mm >= m1) col[mm] = 0.f;
+                rec[kRecT + mm * kCk + k] = col[mm];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------- main kernel
+//
+// One workgroup = (sequence, value head, 16 state rows) with W waves (1, 2 or 4).
+// The dk columns are cut into four quarters; wave w owns quarters [4w/W, 4(w+1)/W)
+// of the state tile, held transposed as MFMA accumulator tiles: lane l = x + 16 g
+// holds S[row0 + x][16 t + 4 g + c] in component c of tile t.  Token-by-row tiles
+// (P, Z, R, U, O) use the MFMA output layout: lane x + 16 g holds token 4 g + c, row x.
+//
+// P and Z are defined as ((X_0 + X_1) + (X_2 + X_3)), X_q the MFMA chain over the
+// tiles of quarter q.  A wave forms the partials of its quarters; with W > 1 they
+// meet in LDS and every wave adds the four in that order, so every W gives the same
+// bits.  R, U and O are then formed alike in every wave (wave 0 stores them); each
+// wave folds its own tiles at a chunk's end.
+//
+// Every global read of a chunk (new keys, queries, values, betas and the record's T
+// and B rows, Gam and chunk-end weights) is sent out when the previous chunk starts
+// its products, into registers, with rows outside the chunk clamped to a valid row
+// and zeroed after the load (no branch per load).
+
+// Four consecutive io elements as loaded (bf16: 8 bytes, fp32: 16 bytes), widened
+// to fp32 only when used, so that a chunk's prefetched rows take half the registers.
+template <class IO>
+struct Raw4 {
+    using T = typename std::conditional<IO::ESZ == 2, uint2, uint4>::type;
+    __device__ static T load(const void *base, size_t idx) {
+        return *reinterpret_cast<const T *>(static_cast<const char *>(base) + idx * IO::ESZ);
+    }
+    // from a (uniform) base pointer and a 32-bit byte offset: one address add per load
+    __device__ static T load_at(const char *base, uint32_t off) { return *reinterpret_cast<const T *>(base + off); }
+    __device__ static T keep(const T &w, bool on) {
+        T z = w;
+        if constexpr (IO::ESZ == 2) {
+            z.x = on ? w.x : 0u;
+            z.y = on ? w.y : 0u;
+        } else {
+            z.x = on ? w.x : 0u;
+            z.y = on ? w.y : 0u;
+            z.z = on ? w.z : 0u;
+            z.w = on ? w.w : 0u;
+        }
+        return z;
+    }
+    __device__ static float4 widen(const T &w) {
+        if constexpr (IO::ESZ == 2)
+            return make_float4(bf16_to_f32(w.x & 0xffffu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xffffu),
+                               bf16_to_f32(w.y >> 16));
+        else
+            return make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
+    }
+    // one element's bits (bf16 in the low half), widened when used
+    __device__ static uint32_t load1_at(const char *base, uint32_t off) {
+        if constexpr (IO::ESZ == 2)
+            return *reinterpret_cast<const uint16_t *>(base + off);
+        else
+            return *reinterpret_cast<const uint32_t *>(base + off);
+    }
+    __device__ static float widen1(uint32_t w) { return IO::ESZ == 2 ? bf16_to_f32(w & 0xffffu) : __uint_as_float(w); }
+};
+
+// What one chunk needs from global memory, per lane of a W-wave workgroup.
+template <int DK, class IO, int W>
+struct ChunkFetch {
+    static constexpr int KIT = kCk * DK / 4 / (64 * W);  // 4-element key items per lane (LDS staging)
+    static constexpr int OT = DK / 16 / W;               // state tiles owned by one wave
+    typename Raw4<IO>::T kr[KIT];   // key rows for LDS: item tid + 64 W s
+    typename Raw4<IO>::T qa[OT];    // query operand: token x, columns of the wave's tiles
+    uint32_t v[4];                  // value bits (row x) of tokens 4 g + c
+    float b[4];                     // their betas
+    float4 trow, brow;              // T[x][4 g ..] and B[x][4 g ..]
+    float4 gam, dw;                 // Gam_{4 g + c} and chunk-end weights Gam_{15, 4 g + c}
+    float g15;                      // Gam_15
+};
+
+template <int DK, class IO, int W>
+__global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p) {
+    constexpr int NT = DK / 16;
+    constexpr int KP = DK + 4;
+    constexpr int OT = NT / W;       // tiles per wave
+    constexpr int QT = NT / 4;       // tiles per quarter
+    constexpr int OQ = 4 / W;        // quarters per wave
+    using CF = ChunkFetch<DK, IO, W>;
+    using RW = Raw4<IO>;
+    static_assert(NT % 4 == 0 && OT * W == NT, "tiles");
+    __shared__ float Ks[kCk][KP];                       // the chunk's keys, fp32
+    __shared__ float4 Xch[W > 1 ? 8 : 1][64];           // P and Z partials of the four quarters
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int x = lane & 15, g = lane >> 4;
+    const int tiles = p.dv / 16;
+    // Workgroups are handed to the eight XCDs round robin by id.  The ones that read
+    // the same keys and queries (one sequence and key head: hv/hk value heads x
+    // tiles) get ids equal modulo 8, so they share one XCD's L2; groups are numbered
+    // rank-major so that lower ids still go to longer sequences.
+    int rank, h, tile;
+    {
+        const int G = p.hv / p.hk, gsize = G * tiles;
+        const int ngroups = p.n_seqs * p.hk;
+        const int full = (ngroups / 8) * 8 * gsize;
+        const int id = blockIdx.x;
+        int grp, member;
+        if (id < full) {
+            const int xcd = id % 8, slot = id / 8;
+            grp = (slot / gsize) * 8 + xcd;
+            member = slot % gsize;
+        } else {
+            grp = full / gsize + (id - full) / gsize;
+            member = (id - full) % gsize;
+        }
+        rank = grp / p.hk;
+        h = (grp % p.hk) * G + member / tiles;
+        tile = member % tiles;
+    }
+    const int n = p.rank_by_length ? seq_by_length_rank(p.cu_seqlens, p.n_seqs, rank, tid, 64 * W) : rank;
+    const int kh = h / (p.hv / p.hk);
+    const int row0 = tile * 16;
+    const int t_first = wave * OT;   // first state tile of this wave
+    const SeqChunks sc = seq_chunks(p, n);
+    const bool inplace = p.inplace != 0;
+    const size_t krow = (size_t)p.hk * DK, vrow = (size_t)p.hv * p.dv;
+
+    // state tiles of this wave
+    f4 S[OT];
+    {
+        const float *src = p.in_S ? p.in_S + (((size_t)n * p.hv + h) * p.dv + row0 + x) * DK : nullptr;
+#pragma unroll
+        for (int t = 0; t < OT; ++t) {
+            S[t] = f4_zero();
+            if (src) {
+                const float4 v4 = *reinterpret_cast<const float4 *>(src + 16 * (t_first + t) + 4 * g);
+                S[t] = f4{v4.x, v4.y, v4.z, v4.w};
+            }
+        }
+    }
+
+    int nch = sc.nch;  // chunks with a workspace slot (all of them for a well-formed cu_seqlens)
+    if (sc.base + nch > p.ws_slots) nch = (int)(p.ws_slots - sc.base > 0 ? p.ws_slots - sc.base : 0);
+    // chunk j: positions [m0, m1) are this call's tokens, token of position 0 is t0
+    auto geom = [&](int j, int &m0, int &m1, int64_t &t0) {
+        m0 = j == 0 ? sc.c0 : 0;
+        const int64_t left = sc.c0 + sc.len - (int64_t)kCk * j;
+        m1 = left < kCk ? (int)left : kCk;
+        t0 = sc.tb + (int64_t)kCk * j - sc.c0;
+    };
+    auto clampm = [](int m, int lo, int hi) { return m < lo ? lo : (m >= hi ? hi - 1 : m); };
+    // (j is clamped to the last chunk, so that a read past it repeats that chunk's
+    // reads instead of needing a branch; nch >= 1 whenever this is called)
+    auto fetch = [&](CF &F, int j_) {
+        const int j = j_ < nch ? j_ : nch - 1;
+        int m0, m1;
+        int64_t t0;
+        geom(j, m0, m1, t0);
+        // uniform bases of this chunk; per-lane offsets in bytes (a chunk spans 16 tokens)
+        constexpr uint32_t E = IO::ESZ;
+        const char *kb = static_cast<const char *>(p.k) + ((size_t)t0 * p.hk + kh) * DK * E;
+        const char *qb = static_cast<const char *>(p.q) + ((size_t)t0 * p.hk + kh) * DK * E;
+        const char *vb = static_cast<const char *>(p.v) + ((size_t)t0 * p.hv + h) * p.dv * E;
+        const char *bb = reinterpret_cast<const char *>(p.beta + (size_t)t0 * p.hv + h);
+        const uint32_t krow_b = (uint32_t)krow * E, vrow_b = (uint32_t)vrow * E, brow_b = (uint32_t)p.hv * 4;
+#pragma unroll
+        for (int s = 0; s < CF::KIT; ++s) {
+            const int it = tid + 64 * W * s;
+            const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+            F.kr[s] = RW::load_at(kb, (uint32_t)clampm(m, m0, m1) * krow_b + (uint32_t)c * E);
+        }
+        const uint32_t qoff = (uint32_t)clampm(x, m0, m1) * krow_b + (uint32_t)(16 * t_first + 4 * g) * E;
+#pragma unroll
+        for (int t = 0; t < OT; ++t) F.qa[t] = RW::load_at(qb, qoff + 16u * t * E);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t tm = (uint32_t)clampm(4 * g + c, m0, m1);
+            F.b[c] = *reinterpret_cast<const float *>(bb + tm * brow_b);
+            F.v[c] = RW::load1_at(vb, tm * vrow_b + (uint32_t)(row0 + x) * E);
+        }
+        const char *rec = reinterpret_cast<const char *>(p.ws + ((size_t)(sc.base + j) * p.hv + h) * kChunkRec);
+        F.trow = *reinterpret_cast<const float4 *>(rec + 4u * (kRecT + x * kCk + 4 * g));
+        F.brow = *reinterpret_cast<const float4 *>(rec + 4u * (kRecB + x * kCk + 4 * g));
+        F.gam = *reinterpret_cast<const float4 *>(rec + 4u * (kRecGam + 4 * g));
+        F.dw = *reinterpret_cast<const float4 *>(rec + 4u * (kRecD + 4 * g));
+        F.g15 = *reinterpret_cast<const float *>(rec + 4u * (kRecGam + kCk - 1));
+    };
+
+    int last_m0 = sc.c0, mo = sc.c0;
+    bool folded = false;
+    // R rows of the open chunk (tokens 4 g + c, row x): cached ones first
+    float Rkeep[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (4 * g + c < sc.c0 && p.in_r) Rkeep[c] = p.in_r[(((size_t)n * kCk + 4 * g + c) * p.hv + h) * p.dv + row0 + x];
+
+    CF F;
+    if (nch > 0) fetch(F, 0);
+    for (int j = 0; j < nch; ++j) {
+        int m0, m1;
+        int64_t t0;
+        geom(j, m0, m1, t0);
+        const bool full = m1 == kCk;
+
+        // keys into LDS (cached keys of a resumed chunk only when it closes here), the
+        // rest of this chunk's reads into working registers, then the next chunk's reads
+#pragma unroll
+        for (int s = 0; s < CF::KIT; ++s) {
+            const int it = tid + 64 * W * s;
+            const int m = it / (DK / 4);
+            *reinterpret_cast<float4 *>(&Ks[m][4 * (it % (DK / 4))]) = RW::widen(RW::keep(F.kr[s], m >= m0 && m < m1));
+        }
+        if (m0 > 0 && full) {
+            for (int it = tid; it < m0 * (DK / 4); it += 64 * W) {
+                const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+                *reinterpret_cast<float4 *>(&Ks[m][c]) =
+                    *reinterpret_cast<const float4 *>(p.in_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + c);
+            }
+        }
+        float4 qv[OT];
+#pragma unroll
+        for (int t = 0; t < OT; ++t) qv[t] = RW::widen(RW::keep(F.qa[t], x >= m0 && x < m1));
+        float vb[4], bb[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bool on = 4 * g + c >= m0 && 4 * g + c < m1;
+            bb[c] = on ? F.b[c] : 0.f;
+            vb[c] = bb[c] * (on ? RW::widen1(F.v[c]) : 0.f);
+        }
+        const float4 trow = F.trow, brow = F.brow, gam = F.gam, dwv = F.dw;
+        const float g15 = F.g15;
+        fetch(F, j + 1);
+        lds_barrier();
+
+        // partial products of this wave's quarters
+        f4 Pq[OQ], Zq[OQ];
+#pragma unroll
+        for (int q = 0; q < OQ; ++q) {
+            Pq[q] = f4_zero();
+            Zq[q] = f4_zero();
+#pragma unroll
+            for (int tt = 0; tt < QT; ++tt) {
+                const int t = q * QT + tt;  // the wave's tile index
+                const float4 ka = *reinterpret_cast<const float4 *>(&Ks[x][16 * (t_first + t) + 4 * g]);
+                Pq[q] = mfma_16x16x4(ka.x, S[t][0], Pq[q]);
+                Zq[q] = mfma_16x16x4(qv[t].x, S[t][0], Zq[q]);
+                Pq[q] = mfma_16x16x4(ka.y, S[t][1], Pq[q]);
+                Zq[q] = mfma_16x16x4(qv[t].y, S[t][1], Zq[q]);
+                Pq[q] = mfma_16x16x4(ka.z, S[t][2], Pq[q]);
+                Zq[q] = mfma_16x16x4(qv[t].z, S[t][2], Zq[q]);
+                Pq[q] = mfma_16x16x4(ka.w, S[t][3], Pq[q]);
+                Zq[q] = mfma_16x16x4(qv[t].w, S[t][3], Zq[q]);
+            }
+        }
+        f4 P4[4], Z4[4];
+        if constexpr (W == 1) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                P4[q] = Pq[q];
+                Z4[q] = Zq[q];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < OQ; ++q) {
+                const int gq = wave * OQ + q;
+                Xch[gq][lane] = make_float4(Pq[q][0], Pq[q][1], Pq[q][2], Pq[q][3]);
+                Xch[4 + gq][lane] = make_float4(Zq[q][0], Zq[q][1], Zq[q][2], Zq[q][3]);
+            }
+            lds_barrier();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 a4 = Xch[q][lane], b4 = Xch[4 + q][lane];
+                P4[q] = f4{a4.x, a4.y, a4.z, a4.w};
+                Z4[q] = f4{b4.x, b4.y, b4.z, b4.w};
+            }
+        }
+        f4 P, Z;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            P[c] = (P4[0][c] + P4[1][c]) + (P4[2][c] + P4[3][c]);
+            Z[c] = (Z4[0][c] + Z4[1][c]) + (Z4[2][c] + Z4[3][c]);
+        }
+
+        // the chunk-end update's key operands (K^T tiles of this wave), read early
+        float kt[OT][4];
+        if (full) {
+#pragma unroll
+            for (int t = 0; t < OT; ++t)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) kt[t][c] = Ks[4 * g + c][16 * (t_first + t) + x];
+        }
+
+        // R_m = fma(-(beta_m Gam_m), P_m, beta_m v_m) for this call's tokens, cached R
+        // for the chunk's earlier tokens, 0 for tokens not reached yet
+        const float gm[4] = {gam.x, gam.y, gam.z, gam.w};
+        f4 R, OC;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int m = 4 * g + c;
+            const bool on = m >= m0 && m < m1;
+            const float fresh = __builtin_fmaf(-(bb[c] * gm[c]), P[c], vb[c]);
+            R[c] = on ? fresh : (m < m0 ? Rkeep[c] : 0.f);
+            Rkeep[c] = on ? fresh : Rkeep[c];
+            OC[c] = gm[c] * Z[c];
+        }
+
+        // U = T R, then O = Gam Z + B U (instruction c adds the tokens 4 g + c)
+        f4 U = f4_zero();
+        U = mfma_16x16x4(trow.x, R[0], U);
+        U = mfma_16x16x4(trow.y, R[1], U);
+        U = mfma_16x16x4(trow.z, R[2], U);
+        U = mfma_16x16x4(trow.w, R[3], U);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) U[c] = U[c] + 0.f;
+        f4 O = OC;
+        O = mfma_16x16x4(brow.x, U[0], O);
+        O = mfma_16x16x4(brow.y, U[1], O);
+        O = mfma_16x16x4(brow.z, U[2], O);
+        O = mfma_16x16x4(brow.w, U[3], O);
+        if (wave == 0) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int m = 4 * g + c;
+                if (m >= m0 && m < m1) IO::store1(p.out, (size_t)(t0 + m) * vrow + (size_t)h * p.dv + row0 + x, O[c] + 0.f);
+            }
+        }
+
+        // chunk complete: S^T = Gam_15 S^T + K^T W, W[s][row] = Gam_{15,s} u_s (own tiles)
+        if (full) {
+            const float w0 = dwv.x * U[0], w1 = dwv.y * U[1], w2 = dwv.z * U[2], w3 = dwv.w * U[3];
+#pragma unroll
+            for (int t = 0; t < OT; ++t) {
+                f4 C = f4{g15 * S[t][0], g15 * S[t][1], g15 * S[t][2], g15 * S[t][3]};
+                C = mfma_16x16x4(kt[t][0], w0, C);
+                C = mfma_16x16x4(kt[t][1], w1, C);
+                C = mfma_16x16x4(kt[t][2], w2, C);
+                C = mfma_16x16x4(kt[t][3], w3, C);
+                S[t] = C;
+            }
+            folded = true;
+        }
+        last_m0 = full ? 0 : m0;
+        mo = full ? 0 : m1;
+        lds_barrier();  // Ks and Xch are refilled by the next chunk
+    }
+
+    // ---- outgoing state: S0 of the open chunk (each wave its tiles), then, from wave
+    // 0, its R rows, keys, decays, betas and count
+    if (!inplace || folded) {
+        float *dst = p.out_S + (((size_t)n * p.hv + h) * p.dv + row0 + x) * DK;
+#pragma unroll
+        for (int t = 0; t < OT; ++t)
+            *reinterpret_cast<float4 *>(dst + 16 * (t_first + t) + 4 * g) =
+                make_float4(S[t][0], S[t][1], S[t][2], S[t][3]);
+    }
+    if (wave != 0) return;
+    const int first = inplace ? last_m0 : 0;  // rows already in place need no write
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int m = 4 * g + c;
+        if (m >= first && m < mo) p.out_r[(((size_t)n * kCk + m) * p.hv + h) * p.dv + row0 + x] = Rkeep[c];
+    }
+    if (tile == 0) {
+        // Rows [first, mo) of the open chunk.  With a chunk processed in this call, its
+        // record holds every row's decay factor and beta (the cached ones copied by the
+        // prep kernel); its rows below last_m0 are cached keys (only when no chunk
+        // boundary was crossed), the others this call's keys.  With none, all cached.
+        const bool any = nch > 0;
+        const int64_t t0 = sc.tb + (int64_t)kCk * (any ? nch - 1 : 0) - sc.c0;  // token of the last chunk's slot 0
+        if (lane >= first && lane < mo) {
+            const float *rec = p.ws + ((size_t)(sc.base + nch - 1) * p.hv + h) * kChunkRec;
+            const size_t e = ((size_t)n * kCk + lane) * p.hv + h;
+            p.out_a[e] = any ? rec[kRecDecay + lane] : p.in_a[e];
+            p.out_b[e] = any ? rec[kRecBeta + lane] : p.in_b[e];
+        }
+        if (h % (p.hv / p.hk) == 0) {
+            for (int it = lane; it < kCk * (DK / 4); it += 64) {
+                const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+                if (m < first || m >= mo) continue;
+                float4 kv;
+                if (any && m >= last_m0)
+                    kv = IO::load4(p.k, ((size_t)(t0 + m) * p.hk + kh) * DK + c);
+                else
+                    kv = *reinterpret_cast<const float4 *>(p.in_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + c);
+                *reinterpret_cast<float4 *>(p.out_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + c) = kv;
+            }
+            if (h == 0 && lane == 0) p.out_count[n] = mo;
+        }
+    }
+}
+
+template <class IO, int DK>
+hipError_t chunked_launch(const ChunkedParams &p, hipStream_t s) {
+    if (p.ws_slots > 0) {
+        hipLaunchKernelGGL((gdn_chunk_prep_kernel<DK, IO>), dim3((unsigned)p.ws_slots, (unsigned)p.hk), dim3(256), 0, s,
+                           p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid((unsigned)((int64_t)p.n_seqs * p.hv * (p.dv / 16)));
+    switch (p.waves) {
+        case 1: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 1>), grid, dim3(64), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 2>), grid, dim3(128), 0, s, p); break;
+        case 4: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 4>), grid, dim3(256), 0, s, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <class IO>
 hipError_t chunked_io(const ChunkedParams &p, hipStream_t s) {
-    const dim3 grid((unsigned)((int64_t)p.n_seqs * p.hv * (p.dv / kChRows)));
     switch (p.dk) {
-        case 64: hipLaunchKernelGGL((gdn_chunked_kernel<64, IO>), grid, dim3(kChThreads), 0, s, p); break;
-        case 128: hipLaunchKernelGGL((gdn_chunked_kernel<128, IO>), grid, dim3(kChThreads), 0, s, p); break;
+        case 64: return chunked_launch<IO, 64>(p, s);
+        case 128: return chunked_launch<IO, 128>(p, s);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace

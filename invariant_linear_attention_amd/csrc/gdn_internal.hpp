@@ -100,21 +100,36 @@ BwdWorkspace backward_workspace(int64_t T, int64_t N, int hv, int dk, int dv);
 
 // Kernel arguments of the chunked form with its replaying decode (gdn_fwd_chunked).
 // A chunked state is the state at the start of the open chunk plus that chunk's
-// keys, write vectors u and cumulative log decays, and its token count.
+// keys, R rows beta (v - Gam S0 k), decay factors a and betas, and its token count.
 constexpr int kChunkLen = 16;
 struct ChunkedParams {
     const void *q, *k, *v;
     const float *g, *beta;
     const int32_t *cu_seqlens;
-    const float *in_S, *in_k, *in_u, *in_G;  // null in_S: zero state; null in_count: empty chunk
+    const float *in_S, *in_k, *in_r, *in_a, *in_b;  // null in_S: zero state; null in_count: empty chunk
     const int32_t *in_count;
-    float *out_S, *out_k, *out_u, *out_G;
+    float *out_S, *out_k, *out_r, *out_a, *out_b;
     int32_t *out_count;
     void *out;
+    float *ws;         // per (workspace slot, value head) records of kChunkRec floats
+    int64_t ws_slots;  // slots in the workspace
     int64_t total_tokens;
     int32_t n_seqs, hk, hv, dk, dv;
+    int32_t rank_by_length;  // workgroups take sequences longest first (n_seqs <= kMaxRankedSeqs)
+    int32_t inplace;         // out shares S, k, r, a and b with in (one-token calls only)
+    int32_t waves;           // waves per 16-row tile: 1, 2 or 4 (each owns 4 / waves dk quarters)
 };
 hipError_t launch_chunked(const ChunkedParams &p, int io_dtype, hipStream_t s);
+
+// Workspace of the chunked form: one record per (chunk a call touches, value head).
+// Sequence n's chunks take slots chunk_slot_base(cu[n], n) + j: floor(cu[n] / 16)
+// + 2 n grows by at least floor(len / 16) + 2 from one sequence to the next, which
+// covers the at most ceil((15 + len) / 16) chunks a sequence of len tokens touches,
+// so floor(T / 16) + 2 N + 2 slots hold every call.
+constexpr int kChunkRec = 576;  // floats: T[16][16], B[16][16], Gam[16], D[16], a[16], beta[16]
+constexpr int kRecT = 0, kRecB = 256, kRecGam = 512, kRecD = 528, kRecDecay = 544, kRecBeta = 560;
+__host__ __device__ inline int64_t chunk_slot_base(int64_t cu_n, int n) { return cu_n / kChunkLen + 2 * (int64_t)n; }
+__host__ __device__ inline int64_t chunk_ws_slots(int64_t T, int64_t N) { return T / kChunkLen + 2 * N + 2; }
 
 // A launch shape: `lanes` lanes hold one state row, each lane holds `rows` rows,
 // and a workgroup has `waves` waves; it owns waves * (64 / lanes) * rows

@@ -22,7 +22,7 @@ STATUS = {
 GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
            "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_bwd_varlen_noalloc", "gdn_fwd_chunked",
-           "gdn_status_string", "gdn_abi_version")
+           "gdn_chunked_workspace_size", "gdn_status_string", "gdn_abi_version")
 
 GDN_CHUNK = 16
 
@@ -71,8 +71,8 @@ _lib = None
 
 class GdnChunkState(ctypes.Structure):
     """Mirror of ``gdn_chunk_state``."""
-    _fields_ = [("S", ctypes.c_void_p), ("k", ctypes.c_void_p), ("u", ctypes.c_void_p), ("G", ctypes.c_void_p),
-                ("count", ctypes.c_void_p)]
+    _fields_ = [("S", ctypes.c_void_p), ("k", ctypes.c_void_p), ("r", ctypes.c_void_p), ("a", ctypes.c_void_p),
+                ("b", ctypes.c_void_p), ("count", ctypes.c_void_p)]
 
 
 def load_library(path: str = LIBRARY):
@@ -104,7 +104,10 @@ def load_library(path: str = LIBRARY):
         lib.gdn_fwd_varlen_train.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdn_fwd_chunked.restype = ctypes.c_int
         lib.gdn_fwd_chunked.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp,
-                                        ctypes.POINTER(GdnChunkState), ctypes.POINTER(GdnChunkState), vp, vp]
+                                        ctypes.POINTER(GdnChunkState), ctypes.POINTER(GdnChunkState), vp, vp,
+                                        ctypes.c_uint64, vp]
+        lib.gdn_chunked_workspace_size.restype = ctypes.c_int
+        lib.gdn_chunked_workspace_size.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(ctypes.c_uint64)]
         lib.gdn_query_plan.restype = ctypes.c_int
         lib.gdn_query_plan.argtypes = [ctypes.POINTER(GdnDims), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
         lib.gdn_status_string.restype = ctypes.c_char_p
@@ -380,31 +383,48 @@ def gdn_bwd_varlen(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=N
 
 def make_chunk_state(n_seqs: int, hk: int, hv: int, dk: int, dv: int, device, h0=None):
     """A chunked state (see gdn_fwd_chunked): dict of S [N, hv, dv, dk], k [N, 16, hk, dk],
-    u [N, 16, hv, dv], G [N, 16, hv] (fp32) and count [N] (int32), with an empty open
-    chunk and S = h0 (or zeros)."""
+    r [N, 16, hv, dv], a and b [N, 16, hv] (fp32) and count [N] (int32), with an empty
+    open chunk and S = h0 (or zeros)."""
     import torch
     f32 = dict(dtype=torch.float32, device=device)
     S = torch.zeros((n_seqs, hv, dv, dk), **f32) if h0 is None else h0.to(device=device, dtype=torch.float32).clone()
     return {"S": S.contiguous(), "k": torch.zeros((n_seqs, GDN_CHUNK, hk, dk), **f32),
-            "u": torch.zeros((n_seqs, GDN_CHUNK, hv, dv), **f32), "G": torch.zeros((n_seqs, GDN_CHUNK, hv), **f32),
+            "r": torch.zeros((n_seqs, GDN_CHUNK, hv, dv), **f32), "a": torch.zeros((n_seqs, GDN_CHUNK, hv), **f32),
+            "b": torch.zeros((n_seqs, GDN_CHUNK, hv), **f32),
             "count": torch.zeros((n_seqs,), dtype=torch.int32, device=device)}
 
 
 def _chunk_struct(st):
     if st is None:
         return None
-    return GdnChunkState(_ptr(st["S"]), _ptr(st["k"]), _ptr(st["u"]), _ptr(st["G"]), _ptr(st["count"]))
+    return GdnChunkState(_ptr(st["S"]), _ptr(st["k"]), _ptr(st["r"]), _ptr(st["a"]), _ptr(st["b"]), _ptr(st["count"]))
 
 
-def gdn_fwd_chunked(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=None, stream=None):
+def gdn_chunked_workspace_size(dims: GdnDims) -> int:
+    """Workspace bytes gdn_fwd_chunked needs for ``dims`` (host only)."""
+    n = ctypes.c_uint64(0)
+    _check(load_library().gdn_chunked_workspace_size(ctypes.byref(dims), ctypes.byref(n)))
+    return int(n.value)
+
+
+def gdn_fwd_chunked(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=None, stream=None, workspace=None,
+                    inplace: bool = False, count_out=None, waves: int = 0):
     """Chunked form with a replaying decode (see include/gdn.h).  ``state_in`` is a
     chunked state dict (make_chunk_state) or None for empty states; ``state_out``
     (allocated when None) receives the new states and must not overlap ``state_in``.
-    Returns (out [T, Hv, dv], state_out)."""
+    With ``inplace`` (one token per sequence only) the state's S, k, r, a and b are
+    updated where they are and the new token counts go to ``count_out`` (int32 [N],
+    allocated when None); the returned state shares those arrays with ``state_in``
+    and holds the new counts.  ``workspace`` (uint8, at least
+    gdn_chunked_workspace_size bytes) is allocated when None.  ``waves`` (0 = automatic,
+    else 1, 2 or 4) sets how many waves share a 16-row state tile (never a bit of the
+    result).  Returns (out [T, Hv, dv], state_out)."""
     import torch
     T, hk, dk, hv, dv, N = _dims_of(q, k, v, g, beta, cu_seqlens, require_cu=True)
-    want = {"S": (N, hv, dv, dk), "k": (N, GDN_CHUNK, hk, dk), "u": (N, GDN_CHUNK, hv, dv), "G": (N, GDN_CHUNK, hv),
-            "count": (N,)}
+    want = {"S": (N, hv, dv, dk), "k": (N, GDN_CHUNK, hk, dk), "r": (N, GDN_CHUNK, hv, dv), "a": (N, GDN_CHUNK, hv),
+            "b": (N, GDN_CHUNK, hv), "count": (N,)}
+    if inplace and (state_in is None or state_out is not None):
+        raise ValueError("inplace updates state_in and takes no state_out")
     for which, st in (("state_in", state_in), ("state_out", state_out)):
         if st is not None:
             for name, shp in want.items():
@@ -412,6 +432,8 @@ def gdn_fwd_chunked(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=
                     raise ValueError("%s[%r] is required" % (which, name))
                 _shape(st[name], "%s.%s" % (which, name), shp)
     _shape(out, "out", (T, hv, dv))
+    if workspace is not None and workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
@@ -420,19 +442,27 @@ def gdn_fwd_chunked(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=
     _need(cu_seqlens, "cu_seqlens", torch.int32)
     for st in (state_in, state_out):
         if st is not None:
-            for name in ("S", "k", "u", "G"):
+            for name in ("S", "k", "r", "a", "b"):
                 _need(st[name], "state." + name, torch.float32)
             _need(st["count"], "state.count", torch.int32)
+    if inplace:
+        _shape(count_out, "count_out", (N,))
+        _need(count_out, "count_out", torch.int32)
+        state_out = dict(state_in)
+        state_out["count"] = count_out if count_out is not None else torch.empty_like(state_in["count"])
     if state_out is None:
         state_out = make_chunk_state(N, hk, hv, dk, dv, q.device)
     if out is None:
         out = torch.empty((T, hv, dv), dtype=q.dtype, device=q.device)
     _need(out, "out", q.dtype)
-    dims = make_dims(q, v, N, T)
+    dims = make_dims(q, v, N, T, plan=(0, 0, int(waves)))
+    if workspace is None:
+        workspace = torch.empty(gdn_chunked_workspace_size(dims), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
     sin, sout = _chunk_struct(state_in), _chunk_struct(state_out)
     _check(lib.gdn_fwd_chunked(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                ctypes.byref(sin) if sin is not None else None, ctypes.byref(sout), _ptr(out),
-                               _stream_handle(stream)))
+                               _ptr(workspace), int(workspace.numel()), _stream_handle(stream)))
     return out, state_out
 
 

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
                           "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_bwd_varlen_noalloc",
-                          "gdn_fwd_chunked",
+                          "gdn_fwd_chunked", "gdn_chunked_workspace_size",
                           "gdn_status_string", "gdn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -448,35 +448,64 @@ def test_bwd_rejects_preprocessing(lib):
 # ------------------------------------------------------------------ chunked form
 
 CH = {name: BASE + (80 + i) * MB for i, name in enumerate(
-    ["q", "k", "v", "g", "b", "cu", "o", "iS", "ik", "iu", "iG", "ic", "oS", "ok", "ou", "oG", "oc"])}
+    ["q", "k", "v", "g", "b", "cu", "o", "iS", "ik", "ir", "ia", "ib", "ic", "oS", "ok", "or", "oa", "ob", "oc", "ws"])}
 
 
-def call_chunked(lib, dims, with_in=True, **over):
+def ch_ws(lib, dims):
+    """Workspace bytes for dims (0 where the dims themselves are refused)."""
+    n = ctypes.c_uint64(0)
+    return int(n.value) if lib.gdn_chunked_workspace_size(ctypes.byref(dims), ctypes.byref(n)) == 0 else 0
+
+
+def call_chunked(lib, dims, with_in=True, ws_bytes=None, **over):
     from invariant_linear_attention_amd.gdn import GdnChunkState
     a = dict(CH)
     a.update(over)
-    sin = GdnChunkState(a["iS"], a["ik"], a["iu"], a["iG"], a["ic"])
-    sout = GdnChunkState(a["oS"], a["ok"], a["ou"], a["oG"], a["oc"])
+    if ws_bytes is None:
+        ws_bytes = ch_ws(lib, dims) if dims is not None else 0
+    sin = GdnChunkState(a["iS"], a["ik"], a["ir"], a["ia"], a["ib"], a["ic"])
+    sout = GdnChunkState(a["oS"], a["ok"], a["or"], a["oa"], a["ob"], a["oc"])
     return lib.gdn_fwd_chunked(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], a["v"], a["g"],
                                a["b"], a["cu"], ctypes.byref(sin) if with_in else None, ctypes.byref(sout), a["o"],
-                               None)
+                               a["ws"], ctypes.c_uint64(ws_bytes), None)
+
+
+def test_chunked_workspace_size(lib):
+    """One record of 576 floats per (slot, value head), floor(T / 16) + 2 N + 2 slots."""
+    d = _dims(n_seqs=3, total_tokens=100, hv=4)
+    assert ch_ws(lib, d) == (100 // 16 + 2 * 3 + 2) * 4 * 576 * 4
+    n = ctypes.c_uint64(0)
+    assert lib.gdn_chunked_workspace_size(None, ctypes.byref(n)) == 1
+    assert lib.gdn_chunked_workspace_size(ctypes.byref(d), None) == 1
+
+
+# the five arrays an in-place update shares between in and out
+SHARED = dict(oS=CH["iS"], ok=CH["ik"], oa=CH["ia"], ob=CH["ib"], **{"or": CH["ir"]})
 
 
 @pytest.mark.parametrize("case,over,code", [
-    (dict(dk=32), {}, 6), (dict(dk=16), {}, 6), (dict(dv=48), {}, 6), (dict(plan_rows=1), {}, 6),
-    (dict(hv=3), {}, 2), (dict(io_dtype=4), {}, 3), (dict(n_seqs=0, total_tokens=2), {}, 2),
+    (dict(dk=32), {}, 6), (dict(dk=16), {}, 6), (dict(plan_rows=1), {}, 6), (dict(plan_waves=3), {}, 6),
+    (dict(hk=1, hv=32), {}, 6), (dict(hv=3), {}, 2), (dict(io_dtype=4), {}, 3), (dict(n_seqs=0, total_tokens=2), {}, 2),
     ({}, dict(cu=None), 1), ({}, dict(oS=None), 1), ({}, dict(oc=None), 1), ({}, dict(q=None), 1),
-    ({}, dict(o=None), 1), ({}, dict(ik=None), 1),
+    ({}, dict(o=None), 1), ({}, dict(ik=None), 1), ({}, dict(ia=None), 1), ({}, dict(oa=None), 1),
+    ({}, dict(ib=None), 1), ({}, dict(ob=None), 1), ({}, dict(ir=None), 1),
+    ({}, dict(ws=None), 1),
     ({}, dict(q=CH["q"] + 8), 4), ({}, dict(oS=CH["oS"] + 4), 4), ({}, dict(oc=CH["oc"] + 2), 4),
-    ({}, dict(ik=CH["ik"] + 4), 4), ({}, dict(ok=CH["ok"] + 8), 4),
-    ({}, dict(oS=CH["iS"]), 5), ({}, dict(ou=CH["iu"] + 64), 5), ({}, dict(o=CH["v"]), 5),
-    ({}, dict(oG=CH["ou"]), 5), ({}, dict(oc=CH["q"]), 5),
+    ({}, dict(ik=CH["ik"] + 4), 4), ({}, dict(ok=CH["ok"] + 8), 4), ({}, dict(ws=CH["ws"] + 4), 4),
+    ({}, dict(oS=CH["iS"]), 5), ({}, {"or": CH["ir"] + 64}, 5), ({}, dict(o=CH["v"]), 5),
+    ({}, dict(oa=CH["or"]), 5), ({}, dict(ob=CH["ia"]), 5), ({}, dict(oc=CH["q"]), 5), ({}, dict(ws=CH["oS"]), 5),
+    ({}, dict(o=CH["ws"]), 5),
+    # in place needs one token per sequence (T == N) and distinct count arrays
+    ({}, SHARED, 5), (dict(total_tokens=2), dict(SHARED, oc=CH["ic"]), 5),
+    (dict(total_tokens=2), dict(SHARED, oS=CH["oS"]), 5),
 ])
 def test_chunked_rejects(lib, case, over, code):
     assert call_chunked(lib, _dims(**case), **over) == code
 
 
-def test_chunked_null_in_and_noop(lib):
+def test_chunked_small_workspace_null_in_and_noop(lib):
+    d = _dims()
+    assert call_chunked(lib, d, ws_bytes=ch_ws(lib, d) - 1) == 2
     assert call_chunked(lib, None) == 1
     assert call_chunked(lib, _dims(n_seqs=0, total_tokens=0)) == 0
     # no incoming state is allowed (empty states); a missing out array is not

@@ -132,10 +132,10 @@ def test_backward_refuses_gradient_buffers():
 
 def test_chunked_refuses_state_shapes():
     b = batch()
-    st = {"S": torch.zeros((N, HV, DV, DK)), "k": torch.zeros((N, 16, HK, DK)), "u": torch.zeros((N, 16, HV, DV)),
-          "G": torch.zeros((N, 16, HV)), "count": torch.zeros((N,), dtype=torch.int32)}
-    for name, shape in (("S", (N, HV, DV, DK * 2)), ("k", (N, 8, HK, DK)), ("u", (N, 16, HK, DV)),
-                        ("G", (N, 16)), ("count", (N + 1,))):
+    st = {"S": torch.zeros((N, HV, DV, DK)), "k": torch.zeros((N, 16, HK, DK)), "r": torch.zeros((N, 16, HV, DV)),
+          "a": torch.zeros((N, 16, HV)), "b": torch.zeros((N, 16, HV)), "count": torch.zeros((N,), dtype=torch.int32)}
+    for name, shape in (("S", (N, HV, DV, DK * 2)), ("k", (N, 8, HK, DK)), ("r", (N, 16, HK, DV)),
+                        ("a", (N, 16)), ("b", (N, 17, HV)), ("count", (N + 1,))):
         bad = dict(st)
         bad[name] = torch.zeros(shape, dtype=st[name].dtype)
         expect_shape_error(gdn.gdn_fwd_chunked, b["q"], b["k"], b["v"], b["g"], b["beta"], b["cu_seqlens"], bad)

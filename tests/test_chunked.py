@@ -2,10 +2,10 @@
 
 Parity: outputs against the fp64 recurrence oracle (the chunked form is the same
 rule written from each chunk's start), and the final state, rebuilt on the host in
-fp64 from the chunked state (S at the open chunk's start plus its u, k and G),
-against the oracle's hT, under the same gates as the recurrent path.
-Bitwise: any split of a sequence into calls, one-token decode steps included,
-and any batch give the same outputs and chunked states.
+fp64 from the chunked state (S at the open chunk's start plus its u, k and decay
+factors a), against the oracle's hT, under the same gates as the recurrent path.
+Bitwise: any split of a sequence into calls, one-token decode steps included (in
+place or not), and any batch give the same outputs and chunked states.
 """
 import numpy as np
 import pytest
@@ -20,11 +20,15 @@ CK = 16
 
 
 def final_state(st):
-    """fp64 state after the open chunk's tokens: Gam_{c-1} S0 + sum_s Gam_{c-1,s} u_s k_s^T."""
+    """fp64 state after the open chunk's tokens, rebuilt from the chunked state: the
+    open chunk's u from its R rows by forward substitution (u_m = R_m - sum_{r<m}
+    beta_m Gam_{m,r} (k_m . k_r) u_r), then Gam_{c-1} S0 + sum_s Gam_{c-1,s} u_s k_s^T,
+    with Gam_{m,s} = a_m ... a_{s+1} and Gam_{c-1} = a_{c-1} ... a_0."""
     S0 = st["S"].double().cpu().numpy()
     K = st["k"].double().cpu().numpy()
-    U = st["u"].double().cpu().numpy()
-    G = st["G"].double().cpu().numpy()
+    R = st["r"].double().cpu().numpy()
+    A = st["a"].double().cpu().numpy()
+    B = st["b"].double().cpu().numpy()
     cnt = st["count"].cpu().numpy()
     N, hv = S0.shape[0], S0.shape[1]
     hk = K.shape[2]
@@ -35,17 +39,23 @@ def final_state(st):
             continue
         for h in range(hv):
             kh = h // (hv // hk)
-            Gl = G[n, c - 1, h]
-            acc = np.exp(Gl) * S0[n, h]
+            u = []
+            for m in range(c):
+                um = R[n, m, h].copy()
+                for r in range(m):
+                    um -= B[n, m, h] * np.prod(A[n, r + 1:m + 1, h]) * (K[n, m, kh] @ K[n, r, kh]) * u[r]
+                u.append(um)
+            acc = np.prod(A[n, :c, h]) * S0[n, h]
             for s in range(c):
-                acc += np.exp(Gl - G[n, s, h]) * np.outer(U[n, s, h], K[n, s, kh])
+                acc += np.prod(A[n, s + 1:c, h]) * np.outer(u[s], K[n, s, kh])
             out[n, h] = acc
     return out
 
 
-def run(gdn, w, st_in=None, d=None):
+def run(gdn, w, st_in=None, d=None, inplace=False, waves=0):
     d = d if d is not None else to_dev(w)
-    out, st = gdn.gdn_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], st_in)
+    out, st = gdn.gdn_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], st_in, inplace=inplace,
+                                  waves=waves)
     torch.cuda.synchronize()
     return out, st
 
@@ -60,13 +70,14 @@ def states_equal(a, b):
     if not torch.equal(a["count"], b["count"]) or not bit_equal(a["S"], b["S"]):
         return False
     for n, c in enumerate(a["count"].cpu().tolist()):
-        for key in ("k", "u", "G"):
+        for key in ("k", "r", "a", "b"):
             if not bit_equal(a[key][n, :c], b[key][n, :c]):
                 return False
     return True
 
 
-@pytest.mark.parametrize("dk,dv,io", [(128, 128, torch.bfloat16), (64, 64, torch.float32), (128, 32, torch.bfloat16)])
+@pytest.mark.parametrize("dk,dv,io", [(128, 128, torch.bfloat16), (64, 64, torch.float32), (128, 32, torch.bfloat16),
+                                      (64, 48, torch.bfloat16)])
 @pytest.mark.parametrize("h0", [0.0, 0.1])
 def test_parity(gpu, dk, dv, io, h0):
     from oracle import oracle
@@ -82,19 +93,36 @@ def test_parity(gpu, dk, dv, io, h0):
 
 
 def test_parity_benchmark_batch(gpu):
-    """The benchmark batch, oracle on two key heads."""
+    """The benchmark batch (8 sequences, 17,459 tokens, 16/32 heads, dk = dv = 128):
+    every head against the oracle, outputs and rebuilt final states."""
     from oracle import oracle
     w = synth.varlen_prefill(1001)
     out, st = run(gpu, w, start_state(gpu, w))
     fs = final_state(st)
-    for kh in (0, 9):
-        s = synth.head_slice(w, kh)
-        ro, rh = oracle.gdn_forward(s.q, s.k, s.v, s.g, s.beta, s.cu_seqlens, s.h0)
-        vs = slice(2 * kh, 2 * kh + 2)
-        e = max(seq_errors(out[:, vs].float().cpu().numpy(), ro, w.cu_seqlens.tolist()))
-        es = max(state_errors(fs[:, vs], rh))
-        say("chunked benchmark batch kh%d: out %.2e state %.2e" % (kh, e, es))
-        assert e <= OUT_TOL[torch.bfloat16] and es <= STATE_TOL
+    ro, rh = oracle.gdn_forward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, w.h0)
+    e = max(seq_errors(out.float().cpu().numpy(), ro, w.cu_seqlens.tolist()))
+    es = max(state_errors(fs, rh))
+    say("chunked benchmark batch, all heads: out %.2e state %.2e" % (e, es))
+    assert e <= OUT_TOL[torch.bfloat16] and es <= STATE_TOL
+
+
+def test_parity_long_sequence_and_extreme_gates(gpu):
+    """A 2,000-token sequence against the oracle, plus gates the chunk products must
+    survive: g = -1e4 (full forget inside a chunk), g = 0, beta = 0 and beta = 1.5."""
+    from oracle import oracle
+    w = synth.make_workload(541, [2000, 77], hk=2, hv=4, dk=128, dv=128, h0_std=0.1)
+    g, b = w.g.clone(), w.beta.clone()
+    g[100:103] = -1e4
+    g[300:340] = 0.0
+    b[500:530] = 0.0
+    b[700:760] = 1.5
+    w = synth.Workload(w.q, w.k, w.v, g, b, w.cu_seqlens, w.h0)
+    out, st = run(gpu, w, start_state(gpu, w))
+    ro, rh = oracle.gdn_forward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, w.h0)
+    e = max(seq_errors(out.float().cpu().numpy(), ro, w.cu_seqlens.tolist()))
+    es = max(state_errors(final_state(st), rh))
+    say("chunked extreme gates: out %.2e state %.2e" % (e, es))
+    assert e <= OUT_TOL[torch.bfloat16] and es <= STATE_TOL
 
 
 @pytest.mark.parametrize("hk,hv", [(2, 4), (1, 8)])
@@ -139,7 +167,7 @@ def test_alone_vs_in_batch(gpu):
         assert bit_equal(o, ref_out[cu[n]:cu[n + 1]]), n
         assert bit_equal(st["S"][0], ref_st["S"][n]) and int(st["count"][0]) == int(ref_st["count"][n])
         c = int(st["count"][0])
-        for key in ("k", "u", "G"):
+        for key in ("k", "r", "a", "b"):
             assert bit_equal(st[key][0, :c], ref_st[key][n, :c]), (n, key)
 
 
@@ -174,3 +202,58 @@ def test_decode_replay_benchmark_heads(gpu):
             assert bit_equal(o[n:n + 1], ref_out[cu[n] + L0 + j:cu[n] + L0 + j + 1]), (n, j)
     assert states_equal(st, ref_st)
     say("chunked: 512-token prefill + 9 decode steps == 521-token prefill, 32 heads, bitwise")
+
+
+def test_inplace_decode_equals_out_of_place(gpu):
+    """One-token steps with the state updated in place (S written only when a chunk
+    closes) give the bits of out-of-place steps and of one prefill, across a chunk end."""
+    L0, steps = 40, 12
+    w = synth.make_workload(641, [L0 + steps] * 4, hk=2, hv=4, dk=128, dv=64, h0_std=0.1)
+    ref_out, ref_st = run(gpu, w, start_state(gpu, w))
+    cu = w.cu_seqlens.tolist()
+
+    def part(a, b):
+        idx = torch.cat([torch.arange(cu[n] + a, cu[n] + b) for n in range(4)])
+        return synth.Workload(w.q[idx], w.k[idx], w.v[idx], w.g[idx], w.beta[idx],
+                              synth.cu_from_lengths([b - a] * 4), None)
+
+    _, st = run(gpu, part(0, L0), start_state(gpu, w))
+    S_addr = st["S"].data_ptr()
+    for j in range(steps):
+        o, st = run(gpu, part(L0 + j, L0 + j + 1), st, inplace=True)
+        for n in range(4):
+            assert bit_equal(o[n:n + 1], ref_out[cu[n] + L0 + j:cu[n] + L0 + j + 1]), (n, j)
+    assert st["S"].data_ptr() == S_addr
+    assert states_equal(st, ref_st)
+
+
+def test_nan_stays_in_its_chunk_and_row(gpu):
+    """A NaN in v[t, h, j] reaches row j of head h from the start of t's 16-token
+    chunk on (0 x NaN in the chunk's tile products), never an earlier chunk, another
+    row, head or sequence; everything else keeps the clean run's bits."""
+    w = synth.make_workload(651, [45, 30], hk=2, hv=4, dk=128, dv=64, h0_std=0.1)
+    clean, _ = run(gpu, w, start_state(gpu, w))
+    t, h, j = 21, 3, 9     # position 21: inside the second chunk (16 .. 31) of sequence 0
+    v = w.v.clone()
+    v[t, h, j] = float("nan")
+    bad = synth.Workload(w.q, w.k, v, w.g, w.beta, w.cu_seqlens, w.h0)
+    out, _ = run(gpu, bad, start_state(gpu, bad))
+    mask = torch.zeros(out.shape, dtype=torch.bool)
+    mask[16:45, h, j] = True
+    assert bool(torch.isnan(out.cpu()[mask].float()).all())
+    assert bit_equal(out.cpu()[~mask], clean.cpu()[~mask])
+
+
+@pytest.mark.parametrize("dk,io", [(128, torch.bfloat16), (64, torch.float32)])
+def test_every_wave_split_gives_the_same_bits(gpu, dk, io):
+    """1, 2 or 4 waves per 16-row tile (the dk quarters spread over them) give the
+    same outputs and states, and so do a prefill and one-token steps under each."""
+    w = synth.make_workload(661, [70, 1, 33, 16], hk=2, hv=4, dk=dk, dv=64, io_dtype=io, h0_std=0.1)
+    ref_out, ref_st = run(gpu, w, start_state(gpu, w), waves=1)
+    for W in (2, 4):
+        o, st = run(gpu, w, start_state(gpu, w), waves=W)
+        assert bit_equal(o, ref_out) and states_equal(st, ref_st), W
+    one = synth.select(w, [0])
+    _, st1 = run(gpu, synth.token_slice(one, 0, 69, h0=one.h0), start_state(gpu, one), waves=4)
+    o, st2 = run(gpu, synth.token_slice(one, 69, 70), st1, waves=2)
+    assert bit_equal(o, ref_out[69:70])
