@@ -268,6 +268,179 @@ int gdn_oracle_short_conv(int32_t n_seqs, const int32_t *cu_seqlens, int32_t C, 
 }
 
 /*
+ * Gradients of gdn_oracle_preprocess, in fp64 (reverse mode of each of its maps),
+ * given the gradients of a loss with respect to its outputs:
+ *
+ *   L2 norm, y = x / s with s = sqrt(sum_i x_i^2 + eps):
+ *       dL/dx_i = (dL/dy_i) / s - x_i (x . dL/dy) / s^3
+ *   gate, g = -exp(A_log) softplus(z) with z = a + dt_bias (softplus' = sigmoid):
+ *       dL/da = dL/dg * (-exp(A_log) sigmoid(z)),   dL/dA_log[h] = sum_t dL/dg g,
+ *       dL/ddt_bias[h] = sum_t dL/da          (sums over t = 0 .. T-1 in order)
+ *   write strength, beta = sigmoid(b):  dL/db = dL/dbeta beta (1 - beta)
+ *
+ * The maps are those of gdn_oracle_preprocess (normalised keys and queries, the
+ * Mamba2-style decay and the sigmoid write strength of the gated delta rule layer,
+ * Yang, Kautz, Hatamizadeh, ICLR 2025).  Without norm_qk the first map is the
+ * identity (dq = dqn); without A_log the gate and beta maps are identities
+ * (da = dg, db = dbeta) and dA_log, ddt_bias are left alone.
+ *
+ * Inputs as gdn_oracle_preprocess plus dqn, dkn [T][hk][dk] and dg, dbeta [T][hv],
+ * fp64.  Outputs, fp64: dq, dk [T][hk][dk]; da, db [T][hv]; dA_log, ddt_bias [hv]
+ * (either may be NULL to skip it).
+ */
+int gdn_oracle_preprocess_backward(int64_t T, int32_t hk, int32_t hv, int32_t dk, int32_t io_dtype,
+                                   const void *q, const void *k, const float *a, const float *b,
+                                   const float *A_log, const float *dt_bias, int32_t norm_qk, double eps,
+                                   const double *dqn, const double *dkn, const double *dg, const double *dbeta,
+                                   double *dq, double *dk_out, double *da, double *db,
+                                   double *dA_log, double *ddt_bias)
+{
+    if (T < 0 || hk <= 0 || hv <= 0 || dk <= 0 || (io_dtype != 0 && io_dtype != 1))
+        return -1;
+    if (T > 0 && (!q || !k || !a || !b || !dqn || !dkn || !dg || !dbeta || !dq || !dk_out || !da || !db))
+        return -4;
+    for (int64_t r = 0; r < T * hk; ++r) {
+        const int64_t off = r * dk;
+        for (int side = 0; side < 2; ++side) {
+            const void *x = side ? k : q;
+            const double *dy = side ? dkn : dqn;
+            double *dx = side ? dk_out : dq;
+            if (!norm_qk) {
+                for (int32_t i = 0; i < dk; ++i)
+                    dx[off + i] = dy[off + i];
+                continue;
+            }
+            double ss = 0.0, xdy = 0.0;
+            for (int32_t i = 0; i < dk; ++i) {
+                const double xi = oracle_load(x, off + i, io_dtype);
+                ss += xi * xi;
+                xdy += xi * dy[off + i];
+            }
+            const double s = sqrt(ss + eps);
+            for (int32_t i = 0; i < dk; ++i) {
+                const double xi = oracle_load(x, off + i, io_dtype);
+                dx[off + i] = dy[off + i] / s - xi * xdy / (s * s * s);
+            }
+        }
+    }
+    if (A_log) {
+        if (dA_log)
+            for (int32_t h = 0; h < hv; ++h)
+                dA_log[h] = 0.0;
+        if (ddt_bias)
+            for (int32_t h = 0; h < hv; ++h)
+                ddt_bias[h] = 0.0;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < hv; ++h) {
+            const int64_t i = t * hv + h;
+            if (!A_log) {
+                da[i] = dg[i];
+                db[i] = dbeta[i];
+                continue;
+            }
+            const double z = (double)a[i] + (dt_bias ? (double)dt_bias[h] : 0.0);
+            const double e = exp((double)A_log[h]);
+            const double sig = 1.0 / (1.0 + exp(-z));
+            const double g = -e * log1p(exp(z));
+            da[i] = dg[i] * (-e * sig);
+            const double beta = 1.0 / (1.0 + exp(-(double)b[i]));
+            db[i] = dbeta[i] * beta * (1.0 - beta);
+            if (dA_log)
+                dA_log[h] += dg[i] * g;
+            if (ddt_bias)
+                ddt_bias[h] += da[i];
+        }
+    }
+    return 0;
+}
+
+/*
+ * Gradients of gdn_oracle_short_conv, in fp64, given dL/dy: with the window
+ * x(s, c) (old state first, as in the forward), z[t] = bias + sum_j w[j] x(t-K+1+j)
+ * and y = z sigmoid(z) (SiLU, derivative sigmoid(z) (1 + z (1 - sigmoid(z)))) or
+ * y = z,
+ *
+ *   dz[t]        = dL/dy[t] * dy/dz
+ *   dL/dx(s)    += w[j] dz[t]          for every t, j with s = t - K + 1 + j
+ *   dL/dw[c][j]  = sum_t dz[t] x(t-K+1+j)
+ *   dL/dbias[c]  = sum_t dz[t]
+ *
+ * over every sequence and token in order.  dL/dx for positions before the first
+ * token is the gradient of the carried conv state (dstate, [N][C][K-1], oldest
+ * first).  The state written after the sequence is a copy of inputs kept for the
+ * next call, not a function the loss is taken of here.
+ *
+ * Inputs as gdn_oracle_short_conv plus dy [T][C] fp64.  Outputs, fp64: dx [T][C],
+ * dw [C][K], dbias [C] (or NULL), dstate [N][C][K-1] (or NULL).
+ */
+int gdn_oracle_short_conv_backward(int32_t n_seqs, const int32_t *cu_seqlens, int32_t C, int32_t K,
+                                   int32_t io_dtype, const void *x, const float *w, const float *bias,
+                                   const double *state, int32_t silu, const double *dy,
+                                   double *dx, double *dw, double *dbias, double *dstate)
+{
+    if (n_seqs < 0 || C <= 0 || K < 1 || (io_dtype != 0 && io_dtype != 1))
+        return -1;
+    if (!w || !dw)
+        return -4;
+    for (int64_t i = 0; i < (int64_t)C * K; ++i)
+        dw[i] = 0.0;
+    if (dbias)
+        for (int32_t c = 0; c < C; ++c)
+            dbias[c] = 0.0;
+    if (n_seqs == 0)
+        return 0;
+    if (!cu_seqlens || (cu_seqlens[n_seqs] > 0 && (!x || !dy || !dx)))
+        return -4;
+    const int32_t M = K - 1;
+    for (int32_t n = 0; n < n_seqs; ++n) {
+        const int64_t tb = cu_seqlens[n], te = cu_seqlens[n + 1];
+        if (te < tb)
+            return -5;
+        const int64_t len = te - tb;
+        double *win = (double *)malloc(sizeof(double) * (size_t)(M + len + 1));
+        double *dwin = (double *)malloc(sizeof(double) * (size_t)(M + len + 1));
+        if (!win || !dwin) {
+            free(win);
+            free(dwin);
+            return -6;
+        }
+        for (int32_t c = 0; c < C; ++c) {
+            for (int32_t m = 0; m < M; ++m)
+                win[m] = state ? state[((int64_t)n * C + c) * M + m] : 0.0;
+            for (int64_t t = 0; t < len; ++t)
+                win[M + t] = oracle_load(x, (tb + t) * C + c, io_dtype);
+            for (int64_t s = 0; s < M + len; ++s)
+                dwin[s] = 0.0;
+            for (int64_t t = 0; t < len; ++t) {
+                double z = bias ? (double)bias[c] : 0.0;
+                for (int32_t j = 0; j < K; ++j)
+                    z += (double)w[(int64_t)c * K + j] * win[t + j];
+                double dz = dy[(tb + t) * C + c];
+                if (silu) {
+                    const double sig = 1.0 / (1.0 + exp(-z));
+                    dz *= sig * (1.0 + z * (1.0 - sig));
+                }
+                for (int32_t j = 0; j < K; ++j) {
+                    dwin[t + j] += (double)w[(int64_t)c * K + j] * dz;
+                    dw[(int64_t)c * K + j] += dz * win[t + j];
+                }
+                if (dbias)
+                    dbias[c] += dz;
+            }
+            for (int64_t t = 0; t < len; ++t)
+                dx[(tb + t) * C + c] = dwin[M + t];
+            if (dstate)
+                for (int32_t m = 0; m < M; ++m)
+                    dstate[((int64_t)n * C + c) * M + m] = dwin[m];
+        }
+        free(win);
+        free(dwin);
+    }
+    return 0;
+}
+
+/*
  * Gradients of the recurrent forward (reverse-mode differentiation of the loop of
  * gdn_oracle_forward), in fp64.
  *

@@ -65,6 +65,20 @@ def load(library: str = LIBRARY):
     c.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                   ctypes.c_void_p, ctypes.c_void_p]
+    pb = lib.gdn_oracle_preprocess_backward
+    pb.restype = ctypes.c_int
+    pb.argtypes = [
+        ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_double,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    cb = lib.gdn_oracle_short_conv_backward
+    cb.restype = ctypes.c_int
+    cb.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     b = lib.gdn_oracle_backward
     b.restype = ctypes.c_int
     b.argtypes = [
@@ -221,6 +235,71 @@ def preprocess(q, k, a, b, A_log=None, dt_bias=None, norm_qk=True, eps=1e-6, lib
     return q2, k2, g2, b2
 
 
+def _f64(x, shape, name):
+    """Gradient input (torch or numpy, fp32, bf16 or fp64) as a contiguous float64 array."""
+    xn, xc = _as_numpy(x)
+    if xc == 1:
+        import torch
+        xn = torch.from_numpy(xn.view(np.int16)).view(torch.bfloat16).double().numpy()
+    elif xc not in (0, 2):
+        raise TypeError("%s must be fp32, bf16 or fp64" % name)
+    xn = np.ascontiguousarray(xn, dtype=np.float64)
+    if xn.shape != tuple(shape):
+        raise ValueError("%s must have shape %s" % (name, tuple(shape)))
+    return xn
+
+
+def preprocess_backward(q, k, a, b, dqn, dkn, dg, dbeta, A_log=None, dt_bias=None, norm_qk=True, eps=1e-6,
+                        library=None):
+    """fp64 gradients of preprocess() (see gdn_oracle_preprocess_backward).
+
+    q, k, a, b, A_log, dt_bias as preprocess(); dqn, dkn [T, Hk, dk] and dg, dbeta
+    [T, Hv]: the loss's gradients with respect to preprocess()'s four outputs.
+    Returns a dict of float64 arrays: dq, dk [T, Hk, dk]; da, db [T, Hv]; and, with
+    A_log, dA_log and ddt_bias [Hv].
+    """
+    qn, qc = _as_numpy(q)
+    kn, kc = _as_numpy(k)
+    if not (qc == kc and qc in (0, 1)):
+        raise TypeError("q and k must share one dtype: fp32 or bf16")
+    an, ac = _as_numpy(a)
+    bn, bc = _as_numpy(b)
+    if ac != 0 or bc != 0:
+        raise TypeError("a and b must be fp32")
+    T, hk, dk = qn.shape
+    hv = an.shape[1]
+    if kn.shape != qn.shape or an.shape != (T, hv) or bn.shape != (T, hv):
+        raise ValueError("inconsistent shapes")
+    Ln = Dn = None
+    if A_log is not None:
+        Ln, lc = _as_numpy(A_log)
+        if lc != 0 or Ln.shape != (hv,):
+            raise ValueError("A_log must be fp32 [Hv]")
+    if dt_bias is not None:
+        Dn, dc = _as_numpy(dt_bias)
+        if dc != 0 or Dn.shape != (hv,):
+            raise ValueError("dt_bias must be fp32 [Hv]")
+    gq, gk = _f64(dqn, (T, hk, dk), "dqn"), _f64(dkn, (T, hk, dk), "dkn")
+    gg, gb = _f64(dg, (T, hv), "dg"), _f64(dbeta, (T, hv), "dbeta")
+    res = {"dq": np.zeros((T, hk, dk)), "dk": np.zeros((T, hk, dk)), "da": np.zeros((T, hv)),
+           "db": np.zeros((T, hv))}
+    if A_log is not None:
+        res["dA_log"] = np.zeros(hv)
+        res["ddt_bias"] = np.zeros(hv)
+    lib = load(library) if library is not None else _get_lib()
+
+    def ptr(x):
+        return None if x is None or x.size == 0 else x.ctypes.data
+
+    rc = lib.gdn_oracle_preprocess_backward(
+        T, hk, hv, dk, qc, ptr(qn), ptr(kn), ptr(an), ptr(bn), ptr(Ln), ptr(Dn), 1 if norm_qk else 0, float(eps),
+        ptr(gq), ptr(gk), ptr(gg), ptr(gb), ptr(res["dq"]), ptr(res["dk"]), ptr(res["da"]), ptr(res["db"]),
+        ptr(res.get("dA_log")), ptr(res.get("ddt_bias")))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (code %d)" % rc)
+    return res
+
+
 def gdn_forward_fused(q, k, v, a, b, cu_seqlens, h0=None, A_log=None, dt_bias=None, norm_qk=True, eps=1e-6,
                       n_threads=None, library=None):
     """preprocess() followed by gdn_forward() on its fp64 results."""
@@ -339,6 +418,51 @@ def gdn_backward(q, k, v, g, beta, cu_seqlens, dout, h0=None, dhT=None, n_thread
         ptr(qn), ptr(kn), ptr(vn), ptr(gn), ptr(bn), ptr(h0n), ptr(dn), ptr(dhn),
         ptr(res["dq"]), ptr(res["dk"]), ptr(res["dv"]), ptr(res["dg"]), ptr(res["dbeta"]), ptr(res["dh0"]),
         int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (code %d)" % rc)
+    return res
+
+
+def short_conv_backward(x, w, cu_seqlens, dy, bias=None, state=None, silu=True, library=None):
+    """fp64 gradients of short_conv() (see gdn_oracle_short_conv_backward).
+
+    x, w, cu_seqlens, bias, state as short_conv(); dy [T, C] (fp32, bf16 or fp64):
+    dL/dy.  Returns a dict of float64 arrays: dx [T, C], dw [C, K], dbias [C] and
+    dstate [N, C, K-1] (the gradient of the carried state taken in).
+    """
+    xn, xc = _as_numpy(x)
+    if xc not in (0, 1):
+        raise TypeError("x must be fp32 or bf16")
+    wn, wc = _as_numpy(w)
+    if wc != 0 or wn.ndim != 2:
+        raise TypeError("w must be fp32 [C, K]")
+    cu, cc = _as_numpy(cu_seqlens)
+    if cc != 3:
+        raise TypeError("cu_seqlens must be int32")
+    T, C = xn.shape
+    K = wn.shape[1]
+    if wn.shape[0] != C:
+        raise ValueError("w must be [C, K]")
+    n = cu.shape[0] - 1
+    bn = None
+    if bias is not None:
+        bn, bc = _as_numpy(bias)
+        if bc != 0 or bn.shape != (C,):
+            raise ValueError("bias must be fp32 [C]")
+    sn = None
+    if state is not None:
+        sn = _f64(state, (n, C, K - 1), "state")
+    gy = _f64(dy, (T, C), "dy")
+    res = {"dx": np.zeros((T, C)), "dw": np.zeros((C, K)), "dbias": np.zeros(C),
+           "dstate": np.zeros((max(n, 0), C, K - 1))}
+    lib = load(library) if library is not None else _get_lib()
+
+    def ptr(a):
+        return None if a is None or a.size == 0 else a.ctypes.data
+
+    rc = lib.gdn_oracle_short_conv_backward(n, ptr(cu), C, K, xc, ptr(xn), ptr(wn), ptr(bn), ptr(sn),
+                                            1 if silu else 0, ptr(gy), ptr(res["dx"]), ptr(res["dw"]),
+                                            ptr(res["dbias"]), ptr(res["dstate"]))
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
     return res

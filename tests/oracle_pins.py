@@ -736,3 +736,190 @@ GRAD_PINS = [
     pin_grad_split_sequence,
     pin_grad_grouped_heads,
 ]
+
+
+# ------------------------------------- gradients of the preprocessing and the conv
+#
+# Finite differences on exact perturbations: inputs sit on the grid of multiples
+# of 2^-12, so x + j h with h = 2^-10 and j = -2..2 is an fp32 number and the
+# forward is evaluated exactly there (in fp64).  The five-point stencil
+# (f(x-2h) - 8 f(x-h) + 8 f(x+h) - f(x+2h)) / 12h then has an O(h^4) truncation
+# error, about 1e-12 of the derivative's scale for these smooth maps.
+
+FD_H = 2.0 ** -10
+
+
+def _grid(x):
+    return (np.round(np.asarray(x, dtype=np.float64) * 4096.0) / 4096.0).astype(np.float32)
+
+
+def _fd5(loss, x):
+    """dloss/dx for every element of x (modified in place and restored)."""
+    out = np.zeros(x.shape)
+    for idx in np.ndindex(x.shape):
+        keep = x[idx]
+        vals = []
+        for j in (-2, -1, 1, 2):
+            x[idx] = keep + j * FD_H
+            assert float(x[idx]) == float(keep) + j * FD_H, "perturbation not exact"
+            vals.append(loss())
+        x[idx] = keep
+        out[idx] = (vals[0] - 8.0 * vals[1] + 8.0 * vals[2] - vals[3]) / (12.0 * FD_H)
+    return out
+
+
+def _pre_grad_case(seed, T, hk, hv, dk, gate=True, bias=True):
+    r = _rng(seed)
+    c = dict(q=_grid(1.5 * r.standard_normal((T, hk, dk))), k=_grid(1.5 * r.standard_normal((T, hk, dk))),
+             a=_grid(2.0 * r.standard_normal((T, hv))), b=_grid(2.0 * r.standard_normal((T, hv))),
+             A_log=_grid(r.uniform(-1.0, 1.5, hv)) if gate else None,
+             dt_bias=_grid(r.standard_normal(hv)) if (gate and bias) else None)
+    w = dict(dqn=r.standard_normal((T, hk, dk)), dkn=r.standard_normal((T, hk, dk)),
+             dg=r.standard_normal((T, hv)), dbeta=r.standard_normal((T, hv)))
+    return c, w
+
+
+def pin_pre_grad_finite_differences(pre_backward, preprocess):
+    """Every gradient of the preprocessing against five-point differences of the
+    (pinned) preprocessing, for L = sum of random weights times its four outputs;
+    with the norm and gate maps on and off, with and without dt_bias, eps small and
+    large."""
+    for seed, gate, bias, norm, eps in ((81, True, True, True, 1e-6), (82, True, False, True, 0.25),
+                                        (83, False, False, True, 1e-6), (84, True, True, False, 1e-6)):
+        c, w = _pre_grad_case(seed, T=3, hk=2, hv=4, dk=5, gate=gate, bias=bias)
+
+        def loss():
+            qn, kn, g, beta = preprocess(c["q"], c["k"], c["a"], c["b"], c["A_log"], c["dt_bias"],
+                                         norm_qk=norm, eps=eps)
+            return float((qn * w["dqn"]).sum() + (kn * w["dkn"]).sum() + (g * w["dg"]).sum()
+                         + (beta * w["dbeta"]).sum())
+
+        r = pre_backward(c["q"], c["k"], c["a"], c["b"], w["dqn"], w["dkn"], w["dg"], w["dbeta"],
+                         A_log=c["A_log"], dt_bias=c["dt_bias"], norm_qk=norm, eps=eps)
+        names = [("q", "dq"), ("k", "dk"), ("a", "da"), ("b", "db")]
+        if gate:
+            names.append(("A_log", "dA_log"))
+            if bias:
+                names.append(("dt_bias", "ddt_bias"))
+        for name, gname in names:
+            _close(r[gname], _fd5(loss, c[name]), tol=1e-9,
+                   what="%s vs finite differences (seed %d)" % (gname, seed))
+
+
+def pin_pre_grad_constants(pre_backward, preprocess):
+    """At a = dt_bias = A_log = 0 and b = 0: softplus'(0) = sigmoid(0) = 1/2 and
+    g = -ln 2, so da = -dg / 2, dA_log = -ln 2 * sum_t dg, ddt_bias = sum_t da and
+    db = dbeta / 4.  A unit row with eps = 0 has dq = dqn - q (q . dqn)."""
+    T, hv = 3, 2
+    z = np.zeros((T, hv), dtype=np.float32)
+    q = np.array([[[0.5, 0.5, 0.5, 0.5]], [[1.0, 0.0, 0.0, 0.0]], [[0.0, 0.0, -1.0, 0.0]]], dtype=np.float32)
+    dg = np.array([[1.0, -2.0], [0.5, 3.0], [-1.0, 0.25]])
+    dbeta = np.array([[2.0, 4.0], [-8.0, 1.0], [0.0, 0.5]])
+    dqn = np.arange(12, dtype=np.float64).reshape(T, 1, 4) / 7.0
+    r = pre_backward(q, q, z, z, dqn, dqn, dg, dbeta, A_log=np.zeros(hv, np.float32),
+                     dt_bias=np.zeros(hv, np.float32), norm_qk=True, eps=0.0)
+    _close(r["da"], -0.5 * dg, tol=1e-15, what="da at zero logits")
+    _close(r["db"], 0.25 * dbeta, tol=1e-15, what="db at zero logits")
+    _close(r["dA_log"], -math.log(2.0) * dg.sum(axis=0), tol=1e-15, what="dA_log at zero logits")
+    _close(r["ddt_bias"], -0.5 * dg.sum(axis=0), tol=1e-15, what="ddt_bias at zero logits")
+    qq = q.astype(np.float64)
+    expect = dqn - qq * (qq * dqn).sum(axis=-1, keepdims=True)
+    _close(r["dq"], expect, tol=1e-14, what="dq of a unit row")
+    _close(r["dk"], expect, tol=1e-14, what="dk of a unit row")
+
+
+def pin_pre_grad_norm_is_scale_invariant(pre_backward, preprocess):
+    """With eps = 0 the normalised row does not change along x, so the gradient
+    is orthogonal to x whatever dL/dq' is: x . dq = 0."""
+    c, w = _pre_grad_case(85, T=4, hk=3, hv=3, dk=6)
+    r = pre_backward(c["q"], c["k"], c["a"], c["b"], w["dqn"], w["dkn"], w["dg"], w["dbeta"],
+                     A_log=c["A_log"], dt_bias=c["dt_bias"], norm_qk=True, eps=0.0)
+    for x, g in ((c["q"], r["dq"]), (c["k"], r["dk"])):
+        dots = (x.astype(np.float64) * g).sum(axis=-1)
+        scale = np.linalg.norm(x, axis=-1) * np.linalg.norm(g, axis=-1)
+        assert np.all(np.abs(dots) <= 1e-14 * scale), "norm gradient not orthogonal to its row"
+
+
+PRE_GRAD_PINS = [
+    pin_pre_grad_finite_differences,
+    pin_pre_grad_constants,
+    pin_pre_grad_norm_is_scale_invariant,
+]
+
+
+def pin_conv_grad_finite_differences(conv_backward, conv):
+    """dx, dw, dbias and dstate against five-point differences of the (pinned)
+    convolution, with SiLU on and off, a sequence shorter than K - 1, an empty one,
+    and with and without a carried state."""
+    for seed, silu, with_state in ((91, True, True), (92, False, True), (93, True, False)):
+        r = _rng(seed)
+        lengths, C, K = [5, 0, 2], 3, 4
+        x, w, bias, cu, state = _conv_case(seed, lengths, C, K, with_state=with_state)
+        x, w, bias = _grid(x), _grid(0.5 * w), _grid(bias)
+        if state is not None:
+            state = _grid(state).astype(np.float64)
+        dy = r.standard_normal(x.shape)
+
+        def loss():
+            y, _ = conv(x, w, cu, bias=bias, state=state, silu=silu)
+            return float((y * dy).sum())
+
+        g = conv_backward(x, w, cu, dy, bias=bias, state=state, silu=silu)
+        arrays = [("x", x, "dx"), ("w", w, "dw"), ("bias", bias, "dbias")]
+        if state is not None:
+            arrays.append(("state", state, "dstate"))
+        for name, arr, gname in arrays:
+            _close(g[gname], _fd5(loss, arr), tol=1e-9, what="%s vs finite differences (seed %d)" % (gname, seed))
+
+
+def pin_conv_grad_adjoint(conv_backward, conv):
+    """Without SiLU, bias and state the convolution is linear in x and in w, so
+    <dy, conv(x)> = <dx, x> = <dw, w> (the adjoint identity)."""
+    r = _rng(94)
+    lengths, C, K = [7, 3, 1], 5, 3
+    x, w, _, cu, _ = _conv_case(94, lengths, C, K, with_state=False)
+    dy = r.standard_normal(x.shape)
+    y, _ = conv(x, w, cu, bias=None, state=None, silu=False)
+    g = conv_backward(x, w, cu, dy, bias=None, state=None, silu=False)
+    lhs = float((dy * y).sum())
+    for name, arr, gname in (("x", x, "dx"), ("w", w, "dw")):
+        rhs = float((g[gname] * arr.astype(np.float64)).sum())
+        assert abs(lhs - rhs) <= 1e-12 * (1.0 + abs(lhs)), "adjoint identity fails for %s" % name
+
+
+CONV_GRAD_PINS = [
+    pin_conv_grad_finite_differences,
+    pin_conv_grad_adjoint,
+]
+
+
+def pin_fused_layer_chain(pre_backward, preprocess, backward, forward):
+    """The fused layer end to end: raw q, k, a, b, A_log, dt_bias -> preprocessing
+    -> the rule -> L = sum(dout * out) + sum(dhT * hT).  The chained gradients
+    (the rule's backward, then the preprocessing's) against five-point differences
+    of the whole forward, on two sequences with grouped heads and h0."""
+    r = _rng(95)
+    lengths, hk, hv, dk, dv = [3, 2], 1, 2, 3, 2
+    T = sum(lengths)
+    c, _ = _pre_grad_case(95, T=T, hk=hk, hv=hv, dk=dk)
+    v = _grid(r.standard_normal((T, hv, dv)))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    h0 = 0.5 * r.standard_normal((len(lengths), hv, dv, dk))
+    dout = r.standard_normal((T, hv, dv))
+    dhT = r.standard_normal((len(lengths), hv, dv, dk))
+
+    def pre():
+        return preprocess(c["q"], c["k"], c["a"], c["b"], c["A_log"], c["dt_bias"], norm_qk=True, eps=1e-6)
+
+    def loss():
+        qn, kn, g, beta = pre()
+        out, hT = forward(qn, kn, v, g, beta, cu, h0)
+        return float((out * dout).sum() + (hT * dhT).sum())
+
+    qn, kn, g, beta = pre()
+    gb = backward(qn, kn, v, g, beta, cu, dout, h0=h0, dhT=dhT)
+    gp = pre_backward(c["q"], c["k"], c["a"], c["b"], gb["dq"], gb["dk"], gb["dg"], gb["dbeta"],
+                      A_log=c["A_log"], dt_bias=c["dt_bias"], norm_qk=True, eps=1e-6)
+    for name, gname in (("q", "dq"), ("k", "dk"), ("a", "da"), ("b", "db"), ("A_log", "dA_log"),
+                        ("dt_bias", "ddt_bias")):
+        _close(gp[gname], _fd5(loss, c[name]), tol=1e-8, what="fused-layer %s vs finite differences" % gname)

@@ -26,6 +26,21 @@ def test_oracle_preprocessing_pin(pin):
     pin(oracle.preprocess, oracle.gdn_forward)
 
 
+@pytest.mark.parametrize("pin", oracle_pins.PRE_GRAD_PINS, ids=lambda p: p.__name__)
+def test_oracle_preprocessing_gradient_pin(pin):
+    pin(oracle.preprocess_backward, oracle.preprocess)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.CONV_GRAD_PINS, ids=lambda p: p.__name__)
+def test_oracle_short_conv_gradient_pin(pin):
+    pin(oracle.short_conv_backward, oracle.short_conv)
+
+
+def test_oracle_fused_layer_gradient_chain():
+    oracle_pins.pin_fused_layer_chain(oracle.preprocess_backward, oracle.preprocess, oracle.gdn_backward,
+                                      oracle.gdn_forward)
+
+
 def test_bruteforce_is_not_the_recurrence():
     """The brute force must itself respect the transition-product algebra: with
     one token and S0 = 0 it reduces to beta v k^T, whatever the gate."""

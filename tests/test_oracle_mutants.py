@@ -101,6 +101,62 @@ GRAD_MUTANTS = [
 ]
 
 
+# Mistakes in the gradients of the preprocessing and the conv.
+PRE_GRAD_MUTANTS = [
+    ("norm_grad_without_projection", "dx[off + i] = dy[off + i] / s - xi * xdy / (s * s * s);",
+     "dx[off + i] = dy[off + i] / s;"),
+    ("norm_grad_cubed_as_squared", "dx[off + i] = dy[off + i] / s - xi * xdy / (s * s * s);",
+     "dx[off + i] = dy[off + i] / s - xi * xdy / (s * s);"),
+    ("norm_grad_without_eps", "const double s = sqrt(ss + eps);", "const double s = sqrt(ss);"),
+    ("gate_grad_softplus_for_sigmoid", "da[i] = dg[i] * (-e * sig);", "da[i] = dg[i] * (-e * log1p(exp(z)));"),
+    ("gate_grad_sign", "da[i] = dg[i] * (-e * sig);", "da[i] = dg[i] * (e * sig);"),
+    ("beta_grad_as_beta", "db[i] = dbeta[i] * beta * (1.0 - beta);", "db[i] = dbeta[i] * beta;"),
+    ("A_log_grad_missing_g", "dA_log[h] += dg[i] * g;", "dA_log[h] += dg[i];"),
+    ("dt_bias_grad_from_dg", "ddt_bias[h] += da[i];", "ddt_bias[h] += dg[i];"),
+    ("gate_grad_ignores_dt_bias", "const double z = (double)a[i] + (dt_bias ? (double)dt_bias[h] : 0.0);\n"
+     "            const double e", "const double z = (double)a[i];\n            const double e"),
+]
+
+CONV_GRAD_MUTANTS = [
+    ("silu_grad_as_sigmoid", "dz *= sig * (1.0 + z * (1.0 - sig));", "dz *= sig;"),
+    ("conv_grad_taps_reversed", "dwin[t + j] += (double)w[(int64_t)c * K + j] * dz;",
+     "dwin[t + j] += (double)w[(int64_t)c * K + (K - 1 - j)] * dz;"),
+    ("dw_from_next_token", "dw[(int64_t)c * K + j] += dz * win[t + j];",
+     "dw[(int64_t)c * K + j] += dz * win[t + j + 1];"),
+    ("dbias_from_dy", "dbias[c] += dz;", "dbias[c] += dy[(tb + t) * C + c];"),
+    ("dstate_newest_first", "dstate[((int64_t)n * C + c) * M + m] = dwin[m];",
+     "dstate[((int64_t)n * C + c) * M + m] = dwin[M - 1 - m];"),
+    ("dx_shifted", "dx[(tb + t) * C + c] = dwin[M + t];", "dx[(tb + t) * C + c] = dwin[M + t - 1];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PRE_GRAD_MUTANTS + CONV_GRAD_MUTANTS,
+                         ids=[m[0] for m in PRE_GRAD_MUTANTS + CONV_GRAD_MUTANTS])
+def test_preprocessing_and_conv_gradient_pins_catch_mutant(tmp_path, name, old, new):
+    with open(oracle_mod.SOURCE) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation site for %s not found once in the oracle source" % name
+    mpath = tmp_path / ("pg_mutant_%s.c" % name)
+    mpath.write_text(src.replace(old, new))
+    lib = str(tmp_path / ("libpg_mutant_%s.so" % name))
+    oracle.build(str(mpath), lib)
+    caught = []
+    if any(name == m[0] for m in PRE_GRAD_MUTANTS):
+        pb = functools.partial(oracle_mod.preprocess_backward, library=lib)
+        pre = functools.partial(oracle_mod.preprocess, library=lib)
+        pins = [functools.partial(p, pb, pre) for p in oracle_pins.PRE_GRAD_PINS]
+    else:
+        cb = functools.partial(oracle_mod.short_conv_backward, library=lib)
+        conv = functools.partial(oracle_mod.short_conv, library=lib)
+        pins = [functools.partial(p, cb, conv) for p in oracle_pins.CONV_GRAD_PINS]
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            caught.append(pin.func.__name__)
+    assert caught, "gradient mutant %s passed every pin" % name
+
+
 @pytest.mark.parametrize("name,old,new", GRAD_MUTANTS, ids=[m[0] for m in GRAD_MUTANTS])
 def test_gradient_pins_catch_mutant(tmp_path, name, old, new):
     with open(oracle_mod.SOURCE) as f:
