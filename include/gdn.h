@@ -437,6 +437,54 @@ gdn_status gdn_fwd_chunked(const gdn_dims *dims,
                            const gdn_chunk_state *in, const gdn_chunk_state *out,
                            void *o, void *workspace, uint64_t workspace_bytes, void *stream);
 
+/*
+ * Chunked backward: the gradients of gdn_bwd_varlen (same operation, inputs and
+ * outputs; dims->pre must be NULL) taken chunk by chunk on the matrix cores.  The
+ * page "Defending Against the Training-Inference Numeric Mismatch in RL (Especially
+ * Linear Attention)" (section 3.2, "Solution") keeps every forward on the recurrent
+ * kernel and the chunked kernel for the training backward; this is that backward,
+ * for the recurrence gdn_fwd_varlen computes.
+ *
+ * In the notation of gdn_fwd_chunked (chunks at positions 16c .. 16c+15, l the
+ * chunk's last token, x_m = v_m - Gam_m S0 k_m, U = T (beta x)), with D = dL/dS
+ * after the chunk and dO its output gradients, a chunk contributes
+ *
+ *   dU = B^T dO + Gam_{l,.} (K D^T),   dR = T^T dU,   dv = beta dR,
+ *   dB = dO U^T,  dA = -dR U^T,  H[m][r] = dA[m][r] beta_m Gam_{m,r}  (r < m),
+ *   dq_m  = Gam_m S0^T dO_m + sum_{s<=m} dB[m][s] Gam_{m,s} k_s,
+ *   dk_s  = -beta_s Gam_s S0^T dR_s + Gam_{l,s} D^T u_s + sum_{m>=s} dB[m][s] Gam_{m,s} q_m
+ *           + sum_r (H[s][r] + H[r][s]) k_r,
+ *   dbeta_m = dR_m . x_m + sum_{r<m} dA[m][r] Gam_{m,r} (k_m . k_r),
+ *   D at the chunk's start = Gam_l D + sum_m Gam_m dO_m q_m^T - sum_m beta_m Gam_m dR_m k_m^T,
+ *
+ * dg as in gdn_bwd_varlen (<dhT, hT> plus the reverse sum of dO . o - dv . v) and
+ * dh0 = D at the sequence's start.  A forward walk over the chunks first stores
+ * the state at every chunk's start in the workspace; one workgroup per sequence and
+ * value head then walks the chunks backwards.  Every sum has a fixed order and
+ * nothing crosses sequences: the gradients are deterministic and do not depend on
+ * the batch (fp32 computations, equal to gdn_bwd_varlen's to rounding, not
+ * bitwise).
+ *
+ *   workspace : device scratch of at least gdn_bwd_chunked_workspace_size bytes,
+ *               16-byte aligned, owned by the caller; contents on entry do not
+ *               matter.  About 4 dv dk bytes per (16-token chunk, value head) for the
+ *               chunk-start states, plus 4 hv (dv + 2 dk) bytes per token (the
+ *               second term only when hv > hk) and 4.3 KB per (chunk, value head).
+ * dk must be 64 or 128, dv 32, 64 or 128 and hv / hk at most 16 (else
+ * GDN_ERR_UNSUPPORTED, as are dims->pre, plan_lanes and plan_rows; plan_waves
+ * (0, 1, 2 or 4) sets the forward walk's waves per 16-row tile).  Other errors as
+ * gdn_bwd_varlen.
+ */
+gdn_status gdn_bwd_chunked_workspace_size(const gdn_dims *dims, uint64_t *bytes);
+
+gdn_status gdn_bwd_chunked(const gdn_dims *dims,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           const float *h0, const int32_t *cu_seqlens,
+                           const void *dout, const float *dhT,
+                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dh0,
+                           void *workspace, uint64_t workspace_bytes, void *stream);
+
 /* Human-readable description of a status code (static storage; an unknown code
  * gives "unknown gdn_status").  Every refusal is reported as one of these codes rather than
  * served by another, non-invariant path: the bitwise-parity post on linear
@@ -448,7 +496,7 @@ const char *gdn_status_string(gdn_status status);
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 207
+#define GDN_ABI_VERSION 208
 
 #ifdef __cplusplus
 }

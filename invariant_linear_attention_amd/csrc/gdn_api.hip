@@ -631,6 +631,139 @@ gdn_status gdn_fwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+}  // extern "C"
+
+namespace gdn {
+namespace {
+
+// Workspace of the chunked backward, byte offsets (each 256-byte aligned).
+struct BwdChunkWorkspace {
+    uint64_t rec, ck, xv, hdot, dq, dk, total;
+};
+
+uint64_t round256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
+
+BwdChunkWorkspace bwd_chunked_workspace(int64_t T, int64_t N, int hk, int hv, int dk, int dv) {
+    BwdChunkWorkspace w{};
+    const uint64_t slots = (uint64_t)chunk_ws_slots(T, N);
+    uint64_t o = 0;
+    w.rec = o; o = round256(o + slots * hv * kChunkRecBwd * 4);
+    w.ck = o; o = round256(o + slots * hv * (uint64_t)ck_stride_floats(dk, dv) * 4);
+    w.xv = o; o = round256(o + (uint64_t)T * hv * dv * 4);
+    w.hdot = o; o = round256(o + (uint64_t)N * hv * (dv / 16) * 4 * 4);
+    w.dq = o; o = round256(o + (hv > hk ? (uint64_t)T * hv * dk * 4 : 0));
+    w.dk = o; o = round256(o + (hv > hk ? (uint64_t)T * hv * dk * 4 : 0));
+    w.total = o;
+    return w;
+}
+
+gdn_status bwd_chunked_check_dims(const gdn_dims *dims) {
+    gdn_status st = check_common(dims);
+    if (st != GDN_OK) return st;
+    const gdn_dims &d = *dims;
+    if (d.pre || d.plan_lanes || d.plan_rows) return GDN_ERR_UNSUPPORTED;
+    if (d.plan_waves != 0 && d.plan_waves != 1 && d.plan_waves != 2 && d.plan_waves != 4) return GDN_ERR_UNSUPPORTED;
+    if ((d.dk != 64 && d.dk != 128) || (d.dv != 32 && d.dv != 64 && d.dv != 128) || d.hv / d.hk > 16)
+        return GDN_ERR_UNSUPPORTED;
+    if (d.n_seqs == 0 && d.total_tokens != 0) return GDN_ERR_SHAPE;
+    return GDN_OK;
+}
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" {
+
+gdn_status gdn_bwd_chunked_workspace_size(const gdn_dims *dims, uint64_t *bytes) {
+    using namespace gdn;
+    if (!bytes) return GDN_ERR_NULL;
+    const gdn_status st = bwd_chunked_check_dims(dims);
+    if (st != GDN_OK) return st;
+    const gdn_dims &d = *dims;
+    *bytes = bwd_chunked_workspace(d.total_tokens, d.n_seqs, d.hk, d.hv, d.dk, d.dv).total;
+    return GDN_OK;
+}
+
+gdn_status gdn_bwd_chunked(const gdn_dims *dims, const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *h0, const int32_t *cu_seqlens, const void *dout,
+                           const float *dhT, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dh0,
+                           void *workspace, uint64_t workspace_bytes, void *stream) {
+    using namespace gdn;
+    gdn_status st = bwd_chunked_check_dims(dims);
+    if (st != GDN_OK) return st;
+    const gdn_dims &d = *dims;
+    const int64_t T = d.total_tokens, N = d.n_seqs;
+    if (N == 0) return GDN_OK;
+    if (!cu_seqlens || !workspace) return GDN_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
+        return GDN_ERR_NULL;
+    const BwdChunkWorkspace ws = bwd_chunked_workspace(T, N, d.hk, d.hv, d.dk, d.dv);
+    if (workspace_bytes < ws.total) return GDN_ERR_SHAPE;
+    const int64_t slots = chunk_ws_slots(T, N);
+    if (slots > 0x7FFFFFFFll || N * d.hv * (int64_t)(d.dv / 16) > 0x7FFFFFFFll ||
+        (T * d.hk * d.dk / 4 + 255) / 256 > 0x7FFFFFFFll)
+        return GDN_ERR_SHAPE;  // 1-D grids
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(h0, 16) ||
+        !aligned(dhT, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dh0, 16) ||
+        !aligned(workspace, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(dg, 4) || !aligned(dbeta, 4) ||
+        !aligned(cu_seqlens, 4))
+        return GDN_ERR_ALIGN;
+
+    const uint64_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
+    const uint64_t qk_n = (uint64_t)T * d.hk * d.dk, vo_n = (uint64_t)T * d.hv * d.dv;
+    const uint64_t gb_bytes = (uint64_t)T * d.hv * 4, s_bytes = (uint64_t)N * d.hv * d.dv * d.dk * 4;
+    const Range inputs[] = {range_of(q, qk_n * esz), range_of(k, qk_n * esz), range_of(v, vo_n * esz),
+                            range_of(g, gb_bytes), range_of(beta, gb_bytes), range_of(h0, h0 ? s_bytes : 0),
+                            range_of(cu_seqlens, (uint64_t)(N + 1) * 4), range_of(dout, vo_n * esz),
+                            range_of(dhT, dhT ? s_bytes : 0)};
+    const Range outputs[] = {range_of(dq, qk_n * 4), range_of(dk, qk_n * 4), range_of(dv, vo_n * 4),
+                             range_of(dg, gb_bytes), range_of(dbeta, gb_bytes), range_of(dh0, dh0 ? s_bytes : 0),
+                             range_of(workspace, ws.total)};
+    for (size_t i = 0; i < sizeof(outputs) / sizeof(outputs[0]); ++i) {
+        for (const Range &in : inputs)
+            if (overlap(outputs[i], in)) return GDN_ERR_ALIAS;
+        for (size_t j = i + 1; j < sizeof(outputs) / sizeof(outputs[0]); ++j)
+            if (overlap(outputs[i], outputs[j])) return GDN_ERR_ALIAS;
+    }
+
+    char *w = static_cast<char *>(workspace);
+    const hipStream_t strm = static_cast<hipStream_t>(stream);
+    const int rank = (N > 1 && N <= kMaxRankedSeqs && T >= 32 * N) ? 1 : 0;
+    const int64_t units = N * d.hv * (int64_t)(d.dv / 16);
+    const int fw_waves = d.plan_waves ? d.plan_waves : (units < 1024 ? 4 : (units <= 4096 ? 2 : 1));
+
+    // forward walk: records, the state at every chunk's start, x = v - Gam P, <dhT, hT>
+    ChunkedParams f{};
+    f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.cu_seqlens = cu_seqlens;
+    f.in_S = h0;
+    f.ws = reinterpret_cast<float *>(w + ws.rec);
+    f.ws_slots = slots;
+    f.total_tokens = T; f.n_seqs = (int32_t)N; f.hk = d.hk; f.hv = d.hv; f.dk = d.dk; f.dv = d.dv;
+    f.rank_by_length = rank;
+    f.waves = fw_waves;
+    f.ck = reinterpret_cast<float *>(w + ws.ck);
+    f.ck_stride = ck_stride_floats(d.dk, d.dv);
+    f.xv = reinterpret_cast<float *>(w + ws.xv);
+    f.dhT = dhT;
+    f.hdot = reinterpret_cast<float *>(w + ws.hdot);
+    hipError_t e = launch_chunked_bwd_walk(f, d.io_dtype, strm);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+
+    BwdChunkParams p{};
+    p.q = q; p.k = k; p.v = v; p.dout = dout; p.beta = beta; p.dhT = dhT; p.cu_seqlens = cu_seqlens;
+    p.rec = f.ws; p.ck = f.ck; p.xv = f.xv; p.hdot = f.hdot;
+    p.grad_v = dv; p.grad_g = dg; p.grad_beta = dbeta; p.grad_h0 = dh0;
+    p.grad_q = dq; p.grad_k = dk;
+    p.dqh = d.hv > d.hk ? reinterpret_cast<float *>(w + ws.dq) : dq;
+    p.dkh = d.hv > d.hk ? reinterpret_cast<float *>(w + ws.dk) : dk;
+    p.ws_slots = slots; p.ck_stride = f.ck_stride; p.total_tokens = T;
+    p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dk = d.dk; p.dv = d.dv;
+    p.rank_by_length = rank;
+    p.hdot_parts = (d.dv / 16) * 4;  // one per (16-row tile, dk quarter)
+    e = launch_bwd_chunked(p, d.io_dtype, strm);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 const char *gdn_status_string(gdn_status status) {
     switch (status) {
         case GDN_OK: return "GDN_OK";

@@ -1,0 +1,529 @@
+// gdn_bwd_chunked.hip -- gradients of the gated delta rule in the chunked (WY) form,
+// on the matrix cores (gdn_bwd_chunked).
+//
+// The page "Defending Against the Training-Inference Numeric Mismatch in RL
+// (Especially Linear Attention)" (section 3.2, "Solution") runs the recurrence token
+// by token in every forward and keeps the chunked kernel for the training backward.
+// This is that backward: the gradients of the same recurrence, taken chunk by chunk
+// (16 tokens at positions 16c .. 16c + 15 of a sequence) with every product against a
+// state on fp32 MFMA.
+//
+// Within a chunk (notation of gdn_chunked.hip: S0 the state at its start, Gam_{m,s}
+// the decay products, Gam_m = Gam_{m,0} a_0, T = (I + A)^-1, B[m][s] = Gam_{m,s}
+// (q_m . k_s), x_m = v_m - Gam_m S0 k_m, R = beta x, U = T R, O = Gam S0 Q + B U, and
+// the state after the chunk's last token l: S1 = Gam_l S0 + sum_s Gam_{l,s} u_s k_s^T),
+// given D = dL/dS1 and dO:
+//
+//     E     = K D^T                          dU = B^T dO + Gam_{l,.} E
+//     dR    = T^T dU                         dv = beta dR
+//     dB    = dO U^T  (s <= m)               dA = -dR U^T  (s < m)
+//     dq_m  = Gam_m S0^T dO_m + sum_s dB[m][s] Gam_{m,s} k_s
+//     dk_s  = -beta_s Gam_s S0^T dR_s + Gam_{l,s} D^T u_s + sum_m dB[m][s] Gam_{m,s} q_m
+//             + sum_r (H[s][r] + H[r][s]) k_r,        H[m][r] = dA[m][r] beta_m Gam_{m,r}
+//     dbeta_m = dR_m . x_m + sum_r dA[m][r] Gam_{m,r} (k_m . k_r)
+//     dL/dS0 = Gam_l D + sum_m Gam_m dO_m q_m^T - sum_m beta_m Gam_m dR_m k_m^T
+//
+// and the gate gradient needs no derivative of the decay products: with Phi_t =
+// <dL/dS_t, S_t>, dg_t = <dhT, hT> + sum_{s >= t} (dO_s . o_s - dv_s . v_s) over the
+// sequence, and dO_s . o_s = q_s . dq_s (dq of this value head).
+//
+// Launches: the chunked form's prep kernel (records with T, B, Gam and the two extra
+// tables), its main kernel as a forward walk that stores the state at every chunk's
+// start and x = v - Gam P, then the reverse walk below (one workgroup per sequence and
+// value head, all of its state in the workgroup) and, when value heads share key
+// heads, a fixed-order sum of dq and dk over them.  Every sum has a fixed order and
+// nothing crosses sequences, so the gradients are deterministic and batch-invariant.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_internal.hpp"
+#include "gdn_mfma.hpp"
+
+#pragma clang fp contract(off)
+
+namespace gdn {
+namespace {
+
+constexpr int kCk = kChunkLen;
+
+// What one chunk of the reverse walk reads from global memory, per lane.
+template <int DK, int DV, class IO>
+struct RevFetch {
+    static constexpr int NW = DV / 16, NT = DK / 16, CTW = (NT + NW - 1) / NW, RT = DV / 16;
+    static constexpr int KITEMS = kCk * DK / 4;                      // 4-element items of a K (or Q) tile
+    static constexpr int KIT = (KITEMS + 64 * NW - 1) / (64 * NW);   // per lane
+    static constexpr int EPT = (kCk * kCk + 64 * NW - 1) / (64 * NW);  // 16 x 16 entries per lane
+    typename Raw4<IO>::T kr[KIT], qr[KIT];
+    uint32_t dor[4], vr[4];   // dO and v bits, token 4 g + c, row r0 + x
+    float xr[4];              // x = v - Gam P, same place
+    float4 bet, gam, wl;      // beta, Gam_m and Gam_{l,m} of tokens 4 g .. 4 g + 3
+    float bx, gx, wx, gl;     // beta, Gam and Gam_{l,x} of token x; Gam_l
+    float4 trow;              // T[x][4 g ..]
+    float tcol[4], bcol[4];   // T[4 g + c][x], B[4 g + c][x]
+    float ge[EPT], ae[EPT], be[EPT];  // Gam_{m,s}, Gam_{m,s} (k_m . k_s) and beta_m of entries tid + 64 NW e
+};
+
+template <int DK, int DV, class IO>
+__global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdChunkParams p) {
+    using RF = RevFetch<DK, DV, IO>;
+    using RW = Raw4<IO>;
+    constexpr int NW = RF::NW, NT = RF::NT, CTW = RF::CTW, RT = RF::RT;
+    constexpr int KP = DK + 4, VP = DV + 4;
+    constexpr int NTH = 64 * NW;
+    // (16-byte aligned: read and written as float4)
+    __shared__ __align__(16) float Ks[kCk][KP];
+    __shared__ __align__(16) float Qs[kCk][KP];
+    __shared__ __align__(16) float dOs[kCk][VP];  // token rows of dO, dR and U
+    __shared__ __align__(16) float dRs[kCk][VP];
+    __shared__ __align__(16) float Us[kCk][VP];
+    __shared__ __align__(16) float Ds[DV][KP];    // D = dL/dS at the chunk's end
+    __shared__ float dBp[NW][kCk][kCk + 1], dAp[NW][kCk][kCk + 1];
+    __shared__ float Ms[kCk][kCk + 1], Hs[kCk][kCk + 1];       // dB Gam (s <= m), dA beta Gam (s < m)
+    __shared__ float Ab[kCk][kCk + 1];                         // dA Gam (k.k), summed into dbeta
+    __shared__ float red[NW][kCk][4];                          // per wave and token: dR.x, dv.v, q.dq
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int x = lane & 15, g = lane >> 4;
+    // Workgroups that read the same keys and queries (one sequence and key head) get
+    // ids equal modulo 8, so they run on one XCD and share its L2.
+    int rank, h;
+    {
+        const int G = p.hv / p.hk;
+        const int ngroups = p.n_seqs * p.hk;
+        const int full = (ngroups / 8) * 8 * G;
+        const int id = blockIdx.x;
+        int grp, member;
+        if (id < full) {
+            const int xcd = id % 8, slot = id / 8;
+            grp = (slot / G) * 8 + xcd;
+            member = slot % G;
+        } else {
+            grp = full / G + (id - full) / G;
+            member = (id - full) % G;
+        }
+        rank = grp / p.hk;
+        h = (grp % p.hk) * G + member;
+    }
+    const int n = p.rank_by_length ? seq_by_length_rank(p.cu_seqlens, p.n_seqs, rank, tid, NTH) : rank;
+    const int kh = h / (p.hv / p.hk);
+    const int r0 = 16 * wave;  // this wave's state rows
+    int64_t tb = p.cu_seqlens[n], te = p.cu_seqlens[n + 1];
+    tb = tb < 0 ? 0 : (tb > p.total_tokens ? p.total_tokens : tb);
+    te = te < tb ? tb : (te > p.total_tokens ? p.total_tokens : te);
+    const int64_t len = te - tb;
+    const int64_t base = chunk_slot_base(tb, n);
+    int nch = (int)((len + kCk - 1) / kCk);
+    if (base + nch > p.ws_slots) nch = (int)(p.ws_slots - base > 0 ? p.ws_slots - base : 0);
+    const size_t krow = (size_t)p.hk * DK, vrow = (size_t)p.hv * DV;
+    constexpr uint32_t E = IO::ESZ;
+
+    // D = dL/dS, rows r0 .. r0 + 15, held transposed: lane x + 16 g, tile t, component c
+    // is D[r0 + x][16 t + 4 g + c]
+    f4 Dt[NT];
+    {
+        const float *src = p.dhT ? p.dhT + (((size_t)n * p.hv + h) * DV + r0 + x) * DK : nullptr;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            Dt[t] = f4_zero();
+            if (src) {
+                const float4 v4 = *reinterpret_cast<const float4 *>(src + 16 * t + 4 * g);
+                Dt[t] = f4{v4.x, v4.y, v4.z, v4.w};
+            }
+        }
+    }
+    // <dhT, hT> from the forward walk's partial sums, in order
+    float carry = 0.f;
+    if (p.dhT)
+        for (int i = 0; i < p.hdot_parts; ++i) carry = carry + p.hdot[((size_t)n * p.hv + h) * p.hdot_parts + i];
+
+    auto clampm = [](int m, int hi) { return m >= hi ? hi - 1 : m; };
+    auto fetch = [&](RF &F, int j_) {
+        const int j = j_ < 0 ? 0 : j_;  // past the first chunk: repeat its reads
+        const int64_t left = len - (int64_t)kCk * j;
+        const int m1 = left < kCk ? (int)left : kCk;
+        const int64_t t0 = tb + (int64_t)kCk * j;
+        const char *kb = static_cast<const char *>(p.k) + ((size_t)t0 * p.hk + kh) * DK * E;
+        const char *qb = static_cast<const char *>(p.q) + ((size_t)t0 * p.hk + kh) * DK * E;
+        const uint32_t krow_b = (uint32_t)krow * E;
+#pragma unroll
+        for (int s = 0; s < RF::KIT; ++s) {
+            int it = tid + NTH * s;
+            it = it < RF::KITEMS ? it : RF::KITEMS - 1;
+            const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+            const uint32_t off = (uint32_t)clampm(m, m1) * krow_b + (uint32_t)c * E;
+            F.kr[s] = RW::load_at(kb, off);
+            F.qr[s] = RW::load_at(qb, off);
+        }
+        const char *ob = static_cast<const char *>(p.dout) + ((size_t)t0 * p.hv + h) * DV * E;
+        const char *vb = static_cast<const char *>(p.v) + ((size_t)t0 * p.hv + h) * DV * E;
+        const float *xb = p.xv + ((size_t)t0 * p.hv + h) * DV;
+        const uint32_t vrow_b = (uint32_t)vrow * E;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t tm = (uint32_t)clampm(4 * g + c, m1);
+            F.dor[c] = RW::load1_at(ob, tm * vrow_b + (uint32_t)(r0 + x) * E);
+            F.vr[c] = RW::load1_at(vb, tm * vrow_b + (uint32_t)(r0 + x) * E);
+            F.xr[c] = xb[(size_t)tm * vrow + r0 + x];
+        }
+        const float *rec = p.rec + ((size_t)(base + j) * p.hv + h) * kChunkRecBwd;
+        const int l = m1 - 1;
+        F.bet = *reinterpret_cast<const float4 *>(rec + kRecBeta + 4 * g);
+        F.gam = *reinterpret_cast<const float4 *>(rec + kRecGam + 4 * g);
+        F.wl = *reinterpret_cast<const float4 *>(rec + kRecGm + l * kCk + 4 * g);
+        F.bx = rec[kRecBeta + x];
+        F.gx = rec[kRecGam + x];
+        F.wx = rec[kRecGm + l * kCk + x];
+        F.gl = rec[kRecGam + l];
+        F.trow = *reinterpret_cast<const float4 *>(rec + kRecT + x * kCk + 4 * g);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            F.tcol[c] = rec[kRecT + (4 * g + c) * kCk + x];
+            F.bcol[c] = rec[kRecB + (4 * g + c) * kCk + x];
+        }
+#pragma unroll
+        for (int e = 0; e < RF::EPT; ++e) {
+            int i = tid + NTH * e;
+            i = i < kCk * kCk ? i : kCk * kCk - 1;
+            F.ge[e] = rec[kRecGm + i];
+            F.ae[e] = rec[kRecAb + i];
+            F.be[e] = rec[kRecBeta + i / kCk];
+        }
+    };
+    // The chunk's start state, this wave's column tiles in the B-operand layout (read
+    // a chunk ahead, once the current one is no longer needed).
+    f4 s0[RT][CTW];
+    auto fetch_s0 = [&](int j_) {
+        const int j = j_ < 0 ? 0 : j_;
+        const float *ck = p.ck + ((size_t)(base + j) * p.hv + h) * p.ck_stride;
+#pragma unroll
+        for (int l2 = 0; l2 < CTW; ++l2)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const float4 v4 = *reinterpret_cast<const float4 *>(ck + (((size_t)wave * CTW + l2) * RT + rt) * 256 + 4 * lane);
+                s0[rt][l2] = f4{v4.x, v4.y, v4.z, v4.w};
+            }
+    };
+
+    RF F;
+    if (nch > 0) {
+        fetch(F, nch - 1);
+        fetch_s0(nch - 1);
+    }
+    for (int j = nch - 1; j >= 0; --j) {
+        const int64_t left = len - (int64_t)kCk * j;
+        const int m1 = left < kCk ? (int)left : kCk;
+        const int64_t t0 = tb + (int64_t)kCk * j;
+
+        // ---- stage this chunk: keys and queries into LDS, the rest into registers
+#pragma unroll
+        for (int s = 0; s < RF::KIT; ++s) {
+            const int it = tid + NTH * s;
+            if (it < RF::KITEMS) {
+                const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+                const bool on = m < m1;
+                *reinterpret_cast<float4 *>(&Ks[m][c]) = RW::widen(RW::keep(F.kr[s], on));
+                *reinterpret_cast<float4 *>(&Qs[m][c]) = RW::widen(RW::keep(F.qr[s], on));
+            }
+        }
+        float dO[4], vv[4], xx[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bool on = 4 * g + c < m1;
+            dO[c] = on ? RW::widen1(F.dor[c]) : 0.f;
+            vv[c] = on ? RW::widen1(F.vr[c]) : 0.f;
+            xx[c] = on ? F.xr[c] : 0.f;
+        }
+        const float bt[4] = {F.bet.x, F.bet.y, F.bet.z, F.bet.w};
+        const float gm[4] = {F.gam.x, F.gam.y, F.gam.z, F.gam.w};
+        const float wl[4] = {F.wl.x, F.wl.y, F.wl.z, F.wl.w};
+        const float bx = F.bx, gx = F.gx, wx = F.wx, gl = F.gl;
+        const float4 trow = F.trow;
+        float tcol[4], bcol[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            tcol[c] = F.tcol[c];
+            bcol[c] = F.bcol[c];
+        }
+        float ge[RF::EPT], ae[RF::EPT], be[RF::EPT];
+#pragma unroll
+        for (int e = 0; e < RF::EPT; ++e) {
+            ge[e] = F.ge[e];
+            ae[e] = F.ae[e];
+            be[e] = F.be[e];
+        }
+        fetch(F, j - 1);
+        lds_barrier();
+
+        // ---- E = K D^T on this wave's rows (token 4 g + c, row r0 + x)
+        f4 Ev = f4_zero();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float4 ka = *reinterpret_cast<const float4 *>(&Ks[x][16 * t + 4 * g]);
+            Ev = mfma_16x16x4(ka.x, Dt[t][0], Ev);
+            Ev = mfma_16x16x4(ka.y, Dt[t][1], Ev);
+            Ev = mfma_16x16x4(ka.z, Dt[t][2], Ev);
+            Ev = mfma_16x16x4(ka.w, Dt[t][3], Ev);
+        }
+        // dU = Gam_{l,.} E + B^T dO;  dR = T^T dU;  U = T (beta x)
+        f4 dU = f4{wl[0] * Ev[0], wl[1] * Ev[1], wl[2] * Ev[2], wl[3] * Ev[3]};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dU = mfma_16x16x4(bcol[c], dO[c], dU);
+        f4 dR = f4_zero();
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dR = mfma_16x16x4(tcol[c], dU[c], dR);
+        f4 U = f4_zero();
+        U = mfma_16x16x4(trow.x, bt[0] * xx[0], U);
+        U = mfma_16x16x4(trow.y, bt[1] * xx[1], U);
+        U = mfma_16x16x4(trow.z, bt[2] * xx[2], U);
+        U = mfma_16x16x4(trow.w, bt[3] * xx[3], U);
+
+        // dv = beta dR; the row sums dR . x and dv . v of this wave's rows
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int m = 4 * g + c;
+            const float dvv = bt[c] * dR[c];
+            if (m < m1) p.grad_v[(size_t)(t0 + m) * vrow + (size_t)h * DV + r0 + x] = dvv;
+            const float sb = sum16(dR[c] * xx[c]);
+            const float sv = sum16(dvv * vv[c]);
+            if (x == 0) {
+                red[wave][m][0] = sb;
+                red[wave][m][1] = sv;
+            }
+        }
+        // token rows of dO, dR and U, and D at the chunk's end, for the products over rows
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            // (the values pass through vector registers first: stores straight from the
+            // MFMA accumulators were merged with wrong offsets by the compiler)
+            float dr = dR[c], uu = U[c];
+            asm volatile("" : "+v"(dr), "+v"(uu));
+            dOs[4 * g + c][r0 + x] = dO[c];
+            dRs[4 * g + c][r0 + x] = dr;
+            Us[4 * g + c][r0 + x] = uu;
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<float4 *>(&Ds[r0 + x][16 * t + 4 * g]) = make_float4(Dt[t][0], Dt[t][1], Dt[t][2], Dt[t][3]);
+
+        // ---- D at the chunk's start: D^T = Gam_l D^T + Q^T (Gam dO) - K^T (beta Gam dR)
+        {
+            float bq[4], bk[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                bq[c] = gm[c] * dO[c];
+                bk[c] = -(bt[c] * gm[c]) * dR[c];
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                f4 C = f4{gl * Dt[t][0], gl * Dt[t][1], gl * Dt[t][2], gl * Dt[t][3]};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) C = mfma_16x16x4(Qs[4 * g + c][16 * t + x], bq[c], C);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) C = mfma_16x16x4(Ks[4 * g + c][16 * t + x], bk[c], C);
+                Dt[t] = C;
+            }
+        }
+        lds_barrier();
+
+        // ---- partial dB = dO U^T and dA = -dR U^T over this wave's rows
+        {
+            const float4 o4 = *reinterpret_cast<const float4 *>(&dOs[x][r0 + 4 * g]);
+            const float4 r4 = *reinterpret_cast<const float4 *>(&dRs[x][r0 + 4 * g]);
+            const float4 u4 = *reinterpret_cast<const float4 *>(&Us[x][r0 + 4 * g]);
+            f4 pb = f4_zero(), pa = f4_zero();
+            pb = mfma_16x16x4(o4.x, u4.x, pb);
+            pb = mfma_16x16x4(o4.y, u4.y, pb);
+            pb = mfma_16x16x4(o4.z, u4.z, pb);
+            pb = mfma_16x16x4(o4.w, u4.w, pb);
+            pa = mfma_16x16x4(-r4.x, u4.x, pa);
+            pa = mfma_16x16x4(-r4.y, u4.y, pa);
+            pa = mfma_16x16x4(-r4.z, u4.z, pa);
+            pa = mfma_16x16x4(-r4.w, u4.w, pa);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                dBp[wave][4 * g + r][x] = pb[r];
+                dAp[wave][4 * g + r][x] = pa[r];
+            }
+        }
+
+        // ---- products over the rows on this wave's column tiles:
+        //      dq0 = dO S0,  dk1 = (-beta Gam dR) S0 + (Gam_{l,.} U) D
+        f4 dq[CTW], dk[CTW];
+        {
+            const float fr = -(bx * gx), fu = wx;  // factors of A-operand row x (token x)
+#pragma unroll
+            for (int l2 = 0; l2 < CTW; ++l2) {
+                const int ct = wave + NW * l2;
+                f4 aq = f4_zero(), ak = f4_zero();
+                if (ct < NT) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        const float4 o4 = *reinterpret_cast<const float4 *>(&dOs[x][16 * rt + 4 * g]);
+                        const float4 r4 = *reinterpret_cast<const float4 *>(&dRs[x][16 * rt + 4 * g]);
+                        const float4 u4 = *reinterpret_cast<const float4 *>(&Us[x][16 * rt + 4 * g]);
+                        const float o[4] = {o4.x, o4.y, o4.z, o4.w};
+                        const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+                        const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            aq = mfma_16x16x4(o[c], s0[rt][l2][c], aq);
+                            ak = mfma_16x16x4(fr * rr[c], s0[rt][l2][c], ak);
+                            ak = mfma_16x16x4(fu * uu[c], Ds[16 * rt + 4 * g + c][16 * ct + x], ak);
+                        }
+                    }
+                }
+                dq[l2] = f4{gm[0] * aq[0], gm[1] * aq[1], gm[2] * aq[2], gm[3] * aq[3]};
+                dk[l2] = ak;
+            }
+        }
+        fetch_s0(j - 1);
+        lds_barrier();
+
+        // ---- dB and dA summed over the waves (in order), masked and weighted
+        for (int e = 0; e < RF::EPT; ++e) {
+            const int i = tid + NTH * e;
+            if (i < kCk * kCk) {
+                const int m = i / kCk, s = i % kCk;
+                float sbv = 0.f, sav = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    sbv = sbv + dBp[w][m][s];
+                    sav = sav + dAp[w][m][s];
+                }
+                Ms[m][s] = sbv * ge[e];                           // Gam is zero above the diagonal
+                Hs[m][s] = s < m ? sav * (be[e] * ge[e]) : 0.f;
+                Ab[m][s] = sav * ae[e];                           // zero unless s < m
+            }
+        }
+        lds_barrier();
+
+        // ---- in-chunk terms: dq += Ms K;  dk += Ms^T Q + (H + H^T) K
+        {
+            float mr[4], mc[4], hh[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                mr[c] = Ms[x][4 * g + c];
+                mc[c] = Ms[4 * g + c][x];
+                hh[c] = Hs[x][4 * g + c] + Hs[4 * g + c][x];
+            }
+            float qd[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int l2 = 0; l2 < CTW; ++l2) {
+                const int ct = wave + NW * l2;
+                if (ct < NT) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dq[l2] = mfma_16x16x4(mr[c], Ks[4 * g + c][16 * ct + x], dq[l2]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(mc[c], Qs[4 * g + c][16 * ct + x], dk[l2]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(hh[c], Ks[4 * g + c][16 * ct + x], dk[l2]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = 4 * g + r;
+                        qd[r] = __builtin_fmaf(Qs[m][16 * ct + x], dq[l2][r], qd[r]);
+                        if (m < m1) {
+                            const size_t o = ((size_t)(t0 + m) * p.hv + h) * DK + 16 * ct + x;
+                            p.dqh[o] = dq[l2][r];
+                            p.dkh[o] = dk[l2][r];
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = sum16(qd[r]);
+                if (x == 0) red[wave][4 * g + r][2] = v;
+            }
+        }
+        lds_barrier();
+
+        // ---- per-token results, in order: dbeta, and dg as a running sum from the end
+        if (tid < kCk) {
+            const int m = tid;
+            float sbv = 0.f, svv = 0.f, sq = 0.f, ab = 0.f;
+            for (int w = 0; w < NW; ++w) {
+                sbv = sbv + red[w][m][0];
+                svv = svv + red[w][m][1];
+                sq = sq + red[w][m][2];
+            }
+            for (int s = 0; s < kCk; ++s) ab = ab + Ab[m][s];
+            if (m < m1) p.grad_beta[(size_t)(t0 + m) * p.hv + h] = sbv + ab;
+            red[0][m][3] = sq - svv;  // dO . o - dv . v
+        }
+        if (tid == 0) {
+            // (wave 0's lane 0 wrote every red[0][m][3] itself)
+            for (int m = m1 - 1; m >= 0; --m) {
+                carry = carry + red[0][m][3];
+                p.grad_g[(size_t)(t0 + m) * p.hv + h] = carry;
+            }
+        }
+        lds_barrier();  // LDS is refilled by the next chunk
+    }
+
+    if (p.grad_h0) {
+        float *dst = p.grad_h0 + (((size_t)n * p.hv + h) * DV + r0 + x) * DK;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<float4 *>(dst + 16 * t + 4 * g) = make_float4(Dt[t][0], Dt[t][1], Dt[t][2], Dt[t][3]);
+    }
+}
+
+// dq and dk of each key head: the value heads that read it, added in head order.
+__global__ __launch_bounds__(256) void gdn_bwd_chunk_gqa_kernel(BwdChunkParams p) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 4-column item
+    const int64_t per_tok = (int64_t)p.hk * p.dk / 4;
+    if (i >= p.total_tokens * per_tok) return;
+    const int64_t t = i / per_tok;
+    const int rem = (int)(i % per_tok);
+    const int kh = rem / (p.dk / 4), c = 4 * (rem % (p.dk / 4));
+    const int G = p.hv / p.hk;
+    const size_t src = ((size_t)t * p.hv + (size_t)kh * G) * p.dk + c;
+    float4 sq = *reinterpret_cast<const float4 *>(p.dqh + src);
+    float4 sk = *reinterpret_cast<const float4 *>(p.dkh + src);
+    for (int gi = 1; gi < G; ++gi) {
+        const float4 a = *reinterpret_cast<const float4 *>(p.dqh + src + (size_t)gi * p.dk);
+        const float4 b = *reinterpret_cast<const float4 *>(p.dkh + src + (size_t)gi * p.dk);
+        sq = make_float4(sq.x + a.x, sq.y + a.y, sq.z + a.z, sq.w + a.w);
+        sk = make_float4(sk.x + b.x, sk.y + b.y, sk.z + b.z, sk.w + b.w);
+    }
+    const size_t dst = ((size_t)t * p.hk + kh) * p.dk + c;
+    *reinterpret_cast<float4 *>(p.grad_q + dst) = sq;
+    *reinterpret_cast<float4 *>(p.grad_k + dst) = sk;
+}
+
+template <int DK, int DV, class IO>
+hipError_t rev_launch(const BwdChunkParams &p, hipStream_t s) {
+    hipLaunchKernelGGL((gdn_bwd_chunk_rev_kernel<DK, DV, IO>), dim3((unsigned)((int64_t)p.n_seqs * p.hv)),
+                       dim3(64 * (DV / 16)), 0, s, p);
+    return hipGetLastError();
+}
+
+template <class IO>
+hipError_t rev_io(const BwdChunkParams &p, hipStream_t s) {
+    if (p.dk == 128) {
+        switch (p.dv) {
+            case 32: return rev_launch<128, 32, IO>(p, s);
+            case 64: return rev_launch<128, 64, IO>(p, s);
+            case 128: return rev_launch<128, 128, IO>(p, s);
+        }
+    } else if (p.dk == 64) {
+        switch (p.dv) {
+            case 32: return rev_launch<64, 32, IO>(p, s);
+            case 64: return rev_launch<64, 64, IO>(p, s);
+            case 128: return rev_launch<64, 128, IO>(p, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_chunked(const BwdChunkParams &p, int io_dtype, hipStream_t s) {
+    hipError_t e = io_dtype == GDN_BF16 ? rev_io<IoBf16>(p, s) : rev_io<IoF32>(p, s);
+    if (e != hipSuccess || p.hv == p.hk || p.total_tokens == 0) return e;
+    const int64_t items = p.total_tokens * p.hk * p.dk / 4;
+    hipLaunchKernelGGL(gdn_bwd_chunk_gqa_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

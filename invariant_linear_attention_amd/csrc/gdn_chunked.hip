@@ -46,10 +46,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "gdn_internal.hpp"
-#include "gdn_kernels.hpp"
+#include "gdn_mfma.hpp"
 
 #pragma clang fp contract(off)
 
@@ -57,22 +55,6 @@ namespace gdn {
 namespace {
 
 constexpr int kCk = kChunkLen;   // tokens per chunk (16)
-
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-// D = C + A B on a 16 x 16 x 4 fp32 tile.  Lane l = x + 16 g supplies A[x][g] and
-// B[g][x]; it receives D[4 g + r][x] in component r.
-__device__ __forceinline__ f4 mfma_16x16x4(float a, float b, f4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f4 f4_zero() { return f4{0.f, 0.f, 0.f, 0.f}; }
-
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not
-// for its global loads (__syncthreads also fences global memory, which would make
-// every chunk wait for the reads it has just sent out for the next one).  The
-// memory clobber keeps the compiler from moving memory operations across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Clamped sequence bounds and chunk bookkeeping shared by both kernels.
 struct SeqChunks {
@@ -105,12 +87,15 @@ __device__ __forceinline__ SeqChunks seq_chunks(const ChunkedParams &p, int n) {
 // the main kernel reads: A[m][r] = (beta_m Gam_{m,r}) (k_m . k_r) for r < m,
 // B[m][s] = Gam_{m,s} (q_m . k_s) for s <= m (rows of the chunk's new tokens only),
 // Gam_m, the chunk-end weights Gam_{15,s} and the decay factors a_m.
-template <int DK, class IO>
+// With BW (the backward's forward walk) the record is kChunkRecBwd floats and also
+// holds Gam_{m,s} for s <= m and Gam_{m,s} (k_m . k_s) for s < m.
+template <int DK, class IO, bool BW>
 __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(ChunkedParams p) {
     constexpr int NT = DK / 16;
+    constexpr int REC = BW ? kChunkRecBwd : kChunkRec;
     constexpr int KP = DK + 4;  // padded LDS row
-    __shared__ float Ks[kCk][KP];
-    __shared__ float Qs[kCk][KP];
+    __shared__ __align__(16) float Ks[kCk][KP];  // (16-byte aligned: accessed as float4)
+    __shared__ __align__(16) float Qs[kCk][KP];
     __shared__ float kap[kCk][kCk + 1];
     __shared__ float xi[kCk][kCk + 1];
 
@@ -208,8 +193,12 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(ChunkedParams p) {
         const bool row = m < m1;
         Am[m][r] = (row && r < m) ? (bet[m] * gmr) * kap[m][r] : 0.f;
         const bool newrow = m >= m0 && m < m1;
-        float *rec = p.ws + ((size_t)slot * p.hv + h) * kChunkRec;
+        float *rec = p.ws + ((size_t)slot * p.hv + h) * REC;
         rec[kRecB + m * kCk + r] = (newrow && r <= m) ? gmr * xi[m][r] : 0.f;
+        if constexpr (BW) {
+            rec[kRecGm + m * kCk + r] = (row && r <= m) ? gmr : 0.f;
+            rec[kRecAb + m * kCk + r] = (row && r < m) ? gmr * kap[m][r] : 0.f;
+        }
         if (r == 0) rec[kRecGam + m] = row ? gmr * dreg[0] : 0.f;
         if (m == kCk - 1) rec[kRecD + r] = gmr;
         if (r == 0) {
@@ -255,46 +244,6 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(ChunkedParams p) {
 // its products, into registers, with rows outside the chunk clamped to a valid row
 // and zeroed after the load (no branch per load).
 
-// Four consecutive io elements as loaded (bf16: 8 bytes, fp32: 16 bytes), widened
-// to fp32 only when used, so that a chunk's prefetched rows take half the registers.
-template <class IO>
-struct Raw4 {
-    using T = typename std::conditional<IO::ESZ == 2, uint2, uint4>::type;
-    __device__ static T load(const void *base, size_t idx) {
-        return *reinterpret_cast<const T *>(static_cast<const char *>(base) + idx * IO::ESZ);
-    }
-    // from a (uniform) base pointer and a 32-bit byte offset: one address add per load
-    __device__ static T load_at(const char *base, uint32_t off) { return *reinterpret_cast<const T *>(base + off); }
-    __device__ static T keep(const T &w, bool on) {
-        T z = w;
-        if constexpr (IO::ESZ == 2) {
-            z.x = on ? w.x : 0u;
-            z.y = on ? w.y : 0u;
-        } else {
-            z.x = on ? w.x : 0u;
-            z.y = on ? w.y : 0u;
-            z.z = on ? w.z : 0u;
-            z.w = on ? w.w : 0u;
-        }
-        return z;
-    }
-    __device__ static float4 widen(const T &w) {
-        if constexpr (IO::ESZ == 2)
-            return make_float4(bf16_to_f32(w.x & 0xffffu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xffffu),
-                               bf16_to_f32(w.y >> 16));
-        else
-            return make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
-    }
-    // one element's bits (bf16 in the low half), widened when used
-    __device__ static uint32_t load1_at(const char *base, uint32_t off) {
-        if constexpr (IO::ESZ == 2)
-            return *reinterpret_cast<const uint16_t *>(base + off);
-        else
-            return *reinterpret_cast<const uint32_t *>(base + off);
-    }
-    __device__ static float widen1(uint32_t w) { return IO::ESZ == 2 ? bf16_to_f32(w & 0xffffu) : __uint_as_float(w); }
-};
-
 // What one chunk needs from global memory, per lane of a W-wave workgroup.
 template <int DK, class IO, int W>
 struct ChunkFetch {
@@ -309,8 +258,13 @@ struct ChunkFetch {
     float g15;                      // Gam_15
 };
 
-template <int DK, class IO, int W>
+// BW: the forward walk of the chunked backward.  No outputs: the state at each
+// chunk's start goes to the checkpoints, x = v - Gam P to xv, and every chunk folds
+// (a sequence's last, partial chunk with the weights of its last token, so that the
+// final state is hT), which gives the partial sums of <dhT, hT>.
+template <int DK, class IO, int W, bool BW>
 __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p) {
+    constexpr int REC = BW ? kChunkRecBwd : kChunkRec;
     constexpr int NT = DK / 16;
     constexpr int KP = DK + 4;
     constexpr int OT = NT / W;       // tiles per wave
@@ -319,7 +273,7 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
     using CF = ChunkFetch<DK, IO, W>;
     using RW = Raw4<IO>;
     static_assert(NT % 4 == 0 && OT * W == NT, "tiles");
-    __shared__ float Ks[kCk][KP];                       // the chunk's keys, fp32
+    __shared__ __align__(16) float Ks[kCk][KP];         // the chunk's keys, fp32 (accessed as float4)
     __shared__ float4 Xch[W > 1 ? 8 : 1][64];           // P and Z partials of the four quarters
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -400,21 +354,29 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
             const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
             F.kr[s] = RW::load_at(kb, (uint32_t)clampm(m, m0, m1) * krow_b + (uint32_t)c * E);
         }
-        const uint32_t qoff = (uint32_t)clampm(x, m0, m1) * krow_b + (uint32_t)(16 * t_first + 4 * g) * E;
+        if constexpr (!BW) {
+            const uint32_t qoff = (uint32_t)clampm(x, m0, m1) * krow_b + (uint32_t)(16 * t_first + 4 * g) * E;
 #pragma unroll
-        for (int t = 0; t < OT; ++t) F.qa[t] = RW::load_at(qb, qoff + 16u * t * E);
+            for (int t = 0; t < OT; ++t) F.qa[t] = RW::load_at(qb, qoff + 16u * t * E);
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const uint32_t tm = (uint32_t)clampm(4 * g + c, m0, m1);
             F.b[c] = *reinterpret_cast<const float *>(bb + tm * brow_b);
             F.v[c] = RW::load1_at(vb, tm * vrow_b + (uint32_t)(row0 + x) * E);
         }
-        const char *rec = reinterpret_cast<const char *>(p.ws + ((size_t)(sc.base + j) * p.hv + h) * kChunkRec);
+        const char *rec = reinterpret_cast<const char *>(p.ws + ((size_t)(sc.base + j) * p.hv + h) * REC);
         F.trow = *reinterpret_cast<const float4 *>(rec + 4u * (kRecT + x * kCk + 4 * g));
-        F.brow = *reinterpret_cast<const float4 *>(rec + 4u * (kRecB + x * kCk + 4 * g));
         F.gam = *reinterpret_cast<const float4 *>(rec + 4u * (kRecGam + 4 * g));
-        F.dw = *reinterpret_cast<const float4 *>(rec + 4u * (kRecD + 4 * g));
-        F.g15 = *reinterpret_cast<const float *>(rec + 4u * (kRecGam + kCk - 1));
+        if constexpr (BW) {
+            // the fold weights of the chunk's last token: Gam_{m1-1, s} and Gam_{m1-1}
+            F.dw = *reinterpret_cast<const float4 *>(rec + 4u * (kRecGm + (m1 - 1) * kCk + 4 * g));
+            F.g15 = *reinterpret_cast<const float *>(rec + 4u * (kRecGam + m1 - 1));
+        } else {
+            F.brow = *reinterpret_cast<const float4 *>(rec + 4u * (kRecB + x * kCk + 4 * g));
+            F.dw = *reinterpret_cast<const float4 *>(rec + 4u * (kRecD + 4 * g));
+            F.g15 = *reinterpret_cast<const float *>(rec + 4u * (kRecGam + kCk - 1));
+        }
     };
 
     int last_m0 = sc.c0, mo = sc.c0;
@@ -424,6 +386,15 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
         if (4 * g + c < sc.c0 && p.in_r) Rkeep[c] = p.in_r[(((size_t)n * kCk + 4 * g + c) * p.hv + h) * p.dv + row0 + x];
+
+    // checkpoint offsets of this lane's state elements (component c at + 4 c): lane
+    // x + 16 g holds S[row0 + x][16 tt + 4 g + c]
+    uint32_t ckoff[BW ? OT : 1];
+    if constexpr (BW) {
+#pragma unroll
+        for (int t = 0; t < OT; ++t)
+            ckoff[t] = (uint32_t)ck_offset(DK, p.dv, row0 + x, 16 * (t_first + t) + 4 * g);
+    }
 
     CF F;
     if (nch > 0) fetch(F, 0);
@@ -448,15 +419,26 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
                     *reinterpret_cast<const float4 *>(p.in_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + c);
             }
         }
-        float4 qv[OT];
+        float4 qv[BW ? 1 : OT];
+        if constexpr (!BW) {
 #pragma unroll
-        for (int t = 0; t < OT; ++t) qv[t] = RW::widen(RW::keep(F.qa[t], x >= m0 && x < m1));
-        float vb[4], bb[4];
+            for (int t = 0; t < OT; ++t) qv[t] = RW::widen(RW::keep(F.qa[t], x >= m0 && x < m1));
+        }
+        float vb[4], bb[4], vraw[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const bool on = 4 * g + c >= m0 && 4 * g + c < m1;
             bb[c] = on ? F.b[c] : 0.f;
-            vb[c] = bb[c] * (on ? RW::widen1(F.v[c]) : 0.f);
+            vraw[c] = on ? RW::widen1(F.v[c]) : 0.f;
+            vb[c] = bb[c] * vraw[c];
+        }
+        if constexpr (BW) {
+            // the state at this chunk's start
+            float *dst = p.ck + ((size_t)(sc.base + j) * p.hv + h) * p.ck_stride;
+#pragma unroll
+            for (int t = 0; t < OT; ++t)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) dst[ckoff[t] + 4 * c] = S[t][c];
         }
         const float4 trow = F.trow, brow = F.brow, gam = F.gam, dwv = F.dw;
         const float g15 = F.g15;
@@ -473,14 +455,21 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
             for (int tt = 0; tt < QT; ++tt) {
                 const int t = q * QT + tt;  // the wave's tile index
                 const float4 ka = *reinterpret_cast<const float4 *>(&Ks[x][16 * (t_first + t) + 4 * g]);
-                Pq[q] = mfma_16x16x4(ka.x, S[t][0], Pq[q]);
-                Zq[q] = mfma_16x16x4(qv[t].x, S[t][0], Zq[q]);
-                Pq[q] = mfma_16x16x4(ka.y, S[t][1], Pq[q]);
-                Zq[q] = mfma_16x16x4(qv[t].y, S[t][1], Zq[q]);
-                Pq[q] = mfma_16x16x4(ka.z, S[t][2], Pq[q]);
-                Zq[q] = mfma_16x16x4(qv[t].z, S[t][2], Zq[q]);
-                Pq[q] = mfma_16x16x4(ka.w, S[t][3], Pq[q]);
-                Zq[q] = mfma_16x16x4(qv[t].w, S[t][3], Zq[q]);
+                if constexpr (BW) {
+                    Pq[q] = mfma_16x16x4(ka.x, S[t][0], Pq[q]);
+                    Pq[q] = mfma_16x16x4(ka.y, S[t][1], Pq[q]);
+                    Pq[q] = mfma_16x16x4(ka.z, S[t][2], Pq[q]);
+                    Pq[q] = mfma_16x16x4(ka.w, S[t][3], Pq[q]);
+                } else {
+                    Pq[q] = mfma_16x16x4(ka.x, S[t][0], Pq[q]);
+                    Zq[q] = mfma_16x16x4(qv[t].x, S[t][0], Zq[q]);
+                    Pq[q] = mfma_16x16x4(ka.y, S[t][1], Pq[q]);
+                    Zq[q] = mfma_16x16x4(qv[t].y, S[t][1], Zq[q]);
+                    Pq[q] = mfma_16x16x4(ka.z, S[t][2], Pq[q]);
+                    Zq[q] = mfma_16x16x4(qv[t].z, S[t][2], Zq[q]);
+                    Pq[q] = mfma_16x16x4(ka.w, S[t][3], Pq[q]);
+                    Zq[q] = mfma_16x16x4(qv[t].w, S[t][3], Zq[q]);
+                }
             }
         }
         f4 P4[4], Z4[4];
@@ -513,8 +502,9 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
         }
 
         // the chunk-end update's key operands (K^T tiles of this wave), read early
+        const bool fold = BW || full;
         float kt[OT][4];
-        if (full) {
+        if (fold) {
 #pragma unroll
             for (int t = 0; t < OT; ++t)
 #pragma unroll
@@ -529,10 +519,17 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
         for (int c = 0; c < 4; ++c) {
             const int m = 4 * g + c;
             const bool on = m >= m0 && m < m1;
-            const float fresh = __builtin_fmaf(-(bb[c] * gm[c]), P[c], vb[c]);
-            R[c] = on ? fresh : (m < m0 ? Rkeep[c] : 0.f);
-            Rkeep[c] = on ? fresh : Rkeep[c];
-            OC[c] = gm[c] * Z[c];
+            if constexpr (BW) {
+                // x = v - Gam P (kept for the reverse walk), R = beta x
+                const float xr = on ? __builtin_fmaf(-gm[c], P[c], vraw[c]) : 0.f;
+                R[c] = bb[c] * xr;
+                if (wave == 0 && on) p.xv[(size_t)(t0 + m) * vrow + (size_t)h * p.dv + row0 + x] = xr;
+            } else {
+                const float fresh = __builtin_fmaf(-(bb[c] * gm[c]), P[c], vb[c]);
+                R[c] = on ? fresh : (m < m0 ? Rkeep[c] : 0.f);
+                Rkeep[c] = on ? fresh : Rkeep[c];
+                OC[c] = gm[c] * Z[c];
+            }
         }
 
         // U = T R, then O = Gam Z + B U (instruction c adds the tokens 4 g + c)
@@ -543,6 +540,7 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
         U = mfma_16x16x4(trow.w, R[3], U);
 #pragma unroll
         for (int c = 0; c < 4; ++c) U[c] = U[c] + 0.f;
+        if constexpr (!BW) {
         f4 O = OC;
         O = mfma_16x16x4(brow.x, U[0], O);
         O = mfma_16x16x4(brow.y, U[1], O);
@@ -555,9 +553,10 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
                 if (m >= m0 && m < m1) IO::store1(p.out, (size_t)(t0 + m) * vrow + (size_t)h * p.dv + row0 + x, O[c] + 0.f);
             }
         }
+        }
 
         // chunk complete: S^T = Gam_15 S^T + K^T W, W[s][row] = Gam_{15,s} u_s (own tiles)
-        if (full) {
+        if (fold) {
             const float w0 = dwv.x * U[0], w1 = dwv.y * U[1], w2 = dwv.z * U[2], w3 = dwv.w * U[3];
 #pragma unroll
             for (int t = 0; t < OT; ++t) {
@@ -575,6 +574,31 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
         lds_barrier();  // Ks and Xch are refilled by the next chunk
     }
 
+    if constexpr (BW) {
+        // partial sums of <dhT, hT>, one per dk quarter of the tile (so the same for
+        // every W), each in a fixed lane order
+        if (p.dhT) {
+            const float *src = p.dhT + (((size_t)n * p.hv + h) * p.dv + row0 + x) * DK;
+#pragma unroll
+            for (int q = 0; q < OQ; ++q) {
+                float acc = 0.f;
+#pragma unroll
+                for (int tt = 0; tt < QT; ++tt) {
+                    const int t = q * QT + tt;
+                    const float4 d4 = *reinterpret_cast<const float4 *>(src + 16 * (t_first + t) + 4 * g);
+                    acc = __builtin_fmaf(S[t][0], d4.x, acc);
+                    acc = __builtin_fmaf(S[t][1], d4.y, acc);
+                    acc = __builtin_fmaf(S[t][2], d4.z, acc);
+                    acc = __builtin_fmaf(S[t][3], d4.w, acc);
+                }
+                acc = sum16(acc);
+                acc = acc + __shfl_xor(acc, 16, 64);
+                acc = acc + __shfl_xor(acc, 32, 64);
+                if (lane == 0) p.hdot[(((size_t)n * p.hv + h) * tiles + tile) * 4 + wave * OQ + q] = acc;
+            }
+        }
+        return;
+    }
     // ---- outgoing state: S0 of the open chunk (each wave its tiles), then, from wave
     // 0, its R rows, keys, decays, betas and count
     if (!inplace || folded) {
@@ -620,29 +644,29 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
     }
 }
 
-template <class IO, int DK>
+template <class IO, int DK, bool BW>
 hipError_t chunked_launch(const ChunkedParams &p, hipStream_t s) {
     if (p.ws_slots > 0) {
-        hipLaunchKernelGGL((gdn_chunk_prep_kernel<DK, IO>), dim3((unsigned)p.ws_slots, (unsigned)p.hk), dim3(256), 0, s,
-                           p);
+        hipLaunchKernelGGL((gdn_chunk_prep_kernel<DK, IO, BW>), dim3((unsigned)p.ws_slots, (unsigned)p.hk), dim3(256),
+                           0, s, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)((int64_t)p.n_seqs * p.hv * (p.dv / 16)));
     switch (p.waves) {
-        case 1: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 1>), grid, dim3(64), 0, s, p); break;
-        case 2: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 2>), grid, dim3(128), 0, s, p); break;
-        case 4: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 4>), grid, dim3(256), 0, s, p); break;
+        case 1: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 1, BW>), grid, dim3(64), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 2, BW>), grid, dim3(128), 0, s, p); break;
+        case 4: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 4, BW>), grid, dim3(256), 0, s, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <class IO>
+template <class IO, bool BW>
 hipError_t chunked_io(const ChunkedParams &p, hipStream_t s) {
     switch (p.dk) {
-        case 64: return chunked_launch<IO, 64>(p, s);
-        case 128: return chunked_launch<IO, 128>(p, s);
+        case 64: return chunked_launch<IO, 64, BW>(p, s);
+        case 128: return chunked_launch<IO, 128, BW>(p, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -650,7 +674,11 @@ hipError_t chunked_io(const ChunkedParams &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_chunked(const ChunkedParams &p, int io_dtype, hipStream_t s) {
-    return io_dtype == GDN_BF16 ? chunked_io<IoBf16>(p, s) : chunked_io<IoF32>(p, s);
+    return io_dtype == GDN_BF16 ? chunked_io<IoBf16, false>(p, s) : chunked_io<IoF32, false>(p, s);
+}
+
+hipError_t launch_chunked_bwd_walk(const ChunkedParams &p, int io_dtype, hipStream_t s) {
+    return io_dtype == GDN_BF16 ? chunked_io<IoBf16, true>(p, s) : chunked_io<IoF32, true>(p, s);
 }
 
 }  // namespace gdn

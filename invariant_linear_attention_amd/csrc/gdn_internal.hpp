@@ -118,8 +118,49 @@ struct ChunkedParams {
     int32_t rank_by_length;  // workgroups take sequences longest first (n_seqs <= kMaxRankedSeqs)
     int32_t inplace;         // out shares S, k, r, a and b with in (one-token calls only)
     int32_t waves;           // waves per 16-row tile: 1, 2 or 4 (each owns 4 / waves dk quarters)
+    // Forward walk of the chunked backward (launch_chunked_bwd_walk): records of
+    // kChunkRecBwd floats, no outputs or outgoing chunked state; instead the state at
+    // every chunk's start (ck, in the layout ck_offset gives), x = v - Gam P of every
+    // token ([T][hv][dv]) and the partial sums of <dhT, hT> ([N][hv][dv / 16][4 dk quarters]).
+    float *ck;
+    int64_t ck_stride;       // floats per (slot, value head) of ck
+    float *xv;
+    const float *dhT;
+    float *hdot;
 };
 hipError_t launch_chunked(const ChunkedParams &p, int io_dtype, hipStream_t s);
+hipError_t launch_chunked_bwd_walk(const ChunkedParams &p, int io_dtype, hipStream_t s);
+
+// Kernel arguments of the reverse walk of the chunked backward (gdn_bwd_chunked).
+struct BwdChunkParams {
+    const void *q, *k, *v, *dout;     // io dtype
+    const float *beta, *dhT;
+    const int32_t *cu_seqlens;
+    const float *rec, *ck, *xv, *hdot;  // from the prep kernel and the forward walk
+    float *grad_v, *grad_g, *grad_beta, *grad_h0;
+    float *dqh, *dkh;                 // [T][hv][dk]: dq, dk of each value head (the outputs when hv == hk)
+    float *grad_q, *grad_k;           // [T][hk][dk]
+    int64_t ws_slots, ck_stride, total_tokens;
+    int32_t n_seqs, hk, hv, dk, dv;
+    int32_t rank_by_length;
+    int32_t hdot_parts;               // partial sums of <dhT, hT> per (sequence, value head)
+};
+hipError_t launch_bwd_chunked(const BwdChunkParams &p, int io_dtype, hipStream_t s);
+
+// Checkpoint layout of the chunked backward, per (slot, value head): the reverse
+// walk's wave w (of dv / 16) reads the column tiles ct = w, w + NW, ... of the state
+// as MFMA B operands over the rows: lane x + 16 g, component c holds S[16 rt + 4 g + c][16 ct + x].
+__host__ __device__ inline int ck_waves(int dv) { return dv / 16; }
+__host__ __device__ inline int ck_tiles_per_wave(int dk, int dv) { return (dk / 16 + dv / 16 - 1) / (dv / 16); }
+__host__ __device__ inline int64_t ck_stride_floats(int dk, int dv) {
+    return (int64_t)ck_waves(dv) * ck_tiles_per_wave(dk, dv) * (dv / 16) * 256;
+}
+__host__ __device__ inline int64_t ck_offset(int dk, int dv, int row, int col) {
+    const int nw = ck_waves(dv), ctw = ck_tiles_per_wave(dk, dv), rt_n = dv / 16;
+    const int ct = col / 16, w = ct % nw, l = ct / nw, x = col % 16;
+    const int rt = row / 16, g = (row % 16) / 4, c = row % 4;
+    return ((((int64_t)w * ctw + l) * rt_n + rt) * 64 + (x + 16 * g)) * 4 + c;
+}
 
 // Workspace of the chunked form: one record per (chunk a call touches, value head).
 // Sequence n's chunks take slots chunk_slot_base(cu[n], n) + j: floor(cu[n] / 16)
@@ -128,6 +169,9 @@ hipError_t launch_chunked(const ChunkedParams &p, int io_dtype, hipStream_t s);
 // so floor(T / 16) + 2 N + 2 slots hold every call.
 constexpr int kChunkRec = 576;  // floats: T[16][16], B[16][16], Gam[16], D[16], a[16], beta[16]
 constexpr int kRecT = 0, kRecB = 256, kRecGam = 512, kRecD = 528, kRecDecay = 544, kRecBeta = 560;
+// The backward's record adds Gam_{m,s} (s <= m) and Gam_{m,s} (k_m . k_s) (s < m), zero elsewhere.
+constexpr int kChunkRecBwd = 1088;
+constexpr int kRecGm = 576, kRecAb = 832;
 __host__ __device__ inline int64_t chunk_slot_base(int64_t cu_n, int n) { return cu_n / kChunkLen + 2 * (int64_t)n; }
 __host__ __device__ inline int64_t chunk_ws_slots(int64_t T, int64_t N) { return T / kChunkLen + 2 * N + 2; }
 

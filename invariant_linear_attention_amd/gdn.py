@@ -22,7 +22,8 @@ STATUS = {
 GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
            "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_bwd_varlen_noalloc", "gdn_fwd_chunked",
-           "gdn_chunked_workspace_size", "gdn_status_string", "gdn_abi_version")
+           "gdn_chunked_workspace_size", "gdn_bwd_chunked_workspace_size", "gdn_bwd_chunked", "gdn_status_string",
+           "gdn_abi_version")
 
 GDN_CHUNK = 16
 
@@ -108,6 +109,10 @@ def load_library(path: str = LIBRARY):
                                         ctypes.c_uint64, vp]
         lib.gdn_chunked_workspace_size.restype = ctypes.c_int
         lib.gdn_chunked_workspace_size.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(ctypes.c_uint64)]
+        lib.gdn_bwd_chunked_workspace_size.restype = ctypes.c_int
+        lib.gdn_bwd_chunked_workspace_size.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(ctypes.c_uint64)]
+        lib.gdn_bwd_chunked.restype = ctypes.c_int
+        lib.gdn_bwd_chunked.argtypes = [ctypes.POINTER(GdnDims)] + [vp] * 16 + [ctypes.c_uint64, vp]
         lib.gdn_query_plan.restype = ctypes.c_int
         lib.gdn_query_plan.argtypes = [ctypes.POINTER(GdnDims), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
         lib.gdn_status_string.restype = ctypes.c_char_p
@@ -378,6 +383,58 @@ def gdn_bwd_varlen(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=N
                               _ptr(grads["dq"]), _ptr(grads["dk"]),
                               _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["dbeta"]), _ptr(grads.get("dh0")),
                               _ptr(workspace), int(workspace.numel()), _stream_handle(stream)))
+    return grads
+
+
+def gdn_bwd_chunked_workspace_size(dims: GdnDims) -> int:
+    """Workspace bytes gdn_bwd_chunked needs for ``dims`` (host only)."""
+    n = ctypes.c_uint64(0)
+    _check(load_library().gdn_bwd_chunked_workspace_size(ctypes.byref(dims), ctypes.byref(n)))
+    return int(n.value)
+
+
+def gdn_bwd_chunked(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=None, grads=None, stream=None,
+                    want_dh0: bool = True, waves: int = 0):
+    """Chunked backward on the matrix cores (see include/gdn.h): the gradients of
+    gdn_bwd_varlen, same arguments and results.  ``workspace`` (uint8, at least
+    gdn_bwd_chunked_workspace_size bytes) and ``grads`` are allocated when None;
+    ``waves`` (0, 1, 2 or 4) is the forward walk's waves per 16-row state tile."""
+    import torch
+    T, hk, dk, hv, dv, N = _dims_of(q, k, v, g, beta, cu_seqlens, require_cu=True)
+    _shape(h0, "h0", (N, hv, dv, dk))
+    _shape(dout, "dout", (T, hv, dv))
+    _shape(dhT, "dhT", (N, hv, dv, dk))
+    if grads is not None:
+        want = {"dq": (T, hk, dk), "dk": (T, hk, dk), "dv": (T, hv, dv), "dg": (T, hv), "dbeta": (T, hv),
+                "dh0": (N, hv, dv, dk)}
+        for name, shp in want.items():
+            if name != "dh0" and grads.get(name) is None:
+                raise ValueError("grads[%r] is required" % name)
+            _shape(grads.get(name), name, shp)
+    if workspace is not None and workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _need(t, name, q.dtype)
+    for name, t in (("g", g), ("beta", beta), ("h0", h0), ("dhT", dhT)):
+        _need(t, name, torch.float32)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    dims = make_dims(q, v, N, T, plan=(0, 0, waves))
+    if workspace is None:
+        workspace = torch.empty(gdn_bwd_chunked_workspace_size(dims), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    if grads is None:
+        f32 = dict(dtype=torch.float32, device=q.device)
+        grads = {"dq": torch.empty((T, hk, dk), **f32), "dk": torch.empty((T, hk, dk), **f32),
+                 "dv": torch.empty((T, hv, dv), **f32), "dg": torch.empty((T, hv), **f32),
+                 "dbeta": torch.empty((T, hv), **f32),
+                 "dh0": torch.empty((N, hv, dv, dk), **f32) if want_dh0 else None}
+    for name, t in grads.items():
+        _need(t, name, torch.float32)
+    _check(lib.gdn_bwd_chunked(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                               _ptr(cu_seqlens), _ptr(dout), _ptr(dhT), _ptr(grads["dq"]), _ptr(grads["dk"]),
+                               _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["dbeta"]), _ptr(grads.get("dh0")),
+                               _ptr(workspace), int(workspace.numel()), _stream_handle(stream)))
     return grads
 
 

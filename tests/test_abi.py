@@ -29,8 +29,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
                           "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_bwd_varlen_noalloc",
-                          "gdn_fwd_chunked", "gdn_chunked_workspace_size",
-                          "gdn_status_string", "gdn_abi_version"}
+                          "gdn_fwd_chunked", "gdn_chunked_workspace_size", "gdn_bwd_chunked_workspace_size",
+                          "gdn_bwd_chunked", "gdn_status_string", "gdn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -443,6 +443,72 @@ def test_bwd_rejects_preprocessing(lib):
     d = _dims()
     d.pre = ctypes.pointer(pre)
     assert call_bwd(lib, d, ws_bytes=1 << 30) == 6
+
+
+# ------------------------------------------------------------- chunked backward
+
+def cbwd_ws(lib, dims):
+    n = ctypes.c_uint64(0)
+    rc = lib.gdn_bwd_chunked_workspace_size(ctypes.byref(dims), ctypes.byref(n))
+    return int(n.value) if rc == 0 else -rc
+
+
+def call_cbwd(lib, dims, ws_bytes=None, **over):
+    a = dict(BP)
+    a.update(over)
+    if ws_bytes is None:
+        ws_bytes = cbwd_ws(lib, dims) if dims is not None else 0
+    return lib.gdn_bwd_chunked(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], a["v"], a["g"],
+                               a["b"], a["h0"], a["cu"], a["dout"], a["dhT"], a["dq"], a["dk"], a["dv"], a["dg"],
+                               a["db"], a["dh0"], a["ws"], ctypes.c_uint64(ws_bytes), None)
+
+
+def test_bwd_chunked_workspace_size(lib):
+    """Records (1,088 floats per slot and value head), the chunk-start states in the
+    reverse walk's layout (dv/16 waves x ceil(dk/dv) column tiles x dv/16 row tiles
+    x 256 floats), x = v - Gam P (T hv dv), the <dhT, hT> partials (N hv dv/16 x 4)
+    and, when value heads share key heads, dq and dk per value head (T hv dk each);
+    slots = T // 16 + 2 N + 2; every part rounded up to 256 bytes."""
+    up = lambda x: (x + 255) // 256 * 256
+    for T, N, hk, hv, dk, dv in ((10, 2, 2, 4, 128, 64), (100, 3, 2, 2, 64, 128), (33, 1, 1, 1, 128, 32)):
+        slots = T // 16 + 2 * N + 2
+        ck = (dv // 16) * ((dk // 16 + dv // 16 - 1) // (dv // 16)) * (dv // 16) * 256
+        want = (up(slots * hv * 1088 * 4) + up(slots * hv * ck * 4) + up(T * hv * dv * 4)
+                + up(N * hv * (dv // 16) * 16) + (2 * up(T * hv * dk * 4) if hv > hk else 0))
+        assert cbwd_ws(lib, _dims(total_tokens=T, n_seqs=N, hk=hk, hv=hv, dk=dk, dv=dv)) == want
+    n = ctypes.c_uint64(0)
+    assert lib.gdn_bwd_chunked_workspace_size(None, ctypes.byref(n)) == 1
+    assert lib.gdn_bwd_chunked_workspace_size(ctypes.byref(_dims()), None) == 1
+    assert cbwd_ws(lib, _dims(hv=3)) == -2
+    assert cbwd_ws(lib, _dims(dk=32)) == -6
+
+
+@pytest.mark.parametrize("case,over,code", [
+    (dict(dk=32), {}, 6), (dict(dk=16), {}, 6), (dict(dv=16), {}, 6), (dict(dv=96), {}, 6),
+    (dict(plan_lanes=8), {}, 6), (dict(plan_rows=1), {}, 6), (dict(plan_waves=3), {}, 6),
+    (dict(hk=1, hv=32), {}, 6), (dict(hv=3), {}, 2), (dict(io_dtype=7), {}, 3),
+    (dict(n_seqs=0, total_tokens=3), {}, 2),
+    ({}, dict(cu=None), 1), ({}, dict(ws=None), 1), ({}, dict(q=None), 1), ({}, dict(dout=None), 1),
+    ({}, dict(dq=None), 1), ({}, dict(dg=None), 1), ({}, dict(db=None), 1), ({}, dict(dv=None), 1),
+    ({}, dict(q=BP["q"] + 8), 4), ({}, dict(dout=BP["dout"] + 8), 4), ({}, dict(ws=BP["ws"] + 4), 4),
+    ({}, dict(dq=BP["dq"] + 4), 4), ({}, dict(g=BP["g"] + 2), 4), ({}, dict(dhT=BP["dhT"] + 4), 4),
+    ({}, dict(dq=BP["q"]), 5), ({}, dict(dk=BP["dq"]), 5), ({}, dict(ws=BP["dout"]), 5),
+    ({}, dict(dh0=BP["h0"]), 5), ({}, dict(dv=BP["ws"] + 256), 5), ({}, dict(dg=BP["db"]), 5),
+    ({}, dict(ws=BP["dhT"]), 5),
+])
+def test_bwd_chunked_rejects(lib, case, over, code):
+    assert call_cbwd(lib, _dims(**case), ws_bytes=(1 << 30), **over) == code
+
+
+def test_bwd_chunked_small_workspace_preprocessing_and_noop(lib):
+    from invariant_linear_attention_amd import gdn
+    d = _dims()
+    assert call_cbwd(lib, d, ws_bytes=cbwd_ws(lib, d) - 1) == 2
+    assert call_cbwd(lib, None) == 1
+    assert call_cbwd(lib, _dims(n_seqs=0, total_tokens=0), ws_bytes=0) == 0
+    pre = gdn.make_preproc(norm_qk=True)
+    d.pre = ctypes.pointer(pre)
+    assert call_cbwd(lib, d, ws_bytes=1 << 30) == 6
 
 
 # ------------------------------------------------------------------ chunked form

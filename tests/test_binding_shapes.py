@@ -165,3 +165,24 @@ def test_matching_shapes_pass_the_shape_checks():
         gdn.gdn_fwd_varlen(b["q"], b["k"], b["v"], b["g"], b["beta"], b["h0"], b["cu_seqlens"])
     with pytest.raises(ValueError, match="device tensor"):
         gdn.gdn_decode_step(*decode_args())
+
+
+@pytest.mark.parametrize("name,shape", [("dout", (T, HV, DV + 1)), ("dhT", (N, HV, DV, 1)), ("h0", (N, HV, 1, DK))])
+def test_chunked_backward_refuses(name, shape):
+    b = batch()
+    kw = dict(dout=torch.zeros((T, HV, DV), dtype=torch.bfloat16), dhT=None)
+    if name == "h0":
+        b["h0"] = torch.zeros(shape)
+    else:
+        kw[name] = torch.zeros(shape, dtype=torch.bfloat16 if name == "dout" else torch.float32)
+    expect_shape_error(gdn.gdn_bwd_chunked, b["q"], b["k"], b["v"], b["g"], b["beta"], b["h0"], b["cu_seqlens"],
+                       kw["dout"], kw["dhT"])
+
+
+def test_chunked_backward_refuses_gradient_buffers():
+    b = batch()
+    f = torch.zeros
+    grads = {"dq": f((T, HK, DK)), "dk": f((T, HK, DK + 4)), "dv": f((T, HV, DV)), "dg": f((T, HV)),
+             "dbeta": f((T, HV)), "dh0": None}
+    expect_shape_error(gdn.gdn_bwd_chunked, b["q"], b["k"], b["v"], b["g"], b["beta"], b["h0"], b["cu_seqlens"],
+                       torch.zeros((T, HV, DV), dtype=torch.bfloat16), grads=grads)
