@@ -648,7 +648,7 @@ BwdChunkWorkspace bwd_chunked_workspace(int64_t T, int64_t N, int hk, int hv, in
     const uint64_t slots = (uint64_t)chunk_ws_slots(T, N);
     uint64_t o = 0;
     w.rec = o; o = round256(o + slots * hv * kChunkRecBwd * 4);
-    w.ck = o; o = round256(o + slots * hv * (uint64_t)ck_stride_floats(dk, dv) * 4);
+    w.ck = o; o = round256(o + slots * hv * (uint64_t)dv * dk * 4);
     w.xv = o; o = round256(o + (uint64_t)T * hv * dv * 4);
     w.hdot = o; o = round256(o + (uint64_t)N * hv * (dv / 16) * 4 * 4);
     w.dq = o; o = round256(o + (hv > hk ? (uint64_t)T * hv * dk * 4 : 0));
@@ -742,7 +742,6 @@ gdn_status gdn_bwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     f.rank_by_length = rank;
     f.waves = fw_waves;
     f.ck = reinterpret_cast<float *>(w + ws.ck);
-    f.ck_stride = ck_stride_floats(d.dk, d.dv);
     f.xv = reinterpret_cast<float *>(w + ws.xv);
     f.dhT = dhT;
     f.hdot = reinterpret_cast<float *>(w + ws.hdot);
@@ -756,7 +755,7 @@ gdn_status gdn_bwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     p.grad_q = dq; p.grad_k = dk;
     p.dqh = d.hv > d.hk ? reinterpret_cast<float *>(w + ws.dq) : dq;
     p.dkh = d.hv > d.hk ? reinterpret_cast<float *>(w + ws.dk) : dk;
-    p.ws_slots = slots; p.ck_stride = f.ck_stride; p.total_tokens = T;
+    p.ws_slots = slots; p.total_tokens = T;
     p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dk = d.dk; p.dv = d.dv;
     p.rank_by_length = rank;
     p.hdot_parts = (d.dv / 16) * 4;  // one per (16-row tile, dk quarter)

@@ -63,6 +63,17 @@ struct RevFetch {
     float ge[EPT], ae[EPT], be[EPT];  // Gam_{m,s}, Gam_{m,s} (k_m . k_s) and beta_m of entries tid + 64 NW e
 };
 
+// One workgroup per (sequence, value head), dv / 16 waves; wave w owns the adjoint
+// state's rows 16 w .. 16 w + 15 (all dk columns, as MFMA accumulators) and, for the
+// products over the rows, the column tiles w, w + dv/16, ...  Per chunk, from the last:
+//   P1  E, dU, dR, U on the wave's rows; dv; the token rows of dO, dR and U and D into
+//       LDS; D moved to the chunk's start; (wave 0) the previous chunk's per-token results
+//   P2  the wave's partial dB, dA over its rows; dq0 and dk1 on its column tiles
+//   P3  dB, dA summed over the waves; the dA part of dbeta
+//   P4  the in-chunk terms of dq and dk; stores; q . dq
+// with one LDS barrier between phases.  Keys and queries and the per-token sums are
+// double-buffered by chunk parity, so no barrier is needed between P4 and the next
+// chunk's staging.
 template <int DK, int DV, class IO>
 __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdChunkParams p) {
     using RF = RevFetch<DK, DV, IO>;
@@ -71,16 +82,16 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
     constexpr int KP = DK + 4, VP = DV + 4;
     constexpr int NTH = 64 * NW;
     // (16-byte aligned: read and written as float4)
-    __shared__ __align__(16) float Ks[kCk][KP];
-    __shared__ __align__(16) float Qs[kCk][KP];
+    __shared__ __align__(16) float Ks[2][kCk][KP];
+    __shared__ __align__(16) float Qs[2][kCk][KP];
     __shared__ __align__(16) float dOs[kCk][VP];  // token rows of dO, dR and U
     __shared__ __align__(16) float dRs[kCk][VP];
     __shared__ __align__(16) float Us[kCk][VP];
     __shared__ __align__(16) float Ds[DV][KP];    // D = dL/dS at the chunk's end
     __shared__ float dBp[NW][kCk][kCk + 1], dAp[NW][kCk][kCk + 1];
-    __shared__ float Ms[kCk][kCk + 1], Hs[kCk][kCk + 1];       // dB Gam (s <= m), dA beta Gam (s < m)
-    __shared__ float Ab[kCk][kCk + 1];                         // dA Gam (k.k), summed into dbeta
-    __shared__ float red[NW][kCk][4];                          // per wave and token: dR.x, dv.v, q.dq
+    __shared__ float Ms[kCk][kCk + 1], Hs[kCk][kCk + 1];  // dB Gam (s <= m), dA beta Gam (s < m)
+    __shared__ float abrow[kCk];                          // sum_s dA[m][s] Gam_{m,s} (k_m . k_s)
+    __shared__ float red[2][NW][kCk][4];                  // per parity, wave and token: dR.x, dv.v, q.dq
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int x = lane & 15, g = lane >> 4;
@@ -114,8 +125,9 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
     const int64_t base = chunk_slot_base(tb, n);
     int nch = (int)((len + kCk - 1) / kCk);
     if (base + nch > p.ws_slots) nch = (int)(p.ws_slots - base > 0 ? p.ws_slots - base : 0);
-    const size_t krow = (size_t)p.hk * DK, vrow = (size_t)p.hv * DV;
+    const size_t vrow = (size_t)p.hv * DV;
     constexpr uint32_t E = IO::ESZ;
+    const uint32_t krow_b = (uint32_t)p.hk * DK * E, vrow_b = (uint32_t)vrow * E;
 
     // D = dL/dS, rows r0 .. r0 + 15, held transposed: lane x + 16 g, tile t, component c
     // is D[r0 + x][16 t + 4 g + c]
@@ -131,39 +143,39 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
             }
         }
     }
-    // <dhT, hT> from the forward walk's partial sums, in order
+    // <dhT, hT> from the forward walk's partial sums, in order (the dg running sum's start)
     float carry = 0.f;
     if (p.dhT)
         for (int i = 0; i < p.hdot_parts; ++i) carry = carry + p.hdot[((size_t)n * p.hv + h) * p.hdot_parts + i];
 
-    auto clampm = [](int m, int hi) { return m >= hi ? hi - 1 : m; };
+    auto chunk_m1 = [&](int j) {
+        const int64_t left = len - (int64_t)kCk * j;
+        return left < kCk ? (int)left : kCk;
+    };
     auto fetch = [&](RF &F, int j_) {
         const int j = j_ < 0 ? 0 : j_;  // past the first chunk: repeat its reads
-        const int64_t left = len - (int64_t)kCk * j;
-        const int m1 = left < kCk ? (int)left : kCk;
+        const int m1 = chunk_m1(j);
         const int64_t t0 = tb + (int64_t)kCk * j;
         const char *kb = static_cast<const char *>(p.k) + ((size_t)t0 * p.hk + kh) * DK * E;
         const char *qb = static_cast<const char *>(p.q) + ((size_t)t0 * p.hk + kh) * DK * E;
-        const uint32_t krow_b = (uint32_t)krow * E;
 #pragma unroll
         for (int s = 0; s < RF::KIT; ++s) {
             int it = tid + NTH * s;
             it = it < RF::KITEMS ? it : RF::KITEMS - 1;
             const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
-            const uint32_t off = (uint32_t)clampm(m, m1) * krow_b + (uint32_t)c * E;
+            const uint32_t off = (uint32_t)(m < m1 ? m : m1 - 1) * krow_b + (uint32_t)c * E;
             F.kr[s] = RW::load_at(kb, off);
             F.qr[s] = RW::load_at(qb, off);
         }
         const char *ob = static_cast<const char *>(p.dout) + ((size_t)t0 * p.hv + h) * DV * E;
         const char *vb = static_cast<const char *>(p.v) + ((size_t)t0 * p.hv + h) * DV * E;
-        const float *xb = p.xv + ((size_t)t0 * p.hv + h) * DV;
-        const uint32_t vrow_b = (uint32_t)vrow * E;
+        const char *xb = reinterpret_cast<const char *>(p.xv + ((size_t)t0 * p.hv + h) * DV);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const uint32_t tm = (uint32_t)clampm(4 * g + c, m1);
+            const uint32_t tm = (uint32_t)(4 * g + c < m1 ? 4 * g + c : m1 - 1);
             F.dor[c] = RW::load1_at(ob, tm * vrow_b + (uint32_t)(r0 + x) * E);
             F.vr[c] = RW::load1_at(vb, tm * vrow_b + (uint32_t)(r0 + x) * E);
-            F.xr[c] = xb[(size_t)tm * vrow + r0 + x];
+            F.xr[c] = *reinterpret_cast<const float *>(xb + tm * (uint32_t)(vrow * 4) + (uint32_t)(r0 + x) * 4);
         }
         const float *rec = p.rec + ((size_t)(base + j) * p.hv + h) * kChunkRecBwd;
         const int l = m1 - 1;
@@ -189,19 +201,50 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
             F.be[e] = rec[kRecBeta + i / kCk];
         }
     };
-    // The chunk's start state, this wave's column tiles in the B-operand layout (read
-    // a chunk ahead, once the current one is no longer needed).
+    // The chunk's start state on this wave's column tiles, as MFMA B operands over the
+    // rows: s0[rt][l2][c] = S0[16 rt + 4 g + c][16 (wave + NW l2) + x] (read a chunk
+    // ahead, once the current one is no longer needed).
     f4 s0[RT][CTW];
     auto fetch_s0 = [&](int j_) {
         const int j = j_ < 0 ? 0 : j_;
-        const float *ck = p.ck + ((size_t)(base + j) * p.hv + h) * p.ck_stride;
+        const float *ck = p.ck + ((size_t)(base + j) * p.hv + h) * DV * DK;
 #pragma unroll
-        for (int l2 = 0; l2 < CTW; ++l2)
+        for (int l2 = 0; l2 < CTW; ++l2) {
+            const int ct = wave + NW * l2 < NT ? wave + NW * l2 : NT - 1;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const float4 v4 = *reinterpret_cast<const float4 *>(ck + (((size_t)wave * CTW + l2) * RT + rt) * 256 + 4 * lane);
-                s0[rt][l2] = f4{v4.x, v4.y, v4.z, v4.w};
-            }
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) s0[rt][l2][c] = ck[(16 * rt + 4 * g + c) * DK + 16 * ct + x];
+        }
+    };
+
+    // The per-token results of a chunk (wave 0, lane m = token): dbeta, and dg as the
+    // running sum from the sequence's end, carry + phi_15 + ... + phi_m in that order
+    // (phi = dO . o - dv . v; tokens past the chunk's end hold exact zeros).
+    auto per_token = [&](int j, int b) {
+        if (wave != 0) return;
+        const int m1 = chunk_m1(j);
+        const int64_t t0 = tb + (int64_t)kCk * j;
+        const int m = lane & 15;
+        float sbv = 0.f, svv = 0.f, sq = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            sbv = sbv + red[b][w][m][0];
+            svv = svv + red[b][w][m][1];
+            sq = sq + red[b][w][m][2];
+        }
+        const float phi = sq - svv;
+        float dg = carry;
+#pragma unroll
+        for (int s = kCk - 1; s >= 0; --s) {
+            const float ps = __shfl(phi, s, 64);
+            dg = s >= m ? dg + ps : dg;
+        }
+        carry = __shfl(dg, 0, 64);
+        if (lane < kCk && m < m1) {
+            p.grad_beta[(size_t)(t0 + m) * p.hv + h] = sbv + abrow[m];
+            p.grad_g[(size_t)(t0 + m) * p.hv + h] = dg;
+        }
     };
 
     RF F;
@@ -210,9 +253,11 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
         fetch_s0(nch - 1);
     }
     for (int j = nch - 1; j >= 0; --j) {
-        const int64_t left = len - (int64_t)kCk * j;
-        const int m1 = left < kCk ? (int)left : kCk;
+        const int m1 = chunk_m1(j);
         const int64_t t0 = tb + (int64_t)kCk * j;
+        const int b = j & 1;
+        float(*Kc)[KP] = Ks[b];
+        float(*Qc)[KP] = Qs[b];
 
         // ---- stage this chunk: keys and queries into LDS, the rest into registers
 #pragma unroll
@@ -221,8 +266,8 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
             if (it < RF::KITEMS) {
                 const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
                 const bool on = m < m1;
-                *reinterpret_cast<float4 *>(&Ks[m][c]) = RW::widen(RW::keep(F.kr[s], on));
-                *reinterpret_cast<float4 *>(&Qs[m][c]) = RW::widen(RW::keep(F.qr[s], on));
+                *reinterpret_cast<float4 *>(&Kc[m][c]) = RW::widen(RW::keep(F.kr[s], on));
+                *reinterpret_cast<float4 *>(&Qc[m][c]) = RW::widen(RW::keep(F.qr[s], on));
             }
         }
         float dO[4], vv[4], xx[4];
@@ -254,11 +299,11 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
         fetch(F, j - 1);
         lds_barrier();
 
-        // ---- E = K D^T on this wave's rows (token 4 g + c, row r0 + x)
+        // ---- P1.  E = K D^T on this wave's rows (token 4 g + c, row r0 + x)
         f4 Ev = f4_zero();
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float4 ka = *reinterpret_cast<const float4 *>(&Ks[x][16 * t + 4 * g]);
+            const float4 ka = *reinterpret_cast<const float4 *>(&Kc[x][16 * t + 4 * g]);
             Ev = mfma_16x16x4(ka.x, Dt[t][0], Ev);
             Ev = mfma_16x16x4(ka.y, Dt[t][1], Ev);
             Ev = mfma_16x16x4(ka.z, Dt[t][2], Ev);
@@ -277,35 +322,35 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
         U = mfma_16x16x4(trow.z, bt[2] * xx[2], U);
         U = mfma_16x16x4(trow.w, bt[3] * xx[3], U);
 
-        // dv = beta dR; the row sums dR . x and dv . v of this wave's rows
+        // the previous chunk's per-token results (its sums are complete: barrier above)
+        if (j + 1 < nch) per_token(j + 1, b ^ 1);
+
+        // dv = beta dR; the row sums dR . x and dv . v of this wave's rows; the token
+        // rows of dO, dR and U and D at the chunk's end for the products over rows
+        // (dR and U pass through vector registers first: stores straight from the MFMA
+        // accumulators were merged with wrong offsets by the compiler)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int m = 4 * g + c;
-            const float dvv = bt[c] * dR[c];
-            if (m < m1) p.grad_v[(size_t)(t0 + m) * vrow + (size_t)h * DV + r0 + x] = dvv;
-            const float sb = sum16(dR[c] * xx[c]);
-            const float sv = sum16(dvv * vv[c]);
-            if (x == 0) {
-                red[wave][m][0] = sb;
-                red[wave][m][1] = sv;
-            }
-        }
-        // token rows of dO, dR and U, and D at the chunk's end, for the products over rows
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            // (the values pass through vector registers first: stores straight from the
-            // MFMA accumulators were merged with wrong offsets by the compiler)
             float dr = dR[c], uu = U[c];
             asm volatile("" : "+v"(dr), "+v"(uu));
-            dOs[4 * g + c][r0 + x] = dO[c];
-            dRs[4 * g + c][r0 + x] = dr;
-            Us[4 * g + c][r0 + x] = uu;
+            const float dvv = bt[c] * dr;
+            if (m < m1) p.grad_v[(size_t)(t0 + m) * vrow + (size_t)h * DV + r0 + x] = dvv;
+            const float sb = lane_sum<16>(dr * xx[c]);
+            const float sv = lane_sum<16>(dvv * vv[c]);
+            if (x == 0) {
+                red[b][wave][m][0] = sb;
+                red[b][wave][m][1] = sv;
+            }
+            dOs[m][r0 + x] = dO[c];
+            dRs[m][r0 + x] = dr;
+            Us[m][r0 + x] = uu;
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             *reinterpret_cast<float4 *>(&Ds[r0 + x][16 * t + 4 * g]) = make_float4(Dt[t][0], Dt[t][1], Dt[t][2], Dt[t][3]);
 
-        // ---- D at the chunk's start: D^T = Gam_l D^T + Q^T (Gam dO) - K^T (beta Gam dR)
+        // D at the chunk's start: D^T = Gam_l D^T + Q^T (Gam dO) - K^T (beta Gam dR)
         {
             float bq[4], bk[4];
 #pragma unroll
@@ -317,15 +362,15 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
             for (int t = 0; t < NT; ++t) {
                 f4 C = f4{gl * Dt[t][0], gl * Dt[t][1], gl * Dt[t][2], gl * Dt[t][3]};
 #pragma unroll
-                for (int c = 0; c < 4; ++c) C = mfma_16x16x4(Qs[4 * g + c][16 * t + x], bq[c], C);
+                for (int c = 0; c < 4; ++c) C = mfma_16x16x4(Qc[4 * g + c][16 * t + x], bq[c], C);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) C = mfma_16x16x4(Ks[4 * g + c][16 * t + x], bk[c], C);
+                for (int c = 0; c < 4; ++c) C = mfma_16x16x4(Kc[4 * g + c][16 * t + x], bk[c], C);
                 Dt[t] = C;
             }
         }
         lds_barrier();
 
-        // ---- partial dB = dO U^T and dA = -dR U^T over this wave's rows
+        // ---- P2.  partial dB = dO U^T and dA = -dR U^T over this wave's rows
         {
             const float4 o4 = *reinterpret_cast<const float4 *>(&dOs[x][r0 + 4 * g]);
             const float4 r4 = *reinterpret_cast<const float4 *>(&dRs[x][r0 + 4 * g]);
@@ -341,13 +386,15 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
             pa = mfma_16x16x4(-r4.w, u4.w, pa);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                dBp[wave][4 * g + r][x] = pb[r];
-                dAp[wave][4 * g + r][x] = pa[r];
+                float vb = pb[r], va = pa[r];
+                asm volatile("" : "+v"(vb), "+v"(va));
+                dBp[wave][4 * g + r][x] = vb;
+                dAp[wave][4 * g + r][x] = va;
             }
         }
 
-        // ---- products over the rows on this wave's column tiles:
-        //      dq0 = dO S0,  dk1 = (-beta Gam dR) S0 + (Gam_{l,.} U) D
+        // products over the rows on this wave's column tiles:
+        //   dq0 = dO S0,  dk1 = (-beta Gam dR) S0 + (Gam_{l,.} U) D
         f4 dq[CTW], dk[CTW];
         {
             const float fr = -(bx * gx), fu = wx;  // factors of A-operand row x (token x)
@@ -379,7 +426,10 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
         fetch_s0(j - 1);
         lds_barrier();
 
-        // ---- dB and dA summed over the waves (in order), masked and weighted
+        // ---- P3.  dB and dA summed over the waves (in order), masked and weighted; the
+        // dA part of dbeta, sum_s dA[m][s] Gam_{m,s} (k_m . k_s), summed across a DPP row
+        // (the 16 entries of row m sit in lanes 16 (m % 4) .. of one wave)
+#pragma unroll
         for (int e = 0; e < RF::EPT; ++e) {
             const int i = tid + NTH * e;
             if (i < kCk * kCk) {
@@ -390,14 +440,15 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
                     sbv = sbv + dBp[w][m][s];
                     sav = sav + dAp[w][m][s];
                 }
-                Ms[m][s] = sbv * ge[e];                           // Gam is zero above the diagonal
+                Ms[m][s] = sbv * ge[e];  // Gam is zero above the diagonal
                 Hs[m][s] = s < m ? sav * (be[e] * ge[e]) : 0.f;
-                Ab[m][s] = sav * ae[e];                           // zero unless s < m
+                const float ab = lane_sum<16>(sav * ae[e]);  // ae is zero unless s < m
+                if (s == 0) abrow[m] = ab;
             }
         }
         lds_barrier();
 
-        // ---- in-chunk terms: dq += Ms K;  dk += Ms^T Q + (H + H^T) K
+        // ---- P4.  in-chunk terms: dq += Ms K;  dk += Ms^T Q + (H + H^T) K; q . dq
         {
             float mr[4], mc[4], hh[4];
 #pragma unroll
@@ -412,15 +463,15 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
                 const int ct = wave + NW * l2;
                 if (ct < NT) {
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) dq[l2] = mfma_16x16x4(mr[c], Ks[4 * g + c][16 * ct + x], dq[l2]);
+                    for (int c = 0; c < 4; ++c) dq[l2] = mfma_16x16x4(mr[c], Kc[4 * g + c][16 * ct + x], dq[l2]);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(mc[c], Qs[4 * g + c][16 * ct + x], dk[l2]);
+                    for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(mc[c], Qc[4 * g + c][16 * ct + x], dk[l2]);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(hh[c], Ks[4 * g + c][16 * ct + x], dk[l2]);
+                    for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(hh[c], Kc[4 * g + c][16 * ct + x], dk[l2]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int m = 4 * g + r;
-                        qd[r] = __builtin_fmaf(Qs[m][16 * ct + x], dq[l2][r], qd[r]);
+                        qd[r] = __builtin_fmaf(Qc[m][16 * ct + x], dq[l2][r], qd[r]);
                         if (m < m1) {
                             const size_t o = ((size_t)(t0 + m) * p.hv + h) * DK + 16 * ct + x;
                             p.dqh[o] = dq[l2][r];
@@ -431,33 +482,14 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float v = sum16(qd[r]);
-                if (x == 0) red[wave][4 * g + r][2] = v;
+                const float v = lane_sum<16>(qd[r]);
+                if (x == 0) red[b][wave][4 * g + r][2] = v;
             }
         }
+    }
+    if (nch > 0) {
         lds_barrier();
-
-        // ---- per-token results, in order: dbeta, and dg as a running sum from the end
-        if (tid < kCk) {
-            const int m = tid;
-            float sbv = 0.f, svv = 0.f, sq = 0.f, ab = 0.f;
-            for (int w = 0; w < NW; ++w) {
-                sbv = sbv + red[w][m][0];
-                svv = svv + red[w][m][1];
-                sq = sq + red[w][m][2];
-            }
-            for (int s = 0; s < kCk; ++s) ab = ab + Ab[m][s];
-            if (m < m1) p.grad_beta[(size_t)(t0 + m) * p.hv + h] = sbv + ab;
-            red[0][m][3] = sq - svv;  // dO . o - dv . v
-        }
-        if (tid == 0) {
-            // (wave 0's lane 0 wrote every red[0][m][3] itself)
-            for (int m = m1 - 1; m >= 0; --m) {
-                carry = carry + red[0][m][3];
-                p.grad_g[(size_t)(t0 + m) * p.hv + h] = carry;
-            }
-        }
-        lds_barrier();  // LDS is refilled by the next chunk
+        per_token(0, 0);
     }
 
     if (p.grad_h0) {

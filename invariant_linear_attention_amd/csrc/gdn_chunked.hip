@@ -387,15 +387,6 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
     for (int c = 0; c < 4; ++c)
         if (4 * g + c < sc.c0 && p.in_r) Rkeep[c] = p.in_r[(((size_t)n * kCk + 4 * g + c) * p.hv + h) * p.dv + row0 + x];
 
-    // checkpoint offsets of this lane's state elements (component c at + 4 c): lane
-    // x + 16 g holds S[row0 + x][16 tt + 4 g + c]
-    uint32_t ckoff[BW ? OT : 1];
-    if constexpr (BW) {
-#pragma unroll
-        for (int t = 0; t < OT; ++t)
-            ckoff[t] = (uint32_t)ck_offset(DK, p.dv, row0 + x, 16 * (t_first + t) + 4 * g);
-    }
-
     CF F;
     if (nch > 0) fetch(F, 0);
     for (int j = 0; j < nch; ++j) {
@@ -434,11 +425,10 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
         }
         if constexpr (BW) {
             // the state at this chunk's start
-            float *dst = p.ck + ((size_t)(sc.base + j) * p.hv + h) * p.ck_stride;
+            float *dst = p.ck + (((size_t)(sc.base + j) * p.hv + h) * p.dv + row0 + x) * DK;
 #pragma unroll
             for (int t = 0; t < OT; ++t)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) dst[ckoff[t] + 4 * c] = S[t][c];
+                *reinterpret_cast<float4 *>(dst + 16 * (t_first + t) + 4 * g) = make_float4(S[t][0], S[t][1], S[t][2], S[t][3]);
         }
         const float4 trow = F.trow, brow = F.brow, gam = F.gam, dwv = F.dw;
         const float g15 = F.g15;

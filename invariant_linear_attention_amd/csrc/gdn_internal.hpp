@@ -120,10 +120,9 @@ struct ChunkedParams {
     int32_t waves;           // waves per 16-row tile: 1, 2 or 4 (each owns 4 / waves dk quarters)
     // Forward walk of the chunked backward (launch_chunked_bwd_walk): records of
     // kChunkRecBwd floats, no outputs or outgoing chunked state; instead the state at
-    // every chunk's start (ck, in the layout ck_offset gives), x = v - Gam P of every
+    // every chunk's start (ck: [slot][hv][dv][dk], like a state), x = v - Gam P of every
     // token ([T][hv][dv]) and the partial sums of <dhT, hT> ([N][hv][dv / 16][4 dk quarters]).
     float *ck;
-    int64_t ck_stride;       // floats per (slot, value head) of ck
     float *xv;
     const float *dhT;
     float *hdot;
@@ -140,27 +139,13 @@ struct BwdChunkParams {
     float *grad_v, *grad_g, *grad_beta, *grad_h0;
     float *dqh, *dkh;                 // [T][hv][dk]: dq, dk of each value head (the outputs when hv == hk)
     float *grad_q, *grad_k;           // [T][hk][dk]
-    int64_t ws_slots, ck_stride, total_tokens;
+    int64_t ws_slots, total_tokens;
     int32_t n_seqs, hk, hv, dk, dv;
     int32_t rank_by_length;
     int32_t hdot_parts;               // partial sums of <dhT, hT> per (sequence, value head)
 };
 hipError_t launch_bwd_chunked(const BwdChunkParams &p, int io_dtype, hipStream_t s);
 
-// Checkpoint layout of the chunked backward, per (slot, value head): the reverse
-// walk's wave w (of dv / 16) reads the column tiles ct = w, w + NW, ... of the state
-// as MFMA B operands over the rows: lane x + 16 g, component c holds S[16 rt + 4 g + c][16 ct + x].
-__host__ __device__ inline int ck_waves(int dv) { return dv / 16; }
-__host__ __device__ inline int ck_tiles_per_wave(int dk, int dv) { return (dk / 16 + dv / 16 - 1) / (dv / 16); }
-__host__ __device__ inline int64_t ck_stride_floats(int dk, int dv) {
-    return (int64_t)ck_waves(dv) * ck_tiles_per_wave(dk, dv) * (dv / 16) * 256;
-}
-__host__ __device__ inline int64_t ck_offset(int dk, int dv, int row, int col) {
-    const int nw = ck_waves(dv), ctw = ck_tiles_per_wave(dk, dv), rt_n = dv / 16;
-    const int ct = col / 16, w = ct % nw, l = ct / nw, x = col % 16;
-    const int rt = row / 16, g = (row % 16) / 4, c = row % 4;
-    return ((((int64_t)w * ctw + l) * rt_n + rt) * 64 + (x + 16 * g)) * 4 + c;
-}
 
 // Workspace of the chunked form: one record per (chunk a call touches, value head).
 // Sequence n's chunks take slots chunk_slot_base(cu[n], n) + j: floor(cu[n] / 16)

@@ -464,15 +464,14 @@ def call_cbwd(lib, dims, ws_bytes=None, **over):
 
 
 def test_bwd_chunked_workspace_size(lib):
-    """Records (1,088 floats per slot and value head), the chunk-start states in the
-    reverse walk's layout (dv/16 waves x ceil(dk/dv) column tiles x dv/16 row tiles
-    x 256 floats), x = v - Gam P (T hv dv), the <dhT, hT> partials (N hv dv/16 x 4)
-    and, when value heads share key heads, dq and dk per value head (T hv dk each);
-    slots = T // 16 + 2 N + 2; every part rounded up to 256 bytes."""
+    """Records (1,088 floats per slot and value head), the chunk-start states (a dv x dk
+    state per slot and value head), x = v - Gam P (T hv dv), the <dhT, hT> partials
+    (N hv dv/16 x 4) and, when value heads share key heads, dq and dk per value head
+    (T hv dk each); slots = T // 16 + 2 N + 2; every part rounded up to 256 bytes."""
     up = lambda x: (x + 255) // 256 * 256
     for T, N, hk, hv, dk, dv in ((10, 2, 2, 4, 128, 64), (100, 3, 2, 2, 64, 128), (33, 1, 1, 1, 128, 32)):
         slots = T // 16 + 2 * N + 2
-        ck = (dv // 16) * ((dk // 16 + dv // 16 - 1) // (dv // 16)) * (dv // 16) * 256
+        ck = dv * dk
         want = (up(slots * hv * 1088 * 4) + up(slots * hv * ck * 4) + up(T * hv * dv * 4)
                 + up(N * hv * (dv // 16) * 16) + (2 * up(T * hv * dk * 4) if hv > hk else 0))
         assert cbwd_ws(lib, _dims(total_tokens=T, n_seqs=N, hk=hk, hv=hv, dk=dk, dv=dv)) == want
