@@ -566,7 +566,9 @@ gdn_status gdn_fwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     if ((d.dk != 64 && d.dk != 128) || d.dv % 16 != 0 || d.hv / d.hk > 16) return GDN_ERR_UNSUPPORTED;
     const int64_t T = d.total_tokens, N = d.n_seqs;
     if (N == 0) return T == 0 ? GDN_OK : GDN_ERR_SHAPE;
-    if (!cu_seqlens || !out || !out->S || !out->k || !out->r || !out->a || !out->b || !out->count || !workspace)
+    // cu_seqlens may be NULL only for one token per sequence (T == N): token n is sequence n's
+    if ((!cu_seqlens && T != N) || !out || !out->S || !out->k || !out->r || !out->a || !out->b || !out->count ||
+        !workspace)
         return GDN_ERR_NULL;
     if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_NULL;
     // an incoming state with an open chunk needs its k, r, a and b
@@ -621,12 +623,15 @@ gdn_status gdn_fwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     p.ws = static_cast<float *>(workspace);
     p.ws_slots = slots;
     p.total_tokens = T; p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dk = d.dk; p.dv = d.dv;
-    p.rank_by_length = (N > 1 && N <= kMaxRankedSeqs && T >= 32 * N) ? 1 : 0;
+    p.rank_by_length = (cu_seqlens && N > 1 && N <= kMaxRankedSeqs && T >= 32 * N) ? 1 : 0;
     p.inplace = inplace ? 1 : 0;
     // Waves per 16-row tile: split the dk quarters over more waves when the call
     // has few tiles to spread over the chip's 1024 SIMDs (never changes a bit).
     const int64_t units = N * d.hv * (int64_t)(d.dv / 16);
     p.waves = d.plan_waves ? d.plan_waves : (units < 1024 ? 4 : (units <= 4096 ? 2 : 1));
+    // one token per sequence on average (a decode step): the lean main kernel, whose
+    // workgroups are latency-bound on the state read rather than on the chunk walk
+    p.lean = T <= N ? 1 : 0;
     const hipError_t e = launch_chunked(p, d.io_dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

@@ -68,8 +68,9 @@ __device__ __forceinline__ int64_t clamp_tok(int64_t x, int64_t T) { return x < 
 
 __device__ __forceinline__ SeqChunks seq_chunks(const ChunkedParams &p, int n) {
     SeqChunks s;
-    s.tb = clamp_tok(p.cu_seqlens[n], p.total_tokens);
-    int64_t te = clamp_tok(p.cu_seqlens[n + 1], p.total_tokens);
+    // (no cu_seqlens: one token per sequence, sequence n's token is token n)
+    s.tb = p.cu_seqlens ? clamp_tok(p.cu_seqlens[n], p.total_tokens) : n;
+    int64_t te = p.cu_seqlens ? clamp_tok(p.cu_seqlens[n + 1], p.total_tokens) : n + 1;
     te = te < s.tb ? s.tb : te;
     s.len = te - s.tb;
     int c0 = p.in_count ? p.in_count[n] : 0;
@@ -99,19 +100,28 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(ChunkedParams p) {
     __shared__ float kap[kCk][kCk + 1];
     __shared__ float xi[kCk][kCk + 1];
 
-    const int64_t slot = blockIdx.x;
     const int kh = blockIdx.y;
     const int tid = threadIdx.x;
-    // The sequence owning this slot: the last n with base(n) <= slot.
-    int lo = 0, hi = p.n_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) / 2;
-        if (chunk_slot_base(clamp_tok(p.cu_seqlens[mid], p.total_tokens), mid) <= slot)
-            lo = mid;
-        else
-            hi = mid - 1;
+    // The sequence owning this slot: the last n with base(n) <= slot.  Without
+    // cu_seqlens (one token per sequence) the grid has one workgroup per sequence,
+    // whose only chunk takes slot base(n).
+    int64_t slot;
+    int n;
+    if (p.cu_seqlens) {
+        slot = blockIdx.x;
+        int lo = 0, hi = p.n_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (chunk_slot_base(clamp_tok(p.cu_seqlens[mid], p.total_tokens), mid) <= slot)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        n = lo;
+    } else {
+        n = blockIdx.x;
+        slot = chunk_slot_base(n, n);
     }
-    const int n = lo;
     const SeqChunks sc = seq_chunks(p, n);
     const int64_t j = slot - sc.base;
     if (j < 0 || j >= sc.nch || slot >= p.ws_slots) return;  // uniform over the workgroup
@@ -244,13 +254,14 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(ChunkedParams p) {
 // its products, into registers, with rows outside the chunk clamped to a valid row
 // and zeroed after the load (no branch per load).
 
-// What one chunk needs from global memory, per lane of a W-wave workgroup.
-template <int DK, class IO, int W>
+// What one chunk needs from global memory, per lane of a W-wave workgroup.  The lean
+// form stages the queries in LDS like the keys instead of holding them as operands.
+template <int DK, class IO, int W, bool LEAN>
 struct ChunkFetch {
     static constexpr int KIT = kCk * DK / 4 / (64 * W);  // 4-element key items per lane (LDS staging)
     static constexpr int OT = DK / 16 / W;               // state tiles owned by one wave
-    typename Raw4<IO>::T kr[KIT];   // key rows for LDS: item tid + 64 W s
-    typename Raw4<IO>::T qa[OT];    // query operand: token x, columns of the wave's tiles
+    typename Raw4<IO>::T kr[LEAN ? 1 : KIT];  // key rows for LDS: item tid + 64 W s
+    typename Raw4<IO>::T qa[LEAN ? 1 : OT];   // query operand: token x, columns of the wave's tiles
     uint32_t v[4];                  // value bits (row x) of tokens 4 g + c
     float b[4];                     // their betas
     float4 trow, brow;              // T[x][4 g ..] and B[x][4 g ..]
@@ -258,22 +269,29 @@ struct ChunkFetch {
     float g15;                      // Gam_15
 };
 
-// BW: the forward walk of the chunked backward.  No outputs: the state at each
+// MODE 0: the chunked form.  MODE 2 (lean): the same arithmetic, instruction for
+// instruction, for calls of a few tokens per sequence (a decode step): no read-ahead
+// of the next chunk, queries and the chunk-end update's key operands read from LDS
+// when used, so that four waves fit on a SIMD and their memory latencies overlap.
+// MODE 1: the forward walk of the chunked backward.  No outputs: the state at each
 // chunk's start goes to the checkpoints, x = v - Gam P to xv, and every chunk folds
 // (a sequence's last, partial chunk with the weights of its last token, so that the
 // final state is hT), which gives the partial sums of <dhT, hT>.
-template <int DK, class IO, int W, bool BW>
-__global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p) {
+template <int DK, class IO, int W, int MODE>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 3 : 1)))
+void gdn_chunk_main_kernel(ChunkedParams p) {
+    constexpr bool BW = MODE == 1, LEAN = MODE == 2;
     constexpr int REC = BW ? kChunkRecBwd : kChunkRec;
     constexpr int NT = DK / 16;
     constexpr int KP = DK + 4;
     constexpr int OT = NT / W;       // tiles per wave
     constexpr int QT = NT / 4;       // tiles per quarter
     constexpr int OQ = 4 / W;        // quarters per wave
-    using CF = ChunkFetch<DK, IO, W>;
+    using CF = ChunkFetch<DK, IO, W, LEAN>;
     using RW = Raw4<IO>;
     static_assert(NT % 4 == 0 && OT * W == NT, "tiles");
     __shared__ __align__(16) float Ks[kCk][KP];         // the chunk's keys, fp32 (accessed as float4)
+    __shared__ __align__(16) float Qs[LEAN ? kCk : 1][KP];  // (lean) the chunk's queries
     __shared__ float4 Xch[W > 1 ? 8 : 1][64];           // P and Z partials of the four quarters
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -352,9 +370,9 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
         for (int s = 0; s < CF::KIT; ++s) {
             const int it = tid + 64 * W * s;
             const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
-            F.kr[s] = RW::load_at(kb, (uint32_t)clampm(m, m0, m1) * krow_b + (uint32_t)c * E);
+            if constexpr (!LEAN) F.kr[s] = RW::load_at(kb, (uint32_t)clampm(m, m0, m1) * krow_b + (uint32_t)c * E);
         }
-        if constexpr (!BW) {
+        if constexpr (!BW && !LEAN) {
             const uint32_t qoff = (uint32_t)clampm(x, m0, m1) * krow_b + (uint32_t)(16 * t_first + 4 * g) * E;
 #pragma unroll
             for (int t = 0; t < OT; ++t) F.qa[t] = RW::load_at(qb, qoff + 16u * t * E);
@@ -388,20 +406,47 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
         if (4 * g + c < sc.c0 && p.in_r) Rkeep[c] = p.in_r[(((size_t)n * kCk + 4 * g + c) * p.hv + h) * p.dv + row0 + x];
 
     CF F;
-    if (nch > 0) fetch(F, 0);
+    if (!LEAN && nch > 0) fetch(F, 0);
     for (int j = 0; j < nch; ++j) {
         int m0, m1;
         int64_t t0;
         geom(j, m0, m1, t0);
         const bool full = m1 == kCk;
+        if constexpr (LEAN) fetch(F, j);
 
         // keys into LDS (cached keys of a resumed chunk only when it closes here), the
         // rest of this chunk's reads into working registers, then the next chunk's reads
+        if constexpr (LEAN) {
+            // zeros in the rows outside this call's tokens, and those rows read
+            // straight into LDS (the same values and zeros as below; no registers held
+            // for the rows; each row written by one loop only)
+            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int s = 0; s < CF::KIT; ++s) {
-            const int it = tid + 64 * W * s;
-            const int m = it / (DK / 4);
-            *reinterpret_cast<float4 *>(&Ks[m][4 * (it % (DK / 4))]) = RW::widen(RW::keep(F.kr[s], m >= m0 && m < m1));
+            for (int s = 0; s < CF::KIT; ++s) {
+                const int it = tid + 64 * W * s;
+                const int m = it / (DK / 4);
+                if (m < m0 || m >= m1) {
+                    *reinterpret_cast<float4 *>(&Ks[m][4 * (it % (DK / 4))]) = z4;
+                    *reinterpret_cast<float4 *>(&Qs[m][4 * (it % (DK / 4))]) = z4;
+                }
+            }
+            const char *kb = static_cast<const char *>(p.k) + ((size_t)t0 * p.hk + kh) * DK * IO::ESZ;
+            const char *qb = static_cast<const char *>(p.q) + ((size_t)t0 * p.hk + kh) * DK * IO::ESZ;
+            const uint32_t krow_b = (uint32_t)krow * IO::ESZ;
+            for (int it = m0 * (DK / 4) + tid; it < m1 * (DK / 4); it += 64 * W) {
+                const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+                const uint32_t off = (uint32_t)m * krow_b + (uint32_t)c * IO::ESZ;
+                const typename RW::T kw = RW::load_at(kb, off), qw = RW::load_at(qb, off);
+                *reinterpret_cast<float4 *>(&Ks[m][c]) = RW::widen(kw);
+                *reinterpret_cast<float4 *>(&Qs[m][c]) = RW::widen(qw);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < CF::KIT; ++s) {
+                const int it = tid + 64 * W * s;
+                const int m = it / (DK / 4);
+                *reinterpret_cast<float4 *>(&Ks[m][4 * (it % (DK / 4))]) = RW::widen(RW::keep(F.kr[s], m >= m0 && m < m1));
+            }
         }
         if (m0 > 0 && full) {
             for (int it = tid; it < m0 * (DK / 4); it += 64 * W) {
@@ -410,8 +455,8 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
                     *reinterpret_cast<const float4 *>(p.in_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + c);
             }
         }
-        float4 qv[BW ? 1 : OT];
-        if constexpr (!BW) {
+        float4 qv[BW || LEAN ? 1 : OT];
+        if constexpr (!BW && !LEAN) {
 #pragma unroll
             for (int t = 0; t < OT; ++t) qv[t] = RW::widen(RW::keep(F.qa[t], x >= m0 && x < m1));
         }
@@ -432,7 +477,7 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
         }
         const float4 trow = F.trow, brow = F.brow, gam = F.gam, dwv = F.dw;
         const float g15 = F.g15;
-        fetch(F, j + 1);
+        if constexpr (!LEAN) fetch(F, j + 1);
         lds_barrier();
 
         // partial products of this wave's quarters
@@ -441,6 +486,8 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
         for (int q = 0; q < OQ; ++q) {
             Pq[q] = f4_zero();
             Zq[q] = f4_zero();
+            // (lean: operands read from LDS one quarter at a time, not all up front)
+            if constexpr (LEAN) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int tt = 0; tt < QT; ++tt) {
                 const int t = q * QT + tt;  // the wave's tile index
@@ -451,14 +498,16 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
                     Pq[q] = mfma_16x16x4(ka.z, S[t][2], Pq[q]);
                     Pq[q] = mfma_16x16x4(ka.w, S[t][3], Pq[q]);
                 } else {
+                    const float4 qa = LEAN ? *reinterpret_cast<const float4 *>(&Qs[x][16 * (t_first + t) + 4 * g])
+                                           : qv[LEAN ? 0 : t];
                     Pq[q] = mfma_16x16x4(ka.x, S[t][0], Pq[q]);
-                    Zq[q] = mfma_16x16x4(qv[t].x, S[t][0], Zq[q]);
+                    Zq[q] = mfma_16x16x4(qa.x, S[t][0], Zq[q]);
                     Pq[q] = mfma_16x16x4(ka.y, S[t][1], Pq[q]);
-                    Zq[q] = mfma_16x16x4(qv[t].y, S[t][1], Zq[q]);
+                    Zq[q] = mfma_16x16x4(qa.y, S[t][1], Zq[q]);
                     Pq[q] = mfma_16x16x4(ka.z, S[t][2], Pq[q]);
-                    Zq[q] = mfma_16x16x4(qv[t].z, S[t][2], Zq[q]);
+                    Zq[q] = mfma_16x16x4(qa.z, S[t][2], Zq[q]);
                     Pq[q] = mfma_16x16x4(ka.w, S[t][3], Pq[q]);
-                    Zq[q] = mfma_16x16x4(qv[t].w, S[t][3], Zq[q]);
+                    Zq[q] = mfma_16x16x4(qa.w, S[t][3], Zq[q]);
                 }
             }
         }
@@ -493,8 +542,8 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
 
         // the chunk-end update's key operands (K^T tiles of this wave), read early
         const bool fold = BW || full;
-        float kt[OT][4];
-        if (fold) {
+        float kt[LEAN ? 1 : OT][4];
+        if (!LEAN && fold) {
 #pragma unroll
             for (int t = 0; t < OT; ++t)
 #pragma unroll
@@ -551,10 +600,13 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
 #pragma unroll
             for (int t = 0; t < OT; ++t) {
                 f4 C = f4{g15 * S[t][0], g15 * S[t][1], g15 * S[t][2], g15 * S[t][3]};
-                C = mfma_16x16x4(kt[t][0], w0, C);
-                C = mfma_16x16x4(kt[t][1], w1, C);
-                C = mfma_16x16x4(kt[t][2], w2, C);
-                C = mfma_16x16x4(kt[t][3], w3, C);
+                float k4[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) k4[c] = LEAN ? Ks[4 * g + c][16 * (t_first + t) + x] : kt[LEAN ? 0 : t][c];
+                C = mfma_16x16x4(k4[0], w0, C);
+                C = mfma_16x16x4(k4[1], w1, C);
+                C = mfma_16x16x4(k4[2], w2, C);
+                C = mfma_16x16x4(k4[3], w3, C);
                 S[t] = C;
             }
             folded = true;
@@ -634,41 +686,322 @@ __global__ __launch_bounds__(64 * W) void gdn_chunk_main_kernel(ChunkedParams p)
     }
 }
 
-template <class IO, int DK, bool BW>
+// A one-token-per-sequence call without cu_seqlens (sequence n's token is row n): one
+// wave per (sequence, value head) forms the chunk's tables itself (no prep launch,
+// the prep kernel's operations in its order), then walks that head's 16-row state
+// tiles, reading the next tile's state while the current one computes.  Each tile's
+// arithmetic is the main kernel's for a one-token call, instruction for instruction
+// (P, Z, R, U, O and the chunk-end update as above), so the bits are the main
+// kernel's, and a prefill's.
+template <int DK, class IO>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gdn_chunk_decode_kernel(ChunkedParams p) {
+    constexpr int NT = DK / 16, KP = DK + 4, QT = NT / 4;
+    using RW = Raw4<IO>;
+    __shared__ __align__(16) float Ks[kCk][KP];
+    __shared__ __align__(16) float Qrow[DK];  // the token's query (the only query row used)
+    __shared__ float decs[kCk], bets[kCk], gams[kCk], dws[kCk];
+    __shared__ float kap[kCk][kCk + 1], xi[kCk][kCk + 1], Tm[kCk][kCk + 1];
+    const int lane = threadIdx.x, x = lane & 15, g = lane >> 4;
+    const int tiles = p.dv / 16;
+    const int G = p.hv / p.hk;
+    int n, h;
+    {
+        // value heads of one key head get ids equal modulo 8 (one XCD, one L2)
+        const int ngroups = p.n_seqs * p.hk;
+        const int full = (ngroups / 8) * 8 * G;
+        const int id = blockIdx.x;
+        int grp, member;
+        if (id < full) {
+            const int xcd = id % 8, slot = id / 8;
+            grp = (slot / G) * 8 + xcd;
+            member = slot % G;
+        } else {
+            grp = full / G + (id - full) / G;
+            member = (id - full) % G;
+        }
+        n = grp / p.hk;
+        h = (grp % p.hk) * G + member;
+    }
+    const int kh = h / G;
+    int c0 = p.in_count ? p.in_count[n] : 0;
+    c0 = c0 < 0 ? 0 : (c0 > kCk - 1 ? kCk - 1 : c0);
+    const int m0 = c0, m1 = c0 + 1;
+    const bool full = m1 == kCk;
+    const bool inplace = p.inplace != 0;
+    const size_t vrow = (size_t)p.hv * p.dv;
+    const float bt = p.beta[(size_t)n * p.hv + h];
+
+    // The chunk's tables, formed here with the prep kernel's operations in its order:
+    // keys (cached, then the token's) in LDS with zero rows after them, the decay
+    // factors and betas, the Gram tiles K K^T and Q K^T (MFMA chains), Gam, A, B, the
+    // chunk-end weights, and T = (I + A)^-1 by columns.  (Query rows other than the
+    // token's are zero in the prep kernel; they only reach rows no result reads.)
+    for (int it = lane; it < kCk * (DK / 4); it += 64) {
+        const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (m < m0)
+            kv = *reinterpret_cast<const float4 *>(p.in_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + c);
+        else if (m == m0)
+            kv = RW::widen(RW::load(p.k, ((size_t)n * p.hk + kh) * DK + c));
+        *reinterpret_cast<float4 *>(&Ks[m][c]) = kv;
+    }
+    for (int it = lane; it < DK / 4; it += 64)
+        *reinterpret_cast<float4 *>(&Qrow[4 * it]) = RW::widen(RW::load(p.q, ((size_t)n * p.hk + kh) * DK + 4 * it));
+    if (lane < kCk) {
+        const int m = lane;
+        float a = 0.f, b = 0.f;
+        if (m < m0) {
+            a = p.in_a[((size_t)n * kCk + m) * p.hv + h];
+            b = p.in_b[((size_t)n * kCk + m) * p.hv + h];
+        } else if (m == m0) {
+            a = decay_factor(p.g[(size_t)n * p.hv + h]);
+            b = bt;
+        }
+        decs[m] = a;
+        bets[m] = b;
+    }
+    lds_barrier();
+    {
+        f4 ak = f4_zero(), aq = f4_zero();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float4 b4 = *reinterpret_cast<const float4 *>(&Ks[x][16 * t + 4 * g]);
+            const float4 q4 = x == m0 ? *reinterpret_cast<const float4 *>(&Qrow[16 * t + 4 * g])
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+            ak = mfma_16x16x4(b4.x, b4.x, ak);
+            aq = mfma_16x16x4(q4.x, b4.x, aq);
+            ak = mfma_16x16x4(b4.y, b4.y, ak);
+            aq = mfma_16x16x4(q4.y, b4.y, aq);
+            ak = mfma_16x16x4(b4.z, b4.z, ak);
+            aq = mfma_16x16x4(q4.z, b4.z, aq);
+            ak = mfma_16x16x4(b4.w, b4.w, ak);
+            aq = mfma_16x16x4(q4.w, b4.w, aq);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            kap[4 * g + r][x] = ak[r];
+            xi[4 * g + r][x] = aq[r];
+        }
+    }
+    lds_barrier();
+    // entries (m, r), four per lane; A over kap and B over xi in place (each entry is
+    // read and written by its own lane)
+    for (int e = lane; e < kCk * kCk; e += 64) {
+        const int m = e / kCk, r = e % kCk;
+        float dreg[kCk];
+#pragma unroll
+        for (int s = 0; s < kCk; ++s) dreg[s] = decs[s];
+        float gmr = 1.f;
+#pragma unroll
+        for (int s = kCk - 1; s >= 0; --s) gmr = (s <= m && s > r) ? gmr * dreg[s] : gmr;
+        const bool row = m < m1;
+        kap[m][r] = (row && r < m) ? (bets[m] * gmr) * kap[m][r] : 0.f;  // A
+        const bool newrow = m >= m0 && m < m1;
+        xi[m][r] = (newrow && r <= m) ? gmr * xi[m][r] : 0.f;            // B
+        if (r == 0) gams[m] = row ? gmr * dreg[0] : 0.f;
+        if (m == kCk - 1) dws[r] = gmr;
+    }
+    lds_barrier();
+    if (lane < kCk) {
+        const int k = lane;
+        float col[kCk];
+#pragma unroll
+        for (int mm = 0; mm < kCk; ++mm) {
+            float acc = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < mm; ++rr)
+                if (rr >= k) acc = __builtin_fmaf(kap[mm][rr], col[rr], acc);
+            col[mm] = mm < k ? 0.f : (mm == k ? 1.f : -acc);
+            if (mm >= m1) col[mm] = 0.f;
+            Tm[mm][k] = col[mm];
+        }
+    }
+    lds_barrier();
+    const float4 trow = make_float4(Tm[x][4 * g], Tm[x][4 * g + 1], Tm[x][4 * g + 2], Tm[x][4 * g + 3]);
+    const float4 brow = make_float4(xi[x][4 * g], xi[x][4 * g + 1], xi[x][4 * g + 2], xi[x][4 * g + 3]);
+    const float gm[4] = {gams[4 * g], gams[4 * g + 1], gams[4 * g + 2], gams[4 * g + 3]};
+    const float4 dwv = make_float4(dws[4 * g], dws[4 * g + 1], dws[4 * g + 2], dws[4 * g + 3]);
+    const float g15 = gams[kCk - 1];
+
+    // tile 0's state, value and cached R rows; then each tile reads the next one's
+    f4 Sn[NT];
+    float vn, rn[4];
+    auto read_tile = [&](int tile) {
+        const int row0 = tile * 16;
+        const float *src = p.in_S ? p.in_S + (((size_t)n * p.hv + h) * p.dv + row0 + x) * DK : nullptr;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            Sn[t] = f4_zero();
+            if (src) {
+                const float4 v4 = *reinterpret_cast<const float4 *>(src + 16 * t + 4 * g);
+                Sn[t] = f4{v4.x, v4.y, v4.z, v4.w};
+            }
+        }
+        vn = IO::load1(p.v, (size_t)n * vrow + (size_t)h * p.dv + row0 + x);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            rn[c] = 0.f;
+            if (4 * g + c < c0 && p.in_r) rn[c] = p.in_r[(((size_t)n * kCk + 4 * g + c) * p.hv + h) * p.dv + row0 + x];
+        }
+    };
+    read_tile(0);
+    const int first = inplace ? (full ? 0 : m0) : 0;  // rows of the open chunk to write (R, a, b, k)
+    const int mo = full ? 0 : m1;
+    for (int tile = 0; tile < tiles; ++tile) {
+        const int row0 = tile * 16;
+        f4 S[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) S[t] = Sn[t];
+        const float vv = vn;
+        float Rkeep[4] = {rn[0], rn[1], rn[2], rn[3]};
+        if (tile + 1 < tiles) read_tile(tile + 1);
+
+        f4 Pq[4], Zq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            Pq[q] = f4_zero();
+            Zq[q] = f4_zero();
+            __builtin_amdgcn_sched_barrier(0);  // operands read one quarter at a time
+#pragma unroll
+            for (int tt = 0; tt < QT; ++tt) {
+                const int t = q * QT + tt;
+                const float4 ka = *reinterpret_cast<const float4 *>(&Ks[x][16 * t + 4 * g]);
+                const float4 qa = x == m0 ? *reinterpret_cast<const float4 *>(&Qrow[16 * t + 4 * g])
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+                Pq[q] = mfma_16x16x4(ka.x, S[t][0], Pq[q]);
+                Zq[q] = mfma_16x16x4(qa.x, S[t][0], Zq[q]);
+                Pq[q] = mfma_16x16x4(ka.y, S[t][1], Pq[q]);
+                Zq[q] = mfma_16x16x4(qa.y, S[t][1], Zq[q]);
+                Pq[q] = mfma_16x16x4(ka.z, S[t][2], Pq[q]);
+                Zq[q] = mfma_16x16x4(qa.z, S[t][2], Zq[q]);
+                Pq[q] = mfma_16x16x4(ka.w, S[t][3], Pq[q]);
+                Zq[q] = mfma_16x16x4(qa.w, S[t][3], Zq[q]);
+            }
+        }
+        f4 P, Z;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            P[c] = (Pq[0][c] + Pq[1][c]) + (Pq[2][c] + Pq[3][c]);
+            Z[c] = (Zq[0][c] + Zq[1][c]) + (Zq[2][c] + Zq[3][c]);
+        }
+        f4 R, OC;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int m = 4 * g + c;
+            const bool on = m >= m0 && m < m1;
+            const float bb = on ? bt : 0.f;
+            const float vb = bb * (on ? vv : 0.f);
+            const float fresh = __builtin_fmaf(-(bb * gm[c]), P[c], vb);
+            R[c] = on ? fresh : (m < m0 ? Rkeep[c] : 0.f);
+            Rkeep[c] = on ? fresh : Rkeep[c];
+            OC[c] = gm[c] * Z[c];
+        }
+        f4 U = f4_zero();
+        U = mfma_16x16x4(trow.x, R[0], U);
+        U = mfma_16x16x4(trow.y, R[1], U);
+        U = mfma_16x16x4(trow.z, R[2], U);
+        U = mfma_16x16x4(trow.w, R[3], U);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) U[c] = U[c] + 0.f;
+        f4 O = OC;
+        O = mfma_16x16x4(brow.x, U[0], O);
+        O = mfma_16x16x4(brow.y, U[1], O);
+        O = mfma_16x16x4(brow.z, U[2], O);
+        O = mfma_16x16x4(brow.w, U[3], O);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (4 * g + c == m0) IO::store1(p.out, (size_t)n * vrow + (size_t)h * p.dv + row0 + x, O[c] + 0.f);
+        if (full) {
+            const float w0 = dwv.x * U[0], w1 = dwv.y * U[1], w2 = dwv.z * U[2], w3 = dwv.w * U[3];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                f4 C = f4{g15 * S[t][0], g15 * S[t][1], g15 * S[t][2], g15 * S[t][3]};
+                C = mfma_16x16x4(Ks[4 * g + 0][16 * t + x], w0, C);
+                C = mfma_16x16x4(Ks[4 * g + 1][16 * t + x], w1, C);
+                C = mfma_16x16x4(Ks[4 * g + 2][16 * t + x], w2, C);
+                C = mfma_16x16x4(Ks[4 * g + 3][16 * t + x], w3, C);
+                S[t] = C;
+            }
+        }
+        // this tile's outgoing state (written in place only when the chunk closed) and R rows
+        if (!inplace || full) {
+            float *dst = p.out_S + (((size_t)n * p.hv + h) * p.dv + row0 + x) * DK;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                *reinterpret_cast<float4 *>(dst + 16 * t + 4 * g) = make_float4(S[t][0], S[t][1], S[t][2], S[t][3]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int m = 4 * g + c;
+            if (m >= first && m < mo) p.out_r[(((size_t)n * kCk + m) * p.hv + h) * p.dv + row0 + x] = Rkeep[c];
+        }
+    }
+    // the open chunk's decay factors, betas and keys, and the token count
+    if (lane >= first && lane < mo) {
+        const size_t e = ((size_t)n * kCk + lane) * p.hv + h;
+        p.out_a[e] = decs[lane];
+        p.out_b[e] = bets[lane];
+    }
+    if (h % G == 0) {
+        for (int it = lane; it < kCk * (DK / 4); it += 64) {
+            const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+            if (m < first || m >= mo) continue;
+            float4 kv;
+            if (m >= (full ? 0 : m0))
+                kv = IO::load4(p.k, ((size_t)(n - c0 + m) * p.hk + kh) * DK + c);
+            else
+                kv = *reinterpret_cast<const float4 *>(p.in_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + c);
+            *reinterpret_cast<float4 *>(p.out_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + c) = kv;
+        }
+        if (h == 0 && lane == 0) p.out_count[n] = mo;
+    }
+}
+
+template <class IO, int DK, int MODE>
 hipError_t chunked_launch(const ChunkedParams &p, hipStream_t s) {
-    if (p.ws_slots > 0) {
-        hipLaunchKernelGGL((gdn_chunk_prep_kernel<DK, IO, BW>), dim3((unsigned)p.ws_slots, (unsigned)p.hk), dim3(256),
-                           0, s, p);
+    if (p.ws_slots > 0 && (MODE == 1 || p.cu_seqlens)) {  // (the decode kernel forms its own tables)
+        const unsigned gx = p.cu_seqlens ? (unsigned)p.ws_slots : (unsigned)p.n_seqs;
+        hipLaunchKernelGGL((gdn_chunk_prep_kernel<DK, IO, MODE == 1>), dim3(gx, (unsigned)p.hk), dim3(256), 0, s, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (MODE != 1 && !p.cu_seqlens) {  // one token per sequence, no cu_seqlens
+        hipLaunchKernelGGL((gdn_chunk_decode_kernel<DK, IO>), dim3((unsigned)((int64_t)p.n_seqs * p.hv)), dim3(64), 0,
+                           s, p);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((int64_t)p.n_seqs * p.hv * (p.dv / 16)));
     switch (p.waves) {
-        case 1: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 1, BW>), grid, dim3(64), 0, s, p); break;
-        case 2: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 2, BW>), grid, dim3(128), 0, s, p); break;
-        case 4: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 4, BW>), grid, dim3(256), 0, s, p); break;
+        case 1: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 1, MODE>), grid, dim3(64), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 2, MODE>), grid, dim3(128), 0, s, p); break;
+        case 4: hipLaunchKernelGGL((gdn_chunk_main_kernel<DK, IO, 4, MODE>), grid, dim3(256), 0, s, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <class IO, bool BW>
+template <class IO, int MODE>
 hipError_t chunked_io(const ChunkedParams &p, hipStream_t s) {
     switch (p.dk) {
-        case 64: return chunked_launch<IO, 64, BW>(p, s);
-        case 128: return chunked_launch<IO, 128, BW>(p, s);
+        case 64: return chunked_launch<IO, 64, MODE>(p, s);
+        case 128: return chunked_launch<IO, 128, MODE>(p, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int MODE>
+hipError_t chunked_mode(const ChunkedParams &p, int io_dtype, hipStream_t s) {
+    return io_dtype == GDN_BF16 ? chunked_io<IoBf16, MODE>(p, s) : chunked_io<IoF32, MODE>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_chunked(const ChunkedParams &p, int io_dtype, hipStream_t s) {
-    return io_dtype == GDN_BF16 ? chunked_io<IoBf16, false>(p, s) : chunked_io<IoF32, false>(p, s);
+    return p.lean ? chunked_mode<2>(p, io_dtype, s) : chunked_mode<0>(p, io_dtype, s);
 }
 
 hipError_t launch_chunked_bwd_walk(const ChunkedParams &p, int io_dtype, hipStream_t s) {
-    return io_dtype == GDN_BF16 ? chunked_io<IoBf16, true>(p, s) : chunked_io<IoF32, true>(p, s);
+    return chunked_mode<1>(p, io_dtype, s);
 }
 
 }  // namespace gdn

@@ -118,6 +118,7 @@ struct ChunkedParams {
     int32_t rank_by_length;  // workgroups take sequences longest first (n_seqs <= kMaxRankedSeqs)
     int32_t inplace;         // out shares S, k, r, a and b with in (one-token calls only)
     int32_t waves;           // waves per 16-row tile: 1, 2 or 4 (each owns 4 / waves dk quarters)
+    int32_t lean;            // the lean form of the main kernel (few tokens per sequence; same bits)
     // Forward walk of the chunked backward (launch_chunked_bwd_walk): records of
     // kChunkRecBwd floats, no outputs or outgoing chunked state; instead the state at
     // every chunk's start (ck: [slot][hv][dv][dk], like a state), x = v - Gam P of every

@@ -475,9 +475,12 @@ def gdn_fwd_chunked(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=
     and holds the new counts.  ``workspace`` (uint8, at least
     gdn_chunked_workspace_size bytes) is allocated when None.  ``waves`` (0 = automatic,
     else 1, 2 or 4) sets how many waves share a 16-row state tile (never a bit of the
-    result).  Returns (out [T, Hv, dv], state_out)."""
+    result).  ``cu_seqlens`` may be None for one token per sequence (a decode step:
+    sequence n's token is row n).  Returns (out [T, Hv, dv], state_out)."""
     import torch
-    T, hk, dk, hv, dv, N = _dims_of(q, k, v, g, beta, cu_seqlens, require_cu=True)
+    T, hk, dk, hv, dv, N = _dims_of(q, k, v, g, beta, cu_seqlens)
+    if N is None:
+        N = T  # one token per sequence
     want = {"S": (N, hv, dv, dk), "k": (N, GDN_CHUNK, hk, dk), "r": (N, GDN_CHUNK, hv, dv), "a": (N, GDN_CHUNK, hv),
             "b": (N, GDN_CHUNK, hv), "count": (N,)}
     if inplace and (state_in is None or state_out is not None):
@@ -496,7 +499,8 @@ def gdn_fwd_chunked(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=
         _need(t, name, q.dtype)
     _need(g, "g", torch.float32)
     _need(beta, "beta", torch.float32)
-    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
     for st in (state_in, state_out):
         if st is not None:
             for name in ("S", "k", "r", "a", "b"):

@@ -571,6 +571,11 @@ def test_chunked_rejects(lib, case, over, code):
 def test_chunked_small_workspace_null_in_and_noop(lib):
     d = _dims()
     assert call_chunked(lib, d, ws_bytes=ch_ws(lib, d) - 1) == 2
+    # no cu_seqlens is allowed for one token per sequence (then the next check, the
+    # workspace size, is what refuses) and refused otherwise
+    one = _dims(total_tokens=2)
+    assert call_chunked(lib, one, ws_bytes=ch_ws(lib, one) - 1, cu=None) == 2
+    assert call_chunked(lib, d, cu=None) == 1
     assert call_chunked(lib, None) == 1
     assert call_chunked(lib, _dims(n_seqs=0, total_tokens=0)) == 0
     # no incoming state is allowed (empty states); a missing out array is not

@@ -257,3 +257,33 @@ def test_every_wave_split_gives_the_same_bits(gpu, dk, io):
     _, st1 = run(gpu, synth.token_slice(one, 0, 69, h0=one.h0), start_state(gpu, one), waves=4)
     o, st2 = run(gpu, synth.token_slice(one, 69, 70), st1, waves=2)
     assert bit_equal(o, ref_out[69:70])
+
+
+def test_decode_without_cu_seqlens(gpu):
+    """A one-token-per-sequence call may pass no cu_seqlens (sequence n's token is
+    row n): the same bits as with cu_seqlens = 0, 1, ..., N, out of place and in
+    place, across a chunk end, for a batch of 5 sequences at different offsets."""
+    w = synth.make_workload(661, [30 + 3 * n for n in range(5)], hk=2, hv=4, dk=128, dv=64, h0_std=0.1)
+    cu = w.cu_seqlens.tolist()
+    N = w.n_seqs
+    pre = synth.Workload(*(torch.cat([getattr(w, nm)[cu[n]:cu[n + 1] - 4] for n in range(N)])
+                           for nm in ("q", "k", "v", "g", "beta")),
+                         synth.cu_from_lengths([cu[n + 1] - cu[n] - 4 for n in range(N)]), w.h0)
+    _, st = run(gpu, pre, start_state(gpu, w))
+    st_a = {k: v.clone() for k, v in st.items()}
+    st_b = {k: v.clone() for k, v in st.items()}
+    for step in range(4):
+        idx = torch.tensor([cu[n + 1] - 4 + step for n in range(N)])
+        d = {nm: getattr(w, nm)[idx].contiguous().to(DEV) for nm in ("q", "k", "v", "g", "beta")}
+        ar = torch.arange(N + 1, dtype=torch.int32, device=DEV)
+        o1, s1 = gpu.gdn_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], ar, st)
+        o2, s2 = gpu.gdn_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], None, st)
+        o3, st_a = gpu.gdn_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], None, st_a, inplace=True)
+        o4, st_b = gpu.gdn_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], ar, st_b, inplace=True)
+        torch.cuda.synchronize()
+        assert bit_equal(o1, o2) and bit_equal(o1, o3) and bit_equal(o1, o4), step
+        assert states_equal(s1, s2) and states_equal(s1, st_a) and states_equal(s1, st_b), step
+        st = s1
+        st_a = {k: v.clone() for k, v in st_a.items()}
+        st_b = {k: v.clone() for k, v in st_b.items()}
+    say("chunked decode without cu_seqlens: same bits as with it, in place and out of place")
