@@ -50,6 +50,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X: 256 CUs x 2.4 GHz x 256 flop/clk
+FP32_MATRIX_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA (the same figure)
 HBM_PEAK_GBS = 8000.0             # MI355X HBM3E
 METRIC = "GDN recurrent fwd tokens/s (prefill, decode) + % HBM/FP32-VALU roofline"
 HEADS = dict(hk=16, hv=32, dk=128, dv=128)
@@ -554,24 +555,63 @@ def main():
         got_g = {"dq": grads["dq"][:, 0:1].cpu(), "dk": grads["dk"][:, 0:1].cpu(), "dv": grads["dv"][:, 0:2].cpu(),
                  "dbeta": grads["dbeta"][:, 0:2].cpu(), "dg": grads["dg"][:, 0:2].cpu(),
                  "dh0": grads["dh0"][:, 0:2].cpu()}
+        # the chunked backward (gdn_bwd_chunked, matrix cores) on the same inputs
+        ws_b_bytes = int(ws.numel())
+        del ws
+        ws_cb = torch.empty(gdn.gdn_bwd_chunked_workspace_size(bdims), dtype=torch.uint8, device=dev)
+        grads_c = gdn.gdn_bwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                                      workspace=ws_cb, stream=stream)
+
+        def bwd_chunked(_i):
+            gdn.gdn_bwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                                workspace=ws_cb, grads=grads_c, stream=stream)
+
+        per_bc, _, _ = time_launches(bwd_chunked, args.steps, 3, stream)
+        bwd_chunked(0)
+        torch.cuda.synchronize()
+        msbc = float(np.median(per_bc))
+        got_gc = {"dq": grads_c["dq"][:, 0:1].cpu(), "dk": grads_c["dk"][:, 0:1].cpu(),
+                  "dv": grads_c["dv"][:, 0:2].cpu(), "dbeta": grads_c["dbeta"][:, 0:2].cpu(),
+                  "dg": grads_c["dg"][:, 0:2].cpu(), "dh0": grads_c["dh0"][:, 0:2].cpu()}
+        rec_bc = {"tokens": T, "n_seqs": w.n_seqs, "ms_median": msbc, "tokens_per_s": T / (msbc / 1e3),
+                  "launch_ms_percentiles": percentiles(per_bc), "launches": 4,
+                  "workspace_bytes": int(ws_cb.numel()),
+                  "roofline": {"bound": "mfma", "achieved": bflops / (msbc / 1e3) / 1e12,
+                               "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": bflops / (msbc / 1e3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
+                               "flops_per_launch": bflops}}
+        workloads["backward_chunked_prefill"] = rec_bc
+        del ws_cb, grads_c
         rec_b = {"tokens": T, "n_seqs": w.n_seqs, "ms_median": msb, "tokens_per_s": T / (msb / 1e3),
                  "launch_ms_percentiles": percentiles(per_b),
-                 "launches": 6, "workspace_bytes": int(ws.numel()),
+                 "launches": 6, "workspace_bytes": ws_b_bytes,
                  "train_forward_ms_median": float(np.median(per_ft)),
                  "ms_median_with_saved_p": float(np.median(per_bs)),
                  "roofline": {"bound": "alu", "achieved": bflops / (msb / 1e3) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": bflops / (msb / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
                               "flops_per_launch": bflops}}
         workloads["backward_varlen_prefill"] = rec_b
-        del dout_d, dhT_d, ws, grads, out_t, hT_t, sp_t
+        del dout_d, dhT_d, grads, out_t, hT_t, sp_t
+        bwd_ref = {}
+
+        def bwd_oracle():
+            if not bwd_ref:
+                s0 = synth.head_slice(w, 0)
+                bwd_ref.update(oracle.gdn_backward(s0.q, s0.k, s0.v, s0.g, s0.beta, s0.cu_seqlens,
+                                                   dout_c[:, 0:2].contiguous(), h0=s0.h0,
+                                                   dhT=dhT_c[:, 0:2].contiguous()))
+            return bwd_ref
 
         def bwd_check():
-            s0 = synth.head_slice(w, 0)
-            rb = oracle.gdn_backward(s0.q, s0.k, s0.v, s0.g, s0.beta, s0.cu_seqlens, dout_c[:, 0:2].contiguous(),
-                                     h0=s0.h0, dhT=dhT_c[:, 0:2].contiguous())
+            rb = bwd_oracle()
             return {"kh0_grads": {k: rel(v.numpy(), rb[k]) for k, v in got_g.items()}}
+
+        def bwd_chunked_check():
+            rb = bwd_oracle()
+            return {"kh0_grads": {k: rel(v.numpy(), rb[k]) for k, v in got_gc.items()}}
         checks.append((rec_b, "parity", bwd_check))
-        progress("backward %.3f ms" % msb)
+        checks.append((rec_bc, "parity", bwd_chunked_check))
+        progress("backward %.3f ms, chunked backward %.3f ms" % (msb, msbc))
 
         # The chunked form with a replaying decode (gdn_fwd_chunked, matrix cores for the
         # products with the state): the benchmark batch as one prefill from h0, and one
@@ -617,16 +657,32 @@ def main():
         got_cd = ocd[:4].cpu()
         del work
 
+        # the same step without cu_seqlens (one token per sequence: the decode kernel)
+        work = {k_: v_.clone() for k_, v_ in st_d.items()}
+        ocd2 = torch.empty_like(ocd)
+        gdn.gdn_fwd_chunked(*dcd, None, work, out=ocd2, stream=stream, workspace=ws_d, inplace=True,
+                            count_out=cnt_out)
+        torch.cuda.synchronize()
+        no_cu_same_bits = bool(torch.equal(ocd.view(torch.int16), ocd2.view(torch.int16)))
+        del work, ocd2
+
         def chunked_dec(_i):
+            gdn.gdn_fwd_chunked(*dcd, None, st_d, out=ocd, stream=stream, workspace=ws_d, inplace=True,
+                                count_out=cnt_out)
+
+        def chunked_dec_cu(_i):
             gdn.gdn_fwd_chunked(*dcd, cu_d, st_d, out=ocd, stream=stream, workspace=ws_d, inplace=True,
                                 count_out=cnt_out)
 
         per_cd2, _, _ = time_launches(chunked_dec, max(args.steps, 50), 10, stream, hold=hold, hold_ms=40.0)
+        per_cd3, _, _ = time_launches(chunked_dec_cu, max(args.steps, 50), 10, stream, hold=hold, hold_ms=40.0)
         rec_ch = {"tokens": T, "n_seqs": w.n_seqs, "chunk": 16, "ms_median": msch, "tokens_per_s": T / (msch / 1e3),
                   "launch_ms_percentiles": percentiles(per_ch),
                   "roofline_frac": FLOPS_PER_TOKEN * T / (msch / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
                   "decode_B256_inplace_us_mean": float(np.mean(per_cd2)) * 1e3,
                   "decode_B256_launch_ms_percentiles": percentiles(per_cd2),
+                  "decode_B256_inplace_with_cu_seqlens_us_mean": float(np.mean(per_cd3)) * 1e3,
+                  "decode_without_cu_seqlens_same_bits": no_cu_same_bits,
                   "decode_states": "chunked prefill of 512 + n % 16 tokens (every open-chunk position)"}
         workloads["chunked_prefill_replay"] = rec_ch
         del st_in, st_out, och, st_d, ocd, ws_c, ws_d
@@ -710,6 +766,8 @@ def main():
             parity_ok = parity_ok and line_ok(rec["parity"])
     if decode:
         parity_ok = parity_ok and decode["bitwise_across_batch_sizes"]
+    if workloads and "chunked_prefill_replay" in workloads:
+        parity_ok = parity_ok and workloads["chunked_prefill_replay"]["decode_without_cu_seqlens_same_bits"]
 
     line = {
         "metric": METRIC,
