@@ -124,6 +124,10 @@ def time_launches(fn, steps, warmup, stream, hold=None, hold_ms=0.0):
     behind a GPU-side spin of ``hold_ms`` first.  Returns (per-launch durations,
     host seconds spent queueing, total ms between the first and last event / K)."""
     import torch
+    if hold is not None and hold_ms > 0:
+        # one untimed call first: a kernel's first launch in the process loads its
+        # code, which can take longer on the host than the hold lasts
+        fn(0)
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -138,6 +142,10 @@ def time_launches(fn, steps, warmup, stream, hold=None, hold_ms=0.0):
         ends[i].record(stream)
     queued = time.perf_counter() - t0
     torch.cuda.synchronize()
+    if hold is not None and hold_ms > 0 and queued * 1e3 > 0.8 * hold_ms:
+        # the host took longer to queue than the hold lasted: the GPU may have idled
+        # inside a timed launch, so time again behind a longer hold
+        return time_launches(fn, steps, warmup, stream, hold, 2.0 * queued * 1e3)
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     span = starts[0].elapsed_time(ends[-1]) / steps
     return per, queued, span
