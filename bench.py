@@ -756,8 +756,8 @@ def main():
                "seconds": dt}
 
     # every line's parity re-check must pass as well
-    def grads_ok(gr):  # the backward's gates: 1e-4 normwise, dg 1e-3
-        return all(e <= (1e-3 if k == "dg" else 1e-4) for k, e in gr.items())
+    def grads_ok(gr):  # the backward's gate: 1e-4 normwise for every gradient
+        return all(e <= 1e-4 for e in gr.values())
 
     def line_ok(par):
         ok = True

@@ -408,6 +408,9 @@ gdn_status gdn_bwd_varlen_noalloc(const gdn_dims *dims,
  *          has exactly one token (total_tokens == n_seqs, a decode step); the count
  *          arrays must always differ.  Any other overlap is GDN_ERR_ALIAS.
  *   o    : [T][hv][dv] outputs, io dtype.
+ *   cu_seqlens : as for gdn_fwd_varlen, or NULL when T == N: then sequence n's one
+ *          token is row n, the results are those of cu_seqlens = 0, 1, .., N, and
+ *          a single kernel does the step (GDN_ERR_NULL if T != N).
  *   workspace : device scratch of at least gdn_chunked_workspace_size bytes,
  *          16-byte aligned, owned by the caller; its contents on entry do not
  *          matter.  About 2.3 KB per (chunk touched, value head).

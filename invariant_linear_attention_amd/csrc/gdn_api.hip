@@ -567,6 +567,7 @@ gdn_status gdn_fwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     const int64_t T = d.total_tokens, N = d.n_seqs;
     if (N == 0) return T == 0 ? GDN_OK : GDN_ERR_SHAPE;
     // cu_seqlens may be NULL only for one token per sequence (T == N): token n is sequence n's
+    // only token.
     if ((!cu_seqlens && T != N) || !out || !out->S || !out->k || !out->r || !out->a || !out->b || !out->count ||
         !workspace)
         return GDN_ERR_NULL;

@@ -7,7 +7,8 @@ gate is 1e-4 normwise per sequence for each gradient (the fp32 state's gate).  d
 is formed as a running sum, over the rest of the sequence, of the terms
 dO_s . o_s - dv_s . v_s, which largely cancel: its error scales with those terms,
 not with dg (which is exactly 0 for a one-token sequence from a zero state), so its
-gate is 1e-3 of the larger of ||dg|| and the norm of the terms in the sequence.
+gate is 1e-4 of the larger of ||dg|| and the norm of the terms in the sequence (the
+measured worst is ~2e-6).
 Determinism and batch invariance are bitwise: every sum has a fixed order and
 nothing crosses sequences.
 """
@@ -20,7 +21,7 @@ from invariant_linear_attention_amd import synth
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-GRAD_TOL = {"dq": 1e-4, "dk": 1e-4, "dv": 1e-4, "dbeta": 1e-4, "dg": 1e-3}
+GRAD_TOL = {"dq": 1e-4, "dk": 1e-4, "dv": 1e-4, "dbeta": 1e-4, "dg": 1e-4}
 DH0_TOL = 1e-4
 
 
