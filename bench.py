@@ -206,7 +206,8 @@ COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 def pmc_pass(dev, stream):
     """One launch of each kernel (prefill, decode at B = 256, the short convolution
-    and its state update, the backward's six), preceded by a plain device copy of COPY_BYTES whose
+    and its state update, the backward's six, the chunked form's prefill and backward),
+    preceded by a plain device copy of COPY_BYTES whose
     FETCH_SIZE / WRITE_SIZE readings calibrate the counters' units."""
     import torch
 
@@ -239,8 +240,15 @@ def pmc_pass(dev, stream):
     dhT = torch.randn((w.n_seqs, 32, 128, 128), generator=gen).to(dev)
     gdn.gdn_bwd_varlen(*d, dout, dhT, stream=stream)
     torch.cuda.synchronize()
-    print("pmc pass: copy %d bytes, prefill %d tokens, decode B=%d, conv %d channels, backward" % (
-        COPY_BYTES, w.total_tokens, B, C), flush=True)
+    # the chunked form (prep + main kernel) and the chunked backward on the same batch
+    st_in = gdn.make_chunk_state(w.n_seqs, 16, 32, 128, 128, dev, h0=d[5])
+    gdn.gdn_fwd_chunked(*d[:5], d[6], st_in, stream=stream)
+    torch.cuda.synchronize()
+    del st_in
+    gdn.gdn_bwd_chunked(*d, dout, dhT, stream=stream)
+    torch.cuda.synchronize()
+    print("pmc pass: copy %d bytes, prefill %d tokens, decode B=%d, conv %d channels, backward, chunked "
+          "prefill and backward" % (COPY_BYTES, w.total_tokens, B, C), flush=True)
 
 
 def main():
@@ -587,7 +595,8 @@ def main():
                   "roofline": {"bound": "mfma", "achieved": bflops / (msbc / 1e3) / 1e12,
                                "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
                                "frac": bflops / (msbc / 1e3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
-                               "flops_per_launch": bflops}}
+                               "flops_per_launch": bflops,
+                               "traffic": traffic_from_profile("backward_chunked", src_hash)}}
         workloads["backward_chunked_prefill"] = rec_bc
         del ws_cb, grads_c
         rec_b = {"tokens": T, "n_seqs": w.n_seqs, "ms_median": msb, "tokens_per_s": T / (msb / 1e3),

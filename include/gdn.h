@@ -462,21 +462,25 @@ gdn_status gdn_fwd_chunked(const gdn_dims *dims,
  *
  * dg as in gdn_bwd_varlen (<dhT, hT> plus the reverse sum of dO . o - dv . v) and
  * dh0 = D at the sequence's start.  A forward walk over the chunks first stores
- * the state at every chunk's start in the workspace; one workgroup per sequence and
- * value head then walks the chunks backwards.  Every sum has a fixed order and
- * nothing crosses sequences: the gradients are deterministic and do not depend on
- * the batch (fp32 computations, equal to gdn_bwd_varlen's to rounding, not
- * bitwise).
+ * the state at every chunk's start in the workspace; P workgroups per sequence and
+ * value head, each holding dv/P rows of D, then walk the chunks backwards, and
+ * the parts' shares of the sums over rows (dq, dk, dbeta, dg) are added in order
+ * afterwards.  Every sum has a fixed order and nothing crosses sequences: the
+ * gradients are deterministic and do not depend on the batch (fp32 computations,
+ * equal to gdn_bwd_varlen's to rounding, not bitwise; P = 1 and P = 2 round
+ * differently).
  *
  *   workspace : device scratch of at least gdn_bwd_chunked_workspace_size bytes,
  *               16-byte aligned, owned by the caller; contents on entry do not
  *               matter.  About 4 dv dk bytes per (16-token chunk, value head) for the
- *               chunk-start states, plus 4 hv (dv + 2 dk) bytes per token (the
- *               second term only when hv > hk) and 4.3 KB per (chunk, value head).
+ *               chunk-start states, plus 4 hv (dv + 2 P dk + 2 P) bytes per token
+ *               (the dk term only when hv > hk or P > 1, the last when P > 1) and
+ *               4.3 KB per (chunk, value head).
  * dk must be 64 or 128, dv 32, 64 or 128 and hv / hk at most 16 (else
- * GDN_ERR_UNSUPPORTED, as are dims->pre, plan_lanes and plan_rows; plan_waves
- * (0, 1, 2 or 4) sets the forward walk's waves per 16-row tile).  Other errors as
- * gdn_bwd_varlen.
+ * GDN_ERR_UNSUPPORTED, as are dims->pre and plan_lanes).  plan_rows sets P (0 =
+ * automatic: 2 for dv = 128, else 1; 2 needs dv >= 64) and plan_waves (0, 1, 2
+ * or 4) the forward walk's waves per 16-row tile, which changes no bit.  Other
+ * errors as gdn_bwd_varlen.
  */
 gdn_status gdn_bwd_chunked_workspace_size(const gdn_dims *dims, uint64_t *bytes);
 
@@ -499,7 +503,7 @@ const char *gdn_status_string(gdn_status status);
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 208
+#define GDN_ABI_VERSION 209
 
 #ifdef __cplusplus
 }

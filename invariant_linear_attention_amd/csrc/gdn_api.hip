@@ -644,21 +644,28 @@ namespace {
 
 // Workspace of the chunked backward, byte offsets (each 256-byte aligned).
 struct BwdChunkWorkspace {
-    uint64_t rec, ck, xv, hdot, dq, dk, total;
+    uint64_t rec, ck, xv, hdot, dq, dk, dbeta, dg, total;
 };
+
+// Workgroups per (sequence, value head) in the chunked backward's reverse walk: each
+// takes a share of the state rows (dims->plan_rows; 0 = 2 for dv = 128, else 1).
+int bwd_chunked_parts(const gdn_dims &d) { return d.plan_rows ? d.plan_rows : (d.dv == 128 ? 2 : 1); }
 
 uint64_t round256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
 
-BwdChunkWorkspace bwd_chunked_workspace(int64_t T, int64_t N, int hk, int hv, int dk, int dv) {
+BwdChunkWorkspace bwd_chunked_workspace(int64_t T, int64_t N, int hk, int hv, int dk, int dv, int parts) {
     BwdChunkWorkspace w{};
     const uint64_t slots = (uint64_t)chunk_ws_slots(T, N);
+    const bool split = hv > hk || parts > 1;  // dq, dk per (value head, part), summed afterwards
     uint64_t o = 0;
     w.rec = o; o = round256(o + slots * hv * kChunkRecBwd * 4);
     w.ck = o; o = round256(o + slots * hv * (uint64_t)dv * dk * 4);
     w.xv = o; o = round256(o + (uint64_t)T * hv * dv * 4);
     w.hdot = o; o = round256(o + (uint64_t)N * hv * (dv / 16) * 4 * 4);
-    w.dq = o; o = round256(o + (hv > hk ? (uint64_t)T * hv * dk * 4 : 0));
-    w.dk = o; o = round256(o + (hv > hk ? (uint64_t)T * hv * dk * 4 : 0));
+    w.dq = o; o = round256(o + (split ? (uint64_t)parts * T * hv * dk * 4 : 0));
+    w.dk = o; o = round256(o + (split ? (uint64_t)parts * T * hv * dk * 4 : 0));
+    w.dbeta = o; o = round256(o + (parts > 1 ? (uint64_t)parts * T * hv * 4 : 0));
+    w.dg = o; o = round256(o + (parts > 1 ? (uint64_t)parts * T * hv * 4 : 0));
     w.total = o;
     return w;
 }
@@ -667,10 +674,11 @@ gdn_status bwd_chunked_check_dims(const gdn_dims *dims) {
     gdn_status st = check_common(dims);
     if (st != GDN_OK) return st;
     const gdn_dims &d = *dims;
-    if (d.pre || d.plan_lanes || d.plan_rows) return GDN_ERR_UNSUPPORTED;
+    if (d.pre || d.plan_lanes) return GDN_ERR_UNSUPPORTED;
     if (d.plan_waves != 0 && d.plan_waves != 1 && d.plan_waves != 2 && d.plan_waves != 4) return GDN_ERR_UNSUPPORTED;
     if ((d.dk != 64 && d.dk != 128) || (d.dv != 32 && d.dv != 64 && d.dv != 128) || d.hv / d.hk > 16)
         return GDN_ERR_UNSUPPORTED;
+    if (d.plan_rows != 0 && d.plan_rows != 1 && !(d.plan_rows == 2 && d.dv >= 64)) return GDN_ERR_UNSUPPORTED;
     if (d.n_seqs == 0 && d.total_tokens != 0) return GDN_ERR_SHAPE;
     return GDN_OK;
 }
@@ -686,7 +694,7 @@ gdn_status gdn_bwd_chunked_workspace_size(const gdn_dims *dims, uint64_t *bytes)
     const gdn_status st = bwd_chunked_check_dims(dims);
     if (st != GDN_OK) return st;
     const gdn_dims &d = *dims;
-    *bytes = bwd_chunked_workspace(d.total_tokens, d.n_seqs, d.hk, d.hv, d.dk, d.dv).total;
+    *bytes = bwd_chunked_workspace(d.total_tokens, d.n_seqs, d.hk, d.hv, d.dk, d.dv, bwd_chunked_parts(d)).total;
     return GDN_OK;
 }
 
@@ -703,7 +711,8 @@ gdn_status gdn_bwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     if (!cu_seqlens || !workspace) return GDN_ERR_NULL;
     if (T > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg || !dbeta))
         return GDN_ERR_NULL;
-    const BwdChunkWorkspace ws = bwd_chunked_workspace(T, N, d.hk, d.hv, d.dk, d.dv);
+    const int parts = bwd_chunked_parts(d);
+    const BwdChunkWorkspace ws = bwd_chunked_workspace(T, N, d.hk, d.hv, d.dk, d.dv, parts);
     if (workspace_bytes < ws.total) return GDN_ERR_SHAPE;
     const int64_t slots = chunk_ws_slots(T, N);
     if (slots > 0x7FFFFFFFll || N * d.hv * (int64_t)(d.dv / 16) > 0x7FFFFFFFll ||
@@ -736,7 +745,9 @@ gdn_status gdn_bwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     const hipStream_t strm = static_cast<hipStream_t>(stream);
     const int rank = (N > 1 && N <= kMaxRankedSeqs && T >= 32 * N) ? 1 : 0;
     const int64_t units = N * d.hv * (int64_t)(d.dv / 16);
-    const int fw_waves = d.plan_waves ? d.plan_waves : (units < 1024 ? 4 : (units <= 4096 ? 2 : 1));
+    // (the walk stores states instead of outputs and holds fewer registers than the
+    // chunked form, so it keeps 4 waves per tile up to more tiles: measured)
+    const int fw_waves = d.plan_waves ? d.plan_waves : (units <= 2048 ? 4 : (units <= 8192 ? 2 : 1));
 
     // forward walk: records, the state at every chunk's start, x = v - Gam P, <dhT, hT>
     ChunkedParams f{};
@@ -759,8 +770,12 @@ gdn_status gdn_bwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     p.rec = f.ws; p.ck = f.ck; p.xv = f.xv; p.hdot = f.hdot;
     p.grad_v = dv; p.grad_g = dg; p.grad_beta = dbeta; p.grad_h0 = dh0;
     p.grad_q = dq; p.grad_k = dk;
-    p.dqh = d.hv > d.hk ? reinterpret_cast<float *>(w + ws.dq) : dq;
-    p.dkh = d.hv > d.hk ? reinterpret_cast<float *>(w + ws.dk) : dk;
+    const bool split = d.hv > d.hk || parts > 1;
+    p.dqh = split ? reinterpret_cast<float *>(w + ws.dq) : dq;
+    p.dkh = split ? reinterpret_cast<float *>(w + ws.dk) : dk;
+    p.dbeta_part = reinterpret_cast<float *>(w + ws.dbeta);
+    p.dg_part = reinterpret_cast<float *>(w + ws.dg);
+    p.parts = parts;
     p.ws_slots = slots; p.total_tokens = T;
     p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dk = d.dk; p.dv = d.dv;
     p.rank_by_length = rank;

@@ -47,9 +47,9 @@ namespace {
 constexpr int kCk = kChunkLen;
 
 // What one chunk of the reverse walk reads from global memory, per lane.
-template <int DK, int DV, class IO>
+template <int DK, int DV, class IO, int P>
 struct RevFetch {
-    static constexpr int NW = DV / 16, NT = DK / 16, CTW = (NT + NW - 1) / NW, RT = DV / 16;
+    static constexpr int NW = DV / 16 / P, NT = DK / 16, CTW = (NT + NW - 1) / NW, RT = NW;
     static constexpr int KITEMS = kCk * DK / 4;                      // 4-element items of a K (or Q) tile
     static constexpr int KIT = (KITEMS + 64 * NW - 1) / (64 * NW);   // per lane
     static constexpr int EPT = (kCk * kCk + 64 * NW - 1) / (64 * NW);  // 16 x 16 entries per lane
@@ -63,9 +63,14 @@ struct RevFetch {
     float ge[EPT], ae[EPT], be[EPT];  // Gam_{m,s}, Gam_{m,s} (k_m . k_s) and beta_m of entries tid + 64 NW e
 };
 
-// One workgroup per (sequence, value head), dv / 16 waves; wave w owns the adjoint
-// state's rows 16 w .. 16 w + 15 (all dk columns, as MFMA accumulators) and, for the
-// products over the rows, the column tiles w, w + dv/16, ...  Per chunk, from the last:
+// P workgroups per (sequence, value head), each of dv / (16 P) waves: part p owns the
+// adjoint state's rows p dv/P .. (p + 1) dv/P - 1, wave w of it rows 16 w .. 16 w + 15
+// of those (all dk columns, as MFMA accumulators) and, for the products over the
+// part's rows, the column tiles w, w + NW, ...  The state rows of D are independent of
+// one another; only the sums over rows (dB, dA, dq, dk, dbeta and the terms of dg)
+// couple them, and each of those is linear in its rows' contributions, so each part
+// writes its own partial results and a last kernel adds the parts in order (P = 1:
+// the results themselves).  Per chunk, from the last:
 //   P1  E, dU, dR, U on the wave's rows; dv; the token rows of dO, dR and U and D into
 //       LDS; D moved to the chunk's start; (wave 0) the previous chunk's per-token results
 //   P2  the wave's partial dB, dA over its rows; dq0 and dk1 on its column tiles
@@ -74,12 +79,13 @@ struct RevFetch {
 // with one LDS barrier between phases.  Keys and queries and the per-token sums are
 // double-buffered by chunk parity, so no barrier is needed between P4 and the next
 // chunk's staging.
-template <int DK, int DV, class IO>
-__global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdChunkParams p) {
-    using RF = RevFetch<DK, DV, IO>;
+template <int DK, int DV, class IO, int P>
+__global__ __launch_bounds__(64 * (DV / 16 / P)) void gdn_bwd_chunk_rev_kernel(BwdChunkParams p) {
+    using RF = RevFetch<DK, DV, IO, P>;
     using RW = Raw4<IO>;
     constexpr int NW = RF::NW, NT = RF::NT, CTW = RF::CTW, RT = RF::RT;
-    constexpr int KP = DK + 4, VP = DV + 4;
+    constexpr int DVP = DV / P;  // state rows of one part
+    constexpr int KP = DK + 4, VP = DVP + 4;
     constexpr int NTH = 64 * NW;
     // (16-byte aligned: read and written as float4)
     __shared__ __align__(16) float Ks[2][kCk][KP];
@@ -87,19 +93,20 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
     __shared__ __align__(16) float dOs[kCk][VP];  // token rows of dO, dR and U
     __shared__ __align__(16) float dRs[kCk][VP];
     __shared__ __align__(16) float Us[kCk][VP];
-    __shared__ __align__(16) float Ds[DV][KP];    // D = dL/dS at the chunk's end
+    __shared__ __align__(16) float Ds[DVP][KP];   // D = dL/dS at the chunk's end (the part's rows)
     __shared__ float dBp[NW][kCk][kCk + 1], dAp[NW][kCk][kCk + 1];
     __shared__ float Ms[kCk][kCk + 1], Hs[kCk][kCk + 1];  // dB Gam (s <= m), dA beta Gam (s < m)
     __shared__ float abrow[kCk];                          // sum_s dA[m][s] Gam_{m,s} (k_m . k_s)
-    __shared__ float red[2][NW][kCk][4];                  // per parity, wave and token: dR.x, dv.v, q.dq
+    __shared__ __align__(16) float red[2][NW][kCk][4];    // per parity, wave and token: dR.x, dv.v, q.dq
+    __shared__ __align__(16) float phis[kCk];             // wave 0: the chunk's phi of every token
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int x = lane & 15, g = lane >> 4;
     // Workgroups that read the same keys and queries (one sequence and key head) get
     // ids equal modulo 8, so they run on one XCD and share its L2.
-    int rank, h;
+    int rank, h, part;
     {
-        const int G = p.hv / p.hk;
+        const int G = p.hv / p.hk * P;  // (value head, part) pairs of a key head
         const int ngroups = p.n_seqs * p.hk;
         const int full = (ngroups / 8) * 8 * G;
         const int id = blockIdx.x;
@@ -113,11 +120,13 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
             member = (id - full) % G;
         }
         rank = grp / p.hk;
-        h = (grp % p.hk) * G + member;
+        h = (grp % p.hk) * (G / P) + member / P;
+        part = member % P;
     }
     const int n = p.rank_by_length ? seq_by_length_rank(p.cu_seqlens, p.n_seqs, rank, tid, NTH) : rank;
     const int kh = h / (p.hv / p.hk);
-    const int r0 = 16 * wave;  // this wave's state rows
+    const int r0 = 16 * wave;           // this wave's state rows within the part
+    const int rg = part * DVP + r0;     // the same rows within the head
     int64_t tb = p.cu_seqlens[n], te = p.cu_seqlens[n + 1];
     tb = tb < 0 ? 0 : (tb > p.total_tokens ? p.total_tokens : tb);
     te = te < tb ? tb : (te > p.total_tokens ? p.total_tokens : te);
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
     // is D[r0 + x][16 t + 4 g + c]
     f4 Dt[NT];
     {
-        const float *src = p.dhT ? p.dhT + (((size_t)n * p.hv + h) * DV + r0 + x) * DK : nullptr;
+        const float *src = p.dhT ? p.dhT + (((size_t)n * p.hv + h) * DV + rg + x) * DK : nullptr;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             Dt[t] = f4_zero();
@@ -143,10 +152,12 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
             }
         }
     }
-    // <dhT, hT> from the forward walk's partial sums, in order (the dg running sum's start)
+    // <dhT, hT> over the part's rows from the forward walk's partial sums (four per
+    // 16-row tile), in order: the start of the part's dg running sum
     float carry = 0.f;
     if (p.dhT)
-        for (int i = 0; i < p.hdot_parts; ++i) carry = carry + p.hdot[((size_t)n * p.hv + h) * p.hdot_parts + i];
+        for (int i = part * (DVP / 16) * 4; i < (part + 1) * (DVP / 16) * 4; ++i)
+            carry = carry + p.hdot[((size_t)n * p.hv + h) * p.hdot_parts + i];
 
     auto chunk_m1 = [&](int j) {
         const int64_t left = len - (int64_t)kCk * j;
@@ -173,9 +184,9 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const uint32_t tm = (uint32_t)(4 * g + c < m1 ? 4 * g + c : m1 - 1);
-            F.dor[c] = RW::load1_at(ob, tm * vrow_b + (uint32_t)(r0 + x) * E);
-            F.vr[c] = RW::load1_at(vb, tm * vrow_b + (uint32_t)(r0 + x) * E);
-            F.xr[c] = *reinterpret_cast<const float *>(xb + tm * (uint32_t)(vrow * 4) + (uint32_t)(r0 + x) * 4);
+            F.dor[c] = RW::load1_at(ob, tm * vrow_b + (uint32_t)(rg + x) * E);
+            F.vr[c] = RW::load1_at(vb, tm * vrow_b + (uint32_t)(rg + x) * E);
+            F.xr[c] = *reinterpret_cast<const float *>(xb + tm * (uint32_t)(vrow * 4) + (uint32_t)(rg + x) * 4);
         }
         const float *rec = p.rec + ((size_t)(base + j) * p.hv + h) * kChunkRecBwd;
         const int l = m1 - 1;
@@ -202,12 +213,12 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
         }
     };
     // The chunk's start state on this wave's column tiles, as MFMA B operands over the
-    // rows: s0[rt][l2][c] = S0[16 rt + 4 g + c][16 (wave + NW l2) + x] (read a chunk
-    // ahead, once the current one is no longer needed).
+    // part's rows: s0[rt][l2][c] = S0[part DVP + 16 rt + 4 g + c][16 (wave + NW l2) + x]
+    // (read a chunk ahead, once the current one is no longer needed).
     f4 s0[RT][CTW];
     auto fetch_s0 = [&](int j_) {
         const int j = j_ < 0 ? 0 : j_;
-        const float *ck = p.ck + ((size_t)(base + j) * p.hv + h) * DV * DK;
+        const float *ck = p.ck + (((size_t)(base + j) * p.hv + h) * DV + part * DVP) * DK;
 #pragma unroll
         for (int l2 = 0; l2 < CTW; ++l2) {
             const int ct = wave + NW * l2 < NT ? wave + NW * l2 : NT - 1;
@@ -220,30 +231,48 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
 
     // The per-token results of a chunk (wave 0, lane m = token): dbeta, and dg as the
     // running sum from the sequence's end, carry + phi_15 + ... + phi_m in that order
-    // (phi = dO . o - dv . v; tokens past the chunk's end hold exact zeros).
+    // (phi = dO . o - dv . v; tokens past the chunk's end hold exact zeros); with
+    // P > 1, the part's share of each.
+    float *const out_beta = P == 1 ? p.grad_beta : p.dbeta_part + (size_t)part * p.total_tokens * p.hv;
+    float *const out_g = P == 1 ? p.grad_g : p.dg_part + (size_t)part * p.total_tokens * p.hv;
     auto per_token = [&](int j, int b) {
         if (wave != 0) return;
         const int m1 = chunk_m1(j);
         const int64_t t0 = tb + (int64_t)kCk * j;
         const int m = lane & 15;
+        float4 rw[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) rw[w] = *reinterpret_cast<const float4 *>(&red[b][w][m][0]);
         float sbv = 0.f, svv = 0.f, sq = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            sbv = sbv + red[b][w][m][0];
-            svv = svv + red[b][w][m][1];
-            sq = sq + red[b][w][m][2];
+            sbv = sbv + rw[w].x;
+            svv = svv + rw[w].y;
+            sq = sq + rw[w].z;
         }
         const float phi = sq - svv;
-        float dg = carry;
+        // every token's phi to every lane (through LDS: one store, four broadcast reads),
+        // then the running sum from token 15 down; lane m keeps it at token m
+        if (lane < kCk) phis[m] = phi;
+        float ph[kCk];
+#pragma unroll
+        for (int i = 0; i < kCk / 4; ++i) {
+            const float4 v4 = *reinterpret_cast<const float4 *>(&phis[4 * i]);
+            ph[4 * i] = v4.x;
+            ph[4 * i + 1] = v4.y;
+            ph[4 * i + 2] = v4.z;
+            ph[4 * i + 3] = v4.w;
+        }
+        float run = carry, dg = carry;
 #pragma unroll
         for (int s = kCk - 1; s >= 0; --s) {
-            const float ps = __shfl(phi, s, 64);
-            dg = s >= m ? dg + ps : dg;
+            run = run + ph[s];
+            dg = s == m ? run : dg;
         }
-        carry = __shfl(dg, 0, 64);
+        carry = run;
         if (lane < kCk && m < m1) {
-            p.grad_beta[(size_t)(t0 + m) * p.hv + h] = sbv + abrow[m];
-            p.grad_g[(size_t)(t0 + m) * p.hv + h] = dg;
+            out_beta[(size_t)(t0 + m) * p.hv + h] = sbv + abrow[m];
+            out_g[(size_t)(t0 + m) * p.hv + h] = dg;
         }
     };
 
@@ -329,13 +358,14 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
         // rows of dO, dR and U and D at the chunk's end for the products over rows
         // (dR and U pass through vector registers first: stores straight from the MFMA
         // accumulators were merged with wrong offsets by the compiler)
+        const auto dv_rsrc = buf_rsrc(p.grad_v + (size_t)t0 * vrow, (uint32_t)(m1 * vrow * 4));
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int m = 4 * g + c;
             float dr = dR[c], uu = U[c];
             asm volatile("" : "+v"(dr), "+v"(uu));
             const float dvv = bt[c] * dr;
-            if (m < m1) p.grad_v[(size_t)(t0 + m) * vrow + (size_t)h * DV + r0 + x] = dvv;
+            buf_store_f32(dv_rsrc, m < m1 ? (uint32_t)((m * vrow + (size_t)h * DV + rg + x) * 4) : kDropped, dvv);
             const float sb = lane_sum<16>(dr * xx[c]);
             const float sv = lane_sum<16>(dvv * vv[c]);
             if (x == 0) {
@@ -458,6 +488,11 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
                 hh[c] = Hs[x][4 * g + c] + Hs[4 * g + c][x];
             }
             float qd[4] = {0.f, 0.f, 0.f, 0.f};
+            // this chunk's rows of the part's dq and dk (stores every lane issues)
+            const uint32_t qrow = (uint32_t)(p.hv * DK);
+            const size_t qbase = ((size_t)part * p.total_tokens + t0) * p.hv * DK;
+            const auto dq_rsrc = buf_rsrc(p.dqh + qbase, (uint32_t)m1 * qrow * 4u);
+            const auto dk_rsrc = buf_rsrc(p.dkh + qbase, (uint32_t)m1 * qrow * 4u);
 #pragma unroll
             for (int l2 = 0; l2 < CTW; ++l2) {
                 const int ct = wave + NW * l2;
@@ -472,11 +507,9 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
                     for (int r = 0; r < 4; ++r) {
                         const int m = 4 * g + r;
                         qd[r] = __builtin_fmaf(Qc[m][16 * ct + x], dq[l2][r], qd[r]);
-                        if (m < m1) {
-                            const size_t o = ((size_t)(t0 + m) * p.hv + h) * DK + 16 * ct + x;
-                            p.dqh[o] = dq[l2][r];
-                            p.dkh[o] = dk[l2][r];
-                        }
+                        const uint32_t o = m < m1 ? ((uint32_t)m * qrow + (uint32_t)(h * DK + 16 * ct + x)) * 4u : kDropped;
+                        buf_store_f32(dq_rsrc, o, dq[l2][r]);
+                        buf_store_f32(dk_rsrc, o, dk[l2][r]);
                     }
                 }
             }
@@ -493,14 +526,15 @@ __global__ __launch_bounds__(64 * (DV / 16)) void gdn_bwd_chunk_rev_kernel(BwdCh
     }
 
     if (p.grad_h0) {
-        float *dst = p.grad_h0 + (((size_t)n * p.hv + h) * DV + r0 + x) * DK;
+        float *dst = p.grad_h0 + (((size_t)n * p.hv + h) * DV + rg + x) * DK;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             *reinterpret_cast<float4 *>(dst + 16 * t + 4 * g) = make_float4(Dt[t][0], Dt[t][1], Dt[t][2], Dt[t][3]);
     }
 }
 
-// dq and dk of each key head: the value heads that read it, added in head order.
+// dq and dk of each key head: the (value head, part) partials that read it, added
+// value head by value head and within a head part by part.
 __global__ __launch_bounds__(256) void gdn_bwd_chunk_gqa_kernel(BwdChunkParams p) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 4-column item
     const int64_t per_tok = (int64_t)p.hk * p.dk / 4;
@@ -510,23 +544,50 @@ __global__ __launch_bounds__(256) void gdn_bwd_chunk_gqa_kernel(BwdChunkParams p
     const int kh = rem / (p.dk / 4), c = 4 * (rem % (p.dk / 4));
     const int G = p.hv / p.hk;
     const size_t src = ((size_t)t * p.hv + (size_t)kh * G) * p.dk + c;
-    float4 sq = *reinterpret_cast<const float4 *>(p.dqh + src);
-    float4 sk = *reinterpret_cast<const float4 *>(p.dkh + src);
-    for (int gi = 1; gi < G; ++gi) {
-        const float4 a = *reinterpret_cast<const float4 *>(p.dqh + src + (size_t)gi * p.dk);
-        const float4 b = *reinterpret_cast<const float4 *>(p.dkh + src + (size_t)gi * p.dk);
-        sq = make_float4(sq.x + a.x, sq.y + a.y, sq.z + a.z, sq.w + a.w);
-        sk = make_float4(sk.x + b.x, sk.y + b.y, sk.z + b.z, sk.w + b.w);
+    const size_t pstride = (size_t)p.total_tokens * p.hv * p.dk;
+    float4 sq = make_float4(0.f, 0.f, 0.f, 0.f), sk = sq;
+    for (int gi = 0; gi < G; ++gi) {
+        for (int pt = 0; pt < p.parts; ++pt) {
+            const size_t o = src + (size_t)gi * p.dk + (size_t)pt * pstride;
+            const float4 a = *reinterpret_cast<const float4 *>(p.dqh + o);
+            const float4 b = *reinterpret_cast<const float4 *>(p.dkh + o);
+            if (gi == 0 && pt == 0) {
+                sq = a;
+                sk = b;
+            } else {
+                sq = make_float4(sq.x + a.x, sq.y + a.y, sq.z + a.z, sq.w + a.w);
+                sk = make_float4(sk.x + b.x, sk.y + b.y, sk.z + b.z, sk.w + b.w);
+            }
+        }
     }
     const size_t dst = ((size_t)t * p.hk + kh) * p.dk + c;
     *reinterpret_cast<float4 *>(p.grad_q + dst) = sq;
     *reinterpret_cast<float4 *>(p.grad_k + dst) = sk;
 }
 
+// dbeta and dg of each (token, value head): the parts' shares, added part by part.
+__global__ __launch_bounds__(256) void gdn_bwd_chunk_parts_kernel(BwdChunkParams p) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t n = p.total_tokens * p.hv;
+    if (i >= n) return;
+    float b = p.dbeta_part[i], g = p.dg_part[i];
+    for (int pt = 1; pt < p.parts; ++pt) {
+        b = b + p.dbeta_part[(size_t)pt * n + i];
+        g = g + p.dg_part[(size_t)pt * n + i];
+    }
+    p.grad_beta[i] = b;
+    p.grad_g[i] = g;
+}
+
 template <int DK, int DV, class IO>
 hipError_t rev_launch(const BwdChunkParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((gdn_bwd_chunk_rev_kernel<DK, DV, IO>), dim3((unsigned)((int64_t)p.n_seqs * p.hv)),
-                       dim3(64 * (DV / 16)), 0, s, p);
+    const unsigned grid = (unsigned)((int64_t)p.n_seqs * p.hv * p.parts);
+    if (p.parts == 1)
+        hipLaunchKernelGGL((gdn_bwd_chunk_rev_kernel<DK, DV, IO, 1>), dim3(grid), dim3(64 * (DV / 16)), 0, s, p);
+    else if constexpr (DV >= 64)
+        hipLaunchKernelGGL((gdn_bwd_chunk_rev_kernel<DK, DV, IO, 2>), dim3(grid), dim3(64 * (DV / 32)), 0, s, p);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -551,11 +612,21 @@ hipError_t rev_io(const BwdChunkParams &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd_chunked(const BwdChunkParams &p, int io_dtype, hipStream_t s) {
+    if (p.parts != 1 && p.parts != 2) return hipErrorInvalidValue;
     hipError_t e = io_dtype == GDN_BF16 ? rev_io<IoBf16>(p, s) : rev_io<IoF32>(p, s);
-    if (e != hipSuccess || p.hv == p.hk || p.total_tokens == 0) return e;
-    const int64_t items = p.total_tokens * p.hk * p.dk / 4;
-    hipLaunchKernelGGL(gdn_bwd_chunk_gqa_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, p);
-    return hipGetLastError();
+    if (e != hipSuccess || p.total_tokens == 0) return e;
+    if (p.hv > p.hk || p.parts > 1) {
+        const int64_t items = p.total_tokens * p.hk * p.dk / 4;
+        hipLaunchKernelGGL(gdn_bwd_chunk_gqa_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (p.parts > 1) {
+        const int64_t items = p.total_tokens * p.hv;
+        hipLaunchKernelGGL(gdn_bwd_chunk_parts_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, p);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 }  // namespace gdn

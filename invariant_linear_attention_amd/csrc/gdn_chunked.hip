@@ -468,16 +468,17 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
             vraw[c] = on ? RW::widen1(F.v[c]) : 0.f;
             vb[c] = bb[c] * vraw[c];
         }
+        const float4 trow = F.trow, brow = F.brow, gam = F.gam, dwv = F.dw;
+        const float g15 = F.g15;
+        if constexpr (!LEAN) fetch(F, j + 1);
         if constexpr (BW) {
-            // the state at this chunk's start
+            // the state at this chunk's start (stored after the next chunk's reads, so
+            // that waiting for those does not wait for these)
             float *dst = p.ck + (((size_t)(sc.base + j) * p.hv + h) * p.dv + row0 + x) * DK;
 #pragma unroll
             for (int t = 0; t < OT; ++t)
                 *reinterpret_cast<float4 *>(dst + 16 * (t_first + t) + 4 * g) = make_float4(S[t][0], S[t][1], S[t][2], S[t][3]);
         }
-        const float4 trow = F.trow, brow = F.brow, gam = F.gam, dwv = F.dw;
-        const float g15 = F.g15;
-        if constexpr (!LEAN) fetch(F, j + 1);
         lds_barrier();
 
         // partial products of this wave's quarters
@@ -554,6 +555,12 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
         // for the chunk's earlier tokens, 0 for tokens not reached yet
         const float gm[4] = {gam.x, gam.y, gam.z, gam.w};
         f4 R, OC;
+        // this chunk's rows of x (backward walk) or of the outputs, as buffer stores
+        // that every lane issues (kDropped where there is nothing to write)
+        const uint32_t col_b = (uint32_t)(h * p.dv + row0 + x);
+        const auto orsrc = BW ? buf_rsrc(p.xv + (size_t)t0 * vrow, (uint32_t)(m1 * vrow * 4))
+                              : buf_rsrc(static_cast<const char *>(p.out) + (size_t)t0 * vrow * IO::ESZ,
+                                         (uint32_t)(m1 * vrow * IO::ESZ));
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int m = 4 * g + c;
@@ -562,7 +569,7 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
                 // x = v - Gam P (kept for the reverse walk), R = beta x
                 const float xr = on ? __builtin_fmaf(-gm[c], P[c], vraw[c]) : 0.f;
                 R[c] = bb[c] * xr;
-                if (wave == 0 && on) p.xv[(size_t)(t0 + m) * vrow + (size_t)h * p.dv + row0 + x] = xr;
+                buf_store_f32(orsrc, wave == 0 && on ? ((uint32_t)m * (uint32_t)vrow + col_b) * 4u : kDropped, xr);
             } else {
                 const float fresh = __builtin_fmaf(-(bb[c] * gm[c]), P[c], vb[c]);
                 R[c] = on ? fresh : (m < m0 ? Rkeep[c] : 0.f);
@@ -585,12 +592,11 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
         O = mfma_16x16x4(brow.y, U[1], O);
         O = mfma_16x16x4(brow.z, U[2], O);
         O = mfma_16x16x4(brow.w, U[3], O);
-        if (wave == 0) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int m = 4 * g + c;
-                if (m >= m0 && m < m1) IO::store1(p.out, (size_t)(t0 + m) * vrow + (size_t)h * p.dv + row0 + x, O[c] + 0.f);
-            }
+        for (int c = 0; c < 4; ++c) {
+            const int m = 4 * g + c;
+            const bool st = wave == 0 && m >= m0 && m < m1;
+            buf_store1<IO>(orsrc, st ? ((uint32_t)m * (uint32_t)vrow + col_b) * (uint32_t)IO::ESZ : kDropped, O[c] + 0.f);
         }
         }
 

@@ -138,12 +138,15 @@ struct BwdChunkParams {
     const int32_t *cu_seqlens;
     const float *rec, *ck, *xv, *hdot;  // from the prep kernel and the forward walk
     float *grad_v, *grad_g, *grad_beta, *grad_h0;
-    float *dqh, *dkh;                 // [T][hv][dk]: dq, dk of each value head (the outputs when hv == hk)
+    float *dqh, *dkh;                 // [parts][T][hv][dk]: dq, dk of each value head and part
+                                      // (the outputs when hv == hk and parts == 1)
+    float *dbeta_part, *dg_part;      // [parts][T][hv] (parts > 1)
     float *grad_q, *grad_k;           // [T][hk][dk]
     int64_t ws_slots, total_tokens;
     int32_t n_seqs, hk, hv, dk, dv;
     int32_t rank_by_length;
     int32_t hdot_parts;               // partial sums of <dhT, hT> per (sequence, value head)
+    int32_t parts;                    // workgroups per (sequence, value head), each a share of the rows
 };
 hipError_t launch_bwd_chunked(const BwdChunkParams &p, int io_dtype, hipStream_t s);
 

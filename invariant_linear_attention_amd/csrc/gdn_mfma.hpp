@@ -67,6 +67,32 @@ struct Raw4 {
     __device__ static float widen1(uint32_t w) { return IO::ESZ == 2 ? bf16_to_f32(w & 0xffffu) : __uint_as_float(w); }
 };
 
+// Stores that every lane issues, whether or not it has something to write.  A wave
+// counts its outstanding vector memory operations in one in-order counter; a store
+// under a branch leaves the count unknown where the paths join, so the next wait for
+// earlier loads must wait for the store's acknowledgement too.  A raw buffer store
+// past the resource's range is discarded, so a lane with nothing to write passes
+// kDropped instead of branching round the store, and the count stays exact.
+constexpr uint32_t kDropped = 0x80000000u;
+
+// A raw buffer resource over [base, base + bytes); bytes must be below kDropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One io element (bf16 rounded to nearest even, as IO::store1) at byte offset off.
+template <class IO>
+__device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, uint32_t off, float f) {
+    if constexpr (IO::ESZ == 2)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)), r, off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float f) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, off, 0, 0);
+}
+
 // Sum over the 16 lanes x of each lane group g (lanes 16 g .. 16 g + 15), in the
 // fixed butterfly order 8, 4, 2, 1; every lane of the group gets the sum.
 __device__ __forceinline__ float sum16(float v) {

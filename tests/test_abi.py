@@ -466,15 +466,22 @@ def call_cbwd(lib, dims, ws_bytes=None, **over):
 def test_bwd_chunked_workspace_size(lib):
     """Records (1,088 floats per slot and value head), the chunk-start states (a dv x dk
     state per slot and value head), x = v - Gam P (T hv dv), the <dhT, hT> partials
-    (N hv dv/16 x 4) and, when value heads share key heads, dq and dk per value head
-    (T hv dk each); slots = T // 16 + 2 N + 2; every part rounded up to 256 bytes."""
+    (N hv dv/16 x 4), then with P row parts (plan_rows; 0 = 2 for dv = 128, else 1):
+    when value heads share key heads or P > 1, dq and dk per value head and part
+    (P T hv dk each), and when P > 1 dbeta and dg per part (P T hv each); slots =
+    T // 16 + 2 N + 2; every part rounded up to 256 bytes."""
     up = lambda x: (x + 255) // 256 * 256
-    for T, N, hk, hv, dk, dv in ((10, 2, 2, 4, 128, 64), (100, 3, 2, 2, 64, 128), (33, 1, 1, 1, 128, 32)):
+    for T, N, hk, hv, dk, dv, rows in ((10, 2, 2, 4, 128, 64, 0), (100, 3, 2, 2, 64, 128, 0),
+                                       (33, 1, 1, 1, 128, 32, 0), (100, 3, 2, 2, 64, 128, 1),
+                                       (10, 2, 2, 4, 128, 64, 2), (21, 1, 1, 1, 64, 64, 2)):
         slots = T // 16 + 2 * N + 2
         ck = dv * dk
+        P = rows or (2 if dv == 128 else 1)
         want = (up(slots * hv * 1088 * 4) + up(slots * hv * ck * 4) + up(T * hv * dv * 4)
-                + up(N * hv * (dv // 16) * 16) + (2 * up(T * hv * dk * 4) if hv > hk else 0))
-        assert cbwd_ws(lib, _dims(total_tokens=T, n_seqs=N, hk=hk, hv=hv, dk=dk, dv=dv)) == want
+                + up(N * hv * (dv // 16) * 16) + (2 * up(P * T * hv * dk * 4) if hv > hk or P > 1 else 0)
+                + (2 * up(P * T * hv * 4) if P > 1 else 0))
+        d = _dims(total_tokens=T, n_seqs=N, hk=hk, hv=hv, dk=dk, dv=dv, plan_rows=rows)
+        assert cbwd_ws(lib, d) == want, (T, N, hk, hv, dk, dv, rows)
     n = ctypes.c_uint64(0)
     assert lib.gdn_bwd_chunked_workspace_size(None, ctypes.byref(n)) == 1
     assert lib.gdn_bwd_chunked_workspace_size(ctypes.byref(_dims()), None) == 1
@@ -484,7 +491,8 @@ def test_bwd_chunked_workspace_size(lib):
 
 @pytest.mark.parametrize("case,over,code", [
     (dict(dk=32), {}, 6), (dict(dk=16), {}, 6), (dict(dv=16), {}, 6), (dict(dv=96), {}, 6),
-    (dict(plan_lanes=8), {}, 6), (dict(plan_rows=1), {}, 6), (dict(plan_waves=3), {}, 6),
+    (dict(plan_lanes=8), {}, 6), (dict(plan_rows=3), {}, 6), (dict(plan_rows=2, dv=32), {}, 6),
+    (dict(plan_waves=3), {}, 6),
     (dict(hk=1, hv=32), {}, 6), (dict(hv=3), {}, 2), (dict(io_dtype=7), {}, 3),
     (dict(n_seqs=0, total_tokens=3), {}, 2),
     ({}, dict(cu=None), 1), ({}, dict(ws=None), 1), ({}, dict(q=None), 1), ({}, dict(dout=None), 1),

@@ -47,6 +47,19 @@ def test_parity_small(gpu, hk, hv, dk, dv, io, with_h0, with_dhT):
                 % (hk, hv, dk, dv, io, with_h0, with_dhT), dout)
 
 
+@pytest.mark.parametrize("hk,hv,dk,dv", [(2, 4, 128, 128), (2, 2, 64, 64), (1, 1, 128, 128), (1, 2, 64, 128)])
+@pytest.mark.parametrize("parts", [1, 2])
+def test_parity_row_parts(gpu, hk, hv, dk, dv, parts):
+    """The reverse walk with the state rows in one workgroup or split over two (each
+    part's sums over its rows added afterwards), against the oracle."""
+    from oracle import oracle
+    w = synth.make_workload(570 + dk + dv + hv, [45, 0, 130, 16, 3], hk=hk, hv=hv, dk=dk, dv=dv, h0_std=0.1)
+    dout, dhT = grad_inputs(w, 22)
+    r = run_cbwd(gpu, w, dout, dhT, parts=parts)
+    ref = oracle.gdn_backward(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, dout, h0=w.h0, dhT=dhT)
+    check_grads(w, r, ref, "chunked bwd parts=%d hk=%d hv=%d dk=%d dv=%d" % (parts, hk, hv, dk, dv), dout)
+
+
 def test_parity_benchmark_batch(gpu):
     """The benchmark batch (8 sequences, 17,459 tokens, 16/32 heads, dk = dv = 128),
     every gradient of every head against the oracle."""
@@ -58,25 +71,30 @@ def test_parity_benchmark_batch(gpu):
     check_grads(w, r, ref, "chunked bwd benchmark batch", dout)
 
 
-def test_deterministic_batch_invariant_any_walk_shape(gpu):
+@pytest.mark.parametrize("parts", [0, 1, 2])
+def test_deterministic_batch_invariant_any_walk_shape(gpu, parts):
     """Repeat, alone vs in a batch, and the forward walk at 1, 2 and 4 waves per
-    state tile: all bitwise equal."""
+    state tile: all bitwise equal for each split of the reverse walk's rows."""
     w = synth.make_workload(521, [70, 5, 33, 0, 130], hk=2, hv=4, dk=128, dv=128, h0_std=0.1)
     dout, dhT = grad_inputs(w, 13)
-    r1 = run_cbwd(gpu, w, dout, dhT)
+    r1 = run_cbwd(gpu, w, dout, dhT, parts=parts)
     for waves in (0, 1, 2, 4):
-        r2 = run_cbwd(gpu, w, dout, dhT, waves=waves)
+        r2 = run_cbwd(gpu, w, dout, dhT, waves=waves, parts=parts)
         for key in r1:
             assert torch.equal(r1[key], r2[key]), (waves, key)
     cu = w.cu_seqlens.tolist()
     for n in (0, 2, 4):
         s = synth.select(w, [n])
         a, b = cu[n], cu[n + 1]
-        rs = run_cbwd(gpu, s, dout[a:b].contiguous(), dhT[n:n + 1].contiguous())
+        rs = run_cbwd(gpu, s, dout[a:b].contiguous(), dhT[n:n + 1].contiguous(), parts=parts)
         for key in ("dq", "dk", "dv", "dg", "dbeta"):
             assert torch.equal(rs[key], r1[key][a:b]), (n, key)
         assert torch.equal(rs["dh0"][0], r1["dh0"][n]), n
-    say("chunked backward: repeat, walk shapes and alone-vs-batch bitwise equal")
+    if parts == 0:  # the automatic split for dv = 128 is two parts
+        r2 = run_cbwd(gpu, w, dout, dhT, parts=2)
+        for key in r1:
+            assert torch.equal(r1[key], r2[key]), ("auto", key)
+    say("chunked backward parts=%d: repeat, walk shapes and alone-vs-batch bitwise equal" % parts)
 
 
 def test_empty_and_single_token_sequences(gpu):
