@@ -100,7 +100,8 @@ __global__ __launch_bounds__(64 * (DV / 16 / P)) void gdn_bwd_chunk_rev_kernel(B
     __shared__ __align__(16) float red[2][NW][kCk][4];    // per parity, wave and token: dR.x, dv.v, q.dq
     __shared__ __align__(16) float phis[kCk];             // wave 0: the chunk's phi of every token
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // (the wave index as a uniform value, so that tests on it are scalar branches)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int x = lane & 15, g = lane >> 4;
     // Workgroups that read the same keys and queries (one sequence and key head) get
     // ids equal modulo 8, so they run on one XCD and share its L2.
@@ -328,15 +329,18 @@ __global__ __launch_bounds__(64 * (DV / 16 / P)) void gdn_bwd_chunk_rev_kernel(B
         fetch(F, j - 1);
         lds_barrier();
 
-        // ---- P1.  E = K D^T on this wave's rows (token 4 g + c, row r0 + x)
+        // ---- P1.  E = K D^T on this wave's rows (token 4 g + c, row r0 + x); the key
+        // tiles are all read before the products
         f4 Ev = f4_zero();
+        float4 kav[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) kav[t] = *reinterpret_cast<const float4 *>(&Kc[x][16 * t + 4 * g]);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float4 ka = *reinterpret_cast<const float4 *>(&Kc[x][16 * t + 4 * g]);
-            Ev = mfma_16x16x4(ka.x, Dt[t][0], Ev);
-            Ev = mfma_16x16x4(ka.y, Dt[t][1], Ev);
-            Ev = mfma_16x16x4(ka.z, Dt[t][2], Ev);
-            Ev = mfma_16x16x4(ka.w, Dt[t][3], Ev);
+            Ev = mfma_16x16x4(kav[t].x, Dt[t][0], Ev);
+            Ev = mfma_16x16x4(kav[t].y, Dt[t][1], Ev);
+            Ev = mfma_16x16x4(kav[t].z, Dt[t][2], Ev);
+            Ev = mfma_16x16x4(kav[t].w, Dt[t][3], Ev);
         }
         // dU = Gam_{l,.} E + B^T dO;  dR = T^T dU;  U = T (beta x)
         f4 dU = f4{wl[0] * Ev[0], wl[1] * Ev[1], wl[2] * Ev[2], wl[3] * Ev[3]};
@@ -388,13 +392,29 @@ __global__ __launch_bounds__(64 * (DV / 16 / P)) void gdn_bwd_chunk_rev_kernel(B
                 bq[c] = gm[c] * dO[c];
                 bk[c] = -(bt[c] * gm[c]) * dR[c];
             }
+            // (the next tile's query and key columns are read while this tile's
+            // products run)
+            float qa[2][4], ka[2][4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                qa[0][c] = Qc[4 * g + c][x];
+                ka[0][c] = Kc[4 * g + c][x];
+            }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
+                if (t + 1 < NT) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        qa[(t + 1) & 1][c] = Qc[4 * g + c][16 * (t + 1) + x];
+                        ka[(t + 1) & 1][c] = Kc[4 * g + c][16 * (t + 1) + x];
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 f4 C = f4{gl * Dt[t][0], gl * Dt[t][1], gl * Dt[t][2], gl * Dt[t][3]};
 #pragma unroll
-                for (int c = 0; c < 4; ++c) C = mfma_16x16x4(Qc[4 * g + c][16 * t + x], bq[c], C);
+                for (int c = 0; c < 4; ++c) C = mfma_16x16x4(qa[t & 1][c], bq[c], C);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) C = mfma_16x16x4(Kc[4 * g + c][16 * t + x], bk[c], C);
+                for (int c = 0; c < 4; ++c) C = mfma_16x16x4(ka[t & 1][c], bk[c], C);
                 Dt[t] = C;
             }
         }
@@ -428,24 +448,46 @@ __global__ __launch_bounds__(64 * (DV / 16 / P)) void gdn_bwd_chunk_rev_kernel(B
         f4 dq[CTW], dk[CTW];
         {
             const float fr = -(bx * gx), fu = wx;  // factors of A-operand row x (token x)
+            // every operand read from LDS before the products, so that no product waits
+            // on a read: the token rows of dO, dR and U over the part's rows (A operands)
+            // and the D columns of this wave's tiles (B operands of the D term)
+            float ao[RT][4], ar[RT][4], au[RT][4], dd[CTW][RT][4];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const float4 o4 = *reinterpret_cast<const float4 *>(&dOs[x][16 * rt + 4 * g]);
+                const float4 r4 = *reinterpret_cast<const float4 *>(&dRs[x][16 * rt + 4 * g]);
+                const float4 u4 = *reinterpret_cast<const float4 *>(&Us[x][16 * rt + 4 * g]);
+                ao[rt][0] = o4.x; ao[rt][1] = o4.y; ao[rt][2] = o4.z; ao[rt][3] = o4.w;
+                ar[rt][0] = r4.x; ar[rt][1] = r4.y; ar[rt][2] = r4.z; ar[rt][3] = r4.w;
+                au[rt][0] = u4.x; au[rt][1] = u4.y; au[rt][2] = u4.z; au[rt][3] = u4.w;
+            }
+#pragma unroll
+            for (int l2 = 0; l2 < CTW; ++l2) {
+                const int ct = wave + NW * l2 < NT ? wave + NW * l2 : NT - 1;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dd[l2][rt][c] = Ds[16 * rt + 4 * g + c][16 * ct + x];
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    ar[rt][c] = fr * ar[rt][c];
+                    au[rt][c] = fu * au[rt][c];
+                }
 #pragma unroll
             for (int l2 = 0; l2 < CTW; ++l2) {
                 const int ct = wave + NW * l2;
                 f4 aq = f4_zero(), ak = f4_zero();
-                if (ct < NT) {
+                if (NT % NW == 0 || ct < NT) {
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) {
-                        const float4 o4 = *reinterpret_cast<const float4 *>(&dOs[x][16 * rt + 4 * g]);
-                        const float4 r4 = *reinterpret_cast<const float4 *>(&dRs[x][16 * rt + 4 * g]);
-                        const float4 u4 = *reinterpret_cast<const float4 *>(&Us[x][16 * rt + 4 * g]);
-                        const float o[4] = {o4.x, o4.y, o4.z, o4.w};
-                        const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
-                        const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
-                            aq = mfma_16x16x4(o[c], s0[rt][l2][c], aq);
-                            ak = mfma_16x16x4(fr * rr[c], s0[rt][l2][c], ak);
-                            ak = mfma_16x16x4(fu * uu[c], Ds[16 * rt + 4 * g + c][16 * ct + x], ak);
+                            aq = mfma_16x16x4(ao[rt][c], s0[rt][l2][c], aq);
+                            ak = mfma_16x16x4(ar[rt][c], s0[rt][l2][c], ak);
+                            ak = mfma_16x16x4(au[rt][c], dd[l2][rt][c], ak);
                         }
                     }
                 }
@@ -480,12 +522,33 @@ __global__ __launch_bounds__(64 * (DV / 16 / P)) void gdn_bwd_chunk_rev_kernel(B
 
         // ---- P4.  in-chunk terms: dq += Ms K;  dk += Ms^T Q + (H + H^T) K; q . dq
         {
-            float mr[4], mc[4], hh[4];
+            float mr[4], mc[4], hh[4], kcol[CTW][4], qcol[CTW][4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 mr[c] = Ms[x][4 * g + c];
                 mc[c] = Ms[4 * g + c][x];
                 hh[c] = Hs[x][4 * g + c] + Hs[4 * g + c][x];
+            }
+            // the key and query columns of this wave's tiles, read before the products
+#pragma unroll
+            for (int l2 = 0; l2 < CTW; ++l2) {
+                const int ct = wave + NW * l2 < NT ? wave + NW * l2 : NT - 1;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    kcol[l2][c] = Kc[4 * g + c][16 * ct + x];
+                    qcol[l2][c] = Qc[4 * g + c][16 * ct + x];
+                }
+            }
+#pragma unroll
+            for (int l2 = 0; l2 < CTW; ++l2) {
+                if (NT % NW == 0 || wave + NW * l2 < NT) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dq[l2] = mfma_16x16x4(mr[c], kcol[l2][c], dq[l2]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(mc[c], qcol[l2][c], dk[l2]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(hh[c], kcol[l2][c], dk[l2]);
+                }
             }
             float qd[4] = {0.f, 0.f, 0.f, 0.f};
             // this chunk's rows of the part's dq and dk (stores every lane issues)
@@ -496,17 +559,11 @@ __global__ __launch_bounds__(64 * (DV / 16 / P)) void gdn_bwd_chunk_rev_kernel(B
 #pragma unroll
             for (int l2 = 0; l2 < CTW; ++l2) {
                 const int ct = wave + NW * l2;
-                if (ct < NT) {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) dq[l2] = mfma_16x16x4(mr[c], Kc[4 * g + c][16 * ct + x], dq[l2]);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(mc[c], Qc[4 * g + c][16 * ct + x], dk[l2]);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(hh[c], Kc[4 * g + c][16 * ct + x], dk[l2]);
+                if (NT % NW == 0 || ct < NT) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int m = 4 * g + r;
-                        qd[r] = __builtin_fmaf(Qc[m][16 * ct + x], dq[l2][r], qd[r]);
+                        qd[r] = __builtin_fmaf(qcol[l2][r], dq[l2][r], qd[r]);
                         const uint32_t o = m < m1 ? ((uint32_t)m * qrow + (uint32_t)(h * DK + 16 * ct + x)) * 4u : kDropped;
                         buf_store_f32(dq_rsrc, o, dq[l2][r]);
                         buf_store_f32(dk_rsrc, o, dk[l2][r]);
