@@ -294,7 +294,8 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
     __shared__ __align__(16) float Qs[LEAN ? kCk : 1][KP];  // (lean) the chunk's queries
     __shared__ float4 Xch[W > 1 ? 8 : 1][64];           // P and Z partials of the four quarters
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // (the wave index as a uniform value, so that tests on it are scalar branches)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int x = lane & 15, g = lane >> 4;
     const int tiles = p.dv / 16;
     // Workgroups are handed to the eight XCDs round robin by id.  The ones that read
@@ -524,14 +525,19 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
             for (int q = 0; q < OQ; ++q) {
                 const int gq = wave * OQ + q;
                 Xch[gq][lane] = make_float4(Pq[q][0], Pq[q][1], Pq[q][2], Pq[q][3]);
-                Xch[4 + gq][lane] = make_float4(Zq[q][0], Zq[q][1], Zq[q][2], Zq[q][3]);
+                if constexpr (!BW) Xch[4 + gq][lane] = make_float4(Zq[q][0], Zq[q][1], Zq[q][2], Zq[q][3]);
             }
             lds_barrier();
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float4 a4 = Xch[q][lane], b4 = Xch[4 + q][lane];
+                const float4 a4 = Xch[q][lane];
                 P4[q] = f4{a4.x, a4.y, a4.z, a4.w};
-                Z4[q] = f4{b4.x, b4.y, b4.z, b4.w};
+                if constexpr (!BW) {
+                    const float4 b4 = Xch[4 + q][lane];
+                    Z4[q] = f4{b4.x, b4.y, b4.z, b4.w};
+                } else {
+                    Z4[q] = f4_zero();
+                }
             }
         }
         f4 P, Z;
