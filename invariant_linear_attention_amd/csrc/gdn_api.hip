@@ -674,7 +674,7 @@ gdn_status bwd_chunked_check_dims(const gdn_dims *dims) {
     gdn_status st = check_common(dims);
     if (st != GDN_OK) return st;
     const gdn_dims &d = *dims;
-    if (d.pre || d.plan_lanes) return GDN_ERR_UNSUPPORTED;
+    if (d.pre || (d.plan_lanes != 0 && d.plan_lanes != 1)) return GDN_ERR_UNSUPPORTED;
     if (d.plan_waves != 0 && d.plan_waves != 1 && d.plan_waves != 2 && d.plan_waves != 4) return GDN_ERR_UNSUPPORTED;
     if ((d.dk != 64 && d.dk != 128) || (d.dv != 32 && d.dv != 64 && d.dv != 128) || d.hv / d.hk > 16)
         return GDN_ERR_UNSUPPORTED;
@@ -776,6 +776,7 @@ gdn_status gdn_bwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     p.dbeta_part = reinterpret_cast<float *>(w + ws.dbeta);
     p.dg_part = reinterpret_cast<float *>(w + ws.dg);
     p.parts = parts;
+    p.plain = d.plan_lanes;  // 1: no wave specialization in the reverse walk (same bits)
     p.ws_slots = slots; p.total_tokens = T;
     p.n_seqs = (int32_t)N; p.hk = d.hk; p.hv = d.hv; p.dk = d.dk; p.dv = d.dv;
     p.rank_by_length = rank;

@@ -590,6 +590,550 @@ __global__ __launch_bounds__(64 * (DV / 16 / P)) void gdn_bwd_chunk_rev_kernel(B
     }
 }
 
+// The reverse walk for dv = 128 in two parts of 64 rows, with specialized waves.
+// Only E, dU, dR and the move of D to the chunk's start lie on the recurrence; the
+// products over rows (dB, dA, dq0, dk1), the in-chunk terms and the per-token sums
+// of a chunk need its D and token rows but feed nothing back.  So four state waves
+// (16 rows of D each) run chunk c while four gradient waves (dk/64 column tiles each)
+// run the rest of chunk c + 1, and each SIMD holds one wave of each kind, whose
+// instruction streams overlap.  A step has two barriers: after the keys and queries
+// of the state waves' chunk are staged, and after both kinds of work.  What one kind
+// writes for the other is double-buffered by chunk parity (the per-token sums, read
+// two steps later, by chunk index mod 3).  The arithmetic and every order of
+// summation are those of gdn_bwd_chunk_rev_kernel with P = 2, so the results are the
+// same bits.
+template <int DK, class IO>
+__global__ __launch_bounds__(512) void gdn_bwd_chunk_ws_kernel(BwdChunkParams p) {
+    using RW = Raw4<IO>;
+    constexpr int DV = 128, P = 2, DVP = DV / P, NWD = DVP / 16;  // state waves: 16 rows each
+    constexpr int NT = DK / 16, CTW = NT / NWD, RT = NWD;          // column tiles per gradient wave
+    constexpr int KP = DK + 4, VP = DVP + 4;
+    constexpr int KITEMS = kCk * DK / 4, KIT = (KITEMS + 511) / 512;  // key (query) items per thread
+    static_assert(NT % NWD == 0, "column tiles");
+    __shared__ __align__(16) float Ks[2][kCk][KP];
+    __shared__ __align__(16) float Qs[2][kCk][KP];
+    __shared__ __align__(16) float dOs[2][kCk][VP];  // token rows of dO, dR and U
+    __shared__ __align__(16) float dRs[2][kCk][VP];
+    __shared__ __align__(16) float Us[2][kCk][VP];
+    __shared__ __align__(16) float Ds[2][DVP][KP];   // D at the chunk's end
+    // the state waves' partial dB and dA, entry-major with the four waves' values
+    // side by side (one 16-byte read gives an entry's four partials; rows padded by
+    // one entry so that reads down a column spread over the banks)
+    __shared__ __align__(16) float dBw[2][kCk][kCk + 1][NWD], dAw[2][kCk][kCk + 1][NWD];
+    __shared__ float abrow[3][kCk];
+    __shared__ __align__(16) float red[3][NWD][kCk][4];  // by chunk mod 3: dR.x, dv.v (state), q.dq (gradient)
+    __shared__ __align__(16) float phis[kCk];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int x = lane & 15, g = lane >> 4;
+    int rank, h, part;
+    {
+        const int G = p.hv / p.hk * P;  // (value head, part) pairs of a key head
+        const int ngroups = p.n_seqs * p.hk;
+        const int full = (ngroups / 8) * 8 * G;
+        const int id = blockIdx.x;
+        int grp, member;
+        if (id < full) {
+            const int xcd = id % 8, slot = id / 8;
+            grp = (slot / G) * 8 + xcd;
+            member = slot % G;
+        } else {
+            grp = full / G + (id - full) / G;
+            member = (id - full) % G;
+        }
+        rank = grp / p.hk;
+        h = (grp % p.hk) * (G / P) + member / P;
+        part = member % P;
+    }
+    const int n = p.rank_by_length ? seq_by_length_rank(p.cu_seqlens, p.n_seqs, rank, tid, 512) : rank;
+    const int kh = h / (p.hv / p.hk);
+    int64_t tb = p.cu_seqlens[n], te = p.cu_seqlens[n + 1];
+    tb = tb < 0 ? 0 : (tb > p.total_tokens ? p.total_tokens : tb);
+    te = te < tb ? tb : (te > p.total_tokens ? p.total_tokens : te);
+    const int64_t len = te - tb;
+    const int64_t base = chunk_slot_base(tb, n);
+    int nch = (int)((len + kCk - 1) / kCk);
+    if (base + nch > p.ws_slots) nch = (int)(p.ws_slots - base > 0 ? p.ws_slots - base : 0);
+    const size_t vrow = (size_t)p.hv * DV;
+    constexpr uint32_t E = IO::ESZ;
+    const uint32_t krow_b = (uint32_t)p.hk * DK * E, vrow_b = (uint32_t)vrow * E;
+    auto chunk_m1 = [&](int j) {
+        const int64_t left = len - (int64_t)kCk * j;
+        return left < kCk ? (int)left : kCk;
+    };
+    auto rec_of = [&](int j) { return p.rec + ((size_t)(base + j) * p.hv + h) * kChunkRecBwd; };
+
+    // keys and queries: every thread stages KIT items of a chunk (read a step ahead)
+    typename RW::T kr[KIT], qr[KIT];
+    auto fetch_kq = [&](int j_) {
+        const int j = j_ < 0 ? 0 : j_;
+        const int m1 = chunk_m1(j);
+        const int64_t t0 = tb + (int64_t)kCk * j;
+        const char *kb = static_cast<const char *>(p.k) + ((size_t)t0 * p.hk + kh) * DK * E;
+        const char *qb = static_cast<const char *>(p.q) + ((size_t)t0 * p.hk + kh) * DK * E;
+#pragma unroll
+        for (int s = 0; s < KIT; ++s) {
+            int it = tid + 512 * s;
+            it = it < KITEMS ? it : KITEMS - 1;
+            const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+            const uint32_t off = (uint32_t)(m < m1 ? m : m1 - 1) * krow_b + (uint32_t)c * E;
+            kr[s] = RW::load_at(kb, off);
+            qr[s] = RW::load_at(qb, off);
+        }
+    };
+    auto stage_kq = [&](int j) {
+        const int m1 = chunk_m1(j);
+#pragma unroll
+        for (int s = 0; s < KIT; ++s) {
+            const int it = tid + 512 * s;
+            if (it < KITEMS) {
+                const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+                const bool on = m < m1;
+                *reinterpret_cast<float4 *>(&Ks[j & 1][m][c]) = RW::widen(RW::keep(kr[s], on));
+                *reinterpret_cast<float4 *>(&Qs[j & 1][m][c]) = RW::widen(RW::keep(qr[s], on));
+            }
+        }
+    };
+    if (nch > 0) fetch_kq(nch - 1);
+
+    if (wave < NWD) {
+        // ================================================================ state waves
+        const int r0 = 16 * wave, rg = part * DVP + r0;
+        f4 Dt[NT];  // D[rg + x][16 t + 4 g + c]
+        {
+            const float *src = p.dhT ? p.dhT + (((size_t)n * p.hv + h) * DV + rg + x) * DK : nullptr;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                Dt[t] = f4_zero();
+                if (src) {
+                    const float4 v4 = *reinterpret_cast<const float4 *>(src + 16 * t + 4 * g);
+                    Dt[t] = f4{v4.x, v4.y, v4.z, v4.w};
+                }
+            }
+        }
+        struct {
+            uint32_t dor[4], vr[4];
+            float xr[4];
+            float4 bet, gam, wl, trow;
+            float gl, tcol[4], bcol[4];
+        } F;
+        auto fetch = [&](int j_) {
+            const int j = j_ < 0 ? 0 : j_;
+            const int m1 = chunk_m1(j);
+            const int64_t t0 = tb + (int64_t)kCk * j;
+            const char *ob = static_cast<const char *>(p.dout) + ((size_t)t0 * p.hv + h) * DV * E;
+            const char *vb = static_cast<const char *>(p.v) + ((size_t)t0 * p.hv + h) * DV * E;
+            const char *xb = reinterpret_cast<const char *>(p.xv + ((size_t)t0 * p.hv + h) * DV);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t tm = (uint32_t)(4 * g + c < m1 ? 4 * g + c : m1 - 1);
+                F.dor[c] = RW::load1_at(ob, tm * vrow_b + (uint32_t)(rg + x) * E);
+                F.vr[c] = RW::load1_at(vb, tm * vrow_b + (uint32_t)(rg + x) * E);
+                F.xr[c] = *reinterpret_cast<const float *>(xb + tm * (uint32_t)(vrow * 4) + (uint32_t)(rg + x) * 4);
+            }
+            const float *rec = rec_of(j);
+            const int l = m1 - 1;
+            F.bet = *reinterpret_cast<const float4 *>(rec + kRecBeta + 4 * g);
+            F.gam = *reinterpret_cast<const float4 *>(rec + kRecGam + 4 * g);
+            F.wl = *reinterpret_cast<const float4 *>(rec + kRecGm + l * kCk + 4 * g);
+            F.gl = rec[kRecGam + l];
+            F.trow = *reinterpret_cast<const float4 *>(rec + kRecT + x * kCk + 4 * g);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                F.tcol[c] = rec[kRecT + (4 * g + c) * kCk + x];
+                F.bcol[c] = rec[kRecB + (4 * g + c) * kCk + x];
+            }
+        };
+        float carry = 0.f;  // (wave 0) the part's dg running sum, from <dhT, hT> over its rows
+        if (p.dhT && wave == 0)
+            for (int i = part * (DVP / 16) * 4; i < (part + 1) * (DVP / 16) * 4; ++i)
+                carry = carry + p.hdot[((size_t)n * p.hv + h) * p.hdot_parts + i];
+        float *const out_beta = p.dbeta_part + (size_t)part * p.total_tokens * p.hv;
+        float *const out_g = p.dg_part + (size_t)part * p.total_tokens * p.hv;
+        // (wave 0) the per-token results of chunk j: dbeta and dg as the running sum
+        // from the sequence's end, as in gdn_bwd_chunk_rev_kernel
+        auto per_token = [&](int j) {
+            const int m1 = chunk_m1(j);
+            const int64_t t0 = tb + (int64_t)kCk * j;
+            const int m = lane & 15;
+            float4 rw[NWD];
+#pragma unroll
+            for (int w = 0; w < NWD; ++w) rw[w] = *reinterpret_cast<const float4 *>(&red[j % 3][w][m][0]);
+            float sbv = 0.f, svv = 0.f, sq = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWD; ++w) {
+                sbv = sbv + rw[w].x;
+                svv = svv + rw[w].y;
+                sq = sq + rw[w].z;
+            }
+            const float phi = sq - svv;
+            if (lane < kCk) phis[m] = phi;
+            float ph[kCk];
+#pragma unroll
+            for (int i = 0; i < kCk / 4; ++i) {
+                const float4 v4 = *reinterpret_cast<const float4 *>(&phis[4 * i]);
+                ph[4 * i] = v4.x;
+                ph[4 * i + 1] = v4.y;
+                ph[4 * i + 2] = v4.z;
+                ph[4 * i + 3] = v4.w;
+            }
+            float run = carry, dg = carry;
+#pragma unroll
+            for (int s = kCk - 1; s >= 0; --s) {
+                run = run + ph[s];
+                dg = s == m ? run : dg;
+            }
+            carry = run;
+            if (lane < kCk && m < m1) {
+                out_beta[(size_t)(t0 + m) * p.hv + h] = sbv + abrow[j % 3][m];
+                out_g[(size_t)(t0 + m) * p.hv + h] = dg;
+            }
+        };
+        // (wave 1) the dA part of dbeta of chunk j, sum_s dA[m][s] Gam_{m,s} (k_m . k_s),
+        // from the partials the state waves left a step before (a row's 16 entries sit
+        // in 16 lanes)
+        auto abrow_calc = [&](int j) {
+            const float *rec = rec_of(j);
+            const int b = j & 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = lane + 64 * e;
+                const int m = i / kCk, s = i % kCk;
+                const float ae = rec[kRecAb + i];
+                const float4 a4 = *reinterpret_cast<const float4 *>(&dAw[b][m][s][0]);
+                const float sav = (((0.f + a4.x) + a4.y) + a4.z) + a4.w;
+                const float ab = lane_sum<16>(sav * ae);
+                if (s == 0) abrow[j % 3][m] = ab;
+            }
+        };
+        if (nch > 0) fetch(nch - 1);
+        for (int st = 0; st <= nch; ++st) {
+            const int j = nch - 1 - st;  // this step's chunk (none at the last step)
+            if (j >= 0) {
+                stage_kq(j);
+                fetch_kq(j - 1);
+            }
+            lds_barrier();
+            if (j >= 0) {
+                const int m1 = chunk_m1(j);
+                const int64_t t0 = tb + (int64_t)kCk * j;
+                const int b = j & 1;
+                float(*Kc)[KP] = Ks[b];
+                float(*Qc)[KP] = Qs[b];
+                float dO[4], vv[4], xx[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const bool on = 4 * g + c < m1;
+                    dO[c] = on ? RW::widen1(F.dor[c]) : 0.f;
+                    vv[c] = on ? RW::widen1(F.vr[c]) : 0.f;
+                    xx[c] = on ? F.xr[c] : 0.f;
+                }
+                const float bt[4] = {F.bet.x, F.bet.y, F.bet.z, F.bet.w};
+                const float gm[4] = {F.gam.x, F.gam.y, F.gam.z, F.gam.w};
+                const float wl[4] = {F.wl.x, F.wl.y, F.wl.z, F.wl.w};
+                const float gl = F.gl;
+                const float4 trow = F.trow;
+                float tcol[4], bcol[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    tcol[c] = F.tcol[c];
+                    bcol[c] = F.bcol[c];
+                }
+                fetch(j - 1);
+
+                // E = K D^T on this wave's rows; dU = Gam_{l,.} E + B^T dO; dR = T^T dU; U = T (beta x)
+                f4 Ev = f4_zero();
+                float4 kav[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) kav[t] = *reinterpret_cast<const float4 *>(&Kc[x][16 * t + 4 * g]);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    Ev = mfma_16x16x4(kav[t].x, Dt[t][0], Ev);
+                    Ev = mfma_16x16x4(kav[t].y, Dt[t][1], Ev);
+                    Ev = mfma_16x16x4(kav[t].z, Dt[t][2], Ev);
+                    Ev = mfma_16x16x4(kav[t].w, Dt[t][3], Ev);
+                }
+                f4 dU = f4{wl[0] * Ev[0], wl[1] * Ev[1], wl[2] * Ev[2], wl[3] * Ev[3]};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) dU = mfma_16x16x4(bcol[c], dO[c], dU);
+                f4 dR = f4_zero();
+#pragma unroll
+                for (int c = 0; c < 4; ++c) dR = mfma_16x16x4(tcol[c], dU[c], dR);
+                f4 U = f4_zero();
+                U = mfma_16x16x4(trow.x, bt[0] * xx[0], U);
+                U = mfma_16x16x4(trow.y, bt[1] * xx[1], U);
+                U = mfma_16x16x4(trow.z, bt[2] * xx[2], U);
+                U = mfma_16x16x4(trow.w, bt[3] * xx[3], U);
+
+                // dv; the row sums dR . x and dv . v; the token rows for the gradient waves
+                // (through vector registers: see gdn_bwd_chunk_rev_kernel)
+                const auto dv_rsrc = buf_rsrc(p.grad_v + (size_t)t0 * vrow, (uint32_t)(m1 * vrow * 4));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int m = 4 * g + c;
+                    float dr = dR[c], uu = U[c];
+                    asm volatile("" : "+v"(dr), "+v"(uu));
+                    const float dvv = bt[c] * dr;
+                    buf_store_f32(dv_rsrc, m < m1 ? (uint32_t)((m * vrow + (size_t)h * DV + rg + x) * 4) : kDropped, dvv);
+                    const float sb = lane_sum<16>(dr * xx[c]);
+                    const float sv = lane_sum<16>(dvv * vv[c]);
+                    if (x == 0) {
+                        red[j % 3][wave][m][0] = sb;
+                        red[j % 3][wave][m][1] = sv;
+                    }
+                    dOs[b][m][r0 + x] = dO[c];
+                    dRs[b][m][r0 + x] = dr;
+                    Us[b][m][r0 + x] = uu;
+                }
+                // partial dB = dO U^T and dA = -dR U^T over this wave's rows (its own
+                // token rows, just written)
+                {
+                    const float4 o4 = *reinterpret_cast<const float4 *>(&dOs[b][x][r0 + 4 * g]);
+                    const float4 r4 = *reinterpret_cast<const float4 *>(&dRs[b][x][r0 + 4 * g]);
+                    const float4 u4 = *reinterpret_cast<const float4 *>(&Us[b][x][r0 + 4 * g]);
+                    f4 pb = f4_zero(), pa = f4_zero();
+                    pb = mfma_16x16x4(o4.x, u4.x, pb);
+                    pb = mfma_16x16x4(o4.y, u4.y, pb);
+                    pb = mfma_16x16x4(o4.z, u4.z, pb);
+                    pb = mfma_16x16x4(o4.w, u4.w, pb);
+                    pa = mfma_16x16x4(-r4.x, u4.x, pa);
+                    pa = mfma_16x16x4(-r4.y, u4.y, pa);
+                    pa = mfma_16x16x4(-r4.z, u4.z, pa);
+                    pa = mfma_16x16x4(-r4.w, u4.w, pa);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float vb = pb[r], va = pa[r];
+                        asm volatile("" : "+v"(vb), "+v"(va));
+                        dBw[b][4 * g + r][x][wave] = vb;
+                        dAw[b][4 * g + r][x][wave] = va;
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    *reinterpret_cast<float4 *>(&Ds[b][r0 + x][16 * t + 4 * g]) =
+                        make_float4(Dt[t][0], Dt[t][1], Dt[t][2], Dt[t][3]);
+
+                // D at the chunk's start: D^T = Gam_l D^T + Q^T (Gam dO) - K^T (beta Gam dR)
+                float bq[4], bk[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    bq[c] = gm[c] * dO[c];
+                    bk[c] = -(bt[c] * gm[c]) * dR[c];
+                }
+                float qa[2][4], ka[2][4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    qa[0][c] = Qc[4 * g + c][x];
+                    ka[0][c] = Kc[4 * g + c][x];
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    if (t + 1 < NT) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            qa[(t + 1) & 1][c] = Qc[4 * g + c][16 * (t + 1) + x];
+                            ka[(t + 1) & 1][c] = Kc[4 * g + c][16 * (t + 1) + x];
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    f4 C = f4{gl * Dt[t][0], gl * Dt[t][1], gl * Dt[t][2], gl * Dt[t][3]};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) C = mfma_16x16x4(qa[t & 1][c], bq[c], C);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) C = mfma_16x16x4(ka[t & 1][c], bk[c], C);
+                    Dt[t] = C;
+                }
+            }
+            // the gradient waves run chunk j + 1 in this step; chunk j + 2 is complete
+            if (wave == 1 && st >= 1) abrow_calc(j + 1);
+            if (wave == 0 && st >= 2) per_token(j + 2);
+            lds_barrier();
+        }
+        if (wave == 0 && nch > 0) per_token(0);
+        if (p.grad_h0) {
+            float *dst = p.grad_h0 + (((size_t)n * p.hv + h) * DV + rg + x) * DK;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                *reinterpret_cast<float4 *>(dst + 16 * t + 4 * g) = make_float4(Dt[t][0], Dt[t][1], Dt[t][2], Dt[t][3]);
+        }
+    } else {
+        // ============================================================= gradient waves
+        const int gw = wave - NWD;
+        struct {
+            float4 gam, gmr, be4;       // Gam_{4 g + c}, Gam_{x, 4 g + c}, beta_{4 g + c}
+            float bx, gx, wx;           // beta, Gam and Gam_{l,x} of token x
+            float gmc[4];               // Gam_{4 g + c, x}
+        } F;
+        // S0[part DVP + 16 rt + 4 g + c][16 (gw + NWD l2) + x], read a chunk ahead once
+        // the current one is no longer needed
+        f4 s0[RT][CTW];
+        auto fetch_s0 = [&](int j_) {
+            const int j = j_ < 0 ? 0 : j_;
+            const float *ck = p.ck + (((size_t)(base + j) * p.hv + h) * DV + part * DVP) * DK;
+#pragma unroll
+            for (int l2 = 0; l2 < CTW; ++l2)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        s0[rt][l2][c] = ck[(16 * rt + 4 * g + c) * DK + 16 * (gw + NWD * l2) + x];
+        };
+        auto fetch = [&](int j_) {
+            const int j = j_ < 0 ? 0 : j_;
+            const float *rec = rec_of(j);
+            const int l = chunk_m1(j) - 1;
+            F.gam = *reinterpret_cast<const float4 *>(rec + kRecGam + 4 * g);
+            F.gmr = *reinterpret_cast<const float4 *>(rec + kRecGm + x * kCk + 4 * g);
+            F.be4 = *reinterpret_cast<const float4 *>(rec + kRecBeta + 4 * g);
+            F.bx = rec[kRecBeta + x];
+            F.gx = rec[kRecGam + x];
+            F.wx = rec[kRecGm + l * kCk + x];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) F.gmc[c] = rec[kRecGm + (4 * g + c) * kCk + x];
+        };
+        if (nch > 0) {
+            fetch(nch - 1);
+            fetch_s0(nch - 1);
+        }
+        for (int st = 0; st <= nch; ++st) {
+            const int js = nch - 1 - st;  // the state waves' chunk
+            const int j = js + 1;         // this step's chunk (none at the first step)
+            if (js >= 0) {
+                stage_kq(js);
+                fetch_kq(js - 1);
+            }
+            lds_barrier();
+            if (st >= 1) {
+                const int m1 = chunk_m1(j);
+                const int64_t t0 = tb + (int64_t)kCk * j;
+                const int b = j & 1;
+                float(*Kc)[KP] = Ks[b];
+                float(*Qc)[KP] = Qs[b];
+                const float gm[4] = {F.gam.x, F.gam.y, F.gam.z, F.gam.w};
+                const float fr = -(F.bx * F.gx), fu = F.wx;  // factors of A-operand row x (token x)
+                const float gmr[4] = {F.gmr.x, F.gmr.y, F.gmr.z, F.gmr.w};
+                const float be4[4] = {F.be4.x, F.be4.y, F.be4.z, F.be4.w};
+                const float bx = F.bx;
+                float gmc[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) gmc[c] = F.gmc[c];
+                fetch(j - 1);
+
+                // the entries of Ms = dB Gam (s <= m) and H = dA beta Gam (s < m) this lane
+                // needs, at (x, 4 g + c) and (4 g + c, x): dB and dA summed over the state
+                // waves in order, then masked and weighted
+                float mr[4], mc[4], hh[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float4 b1 = *reinterpret_cast<const float4 *>(&dBw[b][x][4 * g + c][0]);
+                    const float4 b2 = *reinterpret_cast<const float4 *>(&dBw[b][4 * g + c][x][0]);
+                    const float4 a1 = *reinterpret_cast<const float4 *>(&dAw[b][x][4 * g + c][0]);
+                    const float4 a2 = *reinterpret_cast<const float4 *>(&dAw[b][4 * g + c][x][0]);
+                    const float sb1 = (((0.f + b1.x) + b1.y) + b1.z) + b1.w;
+                    const float sb2 = (((0.f + b2.x) + b2.y) + b2.z) + b2.w;
+                    const float sa1 = (((0.f + a1.x) + a1.y) + a1.z) + a1.w;
+                    const float sa2 = (((0.f + a2.x) + a2.y) + a2.z) + a2.w;
+                    mr[c] = sb1 * gmr[c];
+                    mc[c] = sb2 * gmc[c];
+                    const float h1 = 4 * g + c < x ? sa1 * (bx * gmr[c]) : 0.f;
+                    const float h2 = x < 4 * g + c ? sa2 * (be4[c] * gmc[c]) : 0.f;
+                    hh[c] = h1 + h2;
+                }
+
+                // products over the part's rows on this wave's column tiles:
+                //   dq0 = dO S0,  dk1 = (-beta Gam dR) S0 + (Gam_{l,.} U) D
+                f4 dq[CTW], dk[CTW];
+                {
+                    float ao[RT][4], ar[RT][4], au[RT][4];
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        const float4 o4 = *reinterpret_cast<const float4 *>(&dOs[b][x][16 * rt + 4 * g]);
+                        const float4 r4 = *reinterpret_cast<const float4 *>(&dRs[b][x][16 * rt + 4 * g]);
+                        const float4 u4 = *reinterpret_cast<const float4 *>(&Us[b][x][16 * rt + 4 * g]);
+                        ao[rt][0] = o4.x; ao[rt][1] = o4.y; ao[rt][2] = o4.z; ao[rt][3] = o4.w;
+                        ar[rt][0] = r4.x; ar[rt][1] = r4.y; ar[rt][2] = r4.z; ar[rt][3] = r4.w;
+                        au[rt][0] = u4.x; au[rt][1] = u4.y; au[rt][2] = u4.z; au[rt][3] = u4.w;
+                    }
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            ar[rt][c] = fr * ar[rt][c];
+                            au[rt][c] = fu * au[rt][c];
+                        }
+#pragma unroll
+                    for (int l2 = 0; l2 < CTW; ++l2) {
+                        // this column tile's D columns, read before its products
+                        float dd[RT][4];
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) dd[rt][c] = Ds[b][16 * rt + 4 * g + c][16 * (gw + NWD * l2) + x];
+                        f4 aq = f4_zero(), ak = f4_zero();
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                aq = mfma_16x16x4(ao[rt][c], s0[rt][l2][c], aq);
+                                ak = mfma_16x16x4(ar[rt][c], s0[rt][l2][c], ak);
+                                ak = mfma_16x16x4(au[rt][c], dd[rt][c], ak);
+                            }
+                        }
+                        dq[l2] = f4{gm[0] * aq[0], gm[1] * aq[1], gm[2] * aq[2], gm[3] * aq[3]};
+                        dk[l2] = ak;
+                    }
+                }
+                fetch_s0(j - 1);
+
+                // in-chunk terms: dq += Ms K;  dk += Ms^T Q + (H + H^T) K; stores; q . dq
+                {
+                    float kcol[CTW][4], qcol[CTW][4];
+#pragma unroll
+                    for (int l2 = 0; l2 < CTW; ++l2)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            kcol[l2][c] = Kc[4 * g + c][16 * (gw + NWD * l2) + x];
+                            qcol[l2][c] = Qc[4 * g + c][16 * (gw + NWD * l2) + x];
+                        }
+#pragma unroll
+                    for (int l2 = 0; l2 < CTW; ++l2) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) dq[l2] = mfma_16x16x4(mr[c], kcol[l2][c], dq[l2]);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(mc[c], qcol[l2][c], dk[l2]);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) dk[l2] = mfma_16x16x4(hh[c], kcol[l2][c], dk[l2]);
+                    }
+                    float qd[4] = {0.f, 0.f, 0.f, 0.f};
+                    const uint32_t qrow = (uint32_t)(p.hv * DK);
+                    const size_t qbase = ((size_t)part * p.total_tokens + t0) * p.hv * DK;
+                    const auto dq_rsrc = buf_rsrc(p.dqh + qbase, (uint32_t)m1 * qrow * 4u);
+                    const auto dk_rsrc = buf_rsrc(p.dkh + qbase, (uint32_t)m1 * qrow * 4u);
+#pragma unroll
+                    for (int l2 = 0; l2 < CTW; ++l2) {
+                        const int ct = gw + NWD * l2;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int m = 4 * g + r;
+                            qd[r] = __builtin_fmaf(qcol[l2][r], dq[l2][r], qd[r]);
+                            const uint32_t o =
+                                m < m1 ? ((uint32_t)m * qrow + (uint32_t)(h * DK + 16 * ct + x)) * 4u : kDropped;
+                            buf_store_f32(dq_rsrc, o, dq[l2][r]);
+                            buf_store_f32(dk_rsrc, o, dk[l2][r]);
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float v = lane_sum<16>(qd[r]);
+                        if (x == 0) red[j % 3][gw][4 * g + r][2] = v;
+                    }
+                }
+            }
+            lds_barrier();
+        }
+    }
+}
+
 // dq and dk of each key head: the (value head, part) partials that read it, added
 // value head by value head and within a head part by part.
 __global__ __launch_bounds__(256) void gdn_bwd_chunk_gqa_kernel(BwdChunkParams p) {
@@ -639,6 +1183,12 @@ __global__ __launch_bounds__(256) void gdn_bwd_chunk_parts_kernel(BwdChunkParams
 template <int DK, int DV, class IO>
 hipError_t rev_launch(const BwdChunkParams &p, hipStream_t s) {
     const unsigned grid = (unsigned)((int64_t)p.n_seqs * p.hv * p.parts);
+    if constexpr (DV == 128) {
+        if (p.parts == 2 && !p.plain) {
+            hipLaunchKernelGGL((gdn_bwd_chunk_ws_kernel<DK, IO>), dim3(grid), dim3(512), 0, s, p);
+            return hipGetLastError();
+        }
+    }
     if (p.parts == 1)
         hipLaunchKernelGGL((gdn_bwd_chunk_rev_kernel<DK, DV, IO, 1>), dim3(grid), dim3(64 * (DV / 16)), 0, s, p);
     else if constexpr (DV >= 64)

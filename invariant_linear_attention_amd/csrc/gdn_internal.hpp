@@ -147,6 +147,7 @@ struct BwdChunkParams {
     int32_t rank_by_length;
     int32_t hdot_parts;               // partial sums of <dhT, hT> per (sequence, value head)
     int32_t parts;                    // workgroups per (sequence, value head), each a share of the rows
+    int32_t plain;                    // no wave specialization (same bits; for comparison)
 };
 hipError_t launch_bwd_chunked(const BwdChunkParams &p, int io_dtype, hipStream_t s);
 

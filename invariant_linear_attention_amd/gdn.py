@@ -394,13 +394,13 @@ def gdn_bwd_chunked_workspace_size(dims: GdnDims) -> int:
 
 
 def gdn_bwd_chunked(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=None, grads=None, stream=None,
-                    want_dh0: bool = True, waves: int = 0, parts: int = 0):
+                    want_dh0: bool = True, waves: int = 0, parts: int = 0, plain: bool = False):
     """Chunked backward on the matrix cores (see include/gdn.h): the gradients of
     gdn_bwd_varlen, same arguments and results.  ``workspace`` (uint8, at least
     gdn_bwd_chunked_workspace_size bytes) and ``grads`` are allocated when None;
     ``waves`` (0, 1, 2 or 4) is the forward walk's waves per 16-row state tile and
     ``parts`` (0 = automatic, 1 or 2) the reverse walk's workgroups per (sequence,
-    value head)."""
+    value head); ``plain`` turns off its wave specialization (the same bits)."""
     import torch
     T, hk, dk, hv, dv, N = _dims_of(q, k, v, g, beta, cu_seqlens, require_cu=True)
     _shape(h0, "h0", (N, hv, dv, dk))
@@ -421,7 +421,7 @@ def gdn_bwd_chunked(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=
     for name, t in (("g", g), ("beta", beta), ("h0", h0), ("dhT", dhT)):
         _need(t, name, torch.float32)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
-    dims = make_dims(q, v, N, T, plan=(0, parts, waves))
+    dims = make_dims(q, v, N, T, plan=(int(bool(plain)), parts, waves))
     if workspace is None:
         workspace = torch.empty(gdn_bwd_chunked_workspace_size(dims), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8)

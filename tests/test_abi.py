@@ -491,7 +491,8 @@ def test_bwd_chunked_workspace_size(lib):
 
 @pytest.mark.parametrize("case,over,code", [
     (dict(dk=32), {}, 6), (dict(dk=16), {}, 6), (dict(dv=16), {}, 6), (dict(dv=96), {}, 6),
-    (dict(plan_lanes=8), {}, 6), (dict(plan_rows=3), {}, 6), (dict(plan_rows=2, dv=32), {}, 6),
+    (dict(plan_lanes=8), {}, 6), (dict(plan_lanes=2), {}, 6), (dict(plan_rows=3), {}, 6),
+    (dict(plan_rows=2, dv=32), {}, 6),
     (dict(plan_waves=3), {}, 6),
     (dict(hk=1, hv=32), {}, 6), (dict(hv=3), {}, 2), (dict(io_dtype=7), {}, 3),
     (dict(n_seqs=0, total_tokens=3), {}, 2),

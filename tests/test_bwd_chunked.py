@@ -97,6 +97,19 @@ def test_deterministic_batch_invariant_any_walk_shape(gpu, parts):
     say("chunked backward parts=%d: repeat, walk shapes and alone-vs-batch bitwise equal" % parts)
 
 
+@pytest.mark.parametrize("dk,io", [(128, torch.bfloat16), (64, torch.float32)])
+def test_wave_specialization_same_bits(gpu, dk, io):
+    """dv = 128 in two parts runs with state and gradient waves by default; the plain
+    walk (every wave does a whole chunk) gives the same bits."""
+    w = synth.make_workload(581 + dk, [70, 0, 16, 33, 1, 130], hk=2, hv=4, dk=dk, dv=128, io_dtype=io, h0_std=0.1)
+    dout, dhT = grad_inputs(w, 23)
+    r1 = run_cbwd(gpu, w, dout, dhT, parts=2)
+    r2 = run_cbwd(gpu, w, dout, dhT, parts=2, plain=True)
+    for key in r1:
+        assert torch.equal(r1[key], r2[key]), key
+    say("chunked backward dk=%d: specialized and plain reverse walks bitwise equal" % dk)
+
+
 def test_empty_and_single_token_sequences(gpu):
     from oracle import oracle
     w = synth.make_workload(531, [0, 1, 0, 2, 1, 17], hk=1, hv=2, dk=64, dv=64, h0_std=0.1)
