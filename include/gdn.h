@@ -492,6 +492,43 @@ gdn_status gdn_bwd_chunked(const gdn_dims *dims,
                            float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dh0,
                            void *workspace, uint64_t workspace_bytes, void *stream);
 
+/*
+ * The fused preprocessing as a pass of its own, and its gradients: what a trainer
+ * needs to differentiate through the layer's preprocessing (the gated delta rule
+ * layer of Yang, Kautz, Hatamizadeh, ICLR 2025; A_log kept in fp32 as in the page
+ * "Defending Against the Training-Inference Numeric Mismatch in RL (Especially
+ * Linear Attention)", section 3.1).  With dims->pre (or NULL: no preprocessing):
+ *
+ *   gdn_preprocess: qn, kn = the L2-normalised q, k rows (fp32 [T][hk][dk]) and
+ *     g, beta (fp32 [T][hv]) from the logits a, b, each by the fp32 operations the
+ *     fused kernels use (see gdn_preproc above), so that gdn_fwd_varlen with
+ *     io_dtype GDN_F32 on (qn, kn, v widened, g, beta) computes the fused call's
+ *     state bit for bit and its outputs before their rounding to bf16.
+ *   gdn_preprocess_backward: given dL/dqn, dL/dkn, dL/dg and dL/dbeta (fp32, e.g.
+ *     from gdn_bwd_varlen or gdn_bwd_chunked on the preprocessed values), the
+ *     gradients of the raw inputs:
+ *       dq = (dqn - qn (qn . dqn)) r with r = rsq(sum q^2 + eps) (likewise dk);
+ *       da = dg (-exp(A_log) sigmoid(a + dt_bias));  db = dbeta beta (1 - beta);
+ *       dA_log[h] = sum_t dg g;  ddt_bias[h] = sum_t da  (all T tokens, fixed order)
+ *     Without GDN_PRE_QK_L2NORM dq = dqn (dk = dkn); without GDN_PRE_GATE_LOGITS
+ *     da = dg, db = dbeta and dA_log, ddt_bias are not written; ddt_bias is written
+ *     only when pre->dt_bias is given.
+ *
+ *   q, k : [T][hk][dk] io dtype, 16-byte aligned; a, b, g, beta, da, db, dg, dbeta:
+ *          [T][hv] fp32; qn, kn, dqn, dkn, dq, dk: [T][hk][dk] fp32, 16-byte aligned;
+ *          dA_log, ddt_bias: [hv] fp32.  All device memory, owned by the caller.
+ * Only hk, hv, dk (16, 32, 64 or 128), dv, io_dtype, total_tokens and pre of dims
+ * are used (n_seqs is not).  Errors as gdn_fwd_varlen: NULL, SHAPE, DTYPE,
+ * UNSUPPORTED, ALIGN, ALIAS (an output overlapping an input or another output).
+ */
+gdn_status gdn_preprocess(const gdn_dims *dims, const void *q, const void *k, const float *a, const float *b,
+                          float *qn, float *kn, float *g, float *beta, void *stream);
+
+gdn_status gdn_preprocess_backward(const gdn_dims *dims, const void *q, const void *k, const float *a,
+                                   const float *b, const float *dqn, const float *dkn, const float *dg,
+                                   const float *dbeta, float *dq, float *dk, float *da, float *db, float *dA_log,
+                                   float *ddt_bias, void *stream);
+
 /* Human-readable description of a status code (static storage; an unknown code
  * gives "unknown gdn_status").  Every refusal is reported as one of these codes rather than
  * served by another, non-invariant path: the bitwise-parity post on linear
@@ -503,7 +540,7 @@ const char *gdn_status_string(gdn_status status);
 /* ABI version of this header (major * 100 + minor). */
 int32_t gdn_abi_version(void);
 
-#define GDN_ABI_VERSION 209
+#define GDN_ABI_VERSION 210
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libgdn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["gdn_api.hip", "gdn_bwd.hip", "gdn_bwd_chunked.hip", "gdn_chunked.hip", "gdn_conv.hip", "gdn_dk16.hip", "gdn_dk32.hip", "gdn_dk64.hip", "gdn_dk128.hip"]
+SOURCES = ["gdn_api.hip", "gdn_bwd.hip", "gdn_bwd_chunked.hip", "gdn_chunked.hip", "gdn_conv.hip", "gdn_dk16.hip", "gdn_dk32.hip", "gdn_dk64.hip", "gdn_dk128.hip", "gdn_preproc.hip"]
 
 # -ffp-contract=off: no implicit a*b+c fusion, so every fused multiply-add is an
 # explicit one and the operation sequence is exactly the one written.

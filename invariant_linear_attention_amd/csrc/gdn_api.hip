@@ -785,6 +785,92 @@ gdn_status gdn_bwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_preprocess(const gdn_dims *dims, const void *q, const void *k, const float *a, const float *b,
+                          float *qn, float *kn, float *g, float *beta, void *stream) {
+    using namespace gdn;
+    const gdn_status st = check_common(dims);
+    if (st != GDN_OK) return st;
+    const gdn_dims &d = *dims;
+    const int64_t T = d.total_tokens;
+    if (T == 0) return GDN_OK;
+    if (!q || !k || !a || !b || !qn || !kn || !g || !beta) return GDN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(qn, 16) || !aligned(kn, 16) || !aligned(a, 4) ||
+        !aligned(b, 4) || !aligned(g, 4) || !aligned(beta, 4))
+        return GDN_ERR_ALIGN;
+    const uint64_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
+    const uint64_t qk_n = (uint64_t)T * d.hk * d.dk, gb = (uint64_t)T * d.hv * 4;
+    const Range inputs[] = {range_of(q, qk_n * esz), range_of(k, qk_n * esz), range_of(a, gb), range_of(b, gb),
+                            pre_range(dims, 0), pre_range(dims, 1)};
+    const Range outputs[] = {range_of(qn, qk_n * 4), range_of(kn, qk_n * 4), range_of(g, gb), range_of(beta, gb)};
+    for (size_t i = 0; i < 4; ++i) {
+        for (const Range &in : inputs)
+            if (overlap(outputs[i], in)) return GDN_ERR_ALIAS;
+        for (size_t j = i + 1; j < 4; ++j)
+            if (overlap(outputs[i], outputs[j])) return GDN_ERR_ALIAS;
+    }
+    PreParams p{};
+    p.q = q; p.k = k; p.a = a; p.b = b;
+    p.qn = qn; p.kn = kn; p.g = g; p.beta = beta;
+    if (const gdn_preproc *pre = d.pre) {
+        p.flags = pre->flags;
+        p.eps = pre->eps;
+        p.A_log = pre->A_log;
+        p.dt_bias = pre->dt_bias;
+    }
+    p.total_tokens = T; p.hk = d.hk; p.hv = d.hv;
+    return launch_preprocess(p, d.dk, d.io_dtype, false, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
+gdn_status gdn_preprocess_backward(const gdn_dims *dims, const void *q, const void *k, const float *a,
+                                   const float *b, const float *dqn, const float *dkn, const float *dg,
+                                   const float *dbeta, float *dq, float *dk, float *da, float *db, float *dA_log,
+                                   float *ddt_bias, void *stream) {
+    using namespace gdn;
+    const gdn_status st = check_common(dims);
+    if (st != GDN_OK) return st;
+    const gdn_dims &d = *dims;
+    const int64_t T = d.total_tokens;
+    const bool gated = d.pre && (d.pre->flags & GDN_PRE_GATE_LOGITS);
+    if (T > 0 && (!q || !k || !a || !b || !dqn || !dkn || !dg || !dbeta || !dq || !dk || !da || !db))
+        return GDN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(dqn, 16) || !aligned(dkn, 16) || !aligned(dq, 16) ||
+        !aligned(dk, 16) || !aligned(a, 4) || !aligned(b, 4) || !aligned(dg, 4) || !aligned(dbeta, 4) ||
+        !aligned(da, 4) || !aligned(db, 4) || !aligned(dA_log, 4) || !aligned(ddt_bias, 4))
+        return GDN_ERR_ALIGN;
+    const uint64_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
+    const uint64_t qk_n = (uint64_t)T * d.hk * d.dk, gb = (uint64_t)T * d.hv * 4, hb = (uint64_t)d.hv * 4;
+    const Range inputs[] = {range_of(q, qk_n * esz), range_of(k, qk_n * esz), range_of(a, gb), range_of(b, gb),
+                            range_of(dqn, qk_n * 4), range_of(dkn, qk_n * 4), range_of(dg, gb),
+                            range_of(dbeta, gb), pre_range(dims, 0), pre_range(dims, 1)};
+    const Range outputs[] = {range_of(dq, qk_n * 4), range_of(dk, qk_n * 4), range_of(da, gb), range_of(db, gb),
+                             range_of(gated ? dA_log : nullptr, hb), range_of(gated ? ddt_bias : nullptr, hb)};
+    for (size_t i = 0; i < 6; ++i) {
+        for (const Range &in : inputs)
+            if (overlap(outputs[i], in)) return GDN_ERR_ALIAS;
+        for (size_t j = i + 1; j < 6; ++j)
+            if (overlap(outputs[i], outputs[j])) return GDN_ERR_ALIAS;
+    }
+    PreParams p{};
+    p.q = q; p.k = k; p.a = a; p.b = b;
+    p.dqn = dqn; p.dkn = dkn; p.dg = dg; p.dbeta = dbeta;
+    p.dq = dq; p.dk = dk; p.da = da; p.db = db;
+    if (const gdn_preproc *pre = d.pre) {
+        p.flags = pre->flags;
+        p.eps = pre->eps;
+        p.A_log = pre->A_log;
+        p.dt_bias = pre->dt_bias;
+    }
+    // the parameter gradients (written even for T = 0: sums over no tokens)
+    p.dA_log = gated ? dA_log : nullptr;
+    p.ddt_bias = gated && d.pre->dt_bias ? ddt_bias : nullptr;
+    p.total_tokens = T; p.hk = d.hk; p.hv = d.hv;
+    return launch_preprocess(p, d.dk, d.io_dtype, true, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
 const char *gdn_status_string(gdn_status status) {
     switch (status) {
         case GDN_OK: return "GDN_OK";

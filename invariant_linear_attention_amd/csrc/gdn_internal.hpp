@@ -131,6 +131,21 @@ struct ChunkedParams {
 hipError_t launch_chunked(const ChunkedParams &p, int io_dtype, hipStream_t s);
 hipError_t launch_chunked_bwd_walk(const ChunkedParams &p, int io_dtype, hipStream_t s);
 
+// The fused preprocessing as a pass of its own and its gradients (gdn_preproc.hip).
+struct PreParams {
+    const void *q, *k;                            // raw queries and keys, io dtype [T][hk][dk]
+    const float *a, *b;                           // gate and beta logits (or g, beta) [T][hv]
+    float *qn, *kn, *g, *beta;                    // forward: the preprocessed values (fp32)
+    const float *dqn, *dkn, *dg, *dbeta;          // backward: their gradients (fp32)
+    float *dq, *dk, *da, *db, *dA_log, *ddt_bias; // backward: the raw inputs' gradients
+    const float *A_log, *dt_bias;
+    float eps;
+    int32_t flags;
+    int64_t total_tokens;
+    int32_t hk, hv;
+};
+hipError_t launch_preprocess(const PreParams &p, int dk, int io_dtype, bool backward, hipStream_t s);
+
 // Kernel arguments of the reverse walk of the chunked backward (gdn_bwd_chunked).
 struct BwdChunkParams {
     const void *q, *k, *v, *dout;     // io dtype

@@ -22,8 +22,8 @@ STATUS = {
 GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
            "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_bwd_varlen_noalloc", "gdn_fwd_chunked",
-           "gdn_chunked_workspace_size", "gdn_bwd_chunked_workspace_size", "gdn_bwd_chunked", "gdn_status_string",
-           "gdn_abi_version")
+           "gdn_chunked_workspace_size", "gdn_bwd_chunked_workspace_size", "gdn_bwd_chunked", "gdn_preprocess",
+           "gdn_preprocess_backward", "gdn_status_string", "gdn_abi_version")
 
 GDN_CHUNK = 16
 
@@ -113,6 +113,10 @@ def load_library(path: str = LIBRARY):
         lib.gdn_bwd_chunked_workspace_size.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(ctypes.c_uint64)]
         lib.gdn_bwd_chunked.restype = ctypes.c_int
         lib.gdn_bwd_chunked.argtypes = [ctypes.POINTER(GdnDims)] + [vp] * 16 + [ctypes.c_uint64, vp]
+        lib.gdn_preprocess.restype = ctypes.c_int
+        lib.gdn_preprocess.argtypes = [ctypes.POINTER(GdnDims)] + [vp] * 9
+        lib.gdn_preprocess_backward.restype = ctypes.c_int
+        lib.gdn_preprocess_backward.argtypes = [ctypes.POINTER(GdnDims)] + [vp] * 15
         lib.gdn_query_plan.restype = ctypes.c_int
         lib.gdn_query_plan.argtypes = [ctypes.POINTER(GdnDims), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
         lib.gdn_status_string.restype = ctypes.c_char_p
@@ -437,6 +441,86 @@ def gdn_bwd_chunked(q, k, v, g, beta, h0, cu_seqlens, dout, dhT=None, workspace=
                                _ptr(cu_seqlens), _ptr(dout), _ptr(dhT), _ptr(grads["dq"]), _ptr(grads["dk"]),
                                _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["dbeta"]), _ptr(grads.get("dh0")),
                                _ptr(workspace), int(workspace.numel()), _stream_handle(stream)))
+    return grads
+
+
+def _pre_dims(q, a, pre) -> GdnDims:
+    T, hk, dk = (int(x) for x in q.shape)
+    hv = int(a.shape[1])
+    dims = GdnDims(n_seqs=0, hk=hk, hv=hv, dk=dk, dv=16, io_dtype=_io_code(q), total_tokens=T, pool_size=0,
+                   plan_lanes=0, plan_rows=0, plan_waves=0, reserved=0,
+                   pre=ctypes.pointer(pre) if pre is not None else None)
+    dims._keep = pre
+    return dims
+
+
+def _pre_shapes(q, k, a, b, pre):
+    import torch
+    if q is None or q.dim() != 3:
+        raise ValueError("q must be [T, Hk, dk], got %s" % (None if q is None else tuple(q.shape),))
+    T, hk, dk = (int(x) for x in q.shape)
+    _shape(k, "k", (T, hk, dk))
+    if a is None or a.dim() != 2 or int(a.shape[0]) != T:
+        raise ValueError("a must be [T, Hv] with T = %d, got %s" % (T, None if a is None else tuple(a.shape)))
+    hv = int(a.shape[1])
+    _shape(b, "b", (T, hv))
+    _check_pre(pre, hv)
+    _need(q, "q")
+    _need(k, "k", q.dtype)
+    _need(a, "a", torch.float32)
+    _need(b, "b", torch.float32)
+    return T, hk, dk, hv
+
+
+def gdn_preprocess(q, k, a, b, pre=None, out=None, stream=None):
+    """The fused preprocessing as a pass of its own (see include/gdn.h): q, k
+    [T, Hk, dk] (bf16 or fp32), a, b [T, Hv] fp32 logits (or g, beta when ``pre``
+    has no gate logits).  Returns a dict of fp32 tensors qn, kn [T, Hk, dk] and
+    g, beta [T, Hv] (``out``, a dict of the same, is filled when given)."""
+    import torch
+    T, hk, dk, hv = _pre_shapes(q, k, a, b, pre)
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=q.device)
+        out = {"qn": torch.empty((T, hk, dk), **f32), "kn": torch.empty((T, hk, dk), **f32),
+               "g": torch.empty((T, hv), **f32), "beta": torch.empty((T, hv), **f32)}
+    for name, shp in (("qn", (T, hk, dk)), ("kn", (T, hk, dk)), ("g", (T, hv)), ("beta", (T, hv))):
+        _shape(out.get(name), name, shp)
+        _need(out[name], name, torch.float32)
+    dims = _pre_dims(q, a, pre)
+    _check(load_library().gdn_preprocess(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(a), _ptr(b), _ptr(out["qn"]),
+                                         _ptr(out["kn"]), _ptr(out["g"]), _ptr(out["beta"]), _stream_handle(stream)))
+    return out
+
+
+def gdn_preprocess_backward(q, k, a, b, dqn, dkn, dg, dbeta, pre=None, grads=None, stream=None):
+    """Gradients of gdn_preprocess (see include/gdn.h): given fp32 dqn, dkn
+    [T, Hk, dk] and dg, dbeta [T, Hv], returns a dict of fp32 dq, dk [T, Hk, dk],
+    da, db [T, Hv] and, with gate logits, dA_log [Hv] and (with dt_bias) ddt_bias
+    [Hv]."""
+    import torch
+    T, hk, dk, hv = _pre_shapes(q, k, a, b, pre)
+    for name, t, shp in (("dqn", dqn, (T, hk, dk)), ("dkn", dkn, (T, hk, dk)), ("dg", dg, (T, hv)),
+                         ("dbeta", dbeta, (T, hv))):
+        _shape(t, name, shp)
+        _need(t, name, torch.float32)
+    gated = pre is not None and (pre.flags & GDN_PRE_GATE_LOGITS)
+    has_dtb = gated and pre.dt_bias is not None
+    if grads is None:
+        f32 = dict(dtype=torch.float32, device=q.device)
+        grads = {"dq": torch.empty((T, hk, dk), **f32), "dk": torch.empty((T, hk, dk), **f32),
+                 "da": torch.empty((T, hv), **f32), "db": torch.empty((T, hv), **f32),
+                 "dA_log": torch.empty((hv,), **f32) if gated else None,
+                 "ddt_bias": torch.empty((hv,), **f32) if has_dtb else None}
+    for name, shp in (("dq", (T, hk, dk)), ("dk", (T, hk, dk)), ("da", (T, hv)), ("db", (T, hv)),
+                      ("dA_log", (hv,)), ("ddt_bias", (hv,))):
+        if grads.get(name) is not None:
+            _shape(grads[name], name, shp)
+            _need(grads[name], name, torch.float32)
+    dims = _pre_dims(q, a, pre)
+    _check(load_library().gdn_preprocess_backward(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(a), _ptr(b), _ptr(dqn), _ptr(dkn), _ptr(dg), _ptr(dbeta),
+        _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["da"]), _ptr(grads["db"]), _ptr(grads.get("dA_log")),
+        _ptr(grads.get("ddt_bias")), _stream_handle(stream)))
     return grads
 
 

@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
                           "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_bwd_varlen_noalloc",
                           "gdn_fwd_chunked", "gdn_chunked_workspace_size", "gdn_bwd_chunked_workspace_size",
-                          "gdn_bwd_chunked", "gdn_status_string", "gdn_abi_version"}
+                          "gdn_bwd_chunked", "gdn_preprocess", "gdn_preprocess_backward", "gdn_status_string",
+                          "gdn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -644,3 +645,71 @@ def test_noalloc_capacity_is_the_workspace_size(lib):
     over = _dims(n_seqs=1, total_tokens=993, hk=16, hv=32)
     assert ws_size(lib, fits) <= gdn.GDN_NOALLOC_SCRATCH_BYTES < ws_size(lib, over)
     assert call_bwd_noalloc(lib, over) == 8
+
+
+# ------------------------------------------------- preprocessing and its gradients
+
+PP = {name: BASE + (120 + i) * MB for i, name in enumerate(
+    ["q", "k", "a", "b", "qn", "kn", "g", "beta", "dqn", "dkn", "dg", "dbeta", "dq", "dk", "da", "db", "dA", "dD",
+     "Alog", "dtb"])}
+
+
+def pre_dims(gated=True, norm=True, **kw):
+    from invariant_linear_attention_amd import gdn
+    d = _dims(**kw)
+    if gated or norm:
+        pre = gdn.GdnPreproc(flags=(gdn.GDN_PRE_QK_L2NORM if norm else 0) | (gdn.GDN_PRE_GATE_LOGITS if gated else 0),
+                             eps=1e-6, A_log=PP["Alog"] if gated else None, dt_bias=PP["dtb"] if gated else None)
+        d.pre = ctypes.pointer(pre)
+        d._keep = pre
+    return d
+
+
+def call_pre(lib, dims, **over):
+    a = dict(PP)
+    a.update(over)
+    return lib.gdn_preprocess(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], a["a"], a["b"],
+                              a["qn"], a["kn"], a["g"], a["beta"], None)
+
+
+def call_pre_bwd(lib, dims, **over):
+    a = dict(PP)
+    a.update(over)
+    return lib.gdn_preprocess_backward(ctypes.byref(dims) if dims is not None else None, a["q"], a["k"], a["a"],
+                                       a["b"], a["dqn"], a["dkn"], a["dg"], a["dbeta"], a["dq"], a["dk"], a["da"],
+                                       a["db"], a["dA"], a["dD"], None)
+
+
+@pytest.mark.parametrize("case,over,code", [
+    (dict(dk=24), {}, 6), (dict(hv=3), {}, 2), (dict(io_dtype=5), {}, 3), (dict(reserved=1), {}, 2),
+    ({}, dict(q=None), 1), ({}, dict(kn=None), 1), ({}, dict(beta=None), 1), ({}, dict(a=None), 1),
+    ({}, dict(q=PP["q"] + 8), 4), ({}, dict(qn=PP["qn"] + 4), 4), ({}, dict(g=PP["g"] + 2), 4),
+    ({}, dict(qn=PP["q"]), 5), ({}, dict(g=PP["a"]), 5), ({}, dict(beta=PP["g"]), 5), ({}, dict(kn=PP["qn"]), 5),
+    ({}, dict(g=PP["Alog"]), 5),
+])
+def test_preprocess_rejects(lib, case, over, code):
+    assert call_pre(lib, pre_dims(**case), **over) == code
+
+
+@pytest.mark.parametrize("case,over,code", [
+    (dict(dk=24), {}, 6), (dict(hv=3), {}, 2),
+    ({}, dict(dqn=None), 1), ({}, dict(dq=None), 1), ({}, dict(da=None), 1), ({}, dict(db=None), 1),
+    ({}, dict(dq=PP["dq"] + 4), 4), ({}, dict(dA=PP["dA"] + 2), 4),
+    ({}, dict(dq=PP["q"]), 5), ({}, dict(da=PP["dg"]), 5), ({}, dict(dA=PP["Alog"]), 5), ({}, dict(dD=PP["dA"]), 5),
+    ({}, dict(dk=PP["dq"]), 5),
+])
+def test_preprocess_backward_rejects(lib, case, over, code):
+    assert call_pre_bwd(lib, pre_dims(**case), **over) == code
+
+
+def test_preprocess_gate_needs_A_log_and_empty_calls(lib):
+    from invariant_linear_attention_amd import gdn
+    d = pre_dims()
+    d.pre.contents.A_log = None
+    assert call_pre(lib, d) == 1
+    assert call_pre(lib, None) == 1
+    # no tokens: nothing to do (the backward without gate logits launches nothing either)
+    assert call_pre(lib, pre_dims(total_tokens=0), q=None, k=None, a=None, b=None, qn=None, kn=None, g=None,
+                    beta=None) == 0
+    assert call_pre_bwd(lib, pre_dims(gated=False, total_tokens=0), q=None, k=None, a=None, b=None, dqn=None,
+                        dkn=None, dg=None, dbeta=None, dq=None, dk=None, da=None, db=None) == 0
