@@ -290,6 +290,40 @@ gdn_status gdn_short_conv(const gdn_conv_dims *dims, const void *x, const float 
                           const int32_t *dst_idx, void *y, void *stream);
 
 /*
+ * Backward of gdn_short_conv: given dy = dL/dy (fp32 [T][C]), the gradients of the
+ * inputs x, the taps w, the bias and the carried state the call read, with z
+ * recomputed exactly as the forward forms it:
+ *
+ *     dz(t)    = dy(t) sigmoid(z) (1 + z (1 - sigmoid(z)))   (GDN_CONV_SILU; else dy)
+ *     dx(s)    = sum_{i=0}^{K-1} w[c][K-1-i] dz(s + i)       (s's own sequence only)
+ *     dw[c][j] = sum_t dz(t) x(t - (K-1) + j),   dbias[c] = sum_t dz(t)
+ *     dstate[n][c][m] = sum_{j <= m} w[c][j] dz(t_n + m - j)  (t_n: sequence n's first token)
+ *
+ * dw and dbias sum over every token of the call (blocks of 64 tokens, then the
+ * blocks in order); everything else is per sequence.  The state written by the
+ * forward is a copy of inputs for the next call, not differentiated here.
+ *
+ *   x, w, bias, cu_seqlens, src_idx : as gdn_short_conv
+ *   state_pool  : [P][C][K-1] io dtype, the states the forward read (keep them if
+ *                 the forward updated its slots in place)
+ *   dx          : [T][C] fp32;  dw: [C][K] fp32;  dbias: [C] fp32 or NULL;
+ *   dstate      : [N][C][K-1] fp32 or NULL
+ *   workspace   : device scratch of gdn_short_conv_backward_workspace_size bytes
+ *                 (4 (K+1) C bytes per 64 tokens), 4-byte aligned; contents on
+ *                 entry do not matter.
+ * Errors: NULL, SHAPE (K outside 2..8, C <= 0, P <= 0, P < N without src_idx, a
+ * small workspace), DTYPE, UNSUPPORTED (unknown flags), ALIGN (x and the pool to
+ * their element size, the rest 4 bytes), ALIAS (an output overlapping an input or
+ * another output).
+ */
+gdn_status gdn_short_conv_backward_workspace_size(const gdn_conv_dims *dims, uint64_t *bytes);
+
+gdn_status gdn_short_conv_backward(const gdn_conv_dims *dims, const void *x, const float *w, const float *bias,
+                                   const int32_t *cu_seqlens, const void *state_pool, const int32_t *src_idx,
+                                   const float *dy, float *dx, float *dw, float *dbias, float *dstate,
+                                   void *workspace, uint64_t workspace_bytes, void *stream);
+
+/*
  * Backward of gdn_fwd_varlen: gradients of a loss L with respect to every input,
  * given dL/dout and (optionally) dL/dhT.  The page "Defending Against the
  * Training-Inference Numeric Mismatch in RL (Especially Linear Attention)"

@@ -403,6 +403,75 @@ gdn_status gdn_short_conv(const gdn_conv_dims *dims, const void *x, const float 
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+// Dimension checks of the convolution's backward that need no pointer.
+static gdn_status conv_bwd_check(const gdn_conv_dims *dims) {
+    if (!dims) return GDN_ERR_NULL;
+    const gdn_conv_dims &d = *dims;
+    if (d.n_seqs < 0 || d.total_tokens < 0 || d.channels <= 0 || d.taps < 2 || d.taps > 8 || d.pool_size <= 0 ||
+        d.n_seqs > 65535)
+        return GDN_ERR_SHAPE;
+    if (d.flags & ~GDN_CONV_SILU) return GDN_ERR_UNSUPPORTED;
+    if (d.io_dtype != GDN_F32 && d.io_dtype != GDN_BF16) return GDN_ERR_DTYPE;
+    if (d.n_seqs == 0 && d.total_tokens != 0) return GDN_ERR_SHAPE;
+    if ((d.total_tokens + 63) / 64 > 0x7FFFFFFFll || (d.channels + 255) / 256 > 65535) return GDN_ERR_SHAPE;
+    return GDN_OK;
+}
+
+gdn_status gdn_short_conv_backward_workspace_size(const gdn_conv_dims *dims, uint64_t *bytes) {
+    using namespace gdn;
+    if (!bytes) return GDN_ERR_NULL;
+    const gdn_status st = conv_bwd_check(dims);
+    if (st != GDN_OK) return st;
+    *bytes = conv_bwd_workspace_bytes(dims->total_tokens, dims->channels, dims->taps);
+    return GDN_OK;
+}
+
+gdn_status gdn_short_conv_backward(const gdn_conv_dims *dims, const void *x, const float *w, const float *bias,
+                                   const int32_t *cu_seqlens, const void *state_pool, const int32_t *src_idx,
+                                   const float *dy, float *dx, float *dw, float *dbias, float *dstate,
+                                   void *workspace, uint64_t workspace_bytes, void *stream) {
+    using namespace gdn;
+    const gdn_status st = conv_bwd_check(dims);
+    if (st != GDN_OK) return st;
+    const gdn_conv_dims &d = *dims;
+    const int64_t T = d.total_tokens, N = d.n_seqs, C = d.channels, K = d.taps;
+    if (!w || !dw) return GDN_ERR_NULL;
+    if (N > 0 && (!cu_seqlens || !state_pool)) return GDN_ERR_NULL;
+    if (T > 0 && (!x || !dy || !dx)) return GDN_ERR_NULL;
+    if (N > 0 && !src_idx && d.pool_size < N) return GDN_ERR_SHAPE;
+    const uint64_t ws = conv_bwd_workspace_bytes(T, C, (int)K);
+    if (ws > 0 && !workspace) return GDN_ERR_NULL;
+    if (workspace_bytes < ws) return GDN_ERR_SHAPE;
+    const uintptr_t esz = d.io_dtype == GDN_BF16 ? 2 : 4;
+    if (!aligned(x, esz) || !aligned(state_pool, esz) || !aligned(w, 4) || !aligned(bias, 4) ||
+        !aligned(cu_seqlens, 4) || !aligned(src_idx, 4) || !aligned(dy, 4) || !aligned(dx, 4) || !aligned(dw, 4) ||
+        !aligned(dbias, 4) || !aligned(dstate, 4) || !aligned(workspace, 4))
+        return GDN_ERR_ALIGN;
+    const Range inputs[] = {range_of(x, (uint64_t)T * C * esz), range_of(w, (uint64_t)C * K * 4),
+                            range_of(bias, bias ? (uint64_t)C * 4 : 0),
+                            range_of(cu_seqlens, N > 0 ? (uint64_t)(N + 1) * 4 : 0),
+                            range_of(state_pool, (uint64_t)d.pool_size * C * (K - 1) * esz),
+                            range_of(src_idx, src_idx ? (uint64_t)N * 4 : 0), range_of(dy, (uint64_t)T * C * 4)};
+    const Range outputs[] = {range_of(dx, (uint64_t)T * C * 4), range_of(dw, (uint64_t)C * K * 4),
+                             range_of(dbias, dbias ? (uint64_t)C * 4 : 0),
+                             range_of(dstate, dstate ? (uint64_t)N * C * (K - 1) * 4 : 0),
+                             range_of(workspace, ws)};
+    for (size_t i = 0; i < 5; ++i) {
+        for (const Range &in : inputs)
+            if (overlap(outputs[i], in)) return GDN_ERR_ALIAS;
+        for (size_t j = i + 1; j < 5; ++j)
+            if (overlap(outputs[i], outputs[j])) return GDN_ERR_ALIAS;
+    }
+    ConvBwdParams p{};
+    p.x = x; p.w = w; p.bias = bias; p.cu_seqlens = cu_seqlens; p.src_idx = src_idx; p.state = state_pool;
+    p.dy = dy; p.dx = dx; p.dw = dw; p.dbias = dbias; p.dstate = dstate;
+    p.partial = static_cast<float *>(workspace);
+    p.total_tokens = T; p.n_seqs = (int32_t)N; p.channels = (int32_t)C; p.taps = (int32_t)K;
+    p.pool_size = d.pool_size; p.silu = (d.flags & GDN_CONV_SILU) ? 1 : 0;
+    const hipError_t e = launch_short_conv_backward(p, d.io_dtype, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 gdn_status gdn_bwd_workspace_size(const gdn_dims *dims, uint64_t *bytes) {
     using namespace gdn;
     if (!bytes) return GDN_ERR_NULL;

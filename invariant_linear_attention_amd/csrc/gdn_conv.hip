@@ -265,4 +265,232 @@ hipError_t launch_short_conv(const ConvParams &p, int io_dtype, hipStream_t s) {
     return io_dtype == GDN_BF16 ? launch_io<IoBf16>(p, s) : launch_io<IoF32>(p, s);
 }
 
+// ------------------------------------------------------------------------ backward
+//
+// Gradients of the convolution given dy = dL/dy (fp32):
+//     dz(t) = dy(t) * (sigmoid(z) (1 + z (1 - sigmoid(z))))   (SiLU; else dz = dy)
+//     dx(s) = sum_{i=0}^{K-1} w[K-1-i] dz(s + i)     (tokens of s's own sequence)
+//     dw[c][j] = sum_t dz(t) x(t - (K-1) + j),  dbias[c] = sum_t dz(t)
+//     dstate[n][c][m] = sum_{j<=m} w[j] dz(tb + m - j)   (the carried state's gradient)
+// with z recomputed exactly as the forward does.  One thread per channel walks a
+// block of kConvBwdTokens tokens and K - 1 more (so that the block's last tokens
+// see the dz they need), keeping the last K values of the input window, of dz and
+// of the sequence ends in registers.  dw and dbias are sums over all tokens: each
+// block writes its partial sums, added block by block afterwards.
+
+namespace {
+
+constexpr int kConvBwdTokens = 64;
+
+template <class IO, int K>
+__device__ __forceinline__ float conv_dz(const ConvBwdParams &p, const float (&wc)[K], float bc, const float (&win)[K],
+                                         float dy) {
+    float z = bc;
+#pragma unroll
+    for (int j = 0; j < K; ++j) z = __builtin_fmaf(wc[j], win[j], z);
+    if (!p.silu) return dy;
+    const float sg = sigmoid_f32(z);
+    return dy * (sg * (1.f + z * (1.f - sg)));
+}
+
+template <class IO>
+__device__ __forceinline__ float state_at(const ConvBwdParams &p, int n, int64_t c, int m, int M) {
+    const int64_t src = slot_of(p.src_idx, n, p.pool_size);
+    return src >= 0 ? IO::load1(p.state, ((size_t)src * p.channels + c) * M + m) : 0.f;
+}
+
+__device__ __forceinline__ int64_t bclamp_cu(const ConvBwdParams &p, int i) {
+    int64_t v = p.cu_seqlens[i];
+    return v < 0 ? 0 : (v > p.total_tokens ? p.total_tokens : v);
+}
+
+__device__ int bseq_of(const ConvBwdParams &p, int64_t t) {
+    int lo = 0, hi = p.n_seqs;  // the last n with cu[n] <= t, in [lo, hi)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (bclamp_cu(p, mid) <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+template <class IO, int K>
+__global__ __launch_bounds__(kConvThreads) void gdn_conv_bwd_kernel(ConvBwdParams p) {
+    constexpr int M = K - 1;
+    const int64_t c = (int64_t)blockIdx.y * kConvThreads + threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kConvBwdTokens;
+    if (c >= p.channels || t0 >= p.total_tokens) return;
+    const int64_t T = p.total_tokens, C = p.channels;
+    const int64_t t1 = t0 + kConvBwdTokens < T ? t0 + kConvBwdTokens : T;
+    float wc[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) wc[j] = p.w[c * K + j];
+    const float bc = p.bias ? p.bias[c] : 0.f;
+
+    int n = bseq_of(p, t0);
+    int64_t tb = bclamp_cu(p, n), te = bclamp_cu(p, n + 1);
+    // win[j] = input of token t - M + j (the state before the sequence's first token)
+    float win[K];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        const int64_t s = t0 - M + j;
+        win[j] = s >= tb ? IO::load1(p.x, (size_t)s * C + c) : state_at<IO>(p, n, c, (int)(s - tb + M), M);
+    }
+    // dzr[i] = dz of token t - M + i and er[i] = the end of its sequence (dz of tokens
+    // before the block is never used: their dx belongs to the block before)
+    float dzr[K];
+    int64_t er[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        dzr[i] = 0.f;
+        er[i] = 0;
+    }
+    float pw[K], pb = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) pw[j] = 0.f;
+    const int steps = (int)(t1 - t0) + M;
+    for (int i = 0; i < steps; ++i) {
+        const int64_t t = t0 + i;
+        float dz = 0.f;
+        int64_t et = T;
+        if (t < T) {
+            if (t >= te) {  // a new sequence (empty ones skipped): its state fills the window
+                while (n + 1 < p.n_seqs && bclamp_cu(p, n + 1) <= t) ++n;
+                tb = bclamp_cu(p, n);
+                te = bclamp_cu(p, n + 1);
+#pragma unroll
+                for (int j = 0; j < M; ++j) win[j] = state_at<IO>(p, n, c, j, M);
+            }
+            win[M] = IO::load1(p.x, (size_t)t * C + c);
+            dz = conv_dz<IO, K>(p, wc, bc, win, p.dy[(size_t)t * C + c]);
+            et = te;
+            if (t < t1) {  // this block's share of dw and dbias
+#pragma unroll
+                for (int j = 0; j < K; ++j) pw[j] = __builtin_fmaf(dz, win[j], pw[j]);
+                pb = pb + dz;
+            }
+#pragma unroll
+            for (int j = 0; j < M; ++j) win[j] = win[j + 1];
+        }
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            dzr[j] = dzr[j + 1];
+            er[j] = er[j + 1];
+        }
+        dzr[M] = dz;
+        er[M] = et;
+        const int64_t s = t - M;  // its dz and those of the M tokens after it are known
+        if (s >= t0 && s < t1) {
+            float dx = 0.f;
+#pragma unroll
+            for (int q = 0; q <= M; ++q)
+                if (s + q < er[0]) dx = __builtin_fmaf(wc[M - q], dzr[q], dx);
+            p.dx[(size_t)s * C + c] = dx;
+        }
+    }
+    float *part = p.partial + ((size_t)blockIdx.x * C + c) * (K + 1);
+#pragma unroll
+    for (int j = 0; j < K; ++j) part[j] = pw[j];
+    part[K] = pb;
+}
+
+// dw and dbias: the blocks' partial sums, block by block.
+template <int K>
+__global__ __launch_bounds__(kConvThreads) void gdn_conv_bwd_sum_kernel(ConvBwdParams p) {
+    const int64_t c = (int64_t)blockIdx.x * kConvThreads + threadIdx.x;
+    if (c >= p.channels) return;
+    const int64_t nblk = (p.total_tokens + kConvBwdTokens - 1) / kConvBwdTokens;
+    float acc[K + 1];
+#pragma unroll
+    for (int j = 0; j <= K; ++j) acc[j] = 0.f;
+    for (int64_t b = 0; b < nblk; ++b) {
+        const float *part = p.partial + ((size_t)b * p.channels + c) * (K + 1);
+#pragma unroll
+        for (int j = 0; j <= K; ++j) acc[j] = acc[j] + part[j];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) p.dw[c * K + j] = acc[j];
+    if (p.dbias) p.dbias[c] = acc[K];
+}
+
+// The carried state's gradient of (sequence blockIdx.y, channel): the window of its
+// first K - 1 tokens, dz recomputed as above.
+template <class IO, int K>
+__global__ __launch_bounds__(kConvThreads) void gdn_conv_bwd_state_kernel(ConvBwdParams p) {
+    constexpr int M = K - 1;
+    const int64_t c = (int64_t)blockIdx.x * kConvThreads + threadIdx.x;
+    const int n = blockIdx.y;
+    if (c >= p.channels) return;
+    const int64_t C = p.channels;
+    const int64_t tb = bclamp_cu(p, n);
+    int64_t te = bclamp_cu(p, n + 1);
+    te = te < tb ? tb : te;
+    const int64_t len = te - tb;
+    float wc[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) wc[j] = p.w[c * K + j];
+    const float bc = p.bias ? p.bias[c] : 0.f;
+    float win[K], dz[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) win[j] = state_at<IO>(p, n, c, j, M);
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        dz[i] = 0.f;
+        if (i < len) {
+            win[M] = IO::load1(p.x, (size_t)(tb + i) * C + c);
+            dz[i] = conv_dz<IO, K>(p, wc, bc, win, p.dy[(size_t)(tb + i) * C + c]);
+#pragma unroll
+            for (int j = 0; j < M; ++j) win[j] = win[j + 1];
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j <= m; ++j)
+            if (m - j < len) v = __builtin_fmaf(wc[j], dz[m - j], v);
+        p.dstate[((size_t)n * C + c) * M + m] = v;
+    }
+}
+
+template <class IO, int K>
+hipError_t conv_bwd_launch(const ConvBwdParams &p, hipStream_t s) {
+    const unsigned cblocks = (unsigned)((p.channels + kConvThreads - 1) / kConvThreads);
+    if (p.total_tokens > 0) {
+        const unsigned tblocks = (unsigned)((p.total_tokens + kConvBwdTokens - 1) / kConvBwdTokens);
+        hipLaunchKernelGGL((gdn_conv_bwd_kernel<IO, K>), dim3(tblocks, cblocks), dim3(kConvThreads), 0, s, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((gdn_conv_bwd_sum_kernel<K>), dim3(cblocks), dim3(kConvThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !p.dstate || p.n_seqs == 0) return e;
+    hipLaunchKernelGGL((gdn_conv_bwd_state_kernel<IO, K>), dim3(cblocks, (unsigned)p.n_seqs), dim3(kConvThreads), 0,
+                       s, p);
+    return hipGetLastError();
+}
+
+template <class IO>
+hipError_t conv_bwd_io(const ConvBwdParams &p, hipStream_t s) {
+    switch (p.taps) {
+        case 2: return conv_bwd_launch<IO, 2>(p, s);
+        case 3: return conv_bwd_launch<IO, 3>(p, s);
+        case 4: return conv_bwd_launch<IO, 4>(p, s);
+        case 5: return conv_bwd_launch<IO, 5>(p, s);
+        case 6: return conv_bwd_launch<IO, 6>(p, s);
+        case 7: return conv_bwd_launch<IO, 7>(p, s);
+        case 8: return conv_bwd_launch<IO, 8>(p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+uint64_t conv_bwd_workspace_bytes(int64_t T, int64_t C, int K) {
+    return (uint64_t)((T + kConvBwdTokens - 1) / kConvBwdTokens) * C * (K + 1) * 4;
+}
+
+hipError_t launch_short_conv_backward(const ConvBwdParams &p, int io_dtype, hipStream_t s) {
+    return io_dtype == GDN_BF16 ? conv_bwd_io<IoBf16>(p, s) : conv_bwd_io<IoF32>(p, s);
+}
+
 }  // namespace gdn

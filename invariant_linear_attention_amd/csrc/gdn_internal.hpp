@@ -71,6 +71,21 @@ struct ConvParams {
 };
 hipError_t launch_short_conv(const ConvParams &p, int io_dtype, hipStream_t s);
 
+// Kernel arguments of the convolution's backward (gdn_short_conv_backward).
+struct ConvBwdParams {
+    const void *x;                    // io dtype [T][C]
+    const float *w, *bias;            // [C][K], [C] or null
+    const int32_t *cu_seqlens, *src_idx;
+    const void *state;                // io dtype [P][C][K-1]: the states the forward read
+    const float *dy;                  // [T][C]
+    float *dx, *dw, *dbias, *dstate;  // [T][C], [C][K], [C] or null, [N][C][K-1] or null
+    float *partial;                   // workspace: per token block and channel, K + 1 partial sums
+    int64_t total_tokens;
+    int32_t n_seqs, channels, taps, pool_size, silu;
+};
+uint64_t conv_bwd_workspace_bytes(int64_t T, int64_t C, int K);
+hipError_t launch_short_conv_backward(const ConvBwdParams &p, int io_dtype, hipStream_t s);
+
 // Kernel arguments of the backward (gdn_bwd_varlen).  The four row passes and the
 // two finishing kernels share them; each reads and writes the parts it needs.
 struct BwdParams {

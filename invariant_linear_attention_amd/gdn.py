@@ -23,7 +23,8 @@ GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
            "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_bwd_varlen_noalloc", "gdn_fwd_chunked",
            "gdn_chunked_workspace_size", "gdn_bwd_chunked_workspace_size", "gdn_bwd_chunked", "gdn_preprocess",
-           "gdn_preprocess_backward", "gdn_status_string", "gdn_abi_version")
+           "gdn_preprocess_backward", "gdn_short_conv_backward_workspace_size", "gdn_short_conv_backward",
+           "gdn_status_string", "gdn_abi_version")
 
 GDN_CHUNK = 16
 
@@ -95,6 +96,11 @@ def load_library(path: str = LIBRARY):
         lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gdn_short_conv.restype = ctypes.c_int
         lib.gdn_short_conv.argtypes = [ctypes.POINTER(GdnConvDims), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gdn_short_conv_backward_workspace_size.restype = ctypes.c_int
+        lib.gdn_short_conv_backward_workspace_size.argtypes = [ctypes.POINTER(GdnConvDims),
+                                                               ctypes.POINTER(ctypes.c_uint64)]
+        lib.gdn_short_conv_backward.restype = ctypes.c_int
+        lib.gdn_short_conv_backward.argtypes = [ctypes.POINTER(GdnConvDims)] + [vp] * 12 + [ctypes.c_uint64, vp]
         lib.gdn_bwd_workspace_size.restype = ctypes.c_int
         lib.gdn_bwd_workspace_size.argtypes = [ctypes.POINTER(GdnDims), ctypes.POINTER(ctypes.c_uint64)]
         lib.gdn_bwd_varlen.restype = ctypes.c_int
@@ -714,3 +720,61 @@ def gdn_short_conv(x, w, cu_seqlens, state_pool, bias=None, src_idx=None, dst_id
     _check(lib.gdn_short_conv(ctypes.byref(dims), _ptr(x), _ptr(w), _ptr(bias), _ptr(cu_seqlens), _ptr(state_pool),
                               _ptr(src_idx), _ptr(dst_idx), _ptr(y), _stream_handle(stream)))
     return y
+
+
+def gdn_short_conv_backward_workspace_size(dims: GdnConvDims) -> int:
+    """Workspace bytes gdn_short_conv_backward needs for ``dims`` (host only)."""
+    n = ctypes.c_uint64(0)
+    _check(load_library().gdn_short_conv_backward_workspace_size(ctypes.byref(dims), ctypes.byref(n)))
+    return int(n.value)
+
+
+def gdn_short_conv_backward(x, w, cu_seqlens, state_pool, dy, bias=None, src_idx=None, silu: bool = True,
+                            workspace=None, grads=None, want_dstate: bool = True, stream=None):
+    """Backward of gdn_short_conv (see include/gdn.h): x, w, cu_seqlens, bias, src_idx
+    as the forward, ``state_pool`` the states it read, dy [T, C] fp32.  Returns a
+    dict of fp32 dx [T, C], dw [C, K], dbias [C] (None without ``bias``) and dstate
+    [N, C, K-1] (None unless ``want_dstate``)."""
+    import torch
+    if x is None or x.dim() != 2 or w is None or w.dim() != 2:
+        raise ValueError("x must be [T, C] and w [C, K]")
+    T, C = int(x.shape[0]), int(x.shape[1])
+    K = int(w.shape[1])
+    _shape(w, "w", (C, K))
+    _shape(bias, "bias", (C,))
+    _shape(dy, "dy", (T, C))
+    if cu_seqlens is None or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D [N+1] tensor")
+    N = int(cu_seqlens.numel()) - 1
+    if state_pool is None or state_pool.dim() != 3 or tuple(int(s) for s in state_pool.shape[1:]) != (C, K - 1):
+        raise ValueError("state_pool must be [P, C, K-1] = [P, %d, %d], got %s"
+                         % (C, K - 1, None if state_pool is None else tuple(state_pool.shape)))
+    _check_index(src_idx, "src_idx", N)
+    for name, t in (("x", x),):
+        _need(t, name)
+    _need(w, "w", torch.float32)
+    _need(bias, "bias", torch.float32)
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    _need(state_pool, "state_pool", x.dtype)
+    _need(src_idx, "src_idx", torch.int32)
+    _need(dy, "dy", torch.float32)
+    dims = GdnConvDims(n_seqs=N, channels=C, taps=K, io_dtype=_io_code(x), total_tokens=T,
+                       pool_size=int(state_pool.shape[0]), flags=GDN_CONV_SILU if silu else 0)
+    if workspace is None:
+        workspace = torch.empty(max(gdn_short_conv_backward_workspace_size(dims), 4), dtype=torch.uint8,
+                                device=x.device)
+    _need(workspace, "workspace", torch.uint8)
+    if grads is None:
+        f32 = dict(dtype=torch.float32, device=x.device)
+        grads = {"dx": torch.empty((T, C), **f32), "dw": torch.empty((C, K), **f32),
+                 "dbias": torch.empty((C,), **f32) if bias is not None else None,
+                 "dstate": torch.empty((N, C, K - 1), **f32) if want_dstate else None}
+    for name, shp in (("dx", (T, C)), ("dw", (C, K)), ("dbias", (C,)), ("dstate", (N, C, K - 1))):
+        if grads.get(name) is not None:
+            _shape(grads[name], name, shp)
+            _need(grads[name], name, torch.float32)
+    _check(load_library().gdn_short_conv_backward(
+        ctypes.byref(dims), _ptr(x), _ptr(w), _ptr(bias), _ptr(cu_seqlens), _ptr(state_pool), _ptr(src_idx),
+        _ptr(dy), _ptr(grads["dx"]), _ptr(grads["dw"]), _ptr(grads.get("dbias")), _ptr(grads.get("dstate")),
+        _ptr(workspace), int(workspace.numel()), _stream_handle(stream)))
+    return grads

@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"gdn_fwd_varlen", "gdn_fwd_varlen_train", "gdn_fwd_varlen_pool", "gdn_decode_step", "gdn_short_conv",
                           "gdn_query_plan", "gdn_bwd_workspace_size", "gdn_bwd_varlen", "gdn_bwd_varlen_noalloc",
                           "gdn_fwd_chunked", "gdn_chunked_workspace_size", "gdn_bwd_chunked_workspace_size",
-                          "gdn_bwd_chunked", "gdn_preprocess", "gdn_preprocess_backward", "gdn_status_string",
+                          "gdn_bwd_chunked", "gdn_preprocess", "gdn_preprocess_backward",
+                          "gdn_short_conv_backward_workspace_size", "gdn_short_conv_backward", "gdn_status_string",
                           "gdn_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -713,3 +714,61 @@ def test_preprocess_gate_needs_A_log_and_empty_calls(lib):
                     beta=None) == 0
     assert call_pre_bwd(lib, pre_dims(gated=False, total_tokens=0), q=None, k=None, a=None, b=None, dqn=None,
                         dkn=None, dg=None, dbeta=None, dq=None, dk=None, da=None, db=None) == 0
+
+
+# ------------------------------------------------------- convolution backward
+
+CB = {name: BASE + (150 + i) * MB for i, name in enumerate(
+    ["x", "w", "bias", "cu", "pool", "src", "dy", "dx", "dw", "db", "ds", "ws"])}
+
+
+def conv_dims(**kw):
+    from invariant_linear_attention_amd import gdn
+    a = dict(n_seqs=3, channels=64, taps=4, io_dtype=1, total_tokens=100, pool_size=3, flags=1)
+    a.update(kw)
+    return gdn.GdnConvDims(**a)
+
+
+def conv_ws(lib, dims):
+    n = ctypes.c_uint64(0)
+    rc = lib.gdn_short_conv_backward_workspace_size(ctypes.byref(dims), ctypes.byref(n))
+    return int(n.value) if rc == 0 else -rc
+
+
+def call_conv_bwd(lib, dims, ws_bytes=None, **over):
+    a = dict(CB)
+    a.update(over)
+    if ws_bytes is None:
+        ws_bytes = max(conv_ws(lib, dims), 0) if dims is not None else 0
+    return lib.gdn_short_conv_backward(ctypes.byref(dims) if dims is not None else None, a["x"], a["w"], a["bias"],
+                                       a["cu"], a["pool"], a["src"], a["dy"], a["dx"], a["dw"], a["db"], a["ds"],
+                                       a["ws"], ctypes.c_uint64(ws_bytes), None)
+
+
+def test_conv_backward_workspace_size(lib):
+    """K + 1 partial sums per channel and block of 64 tokens."""
+    for T, C, K in ((100, 64, 4), (64, 16, 2), (1, 8192, 8), (0, 32, 3)):
+        assert conv_ws(lib, conv_dims(total_tokens=T, channels=C, taps=K, n_seqs=1 if T else 0)) == \
+            (T + 63) // 64 * C * (K + 1) * 4
+    assert conv_ws(lib, conv_dims(taps=9)) == -2
+    assert lib.gdn_short_conv_backward_workspace_size(None, ctypes.byref(ctypes.c_uint64(0))) == 1
+
+
+@pytest.mark.parametrize("case,over,code", [
+    (dict(taps=1), {}, 2), (dict(taps=9), {}, 2), (dict(channels=0), {}, 2), (dict(pool_size=0), {}, 2),
+    (dict(flags=2), {}, 6), (dict(io_dtype=3), {}, 3), (dict(n_seqs=0), {}, 2),
+    (dict(pool_size=2), dict(src=None), 2),
+    ({}, dict(w=None), 1), ({}, dict(dw=None), 1), ({}, dict(cu=None), 1), ({}, dict(pool=None), 1),
+    ({}, dict(x=None), 1), ({}, dict(dy=None), 1), ({}, dict(dx=None), 1), ({}, dict(ws=None), 1),
+    ({}, dict(x=CB["x"] + 1), 4), ({}, dict(dy=CB["dy"] + 2), 4), ({}, dict(ws=CB["ws"] + 2), 4),
+    ({}, dict(dx=CB["x"]), 5), ({}, dict(dw=CB["w"]), 5), ({}, dict(ws=CB["dy"]), 5), ({}, dict(ds=CB["dx"]), 5),
+    ({}, dict(db=CB["pool"]), 5), ({}, dict(dx=CB["src"]), 5),
+])
+def test_conv_backward_rejects(lib, case, over, code):
+    assert call_conv_bwd(lib, conv_dims(**case), **over) == code
+
+
+def test_conv_backward_small_workspace(lib):
+    d = conv_dims()
+    assert call_conv_bwd(lib, d, ws_bytes=conv_ws(lib, d) - 1) == 2
+    assert call_conv_bwd(lib, None) == 1
