@@ -465,7 +465,51 @@ def main():
                  "roofline_frac": FLOPS_PER_TOKEN * T / (msf / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
         workloads["varlen_prefill_fused_preprocessing"] = rec_f
         got_fo, got_fs = outr.cpu(), hTr.cpu()
-        del rd, outr, hTr
+        # the preprocessing as a pass of its own and its backward (the fused layer's
+        # training path), on the same raw inputs: HBM-bound elementwise passes
+        pre_out = gdn.gdn_preprocess(rd[0], rd[1], rd[3], rd[4], pre=pre_f, stream=stream)
+        genp = torch.Generator().manual_seed(1008)
+        dqn = torch.randn(tuple(rw.q.shape), generator=genp).to(dev)
+        dkn = torch.randn(tuple(rw.q.shape), generator=genp).to(dev)
+        dgp = torch.randn(tuple(rw.g.shape), generator=genp).to(dev)
+        dbp = torch.randn(tuple(rw.g.shape), generator=genp).to(dev)
+        pre_g = gdn.gdn_preprocess_backward(rd[0], rd[1], rd[3], rd[4], dqn, dkn, dgp, dbp, pre=pre_f, stream=stream)
+
+        def pre_fwd(_i):
+            gdn.gdn_preprocess(rd[0], rd[1], rd[3], rd[4], pre=pre_f, out=pre_out, stream=stream)
+
+        def pre_bwd(_i):
+            gdn.gdn_preprocess_backward(rd[0], rd[1], rd[3], rd[4], dqn, dkn, dgp, dbp, pre=pre_f, grads=pre_g,
+                                        stream=stream)
+
+        per_pf, _, _ = time_launches(pre_fwd, args.steps, 5, stream)
+        per_pb, _, _ = time_launches(pre_bwd, args.steps, 5, stream)
+        qk_el, gb_el = 2.0 * rw.q.numel(), 2.0 * rw.g.numel()
+        pf_bytes = qk_el * 2 + gb_el * 4 + qk_el * 4 + gb_el * 4  # bf16 q, k and logits in; fp32 out
+        pb_bytes = qk_el * 2 + 2 * gb_el * 4 + qk_el * 4 + gb_el * 4 + qk_el * 4 + gb_el * 4 + gb_el * 2
+        rec_pp = {"tokens": T}
+        for name, per_x, nbytes in (("forward", per_pf, pf_bytes), ("backward", per_pb, pb_bytes)):
+            msx = float(np.median(per_x))
+            rec_pp[name] = {"ms_median": msx, "launch_ms_percentiles": percentiles(per_x),
+                            "roofline": {"bound": "hbm", "achieved": nbytes / (msx / 1e3) / 1e9,
+                                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                         "frac": nbytes / (msx / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                         "bytes_per_launch": nbytes, "traffic": None}}
+        workloads["preprocess_passes"] = rec_pp
+        pp_got = {k: v[:, 0:1].cpu() for k, v in pre_g.items() if k in ("dq", "dk")}
+        pp_got.update({k: pre_g[k].cpu() for k in ("da", "db", "dA_log", "ddt_bias")})
+        pp_in = (dqn.cpu(), dkn.cpu(), dgp.cpu(), dbp.cpu())
+        del rd, outr, hTr, pre_out, pre_g, dqn, dkn, dgp, dbp
+
+        def pre_check():
+            r = oracle.preprocess_backward(rw.q, rw.k, rw.g, rw.beta, *pp_in, A_log=rw.meta["A_log"],
+                                           dt_bias=rw.meta["dt_bias"], norm_qk=True)
+            out = {k: rel(pp_got[k].numpy(), r[k][:, 0:1]) for k in ("dq", "dk")}
+            out.update({k: rel(pp_got[k].numpy(), r[k]) for k in ("da", "db", "dA_log", "ddt_bias")})
+            return {"backward": out}
+        checks.append((rec_pp, "parity", pre_check))
+        progress("preprocessing passes %.3f / %.3f ms" % (rec_pp["forward"]["ms_median"],
+                                                         rec_pp["backward"]["ms_median"]))
 
         def fused_check():
             ro, rh = oracle.gdn_forward_fused(rw.q, rw.k, rw.v, rw.g, rw.beta, rw.cu_seqlens, rw.h0,
@@ -515,6 +559,7 @@ def main():
         xc256, wc256, bc256 = xc[:, :256].cpu(), wc[:256].cpu(), bc[:256].cpu()
         workloads["short_conv_decode_B256"] = {"latency_us_mean": float(np.mean(per_cd)) * 1e3,
                                                "launch_ms_percentiles": percentiles(per_cd)}
+        xc_keep = xc.cpu()
         del xc, yc, pool_c, xd, yd, pool_d
 
         def conv_check():
@@ -522,6 +567,35 @@ def main():
             return {"y_first256": rel(got_y.float().numpy(), ry)}
         checks.append((rec_c, "parity", conv_check))
         progress("short convolution %.3f ms" % msc)
+
+        # its backward on the same shape (x bf16 read, dy fp32 read, dx fp32 written)
+        xc = xc_keep.to(dev)
+        pool_c = torch.zeros((w.n_seqs, C, K - 1), dtype=torch.bfloat16, device=dev)
+        dyc = torch.randn((T, C), generator=torch.Generator().manual_seed(1009)).to(dev)
+        cg = gdn.gdn_short_conv_backward(xc, wc, d["cu"], pool_c, dyc, bias=bc, stream=stream)
+
+        def conv_bwd(_i):
+            gdn.gdn_short_conv_backward(xc, wc, d["cu"], pool_c, dyc, bias=bc, grads=cg, stream=stream)
+
+        per_cb, _, _ = time_launches(conv_bwd, args.steps, 5, stream)
+        mscb = float(np.median(per_cb))
+        cbb = T * C * (2.0 + 4.0 + 4.0)
+        rec_cb = {"tokens": T, "channels": C, "taps": K, "ms_median": mscb, "launch_ms_percentiles": percentiles(per_cb),
+                  "roofline": {"bound": "hbm", "achieved": cbb / (mscb / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": cbb / (mscb / 1e3) / 1e9 / HBM_PEAK_GBS,
+                               "bytes_per_launch": cbb, "traffic": None}}
+        workloads["short_conv_backward"] = rec_cb
+        cg_got = {"dx": cg["dx"][:, :256].cpu(), "dw": cg["dw"][:256].cpu(), "dbias": cg["dbias"][:256].cpu(),
+                  "dstate": cg["dstate"][:, :256].cpu()}
+        dy256 = dyc[:, :256].cpu()
+        del xc, pool_c, dyc, cg
+
+        def conv_bwd_check():
+            r = oracle.short_conv_backward(xc256, wc256, w.cu_seqlens, dy256, bias=bc256,
+                                           state=torch.zeros((w.n_seqs, 256, K - 1)))
+            return {"first256": {k: rel(cg_got[k].numpy(), r[k]) for k in cg_got}}
+        checks.append((rec_cb, "parity", conv_bwd_check))
+        progress("short convolution backward %.3f ms" % mscb)
 
         lc = synth.long_context(1003)
         prefill_line("long_context_65536", lc)
@@ -771,10 +845,10 @@ def main():
     def line_ok(par):
         ok = True
         for v in par.values():
-            if isinstance(v, dict) and "dq" in v:
-                ok = ok and grads_ok(v)
-            elif isinstance(v, dict):
+            if isinstance(v, dict) and ("out" in v or "state" in v):
                 ok = ok and v.get("out", 0.0) <= 2e-3 and v.get("state", 0.0) <= 1e-4
+            elif isinstance(v, dict):  # gradients
+                ok = ok and grads_ok(v)
             else:
                 ok = ok and v <= 2e-3
         return ok
