@@ -272,11 +272,12 @@ hipError_t launch_short_conv(const ConvParams &p, int io_dtype, hipStream_t s) {
 //     dx(s) = sum_{i=0}^{K-1} w[K-1-i] dz(s + i)     (tokens of s's own sequence)
 //     dw[c][j] = sum_t dz(t) x(t - (K-1) + j),  dbias[c] = sum_t dz(t)
 //     dstate[n][c][m] = sum_{j<=m} w[j] dz(tb + m - j)   (the carried state's gradient)
-// with z recomputed exactly as the forward does.  One thread per channel walks a
+// with z recomputed exactly as the forward does.  One thread takes four consecutive
+// channels (one, where rows do not start on a four-channel boundary) and walks a
 // block of kConvBwdTokens tokens and K - 1 more (so that the block's last tokens
 // see the dz they need), keeping the last K values of the input window, of dz and
 // of the sequence ends in registers.  dw and dbias are sums over all tokens: each
-// block writes its partial sums, added block by block afterwards.
+// block writes its partial sums, added afterwards in a fixed order.
 
 namespace {
 
@@ -313,103 +314,348 @@ __device__ int bseq_of(const ConvBwdParams &p, int64_t t) {
     return lo;
 }
 
-template <class IO, int K>
-__global__ __launch_bounds__(kConvThreads) void gdn_conv_bwd_kernel(ConvBwdParams p) {
-    constexpr int M = K - 1;
-    const int64_t c = (int64_t)blockIdx.y * kConvThreads + threadIdx.x;
-    const int64_t t0 = (int64_t)blockIdx.x * kConvBwdTokens;
-    if (c >= p.channels || t0 >= p.total_tokens) return;
-    const int64_t T = p.total_tokens, C = p.channels;
-    const int64_t t1 = t0 + kConvBwdTokens < T ? t0 + kConvBwdTokens : T;
-    float wc[K];
+// V consecutive channels of one input element (V = 4: one 8- or 16-byte load).
+template <class IO, int V>
+__device__ __forceinline__ void load_chan(const void *base, size_t idx, float (&f)[V]) {
+    if constexpr (V == 4) {
+        const float4 r = IO::load4(base, idx);
+        f[0] = r.x;
+        f[1] = r.y;
+        f[2] = r.z;
+        f[3] = r.w;
+    } else {
 #pragma unroll
-    for (int j = 0; j < K; ++j) wc[j] = p.w[c * K + j];
-    const float bc = p.bias ? p.bias[c] : 0.f;
+        for (int v = 0; v < V; ++v) f[v] = IO::load1(base, idx + v);
+    }
+}
 
-    int n = bseq_of(p, t0);
-    int64_t tb = bclamp_cu(p, n), te = bclamp_cu(p, n + 1);
-    // win[j] = input of token t - M + j (the state before the sequence's first token)
-    float win[K];
+template <int V>
+__device__ __forceinline__ void load_chan_f32(const float *base, size_t idx, float (&f)[V]) {
+    if constexpr (V == 4) {
+        const float4 r = *reinterpret_cast<const float4 *>(base + idx);
+        f[0] = r.x;
+        f[1] = r.y;
+        f[2] = r.z;
+        f[3] = r.w;
+    } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v) f[v] = base[idx + v];
+    }
+}
+
+template <int V>
+__device__ __forceinline__ void store_chan_f32(float *base, size_t idx, const float (&f)[V]) {
+    if constexpr (V == 4) {
+        *reinterpret_cast<float4 *>(base + idx) = make_float4(f[0], f[1], f[2], f[3]);
+    } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v) base[idx + v] = f[v];
+    }
+}
+
+// A token block that lies inside one sequence together with the K - 1 tokens before
+// it and the K - 1 after it: no sequence end to watch, so the window is indexed by
+// position within a group of G tokens and only its last K - 1 entries carry over.
+// Every row address is the token's (uniform) plus the lane's 32-bit byte offset;
+// dy (read once) and dx (written once) go past the caches with nontemporal hints.
+// The arithmetic, operation by operation, is the general path's.
+template <class IO, int K, int G>
+__device__ __forceinline__ void conv_bwd_interior(const ConvBwdParams &p, int64_t t0, int64_t c0,
+                                                  const float (&wc)[4][K], const float (&bc)[4], float (&pw)[4][K],
+                                                  float (&pb)[4]) {
+    constexpr int M = K - 1, V = 4, W = M + (G > M ? G : M);
+    const size_t C = (size_t)p.channels;
+    const uint32_t xo = (uint32_t)c0 * IO::ESZ, fo = (uint32_t)c0 * 4;
+    const char *xb = static_cast<const char *>(p.x);
+    const char *db = reinterpret_cast<const char *>(p.dy);
+    char *ob = reinterpret_cast<char *>(p.dx);
+    auto ldx = [&](int64_t t, float (&f)[V]) {
+        const float4 r = IO::load4(xb + (size_t)t * C * IO::ESZ + xo, 0);
+        f[0] = r.x;
+        f[1] = r.y;
+        f[2] = r.z;
+        f[3] = r.w;
+    };
+    auto lddy = [&](int64_t t, float (&f)[V]) {
+        const float4 *q = reinterpret_cast<const float4 *>(db + (size_t)t * C * 4 + fo);
+        const float4 r = make_float4(__builtin_nontemporal_load(&q->x), __builtin_nontemporal_load(&q->y),
+                                     __builtin_nontemporal_load(&q->z), __builtin_nontemporal_load(&q->w));
+        f[0] = r.x;
+        f[1] = r.y;
+        f[2] = r.z;
+        f[3] = r.w;
+    };
+    auto stdx = [&](int64_t s, const float (&f)[V]) {
+        float4 *q = reinterpret_cast<float4 *>(ob + (size_t)s * C * 4 + fo);
+        __builtin_nontemporal_store(f[0], &q->x);
+        __builtin_nontemporal_store(f[1], &q->y);
+        __builtin_nontemporal_store(f[2], &q->z);
+        __builtin_nontemporal_store(f[3], &q->w);
+    };
+    // xs[v][i] = x(tg - M + i), ds[v][i] = dz(tg - M + i) for the group starting at tg
+    float xs[V][W], ds[V][W];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        float f[V];
+        ldx(t0 - M + j, f);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            xs[v][j] = f[v];
+            ds[v][j] = 0.f;
+        }
+    }
+    for (int g0 = 0; g0 < kConvBwdTokens; g0 += G) {
+        const int64_t tg = t0 + g0;
+        float dr[G][V];
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            float f[V];
+            ldx(tg + u, f);
+            lddy(tg + u, dr[u]);
+#pragma unroll
+            for (int v = 0; v < V; ++v) xs[v][M + u] = f[v];
+        }
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                float win[K];
+#pragma unroll
+                for (int j = 0; j < K; ++j) win[j] = xs[v][u + j];
+                const float dz = conv_dz<IO, K>(p, wc[v], bc[v], win, dr[u][v]);
+                ds[v][M + u] = dz;
+#pragma unroll
+                for (int j = 0; j < K; ++j) pw[v][j] = __builtin_fmaf(dz, win[j], pw[v][j]);
+                pb[v] = pb[v] + dz;
+            }
+            if (g0 + u >= M) {  // dx of s = tg + u - M: dz(s .. s + M) are ds[u .. u + M]
+                float dx[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    dx[v] = 0.f;
+#pragma unroll
+                    for (int q = 0; q <= M; ++q) dx[v] = __builtin_fmaf(wc[v][M - q], ds[v][u + q], dx[v]);
+                }
+                stdx(tg + u - M, dx);
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+#pragma unroll
+            for (int j = 0; j < M; ++j) {
+                xs[v][j] = xs[v][G + j];
+                ds[v][j] = ds[v][G + j];
+            }
+        }
+    }
+    // the M tokens after the block: their dz (outside this block's sums) completes
+    // the dx of the block's last M tokens
+    const int64_t t1 = t0 + kConvBwdTokens;
+    float dr[M][V];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        float f[V];
+        ldx(t1 + i, f);
+        lddy(t1 + i, dr[i]);
+#pragma unroll
+        for (int v = 0; v < V; ++v) xs[v][M + i] = f[v];
+    }
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            float win[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) win[j] = xs[v][i + j];
+            ds[v][M + i] = conv_dz<IO, K>(p, wc[v], bc[v], win, dr[i][v]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        float dx[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            dx[v] = 0.f;
+#pragma unroll
+            for (int q = 0; q <= M; ++q) dx[v] = __builtin_fmaf(wc[v][M - q], ds[v][i + q], dx[v]);
+        }
+        stdx(t1 - M + i, dx);
+    }
+}
+
+// Any token block: the window refills from a state slot where a sequence starts, and
+// dx sums only the dz of its own sequence.
+template <class IO, int K, int V>
+__device__ __forceinline__ void conv_bwd_general(const ConvBwdParams &p, int64_t t0, int64_t t1, int64_t c0, int n,
+                                                 int64_t tb, int64_t te, const float (&wc)[V][K], const float (&bc)[V],
+                                                 float (&pw)[V][K], float (&pb)[V]) {
+    constexpr int M = K - 1, G = V == 4 ? 2 : (K <= 4 ? 8 : 4);
+    const int64_t T = p.total_tokens, C = p.channels;
+    // win[v][j] = input of token t - M + j (the state before the sequence's first token)
+    float win[V][K];
 #pragma unroll
     for (int j = 0; j < M; ++j) {
         const int64_t s = t0 - M + j;
-        win[j] = s >= tb ? IO::load1(p.x, (size_t)s * C + c) : state_at<IO>(p, n, c, (int)(s - tb + M), M);
+        if (s >= tb) {
+            float f[V];
+            load_chan<IO, V>(p.x, (size_t)s * C + c0, f);
+#pragma unroll
+            for (int v = 0; v < V; ++v) win[v][j] = f[v];
+        } else {
+#pragma unroll
+            for (int v = 0; v < V; ++v) win[v][j] = state_at<IO>(p, n, c0 + v, (int)(s - tb + M), M);
+        }
     }
-    // dzr[i] = dz of token t - M + i and er[i] = the end of its sequence (dz of tokens
-    // before the block is never used: their dx belongs to the block before)
-    float dzr[K];
+    // dzr[v][i] = dz of token t - M + i and er[i] = the end of its sequence (dz of
+    // tokens before the block is never used: their dx belongs to the block before)
+    float dzr[V][K];
     int64_t er[K];
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-        dzr[i] = 0.f;
-        er[i] = 0;
-    }
-    float pw[K], pb = 0.f;
+    for (int i = 0; i < K; ++i) er[i] = 0;
 #pragma unroll
-    for (int j = 0; j < K; ++j) pw[j] = 0.f;
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int i = 0; i < K; ++i) dzr[v][i] = 0.f;
+    }
     const int steps = (int)(t1 - t0) + M;
-    for (int i = 0; i < steps; ++i) {
-        const int64_t t = t0 + i;
-        float dz = 0.f;
-        int64_t et = T;
-        if (t < T) {
-            if (t >= te) {  // a new sequence (empty ones skipped): its state fills the window
-                while (n + 1 < p.n_seqs && bclamp_cu(p, n + 1) <= t) ++n;
-                tb = bclamp_cu(p, n);
-                te = bclamp_cu(p, n + 1);
+    for (int g0 = 0; g0 < steps; g0 += G) {
+        float xr[G][V], dr[G][V];
 #pragma unroll
-                for (int j = 0; j < M; ++j) win[j] = state_at<IO>(p, n, c, j, M);
+        for (int u = 0; u < G; ++u) {
+            const int64_t t = t0 + g0 + u;
+            if (g0 + u < steps && t < T) {
+                load_chan<IO, V>(p.x, (size_t)t * C + c0, xr[u]);
+                load_chan_f32<V>(p.dy, (size_t)t * C + c0, dr[u]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) xr[u][v] = dr[u][v] = 0.f;
             }
-            win[M] = IO::load1(p.x, (size_t)t * C + c);
-            dz = conv_dz<IO, K>(p, wc, bc, win, p.dy[(size_t)t * C + c]);
-            et = te;
-            if (t < t1) {  // this block's share of dw and dbias
-#pragma unroll
-                for (int j = 0; j < K; ++j) pw[j] = __builtin_fmaf(dz, win[j], pw[j]);
-                pb = pb + dz;
-            }
-#pragma unroll
-            for (int j = 0; j < M; ++j) win[j] = win[j + 1];
         }
 #pragma unroll
-        for (int j = 0; j < M; ++j) {
-            dzr[j] = dzr[j + 1];
-            er[j] = er[j + 1];
-        }
-        dzr[M] = dz;
-        er[M] = et;
-        const int64_t s = t - M;  // its dz and those of the M tokens after it are known
-        if (s >= t0 && s < t1) {
-            float dx = 0.f;
+        for (int u = 0; u < G; ++u) {
+            if (g0 + u < steps) {
+                const int64_t t = t0 + g0 + u;
+                float dz[V];
+                int64_t et = T;
 #pragma unroll
-            for (int q = 0; q <= M; ++q)
-                if (s + q < er[0]) dx = __builtin_fmaf(wc[M - q], dzr[q], dx);
-            p.dx[(size_t)s * C + c] = dx;
+                for (int v = 0; v < V; ++v) dz[v] = 0.f;
+                if (t < T) {
+                    if (t >= te) {  // a new sequence (empty ones skipped): its state fills the window
+                        while (n + 1 < p.n_seqs && bclamp_cu(p, n + 1) <= t) ++n;
+                        tb = bclamp_cu(p, n);
+                        te = bclamp_cu(p, n + 1);
+#pragma unroll
+                        for (int v = 0; v < V; ++v) {
+#pragma unroll
+                            for (int j = 0; j < M; ++j) win[v][j] = state_at<IO>(p, n, c0 + v, j, M);
+                        }
+                    }
+                    et = te;
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        win[v][M] = xr[u][v];
+                        dz[v] = conv_dz<IO, K>(p, wc[v], bc[v], win[v], dr[u][v]);
+                        if (t < t1) {  // this block's share of dw and dbias
+#pragma unroll
+                            for (int j = 0; j < K; ++j) pw[v][j] = __builtin_fmaf(dz[v], win[v][j], pw[v][j]);
+                            pb[v] = pb[v] + dz[v];
+                        }
+#pragma unroll
+                        for (int j = 0; j < M; ++j) win[v][j] = win[v][j + 1];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < M; ++j) er[j] = er[j + 1];
+                er[M] = et;
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+#pragma unroll
+                    for (int j = 0; j < M; ++j) dzr[v][j] = dzr[v][j + 1];
+                    dzr[v][M] = dz[v];
+                }
+                const int64_t s = t - M;  // its dz and those of the M tokens after it are known
+                if (s >= t0 && s < t1) {
+                    float dx[V];
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        dx[v] = 0.f;
+#pragma unroll
+                        for (int q = 0; q <= M; ++q)
+                            if (s + q < er[0]) dx[v] = __builtin_fmaf(wc[v][M - q], dzr[v][q], dx[v]);
+                    }
+                    store_chan_f32<V>(p.dx, (size_t)s * C + c0, dx);
+                }
+            }
         }
     }
-    float *part = p.partial + ((size_t)blockIdx.x * C + c) * (K + 1);
-#pragma unroll
-    for (int j = 0; j < K; ++j) part[j] = pw[j];
-    part[K] = pb;
 }
 
-// dw and dbias: the blocks' partial sums, block by block.
+// One thread: V consecutive channels of one token block.  In both paths the x and
+// dy rows of G tokens are loaded together ahead of their use (the token loop's
+// branches depend only on the token, so they are uniform across the workgroup).
+template <class IO, int K, int V>
+__global__ __launch_bounds__(kConvThreads) void gdn_conv_bwd_kernel(ConvBwdParams p) {
+    constexpr int M = K - 1;
+    const int64_t c0 = ((int64_t)blockIdx.y * kConvThreads + threadIdx.x) * V;
+    const int64_t t0 = (int64_t)blockIdx.x * kConvBwdTokens;
+    if (c0 >= p.channels || t0 >= p.total_tokens) return;
+    const int64_t T = p.total_tokens, C = p.channels;
+    const int64_t t1 = t0 + kConvBwdTokens < T ? t0 + kConvBwdTokens : T;
+    float wc[V][K], bc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) wc[v][j] = p.w[(c0 + v) * K + j];
+        bc[v] = p.bias ? p.bias[c0 + v] : 0.f;
+    }
+
+    int n = bseq_of(p, t0);
+    int64_t tb = bclamp_cu(p, n), te = bclamp_cu(p, n + 1);
+    float pw[V][K], pb[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int i = 0; i < K; ++i) pw[v][i] = 0.f;
+        pb[v] = 0.f;
+    }
+    if (V == 4 && tb <= t0 - M && t0 + kConvBwdTokens + M <= te) {
+        if constexpr (V == 4) conv_bwd_interior<IO, K, 4>(p, t0, c0, wc, bc, pw, pb);
+    } else {
+        conv_bwd_general<IO, K, V>(p, t0, t1, c0, n, tb, te, wc, bc, pw, pb);
+    }
+    // partial sums, [block][K + 1][C]: the summing kernel reads them channel-contiguous
+    float *part = p.partial + (size_t)blockIdx.x * (K + 1) * C + c0;
+#pragma unroll
+    for (int j = 0; j <= K; ++j) {
+        float f[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) f[v] = j < K ? pw[v][j] : pb[v];
+        store_chan_f32<V>(part + (size_t)j * C, 0, f);
+    }
+}
+
+// dw and dbias from the blocks' partial sums: a workgroup takes 64 channels of one
+// sum (a tap or the bias); its four waves add a quarter of the blocks each, in block
+// order, and the quarters meet as (q0 + q1) + (q2 + q3).
 template <int K>
 __global__ __launch_bounds__(kConvThreads) void gdn_conv_bwd_sum_kernel(ConvBwdParams p) {
-    const int64_t c = (int64_t)blockIdx.x * kConvThreads + threadIdx.x;
-    if (c >= p.channels) return;
+    __shared__ float qs[4][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, j = blockIdx.y;
+    const int64_t c = (int64_t)blockIdx.x * 64 + lane, C = p.channels;
     const int64_t nblk = (p.total_tokens + kConvBwdTokens - 1) / kConvBwdTokens;
-    float acc[K + 1];
-#pragma unroll
-    for (int j = 0; j <= K; ++j) acc[j] = 0.f;
-    for (int64_t b = 0; b < nblk; ++b) {
-        const float *part = p.partial + ((size_t)b * p.channels + c) * (K + 1);
-#pragma unroll
-        for (int j = 0; j <= K; ++j) acc[j] = acc[j] + part[j];
+    const int64_t b0 = nblk * wv / 4, b1 = nblk * (wv + 1) / 4;
+    float acc = 0.f;
+    if (c < C) {
+        const float *part = p.partial + (size_t)j * C + c;
+#pragma unroll 8
+        for (int64_t b = b0; b < b1; ++b) acc = acc + part[(size_t)b * (K + 1) * C];
     }
-#pragma unroll
-    for (int j = 0; j < K; ++j) p.dw[c * K + j] = acc[j];
-    if (p.dbias) p.dbias[c] = acc[K];
+    qs[wv][lane] = acc;
+    __syncthreads();
+    if (wv != 0 || c >= C) return;
+    const float s = (qs[0][lane] + qs[1][lane]) + (qs[2][lane] + qs[3][lane]);
+    if (j < K) p.dw[c * K + j] = s;
+    else if (p.dbias) p.dbias[c] = s;
 }
 
 // The carried state's gradient of (sequence blockIdx.y, channel): the window of its
@@ -456,12 +702,22 @@ template <class IO, int K>
 hipError_t conv_bwd_launch(const ConvBwdParams &p, hipStream_t s) {
     const unsigned cblocks = (unsigned)((p.channels + kConvThreads - 1) / kConvThreads);
     if (p.total_tokens > 0) {
+        // four channels a thread where every row starts on a 4-channel boundary
+        const bool vec4 = p.channels % 4 == 0 && (uintptr_t)p.x % (4 * IO::ESZ) == 0 &&
+                          (uintptr_t)p.dy % 16 == 0 && (uintptr_t)p.dx % 16 == 0 && (uintptr_t)p.partial % 16 == 0;
         const unsigned tblocks = (unsigned)((p.total_tokens + kConvBwdTokens - 1) / kConvBwdTokens);
-        hipLaunchKernelGGL((gdn_conv_bwd_kernel<IO, K>), dim3(tblocks, cblocks), dim3(kConvThreads), 0, s, p);
+        if (vec4) {
+            const unsigned c4 = (unsigned)((p.channels / 4 + kConvThreads - 1) / kConvThreads);
+            hipLaunchKernelGGL((gdn_conv_bwd_kernel<IO, K, 4>), dim3(tblocks, c4), dim3(kConvThreads), 0, s, p);
+        } else {
+            hipLaunchKernelGGL((gdn_conv_bwd_kernel<IO, K, 1>), dim3(tblocks, cblocks), dim3(kConvThreads), 0, s,
+                               p);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((gdn_conv_bwd_sum_kernel<K>), dim3(cblocks), dim3(kConvThreads), 0, s, p);
+    hipLaunchKernelGGL((gdn_conv_bwd_sum_kernel<K>), dim3((unsigned)((p.channels + 63) / 64), (unsigned)(K + 1)),
+                       dim3(kConvThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.dstate || p.n_seqs == 0) return e;
     hipLaunchKernelGGL((gdn_conv_bwd_state_kernel<IO, K>), dim3(cblocks, (unsigned)p.n_seqs), dim3(kConvThreads), 0,

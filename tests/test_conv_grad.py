@@ -58,6 +58,19 @@ def test_parity(gpu, K, io, silu):
         assert e <= 1e-5, (k, e)
 
 
+@pytest.mark.parametrize("io", [torch.bfloat16, torch.float32])
+def test_channels_off_the_four_channel_grid(gpu, io):
+    """A channel count that is no multiple of four takes the one-channel-a-thread
+    kernel; it gives the same gradients."""
+    from oracle import oracle
+    lengths = [37, 1, 0, 150, 3]
+    x, w, bias, state, dy, cu = case(23, lengths, C=13, K=4, io=io)
+    r = run(gpu, x, w, bias, state, dy, cu)
+    ref = oracle.short_conv_backward(x, w, cu, dy, bias=bias, state=state, silu=True)
+    for k in ("dx", "dw", "dbias", "dstate"):
+        assert rel(r[k].cpu(), ref[k]) <= 1e-5, k
+
+
 def test_slots_no_bias_and_no_state_gradient(gpu):
     """src_idx picks state slots (an out-of-range entry is the zero state); without
     bias and dstate only dx and dw are written."""
