@@ -486,7 +486,8 @@ def main():
         per_pb, _, _ = time_launches(pre_bwd, args.steps, 5, stream)
         qk_el, gb_el = 2.0 * rw.q.numel(), 2.0 * rw.g.numel()
         pf_bytes = qk_el * 2 + gb_el * 4 + qk_el * 4 + gb_el * 4  # bf16 q, k and logits in; fp32 out
-        pb_bytes = qk_el * 2 + 2 * gb_el * 4 + qk_el * 4 + gb_el * 4 + qk_el * 4 + gb_el * 4 + gb_el * 2
+        # backward: bf16 q, k, fp32 dqn, dkn in and dq, dk out; logits, dg, dbeta in and da, db out
+        pb_bytes = qk_el * 2 + qk_el * 4 + qk_el * 4 + gb_el * 4 * 3
         rec_pp = {"tokens": T}
         for name, per_x, nbytes in (("forward", per_pf, pf_bytes), ("backward", per_pb, pb_bytes)):
             msx = float(np.median(per_x))

@@ -299,8 +299,9 @@ gdn_status gdn_short_conv(const gdn_conv_dims *dims, const void *x, const float 
  *     dw[c][j] = sum_t dz(t) x(t - (K-1) + j),   dbias[c] = sum_t dz(t)
  *     dstate[n][c][m] = sum_{j <= m} w[c][j] dz(t_n + m - j)  (t_n: sequence n's first token)
  *
- * dw and dbias sum over every token of the call (blocks of 64 tokens, then the
- * blocks in order); everything else is per sequence.  The state written by the
+ * dw and dbias sum over every token of the call (a partial sum per 64-token
+ * block; per channel, four quarters of the blocks each added in block order, then
+ * (q0 + q1) + (q2 + q3)); everything else is per sequence.  The state written by the
  * forward is a copy of inputs for the next call, not differentiated here.
  *
  *   x, w, bias, cu_seqlens, src_idx : as gdn_short_conv
@@ -511,10 +512,13 @@ gdn_status gdn_fwd_chunked(const gdn_dims *dims,
  *               (the dk term only when hv > hk or P > 1, the last when P > 1) and
  *               4.3 KB per (chunk, value head).
  * dk must be 64 or 128, dv 32, 64 or 128 and hv / hk at most 16 (else
- * GDN_ERR_UNSUPPORTED, as are dims->pre and plan_lanes).  plan_rows sets P (0 =
- * automatic: 2 for dv = 128, else 1; 2 needs dv >= 64) and plan_waves (0, 1, 2
- * or 4) the forward walk's waves per 16-row tile, which changes no bit.  Other
- * errors as gdn_bwd_varlen.
+ * GDN_ERR_UNSUPPORTED, as is dims->pre).  plan_rows sets P (0 = automatic: 2 for
+ * dv = 128, else 1; 2 needs dv >= 64), plan_waves (0, 1, 2 or 4) the forward
+ * walk's waves per 16-row tile, and plan_lanes 0 (automatic) or 1 (the plain
+ * reverse walk: for dv = 128 in two parts the automatic choice overlaps the
+ * chunk-recurrence waves of one chunk with the gradient waves of the next); the
+ * waves and the reverse walk's form change no bit.  plan_lanes above 1 is
+ * GDN_ERR_UNSUPPORTED.  Other errors as gdn_bwd_varlen.
  */
 gdn_status gdn_bwd_chunked_workspace_size(const gdn_dims *dims, uint64_t *bytes);
 
