@@ -854,11 +854,19 @@ gdn_status gdn_bwd_chunked(const gdn_dims *dims, const void *q, const void *k, c
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+// The preprocessing passes' 1-D grids: q/k rows, gate elements, token blocks.
+static bool pre_grid_fits(const gdn_dims &d) {
+    const int64_t T = d.total_tokens;
+    return (T * d.hk * (d.dk / 4) + 255) / 256 <= 0x7FFFFFFFll && (T * d.hv + 255) / 256 <= 0x7FFFFFFFll &&
+           (T + 63) / 64 <= 0x7FFFFFFFll;
+}
+
 gdn_status gdn_preprocess(const gdn_dims *dims, const void *q, const void *k, const float *a, const float *b,
                           float *qn, float *kn, float *g, float *beta, void *stream) {
     using namespace gdn;
     const gdn_status st = check_common(dims);
     if (st != GDN_OK) return st;
+    if (!pre_grid_fits(*dims)) return GDN_ERR_SHAPE;
     const gdn_dims &d = *dims;
     const int64_t T = d.total_tokens;
     if (T == 0) return GDN_OK;
@@ -899,6 +907,7 @@ gdn_status gdn_preprocess_backward(const gdn_dims *dims, const void *q, const vo
     using namespace gdn;
     const gdn_status st = check_common(dims);
     if (st != GDN_OK) return st;
+    if (!pre_grid_fits(*dims)) return GDN_ERR_SHAPE;
     const gdn_dims &d = *dims;
     const int64_t T = d.total_tokens;
     const bool gated = d.pre && (d.pre->flags & GDN_PRE_GATE_LOGITS);

@@ -111,22 +111,51 @@ __global__ __launch_bounds__(kPreThreads) void gdn_pre_gate_kernel(PreParams p) 
     }
 }
 
-// dA_log[h] = sum_t dg g and ddt_bias[h] = sum_t da: one workgroup per value head;
-// thread i adds tokens i, i + 256, ... in order, then the threads' sums meet in a
-// fixed tree (i with i + 128, then i with i + 64, ...).
-__global__ __launch_bounds__(kPreThreads) void gdn_pre_param_grad_kernel(PreParams p) {
+// dA_log[h] = sum_t dg g and ddt_bias[h] = sum_t da, in two launches.  First, per
+// block of kParamTok tokens: lane h of each of four waves adds its head's terms of
+// every fourth token in token order (the lanes read consecutive heads of a token
+// row), and the waves' sums meet as (w0 + w1) + (w2 + w3); the block sums go to the
+// da and db buffers, head-major, before the gate kernel writes those.  Then one
+// workgroup per head adds its blocks: thread i takes blocks i, i + 256, ... in
+// order, and the threads' sums meet in a fixed halving tree.
+constexpr int kParamTok = 64;
+
+__global__ __launch_bounds__(256) void gdn_pre_param_part_kernel(PreParams p) {
+    __shared__ float ps[2][4][64];
+    const int64_t blk = blockIdx.x, nblk = gridDim.x;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int h = blockIdx.y * 64 + lane;
+    float a_acc = 0.f, d_acc = 0.f;
+    if (h < p.hv) {
+        const float amp = gate_amplitude(p.A_log[h]);
+        const float dtb = p.dt_bias ? p.dt_bias[h] : 0.f;
+        const int64_t t0 = blk * kParamTok;
+        const int64_t t1 = t0 + kParamTok < p.total_tokens ? t0 + kParamTok : p.total_tokens;
+#pragma unroll 4
+        for (int64_t t = t0 + wv; t < t1; t += 4) {
+            const size_t i = (size_t)t * p.hv + h;
+            const float dg = p.dg[i], a = p.a[i];
+            const float g = gate_from_logit(amp, dtb, a);
+            const float da = dg * (-amp * sigmoid_f32(a + dtb));
+            a_acc = a_acc + dg * g;
+            d_acc = d_acc + da;
+        }
+    }
+    ps[0][wv][lane] = a_acc;
+    ps[1][wv][lane] = d_acc;
+    __syncthreads();
+    if (wv != 0 || h >= p.hv) return;
+    p.da[(size_t)h * nblk + blk] = (ps[0][0][lane] + ps[0][1][lane]) + (ps[0][2][lane] + ps[0][3][lane]);
+    p.db[(size_t)h * nblk + blk] = (ps[1][0][lane] + ps[1][1][lane]) + (ps[1][2][lane] + ps[1][3][lane]);
+}
+
+__global__ __launch_bounds__(kPreThreads) void gdn_pre_param_sum_kernel(PreParams p, int64_t nblk) {
     __shared__ float sa[kPreThreads], sd[kPreThreads];
     const int h = blockIdx.x, tid = threadIdx.x;
-    const float amp = gate_amplitude(p.A_log[h]);
-    const float dtb = p.dt_bias ? p.dt_bias[h] : 0.f;
     float a_acc = 0.f, d_acc = 0.f;
-    for (int64_t t = tid; t < p.total_tokens; t += kPreThreads) {
-        const size_t i = (size_t)t * p.hv + h;
-        const float dg = p.dg[i], a = p.a[i];
-        const float g = gate_from_logit(amp, dtb, a);
-        const float da = dg * (-amp * sigmoid_f32(a + dtb));
-        a_acc = a_acc + dg * g;
-        d_acc = d_acc + da;
+    for (int64_t b = tid; b < nblk; b += kPreThreads) {
+        a_acc = a_acc + p.da[(size_t)h * nblk + b];
+        d_acc = d_acc + p.db[(size_t)h * nblk + b];
     }
     sa[tid] = a_acc;
     sd[tid] = d_acc;
@@ -168,15 +197,23 @@ template <bool BWD>
 hipError_t pre_launch(const PreParams &p, int dk, int io_dtype, hipStream_t s) {
     hipError_t e = io_dtype == GDN_BF16 ? rows_io<IoBf16, BWD>(p, dk, s) : rows_io<IoF32, BWD>(p, dk, s);
     if (e != hipSuccess) return e;
+    // the parameter gradients first: their partial sums use da and db as scratch
+    if (BWD && (p.flags & GDN_PRE_GATE_LOGITS) && (p.dA_log || p.ddt_bias)) {
+        const int64_t nblk = (p.total_tokens + kParamTok - 1) / kParamTok;
+        if (nblk > 0) {
+            hipLaunchKernelGGL(gdn_pre_param_part_kernel, dim3((unsigned)nblk, (unsigned)((p.hv + 63) / 64)), dim3(256),
+                               0, s, p);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(gdn_pre_param_sum_kernel, dim3((unsigned)p.hv), dim3(kPreThreads), 0, s, p, nblk);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int64_t n = p.total_tokens * p.hv;
     if (n > 0) {
         hipLaunchKernelGGL((gdn_pre_gate_kernel<BWD>), dim3((unsigned)((n + kPreThreads - 1) / kPreThreads)),
                            dim3(kPreThreads), 0, s, p);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (BWD && (p.flags & GDN_PRE_GATE_LOGITS) && (p.dA_log || p.ddt_bias)) {
-        hipLaunchKernelGGL(gdn_pre_param_grad_kernel, dim3((unsigned)p.hv), dim3(kPreThreads), 0, s, p);
         e = hipGetLastError();
     }
     return e;

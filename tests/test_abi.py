@@ -686,7 +686,7 @@ def call_pre_bwd(lib, dims, **over):
     ({}, dict(q=None), 1), ({}, dict(kn=None), 1), ({}, dict(beta=None), 1), ({}, dict(a=None), 1),
     ({}, dict(q=PP["q"] + 8), 4), ({}, dict(qn=PP["qn"] + 4), 4), ({}, dict(g=PP["g"] + 2), 4),
     ({}, dict(qn=PP["q"]), 5), ({}, dict(g=PP["a"]), 5), ({}, dict(beta=PP["g"]), 5), ({}, dict(kn=PP["qn"]), 5),
-    ({}, dict(g=PP["Alog"]), 5),
+    ({}, dict(g=PP["Alog"]), 5), (dict(total_tokens=1 << 40), {}, 2),
 ])
 def test_preprocess_rejects(lib, case, over, code):
     assert call_pre(lib, pre_dims(**case), **over) == code
@@ -697,7 +697,7 @@ def test_preprocess_rejects(lib, case, over, code):
     ({}, dict(dqn=None), 1), ({}, dict(dq=None), 1), ({}, dict(da=None), 1), ({}, dict(db=None), 1),
     ({}, dict(dq=PP["dq"] + 4), 4), ({}, dict(dA=PP["dA"] + 2), 4),
     ({}, dict(dq=PP["q"]), 5), ({}, dict(da=PP["dg"]), 5), ({}, dict(dA=PP["Alog"]), 5), ({}, dict(dD=PP["dA"]), 5),
-    ({}, dict(dk=PP["dq"]), 5),
+    ({}, dict(dk=PP["dq"]), 5), (dict(total_tokens=1 << 40), {}, 2),
 ])
 def test_preprocess_backward_rejects(lib, case, over, code):
     assert call_pre_bwd(lib, pre_dims(**case), **over) == code
