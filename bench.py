@@ -206,9 +206,9 @@ COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 def pmc_pass(dev, stream):
     """One launch of each kernel (prefill, decode at B = 256, the short convolution
-    and its state update, the backward's six, the chunked form's prefill and backward),
-    preceded by a plain device copy of COPY_BYTES whose
-    FETCH_SIZE / WRITE_SIZE readings calibrate the counters' units."""
+    and its state update and backward, the backward's six, the chunked form's prefill
+    and backward, the preprocessing passes), preceded by a plain device copy of
+    COPY_BYTES whose FETCH_SIZE / WRITE_SIZE readings calibrate the counters' units."""
     import torch
 
     from invariant_linear_attention_amd import gdn, synth
@@ -234,7 +234,12 @@ def pmc_pass(dev, stream):
     pool_c = torch.zeros((w.n_seqs, C, K - 1), dtype=torch.bfloat16, device=dev)
     gdn.gdn_short_conv(xc, wc, d[6], pool_c, stream=stream)
     torch.cuda.synchronize()
-    del xc, pool_c
+    pool_c.zero_()
+    dyc = torch.randn((w.total_tokens, C), generator=torch.Generator().manual_seed(1009)).to(dev)
+    bc = torch.zeros((C,), device=dev)
+    gdn.gdn_short_conv_backward(xc, wc, d[6], pool_c, dyc, bias=bc, stream=stream)
+    torch.cuda.synchronize()
+    del xc, pool_c, dyc
     gen = torch.Generator().manual_seed(1006)  # the backward, as in its benchmark line
     dout = torch.randn(tuple(w.v.shape), generator=gen).to(torch.bfloat16).to(dev)
     dhT = torch.randn((w.n_seqs, 32, 128, 128), generator=gen).to(dev)
@@ -247,8 +252,22 @@ def pmc_pass(dev, stream):
     del st_in
     gdn.gdn_bwd_chunked(*d, dout, dhT, stream=stream)
     torch.cuda.synchronize()
-    print("pmc pass: copy %d bytes, prefill %d tokens, decode B=%d, conv %d channels, backward, chunked "
-          "prefill and backward" % (COPY_BYTES, w.total_tokens, B, C), flush=True)
+    del dout, dhT
+    # the preprocessing pass and its backward on the raw inputs of the same shape
+    rw = synth.make_raw_workload(1001, w.lengths, h0_std=0.1)
+    rq, rk, ra, rb = (t.to(dev) for t in (rw.q, rw.k, rw.g, rw.beta))
+    pre = gdn.make_preproc(norm_qk=True, eps=1e-6, A_log=rw.meta["A_log"].to(dev), dt_bias=rw.meta["dt_bias"].to(dev))
+    gdn.gdn_preprocess(rq, rk, ra, rb, pre=pre, stream=stream)
+    genp = torch.Generator().manual_seed(1008)
+    dqn = torch.randn(tuple(rw.q.shape), generator=genp).to(dev)
+    dkn = torch.randn(tuple(rw.q.shape), generator=genp).to(dev)
+    dgp = torch.randn(tuple(rw.g.shape), generator=genp).to(dev)
+    dbp = torch.randn(tuple(rw.g.shape), generator=genp).to(dev)
+    gdn.gdn_preprocess_backward(rq, rk, ra, rb, dqn, dkn, dgp, dbp, pre=pre, stream=stream)
+    torch.cuda.synchronize()
+    print("pmc pass: copy %d bytes, prefill %d tokens, decode B=%d, conv %d channels and its backward, backward, "
+          "chunked prefill and backward, preprocessing and its backward" % (COPY_BYTES, w.total_tokens, B, C),
+          flush=True)
 
 
 def main():
@@ -495,7 +514,8 @@ def main():
                             "roofline": {"bound": "hbm", "achieved": nbytes / (msx / 1e3) / 1e9,
                                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                          "frac": nbytes / (msx / 1e3) / 1e9 / HBM_PEAK_GBS,
-                                         "bytes_per_launch": nbytes, "traffic": None}}
+                                         "bytes_per_launch": nbytes,
+                                         "traffic": traffic_from_profile("preprocess_%s" % name, src_hash)}}
         workloads["preprocess_passes"] = rec_pp
         pp_got = {k: v[:, 0:1].cpu() for k, v in pre_g.items() if k in ("dq", "dk")}
         pp_got.update({k: pre_g[k].cpu() for k in ("da", "db", "dA_log", "ddt_bias")})
@@ -584,7 +604,8 @@ def main():
         rec_cb = {"tokens": T, "channels": C, "taps": K, "ms_median": mscb, "launch_ms_percentiles": percentiles(per_cb),
                   "roofline": {"bound": "hbm", "achieved": cbb / (mscb / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
                                "unit": "GB/s", "frac": cbb / (mscb / 1e3) / 1e9 / HBM_PEAK_GBS,
-                               "bytes_per_launch": cbb, "traffic": None}}
+                               "bytes_per_launch": cbb,
+                               "traffic": traffic_from_profile("short_conv_backward", src_hash)}}
         workloads["short_conv_backward"] = rec_cb
         cg_got = {"dx": cg["dx"][:, :256].cpu(), "dw": cg["dw"][:256].cpu(), "dbias": cg["dbias"][:256].cpu(),
                   "dstate": cg["dstate"][:, :256].cpu()}
@@ -665,7 +686,7 @@ def main():
                   "dv": grads_c["dv"][:, 0:2].cpu(), "dbeta": grads_c["dbeta"][:, 0:2].cpu(),
                   "dg": grads_c["dg"][:, 0:2].cpu(), "dh0": grads_c["dh0"][:, 0:2].cpu()}
         rec_bc = {"tokens": T, "n_seqs": w.n_seqs, "ms_median": msbc, "tokens_per_s": T / (msbc / 1e3),
-                  "launch_ms_percentiles": percentiles(per_bc), "launches": 4,
+                  "launch_ms_percentiles": percentiles(per_bc), "launches": 5,
                   "workspace_bytes": int(ws_cb.numel()),
                   "roofline": {"bound": "mfma", "achieved": bflops / (msbc / 1e3) / 1e12,
                                "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
