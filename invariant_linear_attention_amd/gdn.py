@@ -471,11 +471,15 @@ def _pre_shapes(q, k, a, b, pre):
     hv = int(a.shape[1])
     _shape(b, "b", (T, hv))
     _check_pre(pre, hv)
+    return T, hk, dk, hv
+
+
+def _pre_need(q, k, a, b):
+    import torch
     _need(q, "q")
     _need(k, "k", q.dtype)
     _need(a, "a", torch.float32)
     _need(b, "b", torch.float32)
-    return T, hk, dk, hv
 
 
 def gdn_preprocess(q, k, a, b, pre=None, out=None, stream=None):
@@ -485,12 +489,17 @@ def gdn_preprocess(q, k, a, b, pre=None, out=None, stream=None):
     g, beta [T, Hv] (``out``, a dict of the same, is filled when given)."""
     import torch
     T, hk, dk, hv = _pre_shapes(q, k, a, b, pre)
+    shapes = (("qn", (T, hk, dk)), ("kn", (T, hk, dk)), ("g", (T, hv)), ("beta", (T, hv)))
+    if out is not None:
+        for name, shp in shapes:
+            if out.get(name) is None:
+                raise ValueError("out[%r] is required" % name)
+            _shape(out[name], name, shp)
+    _pre_need(q, k, a, b)
     if out is None:
         f32 = dict(dtype=torch.float32, device=q.device)
-        out = {"qn": torch.empty((T, hk, dk), **f32), "kn": torch.empty((T, hk, dk), **f32),
-               "g": torch.empty((T, hv), **f32), "beta": torch.empty((T, hv), **f32)}
-    for name, shp in (("qn", (T, hk, dk)), ("kn", (T, hk, dk)), ("g", (T, hv)), ("beta", (T, hv))):
-        _shape(out.get(name), name, shp)
+        out = {name: torch.empty(shp, **f32) for name, shp in shapes}
+    for name, _ in shapes:
         _need(out[name], name, torch.float32)
     dims = _pre_dims(q, a, pre)
     _check(load_library().gdn_preprocess(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(a), _ptr(b), _ptr(out["qn"]),
@@ -505,9 +514,20 @@ def gdn_preprocess_backward(q, k, a, b, dqn, dkn, dg, dbeta, pre=None, grads=Non
     [Hv]."""
     import torch
     T, hk, dk, hv = _pre_shapes(q, k, a, b, pre)
-    for name, t, shp in (("dqn", dqn, (T, hk, dk)), ("dkn", dkn, (T, hk, dk)), ("dg", dg, (T, hv)),
-                         ("dbeta", dbeta, (T, hv))):
+    ins = (("dqn", dqn, (T, hk, dk)), ("dkn", dkn, (T, hk, dk)), ("dg", dg, (T, hv)), ("dbeta", dbeta, (T, hv)))
+    for name, t, shp in ins:
+        if t is None:
+            raise ValueError("%s is required" % name)
         _shape(t, name, shp)
+    gshapes = (("dq", (T, hk, dk)), ("dk", (T, hk, dk)), ("da", (T, hv)), ("db", (T, hv)), ("dA_log", (hv,)),
+               ("ddt_bias", (hv,)))
+    if grads is not None:
+        for name, shp in gshapes:
+            if name in ("dq", "dk", "da", "db") and grads.get(name) is None:
+                raise ValueError("grads[%r] is required" % name)
+            _shape(grads.get(name), name, shp)
+    _pre_need(q, k, a, b)
+    for name, t, _ in ins:
         _need(t, name, torch.float32)
     gated = pre is not None and (pre.flags & GDN_PRE_GATE_LOGITS)
     has_dtb = gated and pre.dt_bias is not None
@@ -517,11 +537,8 @@ def gdn_preprocess_backward(q, k, a, b, dqn, dkn, dg, dbeta, pre=None, grads=Non
                  "da": torch.empty((T, hv), **f32), "db": torch.empty((T, hv), **f32),
                  "dA_log": torch.empty((hv,), **f32) if gated else None,
                  "ddt_bias": torch.empty((hv,), **f32) if has_dtb else None}
-    for name, shp in (("dq", (T, hk, dk)), ("dk", (T, hk, dk)), ("da", (T, hv)), ("db", (T, hv)),
-                      ("dA_log", (hv,)), ("ddt_bias", (hv,))):
-        if grads.get(name) is not None:
-            _shape(grads[name], name, shp)
-            _need(grads[name], name, torch.float32)
+    for name, _ in gshapes:
+        _need(grads.get(name), name, torch.float32)
     dims = _pre_dims(q, a, pre)
     _check(load_library().gdn_preprocess_backward(
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(a), _ptr(b), _ptr(dqn), _ptr(dkn), _ptr(dg), _ptr(dbeta),
@@ -750,8 +767,15 @@ def gdn_short_conv_backward(x, w, cu_seqlens, state_pool, dy, bias=None, src_idx
         raise ValueError("state_pool must be [P, C, K-1] = [P, %d, %d], got %s"
                          % (C, K - 1, None if state_pool is None else tuple(state_pool.shape)))
     _check_index(src_idx, "src_idx", N)
-    for name, t in (("x", x),):
-        _need(t, name)
+    gshapes = (("dx", (T, C)), ("dw", (C, K)), ("dbias", (C,)), ("dstate", (N, C, K - 1)))
+    if grads is not None:
+        for name, shp in gshapes:
+            if name in ("dx", "dw") and grads.get(name) is None:
+                raise ValueError("grads[%r] is required" % name)
+            _shape(grads.get(name), name, shp)
+    if dy is None:
+        raise ValueError("dy is required")
+    _need(x, "x")
     _need(w, "w", torch.float32)
     _need(bias, "bias", torch.float32)
     _need(cu_seqlens, "cu_seqlens", torch.int32)
@@ -769,10 +793,8 @@ def gdn_short_conv_backward(x, w, cu_seqlens, state_pool, dy, bias=None, src_idx
         grads = {"dx": torch.empty((T, C), **f32), "dw": torch.empty((C, K), **f32),
                  "dbias": torch.empty((C,), **f32) if bias is not None else None,
                  "dstate": torch.empty((N, C, K - 1), **f32) if want_dstate else None}
-    for name, shp in (("dx", (T, C)), ("dw", (C, K)), ("dbias", (C,)), ("dstate", (N, C, K - 1))):
-        if grads.get(name) is not None:
-            _shape(grads[name], name, shp)
-            _need(grads[name], name, torch.float32)
+    for name, _ in gshapes:
+        _need(grads.get(name), name, torch.float32)
     _check(load_library().gdn_short_conv_backward(
         ctypes.byref(dims), _ptr(x), _ptr(w), _ptr(bias), _ptr(cu_seqlens), _ptr(state_pool), _ptr(src_idx),
         _ptr(dy), _ptr(grads["dx"]), _ptr(grads["dw"]), _ptr(grads.get("dbias")), _ptr(grads.get("dstate")),

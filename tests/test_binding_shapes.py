@@ -186,3 +186,104 @@ def test_chunked_backward_refuses_gradient_buffers():
              "dbeta": f((T, HV)), "dh0": None}
     expect_shape_error(gdn.gdn_bwd_chunked, b["q"], b["k"], b["v"], b["g"], b["beta"], b["h0"], b["cu_seqlens"],
                        torch.zeros((T, HV, DV), dtype=torch.bfloat16), grads=grads)
+
+
+# ------------------------------------------------ the fused layer's training passes
+
+def expect_shape_only(fn, *a, **kw):
+    """A shape error, raised before the device checks (which CPU tensors would fail)."""
+    with pytest.raises(ValueError) as e:
+        fn(*a, **kw)
+    msg = str(e.value)
+    assert ("must" in msg or "required" in msg) and "device tensor" not in msg, msg
+
+
+def pre_inputs():
+    bf = dict(dtype=torch.bfloat16)
+    return dict(q=torch.zeros((T, HK, DK), **bf), k=torch.zeros((T, HK, DK), **bf), a=torch.zeros((T, HV)),
+                b=torch.zeros((T, HV)))
+
+
+def gated_pre(n=HV):
+    pre = gdn.GdnPreproc(flags=gdn.GDN_PRE_QK_L2NORM | gdn.GDN_PRE_GATE_LOGITS, eps=1e-6)
+    pre._keep = (torch.zeros((n,)), None)
+    return pre
+
+
+PRE_WRONG = {"k": torch.zeros((T, HK, DK + 1), dtype=torch.bfloat16), "a": torch.zeros((T - 1, HV)),
+             "b": torch.zeros((T, HV + 1)), "q": torch.zeros((T, HK * DK), dtype=torch.bfloat16)}
+
+
+@pytest.mark.parametrize("name", sorted(PRE_WRONG))
+def test_preprocess_refuses(name):
+    i = pre_inputs()
+    i[name] = PRE_WRONG[name]
+    expect_shape_only(gdn.gdn_preprocess, i["q"], i["k"], i["a"], i["b"], pre=gated_pre())
+
+
+def test_preprocess_refuses_outputs_and_parameters():
+    i = pre_inputs()
+    out = {"qn": torch.zeros((T, HK, DK)), "kn": torch.zeros((T, HK, DK)), "g": torch.zeros((T, HV)),
+           "beta": torch.zeros((T, HV + 1))}
+    expect_shape_only(gdn.gdn_preprocess, i["q"], i["k"], i["a"], i["b"], pre=gated_pre(), out=out)
+    del out["beta"]
+    expect_shape_only(gdn.gdn_preprocess, i["q"], i["k"], i["a"], i["b"], pre=gated_pre(), out=out)
+    expect_shape_only(gdn.gdn_preprocess, i["q"], i["k"], i["a"], i["b"], pre=gated_pre(HV + 1))
+
+
+@pytest.mark.parametrize("which,shape", [("dqn", (T, HK, DK + 1)), ("dkn", (T + 1, HK, DK)), ("dg", (T, HK)),
+                                         ("dbeta", (T, HV, 1))])
+def test_preprocess_backward_refuses(which, shape):
+    i = pre_inputs()
+    g = {"dqn": torch.zeros((T, HK, DK)), "dkn": torch.zeros((T, HK, DK)), "dg": torch.zeros((T, HV)),
+         "dbeta": torch.zeros((T, HV))}
+    g[which] = torch.zeros(shape)
+    expect_shape_only(gdn.gdn_preprocess_backward, i["q"], i["k"], i["a"], i["b"], g["dqn"], g["dkn"], g["dg"],
+                      g["dbeta"], pre=gated_pre())
+
+
+@pytest.mark.parametrize("which,shape", [("dq", (T, HK, DK - 1)), ("da", (T, HV + 1)), ("dA_log", (HV + 1,)),
+                                         ("db", None)])
+def test_preprocess_backward_refuses_gradient_buffers(which, shape):
+    i = pre_inputs()
+    grads = {"dq": torch.zeros((T, HK, DK)), "dk": torch.zeros((T, HK, DK)), "da": torch.zeros((T, HV)),
+             "db": torch.zeros((T, HV)), "dA_log": torch.zeros((HV,)), "ddt_bias": None}
+    grads[which] = None if shape is None else torch.zeros(shape)
+    expect_shape_only(gdn.gdn_preprocess_backward, i["q"], i["k"], i["a"], i["b"], torch.zeros((T, HK, DK)),
+                      torch.zeros((T, HK, DK)), torch.zeros((T, HV)), torch.zeros((T, HV)), pre=gated_pre(),
+                      grads=grads)
+
+
+C, K = 24, 4
+
+
+def conv_inputs():
+    return dict(x=torch.zeros((T, C), dtype=torch.bfloat16), w=torch.zeros((C, K)),
+                cu_seqlens=torch.tensor([0, 4, T], dtype=torch.int32),
+                state_pool=torch.zeros((3, C, K - 1), dtype=torch.bfloat16), dy=torch.zeros((T, C)),
+                bias=torch.zeros((C,)))
+
+
+CONV_WRONG = {"w": torch.zeros((C + 1, K)), "dy": torch.zeros((T, C + 4)), "bias": torch.zeros((C - 1,)),
+              "state_pool": torch.zeros((3, C, K)), "cu_seqlens": torch.zeros((1, N + 1), dtype=torch.int32),
+              "src_idx": torch.zeros((N + 1,), dtype=torch.int32)}
+
+
+@pytest.mark.parametrize("name", sorted(CONV_WRONG))
+def test_conv_backward_refuses(name):
+    i = conv_inputs()
+    i["src_idx"] = None
+    i[name] = CONV_WRONG[name]
+    expect_shape_only(gdn.gdn_short_conv_backward, i["x"], i["w"], i["cu_seqlens"], i["state_pool"], i["dy"],
+                      bias=i["bias"], src_idx=i["src_idx"])
+
+
+@pytest.mark.parametrize("which,shape", [("dx", (T, C + 1)), ("dw", (C, K + 1)), ("dstate", (N, C, K)),
+                                         ("dx", None)])
+def test_conv_backward_refuses_gradient_buffers(which, shape):
+    i = conv_inputs()
+    grads = {"dx": torch.zeros((T, C)), "dw": torch.zeros((C, K)), "dbias": torch.zeros((C,)),
+             "dstate": torch.zeros((N, C, K - 1))}
+    grads[which] = None if shape is None else torch.zeros(shape)
+    expect_shape_only(gdn.gdn_short_conv_backward, i["x"], i["w"], i["cu_seqlens"], i["state_pool"], i["dy"],
+                      bias=i["bias"], grads=grads)
