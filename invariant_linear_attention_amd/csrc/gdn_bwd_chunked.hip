@@ -271,10 +271,13 @@ __global__ __launch_bounds__(64 * (DV / 16 / P)) void gdn_bwd_chunk_rev_kernel(B
             dg = s == m ? run : dg;
         }
         carry = run;
-        if (lane < kCk && m < m1) {
-            out_beta[(size_t)(t0 + m) * p.hv + h] = sbv + abrow[m];
-            out_g[(size_t)(t0 + m) * p.hv + h] = dg;
-        }
+        // unconditional buffer stores (out-of-range offset where there is nothing to
+        // write), so that the memory counters stay exact and no wait drains the next
+        // chunk's reads
+        const uint32_t bytes = (uint32_t)m1 * (uint32_t)p.hv * 4u;
+        const uint32_t off = lane < kCk && m < m1 ? ((uint32_t)m * (uint32_t)p.hv + (uint32_t)h) * 4u : kDropped;
+        buf_store_f32(buf_rsrc(out_beta + (size_t)t0 * p.hv, bytes), off, sbv + abrow[m]);
+        buf_store_f32(buf_rsrc(out_g + (size_t)t0 * p.hv, bytes), off, dg);
     };
 
     RF F;
@@ -784,22 +787,28 @@ __global__ __launch_bounds__(512) void gdn_bwd_chunk_ws_kernel(BwdChunkParams p)
                 dg = s == m ? run : dg;
             }
             carry = run;
-            if (lane < kCk && m < m1) {
-                out_beta[(size_t)(t0 + m) * p.hv + h] = sbv + abrow[j % 3][m];
-                out_g[(size_t)(t0 + m) * p.hv + h] = dg;
-            }
+            // unconditional buffer stores, as in gdn_bwd_chunk_rev_kernel
+            const uint32_t bytes = (uint32_t)m1 * (uint32_t)p.hv * 4u;
+            const uint32_t off = lane < kCk && m < m1 ? ((uint32_t)m * (uint32_t)p.hv + (uint32_t)h) * 4u : kDropped;
+            buf_store_f32(buf_rsrc(out_beta + (size_t)t0 * p.hv, bytes), off, sbv + abrow[j % 3][m]);
+            buf_store_f32(buf_rsrc(out_g + (size_t)t0 * p.hv, bytes), off, dg);
         };
         // (wave 1) the dA part of dbeta of chunk j, sum_s dA[m][s] Gam_{m,s} (k_m . k_s),
         // from the partials the state waves left a step before (a row's 16 entries sit
-        // in 16 lanes)
+        // in 16 lanes); its Gam (k . k) entries are read a step ahead
+        float aen[4];
+        auto fetch_ab = [&](int j_) {
+            const float *rec = rec_of(j_ < 0 ? 0 : j_);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) aen[e] = rec[kRecAb + lane + 64 * e];
+        };
         auto abrow_calc = [&](int j) {
-            const float *rec = rec_of(j);
             const int b = j & 1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = lane + 64 * e;
                 const int m = i / kCk, s = i % kCk;
-                const float ae = rec[kRecAb + i];
+                const float ae = aen[e];
                 const float4 a4 = *reinterpret_cast<const float4 *>(&dAw[b][m][s][0]);
                 const float sav = (((0.f + a4.x) + a4.y) + a4.z) + a4.w;
                 const float ab = lane_sum<16>(sav * ae);
@@ -807,6 +816,7 @@ __global__ __launch_bounds__(512) void gdn_bwd_chunk_ws_kernel(BwdChunkParams p)
             }
         };
         if (nch > 0) fetch(nch - 1);
+        if (wave == 1 && nch > 0) fetch_ab(nch - 1);
         for (int st = 0; st <= nch; ++st) {
             const int j = nch - 1 - st;  // this step's chunk (none at the last step)
             if (j >= 0) {
@@ -945,7 +955,10 @@ __global__ __launch_bounds__(512) void gdn_bwd_chunk_ws_kernel(BwdChunkParams p)
                 }
             }
             // the gradient waves run chunk j + 1 in this step; chunk j + 2 is complete
-            if (wave == 1 && st >= 1) abrow_calc(j + 1);
+            if (wave == 1 && st >= 1) {
+                abrow_calc(j + 1);
+                fetch_ab(j);
+            }
             if (wave == 0 && st >= 2) per_token(j + 2);
             lds_barrier();
         }
