@@ -219,14 +219,15 @@ __global__ __launch_bounds__(64 * (DV / 16 / P)) void gdn_bwd_chunk_rev_kernel(B
     f4 s0[RT][CTW];
     auto fetch_s0 = [&](int j_) {
         const int j = j_ < 0 ? 0 : j_;
-        const float *ck = p.ck + (((size_t)(base + j) * p.hv + h) * DV + part * DVP) * DK;
+        // (the forward walk stores it tile-major: [dk / 16 column tiles][dv rows][16])
+        const float *ck = p.ck + ((size_t)(base + j) * p.hv + h) * DV * DK + (size_t)(part * DVP) * 16;
 #pragma unroll
         for (int l2 = 0; l2 < CTW; ++l2) {
             const int ct = wave + NW * l2 < NT ? wave + NW * l2 : NT - 1;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) s0[rt][l2][c] = ck[(16 * rt + 4 * g + c) * DK + 16 * ct + x];
+                for (int c = 0; c < 4; ++c) s0[rt][l2][c] = ck[((size_t)ct * DV + 16 * rt + 4 * g + c) * 16 + x];
         }
     };
 
@@ -982,14 +983,15 @@ __global__ __launch_bounds__(512) void gdn_bwd_chunk_ws_kernel(BwdChunkParams p)
         f4 s0[RT][CTW];
         auto fetch_s0 = [&](int j_) {
             const int j = j_ < 0 ? 0 : j_;
-            const float *ck = p.ck + (((size_t)(base + j) * p.hv + h) * DV + part * DVP) * DK;
+            // (tile-major, as the forward walk stores it)
+            const float *ck = p.ck + ((size_t)(base + j) * p.hv + h) * DV * DK + (size_t)(part * DVP) * 16;
 #pragma unroll
             for (int l2 = 0; l2 < CTW; ++l2)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        s0[rt][l2][c] = ck[(16 * rt + 4 * g + c) * DK + 16 * (gw + NWD * l2) + x];
+                        s0[rt][l2][c] = ck[((size_t)(gw + NWD * l2) * DV + 16 * rt + 4 * g + c) * 16 + x];
         };
         auto fetch = [&](int j_) {
             const int j = j_ < 0 ? 0 : j_;

@@ -475,10 +475,13 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
         if constexpr (BW) {
             // the state at this chunk's start (stored after the next chunk's reads, so
             // that waiting for those does not wait for these)
-            float *dst = p.ck + (((size_t)(sc.base + j) * p.hv + h) * p.dv + row0 + x) * DK;
+            // (tile-major: [dk / 16 column tiles][dv rows][16 columns], so that each store
+            // instruction writes 1 KB in one piece; nontemporal, read back only by the
+            // reverse walk)
+            float *dst = p.ck + ((size_t)(sc.base + j) * p.hv + h) * p.dv * DK + (size_t)(row0 + x) * 16 + 4 * g;
 #pragma unroll
             for (int t = 0; t < OT; ++t)
-                *reinterpret_cast<float4 *>(dst + 16 * (t_first + t) + 4 * g) = make_float4(S[t][0], S[t][1], S[t][2], S[t][3]);
+                __builtin_nontemporal_store(S[t], reinterpret_cast<f4 *>(dst + (size_t)(t_first + t) * p.dv * 16));
         }
         lds_barrier();
 
