@@ -507,10 +507,10 @@ gdn_status gdn_fwd_chunked(const gdn_dims *dims,
  *
  *   workspace : device scratch of at least gdn_bwd_chunked_workspace_size bytes,
  *               16-byte aligned, owned by the caller; contents on entry do not
- *               matter.  About 4 dv dk bytes per (16-token chunk, value head) for the
- *               chunk-start states, plus 4 hv (dv + 2 P dk + 2 P) bytes per token
- *               (the dk term only when hv > hk or P > 1, the last when P > 1) and
- *               4.3 KB per (chunk, value head).
+ *               matter.  About 4 dv (dk + 16) bytes per (16-token chunk, value head)
+ *               for the chunk-start states and x, plus 4 hv (2 P dk + 2 P) bytes per
+ *               token (the dk term only when hv > hk or P > 1, the last when P > 1)
+ *               and 4.3 KB per (chunk, value head).
  * dk must be 64 or 128, dv 32, 64 or 128 and hv / hk at most 16 (else
  * GDN_ERR_UNSUPPORTED, as is dims->pre).  plan_rows sets P (0 = automatic: 2 for
  * dv = 128, else 1; 2 needs dv >= 64), plan_waves (0, 1, 2 or 4) the forward

@@ -729,7 +729,7 @@ BwdChunkWorkspace bwd_chunked_workspace(int64_t T, int64_t N, int hk, int hv, in
     uint64_t o = 0;
     w.rec = o; o = round256(o + slots * hv * kChunkRecBwd * 4);
     w.ck = o; o = round256(o + slots * hv * (uint64_t)dv * dk * 4);
-    w.xv = o; o = round256(o + (uint64_t)T * hv * dv * 4);
+    w.xv = o; o = round256(o + slots * hv * (uint64_t)dv * kChunkLen * 4);  // x: [row][token] tiles per slot
     w.hdot = o; o = round256(o + (uint64_t)N * hv * (dv / 16) * 4 * 4);
     w.dq = o; o = round256(o + (split ? (uint64_t)parts * T * hv * dk * 4 : 0));
     w.dk = o; o = round256(o + (split ? (uint64_t)parts * T * hv * dk * 4 : 0));

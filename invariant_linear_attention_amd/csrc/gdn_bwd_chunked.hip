@@ -181,13 +181,19 @@ __global__ __launch_bounds__(64 * (DV / 16 / P)) void gdn_bwd_chunk_rev_kernel(B
         }
         const char *ob = static_cast<const char *>(p.dout) + ((size_t)t0 * p.hv + h) * DV * E;
         const char *vb = static_cast<const char *>(p.v) + ((size_t)t0 * p.hv + h) * DV * E;
-        const char *xb = reinterpret_cast<const char *>(p.xv + ((size_t)t0 * p.hv + h) * DV);
+        // x: the forward walk's [row][token] tile of this chunk and 16 rows (tokens
+        // 4 g .. 4 g + 3 of row x in one 16-byte piece)
+        const float4 x4 = *reinterpret_cast<const float4 *>(
+            p.xv + (((size_t)(base + j) * p.hv + h) * DV + rg) * kCk + x * kCk + 4 * g);
+        F.xr[0] = x4.x;
+        F.xr[1] = x4.y;
+        F.xr[2] = x4.z;
+        F.xr[3] = x4.w;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const uint32_t tm = (uint32_t)(4 * g + c < m1 ? 4 * g + c : m1 - 1);
             F.dor[c] = RW::load1_at(ob, tm * vrow_b + (uint32_t)(rg + x) * E);
             F.vr[c] = RW::load1_at(vb, tm * vrow_b + (uint32_t)(rg + x) * E);
-            F.xr[c] = *reinterpret_cast<const float *>(xb + tm * (uint32_t)(vrow * 4) + (uint32_t)(rg + x) * 4);
         }
         const float *rec = p.rec + ((size_t)(base + j) * p.hv + h) * kChunkRecBwd;
         const int l = m1 - 1;
@@ -727,13 +733,18 @@ __global__ __launch_bounds__(512) void gdn_bwd_chunk_ws_kernel(BwdChunkParams p)
             const int64_t t0 = tb + (int64_t)kCk * j;
             const char *ob = static_cast<const char *>(p.dout) + ((size_t)t0 * p.hv + h) * DV * E;
             const char *vb = static_cast<const char *>(p.v) + ((size_t)t0 * p.hv + h) * DV * E;
-            const char *xb = reinterpret_cast<const char *>(p.xv + ((size_t)t0 * p.hv + h) * DV);
+            // x: the forward walk's [row][token] tile (see gdn_bwd_chunk_rev_kernel)
+            const float4 x4 = *reinterpret_cast<const float4 *>(
+                p.xv + (((size_t)(base + j) * p.hv + h) * DV + rg) * kCk + x * kCk + 4 * g);
+            F.xr[0] = x4.x;
+            F.xr[1] = x4.y;
+            F.xr[2] = x4.z;
+            F.xr[3] = x4.w;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const uint32_t tm = (uint32_t)(4 * g + c < m1 ? 4 * g + c : m1 - 1);
                 F.dor[c] = RW::load1_at(ob, tm * vrow_b + (uint32_t)(rg + x) * E);
                 F.vr[c] = RW::load1_at(vb, tm * vrow_b + (uint32_t)(rg + x) * E);
-                F.xr[c] = *reinterpret_cast<const float *>(xb + tm * (uint32_t)(vrow * 4) + (uint32_t)(rg + x) * 4);
             }
             const float *rec = rec_of(j);
             const int l = m1 - 1;

@@ -563,28 +563,29 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
         // R_m = fma(-(beta_m Gam_m), P_m, beta_m v_m) for this call's tokens, cached R
         // for the chunk's earlier tokens, 0 for tokens not reached yet
         const float gm[4] = {gam.x, gam.y, gam.z, gam.w};
-        f4 R, OC;
-        // this chunk's rows of x (backward walk) or of the outputs, as buffer stores
-        // that every lane issues (kDropped where there is nothing to write)
-        const uint32_t col_b = (uint32_t)(h * p.dv + row0 + x);
-        const auto orsrc = BW ? buf_rsrc(p.xv + (size_t)t0 * vrow, (uint32_t)(m1 * vrow * 4))
-                              : buf_rsrc(static_cast<const char *>(p.out) + (size_t)t0 * vrow * IO::ESZ,
-                                         (uint32_t)(m1 * vrow * IO::ESZ));
+        f4 R, OC, X4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int m = 4 * g + c;
             const bool on = m >= m0 && m < m1;
             if constexpr (BW) {
-                // x = v - Gam P (kept for the reverse walk), R = beta x
-                const float xr = on ? __builtin_fmaf(-gm[c], P[c], vraw[c]) : 0.f;
-                R[c] = bb[c] * xr;
-                buf_store_f32(orsrc, wave == 0 && on ? ((uint32_t)m * (uint32_t)vrow + col_b) * 4u : kDropped, xr);
+                // x = v - Gam P (kept for the reverse walk; zero past the chunk's end), R = beta x
+                X4[c] = on ? __builtin_fmaf(-gm[c], P[c], vraw[c]) : 0.f;
+                R[c] = bb[c] * X4[c];
             } else {
                 const float fresh = __builtin_fmaf(-(bb[c] * gm[c]), P[c], vb[c]);
                 R[c] = on ? fresh : (m < m0 ? Rkeep[c] : 0.f);
                 Rkeep[c] = on ? fresh : Rkeep[c];
                 OC[c] = gm[c] * Z[c];
             }
+        }
+
+        if constexpr (BW) {
+            // x of the chunk's 16 tokens on the tile's 16 rows: [row][token] per (chunk
+            // slot, value head, row tile), so that lane (x, g) holds tokens 4 g .. 4 g + 3
+            // of row x as one 16-byte piece and wave 0 writes the tile's 1 KB in one store
+            const auto xrsrc = buf_rsrc(p.xv + (((size_t)(sc.base + j) * p.hv + h) * p.dv + row0) * kCk, 1024u);
+            buf_store_f4_nt(xrsrc, wave == 0 ? (uint32_t)(x * kCk + 4 * g) * 4u : kDropped, X4);
         }
 
         // U = T R, then O = Gam Z + B U (instruction c adds the tokens 4 g + c)
@@ -596,6 +597,11 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) U[c] = U[c] + 0.f;
         if constexpr (!BW) {
+        // this chunk's rows of the outputs, as buffer stores that every lane issues
+        // (kDropped where there is nothing to write)
+        const uint32_t col_b = (uint32_t)(h * p.dv + row0 + x);
+        const auto orsrc = buf_rsrc(static_cast<const char *>(p.out) + (size_t)t0 * vrow * IO::ESZ,
+                                    (uint32_t)(m1 * vrow * IO::ESZ));
         f4 O = OC;
         O = mfma_16x16x4(brow.x, U[0], O);
         O = mfma_16x16x4(brow.y, U[1], O);

@@ -93,6 +93,13 @@ __device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), r, off, 0, 0);
 }
 
+// Four floats as one 16-byte buffer store at byte offset off, nontemporal (written
+// once and read back once, by another kernel); kDropped drops it.
+__device__ __forceinline__ void buf_store_f4_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, f4 v) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 2);
+}
+
 // Sum over the 16 lanes x of each lane group g (lanes 16 g .. 16 g + 15), in the
 // fixed butterfly order 8, 4, 2, 1; every lane of the group gets the sum.
 __device__ __forceinline__ float sum16(float v) {

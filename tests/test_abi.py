@@ -467,7 +467,8 @@ def call_cbwd(lib, dims, ws_bytes=None, **over):
 
 def test_bwd_chunked_workspace_size(lib):
     """Records (1,088 floats per slot and value head), the chunk-start states (a dv x dk
-    state per slot and value head), x = v - Gam P (T hv dv), the <dhT, hT> partials
+    state per slot and value head), x = v - Gam P (a dv x 16 tile per slot and value
+    head), the <dhT, hT> partials
     (N hv dv/16 x 4), then with P row parts (plan_rows; 0 = 2 for dv = 128, else 1):
     when value heads share key heads or P > 1, dq and dk per value head and part
     (P T hv dk each), and when P > 1 dbeta and dg per part (P T hv each); slots =
@@ -479,7 +480,7 @@ def test_bwd_chunked_workspace_size(lib):
         slots = T // 16 + 2 * N + 2
         ck = dv * dk
         P = rows or (2 if dv == 128 else 1)
-        want = (up(slots * hv * 1088 * 4) + up(slots * hv * ck * 4) + up(T * hv * dv * 4)
+        want = (up(slots * hv * 1088 * 4) + up(slots * hv * ck * 4) + up(slots * hv * dv * 16 * 4)
                 + up(N * hv * (dv // 16) * 16) + (2 * up(P * T * hv * dk * 4) if hv > hk or P > 1 else 0)
                 + (2 * up(P * T * hv * 4) if P > 1 else 0))
         d = _dims(total_tokens=T, n_seqs=N, hk=hk, hv=hv, dk=dk, dv=dv, plan_rows=rows)
