@@ -547,7 +547,9 @@ gdn_status gdn_bwd_chunked(const gdn_dims *dims,
  *     gradients of the raw inputs:
  *       dq = (dqn - qn (qn . dqn)) r with r = rsq(sum q^2 + eps) (likewise dk);
  *       da = dg (-exp(A_log) sigmoid(a + dt_bias));  db = dbeta beta (1 - beta);
- *       dA_log[h] = sum_t dg g;  ddt_bias[h] = sum_t da  (all T tokens, fixed order)
+ *       dA_log[h] = sum_t dg g;  ddt_bias[h] = sum_t da  (all T tokens, fixed order:
+ *       64-token blocks, then the blocks; da and db hold the block sums until
+ *       they are overwritten with their own values, within the call)
  *     Without GDN_PRE_QK_L2NORM dq = dqn (dk = dkn); without GDN_PRE_GATE_LOGITS
  *     da = dg, db = dbeta and dA_log, ddt_bias are not written; ddt_bias is written
  *     only when pre->dt_bias is given.
@@ -556,8 +558,9 @@ gdn_status gdn_bwd_chunked(const gdn_dims *dims,
  *          [T][hv] fp32; qn, kn, dqn, dkn, dq, dk: [T][hk][dk] fp32, 16-byte aligned;
  *          dA_log, ddt_bias: [hv] fp32.  All device memory, owned by the caller.
  * Only hk, hv, dk (16, 32, 64 or 128), dv, io_dtype, total_tokens and pre of dims
- * are used (n_seqs is not).  Errors as gdn_fwd_varlen: NULL, SHAPE, DTYPE,
- * UNSUPPORTED, ALIGN, ALIAS (an output overlapping an input or another output).
+ * are used (n_seqs is not).  Errors as gdn_fwd_varlen: NULL, SHAPE (also a call
+ * whose launch grids would pass 2^31 workgroups), DTYPE, UNSUPPORTED, ALIGN, ALIAS
+ * (an output overlapping an input or another output).
  */
 gdn_status gdn_preprocess(const gdn_dims *dims, const void *q, const void *k, const float *a, const float *b,
                           float *qn, float *kn, float *g, float *beta, void *stream);
