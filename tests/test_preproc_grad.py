@@ -115,6 +115,33 @@ def test_preprocess_backward_matches_oracle(gpu, norm, gate, dtb, dk, io):
         assert e <= 1e-5, (key, e)
 
 
+def test_parameter_gradients_many_heads(gpu):
+    """More value heads than a wave has lanes (the block sums take two head groups), a
+    token count that ends mid-block, and every parameter gradient against the oracle;
+    a repeat gives the same bits."""
+    from oracle import oracle
+    w = raw(651, [70, 1, 129, 33], hk=4, hv=96, dk=32, dv=16)
+    pre, keep = make_pre(gpu, w, True, True)
+    gen = torch.Generator().manual_seed(24)
+    T, hk, dk, hv = w.q.shape[0], 4, 32, 96
+    dqn, dkn = torch.randn((T, hk, dk), generator=gen), torch.randn((T, hk, dk), generator=gen)
+    dg, db = torch.randn((T, hv), generator=gen), torch.randn((T, hv), generator=gen)
+    d = to_dev(w)
+    args = (d["q"], d["k"], d["g"], d["beta"], dqn.to(DEV), dkn.to(DEV), dg.to(DEV), db.to(DEV))
+    r1 = gpu.gdn_preprocess_backward(*args, pre=pre)
+    r2 = gpu.gdn_preprocess_backward(*args, pre=pre)
+    torch.cuda.synchronize()
+    for key in r1:
+        if r1[key] is not None:
+            assert torch.equal(r1[key], r2[key]), key
+    ref = oracle.preprocess_backward(w.q, w.k, w.g, w.beta, dqn, dkn, dg, db, A_log=w.meta["A_log"],
+                                     dt_bias=w.meta["dt_bias"], norm_qk=True)
+    errs = {key: rel(r1[key].cpu(), ref[key]) for key in ("da", "db", "dA_log", "ddt_bias")}
+    say("preprocess backward, 96 value heads: %s" % errs)
+    for key, e in errs.items():
+        assert e <= 1e-5, (key, e)
+
+
 def test_fused_layer_gradients(gpu):
     """The whole fused layer: preprocessing, the chunked backward on its outputs (fp32
     io, v and dO widened) and the preprocessing's backward, against the oracle's
