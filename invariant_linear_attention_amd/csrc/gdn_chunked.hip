@@ -263,7 +263,7 @@ struct ChunkFetch {
     typename Raw4<IO>::T kr[LEAN ? 1 : KIT];  // key rows for LDS: item tid + 64 W s
     typename Raw4<IO>::T qa[LEAN ? 1 : OT];   // query operand: token x, columns of the wave's tiles
     uint32_t v[4];                  // value bits (row x) of tokens 4 g + c
-    float b[4];                     // their betas
+    float4 b;                       // their betas (from the record)
     float4 trow, brow;              // T[x][4 g ..] and B[x][4 g ..]
     float4 gam, dw;                 // Gam_{4 g + c} and chunk-end weights Gam_{15, 4 g + c}
     float g15;                      // Gam_15
@@ -353,6 +353,8 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
         t0 = sc.tb + (int64_t)kCk * j - sc.c0;
     };
     auto clampm = [](int m, int lo, int hi) { return m < lo ? lo : (m >= hi ? hi - 1 : m); };
+    // byte offset of this lane's value (row x, token 4 g) within a chunk's value rows
+    const uint32_t v_lane = (uint32_t)(4 * g) * (uint32_t)(vrow * IO::ESZ) + (uint32_t)(row0 + x) * IO::ESZ;
     // (j is clamped to the last chunk, so that a read past it repeats that chunk's
     // reads instead of needing a branch; nch >= 1 whenever this is called)
     auto fetch = [&](CF &F, int j_) {
@@ -365,8 +367,7 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
         const char *kb = static_cast<const char *>(p.k) + ((size_t)t0 * p.hk + kh) * DK * E;
         const char *qb = static_cast<const char *>(p.q) + ((size_t)t0 * p.hk + kh) * DK * E;
         const char *vb = static_cast<const char *>(p.v) + ((size_t)t0 * p.hv + h) * p.dv * E;
-        const char *bb = reinterpret_cast<const char *>(p.beta + (size_t)t0 * p.hv + h);
-        const uint32_t krow_b = (uint32_t)krow * E, vrow_b = (uint32_t)vrow * E, brow_b = (uint32_t)p.hv * 4;
+        const uint32_t krow_b = (uint32_t)krow * E, vrow_b = (uint32_t)vrow * E;
 #pragma unroll
         for (int s = 0; s < CF::KIT; ++s) {
             const int it = tid + 64 * W * s;
@@ -378,13 +379,20 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
 #pragma unroll
             for (int t = 0; t < OT; ++t) F.qa[t] = RW::load_at(qb, qoff + 16u * t * E);
         }
+        if (m0 == 0 && m1 == kCk) {  // a full chunk: token 4 g + c at the lane's offset plus c rows
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t tm = (uint32_t)clampm(4 * g + c, m0, m1);
-            F.b[c] = *reinterpret_cast<const float *>(bb + tm * brow_b);
-            F.v[c] = RW::load1_at(vb, tm * vrow_b + (uint32_t)(row0 + x) * E);
+            for (int c = 0; c < 4; ++c) F.v[c] = RW::load1_at(vb, v_lane + (uint32_t)c * vrow_b);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t tm = (uint32_t)clampm(4 * g + c, m0, m1);
+                F.v[c] = RW::load1_at(vb, tm * vrow_b + (uint32_t)(row0 + x) * E);
+            }
         }
         const char *rec = reinterpret_cast<const char *>(p.ws + ((size_t)(sc.base + j) * p.hv + h) * REC);
+        // the betas of tokens 4 g .. 4 g + 3 as the prep kernel put them in the record
+        // (the same values; zero past the chunk's end)
+        F.b = *reinterpret_cast<const float4 *>(rec + 4u * (kRecBeta + 4 * g));
         F.trow = *reinterpret_cast<const float4 *>(rec + 4u * (kRecT + x * kCk + 4 * g));
         F.gam = *reinterpret_cast<const float4 *>(rec + 4u * (kRecGam + 4 * g));
         if constexpr (BW) {
@@ -465,7 +473,7 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const bool on = 4 * g + c >= m0 && 4 * g + c < m1;
-            bb[c] = on ? F.b[c] : 0.f;
+            bb[c] = on ? (c == 0 ? F.b.x : c == 1 ? F.b.y : c == 2 ? F.b.z : F.b.w) : 0.f;
             vraw[c] = on ? RW::widen1(F.v[c]) : 0.f;
             vb[c] = bb[c] * vraw[c];
         }
