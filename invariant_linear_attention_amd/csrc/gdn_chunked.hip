@@ -414,235 +414,245 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
     for (int c = 0; c < 4; ++c)
         if (4 * g + c < sc.c0 && p.in_r) Rkeep[c] = p.in_r[(((size_t)n * kCk + 4 * g + c) * p.hv + h) * p.dv + row0 + x];
 
-    CF F;
-    if (!LEAN && nch > 0) fetch(F, 0);
-    for (int j = 0; j < nch; ++j) {
-        int m0, m1;
-        int64_t t0;
-        geom(j, m0, m1, t0);
-        const bool full = m1 == kCk;
-        if constexpr (LEAN) fetch(F, j);
-
-        // keys into LDS (cached keys of a resumed chunk only when it closes here), the
-        // rest of this chunk's reads into working registers, then the next chunk's reads
-        if constexpr (LEAN) {
-            // zeros in the rows outside this call's tokens, and those rows read
-            // straight into LDS (the same values and zeros as below; no registers held
-            // for the rows; each row written by one loop only)
-            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    // The chunked form (MODE 0) reads two chunks ahead into alternating register sets,
+    // which it has the registers for; the walk keeps one set and four waves per SIMD.
+    constexpr int AHEAD = MODE == 0 ? 2 : 1;
+    CF FA, FB;
+    if (!LEAN && nch > 0) fetch(FA, 0);
+    if (AHEAD == 2 && nch > 1) fetch(FB, 1);
+    for (int j0 = 0; j0 < nch; j0 += AHEAD) {
 #pragma unroll
-            for (int s = 0; s < CF::KIT; ++s) {
-                const int it = tid + 64 * W * s;
-                const int m = it / (DK / 4);
-                if (m < m0 || m >= m1) {
-                    *reinterpret_cast<float4 *>(&Ks[m][4 * (it % (DK / 4))]) = z4;
-                    *reinterpret_cast<float4 *>(&Qs[m][4 * (it % (DK / 4))]) = z4;
+        for (int half = 0; half < AHEAD; ++half) {
+            const int j = j0 + half;
+            if (j >= nch) break;
+            CF &F = half ? FB : FA;  // (resolved at compile time)
+            int m0, m1;
+            int64_t t0;
+            geom(j, m0, m1, t0);
+            const bool full = m1 == kCk;
+            if constexpr (LEAN) fetch(F, j);
+
+            // keys into LDS (cached keys of a resumed chunk only when it closes here), the
+            // rest of this chunk's reads into working registers, then the next chunk's reads
+            if constexpr (LEAN) {
+                // zeros in the rows outside this call's tokens, and those rows read
+                // straight into LDS (the same values and zeros as below; no registers held
+                // for the rows; each row written by one loop only)
+                const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int s = 0; s < CF::KIT; ++s) {
+                    const int it = tid + 64 * W * s;
+                    const int m = it / (DK / 4);
+                    if (m < m0 || m >= m1) {
+                        *reinterpret_cast<float4 *>(&Ks[m][4 * (it % (DK / 4))]) = z4;
+                        *reinterpret_cast<float4 *>(&Qs[m][4 * (it % (DK / 4))]) = z4;
+                    }
+                }
+                const char *kb = static_cast<const char *>(p.k) + ((size_t)t0 * p.hk + kh) * DK * IO::ESZ;
+                const char *qb = static_cast<const char *>(p.q) + ((size_t)t0 * p.hk + kh) * DK * IO::ESZ;
+                const uint32_t krow_b = (uint32_t)krow * IO::ESZ;
+                for (int it = m0 * (DK / 4) + tid; it < m1 * (DK / 4); it += 64 * W) {
+                    const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+                    const uint32_t off = (uint32_t)m * krow_b + (uint32_t)c * IO::ESZ;
+                    const typename RW::T kw = RW::load_at(kb, off), qw = RW::load_at(qb, off);
+                    *reinterpret_cast<float4 *>(&Ks[m][c]) = RW::widen(kw);
+                    *reinterpret_cast<float4 *>(&Qs[m][c]) = RW::widen(qw);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < CF::KIT; ++s) {
+                    const int it = tid + 64 * W * s;
+                    const int m = it / (DK / 4);
+                    *reinterpret_cast<float4 *>(&Ks[m][4 * (it % (DK / 4))]) = RW::widen(RW::keep(F.kr[s], m >= m0 && m < m1));
                 }
             }
-            const char *kb = static_cast<const char *>(p.k) + ((size_t)t0 * p.hk + kh) * DK * IO::ESZ;
-            const char *qb = static_cast<const char *>(p.q) + ((size_t)t0 * p.hk + kh) * DK * IO::ESZ;
-            const uint32_t krow_b = (uint32_t)krow * IO::ESZ;
-            for (int it = m0 * (DK / 4) + tid; it < m1 * (DK / 4); it += 64 * W) {
-                const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
-                const uint32_t off = (uint32_t)m * krow_b + (uint32_t)c * IO::ESZ;
-                const typename RW::T kw = RW::load_at(kb, off), qw = RW::load_at(qb, off);
-                *reinterpret_cast<float4 *>(&Ks[m][c]) = RW::widen(kw);
-                *reinterpret_cast<float4 *>(&Qs[m][c]) = RW::widen(qw);
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < CF::KIT; ++s) {
-                const int it = tid + 64 * W * s;
-                const int m = it / (DK / 4);
-                *reinterpret_cast<float4 *>(&Ks[m][4 * (it % (DK / 4))]) = RW::widen(RW::keep(F.kr[s], m >= m0 && m < m1));
-            }
-        }
-        if (m0 > 0 && full) {
-            for (int it = tid; it < m0 * (DK / 4); it += 64 * W) {
-                const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
-                *reinterpret_cast<float4 *>(&Ks[m][c]) =
-                    *reinterpret_cast<const float4 *>(p.in_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + c);
-            }
-        }
-        float4 qv[BW || LEAN ? 1 : OT];
-        if constexpr (!BW && !LEAN) {
-#pragma unroll
-            for (int t = 0; t < OT; ++t) qv[t] = RW::widen(RW::keep(F.qa[t], x >= m0 && x < m1));
-        }
-        float vb[4], bb[4], vraw[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const bool on = 4 * g + c >= m0 && 4 * g + c < m1;
-            bb[c] = on ? (c == 0 ? F.b.x : c == 1 ? F.b.y : c == 2 ? F.b.z : F.b.w) : 0.f;
-            vraw[c] = on ? RW::widen1(F.v[c]) : 0.f;
-            vb[c] = bb[c] * vraw[c];
-        }
-        const float4 trow = F.trow, brow = F.brow, gam = F.gam, dwv = F.dw;
-        const float g15 = F.g15;
-        if constexpr (!LEAN) fetch(F, j + 1);
-        if constexpr (BW) {
-            // the state at this chunk's start (stored after the next chunk's reads, so
-            // that waiting for those does not wait for these)
-            // (tile-major: [dk / 16 column tiles][dv rows][16 columns], so that each store
-            // instruction writes 1 KB in one piece; nontemporal, read back only by the
-            // reverse walk)
-            float *dst = p.ck + ((size_t)(sc.base + j) * p.hv + h) * p.dv * DK + (size_t)(row0 + x) * 16 + 4 * g;
-#pragma unroll
-            for (int t = 0; t < OT; ++t)
-                __builtin_nontemporal_store(S[t], reinterpret_cast<f4 *>(dst + (size_t)(t_first + t) * p.dv * 16));
-        }
-        lds_barrier();
-
-        // partial products of this wave's quarters
-        f4 Pq[OQ], Zq[OQ];
-#pragma unroll
-        for (int q = 0; q < OQ; ++q) {
-            Pq[q] = f4_zero();
-            Zq[q] = f4_zero();
-            // (lean: operands read from LDS one quarter at a time, not all up front)
-            if constexpr (LEAN) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int tt = 0; tt < QT; ++tt) {
-                const int t = q * QT + tt;  // the wave's tile index
-                const float4 ka = *reinterpret_cast<const float4 *>(&Ks[x][16 * (t_first + t) + 4 * g]);
-                if constexpr (BW) {
-                    Pq[q] = mfma_16x16x4(ka.x, S[t][0], Pq[q]);
-                    Pq[q] = mfma_16x16x4(ka.y, S[t][1], Pq[q]);
-                    Pq[q] = mfma_16x16x4(ka.z, S[t][2], Pq[q]);
-                    Pq[q] = mfma_16x16x4(ka.w, S[t][3], Pq[q]);
-                } else {
-                    const float4 qa = LEAN ? *reinterpret_cast<const float4 *>(&Qs[x][16 * (t_first + t) + 4 * g])
-                                           : qv[LEAN ? 0 : t];
-                    Pq[q] = mfma_16x16x4(ka.x, S[t][0], Pq[q]);
-                    Zq[q] = mfma_16x16x4(qa.x, S[t][0], Zq[q]);
-                    Pq[q] = mfma_16x16x4(ka.y, S[t][1], Pq[q]);
-                    Zq[q] = mfma_16x16x4(qa.y, S[t][1], Zq[q]);
-                    Pq[q] = mfma_16x16x4(ka.z, S[t][2], Pq[q]);
-                    Zq[q] = mfma_16x16x4(qa.z, S[t][2], Zq[q]);
-                    Pq[q] = mfma_16x16x4(ka.w, S[t][3], Pq[q]);
-                    Zq[q] = mfma_16x16x4(qa.w, S[t][3], Zq[q]);
+            if (m0 > 0 && full) {
+                for (int it = tid; it < m0 * (DK / 4); it += 64 * W) {
+                    const int m = it / (DK / 4), c = 4 * (it % (DK / 4));
+                    *reinterpret_cast<float4 *>(&Ks[m][c]) =
+                        *reinterpret_cast<const float4 *>(p.in_k + (((size_t)n * kCk + m) * p.hk + kh) * DK + c);
                 }
             }
-        }
-        f4 P4[4], Z4[4];
-        if constexpr (W == 1) {
+            float4 qv[BW || LEAN ? 1 : OT];
+            if constexpr (!BW && !LEAN) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                P4[q] = Pq[q];
-                Z4[q] = Zq[q];
+                for (int t = 0; t < OT; ++t) qv[t] = RW::widen(RW::keep(F.qa[t], x >= m0 && x < m1));
             }
-        } else {
+            float vb[4], bb[4], vraw[4];
 #pragma unroll
-            for (int q = 0; q < OQ; ++q) {
-                const int gq = wave * OQ + q;
-                Xch[gq][lane] = make_float4(Pq[q][0], Pq[q][1], Pq[q][2], Pq[q][3]);
-                if constexpr (!BW) Xch[4 + gq][lane] = make_float4(Zq[q][0], Zq[q][1], Zq[q][2], Zq[q][3]);
+            for (int c = 0; c < 4; ++c) {
+                const bool on = 4 * g + c >= m0 && 4 * g + c < m1;
+                bb[c] = on ? (c == 0 ? F.b.x : c == 1 ? F.b.y : c == 2 ? F.b.z : F.b.w) : 0.f;
+                vraw[c] = on ? RW::widen1(F.v[c]) : 0.f;
+                vb[c] = bb[c] * vraw[c];
+            }
+            const float4 trow = F.trow, brow = F.brow, gam = F.gam, dwv = F.dw;
+            const float g15 = F.g15;
+            if constexpr (!LEAN) fetch(F, j + AHEAD);
+            if constexpr (BW) {
+                // the state at this chunk's start (stored after the next chunk's reads, so
+                // that waiting for those does not wait for these)
+                // (tile-major: [dk / 16 column tiles][dv rows][16 columns], so that each store
+                // instruction writes 1 KB in one piece; nontemporal, read back only by the
+                // reverse walk)
+                float *dst = p.ck + ((size_t)(sc.base + j) * p.hv + h) * p.dv * DK + (size_t)(row0 + x) * 16 + 4 * g;
+#pragma unroll
+                for (int t = 0; t < OT; ++t)
+                    __builtin_nontemporal_store(S[t], reinterpret_cast<f4 *>(dst + (size_t)(t_first + t) * p.dv * 16));
             }
             lds_barrier();
+
+            // partial products of this wave's quarters
+            f4 Pq[OQ], Zq[OQ];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 a4 = Xch[q][lane];
-                P4[q] = f4{a4.x, a4.y, a4.z, a4.w};
-                if constexpr (!BW) {
-                    const float4 b4 = Xch[4 + q][lane];
-                    Z4[q] = f4{b4.x, b4.y, b4.z, b4.w};
-                } else {
-                    Z4[q] = f4_zero();
+            for (int q = 0; q < OQ; ++q) {
+                Pq[q] = f4_zero();
+                Zq[q] = f4_zero();
+                // (lean: operands read from LDS one quarter at a time, not all up front)
+                if constexpr (LEAN) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int tt = 0; tt < QT; ++tt) {
+                    const int t = q * QT + tt;  // the wave's tile index
+                    const float4 ka = *reinterpret_cast<const float4 *>(&Ks[x][16 * (t_first + t) + 4 * g]);
+                    if constexpr (BW) {
+                        Pq[q] = mfma_16x16x4(ka.x, S[t][0], Pq[q]);
+                        Pq[q] = mfma_16x16x4(ka.y, S[t][1], Pq[q]);
+                        Pq[q] = mfma_16x16x4(ka.z, S[t][2], Pq[q]);
+                        Pq[q] = mfma_16x16x4(ka.w, S[t][3], Pq[q]);
+                    } else {
+                        const float4 qa = LEAN ? *reinterpret_cast<const float4 *>(&Qs[x][16 * (t_first + t) + 4 * g])
+                                               : qv[LEAN ? 0 : t];
+                        Pq[q] = mfma_16x16x4(ka.x, S[t][0], Pq[q]);
+                        Zq[q] = mfma_16x16x4(qa.x, S[t][0], Zq[q]);
+                        Pq[q] = mfma_16x16x4(ka.y, S[t][1], Pq[q]);
+                        Zq[q] = mfma_16x16x4(qa.y, S[t][1], Zq[q]);
+                        Pq[q] = mfma_16x16x4(ka.z, S[t][2], Pq[q]);
+                        Zq[q] = mfma_16x16x4(qa.z, S[t][2], Zq[q]);
+                        Pq[q] = mfma_16x16x4(ka.w, S[t][3], Pq[q]);
+                        Zq[q] = mfma_16x16x4(qa.w, S[t][3], Zq[q]);
+                    }
                 }
             }
-        }
-        f4 P, Z;
+            f4 P4[4], Z4[4];
+            if constexpr (W == 1) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            P[c] = (P4[0][c] + P4[1][c]) + (P4[2][c] + P4[3][c]);
-            Z[c] = (Z4[0][c] + Z4[1][c]) + (Z4[2][c] + Z4[3][c]);
-        }
-
-        // the chunk-end update's key operands (K^T tiles of this wave), read early
-        const bool fold = BW || full;
-        float kt[LEAN ? 1 : OT][4];
-        if (!LEAN && fold) {
-#pragma unroll
-            for (int t = 0; t < OT; ++t)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) kt[t][c] = Ks[4 * g + c][16 * (t_first + t) + x];
-        }
-
-        // R_m = fma(-(beta_m Gam_m), P_m, beta_m v_m) for this call's tokens, cached R
-        // for the chunk's earlier tokens, 0 for tokens not reached yet
-        const float gm[4] = {gam.x, gam.y, gam.z, gam.w};
-        f4 R, OC, X4;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int m = 4 * g + c;
-            const bool on = m >= m0 && m < m1;
-            if constexpr (BW) {
-                // x = v - Gam P (kept for the reverse walk; zero past the chunk's end), R = beta x
-                X4[c] = on ? __builtin_fmaf(-gm[c], P[c], vraw[c]) : 0.f;
-                R[c] = bb[c] * X4[c];
+                for (int q = 0; q < 4; ++q) {
+                    P4[q] = Pq[q];
+                    Z4[q] = Zq[q];
+                }
             } else {
-                const float fresh = __builtin_fmaf(-(bb[c] * gm[c]), P[c], vb[c]);
-                R[c] = on ? fresh : (m < m0 ? Rkeep[c] : 0.f);
-                Rkeep[c] = on ? fresh : Rkeep[c];
-                OC[c] = gm[c] * Z[c];
+#pragma unroll
+                for (int q = 0; q < OQ; ++q) {
+                    const int gq = wave * OQ + q;
+                    Xch[gq][lane] = make_float4(Pq[q][0], Pq[q][1], Pq[q][2], Pq[q][3]);
+                    if constexpr (!BW) Xch[4 + gq][lane] = make_float4(Zq[q][0], Zq[q][1], Zq[q][2], Zq[q][3]);
+                }
+                lds_barrier();
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 a4 = Xch[q][lane];
+                    P4[q] = f4{a4.x, a4.y, a4.z, a4.w};
+                    if constexpr (!BW) {
+                        const float4 b4 = Xch[4 + q][lane];
+                        Z4[q] = f4{b4.x, b4.y, b4.z, b4.w};
+                    } else {
+                        Z4[q] = f4_zero();
+                    }
+                }
             }
-        }
-
-        if constexpr (BW) {
-            // x of the chunk's 16 tokens on the tile's 16 rows: [row][token] per (chunk
-            // slot, value head, row tile), so that lane (x, g) holds tokens 4 g .. 4 g + 3
-            // of row x as one 16-byte piece and wave 0 writes the tile's 1 KB in one store
-            const auto xrsrc = buf_rsrc(p.xv + (((size_t)(sc.base + j) * p.hv + h) * p.dv + row0) * kCk, 1024u);
-            buf_store_f4_nt(xrsrc, wave == 0 ? (uint32_t)(x * kCk + 4 * g) * 4u : kDropped, X4);
-        }
-
-        // U = T R, then O = Gam Z + B U (instruction c adds the tokens 4 g + c)
-        f4 U = f4_zero();
-        U = mfma_16x16x4(trow.x, R[0], U);
-        U = mfma_16x16x4(trow.y, R[1], U);
-        U = mfma_16x16x4(trow.z, R[2], U);
-        U = mfma_16x16x4(trow.w, R[3], U);
+            f4 P, Z;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) U[c] = U[c] + 0.f;
-        if constexpr (!BW) {
-        // this chunk's rows of the outputs, as buffer stores that every lane issues
-        // (kDropped where there is nothing to write)
-        const uint32_t col_b = (uint32_t)(h * p.dv + row0 + x);
-        const auto orsrc = buf_rsrc(static_cast<const char *>(p.out) + (size_t)t0 * vrow * IO::ESZ,
-                                    (uint32_t)(m1 * vrow * IO::ESZ));
-        f4 O = OC;
-        O = mfma_16x16x4(brow.x, U[0], O);
-        O = mfma_16x16x4(brow.y, U[1], O);
-        O = mfma_16x16x4(brow.z, U[2], O);
-        O = mfma_16x16x4(brow.w, U[3], O);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int m = 4 * g + c;
-            const bool st = wave == 0 && m >= m0 && m < m1;
-            buf_store1<IO>(orsrc, st ? ((uint32_t)m * (uint32_t)vrow + col_b) * (uint32_t)IO::ESZ : kDropped, O[c] + 0.f);
-        }
-        }
-
-        // chunk complete: S^T = Gam_15 S^T + K^T W, W[s][row] = Gam_{15,s} u_s (own tiles)
-        if (fold) {
-            const float w0 = dwv.x * U[0], w1 = dwv.y * U[1], w2 = dwv.z * U[2], w3 = dwv.w * U[3];
-#pragma unroll
-            for (int t = 0; t < OT; ++t) {
-                f4 C = f4{g15 * S[t][0], g15 * S[t][1], g15 * S[t][2], g15 * S[t][3]};
-                float k4[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) k4[c] = LEAN ? Ks[4 * g + c][16 * (t_first + t) + x] : kt[LEAN ? 0 : t][c];
-                C = mfma_16x16x4(k4[0], w0, C);
-                C = mfma_16x16x4(k4[1], w1, C);
-                C = mfma_16x16x4(k4[2], w2, C);
-                C = mfma_16x16x4(k4[3], w3, C);
-                S[t] = C;
+            for (int c = 0; c < 4; ++c) {
+                P[c] = (P4[0][c] + P4[1][c]) + (P4[2][c] + P4[3][c]);
+                Z[c] = (Z4[0][c] + Z4[1][c]) + (Z4[2][c] + Z4[3][c]);
             }
-            folded = true;
+
+            // the chunk-end update's key operands (K^T tiles of this wave), read early
+            const bool fold = BW || full;
+            float kt[LEAN ? 1 : OT][4];
+            if (!LEAN && fold) {
+#pragma unroll
+                for (int t = 0; t < OT; ++t)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) kt[t][c] = Ks[4 * g + c][16 * (t_first + t) + x];
+            }
+
+            // R_m = fma(-(beta_m Gam_m), P_m, beta_m v_m) for this call's tokens, cached R
+            // for the chunk's earlier tokens, 0 for tokens not reached yet
+            const float gm[4] = {gam.x, gam.y, gam.z, gam.w};
+            f4 R, OC, X4;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int m = 4 * g + c;
+                const bool on = m >= m0 && m < m1;
+                if constexpr (BW) {
+                    // x = v - Gam P (kept for the reverse walk; zero past the chunk's end), R = beta x
+                    X4[c] = on ? __builtin_fmaf(-gm[c], P[c], vraw[c]) : 0.f;
+                    R[c] = bb[c] * X4[c];
+                } else {
+                    const float fresh = __builtin_fmaf(-(bb[c] * gm[c]), P[c], vb[c]);
+                    R[c] = on ? fresh : (m < m0 ? Rkeep[c] : 0.f);
+                    Rkeep[c] = on ? fresh : Rkeep[c];
+                    OC[c] = gm[c] * Z[c];
+                }
+            }
+
+            if constexpr (BW) {
+                // x of the chunk's 16 tokens on the tile's 16 rows: [row][token] per (chunk
+                // slot, value head, row tile), so that lane (x, g) holds tokens 4 g .. 4 g + 3
+                // of row x as one 16-byte piece and wave 0 writes the tile's 1 KB in one store
+                const auto xrsrc = buf_rsrc(p.xv + (((size_t)(sc.base + j) * p.hv + h) * p.dv + row0) * kCk, 1024u);
+                buf_store_f4_nt(xrsrc, wave == 0 ? (uint32_t)(x * kCk + 4 * g) * 4u : kDropped, X4);
+            }
+
+            // U = T R, then O = Gam Z + B U (instruction c adds the tokens 4 g + c)
+            f4 U = f4_zero();
+            U = mfma_16x16x4(trow.x, R[0], U);
+            U = mfma_16x16x4(trow.y, R[1], U);
+            U = mfma_16x16x4(trow.z, R[2], U);
+            U = mfma_16x16x4(trow.w, R[3], U);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) U[c] = U[c] + 0.f;
+            if constexpr (!BW) {
+            // this chunk's rows of the outputs, as buffer stores that every lane issues
+            // (kDropped where there is nothing to write)
+            const uint32_t col_b = (uint32_t)(h * p.dv + row0 + x);
+            const auto orsrc = buf_rsrc(static_cast<const char *>(p.out) + (size_t)t0 * vrow * IO::ESZ,
+                                        (uint32_t)(m1 * vrow * IO::ESZ));
+            f4 O = OC;
+            O = mfma_16x16x4(brow.x, U[0], O);
+            O = mfma_16x16x4(brow.y, U[1], O);
+            O = mfma_16x16x4(brow.z, U[2], O);
+            O = mfma_16x16x4(brow.w, U[3], O);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int m = 4 * g + c;
+                const bool st = wave == 0 && m >= m0 && m < m1;
+                buf_store1<IO>(orsrc, st ? ((uint32_t)m * (uint32_t)vrow + col_b) * (uint32_t)IO::ESZ : kDropped, O[c] + 0.f);
+            }
+            }
+
+            // chunk complete: S^T = Gam_15 S^T + K^T W, W[s][row] = Gam_{15,s} u_s (own tiles)
+            if (fold) {
+                const float w0 = dwv.x * U[0], w1 = dwv.y * U[1], w2 = dwv.z * U[2], w3 = dwv.w * U[3];
+#pragma unroll
+                for (int t = 0; t < OT; ++t) {
+                    f4 C = f4{g15 * S[t][0], g15 * S[t][1], g15 * S[t][2], g15 * S[t][3]};
+                    float k4[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) k4[c] = LEAN ? Ks[4 * g + c][16 * (t_first + t) + x] : kt[LEAN ? 0 : t][c];
+                    C = mfma_16x16x4(k4[0], w0, C);
+                    C = mfma_16x16x4(k4[1], w1, C);
+                    C = mfma_16x16x4(k4[2], w2, C);
+                    C = mfma_16x16x4(k4[3], w3, C);
+                    S[t] = C;
+                }
+                folded = true;
+            }
+            last_m0 = full ? 0 : m0;
+            mo = full ? 0 : m1;
+            lds_barrier();  // Ks and Xch are refilled by the next chunk
         }
-        last_m0 = full ? 0 : m0;
-        mo = full ? 0 : m1;
-        lds_barrier();  // Ks and Xch are refilled by the next chunk
     }
 
     if constexpr (BW) {
