@@ -386,6 +386,8 @@ def main():
 
     # ------------------------------------------------ other prefill workloads
     workloads = None
+    late_copies = []  # device -> host copies of checked outputs, run after the benchmark step
+    got_gc = {}
     if not args.no_workloads:
         workloads = {}
 
@@ -625,107 +627,6 @@ def main():
         del lc
         prefill_line("mixed_batch_64", synth.mixed_batch(1004))
 
-        # The backward (gdn_bwd_varlen) on the benchmark batch, dL/dout ~ N(0, 1) in
-        # bf16 and dL/dhT ~ N(0, 1), against the FP32-VALU roofline on its algorithmic
-        # work: 18 flops per state element and token (recompute p and the write: 5;
-        # the adjoint D += dO q^T, du = D k, D -= beta du k^T, D *= a: 7; dq = S^T dO,
-        # dk = D^T u + S^T w: 6).
-        gen = torch.Generator().manual_seed(1006)
-        dout_c = torch.randn(tuple(w.v.shape), generator=gen).to(torch.bfloat16)
-        dhT_c = torch.randn((w.n_seqs, 32, 128, 128), generator=gen)
-        dout_d, dhT_d = dout_c.to(dev), dhT_c.to(dev)
-        bdims = gdn.make_dims(d["q"], d["v"], w.n_seqs, T)
-        ws = torch.empty(gdn.gdn_bwd_workspace_size(bdims), dtype=torch.uint8, device=dev)
-        grads = gdn.gdn_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
-                                   workspace=ws, stream=stream)
-
-        def bwd(_i):
-            gdn.gdn_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
-                               workspace=ws, grads=grads, stream=stream)
-
-        per_b, _, _ = time_launches(bwd, args.steps, 3, stream)
-        msb = float(np.median(per_b))
-        # the training forward (also saves p_t) and the backward fed its p_t
-        out_t = torch.empty((T, 32, 128), dtype=torch.bfloat16, device=dev)
-        hT_t = torch.empty((w.n_seqs, 32, 128, 128), dtype=torch.float32, device=dev)
-        sp_t = torch.empty((T, 32, 128), dtype=torch.float32, device=dev)
-
-        def fwd_train(_i):
-            gdn.gdn_fwd_varlen_train(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], out=out_t, hT=hT_t,
-                                     saved_p=sp_t, stream=stream)
-
-        per_ft, _, _ = time_launches(fwd_train, args.steps, 3, stream)
-
-        def bwd_saved(_i):
-            gdn.gdn_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
-                               workspace=ws, grads=grads, stream=stream, saved_p=sp_t, hT=hT_t)
-
-        per_bs, _, _ = time_launches(bwd_saved, args.steps, 3, stream)
-        bwd(0)
-        torch.cuda.synchronize()
-        bflops = 18.0 * 128 * 128 * 32 * T
-        got_g = {"dq": grads["dq"][:, 0:1].cpu(), "dk": grads["dk"][:, 0:1].cpu(), "dv": grads["dv"][:, 0:2].cpu(),
-                 "dbeta": grads["dbeta"][:, 0:2].cpu(), "dg": grads["dg"][:, 0:2].cpu(),
-                 "dh0": grads["dh0"][:, 0:2].cpu()}
-        # the chunked backward (gdn_bwd_chunked, matrix cores) on the same inputs
-        ws_b_bytes = int(ws.numel())
-        del ws
-        ws_cb = torch.empty(gdn.gdn_bwd_chunked_workspace_size(bdims), dtype=torch.uint8, device=dev)
-        grads_c = gdn.gdn_bwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
-                                      workspace=ws_cb, stream=stream)
-
-        def bwd_chunked(_i):
-            gdn.gdn_bwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
-                                workspace=ws_cb, grads=grads_c, stream=stream)
-
-        per_bc, _, _ = time_launches(bwd_chunked, args.steps, 3, stream)
-        bwd_chunked(0)
-        torch.cuda.synchronize()
-        msbc = float(np.median(per_bc))
-        got_gc = {"dq": grads_c["dq"][:, 0:1].cpu(), "dk": grads_c["dk"][:, 0:1].cpu(),
-                  "dv": grads_c["dv"][:, 0:2].cpu(), "dbeta": grads_c["dbeta"][:, 0:2].cpu(),
-                  "dg": grads_c["dg"][:, 0:2].cpu(), "dh0": grads_c["dh0"][:, 0:2].cpu()}
-        rec_bc = {"tokens": T, "n_seqs": w.n_seqs, "ms_median": msbc, "tokens_per_s": T / (msbc / 1e3),
-                  "launch_ms_percentiles": percentiles(per_bc), "launches": 5,
-                  "workspace_bytes": int(ws_cb.numel()),
-                  "roofline": {"bound": "mfma", "achieved": bflops / (msbc / 1e3) / 1e12,
-                               "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": bflops / (msbc / 1e3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
-                               "flops_per_launch": bflops,
-                               "traffic": traffic_from_profile("backward_chunked", src_hash)}}
-        workloads["backward_chunked_prefill"] = rec_bc
-        del ws_cb, grads_c
-        rec_b = {"tokens": T, "n_seqs": w.n_seqs, "ms_median": msb, "tokens_per_s": T / (msb / 1e3),
-                 "launch_ms_percentiles": percentiles(per_b),
-                 "launches": 6, "workspace_bytes": ws_b_bytes,
-                 "train_forward_ms_median": float(np.median(per_ft)),
-                 "ms_median_with_saved_p": float(np.median(per_bs)),
-                 "roofline": {"bound": "alu", "achieved": bflops / (msb / 1e3) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
-                              "unit": "TFLOP/s", "frac": bflops / (msb / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
-                              "flops_per_launch": bflops}}
-        workloads["backward_varlen_prefill"] = rec_b
-        del dout_d, dhT_d, grads, out_t, hT_t, sp_t
-        bwd_ref = {}
-
-        def bwd_oracle():
-            if not bwd_ref:
-                s0 = synth.head_slice(w, 0)
-                bwd_ref.update(oracle.gdn_backward(s0.q, s0.k, s0.v, s0.g, s0.beta, s0.cu_seqlens,
-                                                   dout_c[:, 0:2].contiguous(), h0=s0.h0,
-                                                   dhT=dhT_c[:, 0:2].contiguous()))
-            return bwd_ref
-
-        def bwd_check():
-            rb = bwd_oracle()
-            return {"kh0_grads": {k: rel(v.numpy(), rb[k]) for k, v in got_g.items()}}
-
-        def bwd_chunked_check():
-            rb = bwd_oracle()
-            return {"kh0_grads": {k: rel(v.numpy(), rb[k]) for k, v in got_gc.items()}}
-        checks.append((rec_b, "parity", bwd_check))
-        checks.append((rec_bc, "parity", bwd_chunked_check))
-        progress("backward %.3f ms, chunked backward %.3f ms" % (msb, msbc))
-
         # The chunked form with a replaying decode (gdn_fwd_chunked, matrix cores for the
         # products with the state): the benchmark batch as one prefill from h0, and one
         # in-place decode step at B = 256 from states a chunked prefill left at every
@@ -812,11 +713,117 @@ def main():
         checks.append((rec_ch, "parity", chunked_check))
         progress("chunked form %.3f ms, decode B=256 %.1f us" % (msch, float(np.mean(per_cd2)) * 1e3))
 
+        # The backward (gdn_bwd_varlen) on the benchmark batch, dL/dout ~ N(0, 1) in
+        # bf16 and dL/dhT ~ N(0, 1), against the FP32-VALU roofline on its algorithmic
+        # work: 18 flops per state element and token (recompute p and the write: 5;
+        # the adjoint D += dO q^T, du = D k, D -= beta du k^T, D *= a: 7; dq = S^T dO,
+        # dk = D^T u + S^T w: 6).
+        gen = torch.Generator().manual_seed(1006)
+        dout_c = torch.randn(tuple(w.v.shape), generator=gen).to(torch.bfloat16)
+        dhT_c = torch.randn((w.n_seqs, 32, 128, 128), generator=gen)
+        dout_d, dhT_d = dout_c.to(dev), dhT_c.to(dev)
+        bdims = gdn.make_dims(d["q"], d["v"], w.n_seqs, T)
+        ws = torch.empty(gdn.gdn_bwd_workspace_size(bdims), dtype=torch.uint8, device=dev)
+        grads = gdn.gdn_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                                   workspace=ws, stream=stream)
+
+        def bwd(_i):
+            gdn.gdn_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                               workspace=ws, grads=grads, stream=stream)
+
+        per_b, _, _ = time_launches(bwd, args.steps, 3, stream)
+        msb = float(np.median(per_b))
+        # the training forward (also saves p_t) and the backward fed its p_t
+        out_t = torch.empty((T, 32, 128), dtype=torch.bfloat16, device=dev)
+        hT_t = torch.empty((w.n_seqs, 32, 128, 128), dtype=torch.float32, device=dev)
+        sp_t = torch.empty((T, 32, 128), dtype=torch.float32, device=dev)
+
+        def fwd_train(_i):
+            gdn.gdn_fwd_varlen_train(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], out=out_t, hT=hT_t,
+                                     saved_p=sp_t, stream=stream)
+
+        per_ft, _, _ = time_launches(fwd_train, args.steps, 3, stream)
+
+        def bwd_saved(_i):
+            gdn.gdn_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                               workspace=ws, grads=grads, stream=stream, saved_p=sp_t, hT=hT_t)
+
+        per_bs, _, _ = time_launches(bwd_saved, args.steps, 3, stream)
+        bwd(0)
+        torch.cuda.synchronize()
+        bflops = 18.0 * 128 * 128 * 32 * T
+        got_g = {"dq": grads["dq"][:, 0:1].cpu(), "dk": grads["dk"][:, 0:1].cpu(), "dv": grads["dv"][:, 0:2].cpu(),
+                 "dbeta": grads["dbeta"][:, 0:2].cpu(), "dg": grads["dg"][:, 0:2].cpu(),
+                 "dh0": grads["dh0"][:, 0:2].cpu()}
+        # the chunked backward (gdn_bwd_chunked, matrix cores) on the same inputs
+        ws_b_bytes = int(ws.numel())
+        del ws
+        ws_cb = torch.empty(gdn.gdn_bwd_chunked_workspace_size(bdims), dtype=torch.uint8, device=dev)
+        grads_c = gdn.gdn_bwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                                      workspace=ws_cb, stream=stream)
+
+        def bwd_chunked(_i):
+            gdn.gdn_bwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                                workspace=ws_cb, grads=grads_c, stream=stream)
+
+        # Timed last, right before the benchmark step, so that the step's warm-ups start
+        # on a chip under load (after even a few idle milliseconds the clock needs tens
+        # of milliseconds of load to climb back); its gradients are copied for the
+        # check only after the step.
+        per_bc, _, _ = time_launches(bwd_chunked, args.steps, 3, stream)
+        msbc = float(np.median(per_bc))
+        late_copies.append(lambda: got_gc.update(
+            {"dq": grads_c["dq"][:, 0:1].cpu(), "dk": grads_c["dk"][:, 0:1].cpu(),
+             "dv": grads_c["dv"][:, 0:2].cpu(), "dbeta": grads_c["dbeta"][:, 0:2].cpu(),
+             "dg": grads_c["dg"][:, 0:2].cpu(), "dh0": grads_c["dh0"][:, 0:2].cpu()}))
+        rec_bc = {"tokens": T, "n_seqs": w.n_seqs, "ms_median": msbc, "tokens_per_s": T / (msbc / 1e3),
+                  "launch_ms_percentiles": percentiles(per_bc), "launches": 5,
+                  "workspace_bytes": int(ws_cb.numel()),
+                  "roofline": {"bound": "mfma", "achieved": bflops / (msbc / 1e3) / 1e12,
+                               "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": bflops / (msbc / 1e3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
+                               "flops_per_launch": bflops,
+                               "traffic": traffic_from_profile("backward_chunked", src_hash)}}
+        workloads["backward_chunked_prefill"] = rec_bc
+        rec_b = {"tokens": T, "n_seqs": w.n_seqs, "ms_median": msb, "tokens_per_s": T / (msb / 1e3),
+                 "launch_ms_percentiles": percentiles(per_b),
+                 "launches": 6, "workspace_bytes": ws_b_bytes,
+                 "train_forward_ms_median": float(np.median(per_ft)),
+                 "ms_median_with_saved_p": float(np.median(per_bs)),
+                 "roofline": {"bound": "alu", "achieved": bflops / (msb / 1e3) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": bflops / (msb / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                              "flops_per_launch": bflops}}
+        workloads["backward_varlen_prefill"] = rec_b
+        del dout_d, dhT_d, grads, out_t, hT_t, sp_t
+        bwd_ref = {}
+
+        def bwd_oracle():
+            if not bwd_ref:
+                s0 = synth.head_slice(w, 0)
+                bwd_ref.update(oracle.gdn_backward(s0.q, s0.k, s0.v, s0.g, s0.beta, s0.cu_seqlens,
+                                                   dout_c[:, 0:2].contiguous(), h0=s0.h0,
+                                                   dhT=dhT_c[:, 0:2].contiguous()))
+            return bwd_ref
+
+        def bwd_check():
+            rb = bwd_oracle()
+            return {"kh0_grads": {k: rel(v.numpy(), rb[k]) for k, v in got_g.items()}}
+
+        def bwd_chunked_check():
+            rb = bwd_oracle()
+            return {"kh0_grads": {k: rel(v.numpy(), rb[k]) for k, v in got_gc.items()}}
+        checks.append((rec_b, "parity", bwd_check))
+        checks.append((rec_bc, "parity", bwd_chunked_check))
+        progress("backward %.3f ms, chunked backward %.3f ms" % (msb, msbc))
+
     # ------------------------------------------------ the benchmark step
     # W warm-up launches queued right before the K timed ones; then the timed
     # outputs are re-checked against the oracle on every head.
     per, queued, span = time_launches(prefill, args.steps, args.warmup, stream)
     torch.cuda.synchronize()
+    for copy in late_copies:
+        copy()
+    late_copies.clear()
     clock = gpu_clock()
     ms = float(np.mean(per))
     ms_med = float(np.median(per))
