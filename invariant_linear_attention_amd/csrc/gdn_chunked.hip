@@ -379,7 +379,7 @@ void gdn_chunk_main_kernel(ChunkedParams p) {
 #pragma unroll
             for (int t = 0; t < OT; ++t) F.qa[t] = RW::load_at(qb, qoff + 16u * t * E);
         }
-        if (m0 == 0 && m1 == kCk) {  // a full chunk: token 4 g + c at the lane's offset plus c rows
+        if (!LEAN && m0 == 0 && m1 == kCk) {  // a full chunk: token 4 g + c at the lane's offset plus c rows
 #pragma unroll
             for (int c = 0; c < 4; ++c) F.v[c] = RW::load1_at(vb, v_lane + (uint32_t)c * vrow_b);
         } else {
