@@ -91,7 +91,7 @@ __device__ __forceinline__ SeqChunks seq_chunks(const ChunkedParams &p, int n) {
 // With BW (the backward's forward walk) the record is kChunkRecBwd floats and also
 // holds Gam_{m,s} for s <= m and Gam_{m,s} (k_m . k_s) for s < m.
 template <int DK, class IO, bool BW>
-__global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(ChunkedParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void gdn_chunk_prep_kernel(ChunkedParams p) {
     constexpr int NT = DK / 16;
     constexpr int REC = BW ? kChunkRecBwd : kChunkRec;
     constexpr int KP = DK + 4;  // padded LDS row
