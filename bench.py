@@ -387,7 +387,7 @@ def main():
     # ------------------------------------------------ other prefill workloads
     workloads = None
     late_copies = []  # device -> host copies of checked outputs, run after the benchmark step
-    got_gc = {}
+    got_g = {}
     if not args.no_workloads:
         workloads = {}
 
@@ -731,9 +731,41 @@ def main():
             gdn.gdn_bwd_varlen(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
                                workspace=ws, grads=grads, stream=stream)
 
+        bflops = 18.0 * 128 * 128 * 32 * T
+        ws_b_bytes = int(ws.numel())
+        # the chunked backward (gdn_bwd_chunked, matrix cores) on the same inputs
+        ws_cb = torch.empty(gdn.gdn_bwd_chunked_workspace_size(bdims), dtype=torch.uint8, device=dev)
+        grads_c = gdn.gdn_bwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                                      workspace=ws_cb, stream=stream)
+
+        def bwd_chunked(_i):
+            gdn.gdn_bwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
+                                workspace=ws_cb, grads=grads_c, stream=stream)
+
+        per_bc, _, _ = time_launches(bwd_chunked, args.steps, 3, stream)
+        msbc = float(np.median(per_bc))
+        got_gc = {"dq": grads_c["dq"][:, 0:1].cpu(), "dk": grads_c["dk"][:, 0:1].cpu(),
+                  "dv": grads_c["dv"][:, 0:2].cpu(), "dbeta": grads_c["dbeta"][:, 0:2].cpu(),
+                  "dg": grads_c["dg"][:, 0:2].cpu(), "dh0": grads_c["dh0"][:, 0:2].cpu()}
+        rec_bc = {"tokens": T, "n_seqs": w.n_seqs, "ms_median": msbc, "tokens_per_s": T / (msbc / 1e3),
+                  "launch_ms_percentiles": percentiles(per_bc), "launches": 5,
+                  "workspace_bytes": int(ws_cb.numel()),
+                  "roofline": {"bound": "mfma", "achieved": bflops / (msbc / 1e3) / 1e12,
+                               "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": bflops / (msbc / 1e3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
+                               "flops_per_launch": bflops,
+                               "traffic": traffic_from_profile("backward_chunked", src_hash)}}
+        workloads["backward_chunked_prefill"] = rec_bc
+        del ws_cb, grads_c
+
+        # The recurrent backward, the training forward (also saves p_t) and the backward
+        # fed its p_t are timed last, right before the benchmark step, so that the
+        # step's warm-ups start on a chip under load of the same (vector ALU) kind:
+        # after even a few idle milliseconds the clock needs tens of milliseconds of
+        # load to climb back.  The checked gradients are those of the plain backward,
+        # formed and copied only after the step.
         per_b, _, _ = time_launches(bwd, args.steps, 3, stream)
         msb = float(np.median(per_b))
-        # the training forward (also saves p_t) and the backward fed its p_t
         out_t = torch.empty((T, 32, 128), dtype=torch.bfloat16, device=dev)
         hT_t = torch.empty((w.n_seqs, 32, 128, 128), dtype=torch.float32, device=dev)
         sp_t = torch.empty((T, 32, 128), dtype=torch.float32, device=dev)
@@ -749,42 +781,14 @@ def main():
                                workspace=ws, grads=grads, stream=stream, saved_p=sp_t, hT=hT_t)
 
         per_bs, _, _ = time_launches(bwd_saved, args.steps, 3, stream)
-        bwd(0)
-        torch.cuda.synchronize()
-        bflops = 18.0 * 128 * 128 * 32 * T
-        got_g = {"dq": grads["dq"][:, 0:1].cpu(), "dk": grads["dk"][:, 0:1].cpu(), "dv": grads["dv"][:, 0:2].cpu(),
-                 "dbeta": grads["dbeta"][:, 0:2].cpu(), "dg": grads["dg"][:, 0:2].cpu(),
-                 "dh0": grads["dh0"][:, 0:2].cpu()}
-        # the chunked backward (gdn_bwd_chunked, matrix cores) on the same inputs
-        ws_b_bytes = int(ws.numel())
-        del ws
-        ws_cb = torch.empty(gdn.gdn_bwd_chunked_workspace_size(bdims), dtype=torch.uint8, device=dev)
-        grads_c = gdn.gdn_bwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
-                                      workspace=ws_cb, stream=stream)
 
-        def bwd_chunked(_i):
-            gdn.gdn_bwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["cu"], dout_d, dhT_d,
-                                workspace=ws_cb, grads=grads_c, stream=stream)
-
-        # Timed last, right before the benchmark step, so that the step's warm-ups start
-        # on a chip under load (after even a few idle milliseconds the clock needs tens
-        # of milliseconds of load to climb back); its gradients are copied for the
-        # check only after the step.
-        per_bc, _, _ = time_launches(bwd_chunked, args.steps, 3, stream)
-        msbc = float(np.median(per_bc))
-        late_copies.append(lambda: got_gc.update(
-            {"dq": grads_c["dq"][:, 0:1].cpu(), "dk": grads_c["dk"][:, 0:1].cpu(),
-             "dv": grads_c["dv"][:, 0:2].cpu(), "dbeta": grads_c["dbeta"][:, 0:2].cpu(),
-             "dg": grads_c["dg"][:, 0:2].cpu(), "dh0": grads_c["dh0"][:, 0:2].cpu()}))
-        rec_bc = {"tokens": T, "n_seqs": w.n_seqs, "ms_median": msbc, "tokens_per_s": T / (msbc / 1e3),
-                  "launch_ms_percentiles": percentiles(per_bc), "launches": 5,
-                  "workspace_bytes": int(ws_cb.numel()),
-                  "roofline": {"bound": "mfma", "achieved": bflops / (msbc / 1e3) / 1e12,
-                               "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": bflops / (msbc / 1e3) / 1e12 / FP32_MATRIX_PEAK_TFLOPS,
-                               "flops_per_launch": bflops,
-                               "traffic": traffic_from_profile("backward_chunked", src_hash)}}
-        workloads["backward_chunked_prefill"] = rec_bc
+        def copy_bwd_grads():
+            bwd(0)
+            torch.cuda.synchronize()
+            got_g.update({"dq": grads["dq"][:, 0:1].cpu(), "dk": grads["dk"][:, 0:1].cpu(),
+                          "dv": grads["dv"][:, 0:2].cpu(), "dbeta": grads["dbeta"][:, 0:2].cpu(),
+                          "dg": grads["dg"][:, 0:2].cpu(), "dh0": grads["dh0"][:, 0:2].cpu()})
+        late_copies.append(copy_bwd_grads)
         rec_b = {"tokens": T, "n_seqs": w.n_seqs, "ms_median": msb, "tokens_per_s": T / (msb / 1e3),
                  "launch_ms_percentiles": percentiles(per_b),
                  "launches": 6, "workspace_bytes": ws_b_bytes,
@@ -794,7 +798,6 @@ def main():
                               "unit": "TFLOP/s", "frac": bflops / (msb / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
                               "flops_per_launch": bflops}}
         workloads["backward_varlen_prefill"] = rec_b
-        del dout_d, dhT_d, grads, out_t, hT_t, sp_t
         bwd_ref = {}
 
         def bwd_oracle():
