@@ -624,6 +624,32 @@ def main():
         lc = synth.long_context(1003)
         prefill_line("long_context_65536", lc)
         prefill_line("long_context_65536_as_8x8192", lc, chunks=8)
+        # The chunked form (gdn_fwd_chunked, its automatic waves per tile) on the same
+        # sequence, from the zero state: the same 7 dk dv flops per token.
+        dl = [t.to(dev) for t in (lc.q, lc.k, lc.v, lc.g, lc.beta)]
+        cul = lc.cu_seqlens.to(dev)
+        Tl = lc.total_tokens
+        ol = torch.empty((Tl, 32, 128), dtype=torch.bfloat16, device=dev)
+        ws_l = torch.empty(gdn.gdn_chunked_workspace_size(gdn.make_dims(dl[0], dl[2], 1, Tl)),
+                           dtype=torch.uint8, device=dev)
+
+        def chunked_long(_i):
+            gdn.gdn_fwd_chunked(*dl, cul, None, out=ol, stream=stream, workspace=ws_l)
+
+        per_cl, _, _ = time_launches(chunked_long, 5, 2, stream)
+        mscl = float(np.median(per_cl))
+        got_cl = ol.cpu()
+        rec_cl = {"tokens": Tl, "n_seqs": 1, "chunk": 16, "ms_median": mscl, "ms_mean": float(np.mean(per_cl)),
+                  "launch_ms_percentiles": percentiles(per_cl), "tokens_per_s": Tl / (mscl / 1e3),
+                  "roofline_frac": FLOPS_PER_TOKEN * Tl / (mscl / 1e3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS}
+        workloads["chunked_long_context_65536"] = rec_cl
+        del dl, ol, ws_l
+
+        def chunked_long_check(lc=lc, got=got_cl):
+            ro, _ = oracle.gdn_forward(lc.q, lc.k, lc.v, lc.g, lc.beta, lc.cu_seqlens, lc.h0)
+            return {"all_heads": {"out": seq_rel_max(got.float().numpy(), ro, lc.cu_seqlens.tolist())}}
+        checks.append((rec_cl, "parity", chunked_long_check))
+        progress("chunked form, long context %.3f ms" % mscl)
         del lc
         prefill_line("mixed_batch_64", synth.mixed_batch(1004))
 
